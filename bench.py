@@ -1,0 +1,250 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+A step is one call of ``gdr_chunk_fwd`` over the 4K-token workload:
+B=4 sequences x H=16 heads x T=4096 tokens, d_k = d_v = 128, chunk 64,
+bfloat16 inputs and outputs, float32 state, S0 = 0, inputs resident in HBM.
+Inputs are seeded synthetic data with the shapes and gate distributions of
+the Muir page's models (q, k = unit-norm SiLU of N(0,1); v ~ N(0,1);
+alpha = sigmoid(N(4, 1.5)); b, w = sigmoid(N(0,1))).
+
+Printed: one JSON line with tokens/s (value), the chunk kernel's roofline
+position (HBM-bound by algorithmic arithmetic intensity ~77 flop/B), its MFMA
+throughput as a fraction of the bf16 dense peak, side measurements for the
+decode step (HBM GB/s) and the mLSTM forward, and the float64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6
+
+
+def chunk_flops_per_chunk(C, dk, dv):
+    """Algorithmic FLOPs of one chunk of one head: Gram L and M, the triangular
+    solve, the three S0/state products and M V~."""
+    return 2 * dk * C * C + C * (C - 1) * (dv + dk) + 6 * C * dk * dv + C * (C + 1) * dv
+
+
+def chunk_bytes(B, H, T, dk, dv, es, s0=False, s_out=True):
+    n = B * H * T
+    b = n * (4 * dk + 2 * dv) * es + n * dv * es
+    b += B * H * dk * dv * 4 * (int(s0) + int(s_out))
+    return b
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "matrix_memory_rnn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, launches_key="chunk_fwd_4k"):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when missing or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        data = json.load(f)
+    e = data.get(launches_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def to_dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32)
+    return t.to(dtype).cuda()
+
+
+def time_launches(fn, steps, warmup):
+    """Run fn warmup times, then `steps` times between events; returns
+    (ms per step over the region, mean ms per launch from per-launch events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    t1.record()
+    torch.cuda.synchronize()
+    region = t0.elapsed_time(t1) / steps
+    per = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return region, per
+
+
+def bench_chunk(steps, warmup):
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    from synth import CONFIGS, gdn2_inputs
+    c = CONFIGS["chunk_4k"]
+    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
+    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=c["alpha_mu"], alpha_sigma=c["alpha_sigma"], seed=0,
+                    dtype="bf16")
+    x = [to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v", "alpha", "b", "w")]
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    fn = lambda: gdr.gdr_chunk_fwd(*x, None, chunk=C, o=o, S_out=S)
+    region_ms, launch_ms = time_launches(fn, steps, warmup)
+    flops = chunk_flops_per_chunk(C, dk, dv) * (T // C) * B * H
+    nbytes = chunk_bytes(B, H, T, dk, dv, 2)
+    return dict(B=B, H=H, T=T, dk=dk, dv=dv, C=C, region_ms=region_ms, launch_ms=launch_ms,
+                flops=flops, bytes=nbytes, inputs=d)
+
+
+def bench_decode(steps=1024):
+    """256 sequences x 16 heads, d = 128, fp32 states resident in HBM, `steps`
+    sequential one-token updates with fresh inputs each step (drawn on the GPU
+    from a seeded generator with the 4K workload's distributions)."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    N, H, dk, dv = 256, 16, 128, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    pool = 16
+
+    def unit_silu(shape):
+        z = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        s = torch.nn.functional.silu(z)
+        return (s / s.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    inp = []
+    for _ in range(pool):
+        q, k = unit_silu((N, H, dk)), unit_silu((N, H, dk))
+        v = torch.randn((N, H, dv), generator=g, device="cuda").to(torch.bfloat16)
+        a = torch.sigmoid(4.0 + 1.5 * torch.randn((N, H, dk), generator=g, device="cuda")).to(torch.bfloat16)
+        b = torch.sigmoid(torch.randn((N, H, dk), generator=g, device="cuda")).to(torch.bfloat16)
+        w = torch.sigmoid(torch.randn((N, H, dv), generator=g, device="cuda")).to(torch.bfloat16)
+        inp.append((q, k, v, a, b, w))
+    S = torch.zeros((N, H, dk, dv), dtype=torch.float32, device="cuda")
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    it = [0]
+
+    def fn():
+        gdr.gdr_decode_step(*inp[it[0] % pool], S, o=o)
+        it[0] += 1
+
+    region_ms, launch_ms = time_launches(fn, steps, 16)
+    nbytes = 2 * N * H * dk * dv * 4 + N * H * (4 * dk + 2 * dv) * 2 + N * H * dv * 2
+    return dict(N=N, H=H, steps=steps, region_ms=region_ms, launch_ms=launch_ms, bytes=nbytes)
+
+
+def bench_mlstm(steps, warmup):
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    from synth import CONFIGS, mlstm_inputs
+    c = CONFIGS["mlstm_8k"]
+    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
+    d = mlstm_inputs(B, H, T, dk, dv, seed=0, dtype="bf16")
+    q, k, v = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    it, ft = (to_dev(d[n], torch.float32) for n in ("i_tilde", "f_tilde"))
+    h = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: gdr.gdr_mlstm_fwd(q, k, v, it, ft, chunk=C, h=h, return_state=False)
+    region_ms, launch_ms = time_launches(fn, steps, warmup)
+    nbytes = B * H * T * (2 * dk + 2 * dv) * 2 + B * H * T * 8
+    return dict(B=B, H=H, T=T, region_ms=region_ms, launch_ms=launch_ms, bytes=nbytes)
+
+
+def cpu_baseline(d):
+    """The float64 oracle on one sequence (b = 0, all 16 heads, 4096 tokens) of
+    the 4K workload, single-threaded."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    sl = lambda x: np.ascontiguousarray(d[x][0:1])
+    args = [sl(x) for x in ("q", "k", "v", "alpha", "b", "w")]
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        oracle.gdn2_recurrent(*args)
+        dt = time.perf_counter() - t
+    T = args[0].shape[2]
+    return {"value": T / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"b=0 of the 4K workload: 16 heads x {T} tokens, float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-side", action="store_true", help="skip the decode and mLSTM side measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(batch/head sharding needs no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    r = bench_chunk(args.steps, args.warmup)
+    tokens = r["B"] * r["T"]
+    value = tokens / (r["region_ms"] * 1e-3)
+    achieved = r["bytes"] / (r["launch_ms"] * 1e-3) / 1e9
+    traffic = load_traffic("chunk_fwd_4k")
+    tflops = r["flops"] / (r["launch_ms"] * 1e-3) / 1e12
+    out = {
+        "metric": "tokens/s + % bf16 MFMA peak, chunk fwd H=16 d=128 T=4K; decode HBM GB/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["region_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; gate distributions of the Muir page's models)",
+        "config": {"workload": "gdn2 chunk fwd B=4 H=16 T=4096 dk=dv=128 C=64, bf16 in/out, fp32 state, S0=0",
+                   "global_batch": r["B"], "seq_len": r["T"], "heads": r["H"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "mfma": {"tflops": tflops, "peak": PEAK_BF16_TFLOPS, "frac": tflops / PEAK_BF16_TFLOPS,
+                 "flops_per_launch": r["flops"], "note": "algorithmic FLOPs (masked tiles not counted)"},
+        "kernel_ms": r["launch_ms"],
+        "bytes_per_launch": r["bytes"],
+        "token_heads_per_s": value * r["H"],
+    }
+    if not args.no_side:
+        dd = bench_decode()
+        gbs = dd["bytes"] / (dd["launch_ms"] * 1e-3) / 1e9
+        out["decode"] = {"workload": "256 seq x 16 heads, d=128, fp32 state, 1024 steps", "ms_per_step": dd["region_ms"],
+                         "kernel_ms": dd["launch_ms"], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                         "tokens/s": dd["N"] / (dd["region_ms"] * 1e-3)}
+        mm = bench_mlstm(args.steps, args.warmup)
+        mt = mm["B"] * mm["T"] / (mm["region_ms"] * 1e-3)
+        out["mlstm"] = {"workload": "B=2 H=8 T=8192 d=256 C=64 bf16", "ms_per_step": mm["region_ms"],
+                        "kernel_ms": mm["launch_ms"], "tokens/s": mt,
+                        "GB/s": mm["bytes"] / (mm["launch_ms"] * 1e-3) / 1e9}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(r["inputs"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

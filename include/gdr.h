@@ -1,0 +1,143 @@
+/*
+ * gdr.h — gated delta-rule matrix-memory kernels for AMD MI355X (gfx950).
+ *
+ * C ABI of libgdr.so. Every entry point takes plain device pointers, sizes and
+ * a HIP stream, validates its arguments on the host, enqueues its kernels on
+ * that stream and returns without synchronising. No entry point allocates or
+ * frees memory, and the library keeps no hidden state between calls: the
+ * caller owns every buffer. Calls are reentrant; calls that write the same
+ * buffers must be ordered by the caller (same stream or events).
+ *
+ * Notation follows "Muir: Linear Attention with Sensitivity-Allocated Gating
+ * and Matched-Filter Readout" (§2.1 eq.(1)): row vectors, state S[d_k, d_v]
+ * acted on from the left, readout o = q S.
+ *
+ * Layouts: all tensors are contiguous, last dimension fastest.
+ *   sequence tensors  [B, H, T, d]     (head-major: one head's tokens are contiguous)
+ *   states            [B, H, d_k, d_v] (float32, d_v fastest)
+ *   decode tensors    [N, H, d]
+ *
+ * Supported sizes: d_k, d_v in {16, 32, 64, 128} for the gated delta rule,
+ * {16, 32, 64, 128, 256} for mLSTM; chunk in {16, 32, 64}; any T >= 1 (a
+ * ragged last chunk behaves as if padded with identity steps alpha = 1, k = 0,
+ * v = 0, whose outputs are discarded). With float32 inputs and d_k = 128 the
+ * chunk must be at most 32.
+ * Alignment: every pointer must be 16-byte aligned.
+ *
+ * Preconditions not checked on the hot path: alpha in (0, 1]; inputs finite;
+ * output buffers do not overlap input buffers except where stated.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. Negative values are errors; no kernel was enqueued. */
+#define GDR_OK               0
+#define GDR_ERR_NULL        -1  /* a required pointer is NULL */
+#define GDR_ERR_SHAPE       -2  /* a size is out of range (e.g. T < 1, B < 1) */
+#define GDR_ERR_DTYPE       -3  /* unknown dtype code */
+#define GDR_ERR_UNSUPPORTED -4  /* sizes valid but not built (d or chunk outside the supported set) */
+#define GDR_ERR_ALIGN       -5  /* a pointer is not 16-byte aligned */
+#define GDR_ERR_LAUNCH      -6  /* the HIP runtime rejected a kernel launch */
+#define GDR_ERR_ALIAS       -7  /* an output buffer overlaps an input buffer */
+
+/* Input/output element types. States (S, C, n, m) are always float32. */
+#define GDR_F32  0
+#define GDR_BF16 1
+
+/*
+ * gdr_chunk_fwd — chunkwise-parallel forward of the channel-wise gated delta
+ * rule over whole sequences.
+ *
+ * Computes, for every (b, h) and t = 1..T, the recurrence of "Muir: ...",
+ * §2.1 eq.(1):
+ *     S_t = (I - k_t^T (b_t * k_t)) Diag(alpha_t) S_{t-1} + k_t^T (w_t * v_t),
+ *     o_t = q_t S_t,
+ * starting from S_0, and returns all o_t and S_T. It evaluates the recurrence
+ * chunk by chunk with the UT form of §2.2 (T V~ = V^ - K^_pi S_0, O = Q_pi S_0
+ * + M V~, S_C = Diag(pi_C) S_0 + K~^T V~), keeping every decay factor a
+ * product of alphas over an interval so that nothing divides by a vanishing
+ * cumulative decay.
+ *
+ *   q, k, alpha, b  [B,H,T,dk]  input dtype (query, key, decay gate, erase gate)
+ *   v, w            [B,H,T,dv]  input dtype (value, write gate)
+ *   S0              [B,H,dk,dv] float32 initial state, or NULL for zeros
+ *   o               [B,H,T,dv]  output, input dtype
+ *   S_out           [B,H,dk,dv] float32 final state, or NULL to skip; may
+ *                   equal S0 (in-place update), must not otherwise overlap it
+ *   chunk           chunk length C (16, 32 or 64)
+ *   dtype           GDR_F32 or GDR_BF16 (applies to q, k, v, alpha, b, w, o)
+ *   stream          hipStream_t to enqueue on (NULL = default stream)
+ * Returns GDR_OK or a negative GDR_ERR_* code.
+ */
+int gdr_chunk_fwd(const void* q, const void* k, const void* v,
+                  const void* alpha, const void* b, const void* w,
+                  const float* S0, void* o, float* S_out,
+                  int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                  void* stream);
+
+/*
+ * gdr_decode_step — one recurrent step of "Muir: ...", §2.1 eq.(1) for N
+ * independent sequences, updating their resident states in place.
+ *
+ * For each (n, h): with S the state before the call,
+ *     S <- (I - k^T (b * k)) Diag(alpha) S + k^T (w * v),   o = q S (new S).
+ * It reads S once and writes it once: r = (alpha*b*k) S and p = (alpha*q) S
+ * come from one pass, then S <- Diag(alpha) S + k^T (w*v - r) and
+ * o = p + (q . k)(w*v - r).
+ *
+ *   q, k, alpha, b  [N,H,dk]     input dtype
+ *   v, w            [N,H,dv]     input dtype
+ *   S               [N,H,dk,dv]  float32 state, read and written in place
+ *   o               [N,H,dv]     output, input dtype
+ * Returns GDR_OK or a negative GDR_ERR_* code.
+ */
+int gdr_decode_step(const void* q, const void* k, const void* v,
+                    const void* alpha, const void* b, const void* w,
+                    float* S, void* o,
+                    int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * gdr_mlstm_fwd — chunkwise forward of the xLSTM mLSTM cell with its
+ * log-domain stabiliser ("Exponential gates and matrix memory: xLSTM and
+ * RWKV-7", §13.4 and Exercise 13.6), in the [dk, dv] orientation:
+ *     log f_t = log sigmoid(f_tilde_t),  m_t = max(log f_t + m_{t-1}, i_tilde_t),
+ *     C_t = e^{log f_t + m_{t-1} - m_t} C_{t-1} + e^{i_tilde_t - m_t} k_t^T v_t,
+ *     n_t = e^{log f_t + m_{t-1} - m_t} n_{t-1} + e^{i_tilde_t - m_t} k_t,
+ *     h_t = q_t C_t / max(|q_t . n_t|, e^{-m_t}).
+ * Within a chunk the running max is evaluated in its closed form
+ * m_t = F_t + max(m_0, max_{s<=t}(i_tilde_s - F_s)), F_t = sum_{r<=t} log f_r,
+ * so every exponent is <= 0.
+ *
+ *   q, k            [B,H,T,dk]  input dtype
+ *   v               [B,H,T,dv]  input dtype
+ *   i_tilde, f_tilde [B,H,T]    float32 input log-gate and forget-gate logit
+ *   C0, n0, m0      [B,H,dk,dv], [B,H,dk], [B,H] float32 initial state; pass
+ *                   all three NULL for the empty state (C = 0, n = 0, m = -inf)
+ *   h               [B,H,T,dv]  output, input dtype
+ *   C_out, n_out, m_out  final state (float32); all NULL to skip. C_out may
+ *                   equal C0 (in-place update); n_out and m_out must not
+ *                   overlap n0 or m0 (every value tile of a head reads them).
+ * Returns GDR_OK or a negative GDR_ERR_* code.
+ */
+int gdr_mlstm_fwd(const void* q, const void* k, const void* v,
+                  const float* i_tilde, const float* f_tilde,
+                  const float* C0, const float* n0, const float* m0,
+                  void* h, float* C_out, float* n_out, float* m_out,
+                  int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                  void* stream);
+
+/* Human-readable text for a return code (static storage). */
+const char* gdr_status_string(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

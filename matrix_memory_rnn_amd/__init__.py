@@ -1,0 +1,197 @@
+"""Gated delta-rule matrix-memory kernels for AMD MI355X — Python binding.
+
+A thin ctypes layer over ``libgdr.so`` (see ``include/gdr.h``): it checks
+tensor shapes and dtypes, allocates outputs with torch, and passes raw device
+pointers and the current HIP stream to the C entry points. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. If the
+library has not been built the first call raises.
+
+Entry points (same names as the C ABI):
+
+* :func:`gdr_chunk_fwd` — chunkwise forward of the channel-wise gated delta
+  rule ("Muir: Linear Attention with Sensitivity-Allocated Gating and
+  Matched-Filter Readout", §2.1 eq.(1), §2.2).
+* :func:`gdr_decode_step` — one recurrent decode step, state updated in place.
+* :func:`gdr_mlstm_fwd` — chunkwise forward of the stabilised mLSTM cell
+  ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["gdr_chunk_fwd", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
+           "GdrError", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libgdr.so")
+
+GDR_F32, GDR_BF16 = 0, 1
+_lib = None
+
+
+class GdrError(RuntimeError):
+    """A libgdr entry point returned a negative status."""
+
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def load_library():
+    """Load libgdr.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(
+            f"{lib_path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or `python matrix_memory_rnn_amd/build.py`); there is no fallback implementation")
+    lib = ctypes.CDLL(lib_path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 7 + [P]
+    lib.gdr_chunk_fwd.restype = I
+    lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
+    lib.gdr_decode_step.restype = I
+    lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
+    lib.gdr_mlstm_fwd.restype = I
+    lib.gdr_status_string.argtypes = [I]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_version.argtypes = []
+    lib.gdr_version.restype = I
+    _lib = lib
+    return lib
+
+
+def gdr_version() -> int:
+    return load_library().gdr_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        lib = load_library()
+        raise GdrError(fn, status, lib.gdr_status_string(status).decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _req(t, name, shape, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device or not t.is_cuda:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gdr_chunk_fwd(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=None,
+                  return_state=True, stream=None):
+    """Chunkwise gated delta rule over whole sequences.
+
+    q, k, alpha, b: ``[B,H,T,dk]``; v, w: ``[B,H,T,dv]`` (bfloat16 or float32,
+    all the same dtype, on one GPU). S0: ``[B,H,dk,dv]`` float32 or None (zero
+    state). Returns ``(o, S_T)`` with o ``[B,H,T,dv]`` in the input dtype and
+    S_T float32 (None if ``return_state`` is False). ``S_out`` may be S0 for
+    an in-place state update.
+    """
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("alpha", alpha, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _req(t, name, (B, H, T, d), dt, dev)
+    if S0 is not None:
+        _req(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _req(o, "o", (B, H, T, dv), dt, dev)
+    if S_out is None and return_state:
+        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if S_out is not None:
+        _req(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
+    lib = load_library()
+    st = lib.gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                           _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q),
+                           _stream(stream))
+    _check("gdr_chunk_fwd", st)
+    return o, S_out
+
+
+def gdr_decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
+    """One decode step for N sequences: q, k, alpha, b ``[N,H,dk]``; v, w ``[N,H,dv]``;
+    S ``[N,H,dk,dv]`` float32, updated in place. Returns o ``[N,H,dv]``."""
+    import torch
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("alpha", alpha, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _req(t, name, (N, H, d), dt, dev)
+    _req(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _req(o, "o", (N, H, dv), dt, dev)
+    lib = load_library()
+    st = lib.gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S),
+                             _ptr(o), N, H, dk, dv, _dtype_code(q), _stream(stream))
+    _check("gdr_decode_step", st)
+    return o
+
+
+def gdr_mlstm_fwd(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, chunk=64, h=None,
+                  C_out=None, n_out=None, m_out=None, return_state=True, stream=None):
+    """Stabilised mLSTM forward. q, k ``[B,H,T,dk]``, v ``[B,H,T,dv]`` (bf16/fp32);
+    i_tilde, f_tilde ``[B,H,T]`` float32; optional state (C0 ``[B,H,dk,dv]``,
+    n0 ``[B,H,dk]``, m0 ``[B,H]``, float32; all or none). Returns
+    ``(h, C_T, n_T, m_T)`` (state entries None if ``return_state`` is False)."""
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    _req(q, "q", (B, H, T, dk), dt, dev)
+    _req(k, "k", (B, H, T, dk), dt, dev)
+    _req(v, "v", (B, H, T, dv), dt, dev)
+    _req(i_tilde, "i_tilde", (B, H, T), torch.float32, dev)
+    _req(f_tilde, "f_tilde", (B, H, T), torch.float32, dev)
+    if (C0 is None) != (n0 is None) or (C0 is None) != (m0 is None):
+        raise ValueError("pass all of C0, n0, m0 or none of them")
+    if C0 is not None:
+        _req(C0, "C0", (B, H, dk, dv), torch.float32, dev)
+        _req(n0, "n0", (B, H, dk), torch.float32, dev)
+        _req(m0, "m0", (B, H), torch.float32, dev)
+    if h is None:
+        h = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    _req(h, "h", (B, H, T, dv), dt, dev)
+    if return_state and C_out is None:
+        C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    lib = load_library()
+    st = lib.gdr_mlstm_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(i_tilde), _ptr(f_tilde), _ptr(C0),
+                           _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
+                           B, H, T, dk, dv, int(chunk), _dtype_code(q), _stream(stream))
+    _check("gdr_mlstm_fwd", st)
+    return h, C_out, n_out, m_out

@@ -1,0 +1,42 @@
+// Internal host-side interface between the C-ABI entry points (gdr_api.hip)
+// and the kernel launchers. Not installed; not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <type_traits>
+
+#include "../../include/gdr.h"
+
+namespace gdr {
+
+struct ChunkArgs {
+  const void *q, *k, *v, *alpha, *b, *w;
+  const float* S0;
+  void* o;
+  float* S_out;
+  int B, H, T, dk, dv, chunk, dtype;
+  void* stream;
+};
+
+struct DecodeArgs {
+  const void *q, *k, *v, *alpha, *b, *w;
+  float* S;
+  void* o;
+  int N, H, dk, dv, dtype;
+  void* stream;
+};
+
+struct MlstmArgs {
+  const void *q, *k, *v;
+  const float *i_tilde, *f_tilde, *C0, *n0, *m0;
+  void* h;
+  float *C_out, *n_out, *m_out;
+  int B, H, T, dk, dv, chunk, dtype;
+  void* stream;
+};
+
+int chunk_fwd_launch(const ChunkArgs& a);
+int decode_launch(const DecodeArgs& a);
+int mlstm_launch(const MlstmArgs& a);
+
+}  // namespace gdr

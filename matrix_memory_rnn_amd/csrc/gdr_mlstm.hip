@@ -1,0 +1,372 @@
+// Chunkwise forward of the xLSTM mLSTM cell with its log-domain stabiliser on
+// gfx950 ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4 and
+// the solution to Exercise 13.6), in the [d_k, d_v] state orientation.
+//
+// Per chunk of C tokens with incoming state (C0, n0, m0):
+//   F_t   = sum_{r<=t} log sigmoid(f_tilde_r)           (within the chunk)
+//   a_s   = i_tilde_s - F_s
+//   mu_t  = max(m0, max_{s<=t} a_s),   m_t = F_t + mu_t  (the running max of
+//           m_t = max(log f_t + m_{t-1}, i_tilde_t), unrolled)
+//   h^_t  = e^{m0 - mu_t} q_t C0 + sum_{s<=t} (q_t . k_s) e^{a_s - mu_t} v_s
+//   n^_t  = e^{m0 - mu_t} q_t . n0 + sum_{s<=t} (q_t . k_s) e^{a_s - mu_t}
+//   h_t   = h^_t / max(|n^_t|, e^{-m_t})
+//   C_C   = e^{m0 - mu_C} C0 + sum_s e^{a_s - mu_C} k_s^T v_s   (n likewise)
+// Every exponent above is <= 0 by construction of mu. The normaliser n rides
+// along as an extra value column (a 16-wide tile whose first column is n and
+// whose value row is all ones), so h^ and n^ come out of the same MFMAs.
+//
+// One workgroup (256 threads) per (b, h, value tile of VT columns); the tile
+// walks the chunks sequentially, holding its [C | n] state slice in registers.
+#include "gdr_device.hpp"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+template <int DK, int VT, int CM, bool SPLIT>
+struct MlstmSmem {
+  static constexpr int NS = SPLIT ? 2 : 1;
+  static constexpr int NVA = VT / 16 + 1;  // value tiles incl. the normaliser tile
+  static constexpr int VA = 16 * NVA;
+  static constexpr int LDK = DK + 8;
+  static constexpr int LDC = CM + 8;
+  static constexpr int P_Q = CM * LDK * 2;
+  static constexpr int P_KT = DK * LDC * 2;
+  static constexpr int P_V = VA * LDC * 2;
+  static constexpr int P_W = CM * LDC * 2;
+  static constexpr int P_C0 = VA * LDK * 2;
+  static constexpr int Q = 0;
+  static constexpr int K = Q + NS * P_Q;
+  static constexpr int KT = K + NS * P_Q;
+  static constexpr int VTR = KT + NS * P_KT;   // [v][s] raw values, ones row for n
+  static constexpr int VTW = VTR + NS * P_V;   // [v][s] scaled by e^{a_s - mu_C}
+  static constexpr int W = VTW + NS * P_V;     // [t][s] (q.k) e^{a_s - mu_t}
+  static constexpr int C0T = W + NS * P_W;     // [v][j] state^T (+ n row)
+  static constexpr int SC = C0T + NS * P_C0;   // fp32 scalars: a, mu, m, wstate, nbar
+  static constexpr int TOTAL = SC + 5 * CM * 4 + 16;
+  static_assert(TOTAL <= 160 * 1024, "mLSTM kernel LDS exceeds 160 KiB");
+};
+
+__device__ __forceinline__ float log_sigmoid(float x) {
+  // log sigmoid(x) = -softplus(-x) = min(x, 0) - log1p(exp(-|x|))
+  return fminf(x, 0.f) - log1pf(__expf(-fabsf(x)));
+}
+
+template <typename Tin, int DK, int VT, int CM, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ i_tilde, const float* __restrict__ f_tilde,
+    const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
+    Tin* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV, int C) {
+  using L = MlstmSmem<DK, VT, CM, SPLIT>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NVL = VT / 16, NVA = L::NVA;
+  constexpr int NST = (DK / 16) * NVA;
+  constexpr int MAXS = (NST + 3) / 4;
+  constexpr int NBM = CM / 16;
+  constexpr int MAXP = (NBM * (NBM + 1) / 2 + 3) / 4;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nvt = DV / VT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
+  const int NB = C / 16, NP = NB * (NB + 1) / 2;
+  const int nchunks = (T + C - 1) / C;
+  const size_t seqK = (size_t)bh * T * DK, seqV = (size_t)bh * T * DV, seqG = (size_t)bh * T;
+
+  float* sA = (float*)(smem + L::SC);
+  float* sMu = sA + CM;
+  float* sM = sMu + CM;
+  float* sWs = sM + CM;
+  float* sN = sWs + CM;
+
+  // ---- state slice [C | n] -> registers and C0^T (bf16)
+  const bool have_state = (C0 != nullptr);
+  float mprev = have_state ? m0[bh] : -INFINITY;
+  f32x4 Sacc[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    Sacc[i] = f4zero();
+    const int tile = wid + 4 * i;
+    if (tile < NST) {
+      const int jt = tile / NVA, vl = tile % NVA;
+      if (have_state) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * g + e;
+          if (vl < NVL) Sacc[i][e] = C0[(size_t)bh * DK * DV + (size_t)j * DV + vt0 + 16 * vl + c16];
+          else Sacc[i][e] = (c16 == 0) ? n0[(size_t)bh * DK + j] : 0.f;
+        }
+      }
+      st4<SPLIT>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+    }
+  }
+  __syncthreads();
+
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int t0 = ch * C;
+    // ---------------- gates: F, a, mu, m (wave 0, one lane per token)
+    if (wid == 0) {
+      const int t = lane;
+      const bool valid = (t < C) && (t0 + t < T);
+      float lf = 0.f, it = -INFINITY;
+      if (valid) {
+        lf = log_sigmoid(f_tilde[seqG + t0 + t]);
+        it = i_tilde[seqG + t0 + t];
+      }
+      float F = lf;  // inclusive prefix sum over the chunk
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(F, off, 64);
+        if (lane >= off) F += y;
+      }
+      const float a = it - F;
+      float cm = a;  // inclusive prefix max
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(cm, off, 64);
+        if (lane >= off) cm = fmaxf(cm, y);
+      }
+      const float mu = fmaxf(mprev, cm);
+      const float muC = __shfl(mu, C - 1, 64);
+      if (t < C) {
+        sA[t] = a;
+        sMu[t] = mu;
+        sM[t] = F + mu;
+        sWs[t] = valid ? __expf(a - muC) : 0.f;
+      }
+    }
+    // ---------------- q, k (natural and transposed), v^T with the ones row
+    {
+      constexpr int KG = DK / 8;
+      for (int it = tid; it < C * KG; it += 256) {  // q and k, k-contiguous rows
+        const int s = it / KG, j0 = (it % KG) * 8;
+        const int tg = t0 + s;
+        float qv[8], kv[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float2 a2 = make_float2(0.f, 0.f), b2 = make_float2(0.f, 0.f);
+          if (tg < T) {
+            a2 = In<Tin>::load2(q + seqK + (size_t)tg * DK + j0 + e);
+            b2 = In<Tin>::load2(k + seqK + (size_t)tg * DK + j0 + e);
+          }
+          qv[e] = a2.x; qv[e + 1] = a2.y; kv[e] = b2.x; kv[e + 1] = b2.y;
+        }
+        st4<SPLIT>(smem + L::Q, L::P_Q, s * L::LDK + j0, f32x4{qv[0], qv[1], qv[2], qv[3]});
+        st4<SPLIT>(smem + L::Q, L::P_Q, s * L::LDK + j0 + 4, f32x4{qv[4], qv[5], qv[6], qv[7]});
+        st4<SPLIT>(smem + L::K, L::P_Q, s * L::LDK + j0, f32x4{kv[0], kv[1], kv[2], kv[3]});
+        st4<SPLIT>(smem + L::K, L::P_Q, s * L::LDK + j0 + 4, f32x4{kv[4], kv[5], kv[6], kv[7]});
+      }
+      for (int it = tid; it < C * KG; it += 256) {  // k^T: lanes run along s (conflict-free)
+        const int s = it % C, j0 = (it / C) * 8;
+        const int tg = t0 + s;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float2 b2 = make_float2(0.f, 0.f);
+          if (tg < T) b2 = In<Tin>::load2(k + seqK + (size_t)tg * DK + j0 + e);
+          st1<SPLIT>(smem + L::KT, L::P_KT, (j0 + e) * L::LDC + s, b2.x);
+          st1<SPLIT>(smem + L::KT, L::P_KT, (j0 + e + 1) * L::LDC + s, b2.y);
+        }
+      }
+      for (int it = tid; it < L::VA * C; it += 256) {  // v^T (+ normaliser row), lanes along s
+        const int s = it % C, vr = it / C;
+        const int tg = t0 + s;
+        float val = 0.f;
+        if (vr < VT) {
+          if (tg < T) val = In<Tin>::load1(v + seqV + (size_t)tg * DV + vt0 + vr);
+        } else if (vr == VT) {
+          val = (tg < T) ? 1.f : 0.f;
+        }
+        st1<SPLIT>(smem + L::VTR, L::P_V, vr * L::LDC + s, val);
+      }
+    }
+    __syncthreads();
+    // scaled values for the state update
+    for (int it = tid; it < L::VA * C; it += 256) {
+      const int s = it % C, vr = it / C;
+      float val = (float)((const __bf16*)(smem + L::VTR))[vr * L::LDC + s];
+      if constexpr (SPLIT) val += (float)((const __bf16*)(smem + L::VTR + L::P_V))[vr * L::LDC + s];
+      st1<SPLIT>(smem + L::VTW, L::P_V, vr * L::LDC + s, val * sWs[s]);
+    }
+
+    // ---------------- scores (transposed tiles) and the inter-chunk readout
+    f32x4 gP[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+      gP[i] = f4zero();
+      const int p = wid + 4 * i;
+      if (p < NP) {
+        int tb = 0;
+        while ((tb + 1) * (tb + 2) / 2 <= p) ++tb;
+        const int sb = p - tb * (tb + 1) / 2;
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::K, L::P_Q, L::LDK, 16 * sb, k0, DK, lane);
+          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::Q, L::P_Q, L::LDK, 16 * tb, k0, DK, lane);
+          mma<SPLIT>(gP[i], A, B);
+        }
+      }
+    }
+    f32x4 Hin[NVA];
+    if (wid < NB) {
+#pragma unroll
+      for (int vl = 0; vl < NVA; ++vl) {
+        Hin[vl] = f4zero();
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::C0T, L::P_C0, L::LDK, 16 * vl, k0, DK, lane);
+          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::Q, L::P_Q, L::LDK, 16 * wid, k0, DK, lane);
+          mma<SPLIT>(Hin[vl], A, B);
+        }
+      }
+    }
+    __syncthreads();
+    // W[t][s] = (q_t . k_s) e^{a_s - mu_t}, s <= t
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+      const int p = wid + 4 * i;
+      if (p < NP) {
+        int tb = 0;
+        while ((tb + 1) * (tb + 2) / 2 <= p) ++tb;
+        const int sb = p - tb * (tb + 1) / 2;
+        const int t = 16 * tb + c16, s0 = 16 * sb + 4 * g;
+        const float mut = sMu[t];
+        f32x4 wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = s0 + e;
+          wv[e] = (s <= t) ? gP[i][e] * __expf(sA[s] - mut) : 0.f;
+        }
+        st4<SPLIT>(smem + L::W, L::P_W, t * L::LDC + s0, wv);
+      }
+    }
+    __syncthreads();
+
+    // ---------------- intra-chunk readout and normaliser
+    f32x4 Hx[NVA];
+    if (wid < NB) {
+      const int tb = wid, kend = 16 * (tb + 1);
+      const int t = 16 * tb + c16;
+      const float winter = (mprev == -INFINITY) ? 0.f : __expf(mprev - sMu[t]);
+#pragma unroll
+      for (int vl = 0; vl < NVA; ++vl) {
+        f32x4 acc = f4zero();
+        for (int k0 = 0; k0 < kend; k0 += 32) {
+          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::VTR, L::P_V, L::LDC, 16 * vl, k0, kend, lane);
+          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::W, L::P_W, L::LDC, 16 * tb, k0, kend, lane);
+          mma<SPLIT>(acc, A, B);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Hx[vl][e] = winter * Hin[vl][e] + acc[e];
+      }
+      if (g == 0) sN[t] = Hx[NVL][0];  // row 0 of the normaliser tile
+    }
+    __syncthreads();
+    if (wid < NB) {
+      const int t = 16 * wid + c16, tg = t0 + t;
+      const float den = fmaxf(fabsf(sN[t]), __expf(-sM[t]));
+      const float inv = 1.f / den;
+      if (tg < T) {
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl) {
+          f32x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = Hx[vl][e] * inv;
+          In<Tin>::store4(h + seqV + (size_t)tg * DV + vt0 + 16 * vl + 4 * g, hv);
+        }
+      }
+    }
+
+    // ---------------- state update: C <- e^{m0 - mu_C} C + K^T (w .* [V | 1])
+    const float muC = sMu[C - 1];
+    const float dstate = (mprev == -INFINITY) ? 0.f : __expf(mprev - muC);
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + 4 * i;
+      if (tile < NST) {
+        const int jt = tile / NVA, vl = tile % NVA;
+        f32x4 acc = f4zero();
+        for (int k0 = 0; k0 < C; k0 += 32) {
+          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::KT, L::P_KT, L::LDC, 16 * jt, k0, C, lane);
+          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::VTW, L::P_V, L::LDC, 16 * vl, k0, C, lane);
+          mma<SPLIT>(acc, A, B);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[i][e] = dstate * Sacc[i][e] + acc[e];
+      }
+    }
+    mprev = sM[C - 1];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + 4 * i;
+      if (tile < NST) {
+        const int jt = tile / NVA, vl = tile % NVA;
+        st4<SPLIT>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+      }
+    }
+  }
+
+  if (C_out) {
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + 4 * i;
+      if (tile < NST) {
+        const int jt = tile / NVA, vl = tile % NVA;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * g + e;
+          if (vl < NVL) C_out[(size_t)bh * DK * DV + (size_t)j * DV + vt0 + 16 * vl + c16] = Sacc[i][e];
+          else if (c16 == 0 && vt0 == 0) n_out[(size_t)bh * DK + j] = Sacc[i][e];
+        }
+      }
+    }
+    if (tid == 0 && vt0 == 0) m_out[bh] = mprev;
+  }
+}
+
+template <typename Tin, int DK, int VT, int CM>
+static int launch_mlstm(const MlstmArgs& a) {
+  constexpr bool SPLIT = std::is_same<Tin, float>::value;
+  using L = MlstmSmem<DK, VT, CM, SPLIT>;
+  auto kern = mlstm_chunk_kernel<Tin, DK, VT, CM, SPLIT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
+        hipSuccess)
+      return GDR_ERR_LAUNCH;
+    attr_set = true;
+  }
+  const int nblocks = a.B * a.H * (a.dv / VT);
+  const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
+  const float *it = a.i_tilde, *ft = a.f_tilde, *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
+  Tin* h = (Tin*)a.h;
+  float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
+  int T = a.T, DV = a.dv, C = a.chunk;
+  void* args[] = {&q, &k, &v, &it, &ft, &C0, &n0, &m0, &h, &Co, &no, &mo, &T, &DV, &C};
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(256), args, L::TOTAL,
+                                 (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+template <typename Tin, int VT>
+static int mlstm_dk(const MlstmArgs& a) {
+  constexpr bool SPLIT = std::is_same<Tin, float>::value;
+  switch (a.dk) {
+    case 16: return launch_mlstm<Tin, 16, VT, 64>(a);
+    case 32: return launch_mlstm<Tin, 32, VT, 64>(a);
+    case 64: return launch_mlstm<Tin, 64, VT, 64>(a);
+    case 128: return launch_mlstm<Tin, 128, VT, 64>(a);
+    case 256:
+      if constexpr (!SPLIT) return launch_mlstm<Tin, 256, VT, 64>(a);
+      break;
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+int mlstm_launch(const MlstmArgs& a) {
+  if (a.dtype == GDR_BF16) return a.dv == 16 ? mlstm_dk<__bf16, 16>(a) : mlstm_dk<__bf16, 32>(a);
+  return mlstm_dk<float, 16>(a);
+}
+
+}  // namespace gdr

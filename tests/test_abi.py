@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/gdr.h declares, and rejects bad arguments with the documented codes
+before enqueuing anything (all pointers here are fake and never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+LIB = os.path.join(ROOT, "matrix_memory_rnn_amd", "libgdr.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libgdr.so not built")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdr_\w+)\s*\(", txt, re.M)))
+
+
+def _codes():
+    txt = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(GDR_\w+)\s+(-?\d+)", txt)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import matrix_memory_rnn_amd as m
+    return m.load_library()
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared()
+    for n in ("gdr_chunk_fwd", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_status_string", "gdr_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(gdr_\w+)", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_symbols_resolve_through_dlopen(lib):
+    for n in _declared():
+        assert hasattr(lib, n)
+    assert lib.gdr_version() == 100
+
+
+def test_status_strings(lib):
+    codes = _codes()
+    for name, val in codes.items():
+        if name.startswith("GDR_ERR_") or name == "GDR_OK":
+            s = lib.gdr_status_string(val).decode()
+            assert s and s != "unknown status"
+    assert lib.gdr_status_string(12345).decode() == "unknown status"
+
+
+# fake, 16-byte aligned, well-separated device addresses (never touched)
+BASE = 0x7F0000000000
+P = [BASE + i * (1 << 32) for i in range(16)]
+
+
+def _chunk(lib, ptrs=None, B=1, H=2, T=64, dk=16, dv=16, chunk=16, dtype=1, S0=None, S_out=None):
+    p = list(P[:7]) if ptrs is None else ptrs
+    return lib.gdr_chunk_fwd(p[0], p[1], p[2], p[3], p[4], p[5], S0, p[6], S_out,
+                             B, H, T, dk, dv, chunk, dtype, None)
+
+
+def test_chunk_validation(lib):
+    c = _codes()
+    assert _chunk(lib, ptrs=[None] + P[1:7]) == c["GDR_ERR_NULL"]
+    assert _chunk(lib, T=0) == c["GDR_ERR_SHAPE"]
+    assert _chunk(lib, B=0) == c["GDR_ERR_SHAPE"]
+    assert _chunk(lib, dtype=7) == c["GDR_ERR_DTYPE"]
+    assert _chunk(lib, dk=48) == c["GDR_ERR_UNSUPPORTED"]
+    assert _chunk(lib, dv=256) == c["GDR_ERR_UNSUPPORTED"]
+    assert _chunk(lib, chunk=128) == c["GDR_ERR_UNSUPPORTED"]
+    assert _chunk(lib, dk=128, dv=128, chunk=64, dtype=0) == c["GDR_ERR_UNSUPPORTED"]
+    assert _chunk(lib, ptrs=[P[0] + 8] + P[1:7]) == c["GDR_ERR_ALIGN"]
+    assert _chunk(lib, S0=P[8] + 4) == c["GDR_ERR_ALIGN"]
+    # o overlapping q
+    assert _chunk(lib, ptrs=P[:6] + [P[0] + 64]) == c["GDR_ERR_ALIAS"]
+    # S_out overlapping (but not equal to) S0
+    assert _chunk(lib, S0=P[8], S_out=P[8] + 256) == c["GDR_ERR_ALIAS"]
+
+
+def test_decode_validation(lib):
+    c = _codes()
+    f = lambda ptrs, N=4, H=2, dk=16, dv=16, dtype=1: lib.gdr_decode_step(*ptrs, N, H, dk, dv, dtype, None)
+    assert f([None] + P[1:8]) == c["GDR_ERR_NULL"]
+    assert f(P[:8], N=0) == c["GDR_ERR_SHAPE"]
+    assert f(P[:8], dtype=-1) == c["GDR_ERR_DTYPE"]
+    assert f(P[:8], dk=24) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(P[:6] + [P[6] + 2, P[7]]) == c["GDR_ERR_ALIGN"]
+    assert f(P[:6] + [P[6], P[6] + 512]) == c["GDR_ERR_ALIAS"]     # o inside S
+
+
+def test_mlstm_validation(lib):
+    c = _codes()
+
+    def f(q=P[0], k=P[1], v=P[2], it=P[3], ft=P[4], C0=None, n0=None, m0=None, h=P[5],
+          Co=None, no=None, mo=None, B=1, H=2, T=64, dk=16, dv=16, chunk=64, dtype=1):
+        return lib.gdr_mlstm_fwd(q, k, v, it, ft, C0, n0, m0, h, Co, no, mo, B, H, T, dk, dv, chunk, dtype, None)
+
+    assert f(q=None) == c["GDR_ERR_NULL"]
+    assert f(C0=P[6]) == c["GDR_ERR_NULL"]                 # partial initial state
+    assert f(Co=P[6], no=P[7]) == c["GDR_ERR_NULL"]        # partial final state
+    assert f(T=-3) == c["GDR_ERR_SHAPE"]
+    assert f(dtype=2) == c["GDR_ERR_DTYPE"]
+    assert f(dk=512) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(dk=256, dtype=0) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(chunk=8) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(it=P[3] + 4) == c["GDR_ERR_ALIGN"]
+    assert f(h=P[0]) == c["GDR_ERR_ALIAS"]
+    # n_out may not be n0 (all value tiles of a head read n0)
+    assert f(C0=P[6], n0=P[7], m0=P[8], Co=P[9], no=P[7], mo=P[10]) == c["GDR_ERR_ALIAS"]
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import matrix_memory_rnn_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "lib_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        m.load_library()

@@ -1,0 +1,79 @@
+"""Parity of gdr_decode_step (HIP, gfx950) with the float64 oracle, and the
+decode == chunk invariant."""
+import numpy as np
+import pytest
+
+import oracle
+from synth import CONFIGS, decode_inputs, gdn2_inputs
+from tests.gpu_util import TOL, dev, host, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(S, d):
+    import matrix_memory_rnn_amd as gdr
+    t = lambda x: dev(d[x], d["dtype"])
+    return gdr.gdr_decode_step(t("q"), t("k"), t("v"), t("alpha"), t("b"), t("w"), S)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16)])
+def test_decode_steps(dtype, dk, dv):
+    import torch
+    N, H, steps = 3, 2, 6
+    rng = np.random.default_rng(dk * dv)
+    S0 = (0.3 * rng.standard_normal((N, H, dk, dv))).astype(np.float32).astype(np.float64)
+    S = dev(S0)
+    S_ref = S0
+    for st in range(steps):
+        d = decode_inputs(N, H, dk, dv, step=st, seed=1, dtype=dtype, alpha_mu=2.0, alpha_sigma=1.0)
+        o = _step(S, d)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle.gdn2_decode(S_ref, d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"])
+        eo = rel_err(host(o), o_ref)
+        assert eo <= TOL[dtype], (st, eo)
+    es = rel_err(host(S), S_ref)
+    say(f"[decode] {dtype} dk={dk} dv={dv}: err_S={es:.3e}")
+    assert es <= TOL[dtype]
+
+
+def test_decode_equals_chunk():
+    """T decode steps reproduce the chunkwise forward over the same T tokens."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    d = gdn2_inputs(2, 2, 40, 64, 64, alpha_mu=3.0, alpha_sigma=1.0, seed=3, dtype="f32", s0_std=0.2)
+    t = lambda x: dev(d[x], "f32")
+    full = [t(x) for x in ("q", "k", "v", "alpha", "b", "w")]
+    o_c, S_c = gdr.gdr_chunk_fwd(*full, dev(d["S0"]), chunk=16)
+    S = dev(d["S0"])
+    outs = []
+    for i in range(40):
+        outs.append(gdr.gdr_decode_step(*[x[:, :, i].contiguous() for x in full], S))
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, dim=2)
+    assert rel_err(host(o_d), host(o_c)) < 5e-5 and rel_err(host(S), host(S_c)) < 5e-5
+
+
+def test_full_size_decode_sampled_heads():
+    """256 sequences x 16 heads, d = 128, three consecutive steps from S0 = 0;
+    the oracle follows a sample of the 4096 states."""
+    import torch
+    c = CONFIGS["decode"]
+    N, H, dk, dv = c["N"], c["H"], c["dk"], c["dv"]
+    S = torch.zeros((N, H, dk, dv), dtype=torch.float32, device="cuda")
+    sample = [(0, 0), (17, 5), (255, 15), (128, 8)]
+    S_ref = {nh: np.zeros((1, 1, dk, dv)) for nh in sample}
+    for st in range(3):
+        d = decode_inputs(N, H, dk, dv, step=st, seed=0, dtype=c["dtype"])
+        o = host(_step(S, d))
+        torch.cuda.synchronize()
+        for (n, h) in sample:
+            sl = lambda x: x[n:n + 1, h:h + 1]
+            o_ref, S_ref[(n, h)] = oracle.gdn2_decode(S_ref[(n, h)], *(sl(d[x]) for x in
+                                                                        ("q", "k", "v", "alpha", "b", "w")))
+            assert rel_err(sl(o), o_ref) <= TOL["bf16"]
+    Sh = host(S)
+    for (n, h) in sample:
+        es = rel_err(Sh[n:n + 1, h:h + 1], S_ref[(n, h)])
+        say(f"[decode] full-size (n={n},h={h}): err_S={es:.3e}")
+        assert es <= TOL["bf16"]
