@@ -20,8 +20,8 @@
  * Supported sizes: d_k, d_v in {16, 32, 64, 128} for the gated delta rule,
  * {16, 32, 64, 128, 256} for mLSTM; chunk in {16, 32, 64}; any T >= 1 (a
  * ragged last chunk behaves as if padded with identity steps alpha = 1, k = 0,
- * v = 0, whose outputs are discarded). With float32 inputs and d_k = 128 the
- * chunk must be at most 32.
+ * v = 0, whose outputs are discarded). With float32 inputs and d_k >= 64 the
+ * chunk must be at most 32 (fp32 operands take twice the LDS).
  * Alignment: every pointer must be 16-byte aligned.
  *
  * Preconditions not checked on the hot path: alpha in (0, 1]; inputs finite;

@@ -59,7 +59,7 @@ int gdr_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha
   int st = check_sizes(B, H, T, dk, dv, dtype, 128);
   if (st != GDR_OK) return st;
   if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
-  if (dtype == GDR_F32 && dk == 128 && chunk > 32) return GDR_ERR_UNSUPPORTED;
+  if (dtype == GDR_F32 && dk >= 64 && chunk > 32) return GDR_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, alpha, b, w, S0, o, S_out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GDR_ERR_ALIGN;

@@ -8,9 +8,9 @@
 //   O = Q_pi S0 + M V~,   S_C = Diag(pi_C) S0 + K~^T V~,
 // with k^ = b*k, v^ = w*v, pi_{t,s} = prod_{r=s+1..t} alpha_r, rows of K^_pi,
 // Q_pi are pi_t * k^_t, pi_t * q_t (pi_t = prod_{r<=t} alpha_r) and rows of K~
-// are pi_{C,s} * k_s. (§2.2 states T V~ = V^ - K^_pi S0; solving it with the
-// explicit T^{-1} applied to the VT value columns of this workgroup avoids the
-// d_k-wide Y = T^{-1} K^_pi of the page's fused solve.)
+// are pi_{C,s} * k_s. (§2.2 states T V~ = V^ - K^_pi S0; solving it on the VT
+// value columns of this workgroup avoids the d_k-wide Y = T^{-1} K^_pi of the
+// page's fused solve and never forms the off-diagonal blocks of T^{-1}.)
 //
 // Decays. The chunk is cut into 16-row blocks. Per block and channel the kernel
 // keeps the inclusive prefix product P_t (from the block start through t), the
@@ -31,10 +31,22 @@
 // acts on S from the left), so the tiles need no communication; each walks
 // all chunks of its head, holding its S tile (d_k x VT, fp32) in registers.
 //
-// Precision: operands of every contraction are bf16 in LDS with fp32
-// accumulation. For float32 inputs (SPLIT) every operand carries a second bf16
-// plane with the rounding residual and each product takes three MFMAs
-// (hi*hi + hi*lo + lo*hi). T^{-1} is always built from split operands.
+// Phases per chunk (4 waves, 7 workgroup barriers):
+//   prep 1  block totals G, v^ = w*v                          (all waves, VALU)
+//   prep 2  Kr = k^*P, Qr = q*P, Kc = k*Qs, K~^T, per-pair scale vectors
+//   Gram    L^T, M^T tiles = (Kc*D) [Kr; Qr]^T                (MFMA)
+//   write   L as fp32 16x16 blocks, M
+//   solve   wave 0: D_I = (I + L_II)^{-1} by forward substitution and
+//           L'_IJ = D_I L_IJ (MFMA); waves 1-3 meanwhile: R = V^ - Kr (B_I * S0)
+//           and O^T = (B_I * S0)^T Qr^T
+//   V~      block forward substitution, in place over R, one wave per value
+//           tile: V~_I = D_I R_I - sum_{J<I} L'_IJ V~_J (T V~ = R, block rows)
+//   end     O^T += V~^T M^T, store O; S <- Diag(pi_C) S + K~^T V~
+// The next chunk's inputs are fetched into registers during the current chunk.
+//
+// Precision: bf16 inputs use bf16 operands with fp32 accumulation, except
+// T^{-1}, which is built from hi/lo split operands (~16 bits). fp32 inputs use
+// fp32 operands and fp32 MFMA (16x16x4) throughout.
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
 
@@ -42,53 +54,84 @@ namespace gdr {
 
 constexpr float kGuardMin = 8.673617379884035e-19f;  // 2^-60
 
+constexpr int align16(int x) { return (x + 15) / 16 * 16; }
+constexpr int imax(int a, int b) { return a > b ? a : b; }
+
 template <int DK, int VT, int CM, bool SPLIT>
 struct ChunkSmem {
-  static constexpr int NS = SPLIT ? 2 : 1;
+  static constexpr int NS = SPLIT ? 2 : 1;           // bf16 planes' worth of bytes per operand element
   static constexpr int NBM = CM / 16;
-  static constexpr int LDK = DK + 8;   // bf16 pitch, rows of length DK
-  static constexpr int LDC = CM + 8;   // bf16 pitch, rows of length C
-  static constexpr int LDF = CM + 4;   // fp32 pitch, rows of length C
-  static constexpr int LDZ = 24;       // bf16 pitch of the 16x16 merge scratch
+  static constexpr int NPM = NBM * (NBM + 1) / 2;    // lower-triangular 16x16 block pairs
+  static constexpr int LDK = DK + 8;                 // pitch (elements), rows of length DK
+  static constexpr int LDC = CM + 8;                 // pitch (elements), rows of length C
+  static constexpr int LDF = CM + 4;                 // fp32 pitch of v^
+  static constexpr int LDB = 20;                     // fp32 pitch of a 16x16 block
   static constexpr int P_CK = CM * LDK * 2;
   static constexpr int P_CC = CM * LDC * 2;
   static constexpr int P_KC = DK * LDC * 2;
   static constexpr int P_VC = VT * LDC * 2;
   static constexpr int P_VK = VT * LDK * 2;
-  static constexpr int P_Z = 16 * LDZ * 2;
-  // region X, first use (prep -> Gram): row-block-relative operands
-  static constexpr int KR = 0;                       // k^ * P          [C][DK]
-  static constexpr int QR = KR + NS * P_CK;          // q * P           [C][DK]
-  static constexpr int KC = QR + NS * P_CK;          // k * Qs          [C][DK]
-  static constexpr int KHP = KC + NS * P_CK;         // -(k^ * pi_t)    [C][DK]
-  static constexpr int QHP = KHP + NS * P_CK;        // q * pi_t        [C][DK]
-  static constexpr int VH = QHP + NS * P_CK;         // v^ (fp32)       [VT][C]
-  static constexpr int X1_END = VH + VT * LDF * 4;
-  // region X, second use (after the Gram products)
-  static constexpr int LF = 0;                       // L (fp32)        [C][C]
-  static constexpr int LB = LF + CM * LDF * 4;       // L hi/lo         [C][C]
-  static constexpr int TN = LB + 2 * P_CC;           // T^-1 hi/lo      [t][s]
-  static constexpr int TT = TN + 2 * P_CC;           // T^-T hi/lo      [s][t]
-  static constexpr int ZT = TT + 2 * P_CC;           // 4 waves x 16x16 hi/lo
-  static constexpr int RT = ZT + 4 * 2 * P_Z;        // R^T             [VT][C]
-  static constexpr int X2_END = RT + NS * P_VC;
-  static constexpr int X_END = X1_END > X2_END ? X1_END : X2_END;
-  // persistent across the chunk
-  static constexpr int MB = (X_END + 15) / 16 * 16;  // M               [t][s]
-  static constexpr int KTT = MB + NS * P_CC;         // K~^T            [DK][C]
-  static constexpr int VTT = KTT + NS * P_KC;        // V~^T            [VT][C]
-  static constexpr int S0T = VTT + NS * P_VC;        // S0^T            [VT][DK]
-  static constexpr int GS = S0T + NS * P_VK;         // G (fp32)        [NB][DK]
-  static constexpr int PIC = GS + NBM * DK * 4;      // pi_C (fp32)     [DK]
-  static constexpr int FLAG = PIC + DK * 4;          // guard flags     [4]
+  static constexpr int BLK = 16 * LDB * 4;
+  static constexpr int KR = 0;                       // k^ * P   [C][DK]
+  static constexpr int QR = KR + NS * P_CK;          // q * P    [C][DK]
+  static constexpr int KC = QR + NS * P_CK;          // k * Qs   [C][DK]   (Gram only, then reused:)
+  static constexpr int LBK = KC;                     //   L blocks, fp32 [pair][t][s]
+  static constexpr int TBN = LBK + NPM * BLK;        //   D_I = (I + L_II)^-1, fp32 [I][t][s]
+  static constexpr int X_END = imax(KC + NS * P_CK, TBN + NBM * BLK);
+  static constexpr int VH = align16(X_END);          // v^ fp32   [VT][C]
+  static constexpr int TL = VH + VT * LDF * 4;       // [.. -L'_IJ .. | D_I] rows, T mode, [t][s]
+  static constexpr int VR = TL + 2 * P_CC;           // R, then V~ in place, T mode, [VT][C]
+  static constexpr int MB = VR + 2 * P_VC;           // M         [t][s]
+  static constexpr int KTT = MB + NS * P_CC;         // K~^T      [DK][C]
+  static constexpr int VTT = KTT + NS * P_KC;        // V~^T      [VT][C]
+  static constexpr int S0T = VTT + NS * P_VC;        // S0^T      [VT][DK]
+  static constexpr int SCL = S0T + NS * P_VK;        // Gram scale vectors fp32 [pair][DK]
+  static constexpr int GS = SCL + NPM * DK * 4;      // block totals G fp32 [NB][DK]
+  static constexpr int BS = GS + NBM * DK * 4;       // decay to block start fp32 [NB][DK]
+  static constexpr int PIC = BS + NBM * DK * 4;      // pi_C fp32 [DK]
+  static constexpr int FLAG = PIC + DK * 4;          // guard flags [4]
   static constexpr int TOTAL = FLAG + 16;
   static_assert(TOTAL <= 160 * 1024, "chunk kernel LDS exceeds 160 KiB");
 };
+
+__device__ __forceinline__ int pidx(int I, int J) { return I * (I + 1) / 2 + J; }
 
 __device__ __forceinline__ void pair_of(int p, int& I, int& J) {
   I = 0;
   while ((I + 1) * (I + 2) / 2 <= p) ++I;
   J = p - I * (I + 1) / 2;
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 8 consecutive fp32 values from LDS as an operand slice of the given mode.
+template <int MODE>
+__device__ __forceinline__ Frag<MODE> frag_f32(const float* p, bool valid) {
+  Frag<MODE> f;
+  f32x4 a = valid ? *(const f32x4*)p : f4zero();
+  f32x4 b = valid ? *(const f32x4*)(p + 4) : f4zero();
+  if constexpr (MODE == kF32) {
+    f.a = a;
+    f.b = b;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h, l;
+      split_bf(a[e], h, l);
+      f.hi[e] = h;
+      if constexpr (MODE == kSP) f.lo[e] = l;
+      split_bf(b[e], h, l);
+      f.hi[4 + e] = h;
+      if constexpr (MODE == kSP) f.lo[4 + e] = l;
+    }
+  }
+  return f;
 }
 
 // Exact in-block Gram entries for the tile (I, I) from alpha products (slow path).
@@ -125,31 +168,38 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
     const float* __restrict__ S0, Tin* __restrict__ o, float* S_out, int T, int DV, int C) {
   using L = ChunkSmem<DK, VT, CM, SPLIT>;
+  constexpr int MM = SPLIT ? kF32 : kBF;   // main operands
+  constexpr int MT = SPLIT ? kF32 : kSP;   // T^{-1} construction
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NVL = VT / 16;                       // 16-col value tiles per workgroup
   constexpr int NST = (DK / 16) * NVL;               // S accumulator tiles
   constexpr int MAXS = (NST + 3) / 4;
   constexpr int NBM = CM / 16;
-  constexpr int MAXP = (NBM * (NBM + 1) / 2 + 3) / 4;
+  constexpr int MAXP = (L::NPM + 3) / 4;             // Gram pairs per wave
+  constexpr int MAXJ = (NBM * NVL + 2) / 3;          // R/O jobs per wave (waves 1-3)
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int nvt = DV / VT;
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
   const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
-  const int NB = C / 16, NP = NB * (NB + 1) / 2;
+  const int NB = C / 16, NP = NB * (NB + 1) / 2, NJ = NB * NVL;
   const int nchunks = (T + C - 1) / C;
   const size_t seqK = (size_t)bh * T * DK;
   const size_t seqV = (size_t)bh * T * DV;
   const size_t stOff = (size_t)bh * DK * DV;
 
   float* GS = (float*)(smem + L::GS);
+  float* BS = (float*)(smem + L::BS);
+  float* SCL = (float*)(smem + L::SCL);
   float* PIC = (float*)(smem + L::PIC);
   int* FLAGS = (int*)(smem + L::FLAG);
   float* VH = (float*)(smem + L::VH);
-  float* LF = (float*)(smem + L::LF);
+  float* LBK = (float*)(smem + L::LBK);
+  float* TBN = (float*)(smem + L::TBN);
+  constexpr int BLKF = 16 * L::LDB;                  // floats per block
 
-  // ---- state tile -> registers and S0^T (bf16) in LDS
+  // ---- state tile -> registers and S0^T in LDS
   f32x4 Sacc[MAXS];
 #pragma unroll
   for (int i = 0; i < MAXS; ++i) {
@@ -162,70 +212,98 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
         for (int e = 0; e < 4; ++e)
           Sacc[i][e] = S0[stOff + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16];
       }
-      st4<SPLIT>(smem + L::S0T, L::P_VK, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+      st4<MM>(smem + L::S0T, L::P_VK, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
     }
   }
   if (tid < 4) FLAGS[tid] = 0;
   __syncthreads();
 
-  f32x4 Oacc[NVL];
+  f32x4 Oacc[MAXJ];
+
+  // ---- input staging. Thread (I0, j) owns channels j, j+1 of 16-row block I0;
+  // the v^ item of a thread is 8 consecutive value columns of one row. Loads
+  // are branch-free (row clamped into range, padding selected afterwards).
+  // bf16 inputs: the next chunk's words are fetched while this chunk computes.
+  using RW = Raw<Tin>;
+  constexpr bool PF = !SPLIT;
+  const int items = NB * (DK / 2);
+  const bool act = tid < items;
+  const int I0 = act ? tid / (DK / 2) : 0, j = act ? 2 * (tid % (DK / 2)) : 0;
+  const int nvi = C * (VT / 8);
+  const bool vact = tid < nvi;
+  const int vrow = vact ? tid / (VT / 8) : 0, vcol = vact ? (tid % (VT / 8)) * 8 : 0;
+  typename RW::R2 ca[16], ck[16], cb[16], cq[16];
+  typename RW::R2 na[16], nk[16], nb[16], nq[16];
+  typename RW::R8 cv, cw, nv, nw;
+  auto issue = [&](int chk, typename RW::R2* xa, typename RW::R2* xk, typename RW::R2* xb,
+                   typename RW::R2* xq, typename RW::R8& xv, typename RW::R8& xw) {
+    const int tb = chk * C;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = tb + 16 * I0 + r;
+      const size_t off = seqK + (size_t)(t < T ? t : T - 1) * DK + j;
+      xa[r] = RW::ld2(alpha + off);
+      xk[r] = RW::ld2(k + off);
+      xb[r] = RW::ld2(bgate + off);
+      xq[r] = RW::ld2(q + off);
+    }
+    const int tv = tb + vrow;
+    const size_t offv = seqV + (size_t)(tv < T ? tv : T - 1) * DV + vt0 + vcol;
+    xv = RW::ld8(v + offv);
+    xw = RW::ld8(wgate + offv);
+  };
+  if (PF) issue(0, na, nk, nb, nq, nv, nw);
 
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * C;
-
-    // ================= prep, pass 1: block prefix products and block totals
-    const int items = NB * (DK / 2);
-    const bool act = tid < items;
-    const int I0 = tid / (DK / 2), j = 2 * (tid % (DK / 2));
-    float2 ra[16], rk[16], rb[16], rq[16], P[16];
-    if (act) {
+    if constexpr (PF) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { ca[r] = na[r]; ck[r] = nk[r]; cb[r] = nb[r]; cq[r] = nq[r]; }
+      cv = nv;
+      cw = nw;
+      if (ch + 1 < nchunks) issue(ch + 1, na, nk, nb, nq, nv, nw);
+    } else {
+      issue(ch, ca, ck, cb, cq, cv, cw);
+    }
+    // identity padding past the end of the sequence: alpha = 1, k = b = q = 0, v = w = 0
+    {
+      const typename RW::R2 one = RW::pad2(1.f), zero = RW::pad2(0.f);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 16 * I0 + r;
-        if (t < T) {
-          const size_t off = seqK + (size_t)t * DK + j;
-          ra[r] = In<Tin>::load2(alpha + off);
-          rk[r] = In<Tin>::load2(k + off);
-          rb[r] = In<Tin>::load2(bgate + off);
-          rq[r] = In<Tin>::load2(q + off);
-        } else {  // identity padding past the end of the sequence
-          ra[r] = make_float2(1.f, 1.f);
-          rk[r] = rb[r] = rq[r] = make_float2(0.f, 0.f);
-        }
+        const bool ok = t0 + 16 * I0 + r < T;
+        ca[r] = RW::sel(ok, ca[r], one);
+        ck[r] = RW::sel(ok, ck[r], zero);
+        cb[r] = RW::sel(ok, cb[r], zero);
+        cq[r] = RW::sel(ok, cq[r], zero);
       }
+      const bool okv = t0 + vrow < T;
+      cv = RW::sel(okv, cv, RW::zero8());
+      cw = RW::sel(okv, cw, RW::zero8());
+    }
+
+    // ================= prep 1: block totals G, v^
+    if (act) {
       float2 p = make_float2(1.f, 1.f);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p.x *= ra[r].x;
-        p.y *= ra[r].y;
-        P[r] = p;
+        const float2 a = RW::un2(ca[r]);
+        p.x *= a.x;
+        p.y *= a.y;
       }
       GS[I0 * DK + j] = p.x;
       GS[I0 * DK + j + 1] = p.y;
       if (!(p.x >= kGuardMin && p.y >= kGuardMin)) FLAGS[I0] = 1;
     }
-    // v^ = w * v into VH[v][t] (fp32)
-    {
-      const int nvi = C * (VT / 8);
-      for (int it = tid; it < nvi; it += 256) {
-        const int t = it / (VT / 8), vv = (it % (VT / 8)) * 8;
-        const int tg = t0 + t;
+    if (vact) {
+      float fv[8], fw[8];
+      RW::un8(cv, fv);
+      RW::un8(cw, fw);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float2 vv2 = make_float2(0.f, 0.f), ww2 = make_float2(0.f, 0.f);
-          if (tg < T) {
-            const size_t off = seqV + (size_t)tg * DV + vt0 + vv + e;
-            vv2 = In<Tin>::load2(v + off);
-            ww2 = In<Tin>::load2(wgate + off);
-          }
-          VH[(vv + e) * L::LDF + t] = vv2.x * ww2.x;
-          VH[(vv + e + 1) * L::LDF + t] = vv2.y * ww2.y;
-        }
-      }
+      for (int e = 0; e < 8; ++e) VH[(vcol + e) * L::LDF + vrow] = fv[e] * fw[e];
     }
     __syncthreads();
 
-    // ================= prep, pass 2: scaled operands
+    // ================= prep 2: scaled operands and per-pair scale vectors
     if (act) {
       float2 Bst = make_float2(1.f, 1.f), E = make_float2(1.f, 1.f), pic = make_float2(1.f, 1.f);
       for (int J = 0; J < NB; ++J) {
@@ -235,40 +313,56 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
         pic.x *= gx; pic.y *= gy;
       }
       if (I0 == 0) { PIC[j] = pic.x; PIC[j + 1] = pic.y; }
+      BS[I0 * DK + j] = Bst.x;
+      BS[I0 * DK + j + 1] = Bst.y;
+      // scale of pair (I0, J): 1/G_I0 on the diagonal (in-block ratio), the
+      // product of the block totals strictly between J and I0 below it
+      {
+        const float gx = GS[I0 * DK + j], gy = GS[I0 * DK + j + 1];
+        SCL[pidx(I0, I0) * DK + j] = __builtin_amdgcn_rcpf(gx);
+        SCL[pidx(I0, I0) * DK + j + 1] = __builtin_amdgcn_rcpf(gy);
+        float2 d = make_float2(1.f, 1.f);
+        for (int J = I0 - 1; J >= 0; --J) {
+          SCL[pidx(I0, J) * DK + j] = d.x;
+          SCL[pidx(I0, J) * DK + j + 1] = d.y;
+          d.x *= GS[J * DK + j];
+          d.y *= GS[J * DK + j + 1];
+        }
+      }
+      float2 P = make_float2(1.f, 1.f);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tl = 16 * I0 + r;
-        const float khx = rb[r].x * rk[r].x, khy = rb[r].y * rk[r].y;
-        const float krx = khx * P[r].x, kry = khy * P[r].y;
-        const float qrx = rq[r].x * P[r].x, qry = rq[r].y * P[r].y;
+        const float2 a = RW::un2(ca[r]), kk = RW::un2(ck[r]), bb = RW::un2(cb[r]), qq = RW::un2(cq[r]);
+        P.x *= a.x;
+        P.y *= a.y;
         const int off = tl * L::LDK + j;
-        st2<SPLIT>(smem + L::KR, L::P_CK, off, krx, kry);
-        st2<SPLIT>(smem + L::QR, L::P_CK, off, qrx, qry);
-        st2<SPLIT>(smem + L::KHP, L::P_CK, off, -krx * Bst.x, -kry * Bst.y);
-        st2<SPLIT>(smem + L::QHP, L::P_CK, off, qrx * Bst.x, qry * Bst.y);
+        st2<MM>(smem + L::KR, L::P_CK, off, bb.x * kk.x * P.x, bb.y * kk.y * P.y);
+        st2<MM>(smem + L::QR, L::P_CK, off, qq.x * P.x, qq.y * P.y);
       }
       float ktx[16], kty[16];
       float2 qs = make_float2(1.f, 1.f);
 #pragma unroll
       for (int r = 15; r >= 0; --r) {
-        const float kcx = rk[r].x * qs.x, kcy = rk[r].y * qs.y;
-        st2<SPLIT>(smem + L::KC, L::P_CK, (16 * I0 + r) * L::LDK + j, kcx, kcy);
+        const float2 kk = RW::un2(ck[r]), a = RW::un2(ca[r]);
+        const float kcx = kk.x * qs.x, kcy = kk.y * qs.y;
+        st2<MM>(smem + L::KC, L::P_CK, (16 * I0 + r) * L::LDK + j, kcx, kcy);
         ktx[r] = kcx * E.x;
         kty[r] = kcy * E.y;
-        qs.x *= ra[r].x;
-        qs.y *= ra[r].y;
+        qs.x *= a.x;
+        qs.y *= a.y;
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        st4<SPLIT>(smem + L::KTT, L::P_KC, j * L::LDC + 16 * I0 + 4 * r4,
-                   f32x4{ktx[4 * r4], ktx[4 * r4 + 1], ktx[4 * r4 + 2], ktx[4 * r4 + 3]});
-        st4<SPLIT>(smem + L::KTT, L::P_KC, (j + 1) * L::LDC + 16 * I0 + 4 * r4,
-                   f32x4{kty[4 * r4], kty[4 * r4 + 1], kty[4 * r4 + 2], kty[4 * r4 + 3]});
+        st4<MM>(smem + L::KTT, L::P_KC, j * L::LDC + 16 * I0 + 4 * r4,
+                f32x4{ktx[4 * r4], ktx[4 * r4 + 1], ktx[4 * r4 + 2], ktx[4 * r4 + 3]});
+        st4<MM>(smem + L::KTT, L::P_KC, (j + 1) * L::LDC + 16 * I0 + 4 * r4,
+                f32x4{kty[4 * r4], kty[4 * r4 + 1], kty[4 * r4 + 2], kty[4 * r4 + 3]});
       }
     }
     __syncthreads();
 
-    // ================= Gram tiles, R = V^ - K^_pi S0, O^T = S0^T Q_pi^T
+    // ================= Gram tiles: L^T, M^T of pair (I, J) = (Kc_J * scale) [Kr_I; Qr_I]^T
     f32x4 gL[MAXP], gM[MAXP];
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
@@ -281,48 +375,24 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
         const bool scaled = (I == J) || (I > J + 1);
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::KC, L::P_CK, L::LDK, 16 * J, k0, DK, lane);
+          Frag<MM> A = ldfrag<MM>(smem + L::KC, L::P_CK, L::LDK, 16 * J, k0, DK, lane);
           const int kk = k0 + 8 * g;
           if (scaled && kk < DK) {
-            float s[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (I == J) {
-                s[e] = 1.f / GS[I * DK + kk + e];
-              } else {
-                float d = 1.f;
-                for (int K = J + 1; K < I; ++K) d *= GS[K * DK + kk + e];
-                s[e] = d;
-              }
-            }
-            scale_frag<SPLIT>(A, s);
+            const float* sp = SCL + p * DK + kk;
+            const f32x4 s0 = *(const f32x4*)sp, s1 = *(const f32x4*)(sp + 4);
+            const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            scale_frag<MM>(A, sv);
           }
-          Frag<SPLIT> BL = ldfrag<SPLIT>(smem + L::KR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
-          Frag<SPLIT> BM = ldfrag<SPLIT>(smem + L::QR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
-          mma<SPLIT>(gL[i], A, BL);
-          mma<SPLIT>(gM[i], A, BM);
-        }
-      }
-    }
-    f32x4 Racc[NVL];
-    if (wid < NB) {
-#pragma unroll
-      for (int vl = 0; vl < NVL; ++vl) {
-        Racc[vl] = *(const f32x4*)(VH + (16 * vl + c16) * L::LDF + 16 * wid + 4 * g);
-        Oacc[vl] = f4zero();
-#pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += 32) {
-          Frag<SPLIT> Kp = ldfrag<SPLIT>(smem + L::KHP, L::P_CK, L::LDK, 16 * wid, k0, DK, lane);
-          Frag<SPLIT> St = ldfrag<SPLIT>(smem + L::S0T, L::P_VK, L::LDK, 16 * vl, k0, DK, lane);
-          Frag<SPLIT> Qp = ldfrag<SPLIT>(smem + L::QHP, L::P_CK, L::LDK, 16 * wid, k0, DK, lane);
-          mma<SPLIT>(Racc[vl], Kp, St);
-          mma<SPLIT>(Oacc[vl], St, Qp);
+          Frag<MM> BL = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+          Frag<MM> BM = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+          mma<MM>(gL[i], A, BL);
+          mma<MM>(gM[i], A, BM);
         }
       }
     }
     __syncthreads();
 
-    // ================= write L (fp32 + hi/lo), M, R^T into the reused region
+    // ================= write L (fp32 blocks) and M
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
       const int p = wid + 4 * i;
@@ -339,97 +409,124 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
             if (s0 + e > t) mv[e] = 0.f;
           }
         }
-        *(f32x4*)(LF + t * L::LDF + s0) = lv;
-        st4<true>(smem + L::LB, L::P_CC, t * L::LDC + s0, lv);
-        st4<SPLIT>(smem + L::MB, L::P_CC, t * L::LDC + s0, mv);
+        *(f32x4*)(LBK + p * BLKF + c16 * L::LDB + 4 * g) = lv;
+        st4<MM>(smem + L::MB, L::P_CC, t * L::LDC + s0, mv);
       }
-    }
-    if (wid < NB) {
-#pragma unroll
-      for (int vl = 0; vl < NVL; ++vl)
-        st4<SPLIT>(smem + L::RT, L::P_VC, (16 * vl + c16) * L::LDC + 16 * wid + 4 * g, Racc[vl]);
     }
     __syncthreads();
 
-    // ================= T^{-1}: diagonal 16x16 blocks by forward substitution (fp32)
-    if (wid == 0 && g < NB) {
-      const int I = g, cc = c16;
-      float x[16];
+    if (wid == 0) {
+      // ============= D_I = (I + L_II)^{-1}: forward substitution, lane = (block g, column c16)
+      if (tid < 4) FLAGS[tid] = 0;  // last read above; set again by the next chunk's prep 1
+      {
+        const int I = g, cc = c16;
+        const bool live = I < NB;
+        const int pd = live ? pidx(I, I) : 0;
+        const float* Lb = LBK + pd * BLKF;
+        float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float* Lrow = LF + (16 * I + r) * L::LDF + 16 * I;
-        float acc = (r == cc) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < r; ++m) acc -= Lrow[m] * x[m];
-        x[r] = acc;
-      }
+        for (int m = 0; m < 16; ++m) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st1<true>(smem + L::TN, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        st4<true>(smem + L::TT, L::P_CC, (16 * I + cc) * L::LDC + 16 * I + 4 * r4,
-                  f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]});
-    }
-    if (tid < 4) FLAGS[tid] = 0;  // last read above; set again in the next chunk's pass 1
-    __syncthreads();
-
-    // ================= T^{-1}: off-diagonal blocks, X_IJ = -D_I sum_{J<=K<I} L_IK X_KJ
-    for (int d = 1; d < NB; ++d) {
-      const int J = wid, I = J + d;
-      const bool mact = I < NB;
-      char* zt = smem + L::ZT + wid * 2 * L::P_Z;
-      if (mact) {
-        f32x4 z = f4zero();
-        for (int k0 = 16 * J; k0 < 16 * I; k0 += 32) {
-          Frag<true> A = ldfrag<true>(smem + L::LB, L::P_CC, L::LDC, 16 * I, k0, 16 * I, lane);
-          Frag<true> B = ldfrag<true>(smem + L::TT, L::P_CC, L::LDC, 16 * J, k0, 16 * I, lane);
-          mma<true>(z, A, B);
+          for (int r = m + 1; r < 16; ++r) x[r] -= Lb[r * L::LDB + m] * x[m];
         }
-        st4<true>(zt, L::P_Z, c16 * L::LDZ + 4 * g, z);
+        if (live) {
+          float* Tn = TBN + I * BLKF;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            Tn[r * L::LDB + cc] = x[r];
+            st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
+          }
+        }
       }
-      __syncthreads();
-      if (mact) {
-        f32x4 x = f4zero();
-        Frag<true> A = ldfrag<true>(smem + L::TN, L::P_CC, L::LDC, 16 * I, 16 * I, 16 * I + 16, lane);
-        Frag<true> B = ldfrag<true>(zt, L::P_Z, L::LDZ, 0, 0, 16, lane);
-        mma<true>(x, A, B);
-        x = -x;
-        st4<true>(smem + L::TT, L::P_CC, (16 * J + c16) * L::LDC + 16 * I + 4 * g, x);
+      wave_lds_sync();
+      // ============= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL
+      for (int p = 0; p < NP; ++p) {
+        int I, J;
+        pair_of(p, I, J);
+        if (I == J) continue;
+        const bool ok = g < 2;  // k = m spans one 16-row block
+        Frag<MT> A = frag_f32<MT>(TBN + I * BLKF + c16 * L::LDB + 8 * (g & 1), ok);
+        // B[k = m][n = s] = L_IJ[m][s]: gather the column s of the fp32 block
+        float lc[8];
+        const float* lb = LBK + p * BLKF + c16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lc[e] = ok ? lb[(8 * (g & 1) + e) * L::LDB] : 0.f;
+        Frag<MT> B = frag_f32<MT>(lc, true);
+        f32x4 acc = f4zero();
+        mma<MT>(acc, A, B);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          st1<true>(smem + L::TN, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, x[e]);
+          st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
       }
-      __syncthreads();
-    }
-
-    // ================= V~ = T^{-1} R
-    if (wid < NB) {
-      const int I = wid, kend = 16 * (I + 1);
+    } else {
+      // ============= waves 1-3: R = V^ - Kr (B_I * S0) and O^T = (B_I * S0)^T Qr^T
 #pragma unroll
-      for (int vl = 0; vl < NVL; ++vl) {
+      for (int i = 0; i < MAXJ; ++i) {
+        const int job = (wid - 1) + 3 * i;
+        if (job < NJ) {
+          const int I = job / NVL, vl = job % NVL;
+          f32x4 r = f4zero();
+          Oacc[i] = f4zero();
+#pragma unroll
+          for (int k0 = 0; k0 < DK; k0 += 32) {
+            Frag<MM> Sf = ldfrag<MM>(smem + L::S0T, L::P_VK, L::LDK, 16 * vl, k0, DK, lane);
+            const int kk = k0 + 8 * g;
+            if (I > 0 && kk < DK) {
+              const float* bp = BS + I * DK + kk;
+              const f32x4 b0 = *(const f32x4*)bp, b1 = *(const f32x4*)(bp + 4);
+              const float sv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+              scale_frag<MM>(Sf, sv);
+            }
+            Frag<MM> Kf = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+            Frag<MM> Qf = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+            mma<MM>(r, Kf, Sf);
+            mma<MM>(Oacc[i], Sf, Qf);
+          }
+          const f32x4 vh = *(const f32x4*)(VH + (16 * vl + c16) * L::LDF + 16 * I + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = vh[e] - r[e];
+          st4<MT>(smem + L::VR, L::P_VC, (16 * vl + c16) * L::LDC + 16 * I + 4 * g, r);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ================= V~: block forward substitution in place over R (one wave per value tile)
+    if (wid < NVL) {
+      const int vl = wid;
+      for (int I = 0; I < NB; ++I) {
+        const int kend = 16 * (I + 1);
         f32x4 acc = f4zero();
         for (int k0 = 0; k0 < kend; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::TN, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::RT, L::P_VC, L::LDC, 16 * vl, k0, kend, lane);
-          mma<SPLIT>(acc, A, B);
+          Frag<MT> A = ldfrag<MT>(smem + L::TL, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
+          Frag<MT> B = ldfrag<MT>(smem + L::VR, L::P_VC, L::LDC, 16 * vl, k0, kend, lane);
+          mma<MT>(acc, A, B);
         }
-        st4<SPLIT>(smem + L::VTT, L::P_VC, (16 * vl + c16) * L::LDC + 16 * I + 4 * g, acc);
+        const int off = (16 * vl + c16) * L::LDC + 16 * I + 4 * g;
+        st4<MT>(smem + L::VR, L::P_VC, off, acc);
+        st4<MM>(smem + L::VTT, L::P_VC, off, acc);
+        wave_lds_sync();
       }
     }
     __syncthreads();
 
-    // ================= O^T += V~^T M^T, store O; S <- Diag(pi_C) S + K~^T V~
-    if (wid < NB) {
-      const int I = wid, kend = 16 * (I + 1);
+    // ================= O^T += V~^T M^T and store O; S <- Diag(pi_C) S + K~^T V~
+    if (wid > 0) {
 #pragma unroll
-      for (int vl = 0; vl < NVL; ++vl) {
-        for (int k0 = 0; k0 < kend; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::VTT, L::P_VC, L::LDC, 16 * vl, k0, kend, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::MB, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
-          mma<SPLIT>(Oacc[vl], A, B);
+      for (int i = 0; i < MAXJ; ++i) {
+        const int job = (wid - 1) + 3 * i;
+        if (job < NJ) {
+          const int I = job / NVL, vl = job % NVL, kend = 16 * (I + 1);
+          for (int k0 = 0; k0 < kend; k0 += 32) {
+            Frag<MM> A = ldfrag<MM>(smem + L::VTT, L::P_VC, L::LDC, 16 * vl, k0, kend, lane);
+            Frag<MM> B = ldfrag<MM>(smem + L::MB, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
+            mma<MM>(Oacc[i], A, B);
+          }
+          const int t = t0 + 16 * I + c16;
+          if (t < T) In<Tin>::store4(o + seqV + (size_t)t * DV + vt0 + 16 * vl + 4 * g, Oacc[i]);
         }
-        const int t = t0 + 16 * I + c16;
-        if (t < T) In<Tin>::store4(o + seqV + (size_t)t * DV + vt0 + 16 * vl + 4 * g, Oacc[vl]);
       }
     }
 #pragma unroll
@@ -437,12 +534,13 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
       const int tile = wid + 4 * i;
       if (tile < NST) {
         const int jt = tile / NVL, vl = tile % NVL;
+        const f32x4 pc = *(const f32x4*)(PIC + 16 * jt + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sacc[i][e] *= PIC[16 * jt + 4 * g + e];
+        for (int e = 0; e < 4; ++e) Sacc[i][e] *= pc[e];
         for (int k0 = 0; k0 < C; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::KTT, L::P_KC, L::LDC, 16 * jt, k0, C, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::VTT, L::P_VC, L::LDC, 16 * vl, k0, C, lane);
-          mma<SPLIT>(Sacc[i], A, B);
+          Frag<MM> A = ldfrag<MM>(smem + L::KTT, L::P_KC, L::LDC, 16 * jt, k0, C, lane);
+          Frag<MM> B = ldfrag<MM>(smem + L::VTT, L::P_VC, L::LDC, 16 * vl, k0, C, lane);
+          mma<MM>(Sacc[i], A, B);
         }
       }
     }
@@ -452,7 +550,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
       const int tile = wid + 4 * i;
       if (tile < NST) {
         const int jt = tile / NVL, vl = tile % NVL;
-        st4<SPLIT>(smem + L::S0T, L::P_VK, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+        st4<MM>(smem + L::S0T, L::P_VK, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
       }
     }
   }
@@ -497,39 +595,33 @@ static int launch_chunk(const ChunkArgs& a) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
-template <typename Tin, int CM_SPLIT128>
-static int dispatch_dk(const ChunkArgs& a, int VT) {
-  constexpr bool SPLIT = std::is_same<Tin, float>::value;
-  if constexpr (SPLIT) {
-    switch (a.dk) {
-      case 16: return launch_chunk<Tin, 16, 16, 64>(a);
-      case 32: return launch_chunk<Tin, 32, 16, 64>(a);
-      case 64: return launch_chunk<Tin, 64, 16, 64>(a);
-      case 128: return launch_chunk<Tin, 128, 16, CM_SPLIT128>(a);
-    }
-  } else {
-    if (VT == 16) {
+int chunk_fwd_launch(const ChunkArgs& a) {
+  if (a.dtype == GDR_BF16) {
+    if (a.dv == 16) {
       switch (a.dk) {
-        case 16: return launch_chunk<Tin, 16, 16, 64>(a);
-        case 32: return launch_chunk<Tin, 32, 16, 64>(a);
-        case 64: return launch_chunk<Tin, 64, 16, 64>(a);
-        case 128: return launch_chunk<Tin, 128, 16, 64>(a);
+        case 16: return launch_chunk<__bf16, 16, 16, 64>(a);
+        case 32: return launch_chunk<__bf16, 32, 16, 64>(a);
+        case 64: return launch_chunk<__bf16, 64, 16, 64>(a);
+        case 128: return launch_chunk<__bf16, 128, 16, 64>(a);
       }
     } else {
       switch (a.dk) {
-        case 16: return launch_chunk<Tin, 16, 32, 64>(a);
-        case 32: return launch_chunk<Tin, 32, 32, 64>(a);
-        case 64: return launch_chunk<Tin, 64, 32, 64>(a);
-        case 128: return launch_chunk<Tin, 128, 32, 64>(a);
+        case 16: return launch_chunk<__bf16, 16, 32, 64>(a);
+        case 32: return launch_chunk<__bf16, 32, 32, 64>(a);
+        case 64: return launch_chunk<__bf16, 64, 32, 64>(a);
+        case 128: return launch_chunk<__bf16, 128, 32, 64>(a);
       }
+    }
+  } else {
+    // fp32 operands take twice the LDS: chunks of at most 32 rows for d_k >= 64
+    switch (a.dk) {
+      case 16: return launch_chunk<float, 16, 16, 64>(a);
+      case 32: return launch_chunk<float, 32, 16, 64>(a);
+      case 64: return launch_chunk<float, 64, 16, 32>(a);
+      case 128: return launch_chunk<float, 128, 16, 32>(a);
     }
   }
   return GDR_ERR_UNSUPPORTED;
-}
-
-int chunk_fwd_launch(const ChunkArgs& a) {
-  if (a.dtype == GDR_BF16) return dispatch_dk<__bf16, 32>(a, a.dv == 16 ? 16 : 32);
-  return dispatch_dk<float, 32>(a, 16);
 }
 
 }  // namespace gdr

@@ -58,97 +58,211 @@ template <> struct In<__bf16> {
   static __device__ __forceinline__ void store1(__bf16* p, float v) { *p = (__bf16)v; }
 };
 
-// One MFMA operand fragment: 8 bf16 (hi) and, for split precision, 8 more (lo).
-template <bool SPLIT> struct Frag {
-  bf16x8 hi;
-  bf16x8 lo;
+// Raw (undecoded) input words, so loads can be issued early and decoded late.
+// R2 holds two consecutive elements, R8 eight. Loads are unconditional: callers
+// clamp the row index into range and replace out-of-range rows afterwards with
+// `sel`, which keeps the loads branch-free so they issue back to back.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+template <typename T> struct Raw;
+template <> struct Raw<__bf16> {
+  typedef uint32_t R2;
+  typedef u32x4 R8;
+  static __device__ __forceinline__ R2 ld2(const __bf16* p) { return *(const uint32_t*)p; }
+  static __device__ __forceinline__ R8 ld8(const __bf16* p) { return *(const u32x4*)p; }
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  static __device__ __forceinline__ float2 un2(R2 r) { return make_float2(lo(r), hi(r)); }
+  static __device__ __forceinline__ void un8(const R8& r, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = lo(r[i]); o[2 * i + 1] = hi(r[i]); }
+  }
+  static __device__ __forceinline__ R2 pad2(float x) {  // both halves = bf16(x), x exact in bf16
+    const uint32_t h = __float_as_uint(x) >> 16;
+    return h | (h << 16);
+  }
+  static __device__ __forceinline__ R2 sel(bool ok, R2 r, R2 p) { return ok ? r : p; }
+  static __device__ __forceinline__ R8 zero8() { return u32x4{0u, 0u, 0u, 0u}; }
+  static __device__ __forceinline__ R8 sel(bool ok, const R8& r, const R8& p) {
+    return u32x4{ok ? r[0] : p[0], ok ? r[1] : p[1], ok ? r[2] : p[2], ok ? r[3] : p[3]};
+  }
 };
+template <> struct Raw<float> {
+  typedef float2 R2;
+  struct R8 { f32x4 a, b; };
+  static __device__ __forceinline__ R2 ld2(const float* p) { return *(const float2*)p; }
+  static __device__ __forceinline__ R8 ld8(const float* p) {
+    R8 r;
+    r.a = *(const f32x4*)p;
+    r.b = *(const f32x4*)(p + 4);
+    return r;
+  }
+  static __device__ __forceinline__ float2 un2(R2 r) { return r; }
+  static __device__ __forceinline__ void un8(const R8& r, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[i] = r.a[i]; o[4 + i] = r.b[i]; }
+  }
+  static __device__ __forceinline__ R2 pad2(float x) { return make_float2(x, x); }
+  static __device__ __forceinline__ R2 sel(bool ok, R2 r, R2 p) {
+    return make_float2(ok ? r.x : p.x, ok ? r.y : p.y);
+  }
+  static __device__ __forceinline__ R8 zero8() { return R8{f4zero(), f4zero()}; }
+  static __device__ __forceinline__ R8 sel(bool ok, const R8& r, const R8& p) {
+    R8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o.a[i] = ok ? r.a[i] : p.a[i]; o.b[i] = ok ? r.b[i] : p.b[i]; }
+    return o;
+  }
+};
+
+// Operand precision modes of the contractions. Every LDS operand matrix is
+// k-contiguous ([row][k]) and occupies two bf16 "planes" worth of bytes when
+// its mode needs them:
+//   kBF  — one bf16 plane; 1 MFMA 16x16x32 bf16 per 32-k step.
+//   kSP  — bf16 hi plane + bf16 lo plane (x ~ hi + lo, ~16 mantissa bits);
+//          3 MFMAs (hi*hi + hi*lo + lo*hi) per step.
+//   kF32 — one fp32 plane (the same bytes as hi + lo); 8 MFMAs 16x16x4 fp32
+//          per 32-k step, i.e. fp32 products with fp32 accumulation.
+// In kF32 the element offset and row pitch are counted in fp32 elements.
+constexpr int kBF = 0, kSP = 1, kF32 = 2;
+
+template <int MODE> struct Frag;
+template <> struct Frag<kBF> { bf16x8 hi; };
+template <> struct Frag<kSP> { bf16x8 hi, lo; };
+template <> struct Frag<kF32> { f32x4 a, b; };
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
-// acc += A * B with 1 MFMA (hi*hi) or 3 MFMAs (hi*hi + hi*lo + lo*hi).
-template <bool SPLIT>
-__device__ __forceinline__ void mma(f32x4& acc, const Frag<SPLIT>& a, const Frag<SPLIT>& b) {
-  acc = mfma_bf16(a.hi, b.hi, acc);
-  if constexpr (SPLIT) {
+// acc += A * B over one 32-wide k step.
+template <int MODE>
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<MODE>& a, const Frag<MODE>& b) {
+  if constexpr (MODE == kBF) {
+    acc = mfma_bf16(a.hi, b.hi, acc);
+  } else if constexpr (MODE == kSP) {
+    acc = mfma_bf16(a.hi, b.hi, acc);
     acc = mfma_bf16(a.hi, b.lo, acc);
     acc = mfma_bf16(a.lo, b.hi, acc);
+  } else {
+    // instruction e takes k = k0 + 8*(lane/16) + e: lane group g supplies the
+    // instruction's k index g, so the 8 instructions cover the 32 k once.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_f32(a.a[e], b.a[e], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_f32(a.b[e], b.b[e], acc);
   }
 }
 
 // Load this lane's 8-element slice of a 16-row fragment from a k-contiguous
 // LDS matrix: rows row0 + (lane % 16), k = k0 + 8*(lane/16) .. +7.
 // Slices at or beyond kend are returned as zeros (tiles are 16-aligned, so a
-// slice is either wholly valid or wholly past the end). The lo plane, when
-// present, sits `plane` bytes after the hi plane.
-template <bool SPLIT>
-__device__ __forceinline__ Frag<SPLIT> ldfrag(const char* base, int plane, int ld, int row0, int k0,
-                                              int kend, int lane) {
-  Frag<SPLIT> f;
+// slice is either wholly valid or wholly past the end). The lo plane (kSP)
+// sits `plane` bytes after the hi plane.
+template <int MODE>
+__device__ __forceinline__ Frag<MODE> ldfrag(const char* base, int plane, int ld, int row0, int k0,
+                                             int kend, int lane) {
+  Frag<MODE> f;
   const int k = k0 + 8 * (lane >> 4);
-  if (k < kend) {
-    const __bf16* p = (const __bf16*)base + (row0 + (lane & 15)) * ld + k;
-    f.hi = *(const bf16x8*)p;
-    if constexpr (SPLIT) f.lo = *(const bf16x8*)((const char*)p + plane);
+  const int off = (row0 + (lane & 15)) * ld + k;
+  if constexpr (MODE == kF32) {
+    if (k < kend) {
+      const float* p = (const float*)base + off;
+      f.a = *(const f32x4*)p;
+      f.b = *(const f32x4*)(p + 4);
+    } else {
+      f.a = f4zero();
+      f.b = f4zero();
+    }
   } else {
-    f.hi = bf16x8{};
-    if constexpr (SPLIT) f.lo = bf16x8{};
+    if (k < kend) {
+      const __bf16* p = (const __bf16*)base + off;
+      f.hi = *(const bf16x8*)p;
+      if constexpr (MODE == kSP) f.lo = *(const bf16x8*)((const char*)p + plane);
+    } else {
+      f.hi = bf16x8{};
+      if constexpr (MODE == kSP) f.lo = bf16x8{};
+    }
   }
   return f;
 }
 
-// Store 4 consecutive values (k-contiguous) as bf16 hi [+ lo] planes.
-template <bool SPLIT>
-__device__ __forceinline__ void st4(char* base, int plane, int off_elems, f32x4 v) {
-  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-  bf16x4 h, l;
-  __bf16 t0, t1, t2, t3, u0, u1, u2, u3;
-  split_bf(v.x, t0, u0); split_bf(v.y, t1, u1); split_bf(v.z, t2, u2); split_bf(v.w, t3, u3);
-  h.x = t0; h.y = t1; h.z = t2; h.w = t3;
-  *(bf16x4*)((__bf16*)base + off_elems) = h;
-  if constexpr (SPLIT) {
-    l.x = u0; l.y = u1; l.z = u2; l.w = u3;
-    *(bf16x4*)((char*)((__bf16*)base + off_elems) + plane) = l;
+// Stores of 4 / 2 / 1 consecutive values in the array's mode.
+template <int MODE>
+__device__ __forceinline__ void st4(char* base, int plane, int off, f32x4 v) {
+  if constexpr (MODE == kF32) {
+    *(f32x4*)((float*)base + off) = v;
+  } else {
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+    bf16x4 h, l;
+    __bf16 t0, t1, t2, t3, u0, u1, u2, u3;
+    split_bf(v.x, t0, u0); split_bf(v.y, t1, u1); split_bf(v.z, t2, u2); split_bf(v.w, t3, u3);
+    h.x = t0; h.y = t1; h.z = t2; h.w = t3;
+    *(bf16x4*)((__bf16*)base + off) = h;
+    if constexpr (MODE == kSP) {
+      l.x = u0; l.y = u1; l.z = u2; l.w = u3;
+      *(bf16x4*)((char*)((__bf16*)base + off) + plane) = l;
+    }
   }
 }
 
-// Store 2 consecutive values as bf16 hi [+ lo].
-template <bool SPLIT>
-__device__ __forceinline__ void st2(char* base, int plane, int off_elems, float a, float b) {
-  bf16x2 h, l;
-  __bf16 t0, t1, u0, u1;
-  split_bf(a, t0, u0); split_bf(b, t1, u1);
-  h.x = t0; h.y = t1;
-  *(bf16x2*)((__bf16*)base + off_elems) = h;
-  if constexpr (SPLIT) {
-    l.x = u0; l.y = u1;
-    *(bf16x2*)((char*)((__bf16*)base + off_elems) + plane) = l;
+template <int MODE>
+__device__ __forceinline__ void st2(char* base, int plane, int off, float a, float b) {
+  if constexpr (MODE == kF32) {
+    *(float2*)((float*)base + off) = make_float2(a, b);
+  } else {
+    bf16x2 h, l;
+    __bf16 t0, t1, u0, u1;
+    split_bf(a, t0, u0); split_bf(b, t1, u1);
+    h.x = t0; h.y = t1;
+    *(bf16x2*)((__bf16*)base + off) = h;
+    if constexpr (MODE == kSP) {
+      l.x = u0; l.y = u1;
+      *(bf16x2*)((char*)((__bf16*)base + off) + plane) = l;
+    }
   }
 }
 
-// Store 1 value as bf16 hi [+ lo].
-template <bool SPLIT>
-__device__ __forceinline__ void st1(char* base, int plane, int off_elems, float a) {
-  __bf16 h, l;
-  split_bf(a, h, l);
-  ((__bf16*)base)[off_elems] = h;
-  if constexpr (SPLIT) *(__bf16*)((char*)((__bf16*)base + off_elems) + plane) = l;
-}
-
-// Scale an 8-element fragment (hi [+ lo]) by per-k factors s[0..7], re-rounding.
-template <bool SPLIT>
-__device__ __forceinline__ void scale_frag(Frag<SPLIT>& f, const float* s) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float x = (float)f.hi[e];
-    if constexpr (SPLIT) x += (float)f.lo[e];
-    x *= s[e];
+template <int MODE>
+__device__ __forceinline__ void st1(char* base, int plane, int off, float a) {
+  if constexpr (MODE == kF32) {
+    ((float*)base)[off] = a;
+  } else {
     __bf16 h, l;
-    split_bf(x, h, l);
-    f.hi[e] = h;
-    if constexpr (SPLIT) f.lo[e] = l;
+    split_bf(a, h, l);
+    ((__bf16*)base)[off] = h;
+    if constexpr (MODE == kSP) *(__bf16*)((char*)((__bf16*)base + off) + plane) = l;
+  }
+}
+
+// Read one element back as float.
+template <int MODE>
+__device__ __forceinline__ float ld1(const char* base, int plane, int off) {
+  if constexpr (MODE == kF32) return ((const float*)base)[off];
+  float x = (float)((const __bf16*)base)[off];
+  if constexpr (MODE == kSP) x += (float)*(const __bf16*)((const char*)((const __bf16*)base + off) + plane);
+  return x;
+}
+
+// Scale an 8-element fragment by per-k factors s[0..7].
+template <int MODE>
+__device__ __forceinline__ void scale_frag(Frag<MODE>& f, const float* s) {
+  if constexpr (MODE == kF32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.a[e] *= s[e]; f.b[e] *= s[4 + e]; }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = (float)f.hi[e];
+      if constexpr (MODE == kSP) x += (float)f.lo[e];
+      x *= s[e];
+      __bf16 h, l;
+      split_bf(x, h, l);
+      f.hi[e] = h;
+      if constexpr (MODE == kSP) f.lo[e] = l;
+    }
   }
 }
 

@@ -17,6 +17,9 @@
 //
 // One workgroup (256 threads) per (b, h, value tile of VT columns); the tile
 // walks the chunks sequentially, holding its [C | n] state slice in registers.
+//
+// Precision: bf16 inputs use bf16 MFMA operands with fp32 accumulation; fp32
+// inputs keep fp32 operands in LDS and use fp32 MFMA (16x16x4).
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
 
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
     const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
     Tin* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV, int C) {
   using L = MlstmSmem<DK, VT, CM, SPLIT>;
+  constexpr int MM = SPLIT ? kF32 : kBF;  // fp32 inputs: fp32 MFMA; bf16 inputs: bf16 MFMA
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NVL = VT / 16, NVA = L::NVA;
   constexpr int NST = (DK / 16) * NVA;
@@ -98,22 +102,75 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
           else Sacc[i][e] = (c16 == 0) ? n0[(size_t)bh * DK + j] : 0.f;
         }
       }
-      st4<SPLIT>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+      st4<MM>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
     }
   }
   __syncthreads();
 
+  // ---- input staging: item (s, j0) = 8 consecutive channels of row s, with
+  // lanes running along s so that one load feeds q, k ([s][j], 16-byte LDS
+  // writes) and k^T ([j][s], 2-byte writes to consecutive addresses) without
+  // bank conflicts. Loads are branch-free (row clamped, padding selected) and,
+  // for bf16 inputs, issued one chunk ahead.
+  using RW = Raw<Tin>;
+  constexpr bool PF = !SPLIT;
+  constexpr int KG = DK / 8;
+  constexpr int NIT = (CM * KG + 255) / 256;
+  constexpr int NIV = (CM * (VT / 8) + 255) / 256;
+  typename RW::R8 cq[NIT], ck[NIT], nq[NIT], nk[NIT], cvv[NIV], nvv[NIV];
+  float cf = 0.f, ci = 0.f, nf = 0.f, ni = 0.f;
+  auto issue = [&](int chk, typename RW::R8* xq, typename RW::R8* xk, typename RW::R8* xv, float& xf,
+                   float& xi) {
+    const int tb = chk * C;
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int it = tid + 256 * i;
+      const int s = it % C, j0 = (it / C) * 8;
+      const int tg = tb + s;
+      const size_t off = seqK + (size_t)(tg < T ? tg : T - 1) * DK + (j0 < DK ? j0 : 0);
+      xq[i] = RW::ld8(q + off);
+      xk[i] = RW::ld8(k + off);
+    }
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
+      const int it = tid + 256 * i;
+      const int s = it % C, v0 = (it / C) * 8;
+      const int tg = tb + s;
+      xv[i] = RW::ld8(v + seqV + (size_t)(tg < T ? tg : T - 1) * DV + vt0 + (v0 < VT ? v0 : 0));
+    }
+    if (wid == 0) {
+      const int tg = tb + (lane < C ? lane : 0);
+      const size_t og = seqG + (tg < T ? tg : T - 1);
+      xf = f_tilde[og];
+      xi = i_tilde[og];
+    }
+  };
+  if (PF) issue(0, nq, nk, nvv, nf, ni);
+  // rows of the normaliser tile below its first row are constant zero
+  for (int it = tid; it < (L::VA - VT - 1) * CM; it += 256) {
+    st1<MM>(smem + L::VTR, L::P_V, (VT + 1 + it / CM) * L::LDC + it % CM, 0.f);
+    st1<MM>(smem + L::VTW, L::P_V, (VT + 1 + it / CM) * L::LDC + it % CM, 0.f);
+  }
+
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * C;
+    if constexpr (PF) {
+#pragma unroll
+      for (int i = 0; i < NIT; ++i) { cq[i] = nq[i]; ck[i] = nk[i]; }
+#pragma unroll
+      for (int i = 0; i < NIV; ++i) cvv[i] = nvv[i];
+      cf = nf;
+      ci = ni;
+      if (ch + 1 < nchunks) issue(ch + 1, nq, nk, nvv, nf, ni);
+    } else {
+      issue(ch, cq, ck, cvv, cf, ci);
+    }
     // ---------------- gates: F, a, mu, m (wave 0, one lane per token)
     if (wid == 0) {
       const int t = lane;
       const bool valid = (t < C) && (t0 + t < T);
-      float lf = 0.f, it = -INFINITY;
-      if (valid) {
-        lf = log_sigmoid(f_tilde[seqG + t0 + t]);
-        it = i_tilde[seqG + t0 + t];
-      }
+      const float lf = valid ? log_sigmoid(cf) : 0.f;
+      const float it = valid ? ci : -INFINITY;
       float F = lf;  // inclusive prefix sum over the chunk
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -136,57 +193,43 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
         sWs[t] = valid ? __expf(a - muC) : 0.f;
       }
     }
-    // ---------------- q, k (natural and transposed), v^T with the ones row
-    {
-      constexpr int KG = DK / 8;
-      for (int it = tid; it < C * KG; it += 256) {  // q and k, k-contiguous rows
-        const int s = it / KG, j0 = (it % KG) * 8;
-        const int tg = t0 + s;
-        float qv[8], kv[8];
+    // ---------------- q, k, k^T, v^T (+ the ones row of the normaliser)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float2 a2 = make_float2(0.f, 0.f), b2 = make_float2(0.f, 0.f);
-          if (tg < T) {
-            a2 = In<Tin>::load2(q + seqK + (size_t)tg * DK + j0 + e);
-            b2 = In<Tin>::load2(k + seqK + (size_t)tg * DK + j0 + e);
-          }
-          qv[e] = a2.x; qv[e + 1] = a2.y; kv[e] = b2.x; kv[e + 1] = b2.y;
-        }
-        st4<SPLIT>(smem + L::Q, L::P_Q, s * L::LDK + j0, f32x4{qv[0], qv[1], qv[2], qv[3]});
-        st4<SPLIT>(smem + L::Q, L::P_Q, s * L::LDK + j0 + 4, f32x4{qv[4], qv[5], qv[6], qv[7]});
-        st4<SPLIT>(smem + L::K, L::P_Q, s * L::LDK + j0, f32x4{kv[0], kv[1], kv[2], kv[3]});
-        st4<SPLIT>(smem + L::K, L::P_Q, s * L::LDK + j0 + 4, f32x4{kv[4], kv[5], kv[6], kv[7]});
-      }
-      for (int it = tid; it < C * KG; it += 256) {  // k^T: lanes run along s (conflict-free)
+    for (int i = 0; i < NIT; ++i) {
+      const int it = tid + 256 * i;
+      if (it < C * KG) {
         const int s = it % C, j0 = (it / C) * 8;
-        const int tg = t0 + s;
+        const bool ok = t0 + s < T;
+        float fq[8], fk[8];
+        RW::un8(RW::sel(ok, cq[i], RW::zero8()), fq);
+        RW::un8(RW::sel(ok, ck[i], RW::zero8()), fk);
+        st4<MM>(smem + L::Q, L::P_Q, s * L::LDK + j0, f32x4{fq[0], fq[1], fq[2], fq[3]});
+        st4<MM>(smem + L::Q, L::P_Q, s * L::LDK + j0 + 4, f32x4{fq[4], fq[5], fq[6], fq[7]});
+        st4<MM>(smem + L::K, L::P_Q, s * L::LDK + j0, f32x4{fk[0], fk[1], fk[2], fk[3]});
+        st4<MM>(smem + L::K, L::P_Q, s * L::LDK + j0 + 4, f32x4{fk[4], fk[5], fk[6], fk[7]});
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float2 b2 = make_float2(0.f, 0.f);
-          if (tg < T) b2 = In<Tin>::load2(k + seqK + (size_t)tg * DK + j0 + e);
-          st1<SPLIT>(smem + L::KT, L::P_KT, (j0 + e) * L::LDC + s, b2.x);
-          st1<SPLIT>(smem + L::KT, L::P_KT, (j0 + e + 1) * L::LDC + s, b2.y);
-        }
-      }
-      for (int it = tid; it < L::VA * C; it += 256) {  // v^T (+ normaliser row), lanes along s
-        const int s = it % C, vr = it / C;
-        const int tg = t0 + s;
-        float val = 0.f;
-        if (vr < VT) {
-          if (tg < T) val = In<Tin>::load1(v + seqV + (size_t)tg * DV + vt0 + vr);
-        } else if (vr == VT) {
-          val = (tg < T) ? 1.f : 0.f;
-        }
-        st1<SPLIT>(smem + L::VTR, L::P_V, vr * L::LDC + s, val);
+        for (int e = 0; e < 8; ++e) st1<MM>(smem + L::KT, L::P_KT, (j0 + e) * L::LDC + s, fk[e]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
+      const int it = tid + 256 * i;
+      if (it < C * (VT / 8)) {
+        const int s = it % C, v0 = (it / C) * 8;
+        const bool ok = t0 + s < T;
+        float fv[8];
+        RW::un8(RW::sel(ok, cvv[i], RW::zero8()), fv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st1<MM>(smem + L::VTR, L::P_V, (v0 + e) * L::LDC + s, fv[e]);
+      }
+    }
+    if (tid < C) st1<MM>(smem + L::VTR, L::P_V, VT * L::LDC + tid, (t0 + tid < T) ? 1.f : 0.f);
     __syncthreads();
     // scaled values for the state update
-    for (int it = tid; it < L::VA * C; it += 256) {
+    for (int it = tid; it < (VT + 1) * C; it += 256) {
       const int s = it % C, vr = it / C;
-      float val = (float)((const __bf16*)(smem + L::VTR))[vr * L::LDC + s];
-      if constexpr (SPLIT) val += (float)((const __bf16*)(smem + L::VTR + L::P_V))[vr * L::LDC + s];
-      st1<SPLIT>(smem + L::VTW, L::P_V, vr * L::LDC + s, val * sWs[s]);
+      const float val = ld1<MM>(smem + L::VTR, L::P_V, vr * L::LDC + s);
+      st1<MM>(smem + L::VTW, L::P_V, vr * L::LDC + s, val * sWs[s]);
     }
 
     // ---------------- scores (transposed tiles) and the inter-chunk readout
@@ -201,9 +244,9 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
         const int sb = p - tb * (tb + 1) / 2;
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::K, L::P_Q, L::LDK, 16 * sb, k0, DK, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::Q, L::P_Q, L::LDK, 16 * tb, k0, DK, lane);
-          mma<SPLIT>(gP[i], A, B);
+          Frag<MM> A = ldfrag<MM>(smem + L::K, L::P_Q, L::LDK, 16 * sb, k0, DK, lane);
+          Frag<MM> B = ldfrag<MM>(smem + L::Q, L::P_Q, L::LDK, 16 * tb, k0, DK, lane);
+          mma<MM>(gP[i], A, B);
         }
       }
     }
@@ -214,9 +257,9 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
         Hin[vl] = f4zero();
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::C0T, L::P_C0, L::LDK, 16 * vl, k0, DK, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::Q, L::P_Q, L::LDK, 16 * wid, k0, DK, lane);
-          mma<SPLIT>(Hin[vl], A, B);
+          Frag<MM> A = ldfrag<MM>(smem + L::C0T, L::P_C0, L::LDK, 16 * vl, k0, DK, lane);
+          Frag<MM> B = ldfrag<MM>(smem + L::Q, L::P_Q, L::LDK, 16 * wid, k0, DK, lane);
+          mma<MM>(Hin[vl], A, B);
         }
       }
     }
@@ -237,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
           const int s = s0 + e;
           wv[e] = (s <= t) ? gP[i][e] * __expf(sA[s] - mut) : 0.f;
         }
-        st4<SPLIT>(smem + L::W, L::P_W, t * L::LDC + s0, wv);
+        st4<MM>(smem + L::W, L::P_W, t * L::LDC + s0, wv);
       }
     }
     __syncthreads();
@@ -252,9 +295,9 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
       for (int vl = 0; vl < NVA; ++vl) {
         f32x4 acc = f4zero();
         for (int k0 = 0; k0 < kend; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::VTR, L::P_V, L::LDC, 16 * vl, k0, kend, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::W, L::P_W, L::LDC, 16 * tb, k0, kend, lane);
-          mma<SPLIT>(acc, A, B);
+          Frag<MM> A = ldfrag<MM>(smem + L::VTR, L::P_V, L::LDC, 16 * vl, k0, kend, lane);
+          Frag<MM> B = ldfrag<MM>(smem + L::W, L::P_W, L::LDC, 16 * tb, k0, kend, lane);
+          mma<MM>(acc, A, B);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Hx[vl][e] = winter * Hin[vl][e] + acc[e];
@@ -287,9 +330,9 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
         const int jt = tile / NVA, vl = tile % NVA;
         f32x4 acc = f4zero();
         for (int k0 = 0; k0 < C; k0 += 32) {
-          Frag<SPLIT> A = ldfrag<SPLIT>(smem + L::KT, L::P_KT, L::LDC, 16 * jt, k0, C, lane);
-          Frag<SPLIT> B = ldfrag<SPLIT>(smem + L::VTW, L::P_V, L::LDC, 16 * vl, k0, C, lane);
-          mma<SPLIT>(acc, A, B);
+          Frag<MM> A = ldfrag<MM>(smem + L::KT, L::P_KT, L::LDC, 16 * jt, k0, C, lane);
+          Frag<MM> B = ldfrag<MM>(smem + L::VTW, L::P_V, L::LDC, 16 * vl, k0, C, lane);
+          mma<MM>(acc, A, B);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[i][e] = dstate * Sacc[i][e] + acc[e];
@@ -302,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
       const int tile = wid + 4 * i;
       if (tile < NST) {
         const int jt = tile / NVA, vl = tile % NVA;
-        st4<SPLIT>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+        st4<MM>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
       }
     }
   }

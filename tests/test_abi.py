@@ -80,6 +80,7 @@ def test_chunk_validation(lib):
     assert _chunk(lib, dv=256) == c["GDR_ERR_UNSUPPORTED"]
     assert _chunk(lib, chunk=128) == c["GDR_ERR_UNSUPPORTED"]
     assert _chunk(lib, dk=128, dv=128, chunk=64, dtype=0) == c["GDR_ERR_UNSUPPORTED"]
+    assert _chunk(lib, dk=64, dv=16, chunk=64, dtype=0) == c["GDR_ERR_UNSUPPORTED"]
     assert _chunk(lib, ptrs=[P[0] + 8] + P[1:7]) == c["GDR_ERR_ALIGN"]
     assert _chunk(lib, S0=P[8] + 4) == c["GDR_ERR_ALIGN"]
     # o overlapping q
