@@ -26,19 +26,19 @@
 //   within 16 tokens).
 // No logarithm, exponential or division by a cumulative decay is taken.
 //
-// Work split: one workgroup (256 threads, 4 waves) per (sequence b, head h,
+// Work split: one workgroup (512 threads, 8 waves) per (sequence b, head h,
 // value tile of VT columns). Value columns of S evolve independently (eq.(1)
 // acts on S from the left), so the tiles need no communication; each walks
 // all chunks of its head, holding its S tile (d_k x VT, fp32) in registers.
 //
-// Phases per chunk (4 waves, 7 workgroup barriers):
+// Phases per chunk (8 waves, 8 workgroup barriers):
 //   prep 1  block totals G, v^ = w*v                          (all waves, VALU)
 //   prep 2  Kr = k^*P, Qr = q*P, Kc = k*Qs, K~^T, per-pair scale vectors
 //   Gram    L^T, M^T tiles = (Kc*D) [Kr; Qr]^T                (MFMA)
 //   write   L as fp32 16x16 blocks, M
-//   solve   wave 0: D_I = (I + L_II)^{-1} by forward substitution and
-//           L'_IJ = D_I L_IJ (MFMA); waves 1-3 meanwhile: R = V^ - Kr (B_I * S0)
-//           and O^T = (B_I * S0)^T Qr^T
+//   solve   wave 0: D_I = (I + L_II)^{-1} by forward substitution; waves 1-7
+//           meanwhile: R = V^ - Kr (B_I * S0) and O^T = (B_I * S0)^T Qr^T;
+//           then L'_IJ = D_I L_IJ (MFMA, one off-diagonal block per wave)
 //   V~      block forward substitution, in place over R, one wave per value
 //           tile: V~_I = D_I R_I - sum_{J<I} L'_IJ V~_J (T V~ = R, block rows)
 //   end     O^T += V~^T M^T, store O; S <- Diag(pi_C) S + K~^T V~
@@ -162,28 +162,39 @@ __device__ void exact_diag(const Tin* __restrict__ k, const Tin* __restrict__ bg
   mv = f32x4{aM[0], aM[1], aM[2], aM[3]};
 }
 
+// Off-diagonal pair index q -> (I, J), J < I.
+__device__ __forceinline__ void offpair_of(int q, int& I, int& J) {
+  I = 1;
+  while ((I + 1) * I / 2 <= q) ++I;
+  J = q - I * (I - 1) / 2;
+}
+
+constexpr int kThreads = 512;  // 8 waves: two per SIMD
+
 template <typename Tin, int DK, int VT, int CM, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gdn2_chunk_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
     const float* __restrict__ S0, Tin* __restrict__ o, float* S_out, int T, int DV, int C) {
   using L = ChunkSmem<DK, VT, CM, SPLIT>;
   constexpr int MM = SPLIT ? kF32 : kBF;   // main operands
-  constexpr int MT = SPLIT ? kF32 : kSP;   // T^{-1} construction
+  constexpr int MT = SPLIT ? kF32 : kSP;   // triangular solve
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NW = kThreads / 64;
   constexpr int NVL = VT / 16;                       // 16-col value tiles per workgroup
   constexpr int NST = (DK / 16) * NVL;               // S accumulator tiles
-  constexpr int MAXS = (NST + 3) / 4;
+  constexpr int MAXS = (NST + NW - 1) / NW;
   constexpr int NBM = CM / 16;
-  constexpr int MAXP = (L::NPM + 3) / 4;             // Gram pairs per wave
-  constexpr int MAXJ = (NBM * NVL + 2) / 3;          // R/O jobs per wave (waves 1-3)
+  constexpr int MAXP = (L::NPM + NW - 1) / NW;       // Gram pairs per wave
+  constexpr int MAXQ = (L::NPM - NBM + NW - 1) / NW; // off-diagonal pairs per wave
+  constexpr int MAXJ = (NBM * NVL + NW - 2) / (NW - 1);  // R/O jobs per wave (waves 1..)
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int nvt = DV / VT;
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
   const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
-  const int NB = C / 16, NP = NB * (NB + 1) / 2, NJ = NB * NVL;
+  const int NB = C / 16, NP = NB * (NB + 1) / 2, NQ = NB * (NB - 1) / 2, NJ = NB * NVL;
   const int nchunks = (T + C - 1) / C;
   const size_t seqK = (size_t)bh * T * DK;
   const size_t seqV = (size_t)bh * T * DV;
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
 #pragma unroll
   for (int i = 0; i < MAXS; ++i) {
     Sacc[i] = f4zero();
-    const int tile = wid + 4 * i;
+    const int tile = wid + NW * i;
     if (tile < NST) {
       const int jt = tile / NVL, vl = tile % NVL;
       if (S0) {
@@ -220,84 +231,86 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
 
   f32x4 Oacc[MAXJ];
 
-  // ---- input staging. Thread (I0, j) owns channels j, j+1 of 16-row block I0;
-  // the v^ item of a thread is 8 consecutive value columns of one row. Loads
-  // are branch-free (row clamped into range, padding selected afterwards).
-  // bf16 inputs: the next chunk's words are fetched while this chunk computes.
+  // ---- input staging. Lanes l and l^32 of a wave share channels (j, j+1) of
+  // one 16-row block I0 and take its rows 0-7 (h = 0) and 8-15 (h = 1); the
+  // half-block products are exchanged across the pair. A v^ item is 8
+  // consecutive value columns of one row. Loads are branch-free (rows clamped,
+  // padding selected afterwards) and the next chunk's are issued while this
+  // chunk's Gram products run.
   using RW = Raw<Tin>;
-  constexpr bool PF = !SPLIT;
-  const int items = NB * (DK / 2);
-  const bool act = tid < items;
-  const int I0 = act ? tid / (DK / 2) : 0, j = act ? 2 * (tid % (DK / 2)) : 0;
+  const int h = lane >> 5;
+  const int fp = wid * 32 + (lane & 31);
+  const bool act = fp < NB * (DK / 2);
+  const int I0 = act ? fp / (DK / 2) : 0, j = act ? 2 * (fp % (DK / 2)) : 0;
+  const int r0 = 16 * I0 + 8 * h;                    // first chunk row of this thread
   const int nvi = C * (VT / 8);
   const bool vact = tid < nvi;
   const int vrow = vact ? tid / (VT / 8) : 0, vcol = vact ? (tid % (VT / 8)) * 8 : 0;
-  typename RW::R2 ca[16], ck[16], cb[16], cq[16];
-  typename RW::R2 na[16], nk[16], nb[16], nq[16];
-  typename RW::R8 cv, cw, nv, nw;
-  auto issue = [&](int chk, typename RW::R2* xa, typename RW::R2* xk, typename RW::R2* xb,
-                   typename RW::R2* xq, typename RW::R8& xv, typename RW::R8& xw) {
+  typename RW::R2 xa[8], xk[8], xb[8], xq[8];
+  typename RW::R8 xv, xw;
+  // per-head base pointers; offsets within a head are 32-bit (T * d < 2^31)
+  const Tin* __restrict__ qh = q + seqK + j;
+  const Tin* __restrict__ kh = k + seqK + j;
+  const Tin* __restrict__ ah = alpha + seqK + j;
+  const Tin* __restrict__ bh_ = bgate + seqK + j;
+  const Tin* __restrict__ vh_ = v + seqV + vt0 + vcol;
+  const Tin* __restrict__ wh_ = wgate + seqV + vt0 + vcol;
+  auto issue = [&](int chk) {
     const int tb = chk * C;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = tb + 16 * I0 + r;
-      const size_t off = seqK + (size_t)(t < T ? t : T - 1) * DK + j;
-      xa[r] = RW::ld2(alpha + off);
-      xk[r] = RW::ld2(k + off);
-      xb[r] = RW::ld2(bgate + off);
-      xq[r] = RW::ld2(q + off);
+    for (int r = 0; r < 8; ++r) {
+      const int t = tb + r0 + r;
+      const int off = (t < T ? t : T - 1) * DK;
+      xa[r] = RW::ld2(ah + off);
+      xk[r] = RW::ld2(kh + off);
+      xb[r] = RW::ld2(bh_ + off);
+      xq[r] = RW::ld2(qh + off);
     }
     const int tv = tb + vrow;
-    const size_t offv = seqV + (size_t)(tv < T ? tv : T - 1) * DV + vt0 + vcol;
-    xv = RW::ld8(v + offv);
-    xw = RW::ld8(wgate + offv);
+    const int offv = (tv < T ? tv : T - 1) * DV;
+    xv = RW::ld8(vh_ + offv);
+    xw = RW::ld8(wh_ + offv);
   };
-  if (PF) issue(0, na, nk, nb, nq, nv, nw);
+  issue(0);
 
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * C;
-    if constexpr (PF) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { ca[r] = na[r]; ck[r] = nk[r]; cb[r] = nb[r]; cq[r] = nq[r]; }
-      cv = nv;
-      cw = nw;
-      if (ch + 1 < nchunks) issue(ch + 1, na, nk, nb, nq, nv, nw);
-    } else {
-      issue(ch, ca, ck, cb, cq, cv, cw);
-    }
     // identity padding past the end of the sequence: alpha = 1, k = b = q = 0, v = w = 0
     {
       const typename RW::R2 one = RW::pad2(1.f), zero = RW::pad2(0.f);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = t0 + 16 * I0 + r < T;
-        ca[r] = RW::sel(ok, ca[r], one);
-        ck[r] = RW::sel(ok, ck[r], zero);
-        cb[r] = RW::sel(ok, cb[r], zero);
-        cq[r] = RW::sel(ok, cq[r], zero);
+      for (int r = 0; r < 8; ++r) {
+        const bool ok = t0 + r0 + r < T;
+        xa[r] = RW::sel(ok, xa[r], one);
+        xk[r] = RW::sel(ok, xk[r], zero);
+        xb[r] = RW::sel(ok, xb[r], zero);
+        xq[r] = RW::sel(ok, xq[r], zero);
       }
       const bool okv = t0 + vrow < T;
-      cv = RW::sel(okv, cv, RW::zero8());
-      cw = RW::sel(okv, cw, RW::zero8());
+      xv = RW::sel(okv, xv, RW::zero8());
+      xw = RW::sel(okv, xw, RW::zero8());
     }
 
-    // ================= prep 1: block totals G, v^
-    if (act) {
-      float2 p = make_float2(1.f, 1.f);
+    // ================= prep 1: half-block products -> block totals G; v^
+    float2 ph = make_float2(1.f, 1.f);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float2 a = RW::un2(ca[r]);
-        p.x *= a.x;
-        p.y *= a.y;
-      }
-      GS[I0 * DK + j] = p.x;
-      GS[I0 * DK + j + 1] = p.y;
-      if (!(p.x >= kGuardMin && p.y >= kGuardMin)) FLAGS[I0] = 1;
+    for (int r = 0; r < 8; ++r) {
+      const float2 a = RW::un2(xa[r]);
+      ph.x *= a.x;
+      ph.y *= a.y;
+    }
+    const float2 po = make_float2(__shfl_xor(ph.x, 32, 64), __shfl_xor(ph.y, 32, 64));
+    const float2 p0 = h ? po : ph, p1 = h ? ph : po;   // products of rows 0-7 and 8-15
+    if (act && h == 0) {
+      const float gx = p0.x * p1.x, gy = p0.y * p1.y;
+      GS[I0 * DK + j] = gx;
+      GS[I0 * DK + j + 1] = gy;
+      if (!(gx >= kGuardMin && gy >= kGuardMin)) FLAGS[I0] = 1;
     }
     if (vact) {
       float fv[8], fw[8];
-      RW::un8(cv, fv);
-      RW::un8(cw, fw);
+      RW::un8(xv, fv);
+      RW::un8(xw, fw);
 #pragma unroll
       for (int e = 0; e < 8; ++e) VH[(vcol + e) * L::LDF + vrow] = fv[e] * fw[e];
     }
@@ -312,12 +325,12 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
         if (J > I0) { E.x *= gx; E.y *= gy; }
         pic.x *= gx; pic.y *= gy;
       }
-      if (I0 == 0) { PIC[j] = pic.x; PIC[j + 1] = pic.y; }
-      BS[I0 * DK + j] = Bst.x;
-      BS[I0 * DK + j + 1] = Bst.y;
-      // scale of pair (I0, J): 1/G_I0 on the diagonal (in-block ratio), the
-      // product of the block totals strictly between J and I0 below it
-      {
+      if (h == 0) {
+        if (I0 == 0) { PIC[j] = pic.x; PIC[j + 1] = pic.y; }
+        BS[I0 * DK + j] = Bst.x;
+        BS[I0 * DK + j + 1] = Bst.y;
+        // scale of pair (I0, J): 1/G_I0 on the diagonal (in-block ratio), the
+        // product of the block totals strictly between J and I0 below it
         const float gx = GS[I0 * DK + j], gy = GS[I0 * DK + j + 1];
         SCL[pidx(I0, I0) * DK + j] = __builtin_amdgcn_rcpf(gx);
         SCL[pidx(I0, I0) * DK + j + 1] = __builtin_amdgcn_rcpf(gy);
@@ -329,38 +342,39 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
           d.y *= GS[J * DK + j + 1];
         }
       }
-      float2 P = make_float2(1.f, 1.f);
+      float2 P = h ? p0 : make_float2(1.f, 1.f);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tl = 16 * I0 + r;
-        const float2 a = RW::un2(ca[r]), kk = RW::un2(ck[r]), bb = RW::un2(cb[r]), qq = RW::un2(cq[r]);
+      for (int r = 0; r < 8; ++r) {
+        const float2 a = RW::un2(xa[r]), kk = RW::un2(xk[r]), bb = RW::un2(xb[r]), qq = RW::un2(xq[r]);
         P.x *= a.x;
         P.y *= a.y;
-        const int off = tl * L::LDK + j;
+        const int off = (r0 + r) * L::LDK + j;
         st2<MM>(smem + L::KR, L::P_CK, off, bb.x * kk.x * P.x, bb.y * kk.y * P.y);
         st2<MM>(smem + L::QR, L::P_CK, off, qq.x * P.x, qq.y * P.y);
       }
-      float ktx[16], kty[16];
-      float2 qs = make_float2(1.f, 1.f);
+      float ktx[8], kty[8];
+      float2 qs = h ? make_float2(1.f, 1.f) : p1;
 #pragma unroll
-      for (int r = 15; r >= 0; --r) {
-        const float2 kk = RW::un2(ck[r]), a = RW::un2(ca[r]);
+      for (int r = 7; r >= 0; --r) {
+        const float2 kk = RW::un2(xk[r]), a = RW::un2(xa[r]);
         const float kcx = kk.x * qs.x, kcy = kk.y * qs.y;
-        st2<MM>(smem + L::KC, L::P_CK, (16 * I0 + r) * L::LDK + j, kcx, kcy);
+        st2<MM>(smem + L::KC, L::P_CK, (r0 + r) * L::LDK + j, kcx, kcy);
         ktx[r] = kcx * E.x;
         kty[r] = kcy * E.y;
         qs.x *= a.x;
         qs.y *= a.y;
       }
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        st4<MM>(smem + L::KTT, L::P_KC, j * L::LDC + 16 * I0 + 4 * r4,
+      for (int r4 = 0; r4 < 2; ++r4) {
+        st4<MM>(smem + L::KTT, L::P_KC, j * L::LDC + r0 + 4 * r4,
                 f32x4{ktx[4 * r4], ktx[4 * r4 + 1], ktx[4 * r4 + 2], ktx[4 * r4 + 3]});
-        st4<MM>(smem + L::KTT, L::P_KC, (j + 1) * L::LDC + 16 * I0 + 4 * r4,
+        st4<MM>(smem + L::KTT, L::P_KC, (j + 1) * L::LDC + r0 + 4 * r4,
                 f32x4{kty[4 * r4], kty[4 * r4 + 1], kty[4 * r4 + 2], kty[4 * r4 + 3]});
       }
     }
     __syncthreads();
+    // the next chunk's loads overlap the Gram MFMAs and stay in flight through the chunk
+    if (ch + 1 < nchunks) issue(ch + 1);
 
     // ================= Gram tiles: L^T, M^T of pair (I, J) = (Kc_J * scale) [Kr_I; Qr_I]^T
     f32x4 gL[MAXP], gM[MAXP];
@@ -368,7 +382,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     for (int i = 0; i < MAXP; ++i) {
       gL[i] = f4zero();
       gM[i] = f4zero();
-      const int p = wid + 4 * i;
+      const int p = wid + NW * i;
       if (p < NP) {
         int I, J;
         pair_of(p, I, J);
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     // ================= write L (fp32 blocks) and M
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
-      const int p = wid + 4 * i;
+      const int p = wid + NW * i;
       if (p < NP) {
         int I, J;
         pair_of(p, I, J);
@@ -418,53 +432,40 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     if (wid == 0) {
       // ============= D_I = (I + L_II)^{-1}: forward substitution, lane = (block g, column c16)
       if (tid < 4) FLAGS[tid] = 0;  // last read above; set again by the next chunk's prep 1
-      {
-        const int I = g, cc = c16;
-        const bool live = I < NB;
-        const int pd = live ? pidx(I, I) : 0;
-        const float* Lb = LBK + pd * BLKF;
-        float x[16];
+      const int I = g, cc = c16;
+      const bool live = I < NB;
+      const float* Lb = LBK + (live ? pidx(I, I) : 0) * BLKF;
+      float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float acc0 = (r == cc) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
+        for (int m4 = 0; 4 * m4 < r; ++m4) {
+          const f32x4 lv = *(const f32x4*)(Lb + r * L::LDB + 4 * m4);
 #pragma unroll
-          for (int r = m + 1; r < 16; ++r) x[r] -= Lb[r * L::LDB + m] * x[m];
-        }
-        if (live) {
-          float* Tn = TBN + I * BLKF;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            Tn[r * L::LDB + cc] = x[r];
-            st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
+          for (int e = 0; e < 4; ++e) {
+            const int m = 4 * m4 + e;
+            if (m < r) {
+              if (m & 1) acc1 -= lv[e] * x[m];
+              else acc0 -= lv[e] * x[m];
+            }
           }
         }
+        x[r] = acc0 + acc1;
       }
-      wave_lds_sync();
-      // ============= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL
-      for (int p = 0; p < NP; ++p) {
-        int I, J;
-        pair_of(p, I, J);
-        if (I == J) continue;
-        const bool ok = g < 2;  // k = m spans one 16-row block
-        Frag<MT> A = frag_f32<MT>(TBN + I * BLKF + c16 * L::LDB + 8 * (g & 1), ok);
-        // B[k = m][n = s] = L_IJ[m][s]: gather the column s of the fp32 block
-        float lc[8];
-        const float* lb = LBK + p * BLKF + c16;
+      if (live) {
+        float* Tn = TBN + I * BLKF;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lc[e] = ok ? lb[(8 * (g & 1) + e) * L::LDB] : 0.f;
-        Frag<MT> B = frag_f32<MT>(lc, true);
-        f32x4 acc = f4zero();
-        mma<MT>(acc, A, B);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
+        for (int r = 0; r < 16; ++r) {
+          Tn[r * L::LDB + cc] = x[r];
+          st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
+        }
       }
     } else {
-      // ============= waves 1-3: R = V^ - Kr (B_I * S0) and O^T = (B_I * S0)^T Qr^T
+      // ============= waves 1..: R = V^ - Kr (B_I * S0) and O^T = (B_I * S0)^T Qr^T
 #pragma unroll
       for (int i = 0; i < MAXJ; ++i) {
-        const int job = (wid - 1) + 3 * i;
+        const int job = (wid - 1) + (NW - 1) * i;
         if (job < NJ) {
           const int I = job / NVL, vl = job % NVL;
           f32x4 r = f4zero();
@@ -493,6 +494,31 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     }
     __syncthreads();
 
+    // ================= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL
+#pragma unroll
+    for (int i = 0; i < MAXQ; ++i) {
+      const int qq = wid + NW * i;
+      if (qq < NQ) {
+        int I, J;
+        offpair_of(qq, I, J);
+        const int p = pidx(I, J);
+        const bool ok = g < 2;  // k = m spans one 16-row block
+        Frag<MT> A = frag_f32<MT>(TBN + I * BLKF + c16 * L::LDB + 8 * (g & 1), ok);
+        // B[k = m][n = s] = L_IJ[m][s]: gather column s of the fp32 block
+        float lc[8];
+        const float* lb = LBK + p * BLKF + c16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lc[e] = ok ? lb[(8 * (g & 1) + e) * L::LDB] : 0.f;
+        Frag<MT> B = frag_f32<MT>(lc, true);
+        f32x4 acc = f4zero();
+        mma<MT>(acc, A, B);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
+      }
+    }
+    __syncthreads();
+
     // ================= V~: block forward substitution in place over R (one wave per value tile)
     if (wid < NVL) {
       const int vl = wid;
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     if (wid > 0) {
 #pragma unroll
       for (int i = 0; i < MAXJ; ++i) {
-        const int job = (wid - 1) + 3 * i;
+        const int job = (wid - 1) + (NW - 1) * i;
         if (job < NJ) {
           const int I = job / NVL, vl = job % NVL, kend = 16 * (I + 1);
           for (int k0 = 0; k0 < kend; k0 += 32) {
@@ -531,7 +557,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     }
 #pragma unroll
     for (int i = 0; i < MAXS; ++i) {
-      const int tile = wid + 4 * i;
+      const int tile = wid + NW * i;
       if (tile < NST) {
         const int jt = tile / NVL, vl = tile % NVL;
         const f32x4 pc = *(const f32x4*)(PIC + 16 * jt + 4 * g);
@@ -547,7 +573,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < MAXS; ++i) {
-      const int tile = wid + 4 * i;
+      const int tile = wid + NW * i;
       if (tile < NST) {
         const int jt = tile / NVL, vl = tile % NVL;
         st4<MM>(smem + L::S0T, L::P_VK, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
@@ -558,7 +584,7 @@ __global__ __launch_bounds__(256, 1) void gdn2_chunk_kernel(
   if (S_out) {
 #pragma unroll
     for (int i = 0; i < MAXS; ++i) {
-      const int tile = wid + 4 * i;
+      const int tile = wid + NW * i;
       if (tile < NST) {
         const int jt = tile / NVL, vl = tile % NVL;
 #pragma unroll
@@ -590,7 +616,7 @@ static int launch_chunk(const ChunkArgs& a) {
   float* So = a.S_out;
   int T = a.T, DV = a.dv, C = a.chunk;
   void* args[] = {&q, &k, &v, &al, &bg, &wg, &S0, &o, &So, &T, &DV, &C};
-  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(256), args, L::TOTAL,
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(kThreads), args, L::TOTAL,
                                  (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }

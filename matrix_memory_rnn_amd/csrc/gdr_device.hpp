@@ -67,8 +67,13 @@ template <typename T> struct Raw;
 template <> struct Raw<__bf16> {
   typedef uint32_t R2;
   typedef u32x4 R8;
+  typedef __attribute__((ext_vector_type(2))) uint32_t R4;
   static __device__ __forceinline__ R2 ld2(const __bf16* p) { return *(const uint32_t*)p; }
+  static __device__ __forceinline__ R4 ld4(const __bf16* p) { return *(const R4*)p; }
   static __device__ __forceinline__ R8 ld8(const __bf16* p) { return *(const u32x4*)p; }
+  static __device__ __forceinline__ f32x4 un4(R4 r) { return f32x4{lo(r[0]), hi(r[0]), lo(r[1]), hi(r[1])}; }
+  static __device__ __forceinline__ R4 pad4(float x) { const uint32_t w = pad2(x); return R4{w, w}; }
+  static __device__ __forceinline__ R4 sel(bool ok, R4 r, R4 p) { return R4{ok ? r[0] : p[0], ok ? r[1] : p[1]}; }
   static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
   static __device__ __forceinline__ float2 un2(R2 r) { return make_float2(lo(r), hi(r)); }
@@ -88,8 +93,15 @@ template <> struct Raw<__bf16> {
 };
 template <> struct Raw<float> {
   typedef float2 R2;
+  typedef f32x4 R4;
   struct R8 { f32x4 a, b; };
   static __device__ __forceinline__ R2 ld2(const float* p) { return *(const float2*)p; }
+  static __device__ __forceinline__ R4 ld4(const float* p) { return *(const f32x4*)p; }
+  static __device__ __forceinline__ f32x4 un4(R4 r) { return r; }
+  static __device__ __forceinline__ R4 pad4(float x) { return f32x4{x, x, x, x}; }
+  static __device__ __forceinline__ R4 sel(bool ok, R4 r, R4 p) {
+    return f32x4{ok ? r[0] : p[0], ok ? r[1] : p[1], ok ? r[2] : p[2], ok ? r[3] : p[3]};
+  }
   static __device__ __forceinline__ R8 ld8(const float* p) {
     R8 r;
     r.a = *(const f32x4*)p;
