@@ -190,6 +190,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-side", action="store_true", help="skip the decode and mLSTM side measurements")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB elementwise copy (dst = src * 1) three times: the "
+                         "known-size kernel that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -241,6 +244,14 @@ def main():
         out["mlstm"] = {"workload": "B=2 H=8 T=8192 d=256 C=64 bf16", "ms_per_step": mm["region_ms"],
                         "kernel_ms": mm["launch_ms"], "tokens/s": mt,
                         "GB/s": mm["bytes"] / (mm["launch_ms"] * 1e-3) / 1e9}
+    if args.calib_copy:
+        n = 64 * 1024 * 1024  # 256 MiB of float32 read, 256 MiB written per launch
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes_each_way"] = n * 4
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(r["inputs"])
     print(json.dumps(out), flush=True)
