@@ -20,8 +20,9 @@
  * Supported sizes: d_k, d_v in {16, 32, 64, 128} for the gated delta rule,
  * {16, 32, 64, 128, 256} for mLSTM; chunk in {16, 32, 64}; any T >= 1 (a
  * ragged last chunk behaves as if padded with identity steps alpha = 1, k = 0,
- * v = 0, whose outputs are discarded). With float32 inputs and d_k >= 64 the
- * chunk must be at most 32 (fp32 operands take twice the LDS).
+ * v = 0, whose outputs are discarded). For gdr_chunk_fwd with float32 inputs
+ * and d_k >= 64 the chunk must be at most 32 (fp32 operands take twice the
+ * LDS); gdr_chunk_fwd_ws has no such limit.
  * Alignment: every pointer must be 16-byte aligned.
  *
  * Preconditions not checked on the hot path: alpha in (0, 1]; inputs finite;
@@ -29,6 +30,8 @@
  */
 #ifndef GDR_H
 #define GDR_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -43,6 +46,7 @@ extern "C" {
 #define GDR_ERR_ALIGN       -5  /* a pointer is not 16-byte aligned */
 #define GDR_ERR_LAUNCH      -6  /* the HIP runtime rejected a kernel launch */
 #define GDR_ERR_ALIAS       -7  /* an output buffer overlaps an input buffer */
+#define GDR_ERR_WORKSPACE   -8  /* workspace smaller than gdr_chunk_workspace_size reports */
 
 /* Input/output element types. States (S, C, n, m) are always float32. */
 #define GDR_F32  0
@@ -78,6 +82,41 @@ int gdr_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* S0, void* o, float* S_out,
                   int B, int H, int T, int dk, int dv, int chunk, int dtype,
                   void* stream);
+
+/*
+ * gdr_chunk_workspace_size — bytes of device workspace gdr_chunk_fwd_ws needs
+ * for these sizes: one record per (b, h, chunk) of C*dk*3 + dv*C + C*C
+ * elements of the input dtype plus dk float32 values.
+ * Writes the size to *bytes (0 on error). Returns GDR_OK or a GDR_ERR_* code.
+ */
+int gdr_chunk_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
+                             int dtype, size_t* bytes);
+
+/*
+ * gdr_chunk_fwd_ws — the computation of gdr_chunk_fwd (same arguments, same
+ * results up to rounding) as two kernels, which is the fast form for long
+ * sequences:
+ *   1. every (b, h, chunk) in parallel: the state-independent part of the
+ *      chunkwise form of "Muir: ...", §2.2 with the fused right-hand side of
+ *      §4.2, [U | Y] = T^{-1} [V^ | K^_pi], together with M, Q_pi, K~^T and
+ *      pi_C, written to `workspace`;
+ *   2. one pass over the chunks of each head: V~ = U - Y S_0,
+ *      O = Q_pi S_0 + M V~, S_C = Diag(pi_C) S_0 + K~^T V~.
+ *
+ *   workspace        device buffer of at least gdr_chunk_workspace_size()
+ *                    bytes, 16-byte aligned, owned by the caller; its contents
+ *                    on entry are ignored and on return are unspecified. It
+ *                    must not overlap any other argument, and calls that run
+ *                    concurrently need separate workspaces.
+ *   workspace_bytes  its size in bytes
+ * Other arguments as for gdr_chunk_fwd. Returns GDR_OK or a negative
+ * GDR_ERR_* code (GDR_ERR_WORKSPACE if the workspace is too small).
+ */
+int gdr_chunk_fwd_ws(const void* q, const void* k, const void* v,
+                     const void* alpha, const void* b, const void* w,
+                     const float* S0, void* o, float* S_out,
+                     int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdr_decode_step — one recurrent step of "Muir: ...", §2.1 eq.(1) for N

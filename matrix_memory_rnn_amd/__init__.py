@@ -10,7 +10,10 @@ Entry points (same names as the C ABI):
 
 * :func:`gdr_chunk_fwd` — chunkwise forward of the channel-wise gated delta
   rule ("Muir: Linear Attention with Sensitivity-Allocated Gating and
-  Matched-Filter Readout", §2.1 eq.(1), §2.2).
+  Matched-Filter Readout", §2.1 eq.(1), §2.2), one fused kernel.
+* :func:`gdr_chunk_fwd_ws` — the same computation as an intra-chunk kernel
+  over all chunks plus a chunk scan, through a device workspace
+  (:func:`gdr_chunk_workspace_size` bytes).
 * :func:`gdr_decode_step` — one recurrent decode step, state updated in place.
 * :func:`gdr_mlstm_fwd` — chunkwise forward of the stabilised mLSTM cell
   ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4).
@@ -20,7 +23,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdr_chunk_fwd", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
+__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +54,10 @@ def load_library():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 7 + [P]
     lib.gdr_chunk_fwd.restype = I
+    lib.gdr_chunk_workspace_size.argtypes = [I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_workspace_size.restype = I
+    lib.gdr_chunk_fwd_ws.argtypes = [P] * 9 + [I] * 7 + [P, ctypes.c_size_t, P]
+    lib.gdr_chunk_fwd_ws.restype = I
     lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
     lib.gdr_decode_step.restype = I
     lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
@@ -106,16 +113,7 @@ def _req(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def gdr_chunk_fwd(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=None,
-                  return_state=True, stream=None):
-    """Chunkwise gated delta rule over whole sequences.
-
-    q, k, alpha, b: ``[B,H,T,dk]``; v, w: ``[B,H,T,dv]`` (bfloat16 or float32,
-    all the same dtype, on one GPU). S0: ``[B,H,dk,dv]`` float32 or None (zero
-    state). Returns ``(o, S_T)`` with o ``[B,H,T,dv]`` in the input dtype and
-    S_T float32 (None if ``return_state`` is False). ``S_out`` may be S0 for
-    an in-place state update.
-    """
+def _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state):
     import torch
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -132,11 +130,61 @@ def gdr_chunk_fwd(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=None
         S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     if S_out is not None:
         _req(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
+    return (B, H, T, dk, dv), o, S_out
+
+
+def gdr_chunk_fwd(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=None,
+                  return_state=True, stream=None):
+    """Chunkwise gated delta rule over whole sequences (single fused kernel).
+
+    q, k, alpha, b: ``[B,H,T,dk]``; v, w: ``[B,H,T,dv]`` (bfloat16 or float32,
+    all the same dtype, on one GPU). S0: ``[B,H,dk,dv]`` float32 or None (zero
+    state). Returns ``(o, S_T)`` with o ``[B,H,T,dv]`` in the input dtype and
+    S_T float32 (None if ``return_state`` is False). ``S_out`` may be S0 for
+    an in-place state update.
+    """
+    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state)
     lib = load_library()
     st = lib.gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
                            _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q),
                            _stream(stream))
     _check("gdr_chunk_fwd", st)
+    return o, S_out
+
+
+def gdr_chunk_workspace_size(B, H, T, dk, dv, chunk=64, dtype=None) -> int:
+    """Bytes of workspace :func:`gdr_chunk_fwd_ws` needs (dtype: torch dtype, default bf16)."""
+    import torch
+    code = GDR_BF16 if dtype in (None, torch.bfloat16) else GDR_F32 if dtype == torch.float32 else -1
+    n = ctypes.c_size_t(0)
+    st = load_library().gdr_chunk_workspace_size(int(B), int(H), int(T), int(dk), int(dv), int(chunk),
+                                                 code, ctypes.byref(n))
+    _check("gdr_chunk_workspace_size", st)
+    return int(n.value)
+
+
+def gdr_chunk_fwd_ws(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=None,
+                     workspace=None, return_state=True, stream=None):
+    """Chunkwise gated delta rule as two kernels through a device workspace.
+
+    Same arguments and results as :func:`gdr_chunk_fwd`. ``workspace`` is a
+    CUDA tensor of at least :func:`gdr_chunk_workspace_size` bytes (any dtype,
+    contiguous); if None, one is allocated for this call.
+    """
+    import torch
+    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state)
+    need = gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if not (isinstance(workspace, torch.Tensor) and workspace.device == q.device
+            and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    st = lib.gdr_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                              _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q),
+                              _ptr(workspace), nbytes, _stream(stream))
+    _check("gdr_chunk_fwd_ws", st)
     return o, S_out
 
 

@@ -34,34 +34,14 @@ int check_sizes(long long B, long long H, long long T, int dk, int dv, int dtype
   return GDR_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gdr_version(void) { return 100; }  // 0.1.0
-
-const char* gdr_status_string(int status) {
-  switch (status) {
-    case GDR_OK: return "ok";
-    case GDR_ERR_NULL: return "a required pointer is NULL";
-    case GDR_ERR_SHAPE: return "a size is out of range";
-    case GDR_ERR_DTYPE: return "unknown dtype code";
-    case GDR_ERR_UNSUPPORTED: return "sizes valid but not supported by this build (head dim or chunk)";
-    case GDR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case GDR_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
-    case GDR_ERR_ALIAS: return "an output buffer overlaps an input buffer";
-  }
-  return "unknown status";
-}
-
-int gdr_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
-                  const void* w, const float* S0, void* o, float* S_out, int B, int H, int T, int dk,
-                  int dv, int chunk, int dtype, void* stream) {
+// Checks shared by the two chunkwise entry points.
+int check_chunk(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                const void* w, const float* S0, const void* o, const float* S_out, int B, int H,
+                int T, int dk, int dv, int chunk, int dtype) {
   if (!q || !k || !v || !alpha || !b || !w || !o) return GDR_ERR_NULL;
   int st = check_sizes(B, H, T, dk, dv, dtype, 128);
   if (st != GDR_OK) return st;
   if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
-  if (dtype == GDR_F32 && dk >= 64 && chunk > 32) return GDR_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, alpha, b, w, S0, o, S_out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GDR_ERR_ALIGN;
@@ -77,8 +57,70 @@ int gdr_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha
     return GDR_ERR_ALIAS;
   if (overlap(S_out, nS, v, nV) || overlap(S_out, nS, w, nV)) return GDR_ERR_ALIAS;
   if (S_out && S0 && S_out != S0 && overlap(S_out, nS, S0, nS)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_version(void) { return 200; }  // 0.2.0
+
+const char* gdr_status_string(int status) {
+  switch (status) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL: return "a required pointer is NULL";
+    case GDR_ERR_SHAPE: return "a size is out of range";
+    case GDR_ERR_DTYPE: return "unknown dtype code";
+    case GDR_ERR_UNSUPPORTED: return "sizes valid but not supported by this build (head dim or chunk)";
+    case GDR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case GDR_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case GDR_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case GDR_ERR_WORKSPACE: return "the workspace is smaller than gdr_chunk_workspace_size reports";
+  }
+  return "unknown status";
+}
+
+int gdr_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                  const void* w, const float* S0, void* o, float* S_out, int B, int H, int T, int dk,
+                  int dv, int chunk, int dtype, void* stream) {
+  int st = check_chunk(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  if (dtype == GDR_F32 && dk >= 64 && chunk > 32) return GDR_ERR_UNSUPPORTED;
   gdr::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::chunk_fwd_launch(a);
+}
+
+int gdr_chunk_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype, size_t* bytes) {
+  if (!bytes) return GDR_ERR_NULL;
+  *bytes = 0;
+  int st = check_sizes(B, H, T, dk, dv, dtype, 128);
+  if (st != GDR_OK) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
+  *bytes = gdr::chunk_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  return GDR_OK;
+}
+
+int gdr_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                     const void* w, const float* S0, void* o, float* S_out, int B, int H, int T,
+                     int dk, int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_chunk(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  if (!workspace) return GDR_ERR_NULL;
+  if (!aligned16(workspace)) return GDR_ERR_ALIGN;
+  const size_t need = gdr::chunk_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
+  const size_t es = esize(dtype);
+  const size_t nK = (size_t)B * H * T * dk * es, nV = (size_t)B * H * T * dv * es;
+  const size_t nS = (size_t)B * H * dk * dv * sizeof(float);
+  struct R { const void* p; size_t n; };
+  const R bufs[] = {{q, nK}, {k, nK}, {alpha, nK}, {b, nK}, {v, nV}, {w, nV},
+                    {S0, nS}, {o, nV}, {S_out, nS}};
+  for (const R& x : bufs)
+    if (overlap(workspace, need, x.p, x.n)) return GDR_ERR_ALIAS;
+  gdr::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
+  return gdr::chunk_fwd_ws_launch(a, workspace);
 }
 
 int gdr_decode_step(const void* q, const void* k, const void* v, const void* alpha, const void* b,

@@ -47,15 +47,10 @@
 // Precision: bf16 inputs use bf16 operands with fp32 accumulation, except
 // T^{-1}, which is built from hi/lo split operands (~16 bits). fp32 inputs use
 // fp32 operands and fp32 MFMA (16x16x4) throughout.
-#include "gdr_device.hpp"
+#include "gdr_chunk_common.hpp"
 #include "gdr_internal.h"
 
 namespace gdr {
-
-constexpr float kGuardMin = 8.673617379884035e-19f;  // 2^-60
-
-constexpr int align16(int x) { return (x + 15) / 16 * 16; }
-constexpr int imax(int a, int b) { return a > b ? a : b; }
 
 template <int DK, int VT, int CM, bool SPLIT>
 struct ChunkSmem {
@@ -93,81 +88,6 @@ struct ChunkSmem {
   static constexpr int TOTAL = FLAG + 16;
   static_assert(TOTAL <= 160 * 1024, "chunk kernel LDS exceeds 160 KiB");
 };
-
-__device__ __forceinline__ int pidx(int I, int J) { return I * (I + 1) / 2 + J; }
-
-__device__ __forceinline__ void pair_of(int p, int& I, int& J) {
-  I = 0;
-  while ((I + 1) * (I + 2) / 2 <= p) ++I;
-  J = p - I * (I + 1) / 2;
-}
-
-// Orders this wave's LDS writes before its later LDS reads by other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// 8 consecutive fp32 values from LDS as an operand slice of the given mode.
-template <int MODE>
-__device__ __forceinline__ Frag<MODE> frag_f32(const float* p, bool valid) {
-  Frag<MODE> f;
-  f32x4 a = valid ? *(const f32x4*)p : f4zero();
-  f32x4 b = valid ? *(const f32x4*)(p + 4) : f4zero();
-  if constexpr (MODE == kF32) {
-    f.a = a;
-    f.b = b;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      __bf16 h, l;
-      split_bf(a[e], h, l);
-      f.hi[e] = h;
-      if constexpr (MODE == kSP) f.lo[e] = l;
-      split_bf(b[e], h, l);
-      f.hi[4 + e] = h;
-      if constexpr (MODE == kSP) f.lo[4 + e] = l;
-    }
-  }
-  return f;
-}
-
-// Exact in-block Gram entries for the tile (I, I) from alpha products (slow path).
-template <typename Tin, int DK>
-__device__ void exact_diag(const Tin* __restrict__ k, const Tin* __restrict__ bg,
-                           const Tin* __restrict__ q, const Tin* __restrict__ al,
-                           size_t seqK, int t0, int T, int t, int s0, f32x4& lv, f32x4& mv) {
-  float aL[4] = {0.f, 0.f, 0.f, 0.f}, aM[4] = {0.f, 0.f, 0.f, 0.f};
-  const int tg = t0 + t;
-  if (tg < T && t >= s0) {
-    for (int j = 0; j < DK; ++j) {
-      const float kt = In<Tin>::load1(k + seqK + (size_t)tg * DK + j);
-      const float kh = kt * In<Tin>::load1(bg + seqK + (size_t)tg * DK + j);
-      const float qt = In<Tin>::load1(q + seqK + (size_t)tg * DK + j);
-      float p = 1.f;  // prod_{r=s+1..t} alpha_r
-      for (int s = t; s >= s0; --s) {
-        if (s < t) p *= In<Tin>::load1(al + seqK + (size_t)(t0 + s + 1) * DK + j);
-        const int e = s - s0;
-        if (e < 4) {
-          const float ks = In<Tin>::load1(k + seqK + (size_t)(t0 + s) * DK + j) * p;
-          if (s < t) aL[e] += kh * ks;
-          aM[e] += qt * ks;
-        }
-      }
-    }
-  }
-  lv = f32x4{aL[0], aL[1], aL[2], aL[3]};
-  mv = f32x4{aM[0], aM[1], aM[2], aM[3]};
-}
-
-// Off-diagonal pair index q -> (I, J), J < I.
-__device__ __forceinline__ void offpair_of(int q, int& I, int& J) {
-  I = 1;
-  while ((I + 1) * I / 2 <= q) ++I;
-  J = q - I * (I - 1) / 2;
-}
 
 constexpr int kThreads = 512;  // 8 waves: two per SIMD
 

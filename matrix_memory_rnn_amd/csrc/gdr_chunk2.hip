@@ -1,0 +1,841 @@
+// Two-kernel chunkwise forward of the channel-wise gated delta rule on gfx950.
+//
+// Method: "Muir: Linear Attention with Sensitivity-Allocated Gating and
+// Matched-Filter Readout", §2.1 eq.(1) in the chunkwise form of §2.2, with
+// the fused right-hand side [V^ | K^_pi] of §4.2. Per chunk of C tokens
+// starting from state S0:
+//   [U | Y] = T^{-1} [V^ | K^_pi],   V~ = U - Y S0,
+//   O = Q_pi S0 + M V~,   S_C = Diag(pi_C) S0 + K~^T V~
+// (T = I + L; L, M, Q_pi, K^_pi, K~ and pi_C as in gdr_chunk.hip). Only the
+// three products with S0 depend on the state, so the work is split:
+//
+//   gdn2_chunk_intra_kernel — every (b, h, chunk) independently, all chunks
+//     of all heads in parallel: block decay products, Gram tiles, T^{-1}
+//     applied to the d_v + d_k right-hand-side columns by block forward
+//     substitution. Writes one record per (b, h, chunk) to a caller-provided
+//     workspace: Y, U^T, M, Q_pi, K~^T (input precision) and pi_C (fp32).
+//   gdn2_chunk_scan_kernel — one workgroup per (b, h, value tile) walks the
+//     chunks of its head in order: V~ = U - Y S0, O, S. Its MFMA operands come
+//     from the record straight into registers, one chunk ahead.
+//
+// Compared with the single fused kernel this moves the S0-independent work
+// (about three quarters of it) off the sequential path and does it once per
+// chunk instead of once per value tile, at the price of writing and reading
+// the record once.
+#include "gdr_chunk_common.hpp"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+// Byte layout of the workspace record of one (b, h, chunk); es = element size.
+struct RecLayout {
+  int y, ut, m, qp, kt, pic, bytes;
+};
+__host__ __device__ __forceinline__ RecLayout rec_layout(int dk, int dv, int C, int es) {
+  RecLayout r;
+  r.y = 0;                          // Y      [t][j]  C x dk
+  r.ut = r.y + C * dk * es;         // U^T    [v][t]  dv x C
+  r.m = r.ut + dv * C * es;         // M      [t][s]  C x C (entries above the diagonal blocks unused)
+  r.qp = r.m + C * C * es;          // Q_pi   [t][j]  C x dk
+  r.kt = r.qp + C * dk * es;        // K~^T   [j][s]  dk x C
+  r.pic = r.kt + dk * C * es;       // pi_C   fp32    dk
+  r.bytes = r.pic + dk * 4;
+  return r;
+}
+
+// Stores of record entries from fp32 values.
+template <typename E> struct Out;
+template <> struct Out<float> {
+  static __device__ __forceinline__ void pair(float* p, float a, float b) { *(float2*)p = make_float2(a, b); }
+  static __device__ __forceinline__ void quad(float* p, f32x4 v) { *(f32x4*)p = v; }
+  static __device__ __forceinline__ void oct(float* p, const float* x) {
+    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+};
+template <> struct Out<__bf16> {
+  static __device__ __forceinline__ void pair(__bf16* p, float a, float b) {
+    bf16x2 h;
+    h.x = (__bf16)a;
+    h.y = (__bf16)b;
+    *(bf16x2*)p = h;
+  }
+  static __device__ __forceinline__ void quad(__bf16* p, f32x4 v) { In<__bf16>::store4(p, v); }
+  static __device__ __forceinline__ void oct(__bf16* p, const float* x) {
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (__bf16)x[e];
+    *(bf16x8*)p = h;
+  }
+};
+
+// ============================================================================ intra kernel
+constexpr int kIntraThreads = 512;
+constexpr int kMaxDv = 128;
+
+template <typename Tin, int DK, int CM>
+struct IntraSmem {
+  static constexpr bool F32 = std::is_same<Tin, float>::value;
+  static constexpr int NS = F32 ? 2 : 1;           // bf16 planes' worth of bytes per MM operand element
+  static constexpr int ES = sizeof(Tin);
+  static constexpr int NBM = CM / 16;
+  static constexpr int NPM = NBM * (NBM + 1) / 2;
+  static constexpr int LDK = DK + 8, LDC = CM + 8, LDB = 20, LDY = DK + 8;
+  static constexpr int P_CK = CM * LDK * 2;
+  static constexpr int P_CC = CM * LDC * 2;
+  static constexpr int P_XC = (kMaxDv + DK) * LDC * 2;
+  static constexpr int BLK = 16 * LDB * 4;
+  // [V^ | K^_pi]^T, solved in place, T mode [col][t]. With bf16 inputs it has
+  // a region of its own and is filled during prep, so no input register is
+  // live across the next item's prefetch; with fp32 (no prefetch) it lies
+  // over the prep / Gram operands to fit in 160 KiB.
+  static constexpr bool XR_EARLY = !F32;
+  static constexpr int XR_BYTES = 2 * P_XC;
+  static constexpr int AB = XR_EARLY ? XR_BYTES : 0;   // base of the phase A / phase B area
+  // phase A: prep and Gram operands
+  static constexpr int KR = AB;                     // k^ * P   [t][j]
+  static constexpr int QR = KR + NS * P_CK;         // q * P    [t][j]
+  static constexpr int KC = QR + NS * P_CK;         // k * Qs   [t][j]
+  static constexpr int A_END = KC + NS * P_CK;
+  // phase B (over phase A, after the Gram products)
+  static constexpr int LBK = AB;                    // L blocks fp32 [pair][t][s]
+  static constexpr int TBN = LBK + NPM * BLK;       // D_I fp32 [I][t][s]
+  static constexpr int TL = TBN + NBM * BLK;        // [.. -L'_IJ .. | D_I] rows, T mode [t][s]
+  static constexpr int XR = XR_EARLY ? 0 : TL + 2 * P_CC;
+  static constexpr int B_END = XR_EARLY ? TL + 2 * P_CC : XR + XR_BYTES;
+  // Y staging [t][j] (input precision): over the L / D_I blocks when they fit
+  // (dead once the solve starts), else a region of its own
+  static constexpr int YS_BYTES = CM * LDY * ES;
+  static constexpr bool YS_OVER = YS_BYTES <= TL - LBK;
+  static constexpr int YS = YS_OVER ? LBK : align16(imax(A_END, B_END));
+  static constexpr int X_END = YS_OVER ? imax(A_END, B_END) : YS + YS_BYTES;
+  static constexpr int SCL = align16(X_END);        // Gram scale vectors fp32 [pair][j]
+  static constexpr int GS = SCL + NPM * DK * 4;     // block totals fp32 [I][j]
+  static constexpr int FLAG = GS + NBM * DK * 4;    // guard flags [4]
+  static constexpr int TOTAL = FLAG + 16;
+  static_assert(TOTAL <= 160 * 1024, "intra kernel LDS exceeds 160 KiB");
+};
+
+template <typename Tin, int DK, int CM>
+__global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
+    char* __restrict__ ws, int T, int DV, int nchunks, int nitems) {
+  using L = IntraSmem<Tin, DK, CM>;
+  constexpr bool F32 = L::F32;
+  constexpr int MM = F32 ? kF32 : kBF;   // Gram operands
+  constexpr int MT = F32 ? kF32 : kSP;   // triangular solve
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NW = kIntraThreads / 64;
+  constexpr int NB = CM / 16;
+  constexpr int NP = L::NPM;
+  constexpr int NQ = NB * (NB - 1) / 2;
+  constexpr int MAXP = (NP + NW - 1) / NW;
+  constexpr int MAXQ = (NQ + NW - 1) / NW;
+  constexpr int MAXX = ((kMaxDv + DK) / 16 + NW - 1) / NW;
+  constexpr int MAXVI = (CM * kMaxDv / 8 + kIntraThreads - 1) / kIntraThreads;
+  constexpr int BLKF = 16 * L::LDB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(Tin));
+  const int NX = (DV + DK) / 16;
+
+  float* GS = (float*)(smem + L::GS);
+  float* SCL = (float*)(smem + L::SCL);
+  int* FLAGS = (int*)(smem + L::FLAG);
+  float* LBK = (float*)(smem + L::LBK);
+  float* TBN = (float*)(smem + L::TBN);
+  Tin* YS = (Tin*)(smem + L::YS);
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  if (tid < 4) FLAGS[tid] = 0;
+
+  // ---- input staging (as in the fused kernel): lanes l and l^32 share
+  // channels (j, j+1) of block I0, rows 0-7 (h = 0) and 8-15 (h = 1).
+  using RW = Raw<Tin>;
+  const int h = lane >> 5;
+  const int fp = wid * 32 + (lane & 31);
+  const bool act = fp < NB * (DK / 2);
+  const int I0 = act ? fp / (DK / 2) : 0, j = act ? 2 * (fp % (DK / 2)) : 0;
+  const int r0 = 16 * I0 + 8 * h;
+  // v^ items: 8 consecutive value columns of one row (coalesced loads)
+  const int nvi = CM * (DV / 8);
+  typename RW::R2 xa[8], xk[8], xb[8], xq[8];
+  typename RW::R8 xv[MAXVI], xw[MAXVI];
+  auto issue = [&](int it) {
+    const int bh = it / nchunks, tb = (it % nchunks) * CM;
+    const size_t sK = (size_t)bh * T * DK + j, sV = (size_t)bh * T * DV;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int t = tb + r0 + r;
+      const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
+      xa[r] = RW::ld2(alpha + off);
+      xk[r] = RW::ld2(k + off);
+      xb[r] = RW::ld2(bgate + off);
+      xq[r] = RW::ld2(q + off);
+    }
+#pragma unroll
+    for (int i = 0; i < MAXVI; ++i) {
+      const int idx = tid + kIntraThreads * i;
+      const int vi = idx < nvi ? idx : 0;
+      const int vrow = vi / (DV / 8), vcol = (vi % (DV / 8)) * 8;
+      const int tv = tb + vrow;
+      const size_t off = sV + (size_t)(tv < T ? tv : T - 1) * DV + vcol;
+      xv[i] = RW::ld8(v + off);
+      xw[i] = RW::ld8(wgate + off);
+    }
+  };
+  // bf16: the next item's inputs are fetched during this item's Gram products;
+  // fp32 (twice the registers) fetches at the start of each item.
+  if constexpr (!F32) issue(item);
+  __syncthreads();
+
+  for (; item < nitems; item += gridDim.x) {
+    if constexpr (F32) issue(item);
+    const int bh = item / nchunks, t0 = (item % nchunks) * CM;
+    const size_t seqK = (size_t)bh * T * DK;
+    char* rec = ws + (size_t)item * RL.bytes;
+    Tin* Yg = (Tin*)(rec + RL.y);
+    Tin* UTg = (Tin*)(rec + RL.ut);
+    Tin* Mg = (Tin*)(rec + RL.m);
+    Tin* QPg = (Tin*)(rec + RL.qp);
+    Tin* KTg = (Tin*)(rec + RL.kt);
+    float* PICg = (float*)(rec + RL.pic);
+
+    // identity padding past the end of the sequence: alpha = 1, k = b = q = 0, v = w = 0
+    float vh[MAXVI][8];
+    {
+      const typename RW::R2 one = RW::pad2(1.f), zero = RW::pad2(0.f);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool ok = t0 + r0 + r < T;
+        xa[r] = RW::sel(ok, xa[r], one);
+        xk[r] = RW::sel(ok, xk[r], zero);
+        xb[r] = RW::sel(ok, xb[r], zero);
+        xq[r] = RW::sel(ok, xq[r], zero);
+      }
+#pragma unroll
+      for (int i = 0; i < MAXVI; ++i) {
+        const int idx = tid + kIntraThreads * i;
+        const bool okv = idx < nvi && t0 + idx / (DV / 8) < T;
+        float fv[8], fw[8];
+        RW::un8(xv[i], fv);
+        RW::un8(xw[i], fw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vh[i][e] = okv ? fv[e] * fw[e] : 0.f;
+      }
+    }
+
+    if constexpr (L::XR_EARLY) {
+#pragma unroll
+      for (int i = 0; i < MAXVI; ++i) {
+        const int idx = tid + kIntraThreads * i;
+        if (idx < nvi) {
+          const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, (vcol + e) * L::LDC + vrow, vh[i][e]);
+        }
+      }
+    }
+
+    // ================= prep 1: half-block products -> block totals G
+    float2 ph = make_float2(1.f, 1.f);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float2 a = RW::un2(xa[r]);
+      ph.x *= a.x;
+      ph.y *= a.y;
+    }
+    const float2 po = make_float2(__shfl_xor(ph.x, 32, 64), __shfl_xor(ph.y, 32, 64));
+    const float2 p0 = h ? po : ph, p1 = h ? ph : po;
+    if (act && h == 0) {
+      const float gx = p0.x * p1.x, gy = p0.y * p1.y;
+      GS[I0 * DK + j] = gx;
+      GS[I0 * DK + j + 1] = gy;
+      if (!(gx >= kGuardMin && gy >= kGuardMin)) FLAGS[I0] = 1;
+    }
+    __syncthreads();
+
+    // ================= prep 2: Gram operands, Q_pi, K~^T, pi_C, scale vectors
+    float2 khp[8];
+    if (act) {
+      float2 Bst = make_float2(1.f, 1.f), E = make_float2(1.f, 1.f), pic = make_float2(1.f, 1.f);
+      for (int J = 0; J < NB; ++J) {
+        const float gx = GS[J * DK + j], gy = GS[J * DK + j + 1];
+        if (J < I0) { Bst.x *= gx; Bst.y *= gy; }
+        if (J > I0) { E.x *= gx; E.y *= gy; }
+        pic.x *= gx;
+        pic.y *= gy;
+      }
+      if (h == 0) {
+        if (I0 == 0) *(float2*)(PICg + j) = pic;
+        const float gx = GS[I0 * DK + j], gy = GS[I0 * DK + j + 1];
+        SCL[pidx(I0, I0) * DK + j] = __builtin_amdgcn_rcpf(gx);
+        SCL[pidx(I0, I0) * DK + j + 1] = __builtin_amdgcn_rcpf(gy);
+        float2 d = make_float2(1.f, 1.f);
+        for (int J = I0 - 1; J >= 0; --J) {
+          SCL[pidx(I0, J) * DK + j] = d.x;
+          SCL[pidx(I0, J) * DK + j + 1] = d.y;
+          d.x *= GS[J * DK + j];
+          d.y *= GS[J * DK + j + 1];
+        }
+      }
+      float2 P = h ? p0 : make_float2(1.f, 1.f);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float2 a = RW::un2(xa[r]), kk = RW::un2(xk[r]), bb = RW::un2(xb[r]), qq = RW::un2(xq[r]);
+        P.x *= a.x;
+        P.y *= a.y;
+        const float krx = bb.x * kk.x * P.x, kry = bb.y * kk.y * P.y;
+        const float qrx = qq.x * P.x, qry = qq.y * P.y;
+        const int off = (r0 + r) * L::LDK + j;
+        st2<MM>(smem + L::KR, L::P_CK, off, krx, kry);
+        st2<MM>(smem + L::QR, L::P_CK, off, qrx, qry);
+        khp[r] = make_float2(Bst.x * krx, Bst.y * kry);
+        Out<Tin>::pair(QPg + (r0 + r) * DK + j, Bst.x * qrx, Bst.y * qry);
+      }
+      float ktx[8], kty[8];
+      float2 qs = h ? make_float2(1.f, 1.f) : p1;
+#pragma unroll
+      for (int r = 7; r >= 0; --r) {
+        const float2 kk = RW::un2(xk[r]), a = RW::un2(xa[r]);
+        const float kcx = kk.x * qs.x, kcy = kk.y * qs.y;
+        st2<MM>(smem + L::KC, L::P_CK, (r0 + r) * L::LDK + j, kcx, kcy);
+        ktx[r] = kcx * E.x;
+        kty[r] = kcy * E.y;
+        qs.x *= a.x;
+        qs.y *= a.y;
+      }
+      Out<Tin>::oct(KTg + j * CM + r0, ktx);
+      Out<Tin>::oct(KTg + (j + 1) * CM + r0, kty);
+      if constexpr (L::XR_EARLY) {
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          const float2* kp = khp + 4 * r4;
+          st4<MT>(smem + L::XR, L::P_XC, (DV + j) * L::LDC + r0 + 4 * r4,
+                  f32x4{kp[0].x, kp[1].x, kp[2].x, kp[3].x});
+          st4<MT>(smem + L::XR, L::P_XC, (DV + j + 1) * L::LDC + r0 + 4 * r4,
+                  f32x4{kp[0].y, kp[1].y, kp[2].y, kp[3].y});
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (!F32) {
+      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x);
+    }
+
+    // ================= Gram tiles: L^T, M^T of pair (I, J) = (Kc_J * scale) [Kr_I; Qr_I]^T
+    f32x4 gL[MAXP], gM[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+      gL[i] = f4zero();
+      gM[i] = f4zero();
+      const int p = wid + NW * i;
+      if (p < NP) {
+        int I, J;
+        pair_of(p, I, J);
+        const bool scaled = (I == J) || (I > J + 1);
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+          Frag<MM> A = ldfrag<MM>(smem + L::KC, L::P_CK, L::LDK, 16 * J, k0, DK, lane);
+          const int kk = k0 + 8 * g;
+          if (scaled && kk < DK) {
+            const float* sp = SCL + p * DK + kk;
+            const f32x4 s0 = *(const f32x4*)sp, s1 = *(const f32x4*)(sp + 4);
+            const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            scale_frag<MM>(A, sv);
+          }
+          Frag<MM> BL = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+          Frag<MM> BM = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+          mma<MM>(gL[i], A, BL);
+          mma<MM>(gM[i], A, BM);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ================= L blocks (fp32, LDS), M (record), right-hand sides [V^ | K^_pi]^T
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+      const int p = wid + NW * i;
+      if (p < NP) {
+        int I, J;
+        pair_of(p, I, J);
+        const int t = 16 * I + c16, s0 = 16 * J + 4 * g;
+        f32x4 lv = gL[i], mv = gM[i];
+        if (I == J) {
+          if (FLAGS[I]) exact_diag<Tin, DK>(k, bgate, q, alpha, seqK, t0, T, t, s0, lv, mv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (s0 + e >= t) lv[e] = 0.f;
+            if (s0 + e > t) mv[e] = 0.f;
+          }
+        }
+        *(f32x4*)(LBK + p * BLKF + c16 * L::LDB + 4 * g) = lv;
+        Out<Tin>::quad(Mg + t * CM + s0, mv);
+      }
+    }
+    if constexpr (!L::XR_EARLY) {
+#pragma unroll
+      for (int i = 0; i < MAXVI; ++i) {
+        const int idx = tid + kIntraThreads * i;
+        if (idx < nvi) {
+          const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, (vcol + e) * L::LDC + vrow, vh[i][e]);
+        }
+      }
+    }
+    if (!L::XR_EARLY && act) {
+#pragma unroll
+      for (int r4 = 0; r4 < 2; ++r4) {
+        const float2* kp = khp + 4 * r4;
+        st4<MT>(smem + L::XR, L::P_XC, (DV + j) * L::LDC + r0 + 4 * r4,
+                f32x4{kp[0].x, kp[1].x, kp[2].x, kp[3].x});
+        st4<MT>(smem + L::XR, L::P_XC, (DV + j + 1) * L::LDC + r0 + 4 * r4,
+                f32x4{kp[0].y, kp[1].y, kp[2].y, kp[3].y});
+      }
+    }
+    __syncthreads();
+
+    // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0)
+    if (wid == 0) {
+      if (tid < 4) FLAGS[tid] = 0;  // read above; set again by the next item's prep 1
+      const int I = g, cc = c16;
+      const bool live = I < NB;
+      const float* Lb = LBK + (live ? pidx(I, I) : 0) * BLKF;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc0 = (r == cc) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int m4 = 0; 4 * m4 < r; ++m4) {
+          const f32x4 lv = *(const f32x4*)(Lb + r * L::LDB + 4 * m4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 4 * m4 + e;
+            if (m < r) {
+              if (m & 1) acc1 -= lv[e] * x[m];
+              else acc0 -= lv[e] * x[m];
+            }
+          }
+        }
+        x[r] = acc0 + acc1;
+      }
+      if (live) {
+        float* Tn = TBN + I * BLKF;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          Tn[r * L::LDB + cc] = x[r];
+          st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ================= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL
+#pragma unroll
+    for (int i = 0; i < MAXQ; ++i) {
+      const int qq = wid + NW * i;
+      if (qq < NQ) {
+        int I, J;
+        offpair_of(qq, I, J);
+        const int p = pidx(I, J);
+        const bool ok = g < 2;
+        Frag<MT> A = frag_f32<MT>(TBN + I * BLKF + c16 * L::LDB + 8 * (g & 1), ok);
+        float lc[8];
+        const float* lb = LBK + p * BLKF + c16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lc[e] = ok ? lb[(8 * (g & 1) + e) * L::LDB] : 0.f;
+        Frag<MT> B = frag_f32<MT>(lc, true);
+        f32x4 acc = f4zero();
+        mma<MT>(acc, A, B);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
+      }
+    }
+    __syncthreads();
+
+    // ================= block forward substitution over all d_v + d_k columns, in place:
+    // X_I = D_I R_I - sum_{J<I} L'_IJ X_J. U^T goes to the record, Y to the staging rows.
+    for (int I = 0; I < NB; ++I) {
+      const int kend = 16 * (I + 1);
+      f32x4 acc[MAXX];
+#pragma unroll
+      for (int i = 0; i < MAXX; ++i) acc[i] = f4zero();
+#pragma unroll
+      for (int k0 = 0; k0 < CM; k0 += 32) {
+        if (k0 < kend) {
+          Frag<MT> A = ldfrag<MT>(smem + L::TL, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
+#pragma unroll
+          for (int i = 0; i < MAXX; ++i) {
+            const int ct = wid + NW * i;
+            if (ct < NX) {
+              Frag<MT> B = ldfrag<MT>(smem + L::XR, L::P_XC, L::LDC, 16 * ct, k0, kend, lane);
+              mma<MT>(acc[i], A, B);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < MAXX; ++i) {
+        const int ct = wid + NW * i;
+        if (ct < NX) {
+          st4<MT>(smem + L::XR, L::P_XC, (16 * ct + c16) * L::LDC + 16 * I + 4 * g, acc[i]);
+          if (16 * ct < DV) {
+            Out<Tin>::quad(UTg + (16 * ct + c16) * CM + 16 * I + 4 * g, acc[i]);
+          } else {
+            const int jj = 16 * ct - DV + c16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) YS[(16 * I + 4 * g + e) * L::LDY + jj] = (Tin)acc[i][e];
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+    __syncthreads();
+
+    // ================= Y rows to the record (16-byte pieces)
+    constexpr int YPR = DK * (int)sizeof(Tin) / 16;  // 16-byte pieces per row
+    for (int idx = tid; idx < CM * YPR; idx += kIntraThreads) {
+      const int t = idx / YPR, pc = idx % YPR;
+      *(u32x4*)((char*)(Yg + t * DK) + 16 * pc) = *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc);
+    }
+  }
+}
+
+// ============================================================================ scan kernel
+constexpr int kScanThreads = 512;
+
+// One 8-element operand slice of a k-contiguous record matrix (global memory),
+// loaded unconditionally (from `safe` when the slice lies outside the matrix).
+// Padding slices are zeroed where the operand is used (zsel): branch-free
+// loads with no use until then let the compiler count outstanding loads
+// exactly, so a prefetch is not waited for early.
+template <int MODE, typename E>
+__device__ __forceinline__ Frag<MODE> gfrag(const E* p, const E* safe, bool valid) {
+  const E* a = valid ? p : safe;
+  Frag<MODE> f;
+  if constexpr (MODE == kF32) {
+    f.a = *(const f32x4*)a;
+    f.b = *(const f32x4*)(a + 4);
+  } else {
+    f.hi = *(const bf16x8*)a;
+  }
+  return f;
+}
+
+template <int MODE>
+__device__ __forceinline__ Frag<MODE> zsel(bool valid, const Frag<MODE>& x) {
+  if (valid) return x;
+  Frag<MODE> z;
+  if constexpr (MODE == kF32) {
+    z.a = f4zero();
+    z.b = f4zero();
+  } else {
+    z.hi = bf16x8{};
+  }
+  return z;
+}
+
+template <typename Tin, int DK, int VT, int CM>
+__global__ __launch_bounds__(kScanThreads, 1) void gdn2_chunk_scan_kernel(
+    const char* __restrict__ ws, const float* __restrict__ S0, Tin* __restrict__ o, float* S_out,
+    int T, int DV) {
+  constexpr bool F32 = std::is_same<Tin, float>::value;
+  constexpr int MM = F32 ? kF32 : kBF;
+  constexpr int NW = kScanThreads / 64;
+  constexpr int NVL = VT / 16;
+  constexpr int NST = (DK / 16) * NVL;              // S tiles (j-block, value block)
+  constexpr int MAXS = (NST + NW - 1) / NW;
+  constexpr int NT = (CM / 16) * NVL;               // V~ / O tiles (t-block, value block)
+  constexpr int MAXV = (NT + NW - 1) / NW;
+  constexpr int KS = DK >= 32 ? DK / 32 : 1;        // 32-wide k steps over d_k
+  constexpr int KSC = CM >= 32 ? CM / 32 : 1;       // 32-wide k steps over the chunk
+  constexpr int LDK = DK + 8, LDC = CM + 8;
+  constexpr int NSP = F32 ? 2 : 1;
+  constexpr int P_VK = VT * LDK * 2, P_VC = VT * LDC * 2;
+  __shared__ __attribute__((aligned(16))) char smem[NSP * (P_VK + P_VC)];
+  char* S0T = smem;                                 // S0^T  [v][j]
+  char* VTT = smem + NSP * P_VK;                    // V~^T  [v][t]
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nvt = DV / VT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
+  const int nchunks = (T + CM - 1) / CM;
+  const size_t stOff = (size_t)bh * DK * DV;
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(Tin));
+  const char* wsh = ws + (size_t)bh * nchunks * RL.bytes;
+
+  // ---- state tile in registers (fp32), S0^T in LDS
+  f32x4 Sacc[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    Sacc[i] = f4zero();
+    const int tile = wid + NW * i;
+    if (tile < NST) {
+      const int jt = tile / NVL, vl = tile % NVL;
+      if (S0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Sacc[i][e] = S0[stOff + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16];
+      }
+      st4<MM>(S0T, P_VK, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+    }
+  }
+
+  // ---- per-chunk operand fragments. V~/O tile i of this wave is (t-block I,
+  // value block vl); S tile i is (j-block jt, value block vl).
+  struct Ops {
+    Frag<MM> y[MAXV][KS];    // Y rows t (A of Y S0)
+    Frag<MM> qp[MAXV][KS];   // Q_pi rows t (B of S0^T Q_pi^T)
+    Frag<MM> m[MAXV][KSC];   // M rows t (B of V~^T M^T)
+    typename Raw<Tin>::R4 u[MAXV];  // U[t..t+3][v] from U^T, undecoded until use
+    Frag<MM> kt[MAXS][KSC];  // K~^T rows j (A of K~^T V~)
+    f32x4 pc[MAXS];          // pi_C[j..j+3]
+  };
+  auto fetch = [&](int ch, Ops& x) {
+    const char* rec = wsh + (size_t)ch * RL.bytes;
+    const Tin* Yp = (const Tin*)(rec + RL.y);
+    const Tin* UTp = (const Tin*)(rec + RL.ut);
+    const Tin* Mp = (const Tin*)(rec + RL.m);
+    const Tin* QPp = (const Tin*)(rec + RL.qp);
+    const Tin* KTp = (const Tin*)(rec + RL.kt);
+    const float* PCp = (const float*)(rec + RL.pic);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int tile = wid + NW * i;
+      const bool ok = tile < NT;
+      const int I = ok ? tile / NVL : 0, vl = ok ? tile % NVL : 0;
+      const int t = 16 * I + c16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int kk = 32 * s + 8 * g;
+        x.y[i][s] = gfrag<MM>(Yp + t * DK + kk, Yp, ok && kk < DK);
+        x.qp[i][s] = gfrag<MM>(QPp + t * DK + kk, QPp, ok && kk < DK);
+      }
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        const int kk = 32 * s + 8 * g;
+        x.m[i][s] = gfrag<MM>(Mp + t * CM + kk, Mp, ok && kk < 16 * (I + 1));
+      }
+      const Tin* up = UTp + (vt0 + 16 * vl + c16) * CM + 16 * I + 4 * g;
+      x.u[i] = Raw<Tin>::ld4(up);                          // unused when !ok (then I = vl = 0)
+    }
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + NW * i;
+      const bool ok = tile < NST;
+      const int jt = ok ? tile / NVL : 0;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        const int kk = 32 * s + 8 * g;
+        x.kt[i][s] = gfrag<MM>(KTp + (16 * jt + c16) * CM + kk, KTp, ok && kk < CM);
+      }
+      x.pc[i] = *(const f32x4*)(PCp + 16 * jt + 4 * g);   // jt = 0 when unused
+    }
+  };
+
+  // one chunk: V~ = U - Y S0 -> V~^T (LDS) and O^T = S0^T Q_pi^T; then
+  // O^T += V~^T M^T, store O; S <- Diag(pi_C) S + K~^T V~, S^T -> LDS
+  auto step = [&](int ch, const Ops& cur) {
+    const int t0 = ch * CM;
+    f32x4 oacc[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      oacc[i] = f4zero();
+      const int tile = wid + NW * i;
+      if (tile < NT) {
+        const int I = tile / NVL, vl = tile % NVL;
+        f32x4 acc = f4zero();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          Frag<MM> Sf = ldfrag<MM>(S0T, P_VK, LDK, 16 * vl, 32 * s, DK, lane);
+          const bool kv = 32 * s + 8 * g < DK;
+          mma<MM>(acc, zsel<MM>(kv, cur.y[i][s]), Sf);      // rows t, cols v
+          mma<MM>(oacc[i], Sf, zsel<MM>(kv, cur.qp[i][s])); // rows v, cols t
+        }
+        // acc[e] = (Y S0)[16I + 4g + e][16vl + c16]; u[e] = U[16I + 4g + e][16vl + c16]
+        const f32x4 u = Raw<Tin>::un4(cur.u[i]);
+        f32x4 vt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[e] = u[e] - acc[e];
+        st4<MM>(VTT, P_VC, (16 * vl + c16) * LDC + 16 * I + 4 * g, vt);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int tile = wid + NW * i;
+      if (tile < NT) {
+        const int I = tile / NVL, vl = tile % NVL, kend = 16 * (I + 1);
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          if (32 * s < kend) {
+            Frag<MM> A = ldfrag<MM>(VTT, P_VC, LDC, 16 * vl, 32 * s, kend, lane);
+            mma<MM>(oacc[i], A, zsel<MM>(32 * s + 8 * g < kend, cur.m[i][s]));
+          }
+        }
+        // oacc[e] = O[t = 16I + c16][v = 16vl + 4g + e]
+        const int t = t0 + 16 * I + c16;
+        if (t < T) In<Tin>::store4(o + ((size_t)bh * T + t) * DV + vt0 + 16 * vl + 4 * g, oacc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + NW * i;
+      if (tile < NST) {
+        const int jt = tile / NVL, vl = tile % NVL;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[i][e] *= cur.pc[i][e];
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          Frag<MM> B = ldfrag<MM>(VTT, P_VC, LDC, 16 * vl, 32 * s, CM, lane);
+          mma<MM>(Sacc[i], zsel<MM>(32 * s + 8 * g < CM, cur.kt[i][s]), B);
+        }
+        st4<MM>(S0T, P_VK, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+      }
+    }
+    __syncthreads();
+  };
+
+  if constexpr (F32) {
+    // fp32 operands take twice the registers: no prefetch
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+      Ops cur;
+      fetch(ch, cur);
+      step(ch, cur);
+    }
+  } else {
+    // two operand sets used in turn (no register copies), each filled one
+    // chunk ahead of its use
+    Ops opA, opB;
+    fetch(0, opA);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ch += 2) {
+      if (ch + 1 < nchunks) fetch(ch + 1, opB);
+      step(ch, opA);
+      if (ch + 1 >= nchunks) break;
+      if (ch + 2 < nchunks) fetch(ch + 2, opA);
+      step(ch + 1, opB);
+    }
+  }
+
+  if (S_out) {
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + NW * i;
+      if (tile < NST) {
+        const int jt = tile / NVL, vl = tile % NVL;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          S_out[stOff + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[i][e];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host launch
+size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  const int es = dtype == GDR_BF16 ? 2 : 4;
+  const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
+  return (size_t)B * H * nchunks * (size_t)rec_layout(dk, dv, chunk, es).bytes;
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <typename Tin, int DK, int CM>
+static int launch_intra(const ChunkArgs& a, char* ws) {
+  using L = IntraSmem<Tin, DK, CM>;
+  auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
+        hipSuccess)
+      return GDR_ERR_LAUNCH;
+    attr_set = true;
+  }
+  int nchunks = (a.T + CM - 1) / CM;
+  int nitems = a.B * a.H * nchunks;
+  // one resident workgroup per CU, each walking items with a stride of the grid
+  const int grid = nitems < device_cus() ? nitems : device_cus();
+  const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
+  const Tin *al = (const Tin*)a.alpha, *bg = (const Tin*)a.b, *wg = (const Tin*)a.w;
+  int T = a.T, DV = a.dv;
+  void* args[] = {&q, &k, &v, &al, &bg, &wg, &ws, &T, &DV, &nchunks, &nitems};
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(grid), dim3(kIntraThreads), args, L::TOTAL,
+                                 (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+template <typename Tin, int DK, int VT, int CM>
+static int launch_scan(const ChunkArgs& a, const char* ws) {
+  auto kern = gdn2_chunk_scan_kernel<Tin, DK, VT, CM>;
+  const int nblocks = a.B * a.H * (a.dv / VT);
+  const float* S0 = a.S0;
+  Tin* o = (Tin*)a.o;
+  float* So = a.S_out;
+  int T = a.T, DV = a.dv;
+  void* args[] = {&ws, &S0, &o, &So, &T, &DV};
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(kScanThreads), args, 0,
+                                 (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+template <typename Tin, int DK, int CM>
+static int launch_pair(const ChunkArgs& a, char* ws) {
+  int st = launch_intra<Tin, DK, CM>(a, ws);
+  if (st != GDR_OK) return st;
+  // value tiles of 32 columns when that still gives a workgroup per CU, else 16
+  const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= device_cus();
+  if constexpr (std::is_same<Tin, float>::value) {
+    return launch_scan<Tin, DK, 16, CM>(a, ws);
+  } else {
+    if (!wide) return launch_scan<Tin, DK, 16, CM>(a, ws);
+    return launch_scan<Tin, DK, 32, CM>(a, ws);
+  }
+}
+
+template <typename Tin, int CM>
+static int dispatch_dk(const ChunkArgs& a, char* ws) {
+  switch (a.dk) {
+    case 16: return launch_pair<Tin, 16, CM>(a, ws);
+    case 32: return launch_pair<Tin, 32, CM>(a, ws);
+    case 64: return launch_pair<Tin, 64, CM>(a, ws);
+    case 128: return launch_pair<Tin, 128, CM>(a, ws);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+template <typename Tin>
+static int dispatch_chunk(const ChunkArgs& a, char* ws) {
+  switch (a.chunk) {
+    case 16: return dispatch_dk<Tin, 16>(a, ws);
+    case 32: return dispatch_dk<Tin, 32>(a, ws);
+    case 64: return dispatch_dk<Tin, 64>(a, ws);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws) {
+  if (a.dtype == GDR_BF16) return dispatch_chunk<__bf16>(a, (char*)ws);
+  return dispatch_chunk<float>(a, (char*)ws);
+}
+
+}  // namespace gdr

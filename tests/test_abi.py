@@ -33,7 +33,8 @@ def lib():
 
 def test_header_declares_the_three_entry_points():
     names = _declared()
-    for n in ("gdr_chunk_fwd", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_status_string", "gdr_version"):
+    for n in ("gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_decode_step",
+              "gdr_mlstm_fwd", "gdr_status_string", "gdr_version"):
         assert n in names
 
 
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 def test_symbols_resolve_through_dlopen(lib):
     for n in _declared():
         assert hasattr(lib, n)
-    assert lib.gdr_version() == 100
+    assert lib.gdr_version() == 200
 
 
 def test_status_strings(lib):
@@ -87,6 +88,47 @@ def test_chunk_validation(lib):
     assert _chunk(lib, ptrs=P[:6] + [P[0] + 64]) == c["GDR_ERR_ALIAS"]
     # S_out overlapping (but not equal to) S0
     assert _chunk(lib, S0=P[8], S_out=P[8] + 256) == c["GDR_ERR_ALIAS"]
+
+
+def _ws_size(lib, B=1, H=2, T=64, dk=16, dv=16, chunk=16, dtype=1):
+    n = ctypes.c_size_t(123)
+    st = lib.gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size(lib):
+    c = _codes()
+    # one record per (b, h, chunk): C*dk (Y) + dv*C (U^T) + C*C (M) + C*dk (Q_pi) + dk*C (K~^T)
+    # elements of the input dtype, then dk float32 (pi_C)
+    for (B, H, T, dk, dv, C, dt) in ((1, 2, 64, 16, 16, 16, 1), (4, 16, 4096, 128, 128, 64, 1),
+                                     (2, 3, 333, 64, 32, 32, 0)):
+        es = 2 if dt == 1 else 4
+        rec = (3 * C * dk + dv * C + C * C) * es + 4 * dk
+        st, n = _ws_size(lib, B, H, T, dk, dv, C, dt)
+        assert st == c["GDR_OK"] and n == B * H * ((T + C - 1) // C) * rec
+    assert _ws_size(lib, T=0) == (c["GDR_ERR_SHAPE"], 0)
+    assert _ws_size(lib, chunk=48)[0] == c["GDR_ERR_UNSUPPORTED"]
+    assert lib.gdr_chunk_workspace_size(1, 1, 1, 16, 16, 16, 1, None) == c["GDR_ERR_NULL"]
+
+
+def test_chunk_ws_validation(lib):
+    c = _codes()
+    need = _ws_size(lib)[1]
+
+    def f(ws=P[10], nbytes=None, ptrs=None, dtype=1, dk=16, chunk=16):
+        p = list(P[:7]) if ptrs is None else ptrs
+        return lib.gdr_chunk_fwd_ws(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], None,
+                                    1, 2, 64, dk, 16, chunk, dtype, ws, need if nbytes is None else nbytes, None)
+
+    assert f(ws=None) == c["GDR_ERR_NULL"]
+    assert f(ws=P[10] + 8) == c["GDR_ERR_ALIGN"]
+    assert f(nbytes=need - 1) == c["GDR_ERR_WORKSPACE"]
+    assert f(ws=P[2] + 1024) == c["GDR_ERR_ALIAS"]          # workspace inside v
+    assert f(chunk=24) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(ptrs=[None] + P[1:7]) == c["GDR_ERR_NULL"]
+    # the fused kernel's fp32 chunk limit does not apply here: validation passes
+    # up to the launch, which is not reached because the pointers are checked first
+    assert f(ws=P[0]) == c["GDR_ERR_ALIAS"]
 
 
 def test_decode_validation(lib):
