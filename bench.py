@@ -1,17 +1,20 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-A step is one call of ``gdr_chunk_fwd`` over the 4K-token workload:
+A step is one forward over the 4K-token workload through the two-kernel
+entry points (``gdr_chunk_intra`` then ``gdr_chunk_scan``, which together
+are ``gdr_chunk_fwd_ws``):
 B=4 sequences x H=16 heads x T=4096 tokens, d_k = d_v = 128, chunk 64,
 bfloat16 inputs and outputs, float32 state, S0 = 0, inputs resident in HBM.
 Inputs are seeded synthetic data with the shapes and gate distributions of
 the Muir page's models (q, k = unit-norm SiLU of N(0,1); v ~ N(0,1);
 alpha = sigmoid(N(4, 1.5)); b, w = sigmoid(N(0,1))).
 
-Printed: one JSON line with tokens/s (value), the chunk kernel's roofline
-position (HBM-bound by algorithmic arithmetic intensity ~77 flop/B), its MFMA
-throughput as a fraction of the bf16 dense peak, side measurements for the
-decode step (HBM GB/s) and the mLSTM forward, and the float64 CPU oracle timed
-on a bounded sample of the same workload.
+Printed: one JSON line with tokens/s (value); the roofline position of the
+dominant kernel (HBM-bound; its compulsory bytes per launch over its mean
+event-timed duration) and of each kernel; the path's algorithmic bytes and
+MFMA throughput against the MI355X peaks; side measurements for the fused
+single-kernel entry point, the decode step (HBM GB/s) and the mLSTM forward;
+and the float64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -53,7 +56,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(name, launches_key="chunk_fwd_4k"):
+def load_traffic(name, launches_key):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None
     when missing or taken on different kernel sources."""
     p = os.path.join(ROOT, "profiles", "counters.json")
@@ -95,23 +98,66 @@ def time_launches(fn, steps, warmup):
     return region, per
 
 
-def bench_chunk(steps, warmup):
+def chunk_inputs():
     import torch
-    import matrix_memory_rnn_amd as gdr
     from synth import CONFIGS, gdn2_inputs
     c = CONFIGS["chunk_4k"]
-    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
-    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=c["alpha_mu"], alpha_sigma=c["alpha_sigma"], seed=0,
-                    dtype="bf16")
+    d = gdn2_inputs(c["B"], c["H"], c["T"], c["dk"], c["dv"], alpha_mu=c["alpha_mu"],
+                    alpha_sigma=c["alpha_sigma"], seed=0, dtype="bf16")
     x = [to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v", "alpha", "b", "w")]
+    return c, d, x
+
+
+def bench_chunk(steps, warmup, c, x):
+    """One step = gdr_chunk_intra then gdr_chunk_scan (= gdr_chunk_fwd_ws) on
+    the 4K workload, with events around each kernel inside the timed region."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    nws = gdr.gdr_chunk_workspace_size(B, H, T, dk, dv, C, torch.bfloat16)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdr.gdr_chunk_intra(*x, chunk=C, workspace=ws)
+        gdr.gdr_chunk_scan(ws, None, o, S, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for e in ev:
+        e[0].record()
+        gdr.gdr_chunk_intra(*x, chunk=C, workspace=ws)
+        e[1].record()
+        gdr.gdr_chunk_scan(ws, None, o, S, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C)
+        e[2].record()
+    t1.record()
+    torch.cuda.synchronize()
+    region = t0.elapsed_time(t1) / steps
+    intra_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    n = B * H * T
+    intra_bytes = n * (4 * dk + 2 * dv) * 2 + nws          # inputs read, workspace written
+    scan_bytes = nws + n * dv * 2 + B * H * dk * dv * 4       # workspace read, o and S_T written
+    flops = chunk_flops_per_chunk(C, dk, dv) * (T // C) * B * H
+    return dict(B=B, H=H, T=T, dk=dk, dv=dv, C=C, region_ms=region, intra_ms=intra_ms, scan_ms=scan_ms,
+                intra_bytes=intra_bytes, scan_bytes=scan_bytes, ws_bytes=nws, flops=flops,
+                bytes=chunk_bytes(B, H, T, dk, dv, 2))
+
+
+def bench_fused(steps, warmup, c, x):
+    """The single-kernel entry point gdr_chunk_fwd on the same workload."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
     o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda")
     S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
     fn = lambda: gdr.gdr_chunk_fwd(*x, None, chunk=C, o=o, S_out=S)
-    region_ms, launch_ms = time_launches(fn, steps, warmup)
-    flops = chunk_flops_per_chunk(C, dk, dv) * (T // C) * B * H
-    nbytes = chunk_bytes(B, H, T, dk, dv, 2)
-    return dict(B=B, H=H, T=T, dk=dk, dv=dv, C=C, region_ms=region_ms, launch_ms=launch_ms,
-                flops=flops, bytes=nbytes, inputs=d)
+    return time_launches(fn, steps, warmup)
 
 
 def bench_decode(steps=1024):
@@ -204,12 +250,23 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    r = bench_chunk(args.steps, args.warmup)
+    c, d, x = chunk_inputs()
+    r = bench_chunk(args.steps, args.warmup, c, x)
     tokens = r["B"] * r["T"]
     value = tokens / (r["region_ms"] * 1e-3)
-    achieved = r["bytes"] / (r["launch_ms"] * 1e-3) / 1e9
-    traffic = load_traffic("chunk_fwd_4k")
-    tflops = r["flops"] / (r["launch_ms"] * 1e-3) / 1e12
+    kern = {
+        "intra": {"ms": r["intra_ms"], "bytes": r["intra_bytes"],
+                  "GB/s": r["intra_bytes"] / (r["intra_ms"] * 1e-3) / 1e9,
+                  "traffic": load_traffic("intra", "chunk_intra_4k")},
+        "scan": {"ms": r["scan_ms"], "bytes": r["scan_bytes"],
+                 "GB/s": r["scan_bytes"] / (r["scan_ms"] * 1e-3) / 1e9,
+                 "traffic": load_traffic("scan", "chunk_scan_4k")},
+    }
+    for v in kern.values():
+        v["frac_hbm"] = v["GB/s"] / PEAK_HBM_GBS
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    path_gbs = r["bytes"] / (r["region_ms"] * 1e-3) / 1e9
+    tflops = r["flops"] / (r["region_ms"] * 1e-3) / 1e12
     out = {
         "metric": "tokens/s + % bf16 MFMA peak, chunk fwd H=16 d=128 T=4K; decode HBM GB/s",
         "value": value,
@@ -225,15 +282,20 @@ def main():
         "data": "synthetic (seeded; gate distributions of the Muir page's models)",
         "config": {"workload": "gdn2 chunk fwd B=4 H=16 T=4096 dk=dv=128 C=64, bf16 in/out, fp32 state, S0=0",
                    "global_batch": r["B"], "seq_len": r["T"], "heads": r["H"], "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "roofline": {"bound": "hbm", "kernel": f"gdn2_chunk_{dom}", "achieved": kern[dom]["GB/s"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm"],
+                     "traffic": kern[dom]["traffic"], "bytes_per_launch": kern[dom]["bytes"]},
+        "kernels": kern,
+        "path": {"algorithmic_bytes": r["bytes"], "GB/s": path_gbs, "frac_hbm": path_gbs / PEAK_HBM_GBS,
+                 "hbm_floor_ms": r["bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3, "workspace_bytes": r["ws_bytes"]},
         "mfma": {"tflops": tflops, "peak": PEAK_BF16_TFLOPS, "frac": tflops / PEAK_BF16_TFLOPS,
-                 "flops_per_launch": r["flops"], "note": "algorithmic FLOPs (masked tiles not counted)"},
-        "kernel_ms": r["launch_ms"],
-        "bytes_per_launch": r["bytes"],
+                 "flops_per_step": r["flops"], "note": "algorithmic FLOPs of the path (masked tiles not counted)"},
         "token_heads_per_s": value * r["H"],
     }
     if not args.no_side:
+        f_region, f_launch = bench_fused(args.steps, args.warmup, c, x)
+        out["fused"] = {"entry": "gdr_chunk_fwd (one kernel, no workspace)", "ms_per_step": f_region,
+                        "kernel_ms": f_launch, "tokens/s": tokens / (f_region * 1e-3)}
         dd = bench_decode()
         gbs = dd["bytes"] / (dd["launch_ms"] * 1e-3) / 1e9
         out["decode"] = {"workload": "256 seq x 16 heads, d=128, fp32 state, 1024 steps", "ms_per_step": dd["region_ms"],
@@ -253,7 +315,7 @@ def main():
         torch.cuda.synchronize()
         out["calib_copy_bytes_each_way"] = n * 4
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(r["inputs"])
+        out["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(out), flush=True)
 
 

@@ -119,6 +119,25 @@ int gdr_chunk_fwd_ws(const void* q, const void* k, const void* v,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdr_chunk_intra, gdr_chunk_scan — the two kernels of gdr_chunk_fwd_ws as
+ * separate calls (same workspace, same stream order): gdr_chunk_intra reads
+ * the inputs and fills the workspace with the state-independent part of every
+ * chunk; gdr_chunk_scan then walks the chunks of every head from S0 and
+ * writes o and S_out. Called in this order with the same sizes they compute
+ * exactly what gdr_chunk_fwd_ws computes. Arguments and errors as for
+ * gdr_chunk_fwd_ws; gdr_chunk_scan reads a workspace that gdr_chunk_intra
+ * filled for the same B, H, T, dk, dv, chunk and dtype (not checked).
+ */
+int gdr_chunk_intra(const void* q, const void* k, const void* v,
+                    const void* alpha, const void* b, const void* w,
+                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int gdr_chunk_scan(const void* workspace, size_t workspace_bytes,
+                   const float* S0, void* o, float* S_out,
+                   int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                   void* stream);
+
+/*
  * gdr_decode_step — one recurrent step of "Muir: ...", §2.1 eq.(1) for N
  * independent sequences, updating their resident states in place.
  *

@@ -23,7 +23,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
+__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_chunk_intra",
+           "gdr_chunk_scan", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +59,10 @@ def load_library():
     lib.gdr_chunk_workspace_size.restype = I
     lib.gdr_chunk_fwd_ws.argtypes = [P] * 9 + [I] * 7 + [P, ctypes.c_size_t, P]
     lib.gdr_chunk_fwd_ws.restype = I
+    lib.gdr_chunk_intra.argtypes = [P] * 6 + [I] * 7 + [P, ctypes.c_size_t, P]
+    lib.gdr_chunk_intra.restype = I
+    lib.gdr_chunk_scan.argtypes = [P, ctypes.c_size_t, P, P, P] + [I] * 7 + [P]
+    lib.gdr_chunk_scan.restype = I
     lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
     lib.gdr_decode_step.restype = I
     lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
@@ -174,17 +179,54 @@ def gdr_chunk_fwd_ws(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=N
     import torch
     (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state)
     need = gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if not (isinstance(workspace, torch.Tensor) and workspace.device == q.device
-            and workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    workspace = _workspace(workspace, need, q.device)
     nbytes = workspace.numel() * workspace.element_size()
     lib = load_library()
     st = lib.gdr_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
                               _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q),
                               _ptr(workspace), nbytes, _stream(stream))
     _check("gdr_chunk_fwd_ws", st)
+    return o, S_out
+
+
+def _workspace(workspace, need, device):
+    import torch
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if not (isinstance(workspace, torch.Tensor) and workspace.device == device and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace
+
+
+def gdr_chunk_intra(q, k, v, alpha, b, w, *, chunk=64, workspace=None, stream=None):
+    """First kernel of :func:`gdr_chunk_fwd_ws`: fills and returns the workspace."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("alpha", alpha, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _req(t, name, (B, H, T, d), q.dtype, q.device)
+    need = gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    st = load_library().gdr_chunk_intra(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                        B, H, T, dk, dv, int(chunk), _dtype_code(q), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gdr_chunk_intra", st)
+    return workspace
+
+
+def gdr_chunk_scan(workspace, S0, o, S_out, *, B, H, T, dk, dv, chunk=64, stream=None):
+    """Second kernel of :func:`gdr_chunk_fwd_ws`: o ``[B,H,T,dv]`` (input dtype) and
+    optional S0 / S_out ``[B,H,dk,dv]`` float32 from a workspace filled by
+    :func:`gdr_chunk_intra` with the same sizes."""
+    import torch
+    _req(o, "o", (B, H, T, dv), o.dtype, o.device)
+    for name, t in (("S0", S0), ("S_out", S_out)):
+        if t is not None:
+            _req(t, name, (B, H, dk, dv), torch.float32, o.device)
+    st = load_library().gdr_chunk_scan(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _ptr(S0), _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk),
+                                       _dtype_code(o), _stream(stream))
+    _check("gdr_chunk_scan", st)
     return o, S_out
 
 

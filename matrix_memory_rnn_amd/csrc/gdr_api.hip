@@ -34,16 +34,28 @@ int check_sizes(long long B, long long H, long long T, int dk, int dv, int dtype
   return GDR_OK;
 }
 
-// Checks shared by the two chunkwise entry points.
-int check_chunk(const void* q, const void* k, const void* v, const void* alpha, const void* b,
-                const void* w, const float* S0, const void* o, const float* S_out, int B, int H,
-                int T, int dk, int dv, int chunk, int dtype) {
-  if (!q || !k || !v || !alpha || !b || !w || !o) return GDR_ERR_NULL;
+// Input checks of the chunkwise entry points: pointers, sizes, chunk, alignment.
+int check_chunk_inputs(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                       const void* w, int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  if (!q || !k || !v || !alpha || !b || !w) return GDR_ERR_NULL;
   int st = check_sizes(B, H, T, dk, dv, dtype, 128);
   if (st != GDR_OK) return st;
   if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
-  const void* ptrs[] = {q, k, v, alpha, b, w, S0, o, S_out};
+  const void* ptrs[] = {q, k, v, alpha, b, w};
   for (const void* p : ptrs)
+    if (!aligned16(p)) return GDR_ERR_ALIGN;
+  return GDR_OK;
+}
+
+// Checks shared by the chunkwise entry points that write o (and S_out).
+int check_chunk(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                const void* w, const float* S0, const void* o, const float* S_out, int B, int H,
+                int T, int dk, int dv, int chunk, int dtype) {
+  if (!o) return GDR_ERR_NULL;
+  int st = check_chunk_inputs(q, k, v, alpha, b, w, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  const void* outs[] = {S0, o, S_out};
+  for (const void* p : outs)
     if (!aligned16(p)) return GDR_ERR_ALIGN;
   const size_t es = esize(dtype);
   const size_t nK = (size_t)B * H * T * dk * es, nV = (size_t)B * H * T * dv * es;
@@ -57,6 +69,27 @@ int check_chunk(const void* q, const void* k, const void* v, const void* alpha, 
     return GDR_ERR_ALIAS;
   if (overlap(S_out, nS, v, nV) || overlap(S_out, nS, w, nV)) return GDR_ERR_ALIAS;
   if (S_out && S0 && S_out != S0 && overlap(S_out, nS, S0, nS)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+// Workspace checks of the two-kernel chunk forward: present, aligned, large
+// enough, and clear of every other buffer.
+int check_workspace(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                    const void* w, const float* S0, const void* o, const float* S_out, int B, int H,
+                    int T, int dk, int dv, int chunk, int dtype, const void* workspace,
+                    size_t workspace_bytes) {
+  if (!workspace) return GDR_ERR_NULL;
+  if (!aligned16(workspace)) return GDR_ERR_ALIGN;
+  const size_t need = gdr::chunk_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
+  const size_t es = esize(dtype);
+  const size_t nK = (size_t)B * H * T * dk * es, nV = (size_t)B * H * T * dv * es;
+  const size_t nS = (size_t)B * H * dk * dv * sizeof(float);
+  struct R { const void* p; size_t n; };
+  const R bufs[] = {{q, nK}, {k, nK}, {alpha, nK}, {b, nK}, {v, nV}, {w, nV},
+                    {S0, nS}, {o, nV}, {S_out, nS}};
+  for (const R& x : bufs)
+    if (overlap(workspace, need, x.p, x.n)) return GDR_ERR_ALIAS;
   return GDR_OK;
 }
 
@@ -107,20 +140,45 @@ int gdr_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* al
                      void* stream) {
   int st = check_chunk(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype);
   if (st != GDR_OK) return st;
-  if (!workspace) return GDR_ERR_NULL;
-  if (!aligned16(workspace)) return GDR_ERR_ALIGN;
+  st = check_workspace(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, workspace,
+                       workspace_bytes);
+  if (st != GDR_OK) return st;
+  gdr::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
+  return gdr::chunk_fwd_ws_launch(a, workspace, 3);
+}
+
+int gdr_chunk_intra(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                    const void* w, int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_chunk_inputs(q, k, v, alpha, b, w, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  st = check_workspace(q, k, v, alpha, b, w, nullptr, nullptr, nullptr, B, H, T, dk, dv, chunk, dtype,
+                       workspace, workspace_bytes);
+  if (st != GDR_OK) return st;
+  gdr::ChunkArgs a{q, k, v, alpha, b, w, nullptr, nullptr, nullptr, B, H, T, dk, dv, chunk, dtype, stream};
+  return gdr::chunk_fwd_ws_launch(a, workspace, 1);
+}
+
+int gdr_chunk_scan(const void* workspace, size_t workspace_bytes, const float* S0, void* o, float* S_out,
+                   int B, int H, int T, int dk, int dv, int chunk, int dtype, void* stream) {
+  if (!workspace || !o) return GDR_ERR_NULL;
+  int st = check_sizes(B, H, T, dk, dv, dtype, 128);
+  if (st != GDR_OK) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
+  const void* ptrs[] = {workspace, S0, o, S_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GDR_ERR_ALIGN;
   const size_t need = gdr::chunk_ws_bytes(B, H, T, dk, dv, chunk, dtype);
   if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
-  const size_t es = esize(dtype);
-  const size_t nK = (size_t)B * H * T * dk * es, nV = (size_t)B * H * T * dv * es;
+  const size_t nV = (size_t)B * H * T * dv * esize(dtype);
   const size_t nS = (size_t)B * H * dk * dv * sizeof(float);
-  struct R { const void* p; size_t n; };
-  const R bufs[] = {{q, nK}, {k, nK}, {alpha, nK}, {b, nK}, {v, nV}, {w, nV},
-                    {S0, nS}, {o, nV}, {S_out, nS}};
-  for (const R& x : bufs)
-    if (overlap(workspace, need, x.p, x.n)) return GDR_ERR_ALIAS;
-  gdr::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
-  return gdr::chunk_fwd_ws_launch(a, workspace);
+  if (overlap(o, nV, workspace, need) || overlap(S_out, nS, workspace, need) ||
+      overlap(S0, nS, workspace, need) || overlap(o, nV, S0, nS) || overlap(o, nV, S_out, nS))
+    return GDR_ERR_ALIAS;
+  if (S_out && S0 && S_out != S0 && overlap(S_out, nS, S0, nS)) return GDR_ERR_ALIAS;
+  gdr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S0, o, S_out, B, H, T, dk, dv,
+                   chunk, dtype, stream};
+  return gdr::chunk_fwd_ws_launch(a, const_cast<void*>(workspace), 2);
 }
 
 int gdr_decode_step(const void* q, const void* k, const void* v, const void* alpha, const void* b,

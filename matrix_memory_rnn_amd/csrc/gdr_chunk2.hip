@@ -69,6 +69,23 @@ template <> struct Out<__bf16> {
   }
 };
 
+// Right-looking forward substitution step for columns 4*M4 .. 4*M4+3 of a
+// unit lower-triangular 16x16 system (rows of L in LDS with pitch LDB): once
+// x[m] is final it is subtracted from every later row, so the dependent chain
+// is one FMA per row and the other updates run alongside.
+template <int M4, int LDB>
+__device__ __forceinline__ void fs_group(const float* Lb, float* x) {
+  f32x4 lc[16];
+#pragma unroll
+  for (int r = 4 * M4 + 1; r < 16; ++r) lc[r] = *(const f32x4*)(Lb + r * LDB + 4 * M4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = 4 * M4 + e;
+#pragma unroll
+    for (int r = m + 1; r < 16; ++r) x[r] -= lc[r][e] * x[m];
+  }
+}
+
 // ============================================================================ intra kernel
 constexpr int kIntraThreads = 512;
 constexpr int kMaxDv = 128;
@@ -117,7 +134,7 @@ struct IntraSmem {
 };
 
 template <typename Tin, int DK, int CM>
-__global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
+__global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
     char* __restrict__ ws, int T, int DV, int nchunks, int nitems) {
@@ -140,6 +157,12 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
   const int g = lane >> 4, c16 = lane & 15;
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(Tin));
   const int NX = (DV + DK) / 16;
+  // XR element offset of (column col, row t): the 8-row slots of a column are
+  // XOR-swizzled by the column's 16-column group, so the transposed 2-byte
+  // writes of a v^ row (16 lanes, columns 8 apart) spread over distinct banks
+  // while a 16-column fragment read still sees one uniform slot order
+  constexpr int XM = CM / 8 - 1;
+  auto xoff = [](int col, int t) { return col * L::LDC + 8 * ((t >> 3) ^ ((col >> 4) & XM)) + (t & 7); };
 
   float* GS = (float*)(smem + L::GS);
   float* SCL = (float*)(smem + L::SCL);
@@ -235,7 +258,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
         if (idx < nvi) {
           const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, (vcol + e) * L::LDC + vrow, vh[i][e]);
+          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, xoff(vcol + e, vrow), vh[i][e]);
         }
       }
     }
@@ -314,9 +337,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
 #pragma unroll
         for (int r4 = 0; r4 < 2; ++r4) {
           const float2* kp = khp + 4 * r4;
-          st4<MT>(smem + L::XR, L::P_XC, (DV + j) * L::LDC + r0 + 4 * r4,
+          st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j, r0 + 4 * r4),
                   f32x4{kp[0].x, kp[1].x, kp[2].x, kp[3].x});
-          st4<MT>(smem + L::XR, L::P_XC, (DV + j + 1) * L::LDC + r0 + 4 * r4,
+          st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j + 1, r0 + 4 * r4),
                   f32x4{kp[0].y, kp[1].y, kp[2].y, kp[3].y});
         }
       }
@@ -384,7 +407,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
         if (idx < nvi) {
           const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, (vcol + e) * L::LDC + vrow, vh[i][e]);
+          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, xoff(vcol + e, vrow), vh[i][e]);
         }
       }
     }
@@ -392,9 +415,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
 #pragma unroll
       for (int r4 = 0; r4 < 2; ++r4) {
         const float2* kp = khp + 4 * r4;
-        st4<MT>(smem + L::XR, L::P_XC, (DV + j) * L::LDC + r0 + 4 * r4,
+        st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j, r0 + 4 * r4),
                 f32x4{kp[0].x, kp[1].x, kp[2].x, kp[3].x});
-        st4<MT>(smem + L::XR, L::P_XC, (DV + j + 1) * L::LDC + r0 + 4 * r4,
+        st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j + 1, r0 + 4 * r4),
                 f32x4{kp[0].y, kp[1].y, kp[2].y, kp[3].y});
       }
     }
@@ -406,24 +429,15 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
       const int I = g, cc = c16;
       const bool live = I < NB;
       const float* Lb = LBK + (live ? pidx(I, I) : 0) * BLKF;
+      // right-looking: once x[m] is final it is subtracted from every later
+      // row at once, so the dependent chain is one FMA per row
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc0 = (r == cc) ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int m4 = 0; 4 * m4 < r; ++m4) {
-          const f32x4 lv = *(const f32x4*)(Lb + r * L::LDB + 4 * m4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = 4 * m4 + e;
-            if (m < r) {
-              if (m & 1) acc1 -= lv[e] * x[m];
-              else acc0 -= lv[e] * x[m];
-            }
-          }
-        }
-        x[r] = acc0 + acc1;
-      }
+      for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+      fs_group<0, L::LDB>(Lb, x);
+      fs_group<1, L::LDB>(Lb, x);
+      fs_group<2, L::LDB>(Lb, x);
+      fs_group<3, L::LDB>(Lb, x);
       if (live) {
         float* Tn = TBN + I * BLKF;
 #pragma unroll
@@ -474,7 +488,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
           for (int i = 0; i < MAXX; ++i) {
             const int ct = wid + NW * i;
             if (ct < NX) {
-              Frag<MT> B = ldfrag<MT>(smem + L::XR, L::P_XC, L::LDC, 16 * ct, k0, kend, lane);
+              // rows 16ct + c16 share the slot swizzle ct & XM
+              const int kk = k0 + 8 * g;
+              Frag<MT> B = ldfrag<MT>(smem + L::XR, L::P_XC, L::LDC, 16 * ct,
+                                      8 * ((kk >> 3) ^ (ct & XM)) - 8 * g, kk < kend ? CM : 0, lane);
               mma<MT>(acc[i], A, B);
             }
           }
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void gdn2_chunk_intra_kernel(
       for (int i = 0; i < MAXX; ++i) {
         const int ct = wid + NW * i;
         if (ct < NX) {
-          st4<MT>(smem + L::XR, L::P_XC, (16 * ct + c16) * L::LDC + 16 * I + 4 * g, acc[i]);
+          st4<MT>(smem + L::XR, L::P_XC, xoff(16 * ct + c16, 16 * I + 4 * g), acc[i]);
           if (16 * ct < DV) {
             Out<Tin>::quad(UTg + (16 * ct + c16) * CM + 16 * I + 4 * g, acc[i]);
           } else {
@@ -741,6 +758,224 @@ __global__ __launch_bounds__(kScanThreads, 1) void gdn2_chunk_scan_kernel(
   }
 }
 
+// ============================================================================ staged scan kernel (bf16)
+// The same chunk pass as gdn2_chunk_scan_kernel with the record slice of each
+// chunk (Y, Q_pi, M, K~^T, pi_C and this workgroup's U^T rows) loaded once per
+// workgroup with 16-byte coalesced loads, two chunks ahead, into two register
+// sets used in turn; at the end of a chunk the set holding the next chunk is
+// written to one of two LDS stages, from which every MFMA operand is read.
+// Rows of a staged matrix keep their global byte layout up to an XOR swizzle
+// of their 16-byte slots (slot ^ swz(row)), which makes both the row-wise
+// stores and the 16-row fragment reads free of bank conflicts.
+template <int DK, int VT, int CM>
+struct StagedScan {
+  static constexpr int WY = DK * 2, WC = CM * 2;   // row bytes of [.][DK] and [.][C] bf16 matrices
+  static constexpr int Y = 0;                       // Y      [t][j]
+  static constexpr int QP = Y + CM * WY;            // Q_pi   [t][j]
+  static constexpr int M = QP + CM * WY;            // M      [t][s]
+  static constexpr int KT = M + CM * WC;            // K~^T   [j][s]
+  static constexpr int UT = KT + DK * WC;           // U^T    [v][t], this workgroup's VT rows
+  static constexpr int PC = UT + VT * WC;           // pi_C   fp32 [j]
+  static constexpr int STAGE = (PC + DK * 4 + 15) / 16 * 16;
+  static constexpr int LDK = DK + 8, LDC = CM + 8;
+  static constexpr int S0T = 2 * STAGE;             // S0^T  [v][j] bf16
+  static constexpr int VTT = S0T + VT * LDK * 2;    // V~^T  [v][t] bf16
+  static constexpr int TOTAL = VTT + VT * LDC * 2;
+  static_assert(TOTAL <= 160 * 1024, "staged scan LDS exceeds 160 KiB");
+  // 16-byte pieces of one stage, in load order
+  static constexpr int NY = CM * WY / 16, NU = VT * WC / 16, NM = CM * WC / 16, NK = DK * WC / 16;
+  static constexpr int NPC = DK * 4 / 16;
+  static constexpr int B_Y = 0, B_U = B_Y + NY, B_M = B_U + NU, B_Q = B_M + NM, B_K = B_Q + NY;
+  static constexpr int B_P = B_K + NK, NPIECE = B_P + NPC;
+};
+
+// Slot swizzle of a row with n 16-byte slots (n = 2, 4, 8 or 16): rows that
+// are 16 apart in a fragment read land on distinct bank groups.
+__device__ __forceinline__ int swz(int r, int n) { return (r / (16 / n)) % n; }
+
+template <int DK, int VT, int CM>
+__global__ __launch_bounds__(kScanThreads, 1) void gdn2_chunk_scan_staged_kernel(
+    const char* __restrict__ ws, const float* __restrict__ S0, __bf16* __restrict__ o, float* S_out,
+    int T, int DV) {
+  using L = StagedScan<DK, VT, CM>;
+  constexpr int MM = kBF;
+  constexpr int NW = kScanThreads / 64;
+  constexpr int NVL = VT / 16;
+  constexpr int NST = (DK / 16) * NVL;
+  constexpr int MAXS = (NST + NW - 1) / NW;
+  constexpr int NT = (CM / 16) * NVL;
+  constexpr int MAXV = (NT + NW - 1) / NW;
+  constexpr int KS = DK >= 32 ? DK / 32 : 1;
+  constexpr int KSC = CM >= 32 ? CM / 32 : 1;
+  constexpr int NPT = (L::NPIECE + kScanThreads - 1) / kScanThreads;  // pieces per thread
+  constexpr int LDK = L::LDK, LDC = L::LDC;
+  constexpr int P_VK = VT * LDK * 2, P_VC = VT * LDC * 2;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* S0T = smem + L::S0T;
+  char* VTT = smem + L::VTT;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nvt = DV / VT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
+  const int nchunks = (T + CM - 1) / CM;
+  const size_t stOff = (size_t)bh * DK * DV;
+  const RecLayout RL = rec_layout(DK, DV, CM, 2);
+  const char* wsh = ws + (size_t)bh * nchunks * RL.bytes;
+
+  // ---- the pieces this thread moves: global byte offset in a record, LDS byte offset in a stage
+  int gof[NPT], lof[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    int p = tid + kScanThreads * i;
+    if (p >= L::NPIECE) p = L::NPIECE - 1;           // duplicate of the last piece (same value)
+    int g0, l0, q, w, base_l;
+    bool rowsw = true;
+    if (p < L::B_U) { q = p - L::B_Y; w = L::WY; g0 = RL.y; base_l = L::Y; }
+    else if (p < L::B_M) { q = p - L::B_U; w = L::WC; g0 = RL.ut + vt0 * L::WC; base_l = L::UT; }
+    else if (p < L::B_Q) { q = p - L::B_M; w = L::WC; g0 = RL.m; base_l = L::M; }
+    else if (p < L::B_K) { q = p - L::B_Q; w = L::WY; g0 = RL.qp; base_l = L::QP; }
+    else if (p < L::B_P) { q = p - L::B_K; w = L::WC; g0 = RL.kt; base_l = L::KT; }
+    else { q = p - L::B_P; w = DK * 4; g0 = RL.pic; base_l = L::PC; rowsw = false; }
+    const int n = w / 16, r = q / n, c = q % n;
+    gof[i] = g0 + r * w + 16 * c;
+    l0 = base_l + r * w + 16 * (rowsw ? (c ^ swz(r, n)) : c);
+    lof[i] = l0;
+  }
+  auto load = [&](int ch, u32x4* R) {
+    const char* rec = wsh + (size_t)(ch < nchunks ? ch : nchunks - 1) * RL.bytes;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) R[i] = *(const u32x4*)(rec + gof[i]);
+  };
+  auto stage = [&](const u32x4* R, int st) {
+    char* base = smem + st * L::STAGE;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) *(u32x4*)(base + lof[i]) = R[i];
+  };
+  // fragment of a staged row-major matrix: rows row0 + c16, 8 elements from k0 + 8g
+  auto sfrag = [&](const char* stg, int moff, int w, int row0, int k0) {
+    const int n = w / 16, r = row0 + c16, c = ((k0 >> 3) + g) & (n - 1);
+    Frag<MM> f;
+    f.hi = *(const bf16x8*)(stg + moff + r * w + 16 * (c ^ swz(r, n)));
+    return f;
+  };
+
+  // ---- state tile in registers (fp32), S0^T in LDS
+  f32x4 Sacc[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    Sacc[i] = f4zero();
+    const int tile = wid + NW * i;
+    if (tile < NST) {
+      const int jt = tile / NVL, vl = tile % NVL;
+      if (S0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Sacc[i][e] = S0[stOff + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16];
+      }
+      st4<MM>(S0T, P_VK, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+    }
+  }
+
+  auto compute = [&](int ch, const char* stg) {
+    const int t0 = ch * CM;
+    f32x4 oacc[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      oacc[i] = f4zero();
+      const int tile = wid + NW * i;
+      if (tile < NT) {
+        const int I = tile / NVL, vl = tile % NVL;
+        f32x4 acc = f4zero();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bool kv = 32 * s + 8 * g < DK;
+          Frag<MM> Sf = ldfrag<MM>(S0T, P_VK, LDK, 16 * vl, 32 * s, DK, lane);
+          mma<MM>(acc, zsel<MM>(kv, sfrag(stg, L::Y, L::WY, 16 * I, 32 * s)), Sf);
+          mma<MM>(oacc[i], Sf, zsel<MM>(kv, sfrag(stg, L::QP, L::WY, 16 * I, 32 * s)));
+        }
+        // U[t = 16I + 4g + e][v = 16vl + c16] from U^T row v: 8 bytes in slot 2I + g/2
+        const int vr = 16 * vl + c16, uc = 2 * I + (g >> 1);
+        typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+        const u2 uw = *(const u2*)(stg + L::UT + vr * L::WC + 16 * (uc ^ swz(vr, L::WC / 16)) + 8 * (g & 1));
+        const f32x4 u = Raw<__bf16>::un4(uw);
+        f32x4 vt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[e] = u[e] - acc[e];
+        st4<MM>(VTT, P_VC, (16 * vl + c16) * LDC + 16 * I + 4 * g, vt);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int tile = wid + NW * i;
+      if (tile < NT) {
+        const int I = tile / NVL, vl = tile % NVL, kend = 16 * (I + 1);
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          if (32 * s < kend) {
+            Frag<MM> A = ldfrag<MM>(VTT, P_VC, LDC, 16 * vl, 32 * s, kend, lane);
+            mma<MM>(oacc[i], A, zsel<MM>(32 * s + 8 * g < kend, sfrag(stg, L::M, L::WC, 16 * I, 32 * s)));
+          }
+        }
+        const int t = t0 + 16 * I + c16;
+        if (t < T) In<__bf16>::store4(o + ((size_t)bh * T + t) * DV + vt0 + 16 * vl + 4 * g, oacc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + NW * i;
+      if (tile < NST) {
+        const int jt = tile / NVL, vl = tile % NVL;
+        const f32x4 pc = *(const f32x4*)(stg + L::PC + 4 * (16 * jt + 4 * g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[i][e] *= pc[e];
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          Frag<MM> B = ldfrag<MM>(VTT, P_VC, LDC, 16 * vl, 32 * s, CM, lane);
+          mma<MM>(Sacc[i], zsel<MM>(32 * s + 8 * g < CM, sfrag(stg, L::KT, L::WC, 16 * jt, 32 * s)), B);
+        }
+        st4<MM>(S0T, P_VK, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+      }
+    }
+  };
+
+  // ---- pipeline: register set R0 holds even chunks, R1 odd ones; loads are
+  // unconditional (past the end they repeat the last chunk) so the compiler
+  // can count outstanding loads exactly
+  u32x4 R0[NPT], R1[NPT];
+  load(0, R0);
+  load(1, R1);
+  stage(R0, 0);
+  __syncthreads();
+  load(2, R0);
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    compute(ch, smem);
+    stage(R1, 1);
+    __syncthreads();
+    load(ch + 3, R1);
+    if (ch + 1 >= nchunks) break;
+    compute(ch + 1, smem + L::STAGE);
+    stage(R0, 0);
+    __syncthreads();
+    load(ch + 4, R0);
+  }
+
+  if (S_out) {
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+      const int tile = wid + NW * i;
+      if (tile < NST) {
+        const int jt = tile / NVL, vl = tile % NVL;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          S_out[stOff + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[i][e];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host launch
 size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
   const int es = dtype == GDR_BF16 ? 2 : 4;
@@ -786,22 +1021,38 @@ static int launch_intra(const ChunkArgs& a, char* ws) {
 
 template <typename Tin, int DK, int VT, int CM>
 static int launch_scan(const ChunkArgs& a, const char* ws) {
-  auto kern = gdn2_chunk_scan_kernel<Tin, DK, VT, CM>;
+  const void* kern;
+  int lds = 0;
+  if constexpr (std::is_same<Tin, __bf16>::value) {
+    using L = StagedScan<DK, VT, CM>;
+    kern = (const void*)gdn2_chunk_scan_staged_kernel<DK, VT, CM>;
+    lds = L::TOTAL;
+    static bool attr_set = false;
+    if (!attr_set) {
+      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return GDR_ERR_LAUNCH;
+      attr_set = true;
+    }
+  } else {
+    kern = (const void*)gdn2_chunk_scan_kernel<Tin, DK, VT, CM>;
+  }
   const int nblocks = a.B * a.H * (a.dv / VT);
   const float* S0 = a.S0;
   Tin* o = (Tin*)a.o;
   float* So = a.S_out;
   int T = a.T, DV = a.dv;
   void* args[] = {&ws, &S0, &o, &So, &T, &DV};
-  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(kScanThreads), args, 0,
-                                 (hipStream_t)a.stream);
+  hipError_t e = hipLaunchKernel(kern, dim3(nblocks), dim3(kScanThreads), args, lds, (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
 template <typename Tin, int DK, int CM>
-static int launch_pair(const ChunkArgs& a, char* ws) {
-  int st = launch_intra<Tin, DK, CM>(a, ws);
-  if (st != GDR_OK) return st;
+static int launch_pair(const ChunkArgs& a, char* ws, int phases) {
+  if (phases & 1) {
+    const int st = launch_intra<Tin, DK, CM>(a, ws);
+    if (st != GDR_OK) return st;
+  }
+  if (!(phases & 2)) return GDR_OK;
   // value tiles of 32 columns when that still gives a workgroup per CU, else 16
   const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= device_cus();
   if constexpr (std::is_same<Tin, float>::value) {
@@ -813,29 +1064,29 @@ static int launch_pair(const ChunkArgs& a, char* ws) {
 }
 
 template <typename Tin, int CM>
-static int dispatch_dk(const ChunkArgs& a, char* ws) {
+static int dispatch_dk(const ChunkArgs& a, char* ws, int phases) {
   switch (a.dk) {
-    case 16: return launch_pair<Tin, 16, CM>(a, ws);
-    case 32: return launch_pair<Tin, 32, CM>(a, ws);
-    case 64: return launch_pair<Tin, 64, CM>(a, ws);
-    case 128: return launch_pair<Tin, 128, CM>(a, ws);
+    case 16: return launch_pair<Tin, 16, CM>(a, ws, phases);
+    case 32: return launch_pair<Tin, 32, CM>(a, ws, phases);
+    case 64: return launch_pair<Tin, 64, CM>(a, ws, phases);
+    case 128: return launch_pair<Tin, 128, CM>(a, ws, phases);
   }
   return GDR_ERR_UNSUPPORTED;
 }
 
 template <typename Tin>
-static int dispatch_chunk(const ChunkArgs& a, char* ws) {
+static int dispatch_chunk(const ChunkArgs& a, char* ws, int phases) {
   switch (a.chunk) {
-    case 16: return dispatch_dk<Tin, 16>(a, ws);
-    case 32: return dispatch_dk<Tin, 32>(a, ws);
-    case 64: return dispatch_dk<Tin, 64>(a, ws);
+    case 16: return dispatch_dk<Tin, 16>(a, ws, phases);
+    case 32: return dispatch_dk<Tin, 32>(a, ws, phases);
+    case 64: return dispatch_dk<Tin, 64>(a, ws, phases);
   }
   return GDR_ERR_UNSUPPORTED;
 }
 
-int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws) {
-  if (a.dtype == GDR_BF16) return dispatch_chunk<__bf16>(a, (char*)ws);
-  return dispatch_chunk<float>(a, (char*)ws);
+int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases) {
+  if (a.dtype == GDR_BF16) return dispatch_chunk<__bf16>(a, (char*)ws, phases);
+  return dispatch_chunk<float>(a, (char*)ws, phases);
 }
 
 }  // namespace gdr

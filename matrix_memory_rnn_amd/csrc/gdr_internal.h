@@ -38,7 +38,8 @@ struct MlstmArgs {
 int chunk_fwd_launch(const ChunkArgs& a);
 // two-kernel form (intra-chunk kernel over all chunks, then the chunk scan)
 size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
-int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws);
+// phases: bit 0 = intra-chunk kernel (writes the workspace), bit 1 = chunk scan
+int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases);
 int decode_launch(const DecodeArgs& a);
 int mlstm_launch(const MlstmArgs& a);
 

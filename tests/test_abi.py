@@ -33,8 +33,8 @@ def lib():
 
 def test_header_declares_the_three_entry_points():
     names = _declared()
-    for n in ("gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_decode_step",
-              "gdr_mlstm_fwd", "gdr_status_string", "gdr_version"):
+    for n in ("gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_chunk_intra",
+              "gdr_chunk_scan", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_status_string", "gdr_version"):
         assert n in names
 
 
@@ -129,6 +129,34 @@ def test_chunk_ws_validation(lib):
     # the fused kernel's fp32 chunk limit does not apply here: validation passes
     # up to the launch, which is not reached because the pointers are checked first
     assert f(ws=P[0]) == c["GDR_ERR_ALIAS"]
+
+
+def test_chunk_phase_validation(lib):
+    c = _codes()
+    need = _ws_size(lib)[1]
+
+    def intra(ptrs=None, ws=P[10], nbytes=None, T=64, chunk=16):
+        p = list(P[:6]) if ptrs is None else ptrs
+        return lib.gdr_chunk_intra(*p, 1, 2, T, 16, 16, chunk, 1, ws, need if nbytes is None else nbytes, None)
+
+    def scan(ws=P[10], nbytes=None, S0=None, o=P[6], S_out=None, chunk=16):
+        return lib.gdr_chunk_scan(ws, need if nbytes is None else nbytes, S0, o, S_out,
+                                  1, 2, 64, 16, 16, chunk, 1, None)
+
+    assert intra(ptrs=[None] + P[1:6]) == c["GDR_ERR_NULL"]
+    assert intra(ws=None) == c["GDR_ERR_NULL"]
+    assert intra(T=0) == c["GDR_ERR_SHAPE"]
+    assert intra(chunk=8) == c["GDR_ERR_UNSUPPORTED"]
+    assert intra(nbytes=need - 16) == c["GDR_ERR_WORKSPACE"]
+    assert intra(ws=P[3] + 64) == c["GDR_ERR_ALIAS"]          # workspace inside alpha
+    assert intra(ptrs=P[:5] + [P[5] + 4]) == c["GDR_ERR_ALIGN"]
+    assert scan(ws=None) == c["GDR_ERR_NULL"]
+    assert scan(o=None) == c["GDR_ERR_NULL"]
+    assert scan(nbytes=need - 1) == c["GDR_ERR_WORKSPACE"]
+    assert scan(o=P[10] + 256) == c["GDR_ERR_ALIAS"]          # o inside the workspace
+    assert scan(S0=P[8], S_out=P[8] + 64) == c["GDR_ERR_ALIAS"]
+    assert scan(S_out=P[8] + 8) == c["GDR_ERR_ALIGN"]
+    assert scan(chunk=128) == c["GDR_ERR_UNSUPPORTED"]
 
 
 def test_decode_validation(lib):

@@ -197,3 +197,23 @@ def test_workspace_reuse_and_agreement_with_fused_kernel():
             f"ws-vs-fused={rel_err(host(o_w), host(o_f)):.3e}")
         assert rel_err(host(o_w), o_ref) <= TOL["bf16"] and rel_err(host(S_w), S_ref) <= TOL["bf16"]
         assert rel_err(host(o_w), host(o_f)) < 1e-2 and rel_err(host(S_w), host(S_f)) < 1e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_phase_entry_points_equal_one_call(dtype):
+    """gdr_chunk_intra then gdr_chunk_scan give bit-identical results to
+    gdr_chunk_fwd_ws (same kernels, same order)."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv, C = 2, 3, 200, 128, 64, 64
+    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=4.0, alpha_sigma=1.5, seed=21, dtype=dtype, s0_std=0.1)
+    t = lambda x: dev(d[x], dtype)
+    x = [t(n) for n in ("q", "k", "v", "alpha", "b", "w")]
+    S0 = dev(d["S0"])
+    o1, S1 = gdr.gdr_chunk_fwd_ws(*x, S0, chunk=C)
+    ws = gdr.gdr_chunk_intra(*x, chunk=C)
+    o2 = torch.empty_like(o1)
+    S2 = torch.empty_like(S1)
+    gdr.gdr_chunk_scan(ws, S0, o2, S2, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
