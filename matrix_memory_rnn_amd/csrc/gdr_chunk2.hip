@@ -345,9 +345,6 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       }
     }
     __syncthreads();
-    if constexpr (!F32) {
-      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x);
-    }
 
     // ================= Gram tiles: L^T, M^T of pair (I, J) = (Kc_J * scale) [Kr_I; Qr_I]^T
     f32x4 gL[MAXP], gM[MAXP];
@@ -423,7 +420,12 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     }
     __syncthreads();
 
-    // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0)
+    // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0);
+    // the next item's loads are issued here (wave 0 first), so their issue
+    // overlaps this one-wave phase
+    if constexpr (!F32) {
+      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x);
+    }
     if (wid == 0) {
       if (tid < 4) FLAGS[tid] = 0;  // read above; set again by the next item's prep 1
       const int I = g, cc = c16;
