@@ -188,6 +188,32 @@ int gdr_mlstm_fwd(const void* q, const void* k, const void* v,
                   int B, int H, int T, int dk, int dv, int chunk, int dtype,
                   void* stream);
 
+/*
+ * gdr_mlstm_workspace_size, gdr_mlstm_fwd_ws — the computation of
+ * gdr_mlstm_fwd (same arguments and results up to rounding) as two kernels
+ * through a caller workspace, the fast form for long sequences:
+ *   1. every (b, h, chunk) in parallel: with F_t, a_s = i~_s - F_s and the
+ *      chunk-local running max A_t = max_{s<=t} a_s, the state-independent
+ *      parts H_t = sum_{s<=t} e^{a_s - A_t} (q_t . k_s) v_s, its normaliser
+ *      N_t (v = 1), K~ = e^{a_s - A_C} k_s, V^T, F and A;
+ *   2. one pass over the chunks of each head: mu_t = max(m0, A_t),
+ *      h^_t = e^{m0 - mu_t} q_t C0 + e^{A_t - mu_t} H_t (n^ likewise),
+ *      h_t = h^_t / max(|n^_t|, e^{-(F_t + mu_t)}),
+ *      [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1],
+ *      m <- F_C + mu_C (the stabiliser of §13.4; every exponent <= 0).
+ * Record per (b, h, chunk): (2*C*dv + dk*C) elements of the input dtype and
+ * 3*C float32, rounded up to 16 bytes. Workspace rules as for
+ * gdr_chunk_fwd_ws. With float32 inputs d_v must be at most 128 here.
+ */
+int gdr_mlstm_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
+                             int dtype, size_t* bytes);
+int gdr_mlstm_fwd_ws(const void* q, const void* k, const void* v,
+                     const float* i_tilde, const float* f_tilde,
+                     const float* C0, const float* n0, const float* m0,
+                     void* h, float* C_out, float* n_out, float* m_out,
+                     int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* gdr_status_string(int status);
 

@@ -16,7 +16,9 @@ Entry points (same names as the C ABI):
   (:func:`gdr_chunk_workspace_size` bytes).
 * :func:`gdr_decode_step` — one recurrent decode step, state updated in place.
 * :func:`gdr_mlstm_fwd` — chunkwise forward of the stabilised mLSTM cell
-  ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4).
+  ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4), one
+  fused kernel; :func:`gdr_mlstm_fwd_ws` the same as an intra-chunk kernel
+  plus a chunk scan through a workspace.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ import ctypes
 import os
 
 __all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_chunk_intra",
-           "gdr_chunk_scan", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
+           "gdr_chunk_scan", "gdr_mlstm_fwd_ws", "gdr_mlstm_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +69,10 @@ def load_library():
     lib.gdr_decode_step.restype = I
     lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
     lib.gdr_mlstm_fwd.restype = I
+    lib.gdr_mlstm_workspace_size.argtypes = [I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_mlstm_workspace_size.restype = I
+    lib.gdr_mlstm_fwd_ws.argtypes = [P] * 12 + [I] * 7 + [P, ctypes.c_size_t, P]
+    lib.gdr_mlstm_fwd_ws.restype = I
     lib.gdr_status_string.argtypes = [I]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -251,12 +257,7 @@ def gdr_decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
     return o
 
 
-def gdr_mlstm_fwd(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, chunk=64, h=None,
-                  C_out=None, n_out=None, m_out=None, return_state=True, stream=None):
-    """Stabilised mLSTM forward. q, k ``[B,H,T,dk]``, v ``[B,H,T,dv]`` (bf16/fp32);
-    i_tilde, f_tilde ``[B,H,T]`` float32; optional state (C0 ``[B,H,dk,dv]``,
-    n0 ``[B,H,dk]``, m0 ``[B,H]``, float32; all or none). Returns
-    ``(h, C_T, n_T, m_T)`` (state entries None if ``return_state`` is False)."""
+def _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, return_state):
     import torch
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -279,9 +280,50 @@ def gdr_mlstm_fwd(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, chunk
         C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
         n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
         m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    return (B, H, T, dk, dv), h, C_out, n_out, m_out
+
+
+def gdr_mlstm_fwd(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, chunk=64, h=None,
+                  C_out=None, n_out=None, m_out=None, return_state=True, stream=None):
+    """Stabilised mLSTM forward (one fused kernel). q, k ``[B,H,T,dk]``, v ``[B,H,T,dv]``
+    (bf16/fp32); i_tilde, f_tilde ``[B,H,T]`` float32; optional state (C0 ``[B,H,dk,dv]``,
+    n0 ``[B,H,dk]``, m0 ``[B,H]``, float32; all or none). Returns
+    ``(h, C_T, n_T, m_T)`` (state entries None if ``return_state`` is False)."""
+    (B, H, T, dk, dv), h, C_out, n_out, m_out = _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h,
+                                                            C_out, n_out, m_out, return_state)
     lib = load_library()
     st = lib.gdr_mlstm_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(i_tilde), _ptr(f_tilde), _ptr(C0),
                            _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
                            B, H, T, dk, dv, int(chunk), _dtype_code(q), _stream(stream))
     _check("gdr_mlstm_fwd", st)
+    return h, C_out, n_out, m_out
+
+
+def gdr_mlstm_workspace_size(B, H, T, dk, dv, chunk=64, dtype=None) -> int:
+    """Bytes of workspace :func:`gdr_mlstm_fwd_ws` needs (dtype: torch dtype, default bf16)."""
+    import torch
+    code = GDR_BF16 if dtype in (None, torch.bfloat16) else GDR_F32 if dtype == torch.float32 else -1
+    n = ctypes.c_size_t(0)
+    st = load_library().gdr_mlstm_workspace_size(int(B), int(H), int(T), int(dk), int(dv), int(chunk),
+                                                 code, ctypes.byref(n))
+    _check("gdr_mlstm_workspace_size", st)
+    return int(n.value)
+
+
+def gdr_mlstm_fwd_ws(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, chunk=64, h=None,
+                     C_out=None, n_out=None, m_out=None, workspace=None, return_state=True,
+                     stream=None):
+    """Stabilised mLSTM forward as two kernels through a workspace (same
+    arguments and results as :func:`gdr_mlstm_fwd`; ``workspace`` as for
+    :func:`gdr_chunk_fwd_ws`)."""
+    (B, H, T, dk, dv), h, C_out, n_out, m_out = _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h,
+                                                            C_out, n_out, m_out, return_state)
+    need = gdr_mlstm_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    lib = load_library()
+    st = lib.gdr_mlstm_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(i_tilde), _ptr(f_tilde), _ptr(C0),
+                              _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
+                              B, H, T, dk, dv, int(chunk), _dtype_code(q), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gdr_mlstm_fwd_ws", st)
     return h, C_out, n_out, m_out

@@ -202,10 +202,15 @@ int gdr_decode_step(const void* q, const void* k, const void* v, const void* alp
   return gdr::decode_launch(a);
 }
 
-int gdr_mlstm_fwd(const void* q, const void* k, const void* v, const float* i_tilde,
-                  const float* f_tilde, const float* C0, const float* n0, const float* m0, void* h,
-                  float* C_out, float* n_out, float* m_out, int B, int H, int T, int dk, int dv,
-                  int chunk, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the mLSTM entry points (everything but the workspace).
+int check_mlstm(const void* q, const void* k, const void* v, const float* i_tilde,
+                const float* f_tilde, const float* C0, const float* n0, const float* m0, void* h,
+                float* C_out, float* n_out, float* m_out, int B, int H, int T, int dk, int dv,
+                int chunk, int dtype) {
   if (!q || !k || !v || !i_tilde || !f_tilde || !h) return GDR_ERR_NULL;
   const bool s_in = C0 || n0 || m0, s_out = C_out || n_out || m_out;
   if (s_in && !(C0 && n0 && m0)) return GDR_ERR_NULL;
@@ -244,9 +249,60 @@ int gdr_mlstm_fwd(const void* q, const void* k, const void* v, const float* i_ti
       if (i == 0 && j == 1 && outs[j].p == st_in[i].p) continue;
       if (overlap(outs[j].p, outs[j].n, st_in[i].p, st_in[i].n)) return GDR_ERR_ALIAS;
     }
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_mlstm_fwd(const void* q, const void* k, const void* v, const float* i_tilde,
+                  const float* f_tilde, const float* C0, const float* n0, const float* m0, void* h,
+                  float* C_out, float* n_out, float* m_out, int B, int H, int T, int dk, int dv,
+                  int chunk, int dtype, void* stream) {
+  int st = check_mlstm(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, B, H, T, dk, dv,
+                       chunk, dtype);
+  if (st != GDR_OK) return st;
   gdr::MlstmArgs a{q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out,
                    B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::mlstm_launch(a);
+}
+
+int gdr_mlstm_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype, size_t* bytes) {
+  if (!bytes) return GDR_ERR_NULL;
+  *bytes = 0;
+  int st = check_sizes(B, H, T, dk, dv, dtype, 256);
+  if (st != GDR_OK) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
+  *bytes = gdr::mlstm_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  return GDR_OK;
+}
+
+int gdr_mlstm_fwd_ws(const void* q, const void* k, const void* v, const float* i_tilde,
+                     const float* f_tilde, const float* C0, const float* n0, const float* m0, void* h,
+                     float* C_out, float* n_out, float* m_out, int B, int H, int T, int dk, int dv,
+                     int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mlstm(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, B, H, T, dk, dv,
+                       chunk, dtype);
+  if (st != GDR_OK) return st;
+  if (dtype == GDR_F32 && dv > 128) return GDR_ERR_UNSUPPORTED;
+  if (!workspace) return GDR_ERR_NULL;
+  if (!aligned16(workspace)) return GDR_ERR_ALIGN;
+  const size_t need = gdr::mlstm_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
+  const size_t es = esize(dtype);
+  const size_t nK = (size_t)B * H * T * dk * es, nV = (size_t)B * H * T * dv * es;
+  const size_t nG = (size_t)B * H * T * sizeof(float);
+  const size_t nC = (size_t)B * H * dk * dv * sizeof(float), nN = (size_t)B * H * dk * sizeof(float);
+  const size_t nM = (size_t)B * H * sizeof(float);
+  struct R { const void* p; size_t n; };
+  const R bufs[] = {{q, nK}, {k, nK}, {v, nV}, {i_tilde, nG}, {f_tilde, nG}, {C0, nC}, {n0, nN},
+                    {m0, nM}, {h, nV}, {C_out, nC}, {n_out, nN}, {m_out, nM}};
+  for (const R& x : bufs)
+    if (overlap(workspace, need, x.p, x.n)) return GDR_ERR_ALIAS;
+  gdr::MlstmArgs a{q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out,
+                   B, H, T, dk, dv, chunk, dtype, stream};
+  return gdr::mlstm_ws_launch(a, workspace);
 }
 
 }  // extern "C"

@@ -42,5 +42,8 @@ size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype)
 int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases);
 int decode_launch(const DecodeArgs& a);
 int mlstm_launch(const MlstmArgs& a);
+// two-kernel form (intra-chunk kernel over all chunks, then the chunk scan)
+size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+int mlstm_ws_launch(const MlstmArgs& a, void* ws);
 
 }  // namespace gdr

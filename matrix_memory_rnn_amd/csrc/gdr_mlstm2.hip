@@ -1,0 +1,738 @@
+// Two-kernel chunkwise forward of the xLSTM mLSTM cell on gfx950
+// ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4 and the
+// solution to Exercise 13.6), [d_k, d_v] state orientation, through a
+// caller-provided workspace.
+//
+// With F_t = sum_{r<=t} log sigmoid(f~_r), a_s = i~_s - F_s and the chunk-local
+// running max A_t = max_{s<=t} a_s, the stabiliser of the page's recurrence is
+// m_t = F_t + mu_t with mu_t = max(m0, A_t). Every term splits into a part
+// that depends only on the chunk and a factor <= 1 that depends on m0:
+//   h^_t = e^{m0 - mu_t} q_t C0 + e^{A_t - mu_t} H_t,
+//          H_t = sum_{s<=t} e^{a_s - A_t} (q_t . k_s) v_s        (same for n^ with v = 1)
+//   C_C  = e^{m0 - mu_C} C0 + e^{A_C - mu_C} sum_s e^{a_s - A_C} k_s^T v_s,
+//   h_t  = h^_t / max(|n^_t|, e^{-m_t}),  m_C = F_C + mu_C.
+// The intra kernel computes the chunk-only parts (H, its normaliser row N,
+// K~ = e^{a_s - A_C} k_s, V^T, F, A) for every chunk in parallel into a
+// workspace record; the scan walks the chunks of each head doing q C0, the
+// combination and the state update. All exponents are <= 0.
+#include "gdr_device.hpp"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+namespace {
+
+constexpr int align16m(int x) { return (x + 15) / 16 * 16; }
+
+// Workspace record of one (b, h, chunk); es = element size of the input dtype.
+struct MRec {
+  int hi, vt, kt, ni, f, a, bytes;
+};
+__host__ __device__ __forceinline__ MRec mrec_layout(int dk, int dv, int C, int es) {
+  MRec r;
+  r.hi = 0;                     // H     [t][v]  C x dv (input precision)
+  r.vt = r.hi + C * dv * es;    // V^T   [v][s]  dv x C
+  r.kt = r.vt + dv * C * es;    // K~^T  [j][s]  dk x C
+  r.ni = r.kt + dk * C * es;    // N     [t] fp32
+  r.f = r.ni + C * 4;           // F     [t] fp32
+  r.a = r.f + C * 4;            // A     [t] fp32
+  r.bytes = align16m(r.a + C * 4);
+  return r;
+}
+
+__device__ __forceinline__ float log_sigmoid2(float x) {
+  // log sigmoid(x) = min(x, 0) - log1p(exp(-|x|))
+  return fminf(x, 0.f) - log1pf(__expf(-fabsf(x)));
+}
+
+// 16-byte slot swizzle of a row with n slots: rows 16 apart in a fragment
+// read fall on distinct bank groups.
+__device__ __forceinline__ int mswz(int r, int n) { return n >= 16 ? (r & 15) : (r / (16 / n)) % n; }
+
+template <typename E> struct MOut;
+template <> struct MOut<float> {
+  static __device__ __forceinline__ void quad(float* p, f32x4 v) { *(f32x4*)p = v; }
+  static __device__ __forceinline__ void oct(float* p, const float* x) {
+    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+};
+template <> struct MOut<__bf16> {
+  static __device__ __forceinline__ void quad(__bf16* p, f32x4 v) { In<__bf16>::store4(p, v); }
+  static __device__ __forceinline__ void oct(__bf16* p, const float* x) {
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (__bf16)x[e];
+    *(bf16x8*)p = h;
+  }
+};
+
+// An operand slice of 1.0 in row 0 of a 16-row tile (the normaliser's "value").
+template <int MODE>
+__device__ __forceinline__ Frag<MODE> ones_row0(int c16) {
+  Frag<MODE> f;
+  const float x = c16 == 0 ? 1.f : 0.f;
+  if constexpr (MODE == kF32) {
+    f.a = f32x4{x, x, x, x};
+    f.b = f.a;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.hi[e] = (__bf16)x;
+  }
+  return f;
+}
+
+}  // namespace
+
+// ============================================================================ intra kernel
+constexpr int kMThreads = 512;
+
+template <typename Tin, int DK, int CM>
+struct MIntraSmem {
+  static constexpr bool F32 = std::is_same<Tin, float>::value;
+  static constexpr int NS = F32 ? 2 : 1;            // bf16 planes' worth of bytes per element
+  static constexpr int DVM = F32 ? 128 : 256;       // largest d_v
+  static constexpr int LDK = DK + 8, LDC = CM + 8;
+  static constexpr int QS = 0;                       // q   [t][j]
+  static constexpr int KS = QS + NS * CM * LDK * 2;  // k   [s][j]
+  static constexpr int VS = KS + NS * CM * LDK * 2;  // V^T [v][s], 8-row slots swizzled per 16 columns
+  static constexpr int WS = VS + NS * DVM * LDC * 2; // W   [t][s]
+  static constexpr int SC = align16m(WS + NS * CM * LDC * 2);  // fp32 F, a, A
+  static constexpr int TOTAL = SC + 3 * CM * 4;
+  static_assert(TOTAL <= 160 * 1024, "mLSTM intra kernel LDS exceeds 160 KiB");
+};
+
+template <typename Tin, int DK, int CM>
+__global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ i_tilde, const float* __restrict__ f_tilde, char* __restrict__ ws,
+    int T, int DV, int nchunks, int nitems) {
+  using L = MIntraSmem<Tin, DK, CM>;
+  constexpr bool F32 = L::F32;
+  constexpr int MM = F32 ? kF32 : kBF;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NW = kMThreads / 64;
+  constexpr int NB = CM / 16;
+  constexpr int NP = NB * (NB + 1) / 2;
+  constexpr int MAXP = (NP + NW - 1) / NW;
+  constexpr int ES = sizeof(Tin);
+  constexpr int KP = DK * ES / 16;                  // 16-byte pieces per q / k row
+  constexpr int NPQ = (CM * KP + kMThreads - 1) / kMThreads;
+  constexpr int NPV = (CM * L::DVM * ES / 16 + kMThreads - 1) / kMThreads;
+  constexpr int EP = 16 / ES;                       // elements per piece
+  constexpr int XM = CM / 8 - 1;
+  typedef u32x4 P16;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const MRec RL = mrec_layout(DK, DV, CM, ES);
+  const int VP = DV * ES / 16;                       // pieces per v row
+  const int NVT = DV / 16 + 1;                       // value tiles + the normaliser tile
+  float* sF = (float*)(smem + L::SC);
+  float* sa = sF + CM;
+  float* sAm = sa + CM;
+  auto voff = [](int col, int t) { return col * L::LDC + 8 * ((t >> 3) ^ ((col >> 4) & XM)) + (t & 7); };
+
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+
+  P16 xq[NPQ], xk[NPQ], xv[NPV];
+  float xf = 0.f, xi = 0.f;
+  auto issue = [&](int it) {
+    const int bh = it / nchunks, tb = (it % nchunks) * CM;
+    const char* qh = (const char*)(q + (size_t)bh * T * DK);
+    const char* kh = (const char*)(k + (size_t)bh * T * DK);
+    const char* vh = (const char*)(v + (size_t)bh * T * DV);
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      int p = tid + kMThreads * i;
+      p = p < CM * KP ? p : 0;
+      const int r = p / KP, c = p % KP, t = tb + r;
+      const size_t off = (size_t)(t < T ? t : T - 1) * DK * ES + 16 * c;
+      xq[i] = *(const P16*)(qh + off);
+      xk[i] = *(const P16*)(kh + off);
+    }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      int p = tid + kMThreads * i;
+      p = p < CM * VP ? p : 0;
+      const int r = p / VP, c = p % VP, t = tb + r;
+      xv[i] = *(const P16*)(vh + (size_t)(t < T ? t : T - 1) * DV * ES + 16 * c);
+    }
+    const int tg = tb + (lane < CM ? lane : 0);
+    const size_t og = (size_t)bh * T + (tg < T ? tg : T - 1);
+    xf = f_tilde[og];
+    xi = i_tilde[og];
+  };
+  // bf16: the next item's inputs are fetched during this item's products;
+  // fp32 fetches at the start of each item
+  if constexpr (!F32) issue(item);
+
+  for (; item < nitems; item += gridDim.x) {
+    if constexpr (F32) issue(item);
+    const int t0 = (item % nchunks) * CM;
+    char* rec = ws + (size_t)item * RL.bytes;
+
+    // ---- q, k -> LDS as they are; v -> V^T; rows past T are zero
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      const int p = tid + kMThreads * i;
+      if (p < CM * KP) {
+        const int r = p / KP, c = p % KP;
+        const bool ok = t0 + r < T;
+        const P16 z = {0u, 0u, 0u, 0u};
+        *(P16*)(smem + L::QS + (r * L::LDK) * 2 * L::NS + 16 * c) = ok ? xq[i] : z;
+        *(P16*)(smem + L::KS + (r * L::LDK) * 2 * L::NS + 16 * c) = ok ? xk[i] : z;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int p = tid + kMThreads * i;
+      if (p < CM * VP) {
+        const int r = p / VP, c0 = (p % VP) * EP;
+        const bool ok = t0 + r < T;
+        if constexpr (F32) {
+          const f32x4 x = __builtin_bit_cast(f32x4, xv[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ((float*)(smem + L::VS))[voff(c0 + e, r)] = ok ? x[e] : 0.f;
+        } else {
+          const u32x4 x = xv[i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t hv = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+            ((uint16_t*)(smem + L::VS))[voff(c0 + e, r)] = ok ? hv : (uint16_t)0;
+          }
+        }
+      }
+    }
+    // ---- gates: F (prefix sum of log sigmoid f~), a = i~ - F, A (prefix max of a)
+    if (wid == 0) {
+      const int t = lane;
+      const bool valid = t < CM && t0 + t < T;
+      float F = valid ? log_sigmoid2(xf) : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(F, off, 64);
+        if (lane >= off) F += y;
+      }
+      const float a = valid ? xi - F : -INFINITY;
+      float A = a;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(A, off, 64);
+        if (lane >= off) A = fmaxf(A, y);
+      }
+      if (t < CM) {
+        sF[t] = F;
+        sa[t] = a;
+        sAm[t] = A;
+        ((float*)(rec + RL.f))[t] = F;
+        ((float*)(rec + RL.a))[t] = A;
+      }
+    }
+    __syncthreads();
+    if constexpr (!F32) {
+      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x);
+    }
+
+    // ---- W[t][s] = (q_t . k_s) e^{a_s - A_t}, s <= t (transposed score tiles)
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+      const int p = wid + NW * i;
+      if (p < NP) {
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= p) ++I;
+        const int J = p - I * (I + 1) / 2;
+        f32x4 acc = f4zero();
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+          Frag<MM> A = ldfrag<MM>(smem + L::KS, 0, L::LDK, 16 * J, k0, DK, lane);
+          Frag<MM> B = ldfrag<MM>(smem + L::QS, 0, L::LDK, 16 * I, k0, DK, lane);
+          mma<MM>(acc, A, B);
+        }
+        const int t = 16 * I + c16, s0 = 16 * J + 4 * g;
+        const float At = sAm[t];
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = s0 + e;
+          w[e] = s <= t ? acc[e] * __expf(sa[s] - At) : 0.f;
+        }
+        st4<MM>(smem + L::WS, 0, t * L::LDC + s0, w);
+      }
+    }
+    __syncthreads();
+
+    // ---- H^T = [V^T; 1] W^T: tile (value tile vt, t-block I); the last value
+    // tile is the normaliser (row 0 all ones), whose row 0 gives N
+    const int nht = NVT * NB;
+    for (int qi = wid; qi < nht; qi += NW) {
+      const int vt = qi / NB, I = qi % NB, kend = 16 * (I + 1);
+      const bool nt = vt == NVT - 1;
+      f32x4 acc = f4zero();
+#pragma unroll
+      for (int k0 = 0; k0 < CM; k0 += 32) {
+        if (k0 < kend) {
+          const int kk = k0 + 8 * g;
+          Frag<MM> A;
+          if (nt) {
+            A = ones_row0<MM>(c16);
+          } else {
+            A = ldfrag<MM>(smem + L::VS, 0, L::LDC, 16 * vt, 8 * ((kk >> 3) ^ (vt & XM)) - 8 * g,
+                           CM, lane);
+          }
+          Frag<MM> B = ldfrag<MM>(smem + L::WS, 0, L::LDC, 16 * I, k0, kend, lane);
+          if (kk >= kend) A = ones_row0<MM>(-1);   // zero slice (B is zero there too)
+          mma<MM>(acc, A, B);
+        }
+      }
+      const int t = 16 * I + c16;
+      if (!nt) {
+        MOut<Tin>::quad((Tin*)(rec + RL.hi) + t * DV + 16 * vt + 4 * g, acc);
+      } else if (g == 0) {
+        ((float*)(rec + RL.ni))[t] = acc[0];
+      }
+    }
+
+    // ---- K~^T = (e^{a_s - A_C} k_s)^T and V^T to the record (16-byte pieces)
+    const float AC = sAm[CM - 1];
+    constexpr int SP = CM / 8;
+    for (int p = tid; p < DK * SP; p += kMThreads) {
+      const int j = p / SP, s0 = (p % SP) * 8;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = ld1<MM>(smem + L::KS, 0, (s0 + e) * L::LDK + j) * __expf(sa[s0 + e] - AC);
+      MOut<Tin>::oct((Tin*)(rec + RL.kt) + j * CM + s0, x);
+    }
+    for (int p = tid; p < DV * SP; p += kMThreads) {
+      const int col = p / SP, s0 = (p % SP) * 8;
+      const char* src = smem + L::VS + (size_t)voff(col, s0) * ES;
+      char* dst = rec + RL.vt + (col * CM + s0) * ES;
+      *(P16*)dst = *(const P16*)src;
+      if constexpr (F32) *(P16*)(dst + 16) = *(const P16*)(src + 16);
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================================ scan kernel
+constexpr int kMScanThreads = 512;
+
+template <typename Tin, int DK, int VT, int CM>
+struct MScanSmem {
+  static constexpr bool F32 = std::is_same<Tin, float>::value;
+  static constexpr int ES = sizeof(Tin);
+  static constexpr int WQ = DK * ES, WC = CM * ES, WH = VT * ES;   // row bytes
+  static constexpr int Q = 0;                        // q     [t][j]
+  static constexpr int KT = Q + CM * WQ;             // K~^T  [j][s]
+  static constexpr int VTS = KT + DK * WC;           // V^T   [v][s], this tile's rows
+  static constexpr int HI = VTS + VT * WC;           // H     [t][v], this tile's columns
+  static constexpr int SF = HI + CM * WH;            // F, A, N fp32 (record order N, F, A)
+  static constexpr int STAGE = align16m(SF + 3 * CM * 4);
+  static constexpr int NS = F32 ? 2 : 1;
+  static constexpr int NVA = VT / 16 + 1;            // value tiles + the normaliser tile
+  static constexpr int LDK = DK + 8;
+  static constexpr int S0T = STAGE;                  // [C | n]^T [v][j]
+  static constexpr int SN = S0T + NS * 16 * NVA * LDK * 2;   // n^ per t, fp32
+  static constexpr int TOTAL = SN + CM * 4;
+  static_assert(TOTAL <= 160 * 1024, "mLSTM scan LDS exceeds 160 KiB");
+  // 16-byte pieces of one chunk: q rows (from the input), then the record parts
+  static constexpr int NQP = CM * WQ / 16;
+  static constexpr int NKP = DK * WC / 16, NVP = VT * WC / 16, NHP = CM * WH / 16, NSP = 3 * CM * 4 / 16;
+  static constexpr int NRP = NKP + NVP + NHP + NSP;
+};
+
+template <typename Tin, int DK, int VT, int CM>
+__global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
+    const Tin* __restrict__ q, const char* __restrict__ ws, const float* __restrict__ C0,
+    const float* __restrict__ n0, const float* __restrict__ m0, Tin* __restrict__ h, float* C_out,
+    float* n_out, float* m_out, int T, int DV) {
+  using L = MScanSmem<Tin, DK, VT, CM>;
+  constexpr bool F32 = L::F32;
+  constexpr int MM = F32 ? kF32 : kBF;
+  constexpr int NW = kMScanThreads / 64;
+  constexpr int NVL = VT / 16, NVA = L::NVA;
+  constexpr int NB = CM / 16;
+  constexpr int KS = DK >= 32 ? DK / 32 : 1;
+  constexpr int KSC = CM >= 32 ? CM / 32 : 1;
+  // readout tiles: wave w takes t-block w % NB and value tiles w / NB,
+  // w / NB + NW / NB, ... (one q fragment per k step feeds all of them);
+  // state tiles: wave w takes j-blocks w, w + NW, ... with every value tile
+  // (one K~^T fragment feeds all value tiles, one V^T fragment all j-blocks)
+  constexpr int VSTEP = NW / NB;
+  constexpr int MAXR = (NVA + VSTEP - 1) / VSTEP;
+  constexpr int NJB = DK / 16;
+  constexpr int JPW = (NJB + NW - 1) / NW;
+  constexpr int MAXU = JPW * NVA;
+  constexpr int NPQ = (L::NQP + kMScanThreads - 1) / kMScanThreads;
+  constexpr int NPR = (L::NRP + kMScanThreads - 1) / kMScanThreads;
+  constexpr int LDK = L::LDK;
+  constexpr int P_S = 16 * NVA * LDK * 2;
+  typedef u32x4 P16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* S0T = smem + L::S0T;
+  float* sN = (float*)(smem + L::SN);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nvt = DV / VT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
+  const int nchunks = (T + CM - 1) / CM;
+  const MRec RL = mrec_layout(DK, DV, CM, L::ES);
+  const char* wsh = ws + (size_t)bh * nchunks * RL.bytes;
+  const char* qh = (const char*)(q + (size_t)bh * T * DK);
+
+  // ---- piece plan (fixed for the pass): q pieces by row; record pieces by offset
+  int qr[NPQ], qlo[NPQ];
+#pragma unroll
+  for (int i = 0; i < NPQ; ++i) {
+    int p = tid + kMScanThreads * i;
+    if (p >= L::NQP) p = L::NQP - 1;
+    constexpr int n = L::WQ / 16;
+    const int r = p / n, c = p % n;
+    qr[i] = r * L::WQ + 16 * c;
+    qlo[i] = L::Q + r * L::WQ + 16 * (c ^ mswz(r, n));
+  }
+  int rgo[NPR], rlo[NPR];
+#pragma unroll
+  for (int i = 0; i < NPR; ++i) {
+    int p = tid + kMScanThreads * i;
+    if (p >= L::NRP) p = L::NRP - 1;
+    int go, lo;
+    if (p < L::NKP) {
+      constexpr int n = L::WC / 16;
+      const int r = p / n, c = p % n;
+      go = RL.kt + r * L::WC + 16 * c;
+      lo = L::KT + r * L::WC + 16 * (c ^ mswz(r, n));
+    } else if (p < L::NKP + L::NVP) {
+      constexpr int n = L::WC / 16;
+      const int qq = p - L::NKP, r = qq / n, c = qq % n;
+      go = RL.vt + (vt0 + r) * L::WC + 16 * c;
+      lo = L::VTS + r * L::WC + 16 * (c ^ mswz(r, n));
+    } else if (p < L::NKP + L::NVP + L::NHP) {
+      constexpr int n = L::WH >= 16 ? L::WH / 16 : 1;
+      const int qq = p - L::NKP - L::NVP, r = qq / n, c = qq % n;
+      go = RL.hi + (r * DV + vt0) * L::ES + 16 * c;
+      lo = L::HI + r * L::WH + 16 * (c ^ mswz(r, n));
+    } else {
+      const int qq = p - L::NKP - L::NVP - L::NHP;
+      go = RL.ni + 16 * qq;
+      lo = L::SF + 16 * qq;
+    }
+    rgo[i] = go;
+    rlo[i] = lo;
+  }
+  struct Set {
+    P16 q[NPQ], r[NPR];
+  };
+  auto load = [&](int ch, Set& x) {
+    const int c = ch < nchunks ? ch : nchunks - 1;
+    const char* rec = wsh + (size_t)c * RL.bytes;
+    const int t0 = c * CM;
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      const int row = qr[i] / L::WQ, t = t0 + row;
+      const size_t off = (size_t)(t < T ? t : T - 1) * L::WQ + (qr[i] - row * L::WQ);
+      x.q[i] = *(const P16*)(qh + off);
+    }
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) x.r[i] = *(const P16*)(rec + rgo[i]);
+  };
+  auto stage = [&](const Set& x) {
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) *(P16*)(smem + qlo[i]) = x.q[i];
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) *(P16*)(smem + rlo[i]) = x.r[i];
+  };
+  // fragment of a staged swizzled row-major matrix (row bytes w)
+  auto sfrag = [&](int moff, int w, int row0, int k0) {
+    const int n = w / 16;
+    const int r = row0 + c16;
+    Frag<MM> f;
+    if constexpr (F32) {
+      const int c = ((k0 >> 2) + 2 * g) & (n - 1);   // 8 fp32 = two slots
+      f.a = *(const f32x4*)(smem + moff + r * w + 16 * (c ^ mswz(r, n)));
+      f.b = *(const f32x4*)(smem + moff + r * w + 16 * ((c + 1) ^ mswz(r, n)));
+    } else {
+      const int c = ((k0 >> 3) + g) & (n - 1);
+      f.hi = *(const bf16x8*)(smem + moff + r * w + 16 * (c ^ mswz(r, n)));
+    }
+    return f;
+  };
+
+  // ---- state [C | n] (j-block, value tile incl. normaliser) in registers, S0^T in LDS
+  const bool have_state = C0 != nullptr;
+  float mprev = have_state ? m0[bh] : -INFINITY;
+  f32x4 Sacc[MAXU];
+#pragma unroll
+  for (int i = 0; i < MAXU; ++i) {
+    Sacc[i] = f4zero();
+    const int jt = wid + NW * (i / NVA), vl = i % NVA;
+    if (jt < NJB) {
+      if (have_state) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * g + e;
+          if (vl < NVL) Sacc[i][e] = C0[(size_t)bh * DK * DV + (size_t)j * DV + vt0 + 16 * vl + c16];
+          else Sacc[i][e] = c16 == 0 ? n0[(size_t)bh * DK + j] : 0.f;
+        }
+      }
+      st4<MM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+    }
+  }
+
+  auto compute = [&](int ch) {
+    const int t0 = ch * CM;
+    const float* stF = (const float*)(smem + L::SF + CM * 4);
+    const float* stA = (const float*)(smem + L::SF + 2 * CM * 4);
+    const float* stN = (const float*)(smem + L::SF);
+    // readout tiles (value tile vl, t-block I): acc[v][t] = (q_t C0)[v]
+    const int I = wid % NB;
+    f32x4 hb[MAXR], acc[MAXR];
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) acc[i] = f4zero();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bool kv = 32 * s + 8 * g < DK;
+      Frag<MM> B = sfrag(L::Q, L::WQ, 16 * I, 32 * s);
+      if (!kv) B = ones_row0<MM>(-1);
+#pragma unroll
+      for (int i = 0; i < MAXR; ++i) {
+        const int vl = wid / NB + VSTEP * i;
+        if (vl < NVA) {
+          Frag<MM> A = ldfrag<MM>(S0T, P_S, LDK, 16 * vl, 32 * s, DK, lane);
+          mma<MM>(acc[i], A, B);
+        }
+      }
+    }
+    {
+      const int t = 16 * I + c16;
+      const float At = stA[t];
+      const float mu = fmaxf(mprev, At);
+      const float si = __expf(At - mu);
+      const float se = mprev == -INFINITY ? 0.f : __expf(mprev - mu);
+#pragma unroll
+      for (int i = 0; i < MAXR; ++i) {
+        const int vl = wid / NB + VSTEP * i;
+        hb[i] = f4zero();
+        if (vl < NVL) {
+          // H[t][16vl + 4g .. +3]
+          constexpr int n = L::WH >= 16 ? L::WH / 16 : 1;
+          const int byte = (16 * vl + 4 * g) * L::ES;
+          const int c = byte / 16;
+          const char* hp = smem + L::HI + t * L::WH + 16 * (c ^ mswz(t, n)) + (byte & 15);
+          f32x4 hv;
+          if constexpr (F32) {
+            hv = *(const f32x4*)hp;
+          } else {
+            typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+            hv = Raw<__bf16>::un4(*(const u2*)hp);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hb[i][e] = se * acc[i][e] + si * hv[e];
+        } else if (vl == NVL && g == 0) {
+          sN[t] = se * acc[i][0] + si * stN[t];
+        }
+      }
+    }
+    __syncthreads();
+    // normalise and store h
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      const int vl = wid / NB + VSTEP * i;
+      {
+        if (vl < NVL) {
+          const int t = 16 * I + c16, tg = t0 + t;
+          const float mu = fmaxf(mprev, stA[t]);
+          const float den = fmaxf(fabsf(sN[t]), __expf(-(stF[t] + mu)));
+          const float inv = 1.f / den;
+          f32x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = hb[i][e] * inv;
+          if (tg < T) In<Tin>::store4(h + ((size_t)bh * T + tg) * DV + vt0 + 16 * vl + 4 * g, hv);
+        }
+      }
+    }
+    // state: [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1]
+    const float AC = stA[CM - 1];
+    const float muC = fmaxf(mprev, AC);
+    const float dI = __expf(AC - muC);
+    const float dC = mprev == -INFINITY ? 0.f : __expf(mprev - muC);
+    f32x4 uacc[MAXU];
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) uacc[i] = f4zero();
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      const bool kv = 32 * s + 8 * g < CM;
+      Frag<MM> Bv[NVA];
+#pragma unroll
+      for (int vl = 0; vl < NVA; ++vl) {
+        Bv[vl] = vl < NVL ? sfrag(L::VTS, L::WC, 16 * vl, 32 * s) : ones_row0<MM>(c16);
+        if (!kv) Bv[vl] = ones_row0<MM>(-1);
+      }
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = wid + NW * jj;
+        if (jt < NJB) {
+          Frag<MM> A = sfrag(L::KT, L::WC, 16 * jt, 32 * s);
+#pragma unroll
+          for (int vl = 0; vl < NVA; ++vl) mma<MM>(uacc[jj * NVA + vl], A, Bv[vl]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+      const int jt = wid + NW * (i / NVA), vl = i % NVA;
+      if (jt < NJB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[i][e] = dC * Sacc[i][e] + dI * uacc[i][e];
+        st4<MM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+      }
+    }
+    mprev = stF[CM - 1] + muC;
+    __syncthreads();
+  };
+
+  // ---- pipeline: two register sets in turn, loads two chunks ahead of use,
+  // one LDS stage written between chunks
+  Set X0, X1;
+  load(0, X0);
+  load(1, X1);
+  stage(X0);
+  __syncthreads();
+  load(2, X0);
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    compute(ch);
+    stage(X1);
+    __syncthreads();
+    load(ch + 3, X1);
+    if (ch + 1 >= nchunks) break;
+    compute(ch + 1);
+    stage(X0);
+    __syncthreads();
+    load(ch + 4, X0);
+  }
+
+  if (C_out) {
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+      const int jt = wid + NW * (i / NVA), vl = i % NVA;
+      if (jt < NJB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * g + e;
+          if (vl < NVL) C_out[(size_t)bh * DK * DV + (size_t)j * DV + vt0 + 16 * vl + c16] = Sacc[i][e];
+          else if (c16 == 0 && vt0 == 0) n_out[(size_t)bh * DK + j] = Sacc[i][e];
+        }
+      }
+    }
+    if (tid == 0 && vt0 == 0) m_out[bh] = mprev;
+  }
+}
+
+// ------------------------------------------------------------------ host launch
+size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  const int es = dtype == GDR_BF16 ? 2 : 4;
+  const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
+  return (size_t)B * H * nchunks * (size_t)mrec_layout(dk, dv, chunk, es).bytes;
+}
+
+static int mdevice_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <typename Tin, int DK, int CM>
+static int launch_mintra(const MlstmArgs& a, char* ws) {
+  using L = MIntraSmem<Tin, DK, CM>;
+  auto kern = mlstm_intra_kernel<Tin, DK, CM>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
+        hipSuccess)
+      return GDR_ERR_LAUNCH;
+    attr_set = true;
+  }
+  int nchunks = (a.T + CM - 1) / CM;
+  int nitems = a.B * a.H * nchunks;
+  const int grid = nitems < mdevice_cus() ? nitems : mdevice_cus();
+  const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
+  const float *it = a.i_tilde, *ft = a.f_tilde;
+  int T = a.T, DV = a.dv;
+  void* args[] = {&q, &k, &v, &it, &ft, &ws, &T, &DV, &nchunks, &nitems};
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(grid), dim3(kMThreads), args, L::TOTAL,
+                                 (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+template <typename Tin, int DK, int VT, int CM>
+static int launch_mscan(const MlstmArgs& a, const char* ws) {
+  using L = MScanSmem<Tin, DK, VT, CM>;
+  auto kern = mlstm_scan_kernel<Tin, DK, VT, CM>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
+        hipSuccess)
+      return GDR_ERR_LAUNCH;
+    attr_set = true;
+  }
+  const int nblocks = a.B * a.H * (a.dv / VT);
+  const Tin* q = (const Tin*)a.q;
+  const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
+  Tin* h = (Tin*)a.h;
+  float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
+  int T = a.T, DV = a.dv;
+  void* args[] = {&q, &ws, &C0, &n0, &m0, &h, &Co, &no, &mo, &T, &DV};
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(kMScanThreads), args, L::TOTAL,
+                                 (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+template <typename Tin, int DK, int CM>
+static int mlstm_pair(const MlstmArgs& a, char* ws) {
+  const int st = launch_mintra<Tin, DK, CM>(a, ws);
+  if (st != GDR_OK) return st;
+  // value tiles of 32 columns when that still gives a workgroup per CU, else 16
+  const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= mdevice_cus();
+  if (!wide) return launch_mscan<Tin, DK, 16, CM>(a, ws);
+  return launch_mscan<Tin, DK, 32, CM>(a, ws);
+}
+
+template <typename Tin, int CM>
+static int mlstm_ws_dk(const MlstmArgs& a, char* ws) {
+  switch (a.dk) {
+    case 16: return mlstm_pair<Tin, 16, CM>(a, ws);
+    case 32: return mlstm_pair<Tin, 32, CM>(a, ws);
+    case 64: return mlstm_pair<Tin, 64, CM>(a, ws);
+    case 128: return mlstm_pair<Tin, 128, CM>(a, ws);
+    case 256:
+      if constexpr (std::is_same<Tin, __bf16>::value) return mlstm_pair<Tin, 256, CM>(a, ws);
+      break;
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+template <typename Tin>
+static int mlstm_ws_chunk(const MlstmArgs& a, char* ws) {
+  switch (a.chunk) {
+    case 16: return mlstm_ws_dk<Tin, 16>(a, ws);
+    case 32: return mlstm_ws_dk<Tin, 32>(a, ws);
+    case 64: return mlstm_ws_dk<Tin, 64>(a, ws);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+int mlstm_ws_launch(const MlstmArgs& a, void* ws) {
+  if (a.dtype == GDR_BF16) return mlstm_ws_chunk<__bf16>(a, (char*)ws);
+  return mlstm_ws_chunk<float>(a, (char*)ws);
+}
+
+}  // namespace gdr

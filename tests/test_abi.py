@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_three_entry_points():
     names = _declared()
     for n in ("gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_chunk_intra",
-              "gdr_chunk_scan", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_status_string", "gdr_version"):
+              "gdr_chunk_scan", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_mlstm_fwd_ws",
+              "gdr_mlstm_workspace_size", "gdr_status_string", "gdr_version"):
         assert n in names
 
 
@@ -189,6 +190,26 @@ def test_mlstm_validation(lib):
     assert f(h=P[0]) == c["GDR_ERR_ALIAS"]
     # n_out may not be n0 (all value tiles of a head read n0)
     assert f(C0=P[6], n0=P[7], m0=P[8], Co=P[9], no=P[7], mo=P[10]) == c["GDR_ERR_ALIAS"]
+
+
+def test_mlstm_ws_validation(lib):
+    c = _codes()
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_mlstm_workspace_size(1, 2, 64, 16, 16, 64, 1, ctypes.byref(n)) == c["GDR_OK"]
+    # record: H and V^T (C*dv each) + K~^T (dk*C) in the input dtype, then N, F, A (fp32)
+    assert n.value == 2 * 1 * ((16 * 64 * 2 + 16 * 64) * 2 + 3 * 64 * 4)
+    need = n.value
+
+    def f(ws=P[12], nbytes=need, dtype=1, dk=16, dv=16, h=P[5]):
+        return lib.gdr_mlstm_fwd_ws(P[0], P[1], P[2], P[3], P[4], None, None, None, h, None, None, None,
+                                    1, 2, 64, dk, dv, 64, dtype, ws, nbytes, None)
+
+    assert f(ws=None) == c["GDR_ERR_NULL"]
+    assert f(ws=P[12] + 4) == c["GDR_ERR_ALIGN"]
+    assert f(nbytes=need - 16) == c["GDR_ERR_WORKSPACE"]
+    assert f(ws=P[2] + 512) == c["GDR_ERR_ALIAS"]
+    assert f(h=P[0]) == c["GDR_ERR_ALIAS"]
+    assert f(dtype=0, dv=256) == c["GDR_ERR_UNSUPPORTED"]      # fp32 d_v > 128 on this path
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

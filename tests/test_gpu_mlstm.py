@@ -1,4 +1,6 @@
-"""Parity of gdr_mlstm_fwd (HIP, gfx950) with the float64 stabilised oracle.
+"""Parity of the mLSTM entry points (HIP, gfx950) with the float64 stabilised
+oracle: gdr_mlstm_fwd (one fused kernel) and gdr_mlstm_fwd_ws (intra-chunk
+kernel plus chunk scan through a workspace).
 
 The readout h is unique and compared directly. The stabiliser m is the running
 max of the xLSTM page in both implementations, so the scaled state (C, n, m)
@@ -13,17 +15,22 @@ from tests.gpu_util import TOL, dev, host, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(d, chunk, state=None):
+PATHS = ["fused", "ws"]
+
+
+def _run(d, chunk, state=None, path="ws"):
     import matrix_memory_rnn_amd as gdr
     t = lambda x: dev(d[x], d["dtype"])
     g = lambda x: dev(d[x], "f32")
     st = (None, None, None) if state is None else tuple(dev(x) for x in state)
-    return gdr.gdr_mlstm_fwd(t("q"), t("k"), t("v"), g("i_tilde"), g("f_tilde"), *st, chunk=chunk)
+    fn = gdr.gdr_mlstm_fwd if path == "fused" else gdr.gdr_mlstm_fwd_ws
+    return fn(t("q"), t("k"), t("v"), g("i_tilde"), g("f_tilde"), *st, chunk=chunk)
 
 
-def _check(d, chunk, label, state=None):
+def _check(d, chunk, label, state=None, path="ws"):
     import torch
-    h, C, n, m = _run(d, chunk, state)
+    label = f"{path} {label}"
+    h, C, n, m = _run(d, chunk, state, path)
     torch.cuda.synchronize()
     kw = {} if state is None else dict(C0=state[0], n0=state[1], m0=state[2])
     h_ref, C_ref, n_ref, m_ref = oracle.mlstm_stabilized(d["q"], d["k"], d["v"], d["i_tilde"],
@@ -35,38 +42,69 @@ def _check(d, chunk, label, state=None):
     assert eh <= tol and eC <= tol and en <= tol and em <= 1e-4 * max(1.0, np.abs(m_ref).max())
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,dv,chunk", [(16, 16, 16), (64, 64, 64), (128, 32, 32), (32, 128, 64)])
-def test_mlstm_shapes(dtype, dk, dv, chunk):
+@pytest.mark.parametrize("dk,dv,chunk", [(16, 16, 16), (64, 64, 64), (128, 32, 32), (32, 128, 64),
+                                         (128, 128, 64), (64, 16, 16)])
+def test_mlstm_shapes(path, dtype, dk, dv, chunk):
     d = mlstm_inputs(2, 2, 2 * chunk + 9, dk, dv, seed=dk + dv, dtype=dtype)
-    _check(d, chunk, f"{dtype} dk={dk} dv={dv} C={chunk}")
+    _check(d, chunk, f"{dtype} dk={dk} dv={dv} C={chunk}", path=path)
 
 
-def test_mlstm_dk256_bf16():
+@pytest.mark.parametrize("path", PATHS)
+def test_mlstm_dk256_bf16(path):
     d = mlstm_inputs(1, 2, 150, 256, 256, seed=2, dtype="bf16")
-    _check(d, 64, "bf16 dk=dv=256")
+    _check(d, 64, "bf16 dk=dv=256", path=path)
 
 
-def test_mlstm_with_initial_state_and_large_gates():
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T", [1, 7, 64, 65])
+def test_mlstm_short_sequences(path, T):
+    d = mlstm_inputs(1, 2, T, 64, 64, seed=T, dtype="bf16")
+    _check(d, 64, f"bf16 T={T}", path=path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mlstm_with_initial_state_and_large_gates(path):
     d = mlstm_inputs(2, 2, 100, 64, 64, seed=4, dtype="f32")
     d["i_tilde"][:, :, 30] = 60.0          # one very strong write
     rng = np.random.default_rng(4)
     C0 = rng.standard_normal((2, 2, 64, 64)).astype(np.float32).astype(np.float64)
     n0 = np.abs(rng.standard_normal((2, 2, 64))).astype(np.float32).astype(np.float64)
     m0 = np.array([[0.5, -1.0], [2.0, 0.0]])
-    _check(d, 32, "f32 with initial state, i_tilde = 60", state=(C0, n0, m0))
+    _check(d, 32, "f32 with initial state, i_tilde = 60", state=(C0, n0, m0), path=path)
 
 
-def test_full_size_mlstm_sampled_heads():
+@pytest.mark.parametrize("path", PATHS)
+def test_full_size_mlstm_sampled_heads(path):
     import torch
     c = CONFIGS["mlstm_8k"]
     d = mlstm_inputs(c["B"], c["H"], c["T"], c["dk"], c["dv"], seed=0, dtype=c["dtype"])
-    h, C, n, m = _run(d, c["chunk"])
+    h, C, n, m = _run(d, c["chunk"], path=path)
     torch.cuda.synchronize()
     h, C = host(h), host(C)
     for (bi, hi) in [(0, 0), (1, 7)]:
         sl = lambda x: x[bi:bi + 1, hi:hi + 1]
         h_ref, C_ref, _, _ = oracle.mlstm_stabilized(*(sl(d[x]) for x in ("q", "k", "v", "i_tilde", "f_tilde")))
         eh, eC = rel_err(sl(h), h_ref), rel_err(sl(C), C_ref)
-        say(f"[mlstm] full-size head (b={bi},h={hi}): err_h={eh:.3e} err_C={eC:.3e}")
+        say(f"[mlstm] {path} full-size head (b={bi},h={hi}): err_h={eh:.3e} err_C={eC:.3e}")
         assert eh <= TOL["bf16"] and eC <= TOL["bf16"]
+
+
+def test_mlstm_ws_agrees_with_fused_and_chains_state():
+    """Two halves through gdr_mlstm_fwd_ws with the state handed over equal one
+    call on the whole sequence (and the fused kernel) to within rounding."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    d = mlstm_inputs(2, 2, 200, 64, 64, seed=31, dtype="f32")
+    t = lambda x, sl=slice(None): dev(d[x][:, :, sl], "f32")
+    args = lambda sl: (t("q", sl), t("k", sl), t("v", sl), t("i_tilde", sl), t("f_tilde", sl))
+    h_all, C_all, n_all, m_all = gdr.gdr_mlstm_fwd_ws(*args(slice(None)), chunk=32)
+    h1, C1, n1, m1 = gdr.gdr_mlstm_fwd_ws(*args(slice(0, 96)), chunk=32)
+    h2, C2, n2, m2 = gdr.gdr_mlstm_fwd_ws(*args(slice(96, None)), C1, n1, m1, chunk=32)
+    hf, Cf, nf, mf = gdr.gdr_mlstm_fwd(*args(slice(None)), chunk=32)
+    torch.cuda.synchronize()
+    h_cat = np.concatenate([host(h1), host(h2)], axis=2)
+    assert rel_err(h_cat, host(h_all)) < 1e-5 and rel_err(host(C2), host(C_all)) < 1e-5
+    assert np.max(np.abs(host(m2) - host(m_all))) < 1e-4
+    assert rel_err(host(h_all), host(hf)) < 1e-5 and rel_err(host(C_all), host(Cf)) < 1e-5
