@@ -67,11 +67,12 @@ template <> struct MOut<__bf16> {
   }
 };
 
-// An operand slice of 1.0 in row 0 of a 16-row tile (the normaliser's "value").
+// An operand slice holding `val` in row 0 of a 16-row tile and 0 elsewhere
+// (the normaliser's "value" column); c16 = -1 gives a zero slice.
 template <int MODE>
-__device__ __forceinline__ Frag<MODE> ones_row0(int c16) {
+__device__ __forceinline__ Frag<MODE> ones_row0(int c16, float val = 1.f) {
   Frag<MODE> f;
-  const float x = c16 == 0 ? 1.f : 0.f;
+  const float x = c16 == 0 ? val : 0.f;
   if constexpr (MODE == kF32) {
     f.a = f32x4{x, x, x, x};
     f.b = f.a;
@@ -333,8 +334,7 @@ struct MScanSmem {
   static constexpr int NVA = VT / 16 + 1;            // value tiles + the normaliser tile
   static constexpr int LDK = DK + 8;
   static constexpr int S0T = STAGE;                  // [C | n]^T [v][j]
-  static constexpr int SN = S0T + NS * 16 * NVA * LDK * 2;   // n^ per t, fp32
-  static constexpr int TOTAL = SN + CM * 4;
+  static constexpr int TOTAL = S0T + NS * 16 * NVA * LDK * 2;
   static_assert(TOTAL <= 160 * 1024, "mLSTM scan LDS exceeds 160 KiB");
   // 16-byte pieces of one chunk: q rows (from the input), then the record parts
   static constexpr int NQP = CM * WQ / 16;
@@ -355,14 +355,14 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
   constexpr int NB = CM / 16;
   constexpr int KS = DK >= 32 ? DK / 32 : 1;
   constexpr int KSC = CM >= 32 ? CM / 32 : 1;
-  // readout tiles: wave w takes t-block w % NB and value tiles w / NB,
-  // w / NB + NW / NB, ... (one q fragment per k step feeds all of them);
-  // state tiles: wave w takes j-blocks w, w + NW, ... with every value tile
-  // (one K~^T fragment feeds all value tiles, one V^T fragment all j-blocks)
-  constexpr int VSTEP = NW / NB;
-  constexpr int MAXR = (NVA + VSTEP - 1) / VSTEP;
+  // Roles: waves w < NB read out t-block w (every value tile and the
+  // normaliser, so each normalises its own rows); the other NU waves update
+  // the state, wave NB + u owning j-blocks u, u + NU, ... with every value
+  // tile. The two run side by side on the same S0 and chunk data.
+  static_assert(NB < NW, "needs a wave for the state update");
+  constexpr int NU = NW - NB;
   constexpr int NJB = DK / 16;
-  constexpr int JPW = (NJB + NW - 1) / NW;
+  constexpr int JPW = (NJB + NU - 1) / NU;
   constexpr int MAXU = JPW * NVA;
   constexpr int NPQ = (L::NQP + kMScanThreads - 1) / kMScanThreads;
   constexpr int NPR = (L::NRP + kMScanThreads - 1) / kMScanThreads;
@@ -371,7 +371,6 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
   typedef u32x4 P16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* S0T = smem + L::S0T;
-  float* sN = (float*)(smem + L::SN);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -464,12 +463,14 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
   // ---- state [C | n] (j-block, value tile incl. normaliser) in registers, S0^T in LDS
   const bool have_state = C0 != nullptr;
   float mprev = have_state ? m0[bh] : -INFINITY;
+  const bool uw = wid >= NB;                        // state-update wave
+  const int uid = wid - NB;
   f32x4 Sacc[MAXU];
 #pragma unroll
   for (int i = 0; i < MAXU; ++i) {
     Sacc[i] = f4zero();
-    const int jt = wid + NW * (i / NVA), vl = i % NVA;
-    if (jt < NJB) {
+    const int jt = uid + NU * (i / NVA), vl = i % NVA;
+    if (uw && jt < NJB) {
       if (have_state) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -482,116 +483,107 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
     }
   }
 
+  // one chunk. Phase 1 (no barrier inside): readout waves form q C0 for
+  // their t-block, combine it with H and N, normalise and store h; update
+  // waves form the new [C | n] in registers. Phase 2, after a barrier (all
+  // reads of S0^T and of the stage done): update waves write S0^T.
   auto compute = [&](int ch) {
     const int t0 = ch * CM;
     const float* stF = (const float*)(smem + L::SF + CM * 4);
     const float* stA = (const float*)(smem + L::SF + 2 * CM * 4);
     const float* stN = (const float*)(smem + L::SF);
-    // readout tiles (value tile vl, t-block I): acc[v][t] = (q_t C0)[v]
-    const int I = wid % NB;
-    f32x4 hb[MAXR], acc[MAXR];
+    if (!uw) {
+      const int I = wid;
+      f32x4 acc[NVA];
 #pragma unroll
-    for (int i = 0; i < MAXR; ++i) acc[i] = f4zero();
+      for (int vl = 0; vl < NVA; ++vl) acc[vl] = f4zero();
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bool kv = 32 * s + 8 * g < DK;
-      Frag<MM> B = sfrag(L::Q, L::WQ, 16 * I, 32 * s);
-      if (!kv) B = ones_row0<MM>(-1);
+      for (int s = 0; s < KS; ++s) {
+        const bool kv = 32 * s + 8 * g < DK;
+        Frag<MM> B = sfrag(L::Q, L::WQ, 16 * I, 32 * s);
+        if (!kv) B = ones_row0<MM>(-1);
 #pragma unroll
-      for (int i = 0; i < MAXR; ++i) {
-        const int vl = wid / NB + VSTEP * i;
-        if (vl < NVA) {
+        for (int vl = 0; vl < NVA; ++vl) {
           Frag<MM> A = ldfrag<MM>(S0T, P_S, LDK, 16 * vl, 32 * s, DK, lane);
-          mma<MM>(acc[i], A, B);
+          mma<MM>(acc[vl], A, B);
         }
       }
-    }
-    {
-      const int t = 16 * I + c16;
+      // acc[vl][e] = (q_t C0)[v = 16vl + 4g + e] for t = 16I + c16; the
+      // normaliser tile's row 0 (lanes g = 0, e = 0) is q_t . n0
+      const int t = 16 * I + c16, tg = t0 + t;
       const float At = stA[t];
       const float mu = fmaxf(mprev, At);
       const float si = __expf(At - mu);
       const float se = mprev == -INFINITY ? 0.f : __expf(mprev - mu);
+      const float nq = __shfl(acc[NVL][0], c16, 64);   // lane (g = 0, c16) holds q_t . n0
+      const float nbar = se * nq + si * stN[t];
+      const float den = fmaxf(fabsf(nbar), __expf(-(stF[t] + mu)));
+      const float inv = 1.f / den;
 #pragma unroll
-      for (int i = 0; i < MAXR; ++i) {
-        const int vl = wid / NB + VSTEP * i;
-        hb[i] = f4zero();
-        if (vl < NVL) {
-          // H[t][16vl + 4g .. +3]
-          constexpr int n = L::WH >= 16 ? L::WH / 16 : 1;
-          const int byte = (16 * vl + 4 * g) * L::ES;
-          const int c = byte / 16;
-          const char* hp = smem + L::HI + t * L::WH + 16 * (c ^ mswz(t, n)) + (byte & 15);
-          f32x4 hv;
-          if constexpr (F32) {
-            hv = *(const f32x4*)hp;
+      for (int vl = 0; vl < NVL; ++vl) {
+        // H[t][16vl + 4g .. +3]
+        constexpr int n = L::WH >= 16 ? L::WH / 16 : 1;
+        const int byte = (16 * vl + 4 * g) * L::ES;
+        const int c = byte / 16;
+        const char* hp = smem + L::HI + t * L::WH + 16 * (c ^ mswz(t, n)) + (byte & 15);
+        f32x4 hv;
+        if constexpr (F32) {
+          hv = *(const f32x4*)hp;
+        } else {
+          typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+          hv = Raw<__bf16>::un4(*(const u2*)hp);
+        }
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (se * acc[vl][e] + si * hv[e]) * inv;
+        if (tg < T) In<Tin>::store4(h + ((size_t)bh * T + tg) * DV + vt0 + 16 * vl + 4 * g, o);
+      }
+    } else {
+      // [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1]
+      const float AC = stA[CM - 1];
+      const float muC = fmaxf(mprev, AC);
+      const float dI = __expf(AC - muC);
+      const float dC = mprev == -INFINITY ? 0.f : __expf(mprev - muC);
+#pragma unroll
+      for (int i = 0; i < MAXU; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[i][e] *= dC;
+      // e^{A_C - mu_C} is folded into the shared [V | 1] operand slices
+      const float dv8[8] = {dI, dI, dI, dI, dI, dI, dI, dI};
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        const bool kv = 32 * s + 8 * g < CM;
+        Frag<MM> Bv[NVA];
+#pragma unroll
+        for (int vl = 0; vl < NVA; ++vl) {
+          if (vl < NVL) {
+            Bv[vl] = sfrag(L::VTS, L::WC, 16 * vl, 32 * s);
+            scale_frag<MM>(Bv[vl], dv8);
           } else {
-            typedef __attribute__((ext_vector_type(2))) uint32_t u2;
-            hv = Raw<__bf16>::un4(*(const u2*)hp);
+            Bv[vl] = ones_row0<MM>(c16, dI);
           }
+          if (!kv) Bv[vl] = ones_row0<MM>(-1);
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hb[i][e] = se * acc[i][e] + si * hv[e];
-        } else if (vl == NVL && g == 0) {
-          sN[t] = se * acc[i][0] + si * stN[t];
+        for (int jj = 0; jj < JPW; ++jj) {
+          const int jt = uid + NU * jj;
+          if (jt < NJB) {
+            Frag<MM> A = sfrag(L::KT, L::WC, 16 * jt, 32 * s);
+#pragma unroll
+            for (int vl = 0; vl < NVA; ++vl) mma<MM>(Sacc[jj * NVA + vl], A, Bv[vl]);
+          }
         }
       }
     }
+    mprev = stF[CM - 1] + fmaxf(mprev, stA[CM - 1]);
     __syncthreads();
-    // normalise and store h
+    if (uw) {
 #pragma unroll
-    for (int i = 0; i < MAXR; ++i) {
-      const int vl = wid / NB + VSTEP * i;
-      {
-        if (vl < NVL) {
-          const int t = 16 * I + c16, tg = t0 + t;
-          const float mu = fmaxf(mprev, stA[t]);
-          const float den = fmaxf(fabsf(sN[t]), __expf(-(stF[t] + mu)));
-          const float inv = 1.f / den;
-          f32x4 hv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hv[e] = hb[i][e] * inv;
-          if (tg < T) In<Tin>::store4(h + ((size_t)bh * T + tg) * DV + vt0 + 16 * vl + 4 * g, hv);
-        }
+      for (int i = 0; i < MAXU; ++i) {
+        const int jt = uid + NU * (i / NVA), vl = i % NVA;
+        if (jt < NJB) st4<MM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
       }
     }
-    // state: [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1]
-    const float AC = stA[CM - 1];
-    const float muC = fmaxf(mprev, AC);
-    const float dI = __expf(AC - muC);
-    const float dC = mprev == -INFINITY ? 0.f : __expf(mprev - muC);
-    f32x4 uacc[MAXU];
-#pragma unroll
-    for (int i = 0; i < MAXU; ++i) uacc[i] = f4zero();
-#pragma unroll
-    for (int s = 0; s < KSC; ++s) {
-      const bool kv = 32 * s + 8 * g < CM;
-      Frag<MM> Bv[NVA];
-#pragma unroll
-      for (int vl = 0; vl < NVA; ++vl) {
-        Bv[vl] = vl < NVL ? sfrag(L::VTS, L::WC, 16 * vl, 32 * s) : ones_row0<MM>(c16);
-        if (!kv) Bv[vl] = ones_row0<MM>(-1);
-      }
-#pragma unroll
-      for (int jj = 0; jj < JPW; ++jj) {
-        const int jt = wid + NW * jj;
-        if (jt < NJB) {
-          Frag<MM> A = sfrag(L::KT, L::WC, 16 * jt, 32 * s);
-#pragma unroll
-          for (int vl = 0; vl < NVA; ++vl) mma<MM>(uacc[jj * NVA + vl], A, Bv[vl]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < MAXU; ++i) {
-      const int jt = wid + NW * (i / NVA), vl = i % NVA;
-      if (jt < NJB) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Sacc[i][e] = dC * Sacc[i][e] + dI * uacc[i][e];
-        st4<MM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
-      }
-    }
-    mprev = stF[CM - 1] + muC;
-    __syncthreads();
   };
 
   // ---- pipeline: two register sets in turn, loads two chunks ahead of use,
@@ -614,10 +606,10 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
     load(ch + 4, X0);
   }
 
-  if (C_out) {
+  if (C_out && uw) {
 #pragma unroll
     for (int i = 0; i < MAXU; ++i) {
-      const int jt = wid + NW * (i / NVA), vl = i % NVA;
+      const int jt = uid + NU * (i / NVA), vl = i % NVA;
       if (jt < NJB) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -627,8 +619,8 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
         }
       }
     }
-    if (tid == 0 && vt0 == 0) m_out[bh] = mprev;
   }
+  if (C_out && tid == 0 && vt0 == 0) m_out[bh] = mprev;
 }
 
 // ------------------------------------------------------------------ host launch
