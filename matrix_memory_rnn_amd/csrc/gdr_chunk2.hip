@@ -43,6 +43,22 @@ __host__ __device__ __forceinline__ RecLayout rec_layout(int dk, int dv, int C, 
   return r;
 }
 
+// "F order" of the bf16 record, read by the 32x32x16 MFMA scan: every matrix
+// is stored so that one 32x32x16 operand slice is 1 KiB of consecutive bytes,
+// lane l's 16 bytes at 16*l. For a row-major R x K matrix (Y, Q_pi, M: rows t;
+// K~^T: rows j) the 8 elements k = 8c .. 8c+7 of row r form 16-byte piece
+// ((r/32)*(K/16) + c/2)*64 + (c%2)*32 + r%32 (element offset returned).
+__host__ __device__ __forceinline__ int fm_off(int r, int k, int K) {
+  return ((((r >> 5) * (K >> 4) + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 + (r & 31)) << 3) + (k & 7);
+}
+// U^T in F order: for value tile v/32 and row block t/32, lane l holds the 16
+// entries v = 32*(v/32) + 8q + 4*(l/32) + e (q, e = 0..3; entry 4q + e) of
+// row t = 32*(t/32) + l%32, contiguous: the accumulator layout of V~^T.
+__host__ __device__ __forceinline__ int fu_off(int v, int t, int C) {
+  return ((((v >> 5) * (C >> 5) + (t >> 5)) * 64 + ((v >> 2) & 1) * 32 + (t & 31)) << 4) +
+         (((v >> 3) & 3) << 2) + (v & 3);
+}
+
 // Stores of record entries from fp32 values.
 template <typename E> struct Out;
 template <> struct Out<float> {
@@ -129,17 +145,22 @@ struct IntraSmem {
   static constexpr int SCL = align16(X_END);        // Gram scale vectors fp32 [pair][j]
   static constexpr int GS = SCL + NPM * DK * 4;     // block totals fp32 [I][j]
   static constexpr int FLAG = GS + NBM * DK * 4;    // guard flags [4]
-  static constexpr int TOTAL = FLAG + 16;
+  // U staging [t][v] (bf16 records in F order): the solve's U tiles are
+  // transposed through it so the record stores are 16-byte and coalesced
+  static constexpr int LDU = kMaxDv + 8;
+  static constexpr int US = align16(FLAG + 16);
+  static constexpr int TOTAL = F32 ? FLAG + 16 : US + CM * LDU * 2;
   static_assert(TOTAL <= 160 * 1024, "intra kernel LDS exceeds 160 KiB");
 };
 
-template <typename Tin, int DK, int CM>
+template <typename Tin, int DK, int CM, bool FM>
 __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
     char* __restrict__ ws, int T, int DV, int nchunks, int nitems) {
   using L = IntraSmem<Tin, DK, CM>;
   constexpr bool F32 = L::F32;
+  static_assert(!FM || (!F32 && DK % 32 == 0 && CM % 32 == 0), "F order needs bf16, d_k and C multiples of 32");
   constexpr int MM = F32 ? kF32 : kBF;   // Gram operands
   constexpr int MT = F32 ? kF32 : kSP;   // triangular solve
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -163,6 +184,11 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   // while a 16-column fragment read still sees one uniform slot order
   constexpr int XM = CM / 8 - 1;
   auto xoff = [](int col, int t) { return col * L::LDC + 8 * ((t >> 3) ^ ((col >> 4) & XM)) + (t & 7); };
+  // record element offsets: row-major, or F order for the 32x32x16 scan
+  auto o_tk = [](int t, int jj) { return FM ? fm_off(t, jj, DK) : t * DK + jj; };   // Y, Q_pi
+  auto o_kt = [](int jj, int t) { return FM ? fm_off(jj, t, CM) : jj * CM + t; };   // K~^T
+  auto o_m = [](int t, int s) { return FM ? fm_off(t, s, CM) : t * CM + s; };       // M
+  auto o_ut = [](int vv, int t) { return FM ? fu_off(vv, t, CM) : vv * CM + t; };    // U^T
 
   float* GS = (float*)(smem + L::GS);
   float* SCL = (float*)(smem + L::SCL);
@@ -317,7 +343,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         st2<MM>(smem + L::KR, L::P_CK, off, krx, kry);
         st2<MM>(smem + L::QR, L::P_CK, off, qrx, qry);
         khp[r] = make_float2(Bst.x * krx, Bst.y * kry);
-        Out<Tin>::pair(QPg + (r0 + r) * DK + j, Bst.x * qrx, Bst.y * qry);
+        if constexpr (FM)   // staged [t][j] in US, stored in F order after the Gram tiles
+          Out<Tin>::pair((Tin*)(smem + L::US) + (r0 + r) * L::LDU + j, Bst.x * qrx, Bst.y * qry);
+        else
+          Out<Tin>::pair(QPg + o_tk(r0 + r, j), Bst.x * qrx, Bst.y * qry);
       }
       float ktx[8], kty[8];
       float2 qs = h ? make_float2(1.f, 1.f) : p1;
@@ -331,8 +360,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         qs.x *= a.x;
         qs.y *= a.y;
       }
-      Out<Tin>::oct(KTg + j * CM + r0, ktx);
-      Out<Tin>::oct(KTg + (j + 1) * CM + r0, kty);
+      Out<Tin>::oct(KTg + o_kt(j, r0), ktx);
+      Out<Tin>::oct(KTg + o_kt(j + 1, r0), kty);
       if constexpr (L::XR_EARLY) {
 #pragma unroll
         for (int r4 = 0; r4 < 2; ++r4) {
@@ -376,6 +405,15 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     }
     __syncthreads();
 
+    if constexpr (FM) {
+      // Q_pi from its staging rows to the record: consecutive threads write
+      // consecutive F-order pieces (US is free again before the solve)
+      for (int idx = tid; idx < CM * DK / 8; idx += kIntraThreads) {
+        const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31), pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
+        *(u32x4*)(QPg + 8 * idx) = *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc));
+      }
+    }
+
     // ================= L blocks (fp32, LDS), M (record), right-hand sides [V^ | K^_pi]^T
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
@@ -394,7 +432,12 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           }
         }
         *(f32x4*)(LBK + p * BLKF + c16 * L::LDB + 4 * g) = lv;
-        Out<Tin>::quad(Mg + t * CM + s0, mv);
+        Out<Tin>::quad(Mg + o_m(t, s0), mv);
+        // F order: the scan multiplies M in 32-column slices up to the
+        // diagonal, so the block right of an even diagonal block is zero
+        if constexpr (FM) {
+          if (I == J && (I & 1) == 0) Out<Tin>::quad(Mg + o_m(t, s0 + 16), f4zero());
+        }
       }
     }
     if constexpr (!L::XR_EARLY) {
@@ -505,7 +548,14 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         if (ct < NX) {
           st4<MT>(smem + L::XR, L::P_XC, xoff(16 * ct + c16, 16 * I + 4 * g), acc[i]);
           if (16 * ct < DV) {
-            Out<Tin>::quad(UTg + (16 * ct + c16) * CM + 16 * I + 4 * g, acc[i]);
+            if constexpr (FM) {
+              // F order wants four consecutive v of one t per 8 bytes: staged in LDS
+              Tin* US = (Tin*)(smem + L::US);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) US[(16 * I + 4 * g + e) * L::LDU + 16 * ct + c16] = (Tin)acc[i][e];
+            } else {
+              Out<Tin>::quad(UTg + o_ut(16 * ct + c16, 16 * I + 4 * g), acc[i]);
+            }
           } else {
             const int jj = 16 * ct - DV + c16;
 #pragma unroll
@@ -520,8 +570,31 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     // ================= Y rows to the record (16-byte pieces)
     constexpr int YPR = DK * (int)sizeof(Tin) / 16;  // 16-byte pieces per row
     for (int idx = tid; idx < CM * YPR; idx += kIntraThreads) {
-      const int t = idx / YPR, pc = idx % YPR;
-      *(u32x4*)((char*)(Yg + t * DK) + 16 * pc) = *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc);
+      if constexpr (FM) {
+        // consecutive threads write consecutive F-order pieces
+        static_assert(!FM || sizeof(Tin) == 2, "F order is bf16");
+        const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31), pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
+        *(u32x4*)(Yg + 8 * idx) = *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc);
+      } else {
+        const int t = idx / YPR, pc = idx % YPR;
+        *(u32x4*)(Yg + o_tk(t, 16 * pc / (int)sizeof(Tin))) = *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc);
+      }
+    }
+    if constexpr (FM) {
+      // U^T in F order: each 32-byte lane slot holds v = 32*vt + 8q + 4*hh + e
+      // of row t = 32*i2 + l%32 (entry 4q + e): four 8-byte runs of a US row
+      typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+      const char* USb = smem + L::US;
+      const int nslots = (DV / 32) * (CM / 32) * 64;
+      for (int sidx = tid; sidx < nslots; sidx += kIntraThreads) {
+        const int ln = sidx & 63, blk = sidx >> 6;
+        const int t = 32 * (blk % (CM / 32)) + (ln & 31), vb = 32 * (blk / (CM / 32)) + 4 * (ln >> 5);
+        const char* row = USb + 2 * (t * L::LDU + vb);
+        const u2 a0 = *(const u2*)(row), a1 = *(const u2*)(row + 16), a2 = *(const u2*)(row + 32),
+                 a3 = *(const u2*)(row + 48);
+        *(u32x4*)(UTg + 16 * sidx) = u32x4{a0.x, a0.y, a1.x, a1.y};
+        *(u32x4*)(UTg + 16 * sidx + 8) = u32x4{a2.x, a2.y, a3.x, a3.y};
+      }
     }
   }
 }
@@ -978,6 +1051,337 @@ __global__ __launch_bounds__(kScanThreads, 1) void gdn2_chunk_scan_staged_kernel
   }
 }
 
+// ============================================================================ F-order scan
+// The chunk pass of the scan kernels above for a bf16 record in F order, with
+// 32x32x16 MFMAs: one workgroup of ten waves per (b, h, 32 value columns).
+// Each record operand has a single consumer wave, so every wave loads its own
+// fragments straight from the record into registers (1 KiB coalesced per
+// slice); only S0, V~ and a partial O pass through LDS. Two barriers split a
+// chunk into phase 1 and phase 2, and every wave computes in one phase and
+// reloads its registers (for a later chunk) in the other: a load can stall
+// its wave at issue while the memory pipeline is busy, and that way the stall
+// holds up no other wave.
+//   V,  waves 0-1 (I2 = w):    phase 1  V~^T rows t = 32*I2.. = U^T - S0^T Y^T -> LDS
+//   O1, waves 2-3 (I2 = w-2):  phase 1  P = S0^T Q_pi^T -> LDS (fp32)
+//   O2, waves 4-5 (I2 = w-4):  phase 2  O^T = P + V~^T M^T, stored
+//   S,  waves 6-9 (J2 = w-6):  phase 2  state rows 32*J2..: S = Diag(pi_C) S + K~^T V~ -> LDS
+// The S waves also touch the record PF chunks ahead so that the other loads
+// hit L2. 32x32x16 lane layout (l = 32h + r): A[m = r][k = 8h + i],
+// B[k = 8h + i][n = r], accumulator entry 4q + e = D[m = 8q + 4h + e][n = r].
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+constexpr int kScanFmWaves = 10;
+constexpr int kScanFmThreads = 64 * kScanFmWaves;
+constexpr int kScanFmPrefetch = 3;   // chunks ahead that the record is pulled into L2
+constexpr int kScanFmSets = 3;       // register sets per wave: loads run NS - 1 chunks ahead
+
+__device__ __forceinline__ f32x16 mma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+template <int N> struct Ic { static constexpr int value = N; };
+__device__ __forceinline__ f32x16 f16zero() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+// Workgroup barrier that the compiler may not schedule anything across, so
+// each phase keeps its own instructions.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int DK, int CM, int PF, int NS>
+__global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
+    const char* __restrict__ ws, const float* __restrict__ S0, __bf16* __restrict__ o, float* S_out,
+    int T, int DV) {
+  constexpr int NI2 = CM / 32, NJ2 = DK / 32, KSD = DK / 16, KSC = CM / 16;
+  constexpr int LDK = DK + 8, LDC = CM + 8;      // LDS row pitches (elements): 16-byte reads conflict free
+  static_assert(DK % 32 == 0 && CM % 32 == 0 && NJ2 <= 4 && NI2 <= 2, "F-order scan shape");
+  __shared__ __attribute__((aligned(16))) __bf16 S0T[32 * LDK];   // S0^T [v][j] (bf16 copy of the state)
+  __shared__ __attribute__((aligned(16))) __bf16 VTT[32 * LDC];   // V~^T [v][t]
+  __shared__ __attribute__((aligned(16))) f32x4 OP[2][4][64];     // partial O^T per row block, per lane
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r = lane & 31;
+  const int nvt = DV / 32;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, vt = lin % nvt, vt0 = 32 * vt;
+  const int nchunks = (T + CM - 1) / CM;
+  const size_t stOff = (size_t)bh * DK * DV;
+  const RecLayout RL = rec_layout(DK, DV, CM, 2);
+  const char* wsh = ws + (size_t)bh * nchunks * RL.bytes;
+  // the records of this head through a buffer resource; the wave-uniform
+  // part of each offset goes in the scalar offset, past the last chunk the
+  // loads repeat it
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wsh), 0, nchunks * RL.bytes, 0x00020000);
+  auto ld16 = [&](int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, soff, 0));
+  };
+  auto cbase = [&](int ch) { return (ch < nchunks ? ch : nchunks - 1) * RL.bytes; };
+  const int l16 = lane * 16;
+  auto s0frag = [&](int s) { return *(const u32x4*)(S0T + r * LDK + 16 * s + 8 * h); };
+  auto vfrag = [&](int s) { return *(const u32x4*)(VTT + r * LDC + 16 * s + 8 * h); };
+  // Each role walks all chunks with two barriers per chunk. Its loop is
+  // unrolled by hand over the register sets (every set keeps its registers)
+  // and has a single exit (so the compiler's wait counts stay exact), with the
+  // leftover chunks after it.
+  static_assert(NS == 3 && PF == 3, "the role loops below are unrolled for three register sets");
+  auto walk = [&](auto&& step) {
+    int ch = 0;
+    for (; ch + 3 <= nchunks; ch += 3) {
+      step(ch, Ic<0>{});
+      step(ch + 1, Ic<1>{});
+      step(ch + 2, Ic<2>{});
+    }
+    if (ch < nchunks) step(ch, Ic<0>{});
+    if (ch + 1 < nchunks) step(ch + 1, Ic<1>{});
+  };
+
+  if (wid < 2) {
+    // ================= V: V~^T = U^T - S0^T Y^T, rows t = 32*I2 ..
+    const int I2 = wid;
+    const bool live = NI2 >= 2 || I2 < NI2;
+    const int b_y = RL.y + I2 * KSD * 1024, b_u = RL.ut + (vt * NI2 + I2) * 2048;
+    constexpr int NPV = KSD + 2;
+    u32x4 R[NS][NPV];
+    auto load = [&](int ch, u32x4* X) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) X[s] = ld16(l16, cb + b_y + 1024 * s);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) X[KSD + s] = ld16(lane * 32, cb + b_u + 16 * s);
+    };
+    __syncthreads();                                    // S0^T written
+    __builtin_amdgcn_s_waitcnt(0);   // nothing outstanding: keeps merged code from loosening the counts below
+    if (live) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        load(u, R[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      if (live) {
+        f32x16 acc = f16zero();
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) acc = mma32(s0frag(s), R[u][s], acc);
+        // entry 4q + e is (v = 8q + 4h + e, t = 32 I2 + r)
+        __bf16* vd = VTT + 4 * h * LDC + 32 * I2 + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4& up = R[u][KSD + (q >> 1)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = up[2 * (q & 1) + (e >> 1)];
+            const float uu = (e & 1) ? Raw<__bf16>::hi(w) : Raw<__bf16>::lo(w);
+            vd[(8 * q + e) * LDC] = (__bf16)(uu - acc[4 * q + e]);
+          }
+        }
+      }
+      phase_barrier();                                  // A: V~ ready
+      // the set just used, for chunk ch + NS
+      if (live) load(ch + NS, R[u]);
+      phase_barrier();                                  // B: S0 ready
+    });
+  } else if (wid < 4) {
+    // ================= O1: P = S0^T Q_pi^T, rows t = 32*I2 ..
+    const int I2 = wid - 2;
+    const bool live = NI2 >= 2 || I2 < NI2;
+    const int b_q = RL.qp + I2 * KSD * 1024;
+    u32x4 RQ[NS][KSD];
+    auto load = [&](int ch, u32x4* X) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) X[s] = ld16(l16, cb + b_q + 1024 * s);
+    };
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (live) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        load(u, RQ[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      if (live) {
+        f32x16 acc = f16zero();
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) acc = mma32(s0frag(s), RQ[u][s], acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) OP[I2][q][lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      }
+      phase_barrier();                                  // A
+      if (live) load(ch + NS, RQ[u]);
+      phase_barrier();                                  // B
+    });
+  } else if (wid < 6) {
+    // ================= O2: O^T = P + V~^T M^T, rows t = 32*I2 .., stored
+    auto run = [&](auto Ic2) {
+      constexpr int I2 = decltype(Ic2)::value;
+      constexpr int NM = 2 * (I2 + 1) < KSC ? 2 * (I2 + 1) : KSC;   // M slices up to the diagonal
+      const int b_m = RL.m + I2 * KSC * 1024;
+      // O of this head from the chunk's first row to row T through a buffer
+      // resource: rows past T are dropped by the hardware. Lane l stores row
+      // t0 + 32 I2 + l % 32, columns vt0 + 8q + 4h ..
+      const int oct = ((32 * I2 + r) * DV + vt0 + 4 * h) * 2;
+      u32x4 RM[NS][NM];
+      auto load = [&](int ch, u32x4* X) {
+        const int cb = cbase(ch);
+#pragma unroll
+        for (int s = 0; s < NM; ++s) X[s] = ld16(l16, cb + b_m + 1024 * s);
+      };
+      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int u = 0; u < NS - 2; ++u) {
+        load(u, RM[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      walk([&](int ch, auto Uc) {
+        constexpr int u = decltype(Uc)::value;
+        // phase 1 is idle here: reload the set the previous chunk used
+        load(ch + NS - 2, RM[(u + NS - 2) % NS]);
+        phase_barrier();                                // A
+        f32x16 acc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 pq = OP[I2][q][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * q + e] = pq[e];
+        }
+#pragma unroll
+        for (int s = 0; s < NM; ++s) acc = mma32(vfrag(s), RM[u][s], acc);
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+        const int t0 = ch * CM;
+        const __amdgpu_buffer_rsrc_t orsrc =
+            __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4 x = bf16x4{(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2],
+                                  (__bf16)acc[4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, x), orsrc, oct + 16 * q, 0, 0);
+        }
+        phase_barrier();                                // B
+      });
+    };
+    const int I2 = wid - 4;
+    if (NI2 < 2 && I2 >= NI2) {
+      __syncthreads();
+      walk([&](int, auto) { phase_barrier(); phase_barrier(); });
+    } else if (I2 == 0) {
+      run(Ic<0>{});
+    } else {
+      run(Ic<(NI2 >= 2 ? 1 : 0)>{});
+    }
+  } else {
+    // ================= S: state rows 32*J2 .. of columns vt0 .. vt0+31
+    const int J2 = wid - 6;
+    const bool live = NJ2 >= 4 || J2 < NJ2;
+    const int b_k = RL.kt + J2 * KSC * 1024, b_p = RL.pic + 128 * J2;
+    u32x4 RK[NS][KSC];
+    float RP[NS];
+    auto load = [&](int ch, u32x4* X, float& pv) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) X[s] = ld16(l16, cb + b_k + 1024 * s);
+      pv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wrsrc, 4 * r, cb + b_p, 0));  // pi_C[32 J2 + r]
+    };
+    // L2 warm-up: three S waves of each value-tile workgroup of a head touch
+    // the record's 128-byte lines, one dword per lane, PF chunks ahead; the
+    // values are folded into `sink` when that chunk comes up, so the loads
+    // are kept and never waited for early
+    constexpr int kLine = 128;
+    const int nlines = (RL.bytes + kLine - 1) / kLine;
+    const int pl = (vt % 4) * 192 + (J2 % 3) * 64 + lane;
+    const int v_pf = (pl < nlines ? pl : nlines - 1) * kLine;
+    const bool toucher = live && J2 < 3;
+    auto touch = [&](int ch) { return __builtin_amdgcn_raw_buffer_load_b32(wrsrc, v_pf, cbase(ch), 0); };
+    uint32_t sink = 0, PFV[PF];
+
+    f32x16 Sacc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Sacc[4 * q + e] = (live && S0) ? S0[stOff + (size_t)(32 * J2 + 8 * q + 4 * h + e) * DV + vt0 + r] : 0.f;
+    auto st_s0t = [&]() {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        In<__bf16>::store4(S0T + r * LDK + 32 * J2 + 8 * q + 4 * h,
+                           f32x4{Sacc[4 * q], Sacc[4 * q + 1], Sacc[4 * q + 2], Sacc[4 * q + 3]});
+    };
+    if (live) st_s0t();
+    __syncthreads();                                    // S0^T written
+    __builtin_amdgcn_s_waitcnt(0);
+    if (live) {
+      if (toucher) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) PFV[u] = touch(u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < NS - 2; ++u) {
+        load(u, RK[u], RP[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    auto step = [&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      if (live) {
+        // phase 1 is idle here: reload the set the previous chunk used (for
+        // the next chunk), touch the record PF chunks ahead, scale the state
+        load(ch + NS - 2, RK[(u + NS - 2) % NS], RP[(u + NS - 2) % NS]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (toucher) {
+          sink ^= PFV[u % PF];
+          PFV[u % PF] = touch(ch + PF);
+        }
+        // entry 4q + e is row 32 J2 + 8q + 4h + e, whose pi_C lane 8q + 4h + e holds
+        const int pb = __builtin_bit_cast(int, RP[u % NS]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(pb, 8 * q + e));
+            const float p1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(pb, 8 * q + 4 + e));
+            Sacc[4 * q + e] *= h ? p1 : p0;
+          }
+      }
+      phase_barrier();                                  // A
+      if (live) {
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) Sacc = mma32(RK[u % NS][s], vfrag(s), Sacc);
+        st_s0t();
+      }
+      phase_barrier();                                  // B
+    };
+    walk(step);
+    if (live) {
+      if (toucher) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) sink ^= PFV[u];
+        if (sink == 0x7fc00001u && T < 0) o[0] = (__bf16)0.f;   // never true (T > 0): keeps the touches alive
+      }
+      if (S_out) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S_out[stOff + (size_t)(32 * J2 + 8 * q + 4 * h + e) * DV + vt0 + r] = Sacc[4 * q + e];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host launch
 size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
   const int es = dtype == GDR_BF16 ? 2 : 4;
@@ -997,10 +1401,10 @@ static int device_cus() {
   return cus[dev];
 }
 
-template <typename Tin, int DK, int CM>
+template <typename Tin, int DK, int CM, bool FM>
 static int launch_intra(const ChunkArgs& a, char* ws) {
   using L = IntraSmem<Tin, DK, CM>;
-  auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM>;
+  auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM, FM>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
@@ -1048,10 +1452,38 @@ static int launch_scan(const ChunkArgs& a, const char* ws) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
+template <int DK, int CM>
+static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
+  const void* kern = (const void*)gdn2_chunk_scan_fm_kernel<DK, CM, kScanFmPrefetch, kScanFmSets>;
+  const int nblocks = a.B * a.H * (a.dv / 32);
+  const float* S0 = a.S0;
+  __bf16* o = (__bf16*)a.o;
+  float* So = a.S_out;
+  int T = a.T, DV = a.dv;
+  void* args[] = {&ws, &S0, &o, &So, &T, &DV};
+  hipError_t e = hipLaunchKernel(kern, dim3(nblocks), dim3(kScanFmThreads), args, 0, (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
 template <typename Tin, int DK, int CM>
 static int launch_pair(const ChunkArgs& a, char* ws, int phases) {
+  // bf16 records with d_k, d_v and C multiples of 32 are written in F order
+  // for the 32x32x16 scan when its (b, h, 32 value columns) workgroups fill
+  // the GPU; with fewer heads the staged scan's 16-column tiles keep more CUs
+  // busy. The decision depends only on the shapes and the device, so the
+  // intra and scan phases (also as separate calls) take the same one.
+  if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
+    if (a.dv % 32 == 0 && (long long)a.B * a.H * (a.dv / 32) >= device_cus()) {
+      if (phases & 1) {
+        const int st = launch_intra<Tin, DK, CM, true>(a, ws);
+        if (st != GDR_OK) return st;
+      }
+      if (!(phases & 2)) return GDR_OK;
+      return launch_scan_fm<DK, CM>(a, ws);
+    }
+  }
   if (phases & 1) {
-    const int st = launch_intra<Tin, DK, CM>(a, ws);
+    const int st = launch_intra<Tin, DK, CM, false>(a, ws);
     if (st != GDR_OK) return st;
   }
   if (!(phases & 2)) return GDR_OK;

@@ -217,3 +217,32 @@ def test_phase_entry_points_equal_one_call(dtype):
     gdr.gdr_chunk_scan(ws, S0, o2, S2, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+# With bfloat16 inputs, d_k, d_v and C multiples of 32, and enough heads that
+# the (b, h, 32 value columns) workgroups fill the GPU (B*H*d_v/32 >= 256 CUs),
+# the record is written in the fragment-major order read by the 32x32x16 scan.
+@pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (64, 64, 32), (32, 32, 64), (128, 64, 64),
+                                         (64, 128, 32)])
+def test_wide_batch_fragment_order_path(dk, dv, chunk):
+    heads = -(-256 // (dv // 32))
+    B, H = 2, heads // 2
+    T = 2 * chunk + 9
+    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=3.5, alpha_sigma=1.2, seed=dk + 3 * dv + chunk,
+                    dtype="bf16", s0_std=0.2)
+    _check(d, chunk, f"bf16 wide B={B} H={H} dk={dk} dv={dv} C={chunk} T={T}", path="ws")
+
+
+def test_wide_batch_phase_entry_points_equal_one_call():
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv, C = 4, 16, 150, 128, 128, 64
+    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=4.0, alpha_sigma=1.5, seed=22, dtype="bf16", s0_std=0.1)
+    x = [dev(d[n], "bf16") for n in ("q", "k", "v", "alpha", "b", "w")]
+    S0 = dev(d["S0"])
+    o1, S1 = gdr.gdr_chunk_fwd_ws(*x, S0, chunk=C)
+    ws = gdr.gdr_chunk_intra(*x, chunk=C)
+    o2, S2 = torch.empty_like(o1), torch.empty_like(S1)
+    gdr.gdr_chunk_scan(ws, S0, o2, S2, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
