@@ -117,13 +117,17 @@ struct IntraSmem {
   static constexpr int P_CK = CM * LDK * 2;
   static constexpr int P_CC = CM * LDC * 2;
   static constexpr int P_XC = (kMaxDv + DK) * LDC * 2;
+  // precision of the triangular solve: bf16 operands with fp32 accumulation
+  // for bf16 inputs (one plane per solve buffer), fp32 for fp32 inputs
+  static constexpr int MT = F32 ? kF32 : kBF;
+  static constexpr int NPL = MT == kBF ? 1 : 2;     // planes (bytes / 2 per element) of XR and TL
   static constexpr int BLK = 16 * LDB * 4;
   // [V^ | K^_pi]^T, solved in place, T mode [col][t]. With bf16 inputs it has
   // a region of its own and is filled during prep, so no input register is
   // live across the next item's prefetch; with fp32 (no prefetch) it lies
   // over the prep / Gram operands to fit in 160 KiB.
   static constexpr bool XR_EARLY = !F32;
-  static constexpr int XR_BYTES = 2 * P_XC;
+  static constexpr int XR_BYTES = NPL * P_XC;
   static constexpr int AB = XR_EARLY ? XR_BYTES : 0;   // base of the phase A / phase B area
   // phase A: prep and Gram operands
   static constexpr int KR = AB;                     // k^ * P   [t][j]
@@ -135,7 +139,7 @@ struct IntraSmem {
   static constexpr int TBN = LBK + NPM * BLK;       // D_I fp32 [I][t][s]
   static constexpr int TL = TBN + NBM * BLK;        // [.. -L'_IJ .. | D_I] rows, T mode [t][s]
   static constexpr int XR = XR_EARLY ? 0 : TL + 2 * P_CC;
-  static constexpr int B_END = XR_EARLY ? TL + 2 * P_CC : XR + XR_BYTES;
+  static constexpr int B_END = XR_EARLY ? TL + NPL * P_CC : XR + XR_BYTES;
   // Y staging [t][j] (input precision): over the L / D_I blocks when they fit
   // (dead once the solve starts), else a region of its own
   static constexpr int YS_BYTES = CM * LDY * ES;
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   constexpr bool F32 = L::F32;
   static_assert(!FM || (!F32 && DK % 32 == 0 && CM % 32 == 0), "F order needs bf16, d_k and C multiples of 32");
   constexpr int MM = F32 ? kF32 : kBF;   // Gram operands
-  constexpr int MT = F32 ? kF32 : kSP;   // triangular solve
+  constexpr int MT = L::MT;              // triangular solve
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NW = kIntraThreads / 64;
   constexpr int NB = CM / 16;
