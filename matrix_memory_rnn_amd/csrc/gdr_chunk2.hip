@@ -1245,14 +1245,15 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
       __syncthreads();
       __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-      for (int u = 0; u < NS - 2; ++u) {
+      for (int u = 0; u < NS - 1; ++u) {
         load(u, RM[u]);
         __builtin_amdgcn_sched_barrier(0);
       }
       walk([&](int ch, auto Uc) {
         constexpr int u = decltype(Uc)::value;
-        // phase 1 is idle here: reload the set the previous chunk used
-        load(ch + NS - 2, RM[(u + NS - 2) % NS]);
+        // phase 1 is idle here: reload the set the previous chunk used, for
+        // chunk ch + NS - 1
+        load(ch + NS - 1, RM[(u + NS - 1) % NS]);
         phase_barrier();                                // A
         f32x16 acc;
 #pragma unroll
@@ -1333,7 +1334,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < NS - 2; ++u) {
+      for (int u = 0; u < NS - 1; ++u) {
         load(u, RK[u], RP[u]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1342,8 +1343,8 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
       constexpr int u = decltype(Uc)::value;
       if (live) {
         // phase 1 is idle here: reload the set the previous chunk used (for
-        // the next chunk), touch the record PF chunks ahead, scale the state
-        load(ch + NS - 2, RK[(u + NS - 2) % NS], RP[(u + NS - 2) % NS]);
+        // chunk ch + NS - 1), touch the record PF chunks ahead, scale the state
+        load(ch + NS - 1, RK[(u + NS - 1) % NS], RP[(u + NS - 1) % NS]);
         __builtin_amdgcn_sched_barrier(0);
         if (toucher) {
           sink ^= PFV[u % PF];
