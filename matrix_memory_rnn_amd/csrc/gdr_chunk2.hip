@@ -52,11 +52,11 @@ __host__ __device__ __forceinline__ int fm_off(int r, int k, int K) {
   return ((((r >> 5) * (K >> 4) + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 + (r & 31)) << 3) + (k & 7);
 }
 // U^T in F order: for value tile v/32 and row block t/32, lane l holds the 16
-// entries v = 32*(v/32) + 8q + 4*(l/32) + e (q, e = 0..3; entry 4q + e) of
-// row t = 32*(t/32) + l%32, contiguous: the accumulator layout of V~^T.
+// entries t = 32*(t/32) + 8q + 4*(l/32) + e (q, e = 0..3; entry 4q + e) of
+// column v = 32*(v/32) + l%32, contiguous: the accumulator layout of V~.
 __host__ __device__ __forceinline__ int fu_off(int v, int t, int C) {
-  return ((((v >> 5) * (C >> 5) + (t >> 5)) * 64 + ((v >> 2) & 1) * 32 + (t & 31)) << 4) +
-         (((v >> 3) & 3) << 2) + (v & 3);
+  return ((((v >> 5) * (C >> 5) + (t >> 5)) * 64 + ((t >> 2) & 1) * 32 + (v & 31)) << 4) +
+         (((t >> 3) & 3) << 2) + (t & 3);
 }
 
 // Stores of record entries from fp32 values.
@@ -149,11 +149,11 @@ struct IntraSmem {
   static constexpr int SCL = align16(X_END);        // Gram scale vectors fp32 [pair][j]
   static constexpr int GS = SCL + NPM * DK * 4;     // block totals fp32 [I][j]
   static constexpr int FLAG = GS + NBM * DK * 4;    // guard flags [4]
-  // U staging [t][v] (bf16 records in F order): the solve's U tiles are
-  // transposed through it so the record stores are 16-byte and coalesced
-  static constexpr int LDU = kMaxDv + 8;
+  // staging for bf16 records in F order, so the record stores are 16-byte
+  // and coalesced: Q_pi [t][j] after prep, then U^T [v][t] during the solve
+  static constexpr int LDU = kMaxDv + 8, LDUT = CM + 8;
   static constexpr int US = align16(FLAG + 16);
-  static constexpr int TOTAL = F32 ? FLAG + 16 : US + CM * LDU * 2;
+  static constexpr int TOTAL = F32 ? FLAG + 16 : US + imax(CM * LDU, kMaxDv * LDUT) * 2;
   static_assert(TOTAL <= 160 * 1024, "intra kernel LDS exceeds 160 KiB");
 };
 
@@ -553,10 +553,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           st4<MT>(smem + L::XR, L::P_XC, xoff(16 * ct + c16, 16 * I + 4 * g), acc[i]);
           if (16 * ct < DV) {
             if constexpr (FM) {
-              // F order wants four consecutive v of one t per 8 bytes: staged in LDS
-              Tin* US = (Tin*)(smem + L::US);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) US[(16 * I + 4 * g + e) * L::LDU + 16 * ct + c16] = (Tin)acc[i][e];
+              // staged as U^T rows in LDS, stored in F order after the solve
+              Out<Tin>::quad((Tin*)(smem + L::US) + (16 * ct + c16) * L::LDUT + 16 * I + 4 * g, acc[i]);
             } else {
               Out<Tin>::quad(UTg + o_ut(16 * ct + c16, 16 * I + 4 * g), acc[i]);
             }
@@ -585,15 +583,15 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       }
     }
     if constexpr (FM) {
-      // U^T in F order: each 32-byte lane slot holds v = 32*vt + 8q + 4*hh + e
-      // of row t = 32*i2 + l%32 (entry 4q + e): four 8-byte runs of a US row
+      // U^T in F order: each 32-byte lane slot holds t = 32*i2 + 8q + 4*hh + e
+      // of column v = 32*vt + l%32 (entry 4q + e): four 8-byte runs of a US row
       typedef __attribute__((ext_vector_type(2))) uint32_t u2;
       const char* USb = smem + L::US;
       const int nslots = (DV / 32) * (CM / 32) * 64;
       for (int sidx = tid; sidx < nslots; sidx += kIntraThreads) {
         const int ln = sidx & 63, blk = sidx >> 6;
-        const int t = 32 * (blk % (CM / 32)) + (ln & 31), vb = 32 * (blk / (CM / 32)) + 4 * (ln >> 5);
-        const char* row = USb + 2 * (t * L::LDU + vb);
+        const int vv = 32 * (blk / (CM / 32)) + (ln & 31), tb = 32 * (blk % (CM / 32)) + 4 * (ln >> 5);
+        const char* row = USb + 2 * (vv * L::LDUT + tb);
         const u2 a0 = *(const u2*)(row), a1 = *(const u2*)(row + 16), a2 = *(const u2*)(row + 32),
                  a3 = *(const u2*)(row + 48);
         *(u32x4*)(UTg + 16 * sidx) = u32x4{a0.x, a0.y, a1.x, a1.y};
@@ -1065,7 +1063,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void gdn2_chunk_scan_staged_kernel
 // reloads its registers (for a later chunk) in the other: a load can stall
 // its wave at issue while the memory pipeline is busy, and that way the stall
 // holds up no other wave.
-//   V,  waves 0-1 (I2 = w):    phase 1  V~^T rows t = 32*I2.. = U^T - S0^T Y^T -> LDS
+//   V,  waves 0-1 (I2 = w):    phase 1  V~ rows t = 32*I2.. = U - Y S0 -> LDS (as V~^T)
 //   O1, waves 2-3 (I2 = w-2):  phase 1  P = S0^T Q_pi^T -> LDS (fp32)
 //   O2, waves 4-5 (I2 = w-4):  phase 2  O^T = P + V~^T M^T, stored
 //   S,  waves 6-9 (J2 = w-6):  phase 2  state rows 32*J2..: S = Diag(pi_C) S + K~^T V~ -> LDS
@@ -1147,7 +1145,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
   };
 
   if (wid < 2) {
-    // ================= V: V~^T = U^T - S0^T Y^T, rows t = 32*I2 ..
+    // ================= V: V~ = U - Y S0, rows t = 32*I2 .., to V~^T in LDS
     const int I2 = wid;
     const bool live = NI2 >= 2 || I2 < NI2;
     const int b_y = RL.y + I2 * KSD * 1024, b_u = RL.ut + (vt * NI2 + I2) * 2048;
@@ -1174,18 +1172,16 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
       if (live) {
         f32x16 acc = f16zero();
 #pragma unroll
-        for (int s = 0; s < KSD; ++s) acc = mma32(s0frag(s), R[u][s], acc);
-        // entry 4q + e is (v = 8q + 4h + e, t = 32 I2 + r)
-        __bf16* vd = VTT + 4 * h * LDC + 32 * I2 + r;
+        for (int s = 0; s < KSD; ++s) acc = mma32(R[u][s], s0frag(s), acc);
+        // entry 4q + e is (t = 32 I2 + 8q + 4h + e, v = r): four consecutive t
+        typedef __attribute__((ext_vector_type(2))) uint32_t u2;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4& up = R[u][KSD + (q >> 1)];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = up[2 * (q & 1) + (e >> 1)];
-            const float uu = (e & 1) ? Raw<__bf16>::hi(w) : Raw<__bf16>::lo(w);
-            vd[(8 * q + e) * LDC] = (__bf16)(uu - acc[4 * q + e]);
-          }
+          const f32x4 uu = Raw<__bf16>::un4(u2{up[2 * (q & 1)], up[2 * (q & 1) + 1]});
+          In<__bf16>::store4(VTT + r * LDC + 32 * I2 + 8 * q + 4 * h,
+                             f32x4{uu[0] - acc[4 * q], uu[1] - acc[4 * q + 1], uu[2] - acc[4 * q + 2],
+                                   uu[3] - acc[4 * q + 3]});
         }
       }
       phase_barrier();                                  // A: V~ ready
