@@ -104,6 +104,7 @@ __device__ __forceinline__ void fs_group(const float* Lb, float* x) {
 
 // ============================================================================ intra kernel
 constexpr int kIntraThreads = 512;
+
 constexpr int kMaxDv = 128;
 
 template <typename Tin, int DK, int CM>
@@ -217,36 +218,48 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   const int nvi = CM * (DV / 8);
   typename RW::R2 xa[8], xk[8], xb[8], xq[8];
   typename RW::R8 xv[MAXVI], xw[MAXVI];
-  auto issue = [&](int it) {
+  // parts: 1 = alpha and k, 2 = b and q, 4 = v and w
+  auto issue = [&](int it, int parts) {
     const int bh = it / nchunks, tb = (it % nchunks) * CM;
     const size_t sK = (size_t)bh * T * DK + j, sV = (size_t)bh * T * DV;
+    if (parts & 1) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int t = tb + r0 + r;
-      const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
-      xa[r] = RW::ld2(alpha + off);
-      xk[r] = RW::ld2(k + off);
-      xb[r] = RW::ld2(bgate + off);
-      xq[r] = RW::ld2(q + off);
+      for (int r = 0; r < 8; ++r) {
+        const int t = tb + r0 + r;
+        const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
+        xa[r] = RW::ld2(alpha + off);
+        xk[r] = RW::ld2(k + off);
+      }
     }
+    if (parts & 2) {
 #pragma unroll
-    for (int i = 0; i < MAXVI; ++i) {
-      const int idx = tid + kIntraThreads * i;
-      const int vi = idx < nvi ? idx : 0;
-      const int vrow = vi / (DV / 8), vcol = (vi % (DV / 8)) * 8;
-      const int tv = tb + vrow;
-      const size_t off = sV + (size_t)(tv < T ? tv : T - 1) * DV + vcol;
-      xv[i] = RW::ld8(v + off);
-      xw[i] = RW::ld8(wgate + off);
+      for (int r = 0; r < 8; ++r) {
+        const int t = tb + r0 + r;
+        const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
+        xb[r] = RW::ld2(bgate + off);
+        xq[r] = RW::ld2(q + off);
+      }
+    }
+    if (parts & 4) {
+#pragma unroll
+      for (int i = 0; i < MAXVI; ++i) {
+        const int idx = tid + kIntraThreads * i;
+        const int vi = idx < nvi ? idx : 0;
+        const int vrow = vi / (DV / 8), vcol = (vi % (DV / 8)) * 8;
+        const int tv = tb + vrow;
+        const size_t off = sV + (size_t)(tv < T ? tv : T - 1) * DV + vcol;
+        xv[i] = RW::ld8(v + off);
+        xw[i] = RW::ld8(wgate + off);
+      }
     }
   };
-  // bf16: the next item's inputs are fetched during this item's Gram products;
+  // bf16: the next item's inputs are fetched while this item is worked on;
   // fp32 (twice the registers) fetches at the start of each item.
-  if constexpr (!F32) issue(item);
+  if constexpr (!F32) issue(item, 7);
   __syncthreads();
 
   for (; item < nitems; item += gridDim.x) {
-    if constexpr (F32) issue(item);
+    if constexpr (F32) issue(item, 7);
     const int bh = item / nchunks, t0 = (item % nchunks) * CM;
     const size_t seqK = (size_t)bh * T * DK;
     char* rec = ws + (size_t)item * RL.bytes;
@@ -279,6 +292,13 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) vh[i][e] = okv ? fv[e] * fw[e] : 0.f;
       }
+    }
+    // bf16: the next item's inputs are fetched in three parts spread over
+    // this item (v and w here, alpha and k with the Gram products, b and q
+    // with D_I), so that the loads of all CUs reach HBM as a steady stream
+    // rather than in one burst per item
+    if constexpr (!F32) {
+      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, 4);
     }
 
     if constexpr (L::XR_EARLY) {
@@ -380,6 +400,9 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     __syncthreads();
 
     // ================= Gram tiles: L^T, M^T of pair (I, J) = (Kc_J * scale) [Kr_I; Qr_I]^T
+    if constexpr (!F32) {
+      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, 1);
+    }
     f32x4 gL[MAXP], gM[MAXP];
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) {
@@ -468,10 +491,9 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     __syncthreads();
 
     // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0);
-    // the next item's loads are issued here (wave 0 first), so their issue
-    // overlaps this one-wave phase
+    // the last part of the next item's loads is issued here
     if constexpr (!F32) {
-      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x);
+      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, 2);
     }
     if (wid == 0) {
       if (tid < 4) FLAGS[tid] = 0;  // read above; set again by the next item's prep 1
