@@ -255,11 +255,23 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   };
   // bf16: the next item's inputs are fetched while this item is worked on;
   // fp32 (twice the registers) fetches at the start of each item.
-  if constexpr (!F32) issue(item, 7);
+  // in the order the loop issues them (v and w first), so that the wait
+  // counts at the top of the loop can be exact
+  if constexpr (!F32) {
+    issue(item, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(item, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(item, 2);
+  }
   __syncthreads();
 
   for (; item < nitems; item += gridDim.x) {
     if constexpr (F32) issue(item, 7);
+    // the item whose inputs are fetched during this one: the next of this
+    // workgroup, or this one again after the last (the loads are always
+    // issued, so the wait counts do not depend on a branch)
+    const int nxt = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : item;
     const int bh = item / nchunks, t0 = (item % nchunks) * CM;
     const size_t seqK = (size_t)bh * T * DK;
     char* rec = ws + (size_t)item * RL.bytes;
@@ -293,13 +305,6 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         for (int e = 0; e < 8; ++e) vh[i][e] = okv ? fv[e] * fw[e] : 0.f;
       }
     }
-    // bf16: the next item's inputs are fetched in three parts spread over
-    // this item (v and w here, alpha and k with the Gram products, b and q
-    // with D_I), so that the loads of all CUs reach HBM as a steady stream
-    // rather than in one burst per item
-    if constexpr (!F32) {
-      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, 4);
-    }
 
     if constexpr (L::XR_EARLY) {
 #pragma unroll
@@ -311,6 +316,13 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, xoff(vcol + e, vrow), vh[i][e]);
         }
       }
+    }
+    // bf16: the next item's inputs are fetched in three parts spread over
+    // this item (v and w here, alpha and k with the Gram products, b and q
+    // with D_I), so that the loads of all CUs reach HBM as a steady stream
+    // rather than in one burst per item
+    if constexpr (!F32) {
+      issue(nxt, 4);
     }
 
     // ================= prep 1: half-block products -> block totals G
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
 
     // ================= Gram tiles: L^T, M^T of pair (I, J) = (Kc_J * scale) [Kr_I; Qr_I]^T
     if constexpr (!F32) {
-      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, 1);
+      issue(nxt, 1);
     }
     f32x4 gL[MAXP], gM[MAXP];
 #pragma unroll
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0);
     // the last part of the next item's loads is issued here
     if constexpr (!F32) {
-      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x, 2);
+      issue(nxt, 2);
     }
     if (wid == 0) {
       if (tid < 4) FLAGS[tid] = 0;  // read above; set again by the next item's prep 1
@@ -544,50 +556,112 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     }
     __syncthreads();
 
-    // ================= block forward substitution over all d_v + d_k columns, in place:
-    // X_I = D_I R_I - sum_{J<I} L'_IJ X_J. U^T goes to the record, Y to the staging rows.
-    for (int I = 0; I < NB; ++I) {
-      const int kend = 16 * (I + 1);
-      f32x4 acc[MAXX];
+    // ================= block forward substitution over all d_v + d_k columns:
+    // X_I = D_I R_I - sum_{J<I} L'_IJ X_J. U^T and Y go to staging rows in LDS.
+    auto stage_x = [&](int I, int ct, const f32x4& x) {
+      if (16 * ct < DV) {
+        if constexpr (FM) {
+          // staged as U^T rows in LDS, stored in F order after the solve
+          Out<Tin>::quad((Tin*)(smem + L::US) + (16 * ct + c16) * L::LDUT + 16 * I + 4 * g, x);
+        } else {
+          Out<Tin>::quad(UTg + o_ut(16 * ct + c16, 16 * I + 4 * g), x);
+        }
+      } else {
+        const int jj = 16 * ct - DV + c16;
 #pragma unroll
-      for (int i = 0; i < MAXX; ++i) acc[i] = f4zero();
+        for (int e = 0; e < 4; ++e) YS[(16 * I + 4 * g + e) * L::LDY + jj] = (Tin)x[e];
+      }
+    };
+    if constexpr (MT == kBF) {
+      // bf16 operands: the solved blocks stay in registers. A 32-wide k step
+      // over blocks (J0, J1) = (2p, 2p + 1) takes, in lane group g, the rows
+      // 4g .. 4g+3 of J0 and then of J1: exactly the accumulator entries a
+      // lane holds for X_J0 and X_J1 of its column, so a solved block feeds
+      // the next products without a trip through LDS. The rows of [-L' | D]
+      // in TL are read with their columns in the same order.
+      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+      const bf16x4 z4 = bf16x4{};
+      const __bf16* TLb = (const __bf16*)(smem + L::TL);
+      const __bf16* XRb = (const __bf16*)(smem + L::XR);
+      // lane indices through an empty asm: the operand addresses below are
+      // formed here rather than hoisted out of the item loop, where they
+      // would hold registers across every phase
+      int sr = c16, sg = g;
+      asm volatile("" : "+v"(sr), "+v"(sg));
+      bf16x4 X[NB][MAXX];
 #pragma unroll
-      for (int k0 = 0; k0 < CM; k0 += 32) {
-        if (k0 < kend) {
-          Frag<MT> A = ldfrag<MT>(smem + L::TL, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
+      for (int I = 0; I < NB; ++I) {
+        bf16x4 A0[(NB + 1) / 2], A1[(NB + 1) / 2], RH[MAXX];
+        const __bf16* trow = TLb + (16 * I + sr) * L::LDC + 4 * sg;
+#pragma unroll
+        for (int pp = 0; 2 * pp <= I; ++pp) {
+          A0[pp] = *(const bf16x4*)(trow + 32 * pp);
+          A1[pp] = 2 * pp + 1 <= I ? *(const bf16x4*)(trow + 32 * pp + 16) : z4;
+        }
+#pragma unroll
+        for (int i = 0; i < MAXX; ++i) {
+          const int ct = wid + NW * i;
+          RH[i] = ct < NX ? *(const bf16x4*)(XRb + xoff(16 * ct + sr, 16 * I + 4 * sg)) : z4;
+        }
+        f32x4 acc[MAXX];
+#pragma unroll
+        for (int i = 0; i < MAXX; ++i) acc[i] = f4zero();
+#pragma unroll
+        for (int pp = 0; 2 * pp <= I; ++pp) {
+          const int J0 = 2 * pp, J1 = 2 * pp + 1;
+          const bf16x8 A = __builtin_shufflevector(A0[pp], A1[pp], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int i = 0; i < MAXX; ++i) {
-            const int ct = wid + NW * i;
-            if (ct < NX) {
-              // rows 16ct + c16 share the slot swizzle ct & XM
-              const int kk = k0 + 8 * g;
-              Frag<MT> B = ldfrag<MT>(smem + L::XR, L::P_XC, L::LDC, 16 * ct,
-                                      8 * ((kk >> 3) ^ (ct & XM)) - 8 * g, kk < kend ? CM : 0, lane);
-              mma<MT>(acc[i], A, B);
+            if (wid + NW * i < NX) {
+              const bf16x4 b0 = J0 < I ? X[J0][i] : RH[i];
+              const bf16x4 b1 = J1 < I ? X[J1][i] : (J1 == I ? RH[i] : z4);
+              acc[i] = mfma_bf16(A, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), acc[i]);
             }
           }
         }
-      }
 #pragma unroll
-      for (int i = 0; i < MAXX; ++i) {
-        const int ct = wid + NW * i;
-        if (ct < NX) {
-          st4<MT>(smem + L::XR, L::P_XC, xoff(16 * ct + c16, 16 * I + 4 * g), acc[i]);
-          if (16 * ct < DV) {
-            if constexpr (FM) {
-              // staged as U^T rows in LDS, stored in F order after the solve
-              Out<Tin>::quad((Tin*)(smem + L::US) + (16 * ct + c16) * L::LDUT + 16 * I + 4 * g, acc[i]);
-            } else {
-              Out<Tin>::quad(UTg + o_ut(16 * ct + c16, 16 * I + 4 * g), acc[i]);
-            }
-          } else {
-            const int jj = 16 * ct - DV + c16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) YS[(16 * I + 4 * g + e) * L::LDY + jj] = (Tin)acc[i][e];
+        for (int i = 0; i < MAXX; ++i) {
+          const int ct = wid + NW * i;
+          if (ct < NX) {
+            X[I][i] = bf16x4{(__bf16)acc[i][0], (__bf16)acc[i][1], (__bf16)acc[i][2], (__bf16)acc[i][3]};
+            stage_x(I, ct, acc[i]);
           }
         }
       }
-      wave_lds_sync();
+    } else {
+      // fp32 operands: in place in XR, one block row after the other
+      for (int I = 0; I < NB; ++I) {
+        const int kend = 16 * (I + 1);
+        f32x4 acc[MAXX];
+#pragma unroll
+        for (int i = 0; i < MAXX; ++i) acc[i] = f4zero();
+#pragma unroll
+        for (int k0 = 0; k0 < CM; k0 += 32) {
+          if (k0 < kend) {
+            Frag<MT> A = ldfrag<MT>(smem + L::TL, L::P_CC, L::LDC, 16 * I, k0, kend, lane);
+#pragma unroll
+            for (int i = 0; i < MAXX; ++i) {
+              const int ct = wid + NW * i;
+              if (ct < NX) {
+                // rows 16ct + c16 share the slot swizzle ct & XM
+                const int kk = k0 + 8 * g;
+                Frag<MT> B = ldfrag<MT>(smem + L::XR, L::P_XC, L::LDC, 16 * ct,
+                                        8 * ((kk >> 3) ^ (ct & XM)) - 8 * g, kk < kend ? CM : 0, lane);
+                mma<MT>(acc[i], A, B);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < MAXX; ++i) {
+          const int ct = wid + NW * i;
+          if (ct < NX) {
+            st4<MT>(smem + L::XR, L::P_XC, xoff(16 * ct + c16, 16 * I + 4 * g), acc[i]);
+            stage_x(I, ct, acc[i]);
+          }
+        }
+        wave_lds_sync();
+      }
     }
     __syncthreads();
 
