@@ -53,6 +53,10 @@ def load_library():
         raise RuntimeError(
             f"{lib_path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
             "(or `python matrix_memory_rnn_amd/build.py`); there is no fallback implementation")
+    # torch's HIP runtime is loaded first, so that the library binds to the
+    # same runtime instance instead of initialising a second one (which then
+    # may see no device)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(lib_path)
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 7 + [P]

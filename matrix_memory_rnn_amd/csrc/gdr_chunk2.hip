@@ -90,16 +90,37 @@ template <> struct Out<__bf16> {
 // x[m] is final it is subtracted from every later row, so the dependent chain
 // is one FMA per row and the other updates run alongside.
 template <int M4, int LDB>
-__device__ __forceinline__ void fs_group(const float* Lb, float* x) {
-  f32x4 lc[16];
+__device__ __forceinline__ void fs_load(const float* Lb, f32x4* lc) {
 #pragma unroll
   for (int r = 4 * M4 + 1; r < 16; ++r) lc[r] = *(const f32x4*)(Lb + r * LDB + 4 * M4);
+}
+template <int M4>
+__device__ __forceinline__ void fs_apply(const f32x4* lc, float* x) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * M4 + e;
 #pragma unroll
     for (int r = m + 1; r < 16; ++r) x[r] -= lc[r][e] * x[m];
   }
+}
+template <int M4, int LDB>
+__device__ __forceinline__ void fs_group(const float* Lb, float* x) {
+  f32x4 lc[16];
+  fs_load<M4, LDB>(Lb, lc);
+  fs_apply<M4>(lc, x);
+}
+// All four column groups, each group's rows read one group ahead of its use.
+template <int LDB>
+__device__ __forceinline__ void fs_all(const float* Lb, float* x) {
+  f32x4 la[16], lb[16];
+  fs_load<0, LDB>(Lb, la);
+  fs_load<1, LDB>(Lb, lb);
+  fs_apply<0>(la, x);
+  fs_load<2, LDB>(Lb, la);
+  fs_apply<1>(lb, x);
+  fs_load<3, LDB>(Lb, lb);
+  fs_apply<2>(la, x);
+  fs_apply<3>(lb, x);
 }
 
 // ============================================================================ intra kernel
@@ -135,26 +156,32 @@ struct IntraSmem {
   static constexpr int QR = KR + NS * P_CK;         // q * P    [t][j]
   static constexpr int KC = QR + NS * P_CK;         // k * Qs   [t][j]
   static constexpr int A_END = KC + NS * P_CK;
-  // phase B (over phase A, after the Gram products)
+  // fp32, phase B (over phase A, after the Gram products): L blocks, D_I,
+  // the [-L' | D] rows and the right-hand sides
   static constexpr int LBK = AB;                    // L blocks fp32 [pair][t][s]
-  static constexpr int TBN = LBK + NPM * BLK;       // D_I fp32 [I][t][s]
-  static constexpr int TL = TBN + NBM * BLK;        // [.. -L'_IJ .. | D_I] rows, T mode [t][s]
-  static constexpr int XR = XR_EARLY ? 0 : TL + 2 * P_CC;
-  static constexpr int B_END = XR_EARLY ? TL + NPL * P_CC : XR + XR_BYTES;
-  // Y staging [t][j] (input precision): over the L / D_I blocks when they fit
-  // (dead once the solve starts), else a region of its own
+  static constexpr int TBN_B = LBK + NPM * BLK;     // D_I fp32 [I][t][s]
+  static constexpr int TL_B = TBN_B + NBM * BLK;    // [.. -L'_IJ .. | D_I] rows, T mode [t][s]
+  static constexpr int XR = XR_EARLY ? 0 : TL_B + 2 * P_CC;
+  static constexpr int B_END = XR_EARLY ? AB : XR + XR_BYTES;
+  // Y staging [t][j] (input precision): bf16 over phase A (dead once the
+  // solve starts), fp32 in a region of its own
   static constexpr int YS_BYTES = CM * LDY * ES;
-  static constexpr bool YS_OVER = YS_BYTES <= TL - LBK;
-  static constexpr int YS = YS_OVER ? LBK : align16(imax(A_END, B_END));
-  static constexpr int X_END = YS_OVER ? imax(A_END, B_END) : YS + YS_BYTES;
+  static_assert(F32 || YS_BYTES <= A_END - AB, "Y staging fits over the Gram operands");
+  static constexpr int YS = F32 ? align16(imax(A_END, B_END)) : AB;
+  static constexpr int X_END = F32 ? YS + YS_BYTES : imax(A_END, B_END);
   static constexpr int SCL = align16(X_END);        // Gram scale vectors fp32 [pair][j]
   static constexpr int GS = SCL + NPM * DK * 4;     // block totals fp32 [I][j]
   static constexpr int FLAG = GS + NBM * DK * 4;    // guard flags [4]
-  // staging for bf16 records in F order, so the record stores are 16-byte
+  // bf16: staging for records in F order, so the record stores are 16-byte
   // and coalesced: Q_pi [t][j] after prep, then U^T [v][t] during the solve
   static constexpr int LDU = kMaxDv + 8, LDUT = CM + 8;
   static constexpr int US = align16(FLAG + 16);
-  static constexpr int TOTAL = F32 ? FLAG + 16 : US + imax(CM * LDU, kMaxDv * LDUT) * 2;
+  // bf16: the diagonal L blocks, D_I and the [-L' | D] rows have regions of
+  // their own, written while other waves still read the Gram operands
+  static constexpr int LBD = US + imax(CM * LDU, kMaxDv * LDUT) * 2;   // diagonal L fp32 [I][t][s]
+  static constexpr int TBN = F32 ? TBN_B : LBD + NBM * BLK;
+  static constexpr int TL = F32 ? TL_B : TBN + NBM * BLK;
+  static constexpr int TOTAL = F32 ? FLAG + 16 : TL + P_CC;
   static_assert(TOTAL <= 160 * 1024, "intra kernel LDS exceeds 160 KiB");
 };
 
@@ -179,7 +206,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   constexpr int MAXVI = (CM * kMaxDv / 8 + kIntraThreads - 1) / kIntraThreads;
   constexpr int BLKF = 16 * L::LDB;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(Tin));
   const int NX = (DV + DK) / 16;
@@ -415,146 +442,299 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     if constexpr (!F32) {
       issue(nxt, 1);
     }
-    f32x4 gL[MAXP], gM[MAXP];
+    if constexpr (F32) {
+      f32x4 gL[MAXP], gM[MAXP];
 #pragma unroll
-    for (int i = 0; i < MAXP; ++i) {
-      gL[i] = f4zero();
-      gM[i] = f4zero();
-      const int p = wid + NW * i;
-      if (p < NP) {
-        int I, J;
-        pair_of(p, I, J);
+      for (int i = 0; i < MAXP; ++i) {
+        gL[i] = f4zero();
+        gM[i] = f4zero();
+        const int p = wid + NW * i;
+        if (p < NP) {
+          int I, J;
+          pair_of(p, I, J);
+          const bool scaled = (I == J) || (I > J + 1);
+#pragma unroll
+          for (int k0 = 0; k0 < DK; k0 += 32) {
+            Frag<MM> A = ldfrag<MM>(smem + L::KC, L::P_CK, L::LDK, 16 * J, k0, DK, lane);
+            const int kk = k0 + 8 * g;
+            if (scaled && kk < DK) {
+              const float* sp = SCL + p * DK + kk;
+              const f32x4 s0 = *(const f32x4*)sp, s1 = *(const f32x4*)(sp + 4);
+              const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+              scale_frag<MM>(A, sv);
+            }
+            Frag<MM> BL = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+            Frag<MM> BM = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
+            mma<MM>(gL[i], A, BL);
+            mma<MM>(gM[i], A, BM);
+          }
+        }
+      }
+      __syncthreads();
+
+      if constexpr (FM) {
+        // Q_pi from its staging rows to the record: consecutive threads write
+        // consecutive F-order pieces (US is free again before the solve)
+        for (int idx = tid; idx < CM * DK / 8; idx += kIntraThreads) {
+          const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31), pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
+          *(u32x4*)(QPg + 8 * idx) = *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc));
+        }
+      }
+
+      // ================= L blocks (fp32, LDS), M (record), right-hand sides [V^ | K^_pi]^T
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int p = wid + NW * i;
+        if (p < NP) {
+          int I, J;
+          pair_of(p, I, J);
+          const int t = 16 * I + c16, s0 = 16 * J + 4 * g;
+          f32x4 lv = gL[i], mv = gM[i];
+          if (I == J) {
+            if (FLAGS[I]) exact_diag<Tin, DK>(k, bgate, q, alpha, seqK, t0, T, t, s0, lv, mv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (s0 + e >= t) lv[e] = 0.f;
+              if (s0 + e > t) mv[e] = 0.f;
+            }
+          }
+          *(f32x4*)(LBK + p * BLKF + c16 * L::LDB + 4 * g) = lv;
+          Out<Tin>::quad(Mg + o_m(t, s0), mv);
+          // F order: the scan multiplies M in 32-column slices up to the
+          // diagonal, so the block right of an even diagonal block is zero
+          if constexpr (FM) {
+            if (I == J && (I & 1) == 0) Out<Tin>::quad(Mg + o_m(t, s0 + 16), f4zero());
+          }
+        }
+      }
+      if constexpr (!L::XR_EARLY) {
+#pragma unroll
+        for (int i = 0; i < MAXVI; ++i) {
+          const int idx = tid + kIntraThreads * i;
+          if (idx < nvi) {
+            const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, xoff(vcol + e, vrow), vh[i][e]);
+          }
+        }
+      }
+      if (!L::XR_EARLY && act) {
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          const float2* kp = khp + 4 * r4;
+          st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j, r0 + 4 * r4),
+                  f32x4{kp[0].x, kp[1].x, kp[2].x, kp[3].x});
+          st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j + 1, r0 + 4 * r4),
+                  f32x4{kp[0].y, kp[1].y, kp[2].y, kp[3].y});
+        }
+      }
+      __syncthreads();
+
+      // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0)
+      if (wid == 0) {
+        if (tid < 4) FLAGS[tid] = 0;  // read above; set again by the next item's prep 1
+        const int I = g, cc = c16;
+        const bool live = I < NB;
+        const float* Lb = LBK + (live ? pidx(I, I) : 0) * BLKF;
+        // right-looking: once x[m] is final it is subtracted from every later
+        // row at once, so the dependent chain is one FMA per row
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+        fs_group<0, L::LDB>(Lb, x);
+        fs_group<1, L::LDB>(Lb, x);
+        fs_group<2, L::LDB>(Lb, x);
+        fs_group<3, L::LDB>(Lb, x);
+        if (live) {
+          float* Tn = TBN + I * BLKF;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            Tn[r * L::LDB + cc] = x[r];
+            st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
+          }
+        }
+      }
+      __syncthreads();
+
+      // ================= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL
+#pragma unroll
+      for (int i = 0; i < MAXQ; ++i) {
+        const int qq = wid + NW * i;
+        if (qq < NQ) {
+          int I, J;
+          offpair_of(qq, I, J);
+          const int p = pidx(I, J);
+          const bool ok = g < 2;
+          Frag<MT> A = frag_f32<MT>(TBN + I * BLKF + c16 * L::LDB + 8 * (g & 1), ok);
+          float lc[8];
+          const float* lb = LBK + p * BLKF + c16;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lc[e] = ok ? lb[(8 * (g & 1) + e) * L::LDB] : 0.f;
+          Frag<MT> B = frag_f32<MT>(lc, true);
+          f32x4 acc = f4zero();
+          mma<MT>(acc, A, B);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
+        }
+      }
+      __syncthreads();
+    } else {
+      // bf16: waves 0 .. NB-1 take the diagonal pairs (I, I) and form
+      // D_I = (I + L_II)^{-1} right away; the other waves take the
+      // off-diagonal pairs and keep their L_IJ in registers for
+      // L'_IJ = D_I L_IJ after the barrier. L is formed as L[t][s]
+      // (A = Kr_I, B = scaled Kc_J: the A and B lane layouts coincide), M as
+      // M^T[s][t].
+      constexpr int NOW = NW - NB;                           // waves of the off-diagonal pairs
+      constexpr int MAXO = NQ > 0 ? (NQ + NOW - 1) / NOW : 1;
+      static_assert(NB < NW, "one wave per diagonal block and at least one more");
+      const bool dwave = wid < NB;
+      float* LBD = (float*)(smem + L::LBD);
+      // the fragments of a pair are read before the first product, so the
+      // reads overlap; pairs with J = I - 1 have unit scale vectors
+      auto gram = [&](int I, int J, f32x4& l, f32x4& m) {
+        constexpr int KS = (DK + 31) / 32;
+        const int p = pidx(I, J);
         const bool scaled = (I == J) || (I > J + 1);
+        Frag<MM> A[KS], BL[KS], BM[KS];
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += 32) {
-          Frag<MM> A = ldfrag<MM>(smem + L::KC, L::P_CK, L::LDK, 16 * J, k0, DK, lane);
-          const int kk = k0 + 8 * g;
-          if (scaled && kk < DK) {
-            const float* sp = SCL + p * DK + kk;
+        for (int ks = 0; ks < KS; ++ks) {
+          A[ks] = ldfrag<MM>(smem + L::KC, L::P_CK, L::LDK, 16 * J, 32 * ks, DK, lane);
+          BL[ks] = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, 32 * ks, DK, lane);
+          BM[ks] = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, 32 * ks, DK, lane);
+        }
+        l = f4zero();
+        m = f4zero();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          // slices past d_k (d_k = 16) are zero fragments and stay unscaled
+          if (scaled && 32 * ks + 8 * g < DK) {
+            const float* sp = SCL + p * DK + 32 * ks + 8 * g;
             const f32x4 s0 = *(const f32x4*)sp, s1 = *(const f32x4*)(sp + 4);
             const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-            scale_frag<MM>(A, sv);
+            scale_frag<MM>(A[ks], sv);
           }
-          Frag<MM> BL = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
-          Frag<MM> BM = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, k0, DK, lane);
-          mma<MM>(gL[i], A, BL);
-          mma<MM>(gM[i], A, BM);
+          mma<MM>(l, BL[ks], A[ks]);
+          mma<MM>(m, A[ks], BM[ks]);
         }
-      }
-    }
-    __syncthreads();
-
-    if constexpr (FM) {
-      // Q_pi from its staging rows to the record: consecutive threads write
-      // consecutive F-order pieces (US is free again before the solve)
-      for (int idx = tid; idx < CM * DK / 8; idx += kIntraThreads) {
-        const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31), pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
-        *(u32x4*)(QPg + 8 * idx) = *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc));
-      }
-    }
-
-    // ================= L blocks (fp32, LDS), M (record), right-hand sides [V^ | K^_pi]^T
-#pragma unroll
-    for (int i = 0; i < MAXP; ++i) {
-      const int p = wid + NW * i;
-      if (p < NP) {
-        int I, J;
-        pair_of(p, I, J);
+      };
+      // M rows t = 16 I + c16, columns 16 J + 4g .. to the record
+      auto store_m = [&](int I, int J, const f32x4& mv) {
         const int t = 16 * I + c16, s0 = 16 * J + 4 * g;
-        f32x4 lv = gL[i], mv = gM[i];
-        if (I == J) {
-          if (FLAGS[I]) exact_diag<Tin, DK>(k, bgate, q, alpha, seqK, t0, T, t, s0, lv, mv);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (s0 + e >= t) lv[e] = 0.f;
-            if (s0 + e > t) mv[e] = 0.f;
-          }
-        }
-        *(f32x4*)(LBK + p * BLKF + c16 * L::LDB + 4 * g) = lv;
         Out<Tin>::quad(Mg + o_m(t, s0), mv);
         // F order: the scan multiplies M in 32-column slices up to the
         // diagonal, so the block right of an even diagonal block is zero
         if constexpr (FM) {
           if (I == J && (I & 1) == 0) Out<Tin>::quad(Mg + o_m(t, s0 + 16), f4zero());
         }
-      }
-    }
-    if constexpr (!L::XR_EARLY) {
-#pragma unroll
-      for (int i = 0; i < MAXVI; ++i) {
-        const int idx = tid + kIntraThreads * i;
-        if (idx < nvi) {
-          const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st1<MT>(smem + L::XR, L::P_XC, xoff(vcol + e, vrow), vh[i][e]);
-        }
-      }
-    }
-    if (!L::XR_EARLY && act) {
-#pragma unroll
-      for (int r4 = 0; r4 < 2; ++r4) {
-        const float2* kp = khp + 4 * r4;
-        st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j, r0 + 4 * r4),
-                f32x4{kp[0].x, kp[1].x, kp[2].x, kp[3].x});
-        st4<MT>(smem + L::XR, L::P_XC, xoff(DV + j + 1, r0 + 4 * r4),
-                f32x4{kp[0].y, kp[1].y, kp[2].y, kp[3].y});
-      }
-    }
-    __syncthreads();
-
-    // ================= D_I = (I + L_II)^{-1} by forward substitution (wave 0);
-    // the last part of the next item's loads is issued here
-    if constexpr (!F32) {
-      issue(nxt, 2);
-    }
-    if (wid == 0) {
-      if (tid < 4) FLAGS[tid] = 0;  // read above; set again by the next item's prep 1
-      const int I = g, cc = c16;
-      const bool live = I < NB;
-      const float* Lb = LBK + (live ? pidx(I, I) : 0) * BLKF;
-      // right-looking: once x[m] is final it is subtracted from every later
-      // row at once, so the dependent chain is one FMA per row
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
-      fs_group<0, L::LDB>(Lb, x);
-      fs_group<1, L::LDB>(Lb, x);
-      fs_group<2, L::LDB>(Lb, x);
-      fs_group<3, L::LDB>(Lb, x);
-      if (live) {
-        float* Tn = TBN + I * BLKF;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          Tn[r * L::LDB + cc] = x[r];
-          st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ================= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL
-#pragma unroll
-    for (int i = 0; i < MAXQ; ++i) {
-      const int qq = wid + NW * i;
-      if (qq < NQ) {
-        int I, J;
-        offpair_of(qq, I, J);
-        const int p = pidx(I, J);
-        const bool ok = g < 2;
-        Frag<MT> A = frag_f32<MT>(TBN + I * BLKF + c16 * L::LDB + 8 * (g & 1), ok);
-        float lc[8];
-        const float* lb = LBK + p * BLKF + c16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lc[e] = ok ? lb[(8 * (g & 1) + e) * L::LDB] : 0.f;
-        Frag<MT> B = frag_f32<MT>(lc, true);
-        f32x4 acc = f4zero();
-        mma<MT>(acc, A, B);
+      };
+      f32x4 gL[MAXO];
+      if (dwave) {
+        const int I = wid;
+        f32x4 lv, mv;
+        gram(I, I, lv, mv);
+        const int t = 16 * I + c16, s0 = 16 * I + 4 * g;
+        // entry e is L[4g + e][c16]: strictly lower part only
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
+          if (c16 >= 4 * g + e) lv[e] = 0.f;
+        if (FLAGS[I]) {
+          // exact products, formed for row t = c16 and columns 4g .. 4g+3 (the
+          // M layout), brought to the L layout through LDS
+          float* Lb = LBD + I * BLKF;   // L_II [t][s], fp32
+          f32x4 lx;
+          exact_diag<Tin, DK>(k, bgate, q, alpha, seqK, t0, T, t, s0, lx, mv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (s0 + e >= t) lx[e] = 0.f;
+          *(f32x4*)(Lb + c16 * L::LDB + 4 * g) = lx;
+          wave_lds_sync();
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lv[e] = Lb[(4 * g + e) * L::LDB + c16];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s0 + e > t) mv[e] = 0.f;
+        store_m(I, I, mv);
+        // column cc of D_I by right-looking substitution; L[r][m] is entry
+        // r % 4 of lane 16 (r / 4) + m, read as a wave-uniform scalar (every
+        // lane group computes the column; group 0 writes it)
+        // (__float_as_int, not __builtin_bit_cast: this compiler's bit cast
+        // of a vector element reads element 0 whatever the index)
+        const int cc = c16;
+        const int li[4] = {__float_as_int(lv[0]), __float_as_int(lv[1]), __float_as_int(lv[2]),
+                           __float_as_int(lv[3])};
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+#pragma unroll
+          for (int r = m + 1; r < 16; ++r) {
+            const float lrm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(li[r & 3], 16 * (r >> 2) + m));
+            x[r] -= lrm * x[m];
+          }
+        }
+        if (g == 0) {
+          float* Tn = TBN + I * BLKF;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            Tn[r * L::LDB + cc] = x[r];
+            st1<MT>(smem + L::TL, L::P_CC, (16 * I + r) * L::LDC + 16 * I + cc, x[r]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MAXO; ++i) {
+          const int qq = (wid - NB) + NOW * i;
+          if (qq < NQ) {
+            int I, J;
+            offpair_of(qq, I, J);
+            f32x4 mv;
+            gram(I, J, gL[i], mv);
+            store_m(I, J, mv);
+          }
+        }
       }
+      __syncthreads();
+
+      // ================= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL.
+      // k runs over t = 4g .. 4g+3 in lane group g (entries 0-3; 4-7 are zero):
+      // the B operand is this wave's L_IJ accumulator as it stands.
+      issue(nxt, 2);
+      if (tid < 4) FLAGS[tid] = 0;   // read above; set again by the next item's prep 1
+      if (dwave) {
+        if constexpr (FM) {
+          // Q_pi from its staging rows to the record: consecutive threads
+          // write consecutive F-order pieces (US is free again before the solve)
+          for (int idx = tid; idx < CM * DK / 8; idx += 64 * NB) {
+            const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31),
+                      pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
+            *(u32x4*)(QPg + 8 * idx) = *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MAXO; ++i) {
+          const int qq = (wid - NB) + NOW * i;
+          if (qq < NQ) {
+            int I, J;
+            offpair_of(qq, I, J);
+            const f32x4 dv4 = *(const f32x4*)(TBN + I * BLKF + c16 * L::LDB + 4 * g);
+            const bf16x8 A = bf16x8{(__bf16)dv4[0], (__bf16)dv4[1], (__bf16)dv4[2], (__bf16)dv4[3],
+                                    (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+            const bf16x8 B = bf16x8{(__bf16)gL[i][0], (__bf16)gL[i][1], (__bf16)gL[i][2], (__bf16)gL[i][3],
+                                    (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+            const f32x4 acc = mfma_bf16(A, B, f4zero());
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
 
     // ================= block forward substitution over all d_v + d_k columns:
     // X_I = D_I R_I - sum_{J<I} L'_IJ X_J. U^T and Y go to staging rows in LDS.
