@@ -28,8 +28,8 @@ int check_sizes(long long B, long long H, long long T, int dk, int dv, int dtype
   if (B < 1 || H < 1 || T < 1 || dk < 1 || dv < 1) return GDR_ERR_SHAPE;
   // element offsets are formed in 64-bit; grid sizes must fit in 31 bits
   if (B * H > (1LL << 24) || B * H * T > (1LL << 40)) return GDR_ERR_SHAPE;
-  // offsets within one head are 32-bit in the kernels
-  if (T * (long long)(dk > dv ? dk : dv) >= (1LL << 31)) return GDR_ERR_SHAPE;
+  // byte offsets within one head are 32-bit signed in the kernels
+  if (T * (long long)(dk > dv ? dk : dv) * (long long)esize(dtype) >= (1LL << 31)) return GDR_ERR_SHAPE;
   if (!is_pow2_dim(dk, maxd) || !is_pow2_dim(dv, maxd)) return GDR_ERR_UNSUPPORTED;
   return GDR_OK;
 }

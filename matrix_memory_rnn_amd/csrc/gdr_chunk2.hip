@@ -248,35 +248,76 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   // parts: 1 = alpha and k, 2 = b and q, 4 = v and w
   auto issue = [&](int it, int parts) {
     const int bh = it / nchunks, tb = (it % nchunks) * CM;
-    const size_t sK = (size_t)bh * T * DK + j, sV = (size_t)bh * T * DV;
-    if (parts & 1) {
+    if constexpr (!F32) {
+      // bf16: buffer loads over one sequence of each input; rows past T lie
+      // past the buffer's end and read as zero (alpha is set to 1 there by
+      // the caller), the row step is the instruction's immediate offset
+      constexpr int ES = (int)sizeof(Tin);
+      const unsigned nbK = (unsigned)T * DK * ES, nbV = (unsigned)T * DV * ES;
+      const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
+      const int vo = ((tb + r0) * DK + j) * ES;
+      auto rs = [&](const Tin* base, size_t off, unsigned nb) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<Tin*>(base + off), 0, nb, 0x00020000);
+      };
+      if (parts & 1) {
+        const __amdgpu_buffer_rsrc_t ra = rs(alpha, sK, nbK), rk = rs(k, sK, nbK);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = tb + r0 + r;
-        const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
-        xa[r] = RW::ld2(alpha + off);
-        xk[r] = RW::ld2(k + off);
+        for (int r = 0; r < 8; ++r) {
+          xa[r] = __builtin_amdgcn_raw_buffer_load_b32(ra, vo + r * DK * ES, 0, 0);
+          xk[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo + r * DK * ES, 0, 0);
+        }
       }
-    }
-    if (parts & 2) {
+      if (parts & 2) {
+        const __amdgpu_buffer_rsrc_t rb = rs(bgate, sK, nbK), rq = rs(q, sK, nbK);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = tb + r0 + r;
-        const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
-        xb[r] = RW::ld2(bgate + off);
-        xq[r] = RW::ld2(q + off);
+        for (int r = 0; r < 8; ++r) {
+          xb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo + r * DK * ES, 0, 0);
+          xq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo + r * DK * ES, 0, 0);
+        }
       }
-    }
-    if (parts & 4) {
+      if (parts & 4) {
+        const __amdgpu_buffer_rsrc_t rv = rs(v, sV, nbV), rw = rs(wgate, sV, nbV);
 #pragma unroll
-      for (int i = 0; i < MAXVI; ++i) {
-        const int idx = tid + kIntraThreads * i;
-        const int vi = idx < nvi ? idx : 0;
-        const int vrow = vi / (DV / 8), vcol = (vi % (DV / 8)) * 8;
-        const int tv = tb + vrow;
-        const size_t off = sV + (size_t)(tv < T ? tv : T - 1) * DV + vcol;
-        xv[i] = RW::ld8(v + off);
-        xw[i] = RW::ld8(wgate + off);
+        for (int i = 0; i < MAXVI; ++i) {
+          const int idx = tid + kIntraThreads * i;
+          const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
+          // items past the tile read past the buffer's end (zero)
+          const int vv = idx < nvi ? ((tb + vrow) * DV + vcol) * ES : 0x7ffffff0;
+          xv[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rv, vv, 0, 0));
+          xw[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rw, vv, 0, 0));
+        }
+      }
+    } else {
+      const size_t sK = (size_t)bh * T * DK + j, sV = (size_t)bh * T * DV;
+      if (parts & 1) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb + r0 + r;
+          const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
+          xa[r] = RW::ld2(alpha + off);
+          xk[r] = RW::ld2(k + off);
+        }
+      }
+      if (parts & 2) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = tb + r0 + r;
+          const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
+          xb[r] = RW::ld2(bgate + off);
+          xq[r] = RW::ld2(q + off);
+        }
+      }
+      if (parts & 4) {
+#pragma unroll
+        for (int i = 0; i < MAXVI; ++i) {
+          const int idx = tid + kIntraThreads * i;
+          const int vi = idx < nvi ? idx : 0;
+          const int vrow = vi / (DV / 8), vcol = (vi % (DV / 8)) * 8;
+          const int tv = tb + vrow;
+          const size_t off = sV + (size_t)(tv < T ? tv : T - 1) * DV + vcol;
+          xv[i] = RW::ld8(v + off);
+          xw[i] = RW::ld8(wgate + off);
+        }
       }
     }
   };
@@ -309,27 +350,37 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     Tin* KTg = (Tin*)(rec + RL.kt);
     float* PICg = (float*)(rec + RL.pic);
 
-    // identity padding past the end of the sequence: alpha = 1, k = b = q = 0, v = w = 0
+    // identity padding past the end of the sequence: alpha = 1, k = b = q = 0,
+    // v = w = 0 (bf16: the buffer loads already read zeros there)
     float vh[MAXVI][8];
     {
       const typename RW::R2 one = RW::pad2(1.f), zero = RW::pad2(0.f);
+      if (t0 + CM > T) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const bool ok = t0 + r0 + r < T;
-        xa[r] = RW::sel(ok, xa[r], one);
-        xk[r] = RW::sel(ok, xk[r], zero);
-        xb[r] = RW::sel(ok, xb[r], zero);
-        xq[r] = RW::sel(ok, xq[r], zero);
+        for (int r = 0; r < 8; ++r) {
+          const bool ok = t0 + r0 + r < T;
+          xa[r] = RW::sel(ok, xa[r], one);
+          if constexpr (F32) {
+            xk[r] = RW::sel(ok, xk[r], zero);
+            xb[r] = RW::sel(ok, xb[r], zero);
+            xq[r] = RW::sel(ok, xq[r], zero);
+          }
+        }
       }
 #pragma unroll
       for (int i = 0; i < MAXVI; ++i) {
         const int idx = tid + kIntraThreads * i;
-        const bool okv = idx < nvi && t0 + idx / (DV / 8) < T;
         float fv[8], fw[8];
         RW::un8(xv[i], fv);
         RW::un8(xw[i], fw);
+        if constexpr (F32) {
+          const bool okv = idx < nvi && t0 + idx / (DV / 8) < T;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vh[i][e] = okv ? fv[e] * fw[e] : 0.f;
+          for (int e = 0; e < 8; ++e) vh[i][e] = okv ? fv[e] * fw[e] : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vh[i][e] = fv[e] * fw[e];
+        }
       }
     }
 
@@ -769,20 +820,27 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       int sr = c16, sg = g;
       asm volatile("" : "+v"(sr), "+v"(sg));
       bf16x4 X[NB][MAXX];
+      // every operand read up front (none of them depends on the solve)
+      bf16x4 A0s[NB][(NB + 1) / 2], A1s[NB][(NB + 1) / 2], RHs[NB][MAXX];
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
-        bf16x4 A0[(NB + 1) / 2], A1[(NB + 1) / 2], RH[MAXX];
         const __bf16* trow = TLb + (16 * I + sr) * L::LDC + 4 * sg;
 #pragma unroll
         for (int pp = 0; 2 * pp <= I; ++pp) {
-          A0[pp] = *(const bf16x4*)(trow + 32 * pp);
-          A1[pp] = 2 * pp + 1 <= I ? *(const bf16x4*)(trow + 32 * pp + 16) : z4;
+          A0s[I][pp] = *(const bf16x4*)(trow + 32 * pp);
+          A1s[I][pp] = 2 * pp + 1 <= I ? *(const bf16x4*)(trow + 32 * pp + 16) : z4;
         }
 #pragma unroll
         for (int i = 0; i < MAXX; ++i) {
           const int ct = wid + NW * i;
-          RH[i] = ct < NX ? *(const bf16x4*)(XRb + xoff(16 * ct + sr, 16 * I + 4 * sg)) : z4;
+          RHs[I][i] = ct < NX ? *(const bf16x4*)(XRb + xoff(16 * ct + sr, 16 * I + 4 * sg)) : z4;
         }
+      }
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        const bf16x4* A0 = A0s[I];
+        const bf16x4* A1 = A1s[I];
+        const bf16x4* RH = RHs[I];
         f32x4 acc[MAXX];
 #pragma unroll
         for (int i = 0; i < MAXX; ++i) acc[i] = f4zero();

@@ -77,6 +77,9 @@ def test_chunk_validation(lib):
     assert _chunk(lib, ptrs=[None] + P[1:7]) == c["GDR_ERR_NULL"]
     assert _chunk(lib, T=0) == c["GDR_ERR_SHAPE"]
     assert _chunk(lib, B=0) == c["GDR_ERR_SHAPE"]
+    # one head's bytes must stay below 2**31 (32-bit signed offsets in the kernels)
+    assert _chunk(lib, T=1 << 23, dk=128, dv=128, chunk=64, dtype=1) == c["GDR_ERR_SHAPE"]
+    assert _chunk(lib, T=1 << 22, dk=128, dv=128, chunk=32, dtype=0) == c["GDR_ERR_SHAPE"]
     assert _chunk(lib, dtype=7) == c["GDR_ERR_DTYPE"]
     assert _chunk(lib, dk=48) == c["GDR_ERR_UNSUPPORTED"]
     assert _chunk(lib, dv=256) == c["GDR_ERR_UNSUPPORTED"]
