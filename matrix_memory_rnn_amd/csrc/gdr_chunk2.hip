@@ -85,6 +85,48 @@ template <> struct Out<__bf16> {
   }
 };
 
+typedef __attribute__((ext_vector_type(2))) uint32_t u2_t;
+
+// Stores into one workspace record through a buffer resource: byte offsets
+// are 32-bit (constant parts become immediates), values converted to the
+// record's element type.
+template <typename E> struct RecSt;
+template <> struct RecSt<float> {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ void pair(int off, float a, float b) const {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, make_float2(a, b)), r, off, 0, 0);
+  }
+  __device__ __forceinline__ void quad(int off, f32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+  }
+  __device__ __forceinline__ void oct(int off, const float* x) const {
+    quad(off, f32x4{x[0], x[1], x[2], x[3]});
+    quad(off + 16, f32x4{x[4], x[5], x[6], x[7]});
+  }
+  __device__ __forceinline__ void raw16(int off, u32x4 v) const { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+};
+template <> struct RecSt<__bf16> {
+  __amdgpu_buffer_rsrc_t r;
+  static __device__ __forceinline__ uint32_t pk(float a, float b) {
+    bf16x2 h;
+    h.x = (__bf16)a;
+    h.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ __forceinline__ void pair(int off, float a, float b) const {
+    __builtin_amdgcn_raw_buffer_store_b32(pk(a, b), r, off, 0, 0);
+  }
+  __device__ __forceinline__ void quad(int off, f32x4 v) const {
+    const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+    __builtin_amdgcn_raw_buffer_store_b64(u2_t{pk(v0, v1), pk(v2, v3)}, r, off, 0, 0);
+  }
+  __device__ __forceinline__ void oct(int off, const float* x) const {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{pk(x[0], x[1]), pk(x[2], x[3]), pk(x[4], x[5]), pk(x[6], x[7])},
+                                           r, off, 0, 0);
+  }
+  __device__ __forceinline__ void raw16(int off, u32x4 v) const { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+};
+
 // Right-looking forward substitution step for columns 4*M4 .. 4*M4+3 of a
 // unit lower-triangular 16x16 system (rows of L in LDS with pitch LDB): once
 // x[m] is final it is subtracted from every later row, so the dependent chain
@@ -343,12 +385,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     const int bh = item / nchunks, t0 = (item % nchunks) * CM;
     const size_t seqK = (size_t)bh * T * DK;
     char* rec = ws + (size_t)item * RL.bytes;
-    Tin* Yg = (Tin*)(rec + RL.y);
-    Tin* UTg = (Tin*)(rec + RL.ut);
-    Tin* Mg = (Tin*)(rec + RL.m);
-    Tin* QPg = (Tin*)(rec + RL.qp);
-    Tin* KTg = (Tin*)(rec + RL.kt);
-    float* PICg = (float*)(rec + RL.pic);
+    const RecSt<Tin> RS{__builtin_amdgcn_make_buffer_rsrc(rec, 0, RL.bytes, 0x00020000)};
+    constexpr int ES = (int)sizeof(Tin);
 
     // identity padding past the end of the sequence: alpha = 1, k = b = q = 0,
     // v = w = 0 (bf16: the buffer loads already read zeros there)
@@ -433,7 +471,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         pic.y *= gy;
       }
       if (h == 0) {
-        if (I0 == 0) *(float2*)(PICg + j) = pic;
+        if (I0 == 0) RecSt<float>{RS.r}.pair(RL.pic + 4 * j, pic.x, pic.y);
         const float gx = GS[I0 * DK + j], gy = GS[I0 * DK + j + 1];
         SCL[pidx(I0, I0) * DK + j] = __builtin_amdgcn_rcpf(gx);
         SCL[pidx(I0, I0) * DK + j + 1] = __builtin_amdgcn_rcpf(gy);
@@ -460,7 +498,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         if constexpr (FM)   // staged [t][j] in US, stored in F order after the Gram tiles
           Out<Tin>::pair((Tin*)(smem + L::US) + (r0 + r) * L::LDU + j, Bst.x * qrx, Bst.y * qry);
         else
-          Out<Tin>::pair(QPg + o_tk(r0 + r, j), Bst.x * qrx, Bst.y * qry);
+          RS.pair(RL.qp + o_tk(r0 + r, j) * ES, Bst.x * qrx, Bst.y * qry);
       }
       float ktx[8], kty[8];
       float2 qs = h ? make_float2(1.f, 1.f) : p1;
@@ -474,8 +512,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         qs.x *= a.x;
         qs.y *= a.y;
       }
-      Out<Tin>::oct(KTg + o_kt(j, r0), ktx);
-      Out<Tin>::oct(KTg + o_kt(j + 1, r0), kty);
+      RS.oct(RL.kt + o_kt(j, r0) * ES, ktx);
+      RS.oct(RL.kt + o_kt(j + 1, r0) * ES, kty);
       if constexpr (L::XR_EARLY) {
 #pragma unroll
         for (int r4 = 0; r4 < 2; ++r4) {
@@ -528,7 +566,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         // consecutive F-order pieces (US is free again before the solve)
         for (int idx = tid; idx < CM * DK / 8; idx += kIntraThreads) {
           const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31), pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
-          *(u32x4*)(QPg + 8 * idx) = *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc));
+          RS.raw16(RL.qp + 16 * idx, *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc)));
         }
       }
 
@@ -550,11 +588,11 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
             }
           }
           *(f32x4*)(LBK + p * BLKF + c16 * L::LDB + 4 * g) = lv;
-          Out<Tin>::quad(Mg + o_m(t, s0), mv);
+          RS.quad(RL.m + o_m(t, s0) * ES, mv);
           // F order: the scan multiplies M in 32-column slices up to the
           // diagonal, so the block right of an even diagonal block is zero
           if constexpr (FM) {
-            if (I == J && (I & 1) == 0) Out<Tin>::quad(Mg + o_m(t, s0 + 16), f4zero());
+            if (I == J && (I & 1) == 0) RS.quad(RL.m + o_m(t, s0 + 16) * ES, f4zero());
           }
         }
       }
@@ -649,23 +687,32 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         const int p = pidx(I, J);
         const bool scaled = (I == J) || (I > J + 1);
         Frag<MM> A[KS], BL[KS], BM[KS];
+        f32x4 sa[KS], sb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           A[ks] = ldfrag<MM>(smem + L::KC, L::P_CK, L::LDK, 16 * J, 32 * ks, DK, lane);
           BL[ks] = ldfrag<MM>(smem + L::KR, L::P_CK, L::LDK, 16 * I, 32 * ks, DK, lane);
           BM[ks] = ldfrag<MM>(smem + L::QR, L::P_CK, L::LDK, 16 * I, 32 * ks, DK, lane);
         }
+        if (scaled) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            // slices past d_k (d_k = 16) are zero fragments: any finite scale
+            const int kk = 32 * ks + 8 * g < DK ? 32 * ks + 8 * g : 0;
+            sa[ks] = *(const f32x4*)(SCL + p * DK + kk);
+            sb[ks] = *(const f32x4*)(SCL + p * DK + kk + 4);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const float sv[8] = {sa[ks][0], sa[ks][1], sa[ks][2], sa[ks][3],
+                                 sb[ks][0], sb[ks][1], sb[ks][2], sb[ks][3]};
+            scale_frag<MM>(A[ks], sv);
+          }
+        }
         l = f4zero();
         m = f4zero();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          // slices past d_k (d_k = 16) are zero fragments and stay unscaled
-          if (scaled && 32 * ks + 8 * g < DK) {
-            const float* sp = SCL + p * DK + 32 * ks + 8 * g;
-            const f32x4 s0 = *(const f32x4*)sp, s1 = *(const f32x4*)(sp + 4);
-            const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-            scale_frag<MM>(A[ks], sv);
-          }
           mma<MM>(l, BL[ks], A[ks]);
           mma<MM>(m, A[ks], BM[ks]);
         }
@@ -673,11 +720,23 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       // M rows t = 16 I + c16, columns 16 J + 4g .. to the record
       auto store_m = [&](int I, int J, const f32x4& mv) {
         const int t = 16 * I + c16, s0 = 16 * J + 4 * g;
-        Out<Tin>::quad(Mg + o_m(t, s0), mv);
+        RS.quad(RL.m + o_m(t, s0) * ES, mv);
         // F order: the scan multiplies M in 32-column slices up to the
         // diagonal, so the block right of an even diagonal block is zero
         if constexpr (FM) {
-          if (I == J && (I & 1) == 0) Out<Tin>::quad(Mg + o_m(t, s0 + 16), f4zero());
+          if (I == J && (I & 1) == 0) RS.quad(RL.m + o_m(t, s0 + 16) * ES, f4zero());
+        }
+      };
+      // waves past the off-diagonal pairs' full rounds have spare time in
+      // the Gram phase
+      constexpr int NLIGHT = NQ % NOW == 0 ? 0 : NOW - NQ % NOW;
+      // Q_pi from its staging rows to the record: consecutive threads write
+      // consecutive F-order pieces (US is free again before the solve)
+      auto qpi_store = [&](int t0i, int nthr) {
+        for (int idx = t0i; idx < CM * DK / 8; idx += nthr) {
+          const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31),
+                    pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
+          RS.raw16(RL.qp + 16 * idx, *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc)));
         }
       };
       f32x4 gL[MAXO];
@@ -747,6 +806,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
             store_m(I, J, mv);
           }
         }
+        if constexpr (FM && NLIGHT > 0) {
+          // the waves with one pair fewer store Q_pi here
+          if (wid >= NW - NLIGHT) qpi_store(tid - 64 * (NW - NLIGHT), 64 * NLIGHT);
+        }
       }
       __syncthreads();
 
@@ -756,15 +819,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       issue(nxt, 2);
       if (tid < 4) FLAGS[tid] = 0;   // read above; set again by the next item's prep 1
       if (dwave) {
-        if constexpr (FM) {
-          // Q_pi from its staging rows to the record: consecutive threads
-          // write consecutive F-order pieces (US is free again before the solve)
-          for (int idx = tid; idx < CM * DK / 8; idx += 64 * NB) {
-            const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31),
-                      pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
-            *(u32x4*)(QPg + 8 * idx) = *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc));
-          }
-        }
+        if constexpr (FM && NLIGHT == 0) qpi_store(tid, 64 * NB);
       } else {
 #pragma unroll
         for (int i = 0; i < MAXO; ++i) {
@@ -795,7 +850,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           // staged as U^T rows in LDS, stored in F order after the solve
           Out<Tin>::quad((Tin*)(smem + L::US) + (16 * ct + c16) * L::LDUT + 16 * I + 4 * g, x);
         } else {
-          Out<Tin>::quad(UTg + o_ut(16 * ct + c16, 16 * I + 4 * g), x);
+          RS.quad(RL.ut + o_ut(16 * ct + c16, 16 * I + 4 * g) * ES, x);
         }
       } else {
         const int jj = 16 * ct - DV + c16;
@@ -910,10 +965,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         // consecutive threads write consecutive F-order pieces
         static_assert(!FM || sizeof(Tin) == 2, "F order is bf16");
         const int q2 = idx >> 6, t = 32 * (q2 / (DK / 16)) + (idx & 31), pc = 2 * (q2 % (DK / 16)) + ((idx >> 5) & 1);
-        *(u32x4*)(Yg + 8 * idx) = *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc);
+        RS.raw16(RL.y + 16 * idx, *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc));
       } else {
         const int t = idx / YPR, pc = idx % YPR;
-        *(u32x4*)(Yg + o_tk(t, 16 * pc / (int)sizeof(Tin))) = *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc);
+        RS.raw16(RL.y + o_tk(t, 16 * pc / ES) * ES, *(const u32x4*)((const char*)(YS + t * L::LDY) + 16 * pc));
       }
     }
     if constexpr (FM) {
@@ -928,8 +983,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         const char* row = USb + 2 * (vv * L::LDUT + tb);
         const u2 a0 = *(const u2*)(row), a1 = *(const u2*)(row + 16), a2 = *(const u2*)(row + 32),
                  a3 = *(const u2*)(row + 48);
-        *(u32x4*)(UTg + 16 * sidx) = u32x4{a0.x, a0.y, a1.x, a1.y};
-        *(u32x4*)(UTg + 16 * sidx + 8) = u32x4{a2.x, a2.y, a3.x, a3.y};
+        RS.raw16(RL.ut + 32 * sidx, u32x4{a0.x, a0.y, a1.x, a1.y});
+        RS.raw16(RL.ut + 32 * sidx + 16, u32x4{a2.x, a2.y, a3.x, a3.y});
       }
     }
   }
