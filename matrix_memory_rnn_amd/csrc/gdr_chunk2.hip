@@ -1696,6 +1696,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
     const bool toucher = live && J2 < 3;
     auto touch = [&](int ch) { return __builtin_amdgcn_raw_buffer_load_b32(wrsrc, v_pf, cbase(ch), 0); };
     uint32_t sink = 0, PFV[PF];
+    const int pbase = 16 * h;                           // lane byte address of pi_C row 4h
 
     f32x16 Sacc;
 #pragma unroll
@@ -1735,16 +1736,15 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
           sink ^= PFV[u % PF];
           PFV[u % PF] = touch(ch + PF);
         }
-        // entry 4q + e is row 32 J2 + 8q + 4h + e, whose pi_C lane 8q + 4h + e holds
-        const int pb = __builtin_bit_cast(int, RP[u % NS]);
+        // entry 4q + e is row 32 J2 + 8q + 4h + e, whose pi_C lane 8q + 4h + e
+        // holds: one lane permute per entry (the constant part of the lane
+        // address is the instruction's offset)
+        const int pb = __float_as_int(RP[u % NS]);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(pb, 8 * q + e));
-            const float p1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(pb, 8 * q + 4 + e));
-            Sacc[4 * q + e] *= h ? p1 : p0;
-          }
+          for (int e = 0; e < 4; ++e)
+            Sacc[4 * q + e] *= __int_as_float(__builtin_amdgcn_ds_bpermute(pbase + 4 * (8 * q + e), pb));
       }
       phase_barrier();                                  // A
       if (live) {
