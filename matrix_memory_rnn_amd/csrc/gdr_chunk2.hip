@@ -379,9 +379,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   for (; item < nitems; item += gridDim.x) {
     if constexpr (F32) issue(item, 7);
     // the item whose inputs are fetched during this one: the next of this
-    // workgroup, or this one again after the last (the loads are always
-    // issued, so the wait counts do not depend on a branch)
-    const int nxt = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : item;
+    // workgroup, or item 0 after the last (the loads are always issued, so the
+    // wait counts do not depend on a branch; every workgroup's last fetch
+    // reads the same item, which the L2 serves)
+    const int nxt = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : 0;
     const int bh = item / nchunks, t0 = (item % nchunks) * CM;
     const size_t seqK = (size_t)bh * T * DK;
     char* rec = ws + (size_t)item * RL.bytes;
