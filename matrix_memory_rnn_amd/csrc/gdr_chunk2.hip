@@ -151,19 +151,6 @@ __device__ __forceinline__ void fs_group(const float* Lb, float* x) {
   fs_load<M4, LDB>(Lb, lc);
   fs_apply<M4>(lc, x);
 }
-// All four column groups, each group's rows read one group ahead of its use.
-template <int LDB>
-__device__ __forceinline__ void fs_all(const float* Lb, float* x) {
-  f32x4 la[16], lb[16];
-  fs_load<0, LDB>(Lb, la);
-  fs_load<1, LDB>(Lb, lb);
-  fs_apply<0>(la, x);
-  fs_load<2, LDB>(Lb, la);
-  fs_apply<1>(lb, x);
-  fs_load<3, LDB>(Lb, lb);
-  fs_apply<2>(la, x);
-  fs_apply<3>(lb, x);
-}
 
 // ============================================================================ intra kernel
 constexpr int kIntraThreads = 512;
@@ -383,6 +370,12 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     // wait counts do not depend on a branch; every workgroup's last fetch
     // reads the same item, which the L2 serves)
     const int nxt = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : 0;
+    // lane-derived values through an empty asm once per item: lane
+    // predicates formed from them are computed where they are used instead of
+    // being kept (and spilled) as scalar lane masks across the loop
+    int hq = h, gq = g, cq = c16;
+    asm volatile("" : "+v"(hq), "+v"(gq), "+v"(cq));
+    const bool actq = (NB * (DK / 2) >= kIntraThreads / 2) || act;
     const int bh = item / nchunks, t0 = (item % nchunks) * CM;
     const size_t seqK = (size_t)bh * T * DK;
     char* rec = ws + (size_t)item * RL.bytes;
@@ -451,8 +444,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       ph.y *= a.y;
     }
     const float2 po = make_float2(__shfl_xor(ph.x, 32, 64), __shfl_xor(ph.y, 32, 64));
-    const float2 p0 = h ? po : ph, p1 = h ? ph : po;
-    if (act && h == 0) {
+    const float2 p0 = hq ? po : ph, p1 = hq ? ph : po;
+    if (actq && hq == 0) {
       const float gx = p0.x * p1.x, gy = p0.y * p1.y;
       GS[I0 * DK + j] = gx;
       GS[I0 * DK + j + 1] = gy;
@@ -462,7 +455,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
 
     // ================= prep 2: Gram operands, Q_pi, K~^T, pi_C, scale vectors
     float2 khp[8];
-    if (act) {
+    if (actq) {
       float2 Bst = make_float2(1.f, 1.f), E = make_float2(1.f, 1.f), pic = make_float2(1.f, 1.f);
       for (int J = 0; J < NB; ++J) {
         const float gx = GS[J * DK + j], gy = GS[J * DK + j + 1];
@@ -471,7 +464,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         pic.x *= gx;
         pic.y *= gy;
       }
-      if (h == 0) {
+      if (hq == 0) {
         if (I0 == 0) RecSt<float>{RS.r}.pair(RL.pic + 4 * j, pic.x, pic.y);
         const float gx = GS[I0 * DK + j], gy = GS[I0 * DK + j + 1];
         SCL[pidx(I0, I0) * DK + j] = __builtin_amdgcn_rcpf(gx);
@@ -484,7 +477,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           d.y *= GS[J * DK + j + 1];
         }
       }
-      float2 P = h ? p0 : make_float2(1.f, 1.f);
+      float2 P = hq ? p0 : make_float2(1.f, 1.f);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const float2 a = RW::un2(xa[r]), kk = RW::un2(xk[r]), bb = RW::un2(xb[r]), qq = RW::un2(xq[r]);
@@ -502,7 +495,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           RS.pair(RL.qp + o_tk(r0 + r, j) * ES, Bst.x * qrx, Bst.y * qry);
       }
       float ktx[8], kty[8];
-      float2 qs = h ? make_float2(1.f, 1.f) : p1;
+      float2 qs = hq ? make_float2(1.f, 1.f) : p1;
 #pragma unroll
       for (int r = 7; r >= 0; --r) {
         const float2 kk = RW::un2(xk[r]), a = RW::un2(xa[r]);
@@ -745,11 +738,11 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         const int I = wid;
         f32x4 lv, mv;
         gram(I, I, lv, mv);
-        const int t = 16 * I + c16, s0 = 16 * I + 4 * g;
+        const int t = 16 * I + cq, s0 = 16 * I + 4 * gq;
         // entry e is L[4g + e][c16]: strictly lower part only
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c16 >= 4 * g + e) lv[e] = 0.f;
+          if (cq >= 4 * gq + e) lv[e] = 0.f;
         if (FLAGS[I]) {
           // exact products, formed for row t = c16 and columns 4g .. 4g+3 (the
           // M layout), brought to the L layout through LDS
@@ -771,23 +764,26 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         // column cc of D_I by right-looking substitution; L[r][m] is entry
         // r % 4 of lane 16 (r / 4) + m, read as a wave-uniform scalar (every
         // lane group computes the column; group 0 writes it)
-        // (__float_as_int, not __builtin_bit_cast: this compiler's bit cast
-        // of a vector element reads element 0 whatever the index)
+        // column cc of D_I by right-looking substitution over the rows of
+        // L_II, staged in LDS and read as broadcast rows (every lane group
+        // computes the column; group 0 writes it). Lane reads of the
+        // accumulator instead would hold up to 15 scalars per step, and the
+        // scalar registers they take cost more spills than the LDS round trip.
         const int cc = c16;
-        const int li[4] = {__float_as_int(lv[0]), __float_as_int(lv[1]), __float_as_int(lv[2]),
-                           __float_as_int(lv[3])};
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+        {
+          float* Lq = LBD + I * BLKF;
 #pragma unroll
-        for (int m = 0; m < 15; ++m) {
-#pragma unroll
-          for (int r = m + 1; r < 16; ++r) {
-            const float lrm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(li[r & 3], 16 * (r >> 2) + m));
-            x[r] -= lrm * x[m];
-          }
+          for (int e = 0; e < 4; ++e) Lq[(4 * g + e) * L::LDB + c16] = lv[e];
+          wave_lds_sync();
+          fs_group<0, L::LDB>(Lq, x);
+          fs_group<1, L::LDB>(Lq, x);
+          fs_group<2, L::LDB>(Lq, x);
+          fs_group<3, L::LDB>(Lq, x);
         }
-        if (g == 0) {
+        if (gq == 0) {
           float* Tn = TBN + I * BLKF;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
