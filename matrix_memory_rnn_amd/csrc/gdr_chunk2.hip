@@ -210,7 +210,10 @@ struct IntraSmem {
   static constexpr int LBD = US + imax(CM * LDU, kMaxDv * LDUT) * 2;   // diagonal L fp32 [I][t][s]
   static constexpr int TBN = F32 ? TBN_B : LBD + NBM * BLK;
   static constexpr int TL = F32 ? TL_B : TBN + NBM * BLK;
-  static constexpr int TOTAL = F32 ? FLAG + 16 : TL + P_CC;
+  // bf16: -L_IJ of the off-diagonal pairs in accumulator lane order (8 bytes
+  // per lane), read by every wave to form the L' blocks it needs
+  static constexpr int LT = TL + P_CC;
+  static constexpr int TOTAL = F32 ? FLAG + 16 : LT + (NBM * (NBM - 1) / 2) * 512;
   static_assert(TOTAL <= 160 * 1024, "intra kernel LDS exceeds 160 KiB");
 };
 
@@ -733,7 +736,6 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           RS.raw16(RL.qp + 16 * idx, *(const u32x4*)(smem + L::US + 2 * (t * L::LDU + 8 * pc)));
         }
       };
-      f32x4 gL[MAXO];
       if (dwave) {
         const int I = wid;
         f32x4 lv, mv;
@@ -798,9 +800,12 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           if (qq < NQ) {
             int I, J;
             offpair_of(qq, I, J);
-            f32x4 mv;
-            gram(I, J, gL[i], mv);
+            f32x4 mv, lv;
+            gram(I, J, lv, mv);
             store_m(I, J, mv);
+            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+            *(bf16x4*)(smem + L::LT + 512 * qq + 8 * lane) =
+                bf16x4{(__bf16)(-lv[0]), (__bf16)(-lv[1]), (__bf16)(-lv[2]), (__bf16)(-lv[3])};
           }
         }
         if constexpr (FM && NLIGHT > 0) {
@@ -810,33 +815,11 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       }
       __syncthreads();
 
-      // ================= L'_IJ = D_I L_IJ (I > J), stored negated in the rows of TL.
-      // k runs over t = 4g .. 4g+3 in lane group g (entries 0-3; 4-7 are zero):
-      // the B operand is this wave's L_IJ accumulator as it stands.
+      __syncthreads();
+      // the last part of the next item's loads
       issue(nxt, 2);
       if (tid < 4) FLAGS[tid] = 0;   // read above; set again by the next item's prep 1
-      if (dwave) {
-        if constexpr (FM && NLIGHT == 0) qpi_store(tid, 64 * NB);
-      } else {
-#pragma unroll
-        for (int i = 0; i < MAXO; ++i) {
-          const int qq = (wid - NB) + NOW * i;
-          if (qq < NQ) {
-            int I, J;
-            offpair_of(qq, I, J);
-            const f32x4 dv4 = *(const f32x4*)(TBN + I * BLKF + c16 * L::LDB + 4 * g);
-            const bf16x8 A = bf16x8{(__bf16)dv4[0], (__bf16)dv4[1], (__bf16)dv4[2], (__bf16)dv4[3],
-                                    (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-            const bf16x8 B = bf16x8{(__bf16)gL[i][0], (__bf16)gL[i][1], (__bf16)gL[i][2], (__bf16)gL[i][3],
-                                    (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-            const f32x4 acc = mfma_bf16(A, B, f4zero());
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              st1<MT>(smem + L::TL, L::P_CC, (16 * I + 4 * g + e) * L::LDC + 16 * J + c16, -acc[e]);
-          }
-        }
-      }
-      __syncthreads();
+      if constexpr (FM && NLIGHT == 0) qpi_store(tid, kIntraThreads);
     }
 
     // ================= block forward substitution over all d_v + d_k columns:
@@ -872,16 +855,17 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       int sr = c16, sg = g;
       asm volatile("" : "+v"(sr), "+v"(sg));
       bf16x4 X[NB][MAXX];
-      // every operand read up front (none of them depends on the solve)
-      bf16x4 A0s[NB][(NB + 1) / 2], A1s[NB][(NB + 1) / 2], RHs[NB][MAXX];
+      // every operand read up front (none of them depends on the solve): the
+      // right-hand sides, D_I (rows of the diagonal blocks of TL), and
+      // -L'_IJ for J < I, formed here by every wave as (L'_IJ)^T = L_IJ^T D_I^T
+      // from -L_IJ in accumulator lane order (the A operand as it stands) and
+      // rows of D_I: the product lands in lane (g, m) as row m, columns
+      // 4g .. 4g+3 of -L'_IJ, which is this step's A operand layout
+      bf16x4 DI[NB], Lp[NB][NB], RHs[NB][MAXX];
+      const int sl = 16 * sg + sr;
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
-        const __bf16* trow = TLb + (16 * I + sr) * L::LDC + 4 * sg;
-#pragma unroll
-        for (int pp = 0; 2 * pp <= I; ++pp) {
-          A0s[I][pp] = *(const bf16x4*)(trow + 32 * pp);
-          A1s[I][pp] = 2 * pp + 1 <= I ? *(const bf16x4*)(trow + 32 * pp + 16) : z4;
-        }
+        DI[I] = *(const bf16x4*)(TLb + (16 * I + sr) * L::LDC + 16 * I + 4 * sg);
 #pragma unroll
         for (int i = 0; i < MAXX; ++i) {
           const int ct = wid + NW * i;
@@ -889,9 +873,19 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         }
       }
 #pragma unroll
+      for (int I = 1; I < NB; ++I) {
+        const f32x4 d4 = *(const f32x4*)(TBN + I * BLKF + sr * L::LDB + 4 * sg);
+        const bf16x8 Bd = bf16x8{(__bf16)d4[0], (__bf16)d4[1], (__bf16)d4[2], (__bf16)d4[3],
+                                 (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+          const bf16x4 lt = *(const bf16x4*)(smem + L::LT + 512 * (I * (I - 1) / 2 + J) + 8 * sl);
+          const f32x4 pr = mfma_bf16(__builtin_shufflevector(lt, z4, 0, 1, 2, 3, 4, 5, 6, 7), Bd, f4zero());
+          Lp[I][J] = bf16x4{(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+        }
+      }
+#pragma unroll
       for (int I = 0; I < NB; ++I) {
-        const bf16x4* A0 = A0s[I];
-        const bf16x4* A1 = A1s[I];
         const bf16x4* RH = RHs[I];
         f32x4 acc[MAXX];
 #pragma unroll
@@ -899,7 +893,9 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
 #pragma unroll
         for (int pp = 0; 2 * pp <= I; ++pp) {
           const int J0 = 2 * pp, J1 = 2 * pp + 1;
-          const bf16x8 A = __builtin_shufflevector(A0[pp], A1[pp], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x4 a0 = J0 < I ? Lp[I][J0] : DI[I];
+          const bf16x4 a1 = J1 < I ? Lp[I][J1] : (J1 == I ? DI[I] : z4);
+          const bf16x8 A = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int i = 0; i < MAXX; ++i) {
             if (wid + NW * i < NX) {
