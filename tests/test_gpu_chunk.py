@@ -233,6 +233,22 @@ def test_wide_batch_fragment_order_path(dk, dv, chunk):
     _check(d, chunk, f"bf16 wide B={B} H={H} dk={dk} dv={dv} C={chunk} T={T}", path="ws")
 
 
+@pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (64, 64, 32)])
+def test_wide_batch_tiny_decay_exact_path(dk, dv, chunk):
+    """The fragment-order path with blocks whose decay leaves the in-block
+    factorisation's range (exact products for those diagonal tiles)."""
+    heads = -(-256 // (dv // 32))
+    B, H = 2, heads // 2
+    T = 3 * chunk + 5
+    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=3.5, alpha_sigma=1.2, seed=7 + dk + chunk,
+                    dtype="bf16", s0_std=0.2)
+    # powers of two: exact in bf16, so the oracle sees the kernel's inputs
+    d["alpha"][0, 1, 20:40, :8] = 2.0 ** -13
+    d["alpha"][1, 3, chunk + 2:chunk + 4, 10:20] = 2.0 ** -100
+    d["alpha"][1, H - 1, T - 7:T - 5, 3] = 0.0
+    _check(d, chunk, f"bf16 wide tiny alpha B={B} H={H} dk={dk} dv={dv} C={chunk} T={T}", path="ws")
+
+
 def test_wide_batch_phase_entry_points_equal_one_call():
     import torch
     import matrix_memory_rnn_amd as gdr
