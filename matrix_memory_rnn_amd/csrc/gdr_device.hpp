@@ -249,6 +249,13 @@ __device__ __forceinline__ void st1(char* base, int plane, int off, float a) {
   }
 }
 
+// acc += A * B with A a split bf16 fragment (hi + lo planes, about 16
+// mantissa bits) and B a plain bf16 one: two MFMAs.
+__device__ __forceinline__ void mma_split(f32x4& acc, const Frag<kSP>& a, const Frag<kBF>& b) {
+  acc = mfma_bf16(a.hi, b.hi, acc);
+  acc = mfma_bf16(a.lo, b.hi, acc);
+}
+
 // Read one element back as float.
 template <int MODE>
 __device__ __forceinline__ float ld1(const char* base, int plane, int off) {

@@ -43,9 +43,10 @@ struct MlstmSmem {
   static constexpr int VTR = KT + NS * P_KT;   // [v][s] raw values, ones row for n
   static constexpr int VTW = VTR + NS * P_V;   // [v][s] scaled by e^{a_s - mu_C}
   static constexpr int W = VTW + NS * P_V;     // [t][s] (q.k) e^{a_s - mu_t}
-  static constexpr int C0T = W + NS * P_W;     // [v][j] state^T (+ n row)
-  static constexpr int SC = C0T + NS * P_C0;   // fp32 scalars: a, mu, m, wstate, nbar
-  static constexpr int TOTAL = SC + 5 * CM * 4 + 16;
+  static constexpr int C0T = W + NS * P_W;     // [v][j] state^T (+ n row): fp32, or bf16 hi + lo planes
+  static constexpr int SC = C0T + 2 * P_C0;    // fp32 scalars: a, mu, m, wstate, nbar
+  static constexpr int WP = SC + 5 * CM * 4 + 16;   // fp32 row sums of W per s-block [J][t]
+  static constexpr int TOTAL = WP + (CM / 16) * CM * 4;
   static_assert(TOTAL <= 160 * 1024, "mLSTM kernel LDS exceeds 160 KiB");
 };
 
@@ -62,6 +63,9 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
     Tin* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV, int C) {
   using L = MlstmSmem<DK, VT, CM, SPLIT>;
   constexpr int MM = SPLIT ? kF32 : kBF;  // fp32 inputs: fp32 MFMA; bf16 inputs: bf16 MFMA
+  // the state copy that q reads: fp32, or bf16 hi + lo planes (the readout's
+  // sums can cancel, so a single bf16 rounding of the state is not enough)
+  constexpr int SM = SPLIT ? kF32 : kSP;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NVL = VT / 16, NVA = L::NVA;
   constexpr int NST = (DK / 16) * NVA;
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
   float* sM = sMu + CM;
   float* sWs = sM + CM;
   float* sN = sWs + CM;
+  float* sWP = (float*)(smem + L::WP);
 
   // ---- state slice [C | n] -> registers and C0^T (bf16)
   const bool have_state = (C0 != nullptr);
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
           else Sacc[i][e] = (c16 == 0) ? n0[(size_t)bh * DK + j] : 0.f;
         }
       }
-      st4<MM>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+      st4<SM>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
     }
   }
   __syncthreads();
@@ -257,9 +262,13 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
         Hin[vl] = f4zero();
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += 32) {
-          Frag<MM> A = ldfrag<MM>(smem + L::C0T, L::P_C0, L::LDK, 16 * vl, k0, DK, lane);
           Frag<MM> B = ldfrag<MM>(smem + L::Q, L::P_Q, L::LDK, 16 * wid, k0, DK, lane);
-          mma<MM>(Hin[vl], A, B);
+          if constexpr (MM == kBF) {
+            mma_split(Hin[vl], ldfrag<kSP>(smem + L::C0T, L::P_C0, L::LDK, 16 * vl, k0, DK, lane), B);
+          } else {
+            Frag<MM> A = ldfrag<MM>(smem + L::C0T, L::P_C0, L::LDK, 16 * vl, k0, DK, lane);
+            mma<MM>(Hin[vl], A, B);
+          }
         }
       }
     }
@@ -281,6 +290,12 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
           wv[e] = (s <= t) ? gP[i][e] * __expf(sA[s] - mut) : 0.f;
         }
         st4<MM>(smem + L::W, L::P_W, t * L::LDC + s0, wv);
+        // the normaliser's sums in fp32, before W is rounded to the operand
+        // precision (they can cancel)
+        float rs = (wv[0] + wv[1]) + (wv[2] + wv[3]);
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        if (g == 0) sWP[sb * CM + t] = rs;
       }
     }
     __syncthreads();
@@ -302,7 +317,12 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) Hx[vl][e] = winter * Hin[vl][e] + acc[e];
       }
-      if (g == 0) sN[t] = Hx[NVL][0];  // row 0 of the normaliser tile
+      if (g == 0) {
+        // q_t . n0 (row 0 of the normaliser tile) plus the fp32 sums of W
+        float ws = 0.f;
+        for (int J = 0; J <= tb; ++J) ws += sWP[J * CM + t];
+        sN[t] = winter * Hin[NVL][0] + ws;
+      }
     }
     __syncthreads();
     if (wid < NB) {
@@ -345,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void mlstm_chunk_kernel(
       const int tile = wid + 4 * i;
       if (tile < NST) {
         const int jt = tile / NVA, vl = tile % NVA;
-        st4<MM>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
+        st4<SM>(smem + L::C0T, L::P_C0, (16 * vl + c16) * L::LDK + 16 * jt + 4 * g, Sacc[i]);
       }
     }
   }
@@ -401,7 +421,9 @@ static int mlstm_dk(const MlstmArgs& a) {
     case 64: return launch_mlstm<Tin, 64, VT, 64>(a);
     case 128: return launch_mlstm<Tin, 128, VT, 64>(a);
     case 256:
-      if constexpr (!SPLIT) return launch_mlstm<Tin, 256, VT, 64>(a);
+      // 16-column tiles: the state copy's two bf16 planes of 32 columns and
+      // the staged chunk do not fit the LDS together at d_k = 256
+      if constexpr (!SPLIT) return launch_mlstm<Tin, 256, 16, 64>(a);
       break;
   }
   return GDR_ERR_UNSUPPORTED;

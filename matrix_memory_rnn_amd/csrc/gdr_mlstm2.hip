@@ -25,19 +25,35 @@ namespace {
 constexpr int align16m(int x) { return (x + 15) / 16 * 16; }
 
 // Workspace record of one (b, h, chunk); es = element size of the input dtype.
+// Row-major form: H [t][v], V^T [v][s], K~^T [j][s]. Fragment form (fm; bf16,
+// d_k and C multiples of 32): the same matrices cut into the 16-row operand
+// tiles of the 16x16x32 MFMA, each tile 1 KiB of consecutive bytes in lane
+// order (lane 16g + c of tile (R, S) holds row 16R + c, k = 32S + 8g .. +7),
+// H in 16x16 accumulator tiles (512 B, lane 16g + c holds t = 16I + c,
+// v = 16V + 4g .. +3), plus q in the operand tiles.
 struct MRec {
-  int hi, vt, kt, ni, f, a, bytes;
+  int hi, vt, kt, qf, ni, f, a, bytes;
 };
-__host__ __device__ __forceinline__ MRec mrec_layout(int dk, int dv, int C, int es) {
+__host__ __device__ __forceinline__ MRec mrec_layout(int dk, int dv, int C, int es, bool fm = false) {
   MRec r;
-  r.hi = 0;                     // H     [t][v]  C x dv (input precision)
-  r.vt = r.hi + C * dv * es;    // V^T   [v][s]  dv x C
-  r.kt = r.vt + dv * C * es;    // K~^T  [j][s]  dk x C
-  r.ni = r.kt + dk * C * es;    // N     [t] fp32
+  r.hi = 0;                     // H     C x dv (input precision)
+  r.vt = r.hi + C * dv * es;    // V^T   dv x C
+  r.kt = r.vt + dv * C * es;    // K~^T  dk x C
+  r.qf = r.kt + dk * C * es;    // q     C x dk (fragment form only)
+  r.ni = r.qf + (fm ? C * dk * es : 0);   // N [t] fp32
   r.f = r.ni + C * 4;           // F     [t] fp32
   r.a = r.f + C * 4;            // A     [t] fp32
   r.bytes = align16m(r.a + C * 4);
   return r;
+}
+
+// Whether the two-kernel mLSTM path of these shapes uses the fragment-form
+// record and the register scan (which addresses a head's records with 32-bit
+// offsets).
+__host__ __forceinline__ bool mlstm_fm(int dtype, int dk, int dv, int C, long long T) {
+  if (dtype != GDR_BF16 || dk % 32 != 0 || C % 32 != 0 || dv % 16 != 0) return false;
+  const long long nchunks = (T + C - 1) / C;
+  return nchunks * mrec_layout(dk, dv, C, 2, true).bytes < (1LL << 31);
 }
 
 __device__ __forceinline__ float log_sigmoid2(float x) {
@@ -99,11 +115,12 @@ struct MIntraSmem {
   static constexpr int VS = KS + NS * CM * LDK * 2;  // V^T [v][s], 8-row slots swizzled per 16 columns
   static constexpr int WS = VS + NS * DVM * LDC * 2; // W   [t][s]
   static constexpr int SC = align16m(WS + NS * CM * LDC * 2);  // fp32 F, a, A
-  static constexpr int TOTAL = SC + 3 * CM * 4;
+  static constexpr int WP = SC + 3 * CM * 4;         // fp32 row sums of W per s-block [J][t]
+  static constexpr int TOTAL = WP + (CM / 16) * CM * 4;
   static_assert(TOTAL <= 160 * 1024, "mLSTM intra kernel LDS exceeds 160 KiB");
 };
 
-template <typename Tin, int DK, int CM>
+template <typename Tin, int DK, int CM, bool FM>
 __global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ i_tilde, const float* __restrict__ f_tilde, char* __restrict__ ws,
@@ -126,12 +143,14 @@ __global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const MRec RL = mrec_layout(DK, DV, CM, ES);
+  const MRec RL = mrec_layout(DK, DV, CM, ES, FM);
+  static_assert(!FM || (!F32 && DK % 32 == 0 && CM % 32 == 0), "fragment-form record shape");
   const int VP = DV * ES / 16;                       // pieces per v row
   const int NVT = DV / 16 + 1;                       // value tiles + the normaliser tile
   float* sF = (float*)(smem + L::SC);
   float* sa = sF + CM;
   float* sAm = sa + CM;
+  float* sWP = (float*)(smem + L::WP);
   auto voff = [](int col, int t) { return col * L::LDC + 8 * ((t >> 3) ^ ((col >> 4) & XM)) + (t & 7); };
 
   int item = blockIdx.x;
@@ -260,57 +279,93 @@ __global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
           w[e] = s <= t ? acc[e] * __expf(sa[s] - At) : 0.f;
         }
         st4<MM>(smem + L::WS, 0, t * L::LDC + s0, w);
+        // the normaliser's sums are taken in fp32 before W is rounded to the
+        // operand precision: they can cancel, and a rounded W would leave an
+        // error of the order of the terms in a small sum
+        float rs = (w[0] + w[1]) + (w[2] + w[3]);
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        if (g == 0) sWP[J * CM + t] = rs;
       }
     }
     __syncthreads();
 
-    // ---- H^T = [V^T; 1] W^T: tile (value tile vt, t-block I); the last value
-    // tile is the normaliser (row 0 all ones), whose row 0 gives N
+    // ---- H^T = V^T W^T: tile (value tile vt, t-block I); the last "tile"
+    // is the normaliser N[t] = sum_s W[t][s] from the fp32 block sums
     const int nht = NVT * NB;
     for (int qi = wid; qi < nht; qi += NW) {
       const int vt = qi / NB, I = qi % NB, kend = 16 * (I + 1);
       const bool nt = vt == NVT - 1;
+      if (nt) {
+        if (g == 0) {
+          const int t = 16 * I + c16;
+          float N = 0.f;
+          for (int J = 0; J <= I; ++J) N += sWP[J * CM + t];
+          ((float*)(rec + RL.ni))[t] = N;
+        }
+        continue;
+      }
       f32x4 acc = f4zero();
 #pragma unroll
       for (int k0 = 0; k0 < CM; k0 += 32) {
         if (k0 < kend) {
           const int kk = k0 + 8 * g;
-          Frag<MM> A;
-          if (nt) {
-            A = ones_row0<MM>(c16);
-          } else {
-            A = ldfrag<MM>(smem + L::VS, 0, L::LDC, 16 * vt, 8 * ((kk >> 3) ^ (vt & XM)) - 8 * g,
-                           CM, lane);
-          }
+          Frag<MM> A = ldfrag<MM>(smem + L::VS, 0, L::LDC, 16 * vt, 8 * ((kk >> 3) ^ (vt & XM)) - 8 * g,
+                                  CM, lane);
           Frag<MM> B = ldfrag<MM>(smem + L::WS, 0, L::LDC, 16 * I, k0, kend, lane);
           if (kk >= kend) A = ones_row0<MM>(-1);   // zero slice (B is zero there too)
           mma<MM>(acc, A, B);
         }
       }
       const int t = 16 * I + c16;
-      if (!nt) {
-        MOut<Tin>::quad((Tin*)(rec + RL.hi) + t * DV + 16 * vt + 4 * g, acc);
-      } else if (g == 0) {
-        ((float*)(rec + RL.ni))[t] = acc[0];
-      }
+      if constexpr (FM) MOut<Tin>::quad((Tin*)(rec + RL.hi) + ((I * (DV / 16) + vt) * 64 + lane) * 4, acc);
+      else MOut<Tin>::quad((Tin*)(rec + RL.hi) + t * DV + 16 * vt + 4 * g, acc);
     }
 
-    // ---- K~^T = (e^{a_s - A_C} k_s)^T and V^T to the record (16-byte pieces)
+    // ---- K~^T = (e^{a_s - A_C} k_s)^T and V^T to the record (16-byte pieces;
+    // in the fragment form piece p is lane p % 64 of tile p / 64, so the
+    // stores are consecutive)
     const float AC = sAm[CM - 1];
     constexpr int SP = CM / 8;
+    constexpr int KSC = CM / 32;
     for (int p = tid; p < DK * SP; p += kMThreads) {
-      const int j = p / SP, s0 = (p % SP) * 8;
+      int j, s0;
+      if constexpr (FM) {
+        const int f = p >> 6, l = p & 63;
+        j = 16 * (f / KSC) + (l & 15);
+        s0 = 32 * (f % KSC) + 8 * (l >> 4);
+      } else {
+        j = p / SP;
+        s0 = (p % SP) * 8;
+      }
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = ld1<MM>(smem + L::KS, 0, (s0 + e) * L::LDK + j) * __expf(sa[s0 + e] - AC);
-      MOut<Tin>::oct((Tin*)(rec + RL.kt) + j * CM + s0, x);
+      MOut<Tin>::oct((Tin*)(rec + RL.kt) + (FM ? 8 * p : j * CM + s0), x);
     }
     for (int p = tid; p < DV * SP; p += kMThreads) {
-      const int col = p / SP, s0 = (p % SP) * 8;
+      int col, s0;
+      if constexpr (FM) {
+        const int f = p >> 6, l = p & 63;
+        col = 16 * (f / KSC) + (l & 15);
+        s0 = 32 * (f % KSC) + 8 * (l >> 4);
+      } else {
+        col = p / SP;
+        s0 = (p % SP) * 8;
+      }
       const char* src = smem + L::VS + (size_t)voff(col, s0) * ES;
-      char* dst = rec + RL.vt + (col * CM + s0) * ES;
+      char* dst = rec + RL.vt + (FM ? 16 * p : (col * CM + s0) * ES);
       *(P16*)dst = *(const P16*)src;
       if constexpr (F32) *(P16*)(dst + 16) = *(const P16*)(src + 16);
+    }
+    if constexpr (FM) {
+      // q (rows past T are zero in LDS) in the operand tiles of the readout
+      constexpr int KSQ = DK / 32;
+      for (int p = tid; p < CM * DK / 8; p += kMThreads) {
+        const int f = p >> 6, l = p & 63;
+        const int r = 16 * (f / KSQ) + (l & 15), c = 4 * (f % KSQ) + (l >> 4);
+        *(P16*)(rec + RL.qf + 16 * p) = *(const P16*)(smem + L::QS + r * L::LDK * 2 + 16 * c);
+      }
     }
     __syncthreads();
   }
@@ -334,7 +389,7 @@ struct MScanSmem {
   static constexpr int NVA = VT / 16 + 1;            // value tiles + the normaliser tile
   static constexpr int LDK = DK + 8;
   static constexpr int S0T = STAGE;                  // [C | n]^T [v][j]
-  static constexpr int TOTAL = S0T + NS * 16 * NVA * LDK * 2;
+  static constexpr int TOTAL = S0T + 2 * 16 * NVA * LDK * 2;   // fp32, or bf16 hi + lo planes
   static_assert(TOTAL <= 160 * 1024, "mLSTM scan LDS exceeds 160 KiB");
   // 16-byte pieces of one chunk: q rows (from the input), then the record parts
   static constexpr int NQP = CM * WQ / 16;
@@ -350,6 +405,9 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
   using L = MScanSmem<Tin, DK, VT, CM>;
   constexpr bool F32 = L::F32;
   constexpr int MM = F32 ? kF32 : kBF;
+  // the state copy that q reads: fp32, or bf16 hi + lo planes (the readout's
+  // sums can cancel, so a single bf16 rounding of the state is not enough)
+  constexpr int SM = F32 ? kF32 : kSP;
   constexpr int NW = kMScanThreads / 64;
   constexpr int NVL = VT / 16, NVA = L::NVA;
   constexpr int NB = CM / 16;
@@ -479,7 +537,7 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
           else Sacc[i][e] = c16 == 0 ? n0[(size_t)bh * DK + j] : 0.f;
         }
       }
-      st4<MM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+      st4<SM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
     }
   }
 
@@ -504,8 +562,12 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
         if (!kv) B = ones_row0<MM>(-1);
 #pragma unroll
         for (int vl = 0; vl < NVA; ++vl) {
-          Frag<MM> A = ldfrag<MM>(S0T, P_S, LDK, 16 * vl, 32 * s, DK, lane);
-          mma<MM>(acc[vl], A, B);
+          if constexpr (F32) {
+            Frag<MM> A = ldfrag<MM>(S0T, P_S, LDK, 16 * vl, 32 * s, DK, lane);
+            mma<MM>(acc[vl], A, B);
+          } else {
+            mma_split(acc[vl], ldfrag<kSP>(S0T, P_S, LDK, 16 * vl, 32 * s, DK, lane), B);
+          }
         }
       }
       // acc[vl][e] = (q_t C0)[v = 16vl + 4g + e] for t = 16I + c16; the
@@ -581,7 +643,7 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
 #pragma unroll
       for (int i = 0; i < MAXU; ++i) {
         const int jt = uid + NU * (i / NVA), vl = i % NVA;
-        if (jt < NJB) st4<MM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
+        if (jt < NJB) st4<SM>(S0T, P_S, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[i]);
       }
     }
   };
@@ -623,11 +685,282 @@ __global__ __launch_bounds__(kMScanThreads, 2) void mlstm_scan_kernel(
   if (C_out && tid == 0 && vt0 == 0) m_out[bh] = mprev;
 }
 
+// ============================================================================ register scan
+// Fragment-form records (bf16, d_k and C multiples of 32). The roles and the
+// arithmetic are those of the scan above, but no record byte passes through
+// LDS: every operand tile is 1 KiB (H: 512 B) of consecutive bytes in lane
+// order, loaded straight into registers with full cache lines. Each wave
+// keeps three register sets and refills one as soon as its chunk is done
+// with it, so loads run two chunks ahead. Only
+// the copy [C | n]^T of the state that q reads goes through LDS, as bf16 hi +
+// lo planes (about 16 mantissa bits: the readout's sums can cancel) and
+// double buffered: the update waves write the next chunk's copy while the
+// readout waves read this chunk's, and one barrier per chunk separates the
+// two.
+constexpr int kMScanRgSets = 3;
+
+__device__ __forceinline__ void rg_phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int N> struct RgI { static constexpr int value = N; };
+
+template <int DK, int VT, int CM>
+__global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
+    const char* __restrict__ ws, const float* __restrict__ C0,
+    const float* __restrict__ n0, const float* __restrict__ m0, __bf16* __restrict__ h, float* C_out,
+    float* n_out, float* m_out, int T, int DV) {
+  constexpr int NS = kMScanRgSets;
+  constexpr int NW = kMScanThreads / 64;
+  constexpr int NB = CM / 16, NU = NW - NB;            // readout waves, update waves
+  constexpr int NVL = VT / 16, NVA = NVL + 1;           // value tiles + the normaliser tile
+  constexpr int KS = DK / 32, KSC = CM / 32;
+  constexpr int NJB = DK / 16, JPW = (NJB + NU - 1) / NU;
+  constexpr int LDK = DK + 8;                           // row pitch: 16-byte fragment reads conflict free
+  constexpr int PL = 16 * NVA * LDK;                    // elements of one plane of the state copy
+  static_assert(DK % 32 == 0 && CM % 32 == 0 && NB < NW && NS == 3, "register mLSTM scan shape");
+  typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  // [C | n]^T [v][j]: copy b (chunk parity) plane p (hi, lo) at (2b + p) PL
+  extern __shared__ __attribute__((aligned(16))) __bf16 S0T[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nvt = DV / VT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, vt0 = (lin % nvt) * VT;
+  const int nchunks = (T + CM - 1) / CM;
+  const MRec RL = mrec_layout(DK, DV, CM, 2, true);
+  // the records of this head through one buffer resource: the wave-uniform
+  // part of every offset is the scalar offset; past the last chunk the loads
+  // repeat it
+  const char* wsh = ws + (size_t)bh * nchunks * RL.bytes;
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wsh), 0, nchunks * RL.bytes, 0x00020000);
+  auto cbase = [&](int ch) { return (ch < nchunks ? ch : nchunks - 1) * RL.bytes; };
+  auto ld16 = [&](int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, soff, 0));
+  };
+  auto ld4 = [&](int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, voff, soff, 0));
+  };
+  const int l16 = 16 * lane;
+  float mprev = C0 != nullptr ? m0[bh] : -INFINITY;
+
+  // hand-unrolled walk over the register sets with a single exit, so the
+  // compiler's wait counts stay exact; leftover chunks after it
+  auto walk = [&](auto&& step) {
+    int ch = 0;
+    for (; ch + 3 <= nchunks; ch += 3) {
+      step(ch, RgI<0>{});
+      step(ch + 1, RgI<1>{});
+      step(ch + 2, RgI<2>{});
+    }
+    if (ch < nchunks) step(ch, RgI<0>{});
+    if (ch + 1 < nchunks) step(ch + 1, RgI<1>{});
+  };
+
+  if (wid < NB) {
+    // ================= readout: t-block I, every value tile and the normaliser
+    const int I = wid;
+    struct Set {
+      u32x4 q[KS];
+      u2 hv[NVL];
+      float sA, sN, sF, aC, fC;
+    };
+    Set R[NS];
+    // h rows t0 + 16 I + c16 from chunk ch: rows past T are not written (the
+    // row offset is in the lane offset, which the bounds check covers)
+    const int lh = (c16 * DV + 4 * g) * 2;
+    auto load = [&](int ch, Set& X) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) X.q[s] = ld16(l16, cb + RL.qf + (I * KS + s) * 1024);
+#pragma unroll
+      for (int vl = 0; vl < NVL; ++vl)
+        X.hv[vl] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              wr, 8 * lane, cb + RL.hi + (I * (DV / 16) + vt0 / 16 + vl) * 512, 0));
+      X.sA = ld4(4 * c16, cb + RL.a + 64 * I);
+      X.sN = ld4(4 * c16, cb + RL.ni + 64 * I);
+      X.sF = ld4(4 * c16, cb + RL.f + 64 * I);
+      X.aC = ld4(0, cb + RL.a + 4 * (CM - 1));
+      X.fC = ld4(0, cb + RL.f + 4 * (CM - 1));
+    };
+    __syncthreads();                                    // first state copy written
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      load(u, R[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      const __bf16* SB = S0T + 2 * (ch & 1) * PL;
+      f32x4 acc[NVA];
+#pragma unroll
+      for (int vl = 0; vl < NVA; ++vl) acc[vl] = f4zero();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 B = __builtin_bit_cast(bf16x8, R[u].q[s]);
+#pragma unroll
+        for (int vl = 0; vl < NVA; ++vl) {
+          const int o = (16 * vl + c16) * LDK + 32 * s + 8 * g;
+          acc[vl] = mfma_bf16(*(const bf16x8*)(SB + o), B, acc[vl]);
+          acc[vl] = mfma_bf16(*(const bf16x8*)(SB + PL + o), B, acc[vl]);
+        }
+      }
+      // acc[vl][e] = (q_t C0)[v = 16vl + 4g + e] for t = 16I + c16; the
+      // normaliser tile's row 0 (lanes g = 0, e = 0) is q_t . n0
+      const float At = R[u].sA;
+      const float mu = fmaxf(mprev, At);
+      const float si = __expf(At - mu);
+      const float se = mprev == -INFINITY ? 0.f : __expf(mprev - mu);
+      const float nq = __shfl(acc[NVL][0], c16, 64);
+      const float nbar = se * nq + si * R[u].sN;
+      const float inv = 1.f / fmaxf(fabsf(nbar), __expf(-(R[u].sF + mu)));
+      const int t0 = ch * CM;
+      const __amdgpu_buffer_rsrc_t hr =
+          __builtin_amdgcn_make_buffer_rsrc(h + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
+#pragma unroll
+      for (int vl = 0; vl < NVL; ++vl) {
+        const f32x4 hv = Raw<__bf16>::un4(R[u].hv[vl]);
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)((se * acc[vl][e] + si * hv[e]) * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, o), hr, lh + (16 * I * DV + vt0 + 16 * vl) * 2,
+                                              0, 0);
+      }
+      mprev = R[u].fC + fmaxf(mprev, R[u].aC);
+      load(ch + NS, R[u]);
+      rg_phase_barrier();
+    });
+  } else {
+    // ================= state update: j-blocks uid, uid + NU, .. of every value tile
+    const int uid = wid - NB;
+    struct Set {
+      u32x4 k[JPW][KSC], v[NVL][KSC];
+      float aC, fC;
+    };
+    Set U[NS];
+    auto load = [&](int ch, Set& X) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = uid + NU * jj;
+        if (jt < NJB) {
+#pragma unroll
+          for (int s = 0; s < KSC; ++s) X.k[jj][s] = ld16(l16, cb + RL.kt + (jt * KSC + s) * 1024);
+        }
+      }
+#pragma unroll
+      for (int vl = 0; vl < NVL; ++vl)
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) X.v[vl][s] = ld16(l16, cb + RL.vt + ((vt0 / 16 + vl) * KSC + s) * 1024);
+      X.aC = ld4(0, cb + RL.a + 4 * (CM - 1));
+      X.fC = ld4(0, cb + RL.f + 4 * (CM - 1));
+    };
+    f32x4 Sacc[JPW][NVA];
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int jt = uid + NU * jj;
+#pragma unroll
+      for (int vl = 0; vl < NVA; ++vl) {
+        Sacc[jj][vl] = f4zero();
+        if (jt < NJB) {
+          if (C0 != nullptr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = 16 * jt + 4 * g + e;
+              if (vl < NVL) Sacc[jj][vl][e] = C0[(size_t)bh * DK * DV + (size_t)j * DV + vt0 + 16 * vl + c16];
+              else Sacc[jj][vl][e] = c16 == 0 ? n0[(size_t)bh * DK + j] : 0.f;
+            }
+          }
+          st4<kSP>((char*)S0T, PL * 2, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[jj][vl]);
+        }
+      }
+    }
+    __syncthreads();                                    // first state copy written
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      load(u, U[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      // [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1]
+      const float AC = U[u].aC;
+      const float muC = fmaxf(mprev, AC);
+      const float dI = __expf(AC - muC);
+      const float dC = mprev == -INFINITY ? 0.f : __expf(mprev - muC);
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+        for (int vl = 0; vl < NVA; ++vl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] *= dC;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        bf16x8 Bv[NVA];
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl) {
+          const bf16x8 x = __builtin_bit_cast(bf16x8, U[u].v[vl][s]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) Bv[vl][e] = (__bf16)((float)x[e] * dI);
+        }
+        const __bf16 one = (__bf16)(c16 == 0 ? dI : 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Bv[NVL][e] = one;
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          if (uid + NU * jj < NJB) {
+            const bf16x8 A = __builtin_bit_cast(bf16x8, U[u].k[jj][s]);
+#pragma unroll
+            for (int vl = 0; vl < NVA; ++vl) Sacc[jj][vl] = mfma_bf16(A, Bv[vl], Sacc[jj][vl]);
+          }
+        }
+      }
+      __bf16* SN = S0T + 2 * ((ch + 1) & 1) * PL;
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = uid + NU * jj;
+        if (jt < NJB) {
+#pragma unroll
+          for (int vl = 0; vl < NVA; ++vl)
+            st4<kSP>((char*)SN, PL * 2, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[jj][vl]);
+        }
+      }
+      mprev = U[u].fC + fmaxf(mprev, AC);
+      load(ch + NS, U[u]);
+      rg_phase_barrier();
+    });
+    if (C_out) {
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = uid + NU * jj;
+        if (jt < NJB) {
+#pragma unroll
+          for (int vl = 0; vl < NVA; ++vl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = 16 * jt + 4 * g + e;
+              if (vl < NVL) C_out[(size_t)bh * DK * DV + (size_t)j * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
+              else if (c16 == 0 && vt0 == 0) n_out[(size_t)bh * DK + j] = Sacc[jj][vl][e];
+            }
+        }
+      }
+      if (uid == 0 && lane == 0 && vt0 == 0) m_out[bh] = mprev;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host launch
 size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
   const int es = dtype == GDR_BF16 ? 2 : 4;
   const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
-  return (size_t)B * H * nchunks * (size_t)mrec_layout(dk, dv, chunk, es).bytes;
+  return (size_t)B * H * nchunks * (size_t)mrec_layout(dk, dv, chunk, es, mlstm_fm(dtype, dk, dv, chunk, T)).bytes;
 }
 
 static int mdevice_cus() {
@@ -642,10 +975,10 @@ static int mdevice_cus() {
   return cus[dev];
 }
 
-template <typename Tin, int DK, int CM>
+template <typename Tin, int DK, int CM, bool FM>
 static int launch_mintra(const MlstmArgs& a, char* ws) {
   using L = MIntraSmem<Tin, DK, CM>;
-  auto kern = mlstm_intra_kernel<Tin, DK, CM>;
+  auto kern = mlstm_intra_kernel<Tin, DK, CM, FM>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
@@ -688,12 +1021,42 @@ static int launch_mscan(const MlstmArgs& a, const char* ws) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
+template <int DK, int VT, int CM>
+static int launch_mscan_rg(const MlstmArgs& a, const char* ws) {
+  auto kern = mlstm_scan_rg_kernel<DK, VT, CM>;
+  constexpr int lds = 4 * 16 * (VT / 16 + 1) * (DK + 8) * 2;   // two copies x two planes
+  static_assert(lds <= 160 * 1024, "register mLSTM scan LDS exceeds 160 KiB");
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+    attr_set = true;
+  }
+  const int nblocks = a.B * a.H * (a.dv / VT);
+  const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
+  __bf16* h = (__bf16*)a.h;
+  float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
+  int T = a.T, DV = a.dv;
+  void* args[] = {&ws, &C0, &n0, &m0, &h, &Co, &no, &mo, &T, &DV};
+  hipError_t e = hipLaunchKernel((const void*)kern, dim3(nblocks), dim3(kMScanThreads), args, lds,
+                                 (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
 template <typename Tin, int DK, int CM>
 static int mlstm_pair(const MlstmArgs& a, char* ws) {
-  const int st = launch_mintra<Tin, DK, CM>(a, ws);
-  if (st != GDR_OK) return st;
   // value tiles of 32 columns when that still gives a workgroup per CU, else 16
   const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= mdevice_cus();
+  if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
+    if (mlstm_fm(a.dtype, DK, a.dv, CM, a.T)) {
+      const int st = launch_mintra<Tin, DK, CM, true>(a, ws);
+      if (st != GDR_OK) return st;
+      if (!wide) return launch_mscan_rg<DK, 16, CM>(a, ws);
+      return launch_mscan_rg<DK, 32, CM>(a, ws);
+    }
+  }
+  const int st = launch_mintra<Tin, DK, CM, false>(a, ws);
+  if (st != GDR_OK) return st;
   if (!wide) return launch_mscan<Tin, DK, 16, CM>(a, ws);
   return launch_mscan<Tin, DK, 32, CM>(a, ws);
 }

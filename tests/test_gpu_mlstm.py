@@ -57,6 +57,14 @@ def test_mlstm_dk256_bf16(path):
     _check(d, 64, "bf16 dk=dv=256", path=path)
 
 
+@pytest.mark.parametrize("dtype,chunk,B,dv", [("bf16", 32, 4, 256), ("bf16", 64, 4, 256), ("f32", 32, 8, 128)])
+def test_mlstm_wide_batch(dtype, chunk, B, dv):
+    """Enough (b, h) pairs that the workspace scan takes 32-column value tiles
+    (B*H*d_v/32 = 256 workgroups)."""
+    d = mlstm_inputs(B, 8, 2 * chunk + 5, 32, dv, seed=chunk + 7, dtype=dtype)
+    _check(d, chunk, f"{dtype} wide batch B={B} H=8 dk=32 dv={dv} C={chunk}", path="ws")
+
+
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T", [1, 7, 64, 65])
 def test_mlstm_short_sequences(path, T):
@@ -65,14 +73,15 @@ def test_mlstm_short_sequences(path, T):
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_mlstm_with_initial_state_and_large_gates(path):
-    d = mlstm_inputs(2, 2, 100, 64, 64, seed=4, dtype="f32")
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("bf16", 32), ("bf16", 64)])
+def test_mlstm_with_initial_state_and_large_gates(path, dtype, chunk):
+    d = mlstm_inputs(2, 2, 100, 64, 64, seed=4, dtype=dtype)
     d["i_tilde"][:, :, 30] = 60.0          # one very strong write
     rng = np.random.default_rng(4)
     C0 = rng.standard_normal((2, 2, 64, 64)).astype(np.float32).astype(np.float64)
     n0 = np.abs(rng.standard_normal((2, 2, 64))).astype(np.float32).astype(np.float64)
     m0 = np.array([[0.5, -1.0], [2.0, 0.0]])
-    _check(d, 32, "f32 with initial state, i_tilde = 60", state=(C0, n0, m0), path=path)
+    _check(d, chunk, f"{dtype} C={chunk} with initial state, i_tilde = 60", state=(C0, n0, m0), path=path)
 
 
 @pytest.mark.parametrize("path", PATHS)
