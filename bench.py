@@ -47,12 +47,26 @@ def chunk_bytes(B, H, T, dk, dv, es, s0=False, s_out=True):
     return b
 
 
-def kernel_source_hash():
+# The sources each measured kernel is compiled from (its file and the headers
+# that file includes): a committed counter reading of that kernel stays valid
+# until one of them changes.
+KERNEL_SOURCES = {
+    "chunk": ("gdr_chunk2.hip", "gdr_chunk_common.hpp", "gdr_device.hpp", "gdr_internal.h"),
+    "chunk_fused": ("gdr_chunk.hip", "gdr_chunk_common.hpp", "gdr_device.hpp", "gdr_internal.h"),
+    "decode": ("gdr_decode.hip", "gdr_device.hpp", "gdr_internal.h"),
+    "mlstm": ("gdr_mlstm2.hip", "gdr_device.hpp", "gdr_internal.h"),
+    "mlstm_fused": ("gdr_mlstm.hip", "gdr_device.hpp", "gdr_internal.h"),
+}
+COUNTER_KEYS = {"chunk_intra_4k": "chunk", "chunk_scan_4k": "chunk", "chunk_fwd_4k": "chunk_fused",
+                "decode_256x16": "decode", "mlstm_intra_8k": "mlstm", "mlstm_scan_8k": "mlstm",
+                "mlstm_fused_8k": "mlstm_fused"}
+
+
+def kernel_source_hash(group):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "matrix_memory_rnn_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[group]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -65,7 +79,7 @@ def load_traffic(name, launches_key):
     with open(p) as f:
         data = json.load(f)
     e = data.get(launches_key)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(COUNTER_KEYS[launches_key]):
         return None
     return e.get("hbm_bytes_per_launch")
 

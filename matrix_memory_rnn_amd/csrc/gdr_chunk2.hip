@@ -1854,9 +1854,11 @@ static int launch_pair(const ChunkArgs& a, char* ws, int phases) {
   // for the 32x32x16 scan when its (b, h, 32 value columns) workgroups fill
   // the GPU; with fewer heads the staged scan's 16-column tiles keep more CUs
   // busy. The decision depends only on the shapes and the device, so the
-  // intra and scan phases (also as separate calls) take the same one.
+  // intra and scan phases (also as separate calls) take the same one. The
+  // F-order scan addresses a head's records with 32-bit offsets.
   if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
-    if (a.dv % 32 == 0 && (long long)a.B * a.H * (a.dv / 32) >= device_cus()) {
+    const long long head_bytes = (long long)((a.T + CM - 1) / CM) * rec_layout(DK, a.dv, CM, 2).bytes;
+    if (a.dv % 32 == 0 && (long long)a.B * a.H * (a.dv / 32) >= device_cus() && head_bytes < (1LL << 31)) {
       if (phases & 1) {
         const int st = launch_intra<Tin, DK, CM, true>(a, ws);
         if (st != GDR_OK) return st;

@@ -233,6 +233,19 @@ def test_wide_batch_fragment_order_path(dk, dv, chunk):
     _check(d, chunk, f"bf16 wide B={B} H={H} dk={dk} dv={dv} C={chunk} T={T}", path="ws")
 
 
+@pytest.mark.parametrize("dk,dv,chunk", [(64, 64, 16), (16, 64, 32)])
+def test_wide_batch_staged_path(dk, dv, chunk):
+    """Wide batches whose d_k or C is not a multiple of 32 take the staged scan
+    with 32-column value tiles (the path also taken when a head's records pass
+    2 GiB)."""
+    heads = -(-256 // (dv // 32))
+    B, H = 2, heads // 2
+    T = 2 * chunk + 9
+    d = gdn2_inputs(B, H, T, dk, dv, alpha_mu=3.5, alpha_sigma=1.2, seed=11 + dk + chunk,
+                    dtype="bf16", s0_std=0.2)
+    _check(d, chunk, f"bf16 wide staged B={B} H={H} dk={dk} dv={dv} C={chunk} T={T}", path="ws")
+
+
 @pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (64, 64, 32)])
 def test_wide_batch_tiny_decay_exact_path(dk, dv, chunk):
     """The fragment-order path with blocks whose decay leaves the in-block
