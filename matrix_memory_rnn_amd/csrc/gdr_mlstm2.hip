@@ -884,12 +884,18 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
     __syncthreads();                                    // first state copy written
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
+    for (int u = 0; u < NS - 1; ++u) {
       load(u, U[u]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The set the previous chunk used is refilled (for chunk ch + NS - 1) at
+    // the start of each chunk, its loads interleaved with the products below:
+    // issued in one burst, they wait for the load queue at the end of the
+    // chunk, on the way to the barrier.
+    constexpr int NLU = JPW * KSC + NVL * KSC + 2;
     walk([&](int ch, auto Uc) {
       constexpr int u = decltype(Uc)::value;
+      load(ch + NS - 1, U[(u + NS - 1) % NS]);
       // [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1]
       const float AC = U[u].aC;
       const float muC = fmaxf(mprev, AC);
@@ -922,6 +928,11 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
           }
         }
       }
+#pragma unroll
+      for (int i = 0; i < NLU; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      }
       __bf16* SN = S0T + 2 * ((ch + 1) & 1) * PL;
 #pragma unroll
       for (int jj = 0; jj < JPW; ++jj) {
@@ -933,7 +944,6 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
         }
       }
       mprev = U[u].fC + fmaxf(mprev, AC);
-      load(ch + NS, U[u]);
       rg_phase_barrier();
     });
     if (C_out) {
