@@ -130,6 +130,26 @@ def test_linear_in_initial_state(path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("B,H", [(2, 4), (2, 64)])
+def test_value_column_permutation(path, B, H):
+    """Each value column of O and S_T depends only on the same column of v,
+    w and S0 (eq.(1) of the Muir page acts on S from the left): permuting the
+    value columns of the inputs permutes the outputs' columns. Across value
+    tiles and workgroups the arithmetic of a column is the same, so the match
+    is exact. (B, H) = (2, 64) takes the fragment-order scan."""
+    import torch
+    d = gdn2_inputs(B, H, 150, 128, 128, alpha_mu=4.0, alpha_sigma=1.5, seed=41, dtype="bf16", s0_std=0.1)
+    perm = np.random.default_rng(3).permutation(128)
+    o1, s1 = _run(d, 64, path=path)
+    dp = dict(d)
+    dp["v"], dp["w"], dp["S0"] = d["v"][..., perm], d["w"][..., perm], d["S0"][..., perm]
+    o2, s2 = _run(dp, 64, path=path)
+    torch.cuda.synchronize()
+    p = torch.as_tensor(perm, device=o1.device)
+    assert torch.equal(o2, o1.index_select(-1, p)) and torch.equal(s2, s1.index_select(-1, p))
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_alpha_exactly_one_and_zero_erase(path):
     d = gdn2_inputs(1, 2, 100, 64, 64, alpha_mu=30.0, alpha_sigma=0.1, seed=9, dtype="bf16", s0_std=0.1)
     assert np.all(d["alpha"] == 1.0)
