@@ -91,25 +91,23 @@ def to_dev(x, dtype):
 
 
 def time_launches(fn, steps, warmup):
-    """Run fn warmup times, then `steps` times between events; returns
-    (ms per step over the region, mean ms per launch from per-launch events)."""
+    """Run fn warmup times, then `steps` times with one event between
+    consecutive launches (launch i runs from event i to event i + 1, so the
+    region is exactly the sum of the launches); returns (ms per step over the
+    region, mean ms per launch)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bnd = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    t0.record()
-    for a, b in evs:
-        a.record()
+    bnd[0].record()
+    for i in range(steps):
         fn()
-        b.record()
-    t1.record()
+        bnd[i + 1].record()
     torch.cuda.synchronize()
-    region = t0.elapsed_time(t1) / steps
-    per = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return region, per
+    per = [bnd[i].elapsed_time(bnd[i + 1]) for i in range(steps)]
+    return bnd[0].elapsed_time(bnd[-1]) / steps, float(np.mean(per))
 
 
 def chunk_inputs():
@@ -124,7 +122,8 @@ def chunk_inputs():
 
 def bench_chunk(steps, warmup, c, x):
     """One step = gdr_chunk_intra then gdr_chunk_scan (= gdr_chunk_fwd_ws) on
-    the 4K workload, with events around each kernel inside the timed region."""
+    the 4K workload, with an event at every kernel boundary inside the timed
+    region."""
     import torch
     import matrix_memory_rnn_amd as gdr
     B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
@@ -140,20 +139,21 @@ def bench_chunk(steps, warmup, c, x):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for e in ev:
-        e[0].record()
+    # one event at each step boundary and one between the two kernels: the
+    # intra kernel of step i runs from bnd[i] to mid[i], its scan from mid[i]
+    # to bnd[i + 1], and the region is exactly the sum of the kernels
+    bnd = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    bnd[0].record()
+    for i in range(steps):
         gdr.gdr_chunk_intra(*x, chunk=C, workspace=ws)
-        e[1].record()
+        mid[i].record()
         gdr.gdr_chunk_scan(ws, None, o, S, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C)
-        e[2].record()
-    t1.record()
+        bnd[i + 1].record()
     torch.cuda.synchronize()
-    region = t0.elapsed_time(t1) / steps
-    intra_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    region = bnd[0].elapsed_time(bnd[-1]) / steps
+    intra_ms = float(np.mean([bnd[i].elapsed_time(mid[i]) for i in range(steps)]))
+    scan_ms = float(np.mean([mid[i].elapsed_time(bnd[i + 1]) for i in range(steps)]))
     n = B * H * T
     intra_bytes = n * (4 * dk + 2 * dv) * 2 + nws          # inputs read, workspace written
     scan_bytes = nws + n * dv * 2 + B * H * dk * dv * 4       # workspace read, o and S_T written
@@ -253,8 +253,8 @@ def cpu_baseline(d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-side", action="store_true", help="skip the decode and mLSTM side measurements")
     ap.add_argument("--calib-copy", action="store_true",
