@@ -846,13 +846,15 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
     Set U[NS];
     auto load = [&](int ch, Set& X) {
       const int cb = cbase(ch);
+      // every wave issues the same loads on every path (a wave with fewer
+      // j-blocks repeats its last one and never uses it): with a branch here
+      // the compiler could not count the loads in flight and would wait for
+      // all of them at the next use
 #pragma unroll
       for (int jj = 0; jj < JPW; ++jj) {
-        const int jt = uid + NU * jj;
-        if (jt < NJB) {
+        const int jt = uid + NU * jj < NJB ? uid + NU * jj : NJB - 1;
 #pragma unroll
-          for (int s = 0; s < KSC; ++s) X.k[jj][s] = ld16(l16, cb + RL.kt + (jt * KSC + s) * 1024);
-        }
+        for (int s = 0; s < KSC; ++s) X.k[jj][s] = ld16(l16, cb + RL.kt + (jt * KSC + s) * 1024);
       }
 #pragma unroll
       for (int vl = 0; vl < NVL; ++vl)
