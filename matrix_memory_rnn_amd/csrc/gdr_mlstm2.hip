@@ -252,7 +252,10 @@ __global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
     }
     __syncthreads();
     if constexpr (!F32) {
-      if (item + (int)gridDim.x < nitems) issue(item + gridDim.x);
+      // always issued (item 0 after the last, an L2-resident re-read), so
+      // the loads in flight do not depend on a branch and the compiler's
+      // wait counts stay exact
+      issue(item + (int)gridDim.x < nitems ? item + (int)gridDim.x : 0);
     }
 
     // ---- W[t][s] = (q_t . k_s) e^{a_s - A_t}, s <= t (transposed score tiles)
