@@ -1851,14 +1851,16 @@ static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
 template <typename Tin, int DK, int CM>
 static int launch_pair(const ChunkArgs& a, char* ws, int phases) {
   // bf16 records with d_k, d_v and C multiples of 32 are written in F order
-  // for the 32x32x16 scan when its (b, h, 32 value columns) workgroups fill
-  // the GPU; with fewer heads the staged scan's 16-column tiles keep more CUs
-  // busy. The decision depends only on the shapes and the device, so the
-  // intra and scan phases (also as separate calls) take the same one. The
-  // F-order scan addresses a head's records with 32-bit offsets.
+  // for the 32x32x16 scan. Every workgroup walks all chunks of its head, so
+  // the time is the per-chunk time times the chunk count whether or not the
+  // workgroups fill the GPU, and the F-order scan's chunk is the shorter one
+  // also with few heads (the staged scan's 16-column tiles only add
+  // workgroups). The decision depends only on the shapes, so the intra and
+  // scan phases (also as separate calls) take the same one. The F-order scan
+  // addresses a head's records with 32-bit offsets.
   if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
     const long long head_bytes = (long long)((a.T + CM - 1) / CM) * rec_layout(DK, a.dv, CM, 2).bytes;
-    if (a.dv % 32 == 0 && (long long)a.B * a.H * (a.dv / 32) >= device_cus() && head_bytes < (1LL << 31)) {
+    if (a.dv % 32 == 0 && head_bytes < (1LL << 31)) {
       if (phases & 1) {
         const int st = launch_intra<Tin, DK, CM, true>(a, ws);
         if (st != GDR_OK) return st;

@@ -239,9 +239,10 @@ def test_phase_entry_points_equal_one_call(dtype):
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-# With bfloat16 inputs, d_k, d_v and C multiples of 32, and enough heads that
-# the (b, h, 32 value columns) workgroups fill the GPU (B*H*d_v/32 >= 256 CUs),
-# the record is written in the fragment-major order read by the 32x32x16 scan.
+# With bfloat16 inputs and d_k, d_v and C multiples of 32 the record is written
+# in the fragment-major order read by the 32x32x16 scan (also for the narrow
+# batches of the other tests); these shapes fill the GPU with its
+# (b, h, 32 value columns) workgroups (B*H*d_v/32 >= 256).
 @pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (64, 64, 32), (32, 32, 64), (128, 64, 64),
                                          (64, 128, 32)])
 def test_wide_batch_fragment_order_path(dk, dv, chunk):
