@@ -202,8 +202,12 @@ int gdr_mlstm_fwd(const void* q, const void* k, const void* v,
  *      [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1],
  *      m <- F_C + mu_C (the stabiliser of §13.4; every exponent <= 0).
  * Record per (b, h, chunk): (2*C*dv + dk*C) elements of the input dtype and
- * 3*C float32, rounded up to 16 bytes. Workspace rules as for
- * gdr_chunk_fwd_ws. With float32 inputs d_v must be at most 128 here.
+ * 3*C float32, rounded up to 16 bytes; with bfloat16 inputs, d_k and C
+ * multiples of 32 and a head's records under 2 GiB, the record also holds
+ * a copy of the chunk's q (C*dk elements) and its matrices are stored in
+ * MFMA tile order. gdr_mlstm_workspace_size reports the size for the given
+ * shapes. Workspace rules as for gdr_chunk_fwd_ws. With float32 inputs d_v
+ * must be at most 128 here.
  */
 int gdr_mlstm_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
                              int dtype, size_t* bytes);
