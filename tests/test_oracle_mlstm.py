@@ -128,6 +128,18 @@ def test_readout_invariant_to_stabilizer_choice(seed):
         assert np.linalg.norm(h - h_ref) / np.linalg.norm(h_ref) < 1e-13
 
 
+@pytest.mark.parametrize("seed", range(2))
+def test_returned_stabilizer_matches_closed_form(seed):
+    """The stabiliser the recurrence carries (and returns) is the running max
+    of §13.4, here against its independent prefix-max closed form (the readout
+    alone does not fix it: any stabiliser gives the same h while the floor is
+    inactive)."""
+    d = mlstm_inputs(2, 2, 30, 4, 3, seed=seed, dtype="f32")
+    _, _, _, m = oracle.mlstm_stabilized(d["q"], d["k"], d["v"], d["i_tilde"], d["f_tilde"])
+    mc = oracle.stabilizer_closed_form(d["i_tilde"], d["f_tilde"])
+    np.testing.assert_allclose(m, mc[..., -1], rtol=0, atol=1e-12)
+
+
 def test_nonempty_initial_state_continues_sequence():
     d = mlstm_inputs(2, 2, 20, 4, 3, seed=9, dtype="f32")
     a = [d[x] for x in ("q", "k", "v", "i_tilde", "f_tilde")]
@@ -137,3 +149,68 @@ def test_nonempty_initial_state_continues_sequence():
     np.testing.assert_allclose(np.concatenate([h1, h2], axis=2), h, rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(C2, C, rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(m2, m, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- mutations are caught
+
+def _stabilized_variant(mistake):
+    """The stabilised recurrence restated with one planted mistake (test code:
+    each variant must make at least one pin above fail)."""
+    def run(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None):
+        q, k, v, i_tilde, f_tilde = (np.asarray(x, dtype=np.float64) for x in (q, k, v, i_tilde, f_tilde))
+        B, H, T, dk = q.shape
+        C = np.zeros((B, H, dk, v.shape[-1])) if C0 is None else np.array(C0, dtype=np.float64)
+        n = np.zeros((B, H, dk)) if n0 is None else np.array(n0, dtype=np.float64)
+        m = np.full((B, H), -np.inf) if m0 is None else np.array(m0, dtype=np.float64)
+        logf = oracle.log_sigmoid(f_tilde)
+        h = np.zeros(v.shape)
+        for t in range(T):
+            lf = 0.0 if mistake == "stabiliser_without_forget" else logf[:, :, t]
+            m_new = np.maximum(lf + m, i_tilde[:, :, t])
+            with np.errstate(invalid="ignore", over="ignore"):
+                fp = np.exp(logf[:, :, t] + m - m_new)
+            fp = np.where(np.isneginf(m), 0.0, fp)
+            ip = np.exp(i_tilde[:, :, t] - m_new)
+            if mistake == "forget_gate_on_write":
+                ip = ip * np.exp(logf[:, :, t])
+            C_prev = C
+            C = fp[..., None, None] * C + ip[..., None, None] * k[:, :, t, :, None] * v[:, :, t, None, :]
+            n = fp[..., None] * n + (1.0 if mistake == "unscaled_normaliser_write" else ip[..., None]) * k[:, :, t]
+            m = m_new
+            Cr = C_prev if mistake == "readout_before_write" else C
+            num = np.einsum("bhi,bhij->bhj", q[:, :, t], Cr)
+            qn = np.sum(q[:, :, t] * n, axis=-1)
+            floor = 1.0 if mistake == "unscaled_floor" else np.exp(-m)
+            den = np.maximum(qn if mistake == "no_abs_in_normaliser" else np.abs(qn), floor)
+            h[:, :, t] = num / den[..., None]
+        return h, C, n, m
+    return run
+
+
+MISTAKES = ["stabiliser_without_forget", "forget_gate_on_write", "unscaled_normaliser_write",
+            "readout_before_write", "unscaled_floor", "no_abs_in_normaliser"]
+
+
+def _run_pins():
+    test_hand_worked_two_steps()
+    for it in (0.0, 100.0, 800.0):
+        test_single_pair_recovery(it)
+    for seed in range(3):
+        test_stabilized_equals_naive_in_safe_regime(seed)
+    test_overflow_cliff()
+    for seed in range(2):
+        test_returned_stabilizer_matches_closed_form(seed)
+    test_nonempty_initial_state_continues_sequence()
+
+
+def test_restated_recurrence_passes_the_pins(monkeypatch):
+    """Control: the restatement without a mistake passes every pin."""
+    monkeypatch.setattr(oracle, "mlstm_stabilized", _stabilized_variant(None))
+    _run_pins()
+
+
+@pytest.mark.parametrize("mistake", MISTAKES)
+def test_pins_reject_planted_mistakes(monkeypatch, mistake):
+    monkeypatch.setattr(oracle, "mlstm_stabilized", _stabilized_variant(mistake))
+    with pytest.raises(AssertionError):
+        _run_pins()
