@@ -117,3 +117,28 @@ def test_mlstm_ws_agrees_with_fused_and_chains_state():
     assert rel_err(h_cat, host(h_all)) < 1e-5 and rel_err(host(C2), host(C_all)) < 1e-5
     assert np.max(np.abs(host(m2) - host(m_all))) < 1e-4
     assert rel_err(host(h_all), host(hf)) < 1e-5 and rel_err(host(C_all), host(Cf)) < 1e-5
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("B,H,dv", [(1, 2, 64), (4, 8, 256)])
+def test_mlstm_state_in_place(path, B, H, dv):
+    """C_out may be C0 (each workgroup reads and writes only its own value
+    columns); n_out and m_out are separate. The in-place call equals the one
+    with separate outputs bit for bit. (4, 8, 256) takes 32-column tiles."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    d = mlstm_inputs(B, H, 100, 32, dv, seed=12, dtype="bf16")
+    q, k, v = (dev(d[n], "bf16") for n in ("q", "k", "v"))
+    it, ft = dev(d["i_tilde"]), dev(d["f_tilde"])
+    rng = np.random.default_rng(12)
+    C0 = dev(rng.standard_normal((B, H, 32, dv)))
+    n0 = dev(np.abs(rng.standard_normal((B, H, 32))))
+    m0 = dev(rng.uniform(-1, 2, (B, H)))
+    fn = gdr.gdr_mlstm_fwd if path == "fused" else gdr.gdr_mlstm_fwd_ws
+    h1, C1, n1, m1 = fn(q, k, v, it, ft, C0, n0, m0, chunk=64)
+    Cin = C0.clone()
+    n_out, m_out = torch.empty_like(n0), torch.empty_like(m0)
+    h2, C2, n2, m2 = fn(q, k, v, it, ft, Cin, n0, m0, chunk=64, C_out=Cin, n_out=n_out, m_out=m_out)
+    torch.cuda.synchronize()
+    assert C2.data_ptr() == Cin.data_ptr()
+    assert torch.equal(h1, h2) and torch.equal(C1, Cin) and torch.equal(n1, n_out) and torch.equal(m1, m_out)
