@@ -142,3 +142,28 @@ def test_mlstm_state_in_place(path, B, H, dv):
     torch.cuda.synchronize()
     assert C2.data_ptr() == Cin.data_ptr()
     assert torch.equal(h1, h2) and torch.equal(C1, Cin) and torch.equal(n1, n_out) and torch.equal(m1, m_out)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mlstm_value_column_permutation(path):
+    """Each value column of h and C depends only on the same column of v and
+    C0 (the normaliser and stabiliser are shared by all columns): permuting
+    the value columns of the inputs permutes the outputs' columns, exactly."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv = 1, 2, 150, 64, 64
+    d = mlstm_inputs(B, H, T, dk, dv, seed=14, dtype="bf16")
+    rng = np.random.default_rng(14)
+    C0 = rng.standard_normal((B, H, dk, dv))
+    n0 = np.abs(rng.standard_normal((B, H, dk)))
+    m0 = rng.uniform(-1, 2, (B, H))
+    perm = rng.permutation(dv)
+    fn = gdr.gdr_mlstm_fwd if path == "fused" else gdr.gdr_mlstm_fwd_ws
+    args = lambda vv, cc: (dev(d["q"], "bf16"), dev(d["k"], "bf16"), dev(vv, "bf16"), dev(d["i_tilde"]),
+                           dev(d["f_tilde"]), dev(cc), dev(n0), dev(m0))
+    h1, C1, n1, m1 = fn(*args(d["v"], C0), chunk=64)
+    h2, C2, n2, m2 = fn(*args(d["v"][..., perm], C0[..., perm]), chunk=64)
+    torch.cuda.synchronize()
+    p = torch.as_tensor(perm, device=h1.device)
+    assert torch.equal(h2, h1.index_select(-1, p)) and torch.equal(C2, C1.index_select(-1, p))
+    assert torch.equal(n2, n1) and torch.equal(m2, m1)
