@@ -167,3 +167,22 @@ def test_mlstm_value_column_permutation(path):
     p = torch.as_tensor(perm, device=h1.device)
     assert torch.equal(h2, h1.index_select(-1, p)) and torch.equal(C2, C1.index_select(-1, p))
     assert torch.equal(n2, n1) and torch.equal(m2, m1)
+
+
+@pytest.mark.parametrize("dv", [64, 256])
+def test_mlstm_bf16_split_at_chunk_boundary_chains_exactly(dv):
+    """Two calls split at a chunk boundary, the state handed over, give the
+    whole-sequence result bit for bit on the workspace path: the second call
+    starts from the same fp32 state the first call's scan carried."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    d = mlstm_inputs(1, 4, 300, 64, dv, seed=21, dtype="bf16")
+    t = lambda x, sl: dev(d[x][:, :, sl], "bf16")
+    g = lambda x, sl: dev(d[x][:, :, sl])
+    args = lambda sl: (t("q", sl), t("k", sl), t("v", sl), g("i_tilde", sl), g("f_tilde", sl))
+    h, C, n, m = gdr.gdr_mlstm_fwd_ws(*args(slice(None)), chunk=64)
+    h1, C1, n1, m1 = gdr.gdr_mlstm_fwd_ws(*args(slice(0, 128)), chunk=64)
+    h2, C2, n2, m2 = gdr.gdr_mlstm_fwd_ws(*args(slice(128, None)), C1, n1, m1, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([h1, h2], dim=2), h)
+    assert torch.equal(C2, C) and torch.equal(n2, n) and torch.equal(m2, m)
