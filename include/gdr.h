@@ -72,7 +72,10 @@ extern "C" {
  *   o               [B,H,T,dv]  output, input dtype
  *   S_out           [B,H,dk,dv] float32 final state, or NULL to skip; may
  *                   equal S0 (in-place update), must not otherwise overlap it
- *   chunk           chunk length C (16, 32 or 64)
+ *   chunk           chunk length C (16, 32 or 64; with float32 inputs and
+ *                   d_k >= 64 at most 32 here, as fp32 operands take twice
+ *                   the LDS: C = 64 then returns GDR_ERR_UNSUPPORTED, while
+ *                   gdr_chunk_fwd_ws takes it)
  *   dtype           GDR_F32 or GDR_BF16 (applies to q, k, v, alpha, b, w, o)
  *   stream          hipStream_t to enqueue on (NULL = default stream)
  * Returns GDR_OK or a negative GDR_ERR_* code.
