@@ -241,13 +241,45 @@ def _mutants():
         S2 = Sh - k[..., :, None] * read[..., None, :] + k[..., :, None] * v[..., None, :]
         return np.einsum("...i,...ij->...j", q, S2), S2
 
+    def decay_after_write(S, q, k, v, alpha, b, w):
+        read = np.einsum("...i,...ij->...j", b * k, S)
+        S2 = alpha[..., :, None] * (S - k[..., :, None] * read[..., None, :] + k[..., :, None] * (w * v)[..., None, :])
+        return np.einsum("...i,...ij->...j", q, S2), S2
+
+    def erase_reads_undecayed(S, q, k, v, alpha, b, w):
+        Sh = alpha[..., :, None] * S
+        read = np.einsum("...i,...ij->...j", b * k, S)
+        S2 = Sh - k[..., :, None] * read[..., None, :] + k[..., :, None] * (w * v)[..., None, :]
+        return np.einsum("...i,...ij->...j", q, S2), S2
+
+    def erase_gate_on_both_sides(S, q, k, v, alpha, b, w):
+        Sh = alpha[..., :, None] * S
+        read = np.einsum("...i,...ij->...j", b * k, Sh)
+        S2 = Sh - (b * k)[..., :, None] * read[..., None, :] + k[..., :, None] * (w * v)[..., None, :]
+        return np.einsum("...i,...ij->...j", q, S2), S2
+
     return [erase_before_decay, transposed_rank_one, readout_before_write, sign_flip_erase,
-            dropped_write_gate]
+            dropped_write_gate, decay_after_write, erase_reads_undecayed, erase_gate_on_both_sides]
 
 
 @pytest.mark.parametrize("mutant", _mutants(), ids=lambda f: f.__name__)
 def test_pins_reject_planted_mistakes(monkeypatch, mutant):
-    """Each planted oracle mistake must fail the hand-worked example."""
+    """Each planted oracle mistake must fail a pin: the hand-worked example,
+    or the exact rational brute force on random dyadic inputs (the hand
+    example's erase gate cannot tell (b*k)^T (b*k) from k^T (b*k))."""
     monkeypatch.setattr(G, "gdn2_step", mutant)
-    with pytest.raises(AssertionError):
+
+    def pins():
         test_hand_worked_two_steps()
+        for seed in range(3):
+            test_bruteforce_exact_dyadic(seed, 5, 3, 2)
+
+    with pytest.raises(AssertionError):
+        pins()
+
+
+def test_pins_pass_the_unmutated_step():
+    """Control for the planted-mistake test: the same pins pass as written."""
+    test_hand_worked_two_steps()
+    for seed in range(3):
+        test_bruteforce_exact_dyadic(seed, 5, 3, 2)
