@@ -8,7 +8,9 @@ Sources (cited by page title and section/equation):
 
 * "Muir: Linear Attention with Sensitivity-Allocated Gating and Matched-Filter
   Readout" — §2.1 eq.(1) (the GDN-2 state update and readout), §2.2 (effective
-  write, GLA form, chunkwise form).
+  write, GLA form, chunkwise form), §4.2 stage (i) and eq.(10) (the chunk
+  matrix T = I + L_strict and the chunkwise readout and state update, used to
+  measure how ill-conditioned the tests' chunk systems are).
 * "Exponential gates and matrix memory: xLSTM and RWKV-7" — §13.2 (spectrum of
   the diagonal-plus-rank-one transition, Prop. 13.1 and Exercise 13.4), §13.3
   (reduction to Gated DeltaNet), §13.4 and Exercise 13.6 (mLSTM cell, log-domain
@@ -31,6 +33,7 @@ from .gdn2 import (  # noqa: F401
     gdn2_recurrent, gdn2_step, gdn2_transition, gdn2_materialized,
     gdn2_effective_write, gdn2_decode, delta_rule_textbook, gated_deltanet,
     gla_closed_form, linear_attention_closed_form, bruteforce_exact,
+    gdn2_chunk_system, gdn2_chunkwise, chunk_condition_numbers,
 )
 from .mlstm import (  # noqa: F401
     mlstm_stabilized, mlstm_naive, mlstm_with_stabilizer, stabilizer_closed_form,

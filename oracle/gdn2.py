@@ -220,3 +220,74 @@ def bruteforce_exact(q, k, v, alpha, b, w, S0):
         outs.append(mm(qt, St)[0])
         S_last = St
     return outs, S_last
+
+
+def _pair_decay(alpha_chunk, t, s):
+    """pi_{t,s} = product of alpha_r over r = s+1..t inside one chunk (an empty
+    product is 1); alpha_chunk is [..., C, dk]."""
+    return np.prod(alpha_chunk[..., s + 1: t + 1, :], axis=-2)
+
+
+def gdn2_chunk_system(k, alpha, b, chunk):
+    """The unit lower-triangular chunk matrices T = I + L_strict of the Muir
+    page's §4.2 stage (i): (L_strict)_{t,s} = <b_t*k_t, pi_{t,s}*k_s> for t > s
+    inside each chunk, with pi_{t,s} the product of alpha over (s, t].
+
+    k, alpha, b: [B, H, T, dk]. Chunks are consecutive runs of ``chunk`` tokens;
+    a shorter last chunk gives a smaller matrix. Returns a list over chunks of
+    arrays [B, H, C_c, C_c].
+    """
+    k, alpha, b = map(_f64, (k, alpha, b))
+    Tn = k.shape[2]
+    out = []
+    for c0 in range(0, Tn, chunk):
+        kc, ac, bc = k[:, :, c0:c0 + chunk], alpha[:, :, c0:c0 + chunk], b[:, :, c0:c0 + chunk]
+        n = kc.shape[2]
+        Tm = np.zeros(kc.shape[:2] + (n, n))
+        for t in range(n):
+            Tm[:, :, t, t] = 1.0
+            for s in range(t):
+                Tm[:, :, t, s] = np.sum(bc[:, :, t] * kc[:, :, t] * _pair_decay(ac, t, s) * kc[:, :, s], axis=-1)
+        out.append(Tm)
+    return out
+
+
+def gdn2_chunkwise(q, k, v, alpha, b, w, S0=None, chunk=64):
+    """The chunkwise form of the Muir page (§2.2 and §4.2 eq.(10)), chunk by chunk:
+    T [U | Y] = [V_hat | K_hat_pi] (rows w_t*v_t and pi_t*b_t*k_t), then
+    O = (Q_pi - M Y) S0 + M U and S_C = (Diag(pi_C) - K_tilde^T Y) S0 + K_tilde^T U,
+    with M_{t,s} = <q_t, pi_{t,s}*k_s> (t >= s), (Q_pi)_t = pi_t*q_t and
+    K_tilde_s = pi_{C,s}*k_s. The triangular systems are solved with
+    numpy.linalg.solve. A shorter last chunk is handled as a chunk of its own
+    length. Returns (o [B,H,T,dv], S_T [B,H,dk,dv]).
+    """
+    q, k, v, alpha, b, w = map(_f64, (q, k, v, alpha, b, w))
+    B, H, Tn, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.zeros((B, H, Tn, dv))
+    systems = gdn2_chunk_system(k, alpha, b, chunk)
+    for ci, c0 in enumerate(range(0, Tn, chunk)):
+        sl = slice(c0, c0 + chunk)
+        qc, kc, vc, ac, bc, wc = (x[:, :, sl] for x in (q, k, v, alpha, b, w))
+        n = qc.shape[2]
+        pi = np.cumprod(ac, axis=2)                                  # pi_t, t = 1..n
+        M = np.zeros((B, H, n, n))
+        for t in range(n):
+            for s in range(t + 1):
+                M[:, :, t, s] = np.sum(qc[:, :, t] * _pair_decay(ac, t, s) * kc[:, :, s], axis=-1)
+        rhs = np.concatenate([wc * vc, pi * bc * kc], axis=-1)       # [V_hat | K_hat_pi]
+        Z = np.linalg.solve(systems[ci], rhs)
+        U, Y = Z[..., :dv], Z[..., dv:]
+        K_t = np.stack([_pair_decay(ac, n - 1, s) * kc[:, :, s] for s in range(n)], axis=2)
+        Q_pi = pi * qc
+        o[:, :, sl] = (Q_pi - M @ Y) @ S + M @ U
+        S = pi[:, :, -1, :, None] * S - np.swapaxes(K_t, -1, -2) @ Y @ S + np.swapaxes(K_t, -1, -2) @ U
+    return o, S
+
+
+def chunk_condition_numbers(k, alpha, b, chunk):
+    """2-norm condition number of every chunk matrix T (see gdn2_chunk_system),
+    as an array [B, H, N_chunks] (chunks shorter than 2 tokens give 1)."""
+    mats = gdn2_chunk_system(k, alpha, b, chunk)
+    return np.stack([np.linalg.cond(m) if m.shape[-1] > 1 else np.ones(m.shape[:2]) for m in mats], axis=-1)

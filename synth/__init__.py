@@ -30,6 +30,7 @@ import numpy as np
 __all__ = [
     "round_to",
     "gdn2_inputs",
+    "gdn2_inputs_correlated",
     "decode_inputs",
     "mlstm_inputs",
     "CONFIGS",
@@ -81,6 +82,43 @@ def gdn2_inputs(B, H, T, dk, dv, *, alpha_mu, alpha_sigma, seed=0, dtype="bf16",
     v = g.standard_normal((B, H, T, dv))
     alpha = _sigmoid(alpha_mu + alpha_sigma * g.standard_normal((B, H, T, dk)))
     b = _sigmoid(g.standard_normal((B, H, T, dk)))
+    w = _sigmoid(g.standard_normal((B, H, T, dv)))
+    S0 = None
+    if s0_std is not None:
+        S0 = round_to(s0_std * g.standard_normal((B, H, dk, dv)), "f32")
+    out = {name: round_to(x, dtype) for name, x in
+           (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("b", b), ("w", w))}
+    out["S0"] = S0
+    out["dtype"] = dtype
+    return out
+
+
+def gdn2_inputs_correlated(B, H, T, dk, dv, *, n_dirs=4, noise=0.3, b_mu=3.0, b_sigma=0.5,
+                           alpha_mu=4.0, alpha_sigma=1.5, seed=0, dtype="bf16", s0_std=None):
+    """Inputs whose chunk systems are ill-conditioned, as trained models' are.
+
+    Keys cluster around a few shared directions: per (b, h), ``n_dirs`` unit
+    directions are drawn, and key t is the unit vector along direction
+    ``idx_t`` (uniform) plus isotropic noise of norm about ``noise``. Erase
+    gates sit near the top of the pages' range (0, 2): b = 2*sigmoid(N(b_mu,
+    b_sigma)), about 1.9 by default. Repeated, strongly erased keys make the
+    unit lower-triangular chunk matrix far from the identity. q, v, alpha, w
+    and S0 are drawn as in :func:`gdn2_inputs`.
+
+    Draw order: q, directions, direction indices, key noise, v, alpha-logit,
+    b-logit, w-logit, S0, all from ``numpy.random.Generator(PCG64(seed))``.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = _unit_silu(g.standard_normal((B, H, T, dk)))
+    dirs = g.standard_normal((B, H, n_dirs, dk))
+    dirs /= np.linalg.norm(dirs, axis=-1, keepdims=True)
+    idx = g.integers(0, n_dirs, size=(B, H, T))
+    k = np.take_along_axis(dirs, idx[..., None], axis=2)
+    k = k + noise * g.standard_normal((B, H, T, dk)) / np.sqrt(dk)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal((B, H, T, dv))
+    alpha = _sigmoid(alpha_mu + alpha_sigma * g.standard_normal((B, H, T, dk)))
+    b = 2.0 * _sigmoid(b_mu + b_sigma * g.standard_normal((B, H, T, dk)))
     w = _sigmoid(g.standard_normal((B, H, T, dv)))
     S0 = None
     if s0_std is not None:

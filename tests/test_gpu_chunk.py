@@ -3,14 +3,16 @@ gdr_chunk_fwd (one fused kernel) and gdr_chunk_fwd_ws (intra-chunk kernel over
 all chunks, then the chunk scan, through a workspace).
 
 Tolerances (max over heads of the relative Frobenius error of O and S_T):
-1e-4 for float32 inputs, 2e-2 for bfloat16 inputs with float32 state.
+1e-4 for float32 inputs, 2e-2 for bfloat16 inputs with float32 state; every
+output row (token) is also bounded on its own, and float32 results element
+by element (``tests/gpu_util.py``).
 """
 import numpy as np
 import pytest
 
 import oracle
 from synth import CONFIGS, gdn2_inputs
-from tests.gpu_util import TOL, dev, host, rel_err, say
+from tests.gpu_util import TOL, check_outputs, dev, host, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -32,15 +34,11 @@ def _run(d, chunk, S0=None, S_out=None, path="ws"):
 
 def _check(d, chunk, label, tol=None, path="ws"):
     import torch
-    label = f"{path} {label}"
+    label = f"[chunk] {path} {label}"
     o, S = _run(d, chunk, path=path)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle.gdn2_recurrent(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], S0=d["S0"])
-    eo, es = rel_err(host(o), o_ref), rel_err(host(S), S_ref)
-    tol = TOL[d["dtype"]] if tol is None else tol
-    say(f"[chunk] {label}: err_o={eo:.3e} err_S={es:.3e} tol={tol:g}")
-    assert np.all(np.isfinite(host(o))) and np.all(np.isfinite(host(S)))
-    assert eo <= tol and es <= tol
+    eo, es, _ = check_outputs(host(o), o_ref, host(S), S_ref, d["dtype"], label, tol)
     return eo, es
 
 
@@ -173,6 +171,8 @@ def test_tiny_decay_takes_exact_in_block_path(path, dtype):
 
 
 def _head_parity(name, heads, path):
+    """Full-size workload through one entry point; the oracle follows the
+    listed (b, h) pairs (all of them at once, vectorised over heads)."""
     import torch
     c = CONFIGS[name]
     d = gdn2_inputs(c["B"], c["H"], c["T"], c["dk"], c["dv"], alpha_mu=c["alpha_mu"],
@@ -181,24 +181,24 @@ def _head_parity(name, heads, path):
     o, S = _run(d, c["chunk"], path=path)
     torch.cuda.synchronize()
     o, S = host(o), host(S)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
-    for (bi, hi) in heads:
-        sl = lambda x: x[bi:bi + 1, hi:hi + 1]
-        o_ref, S_ref = oracle.gdn2_recurrent(*(sl(d[x]) for x in ("q", "k", "v", "alpha", "b", "w")),
-                                             S0=None if d["S0"] is None else sl(d["S0"]))
-        eo, es = rel_err(sl(o), o_ref), rel_err(sl(S), S_ref)
-        say(f"[chunk] {path} {name} head (b={bi},h={hi}): err_o={eo:.3e} err_S={es:.3e}")
-        assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
+    bi = np.array([x[0] for x in heads])
+    hi = np.array([x[1] for x in heads])
+    sl = lambda x: x[bi, hi][None]
+    o_ref, S_ref = oracle.gdn2_recurrent(*(sl(d[x]) for x in ("q", "k", "v", "alpha", "b", "w")),
+                                         S0=None if d["S0"] is None else sl(d["S0"]))
+    say(f"[chunk] {name}: oracle done over {len(heads)} heads")
+    check_outputs(sl(o), o_ref, sl(S), S_ref, c["dtype"], f"[chunk] {path} {name} {len(heads)} heads")
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_full_size_chunk_4k_sampled_heads(path):
-    _head_parity("chunk_4k", [(0, 0), (3, 15), (2, 7)], path)
+def test_full_size_chunk_4k_all_heads(path):
+    c = CONFIGS["chunk_4k"]
+    _head_parity("chunk_4k", [(b, h) for b in range(c["B"]) for h in range(c["H"])], path)
 
 
 @pytest.mark.parametrize("path", PATHS)
 def test_full_size_chunk_32k_sampled_heads(path):
-    _head_parity("chunk_32k", [(0, 0), (0, 11)], path)
+    _head_parity("chunk_32k", [(0, 0), (0, 5), (0, 11), (0, 15)], path)
 
 
 def test_workspace_reuse_and_agreement_with_fused_kernel():

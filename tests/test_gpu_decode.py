@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from synth import CONFIGS, decode_inputs, gdn2_inputs
-from tests.gpu_util import TOL, dev, host, rel_err, say
+from tests.gpu_util import TOKEN_TOL, TOL, dev, host, rel_err, say, token_err
 
 pytestmark = pytest.mark.gpu
 
@@ -55,25 +55,27 @@ def test_decode_equals_chunk():
 
 
 def test_full_size_decode_sampled_heads():
-    """256 sequences x 16 heads, d = 128, three consecutive steps from S0 = 0;
-    the oracle follows a sample of the 4096 states."""
+    """256 sequences x 16 heads, d = 128: four consecutive steps from a nonzero
+    state (N(0, 0.05)); the oracle follows 256 of the 4096 states, spread over
+    every sequence group and head."""
     import torch
     c = CONFIGS["decode"]
     N, H, dk, dv = c["N"], c["H"], c["dk"], c["dv"]
-    S = torch.zeros((N, H, dk, dv), dtype=torch.float32, device="cuda")
-    sample = [(0, 0), (17, 5), (255, 15), (128, 8)]
-    S_ref = {nh: np.zeros((1, 1, dk, dv)) for nh in sample}
-    for st in range(3):
+    rng = np.random.default_rng(77)
+    S0 = (0.05 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    S = torch.from_numpy(S0).cuda()
+    flat = np.arange(0, N * H, 16) + np.arange(N * H // 16) % 16   # one state per 16, every head
+    ni, hi = flat // H, flat % H
+    S_ref = S0[ni, hi][None].astype(np.float64)
+    for st in range(4):
         d = decode_inputs(N, H, dk, dv, step=st, seed=0, dtype=c["dtype"])
         o = host(_step(S, d))
         torch.cuda.synchronize()
-        for (n, h) in sample:
-            sl = lambda x: x[n:n + 1, h:h + 1]
-            o_ref, S_ref[(n, h)] = oracle.gdn2_decode(S_ref[(n, h)], *(sl(d[x]) for x in
-                                                                        ("q", "k", "v", "alpha", "b", "w")))
-            assert rel_err(sl(o), o_ref) <= TOL["bf16"]
-    Sh = host(S)
-    for (n, h) in sample:
-        es = rel_err(Sh[n:n + 1, h:h + 1], S_ref[(n, h)])
-        say(f"[decode] full-size (n={n},h={h}): err_S={es:.3e}")
-        assert es <= TOL["bf16"]
+        sl = lambda x: x[ni, hi][None]
+        o_ref, S_ref = oracle.gdn2_decode(S_ref, *(sl(d[x]) for x in ("q", "k", "v", "alpha", "b", "w")))
+        eo, to = rel_err(sl(o), o_ref), token_err(sl(o)[:, :, None], o_ref[:, :, None])
+        say(f"[decode] full-size step {st}: err_o={eo:.3e} tok_o={to:.3e}")
+        assert eo <= TOL["bf16"] and to <= TOKEN_TOL["bf16"]
+    es = rel_err(host(S)[ni, hi][None], S_ref)
+    say(f"[decode] full-size 256 sampled states: err_S={es:.3e}")
+    assert es <= TOL["bf16"]

@@ -283,3 +283,49 @@ def test_pins_pass_the_unmutated_step():
     test_hand_worked_two_steps()
     for seed in range(3):
         test_bruteforce_exact_dyadic(seed, 5, 3, 2)
+
+
+# --------------------------------------------------------------------------- chunkwise form
+
+@pytest.mark.parametrize("chunk,T", [(4, 16), (8, 21), (16, 16), (5, 1)])
+def test_chunkwise_form_equals_recurrence(chunk, T):
+    """The Muir page's eq.(10) (T [U|Y] = [V_hat|K_hat_pi], O = (Q_pi - M Y) S0 + M U,
+    S_C = (Diag(pi_C) - K_tilde^T Y) S0 + K_tilde^T U) reproduces eq.(1) step by
+    step, including a ragged last chunk."""
+    d = _rand(40 + chunk, T=T, dk=6, dv=5, alpha_mu=1.5)
+    o1, S1 = oracle.gdn2_recurrent(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], S0=d["S0"])
+    o2, S2 = G.gdn2_chunkwise(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], S0=d["S0"], chunk=chunk)
+    assert _rel(o2, o1) < 1e-13 and _rel(S2, S1) < 1e-13
+
+
+def test_chunk_system_is_identity_without_erase():
+    """b = 0: no erase term, the chunk matrix is I and its condition number 1."""
+    d = _rand(50, T=12, dk=4, dv=3)
+    mats = G.gdn2_chunk_system(d["k"], d["alpha"], np.zeros_like(d["b"]), 8)
+    for m in mats:
+        assert np.array_equal(m, np.broadcast_to(np.eye(m.shape[-1]), m.shape))
+    kap = G.chunk_condition_numbers(d["k"], d["alpha"], np.zeros_like(d["b"]), 8)
+    assert np.allclose(kap, 1.0)
+
+
+def test_chunk_system_two_tokens_closed_form():
+    """Two tokens: T = [[1, 0], [<b_2*k_2, alpha_2*k_1>, 1]] (pi_{2,1} = alpha_2)."""
+    k = np.array([[[[0.6, 0.8], [1.0, 0.0]]]])
+    alpha = np.array([[[[0.5, 0.25], [0.5, 0.25]]]])
+    b = np.array([[[[1.0, 2.0], [1.5, 0.5]]]])
+    (m,) = G.gdn2_chunk_system(k, alpha, b, 2)
+    l21 = 1.5 * 1.0 * 0.5 * 0.6 + 0.5 * 0.0 * 0.25 * 0.8
+    assert np.allclose(m[0, 0], [[1.0, 0.0], [l21, 1.0]], rtol=0, atol=1e-15)
+
+
+def test_chunkwise_solve_catches_a_planted_transpose():
+    """Solving with T^T instead of T (a plausible slip) breaks the agreement."""
+    d = _rand(60, T=16, dk=5, dv=4, alpha_mu=1.5)
+    orig = G.gdn2_chunk_system
+    try:
+        G.gdn2_chunk_system = lambda *a: [np.swapaxes(m, -1, -2) for m in orig(*a)]
+        o2, _ = G.gdn2_chunkwise(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], S0=d["S0"], chunk=8)
+    finally:
+        G.gdn2_chunk_system = orig
+    o1, _ = oracle.gdn2_recurrent(d["q"], d["k"], d["v"], d["alpha"], d["b"], d["w"], S0=d["S0"])
+    assert _rel(o2, o1) > 1e-3
