@@ -22,6 +22,7 @@ Entry points (same names as the C ABI):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -108,6 +109,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _alloc_on(stream):
+    """Context in which this binding allocates outputs and workspaces: the
+    launch stream when one is given, so torch's caching allocator ties the
+    memory to the stream the kernels use (a block freed after the call is not
+    handed to another stream while those kernels may still run)."""
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -128,7 +138,7 @@ def _req(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state):
+def _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state, stream=None):
     import torch
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -138,11 +148,12 @@ def _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state):
         _req(t, name, (B, H, T, d), dt, dev)
     if S0 is not None:
         _req(S0, "S0", (B, H, dk, dv), torch.float32, dev)
-    if o is None:
-        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+        if S_out is None and return_state:
+            S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _req(o, "o", (B, H, T, dv), dt, dev)
-    if S_out is None and return_state:
-        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     if S_out is not None:
         _req(S_out, "S_out", (B, H, dk, dv), torch.float32, dev)
     return (B, H, T, dk, dv), o, S_out
@@ -158,7 +169,8 @@ def gdr_chunk_fwd(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=None
     S_T float32 (None if ``return_state`` is False). ``S_out`` may be S0 for
     an in-place state update.
     """
-    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state)
+    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state,
+                                                stream)
     lib = load_library()
     st = lib.gdr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
                            _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q),
@@ -187,9 +199,10 @@ def gdr_chunk_fwd_ws(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=N
     contiguous); if None, one is allocated for this call.
     """
     import torch
-    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state)
+    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, return_state,
+                                                stream)
     need = gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
-    workspace = _workspace(workspace, need, q.device)
+    workspace = _workspace(workspace, need, q.device, stream)
     nbytes = workspace.numel() * workspace.element_size()
     lib = load_library()
     st = lib.gdr_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
@@ -199,10 +212,11 @@ def gdr_chunk_fwd_ws(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=N
     return o, S_out
 
 
-def _workspace(workspace, need, device):
+def _workspace(workspace, need, device, stream=None):
     import torch
     if workspace is None:
-        return torch.empty(need, dtype=torch.uint8, device=device)
+        with _alloc_on(stream):
+            return torch.empty(need, dtype=torch.uint8, device=device)
     if not (isinstance(workspace, torch.Tensor) and workspace.device == device and workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     return workspace
@@ -216,7 +230,7 @@ def gdr_chunk_intra(q, k, v, alpha, b, w, *, chunk=64, workspace=None, stream=No
                        ("v", v, dv), ("w", w, dv)):
         _req(t, name, (B, H, T, d), q.dtype, q.device)
     need = gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
-    workspace = _workspace(workspace, need, q.device)
+    workspace = _workspace(workspace, need, q.device, stream)
     st = load_library().gdr_chunk_intra(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                         B, H, T, dk, dv, int(chunk), _dtype_code(q), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream))
@@ -252,7 +266,8 @@ def gdr_decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
         _req(t, name, (N, H, d), dt, dev)
     _req(S, "S", (N, H, dk, dv), torch.float32, dev)
     if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+        with _alloc_on(stream):
+            o = torch.empty((N, H, dv), dtype=dt, device=dev)
     _req(o, "o", (N, H, dv), dt, dev)
     lib = load_library()
     st = lib.gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S),
@@ -261,7 +276,8 @@ def gdr_decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
     return o
 
 
-def _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, return_state):
+def _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, return_state,
+                stream=None):
     import torch
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -277,13 +293,14 @@ def _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, r
         _req(C0, "C0", (B, H, dk, dv), torch.float32, dev)
         _req(n0, "n0", (B, H, dk), torch.float32, dev)
         _req(m0, "m0", (B, H), torch.float32, dev)
-    if h is None:
-        h = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    with _alloc_on(stream):
+        if h is None:
+            h = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+        if return_state and C_out is None:
+            C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+            n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+            m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
     _req(h, "h", (B, H, T, dv), dt, dev)
-    if return_state and C_out is None:
-        C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-        n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
-        m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
     return (B, H, T, dk, dv), h, C_out, n_out, m_out
 
 
@@ -294,7 +311,7 @@ def gdr_mlstm_fwd(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, chunk
     n0 ``[B,H,dk]``, m0 ``[B,H]``, float32; all or none). Returns
     ``(h, C_T, n_T, m_T)`` (state entries None if ``return_state`` is False)."""
     (B, H, T, dk, dv), h, C_out, n_out, m_out = _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h,
-                                                            C_out, n_out, m_out, return_state)
+                                                            C_out, n_out, m_out, return_state, stream)
     lib = load_library()
     st = lib.gdr_mlstm_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(i_tilde), _ptr(f_tilde), _ptr(C0),
                            _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
@@ -321,9 +338,9 @@ def gdr_mlstm_fwd_ws(q, k, v, i_tilde, f_tilde, C0=None, n0=None, m0=None, *, ch
     arguments and results as :func:`gdr_mlstm_fwd`; ``workspace`` as for
     :func:`gdr_chunk_fwd_ws`)."""
     (B, H, T, dk, dv), h, C_out, n_out, m_out = _mlstm_args(q, k, v, i_tilde, f_tilde, C0, n0, m0, h,
-                                                            C_out, n_out, m_out, return_state)
+                                                            C_out, n_out, m_out, return_state, stream)
     need = gdr_mlstm_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
-    workspace = _workspace(workspace, need, q.device)
+    workspace = _workspace(workspace, need, q.device, stream)
     lib = load_library()
     st = lib.gdr_mlstm_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(i_tilde), _ptr(f_tilde), _ptr(C0),
                               _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),

@@ -49,6 +49,7 @@
 // fp32 operands and fp32 MFMA (16x16x4) throughout.
 #include "gdr_chunk_common.hpp"
 #include "gdr_internal.h"
+#include "gdr_host.hpp"
 
 namespace gdr {
 
@@ -521,13 +522,7 @@ static int launch_chunk(const ChunkArgs& a) {
   constexpr bool SPLIT = std::is_same<Tin, float>::value;
   using L = ChunkSmem<DK, VT, CM, SPLIT>;
   auto kern = gdn2_chunk_kernel<Tin, DK, VT, CM, SPLIT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   const int nblocks = a.B * a.H * (a.dv / VT);
   const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
   const Tin *al = (const Tin*)a.alpha, *bg = (const Tin*)a.b, *wg = (const Tin*)a.w;

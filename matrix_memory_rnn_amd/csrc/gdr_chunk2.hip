@@ -24,6 +24,7 @@
 // the record once.
 #include "gdr_chunk_common.hpp"
 #include "gdr_internal.h"
+#include "gdr_host.hpp"
 
 namespace gdr {
 
@@ -1772,33 +1773,16 @@ size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype)
   return (size_t)B * H * nchunks * (size_t)rec_layout(dk, dv, chunk, es).bytes;
 }
 
-static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <typename Tin, int DK, int CM, bool FM>
 static int launch_intra(const ChunkArgs& a, char* ws) {
   using L = IntraSmem<Tin, DK, CM>;
   auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM, FM>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   int nchunks = (a.T + CM - 1) / CM;
   int nitems = a.B * a.H * nchunks;
   // one resident workgroup per CU, each walking items with a stride of the grid
-  const int grid = nitems < device_cus() ? nitems : device_cus();
+  const int cus = stream_cus(a.stream);
+  const int grid = nitems < cus ? nitems : cus;
   const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
   const Tin *al = (const Tin*)a.alpha, *bg = (const Tin*)a.b, *wg = (const Tin*)a.w;
   int T = a.T, DV = a.dv;
@@ -1816,12 +1800,7 @@ static int launch_scan(const ChunkArgs& a, const char* ws) {
     using L = StagedScan<DK, VT, CM>;
     kern = (const void*)gdn2_chunk_scan_staged_kernel<DK, VT, CM>;
     lds = L::TOTAL;
-    static bool attr_set = false;
-    if (!attr_set) {
-      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-        return GDR_ERR_LAUNCH;
-      attr_set = true;
-    }
+    if (!allow_lds(kern, lds)) return GDR_ERR_LAUNCH;
   } else {
     kern = (const void*)gdn2_chunk_scan_kernel<Tin, DK, VT, CM>;
   }
@@ -1875,7 +1854,7 @@ static int launch_pair(const ChunkArgs& a, char* ws, int phases) {
   }
   if (!(phases & 2)) return GDR_OK;
   // value tiles of 32 columns when that still gives a workgroup per CU, else 16
-  const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= device_cus();
+  const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= stream_cus(a.stream);
   if constexpr (std::is_same<Tin, float>::value) {
     return launch_scan<Tin, DK, 16, CM>(a, ws);
   } else {

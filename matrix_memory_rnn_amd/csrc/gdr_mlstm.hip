@@ -22,6 +22,7 @@
 // inputs keep fp32 operands in LDS and use fp32 MFMA (16x16x4).
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
+#include "gdr_host.hpp"
 
 namespace gdr {
 
@@ -393,13 +394,7 @@ static int launch_mlstm(const MlstmArgs& a) {
   constexpr bool SPLIT = std::is_same<Tin, float>::value;
   using L = MlstmSmem<DK, VT, CM, SPLIT>;
   auto kern = mlstm_chunk_kernel<Tin, DK, VT, CM, SPLIT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   const int nblocks = a.B * a.H * (a.dv / VT);
   const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
   const float *it = a.i_tilde, *ft = a.f_tilde, *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;

@@ -17,6 +17,7 @@
 // combination and the state update. All exponents are <= 0.
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
+#include "gdr_host.hpp"
 
 namespace gdr {
 
@@ -978,32 +979,15 @@ size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype)
   return (size_t)B * H * nchunks * (size_t)mrec_layout(dk, dv, chunk, es, mlstm_fm(dtype, dk, dv, chunk, T)).bytes;
 }
 
-static int mdevice_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <typename Tin, int DK, int CM, bool FM>
 static int launch_mintra(const MlstmArgs& a, char* ws) {
   using L = MIntraSmem<Tin, DK, CM>;
   auto kern = mlstm_intra_kernel<Tin, DK, CM, FM>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   int nchunks = (a.T + CM - 1) / CM;
   int nitems = a.B * a.H * nchunks;
-  const int grid = nitems < mdevice_cus() ? nitems : mdevice_cus();
+  const int cus = stream_cus(a.stream);
+  const int grid = nitems < cus ? nitems : cus;
   const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
   const float *it = a.i_tilde, *ft = a.f_tilde;
   int T = a.T, DV = a.dv;
@@ -1017,13 +1001,7 @@ template <typename Tin, int DK, int VT, int CM>
 static int launch_mscan(const MlstmArgs& a, const char* ws) {
   using L = MScanSmem<Tin, DK, VT, CM>;
   auto kern = mlstm_scan_kernel<Tin, DK, VT, CM>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   const int nblocks = a.B * a.H * (a.dv / VT);
   const Tin* q = (const Tin*)a.q;
   const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
@@ -1041,12 +1019,7 @@ static int launch_mscan_rg(const MlstmArgs& a, const char* ws) {
   auto kern = mlstm_scan_rg_kernel<DK, VT, CM>;
   constexpr int lds = 4 * 16 * (VT / 16 + 1) * (DK + 8) * 2;   // two copies x two planes
   static_assert(lds <= 160 * 1024, "register mLSTM scan LDS exceeds 160 KiB");
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-      return GDR_ERR_LAUNCH;
-    attr_set = true;
-  }
+  if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
   const int nblocks = a.B * a.H * (a.dv / VT);
   const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
   __bf16* h = (__bf16*)a.h;
@@ -1061,7 +1034,7 @@ static int launch_mscan_rg(const MlstmArgs& a, const char* ws) {
 template <typename Tin, int DK, int CM>
 static int mlstm_pair(const MlstmArgs& a, char* ws) {
   // value tiles of 32 columns when that still gives a workgroup per CU, else 16
-  const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= mdevice_cus();
+  const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= stream_cus(a.stream);
   if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
     if (mlstm_fm(a.dtype, DK, a.dv, CM, a.T)) {
       const int st = launch_mintra<Tin, DK, CM, true>(a, ws);
