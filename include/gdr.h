@@ -5,8 +5,10 @@
  * a HIP stream, validates its arguments on the host, enqueues its kernels on
  * that stream and returns without synchronising. No entry point allocates or
  * frees memory, and the library keeps no hidden state between calls: the
- * caller owns every buffer. Calls are reentrant; calls that write the same
- * buffers must be ordered by the caller (same stream or events).
+ * caller owns every buffer (the one exception is gdr_chunk_fwd_noalloc, whose
+ * records go through a static per-device scratch array, see there). Calls are
+ * reentrant; calls that write the same buffers must be ordered by the caller
+ * (same stream or events).
  *
  * Notation follows "Muir: Linear Attention with Sensitivity-Allocated Gating
  * and Matched-Filter Readout" (§2.1 eq.(1)): row vectors, state S[d_k, d_v]
@@ -47,6 +49,7 @@ extern "C" {
 #define GDR_ERR_LAUNCH      -6  /* the HIP runtime rejected a kernel launch */
 #define GDR_ERR_ALIAS       -7  /* an output buffer overlaps an input buffer */
 #define GDR_ERR_WORKSPACE   -8  /* workspace smaller than gdr_chunk_workspace_size reports */
+#define GDR_ERR_TOO_LARGE   -9  /* one head needs more than gdr_chunk_fwd_noalloc's static scratch */
 
 /* Input/output element types. States (S, C, n, m) are always float32. */
 #define GDR_F32  0
@@ -139,6 +142,38 @@ int gdr_chunk_scan(const void* workspace, size_t workspace_bytes,
                    const float* S0, void* o, float* S_out,
                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
                    void* stream);
+
+/*
+ * gdr_chunk_fwd_noalloc — gdr_chunk_fwd_ws without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, results and errors as gdr_chunk_fwd_ws minus
+ * the workspace; the results equal it up to rounding, and bit for bit for
+ * bfloat16 inputs with d_k, d_v and C multiples of 32 (the fragment-order
+ * record, whose kernels do the same arithmetic per head whatever the batch).
+ *
+ * The records go through a scratch array of GDR_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * compiled into the library: every GPU the library runs on holds its own copy
+ * from the first call on that device until the process ends. Heads are
+ * processed in groups of consecutive (b, h) pairs that fit the array
+ * (gdr_chunk_workspace_size(1, 1, T, ...) bytes per head; 4.75 MB at T = 4096,
+ * d = 128, C = 64, so 14 heads per group), intra kernel then scan per group,
+ * all on `stream`. If one head alone needs more than the array (T above about
+ * 57,800 tokens at d = 128, C = 64, bf16) it returns GDR_ERR_TOO_LARGE before
+ * enqueuing anything. The stream must belong to the calling thread's current
+ * device (else GDR_ERR_LAUNCH).
+ *
+ * Every call on a GPU shares that GPU's array: calls that may overlap on one
+ * GPU (different streams without ordering) race and give wrong results, so
+ * order them. Nothing in the array needs clearing between calls (each record
+ * is written whole before it is read).
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                          const void* alpha, const void* b, const void* w,
+                          const float* S0, void* o, float* S_out,
+                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                          void* stream);
 
 /*
  * gdr_decode_step — one recurrent step of "Muir: ...", §2.1 eq.(1) for N

@@ -26,7 +26,7 @@ import contextlib
 import ctypes
 import os
 
-__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_workspace_size", "gdr_chunk_intra",
+__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_fwd_noalloc", "gdr_chunk_workspace_size", "gdr_chunk_intra",
            "gdr_chunk_scan", "gdr_mlstm_fwd_ws", "gdr_mlstm_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
 
@@ -68,6 +68,8 @@ def load_library():
     lib.gdr_chunk_fwd_ws.restype = I
     lib.gdr_chunk_intra.argtypes = [P] * 6 + [I] * 7 + [P, ctypes.c_size_t, P]
     lib.gdr_chunk_intra.restype = I
+    lib.gdr_chunk_fwd_noalloc.argtypes = [P] * 9 + [I] * 7 + [P]
+    lib.gdr_chunk_fwd_noalloc.restype = I
     lib.gdr_chunk_scan.argtypes = [P, ctypes.c_size_t, P, P, P] + [I] * 7 + [P]
     lib.gdr_chunk_scan.restype = I
     lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
@@ -209,6 +211,21 @@ def gdr_chunk_fwd_ws(q, k, v, alpha, b, w, S0=None, *, chunk=64, o=None, S_out=N
                               _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q),
                               _ptr(workspace), nbytes, _stream(stream))
     _check("gdr_chunk_fwd_ws", st)
+    return o, S_out
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, alpha, b, w, S0=None, *, chunk=64, o, S_out=None, stream=None):
+    """:func:`gdr_chunk_fwd_ws` through the library's static scratch array: no
+    workspace and no allocation, by the binding or the library, so the caller
+    passes ``o`` (and ``S_out`` if wanted). Returns ``(o, S_out)``. Calls that
+    may overlap on one GPU share the array and must be ordered."""
+    if o is None:
+        raise ValueError("gdr_chunk_fwd_noalloc allocates nothing: pass o (and S_out)")
+    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, alpha, b, w, S0, o, S_out, False, stream)
+    st = load_library().gdr_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                              _ptr(S0), _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk),
+                                              _dtype_code(q), _stream(stream))
+    _check("gdr_chunk_fwd_noalloc", st)
     return o, S_out
 
 

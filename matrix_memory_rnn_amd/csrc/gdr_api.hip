@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdr_internal.h"
+#include "gdr_host.hpp"
 
 namespace {
 
@@ -110,6 +113,8 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case GDR_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case GDR_ERR_WORKSPACE: return "the workspace is smaller than gdr_chunk_workspace_size reports";
+    case GDR_ERR_TOO_LARGE:
+      return "one head needs more scratch than the library's static array holds (GDR_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -306,3 +311,67 @@ int gdr_mlstm_fwd_ws(const void* q, const void* k, const void* v, const float* i
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation entry point
+//
+// gdr_chunk_fwd_noalloc runs the two-kernel chunk forward through a scratch
+// array that lives in the library's code object instead of a caller
+// workspace. Each GPU the library runs on holds its own copy of the array
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory, so its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+
+namespace {
+
+constexpr size_t kScratchBytes = GDR_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// per-device device address of `scratch` (null until first looked up)
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's `scratch`; called with that device current.
+// Concurrent first calls look up the same address, so the race is benign.
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+extern "C" int gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                                     const void* b, const void* w, const float* S0, void* o, float* S_out,
+                                     int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                                     void* stream) {
+  int st = check_chunk(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  // heads are independent: they go through the scratch array in groups of
+  // consecutive (b, h) pairs, as many per group as the array holds
+  const size_t per_head = gdr::chunk_ws_bytes(1, 1, T, dk, dv, chunk, dtype);
+  if (per_head > kScratchBytes) return GDR_ERR_TOO_LARGE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_LAUNCH;
+  if (gdr::stream_device(stream) != dev) return GDR_ERR_LAUNCH;
+  char* ws = (char*)scratch_ptr(dev);
+  if (!ws) return GDR_ERR_LAUNCH;
+  const long long heads = (long long)B * H;
+  const long long group = (long long)(kScratchBytes / per_head);
+  const size_t es = esize(dtype);
+  for (long long h0 = 0; h0 < heads; h0 += group) {
+    const int g = (int)(heads - h0 < group ? heads - h0 : group);
+    const size_t oK = (size_t)h0 * T * dk * es, oV = (size_t)h0 * T * dv * es;
+    const size_t oS = (size_t)h0 * dk * dv;
+    gdr::ChunkArgs a{(const char*)q + oK, (const char*)k + oK, (const char*)v + oV,
+                     (const char*)alpha + oK, (const char*)b + oK, (const char*)w + oV,
+                     S0 ? S0 + oS : nullptr, (char*)o + oV, S_out ? S_out + oS : nullptr,
+                     1, g, T, dk, dv, chunk, dtype, stream};
+    st = gdr::chunk_fwd_ws_launch(a, ws, 3);
+    if (st != GDR_OK) return st;
+  }
+  return GDR_OK;
+}

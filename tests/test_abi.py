@@ -221,3 +221,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(m, "lib_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         m.load_library()
+
+
+def test_noalloc_rejects_a_head_larger_than_its_scratch(lib):
+    """gdr_chunk_fwd_noalloc checks the per-head record size against its static
+    scratch array on the host, before touching the GPU."""
+    c = _codes()
+    assert c["GDR_ERR_TOO_LARGE"] == -9
+    p = P[:7]
+    # one head of 100,000 tokens at d = 128, C = 64, bf16 needs 1563 records of
+    # 74,240 B (116 MB), more than the 64 MiB array
+    st = lib.gdr_chunk_fwd_noalloc(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], None,
+                                   1, 2, 100000, 128, 128, 64, 1, None)
+    assert st == c["GDR_ERR_TOO_LARGE"]
+    assert "scratch" in lib.gdr_status_string(st).decode()
+    # argument errors come first, as for the other entry points
+    st = lib.gdr_chunk_fwd_noalloc(None, p[1], p[2], p[3], p[4], p[5], None, p[6], None,
+                                   1, 2, 64, 16, 16, 16, 1, None)
+    assert st == c["GDR_ERR_NULL"]
