@@ -183,6 +183,30 @@ def bench_fused(steps, warmup, c, x, S0):
     return time_launches(fn, steps, warmup)
 
 
+def bench_muir(steps, warmup):
+    """The Muir gate prologue on the 4K workload's shape: gdr_muir_chunk_fwd_ws
+    reads q, k, v and the logits z_f, z_b, z_w, z_q (bf16) plus a_log and
+    gamma_stat, and forms the gates inside the intra-chunk kernel."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    from synth import CONFIGS, muir_inputs
+    c = CONFIGS["chunk_4k"]
+    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
+    d = muir_inputs(B, H, T, dk, dv, seed=0, dtype="bf16")
+    x = [to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v", "z_f", "z_b", "z_w")]
+    zq = to_dev(d["z_q"], torch.bfloat16)
+    al, gs = to_dev(d["a_log"], torch.float32), to_dev(d["gamma_stat"], torch.float32)
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdr.gdr_chunk_workspace_size(B, H, T, dk, dv, C, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: gdr.gdr_muir_chunk_fwd_ws(*x, al, zq, gs, chunk=C, o=o, S_out=S, workspace=ws)
+    region_ms, _ = time_launches(fn, steps, warmup)
+    n = B * H * T
+    nbytes = n * (5 * dk + 2 * dv) * 2 + n * dv * 2 + B * H * dk * dv * 4 + H * (dk + 1) * 4
+    return dict(B=B, T=T, region_ms=region_ms, bytes=nbytes)
+
+
 def bench_decode(N, steps=1024):
     """N sequences x 16 heads, d = 128, fp32 states resident in HBM: `steps`
     sequential one-token updates, each with its own inputs (all `steps` input
@@ -373,6 +397,13 @@ def main():
         out["fused"] = {"entry": "gdr_chunk_fwd (one kernel, no workspace), 4K workload", "ms_per_step": f_region,
                         "kernel_ms": f_launch, "tokens/s": tokens / (f_region * 1e-3), "GB/s": fb,
                         "frac_hbm": fb / PEAK_HBM_GBS}
+        mu = bench_muir(args.steps, args.warmup)
+        mg = mu["bytes"] / (mu["region_ms"] * 1e-3) / 1e9
+        out["muir_prologue"] = {"workload": "4K workload shape with gate logits: q, k, v, z_f, z_b, z_w, z_q bf16, "
+                                            "a_log [H], gamma_stat [H, dk]",
+                                "entry": "gdr_muir_chunk_fwd_ws", "ms_per_step": mu["region_ms"],
+                                "tokens/s": mu["B"] * mu["T"] / (mu["region_ms"] * 1e-3),
+                                "algorithmic_bytes": mu["bytes"], "GB/s": mg, "frac_hbm": mg / PEAK_HBM_GBS}
         c3, _, x3, S03 = chunk_inputs("chunk_32k")
         r3 = bench_chunk(max(10, args.steps // 4), max(5, args.warmup // 4), c3, x3, S03)
         g3 = r3["bytes"] / (r3["region_ms"] * 1e-3) / 1e9

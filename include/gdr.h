@@ -197,6 +197,44 @@ int gdr_decode_step(const void* q, const void* k, const void* v,
                     int N, int H, int dk, int dv, int dtype, void* stream);
 
 /*
+ * gdr_muir_chunk_fwd_ws, gdr_muir_decode_step — gdr_chunk_fwd_ws and
+ * gdr_decode_step with the gate activations of "Muir: Linear Attention with
+ * Sensitivity-Allocated Gating and Matched-Filter Readout" folded into the
+ * kernels' load stage: the caller passes pre-activation logits instead of the
+ * gates, and the gates are formed in float32 from them (§2.1 "Gate
+ * Parameterization", §4.1 eq.(9) and the gate list after it, eq.(8)):
+ *     log alpha = -exp(a_log[h]) * softplus(z_f),   b = 2 sigmoid(z_b),
+ *     w = sigmoid(z_w),   gamma = gamma_stat[h] * 2 sigmoid(z_q),
+ * and the recurrence reads out with the gain-modulated query:
+ *     S_t = (I - k_t^T (b_t * k_t)) Diag(alpha_t) S_{t-1} + k_t^T (w_t * v_t),
+ *     o_t = (gamma_t * q_t) S_t.
+ * k stays as given (unit norm on the pages); gamma scales only the readout.
+ *
+ *   z_f, z_b        [B,H,T,dk] (decode [N,H,dk])  input dtype; decay and erase
+ *                   logits (z_f including its bias c_f)
+ *   z_w             [B,H,T,dv] (decode [N,H,dv])  input dtype; write logits
+ *   z_q             [B,H,T,dk] (decode [N,H,dk])  input dtype; query-gain
+ *                   logits, or NULL for z_q = 0 (gamma = gamma_stat: the
+ *                   pages' static-gain ablation)
+ *   a_log           [H] float32 per-head log-rate (required)
+ *   gamma_stat      [H, dk] float32 static readout gain, or NULL for ones
+ * a_log and gamma_stat need 4-byte alignment, z_q 16 bytes; outputs must not
+ * overlap them. Everything else (shapes, layouts, workspace, state, errors)
+ * as for gdr_chunk_fwd_ws and gdr_decode_step.
+ */
+int gdr_muir_chunk_fwd_ws(const void* q, const void* k, const void* v,
+                          const void* z_f, const void* z_b, const void* z_w, const void* z_q,
+                          const float* a_log, const float* gamma_stat,
+                          const float* S0, void* o, float* S_out,
+                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int gdr_muir_decode_step(const void* q, const void* k, const void* v,
+                         const void* z_f, const void* z_b, const void* z_w, const void* z_q,
+                         const float* a_log, const float* gamma_stat,
+                         float* S, void* o,
+                         int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
  * gdr_mlstm_fwd — chunkwise forward of the xLSTM mLSTM cell with its
  * log-domain stabiliser ("Exponential gates and matrix memory: xLSTM and
  * RWKV-7", §13.4 and Exercise 13.6), in the [dk, dv] orientation:

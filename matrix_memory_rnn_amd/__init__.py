@@ -26,7 +26,8 @@ import contextlib
 import ctypes
 import os
 
-__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_fwd_noalloc", "gdr_chunk_workspace_size", "gdr_chunk_intra",
+__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_fwd_noalloc", "gdr_muir_chunk_fwd_ws",
+           "gdr_muir_decode_step", "gdr_chunk_workspace_size", "gdr_chunk_intra",
            "gdr_chunk_scan", "gdr_mlstm_fwd_ws", "gdr_mlstm_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
 
@@ -72,6 +73,10 @@ def load_library():
     lib.gdr_chunk_fwd_noalloc.restype = I
     lib.gdr_chunk_scan.argtypes = [P, ctypes.c_size_t, P, P, P] + [I] * 7 + [P]
     lib.gdr_chunk_scan.restype = I
+    lib.gdr_muir_chunk_fwd_ws.argtypes = [P] * 12 + [I] * 7 + [P, ctypes.c_size_t, P]
+    lib.gdr_muir_chunk_fwd_ws.restype = I
+    lib.gdr_muir_decode_step.argtypes = [P] * 11 + [I] * 5 + [P]
+    lib.gdr_muir_decode_step.restype = I
     lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
     lib.gdr_decode_step.restype = I
     lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
@@ -290,6 +295,57 @@ def gdr_decode_step(q, k, v, alpha, b, w, S, *, o=None, stream=None):
     st = lib.gdr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S),
                              _ptr(o), N, H, dk, dv, _dtype_code(q), _stream(stream))
     _check("gdr_decode_step", st)
+    return o
+
+
+def _muir_params(q, z_q, a_log, gamma_stat, H, dk, lead):
+    import torch
+    if z_q is not None:
+        _req(z_q, "z_q", tuple(lead) + (dk,), q.dtype, q.device)
+    _req(a_log, "a_log", (H,), torch.float32, q.device)
+    if gamma_stat is not None:
+        _req(gamma_stat, "gamma_stat", (H, dk), torch.float32, q.device)
+
+
+def gdr_muir_chunk_fwd_ws(q, k, v, z_f, z_b, z_w, a_log, z_q=None, gamma_stat=None, S0=None, *, chunk=64,
+                          o=None, S_out=None, workspace=None, return_state=True, stream=None):
+    """Chunkwise forward with the Muir gate prologue folded into the kernel:
+    z_f, z_b ``[B,H,T,dk]`` and z_w ``[B,H,T,dv]`` are the decay, erase and
+    write logits, z_q ``[B,H,T,dk]`` (or None) the query-gain logits, a_log
+    ``[H]`` and gamma_stat ``[H,dk]`` (or None) float32 per-head parameters
+    ("Muir: ...", §2.1, §4.1 eq.(8)-(9)). Otherwise as :func:`gdr_chunk_fwd_ws`."""
+    (B, H, T, dk, dv), o, S_out = _chunk_args(q, k, v, z_f, z_b, z_w, S0, o, S_out, return_state, stream)
+    _muir_params(q, z_q, a_log, gamma_stat, H, dk, (B, H, T))
+    need = gdr_chunk_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
+    workspace = _workspace(workspace, need, q.device, stream)
+    st = load_library().gdr_muir_chunk_fwd_ws(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z_f), _ptr(z_b), _ptr(z_w), _ptr(z_q), _ptr(a_log), _ptr(gamma_stat),
+        _ptr(S0), _ptr(o), _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gdr_muir_chunk_fwd_ws", st)
+    return o, S_out
+
+
+def gdr_muir_decode_step(q, k, v, z_f, z_b, z_w, a_log, S, z_q=None, gamma_stat=None, *, o=None, stream=None):
+    """One decode step with the Muir gate prologue (logits as in
+    :func:`gdr_muir_chunk_fwd_ws`, shapes ``[N,H,d]``); S updated in place."""
+    import torch
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("z_f", z_f, dk), ("z_b", z_b, dk),
+                       ("v", v, dv), ("z_w", z_w, dv)):
+        _req(t, name, (N, H, d), dt, dev)
+    _req(S, "S", (N, H, dk, dv), torch.float32, dev)
+    _muir_params(q, z_q, a_log, gamma_stat, H, dk, (N, H))
+    if o is None:
+        with _alloc_on(stream):
+            o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    _req(o, "o", (N, H, dv), dt, dev)
+    st = load_library().gdr_muir_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z_f), _ptr(z_b), _ptr(z_w), _ptr(z_q), _ptr(a_log), _ptr(gamma_stat),
+        _ptr(S), _ptr(o), N, H, dk, dv, _dtype_code(q), _stream(stream))
+    _check("gdr_muir_decode_step", st)
     return o
 
 

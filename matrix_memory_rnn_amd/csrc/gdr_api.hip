@@ -96,6 +96,26 @@ int check_workspace(const void* q, const void* k, const void* v, const void* alp
   return GDR_OK;
 }
 
+// Checks of the decode entry points.
+int check_decode(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                 const void* w, const float* S, const void* o, int N, int H, int dk, int dv, int dtype) {
+  if (!q || !k || !v || !alpha || !b || !w || !S || !o) return GDR_ERR_NULL;
+  int st = check_sizes(N, H, 1, dk, dv, dtype, 128);
+  if (st != GDR_OK) return st;
+  const void* ptrs[] = {q, k, v, alpha, b, w, S, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GDR_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const size_t nK = (size_t)N * H * dk * es, nV = (size_t)N * H * dv * es;
+  const size_t nS = (size_t)N * H * dk * dv * sizeof(float);
+  const void* insK[] = {q, k, alpha, b};
+  for (const void* p : insK)
+    if (overlap(o, nV, p, nK) || overlap(S, nS, p, nK)) return GDR_ERR_ALIAS;
+  if (overlap(o, nV, v, nV) || overlap(o, nV, w, nV) || overlap(o, nV, S, nS)) return GDR_ERR_ALIAS;
+  if (overlap(S, nS, v, nV) || overlap(S, nS, w, nV)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,21 +209,73 @@ int gdr_chunk_scan(const void* workspace, size_t workspace_bytes, const float* S
 int gdr_decode_step(const void* q, const void* k, const void* v, const void* alpha, const void* b,
                     const void* w, float* S, void* o, int N, int H, int dk, int dv, int dtype,
                     void* stream) {
-  if (!q || !k || !v || !alpha || !b || !w || !S || !o) return GDR_ERR_NULL;
-  int st = check_sizes(N, H, 1, dk, dv, dtype, 128);
+  int st = check_decode(q, k, v, alpha, b, w, S, o, N, H, dk, dv, dtype);
   if (st != GDR_OK) return st;
-  const void* ptrs[] = {q, k, v, alpha, b, w, S, o};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return GDR_ERR_ALIGN;
-  const size_t es = esize(dtype);
-  const size_t nK = (size_t)N * H * dk * es, nV = (size_t)N * H * dv * es;
-  const size_t nS = (size_t)N * H * dk * dv * sizeof(float);
-  const void* insK[] = {q, k, alpha, b};
-  for (const void* p : insK)
-    if (overlap(o, nV, p, nK) || overlap(S, nS, p, nK)) return GDR_ERR_ALIAS;
-  if (overlap(o, nV, v, nV) || overlap(o, nV, w, nV) || overlap(o, nV, S, nS)) return GDR_ERR_ALIAS;
-  if (overlap(S, nS, v, nV) || overlap(S, nS, w, nV)) return GDR_ERR_ALIAS;
   gdr::DecodeArgs a{q, k, v, alpha, b, w, S, o, N, H, dk, dv, dtype, stream};
+  return gdr::decode_launch(a);
+}
+
+
+}  // extern "C"
+
+namespace {
+
+// Extra checks of the Muir gate-prologue entry points: z_q (optional) is a
+// [.., dk] input like q; a_log [H] and gamma_stat [H, dk] (optional) are
+// float32, 4-byte aligned, and no output may overlap them.
+int check_muir_extra(const void* zq, const float* a_log, const float* gamma_stat, const void* o,
+                     size_t no, const float* S_out, size_t nS, size_t nK, int H, int dk) {
+  if (!a_log) return GDR_ERR_NULL;
+  if (!aligned16(zq)) return GDR_ERR_ALIGN;
+  if (((uintptr_t)a_log & 3u) || ((uintptr_t)gamma_stat & 3u)) return GDR_ERR_ALIGN;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{zq, nK}, {a_log, (size_t)H * 4}, {gamma_stat, (size_t)H * dk * 4}};
+  for (const R& x : ins)
+    if (overlap(o, no, x.p, x.n) || overlap(S_out, nS, x.p, x.n)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_muir_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* z_f, const void* z_b,
+                          const void* z_w, const void* z_q, const float* a_log, const float* gamma_stat,
+                          const float* S0, void* o, float* S_out, int B, int H, int T, int dk, int dv,
+                          int chunk, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_chunk(q, k, v, z_f, z_b, z_w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  const size_t es = esize(dtype);
+  st = check_muir_extra(z_q, a_log, gamma_stat, o, (size_t)B * H * T * dv * es, S_out,
+                        (size_t)B * H * dk * dv * 4, (size_t)B * H * T * dk * es, H, dk);
+  if (st != GDR_OK) return st;
+  st = check_workspace(q, k, v, z_f, z_b, z_w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, workspace,
+                       workspace_bytes);
+  if (st != GDR_OK) return st;
+  if (overlap(workspace, gdr::chunk_ws_bytes(B, H, T, dk, dv, chunk, dtype), z_q, (size_t)B * H * T * dk * es))
+    return GDR_ERR_ALIAS;
+  gdr::ChunkArgs a{q, k, v, z_f, z_b, z_w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
+  a.gated = true;
+  a.zq = z_q;
+  a.a_log = a_log;
+  a.gamma_stat = gamma_stat;
+  return gdr::chunk_fwd_ws_launch(a, workspace, 3);
+}
+
+int gdr_muir_decode_step(const void* q, const void* k, const void* v, const void* z_f, const void* z_b,
+                         const void* z_w, const void* z_q, const float* a_log, const float* gamma_stat,
+                         float* S, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+  int st = check_decode(q, k, v, z_f, z_b, z_w, S, o, N, H, dk, dv, dtype);
+  if (st != GDR_OK) return st;
+  const size_t es = esize(dtype);
+  st = check_muir_extra(z_q, a_log, gamma_stat, o, (size_t)N * H * dv * es, S,
+                        (size_t)N * H * dk * dv * 4, (size_t)N * H * dk * es, H, dk);
+  if (st != GDR_OK) return st;
+  gdr::DecodeArgs a{q, k, v, z_f, z_b, z_w, S, o, N, H, dk, dv, dtype, stream};
+  a.gated = true;
+  a.zq = z_q;
+  a.a_log = a_log;
+  a.gamma_stat = gamma_stat;
   return gdr::decode_launch(a);
 }
 

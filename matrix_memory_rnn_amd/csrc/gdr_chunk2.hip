@@ -218,11 +218,17 @@ struct IntraSmem {
   static_assert(TOTAL <= 160 * 1024, "intra kernel LDS exceeds 160 KiB");
 };
 
-template <typename Tin, int DK, int CM, bool FM>
+// GATED: alpha, bgate and wgate hold the gate logits z_f, z_b, z_w of the Muir
+// page (§2.1, §4.1) and the gates are formed here in fp32 (gate_alpha,
+// 2 gate_sigmoid, gate_sigmoid); q is read as the gain-modulated query
+// gamma * q with gamma = gstat[h] * 2 sigmoid(z_q) (zq NULL: z_q = 0; gstat
+// NULL: ones), and alog[h] is the head's log-rate.
+template <typename Tin, int DK, int CM, bool FM, bool GATED>
 __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
-    char* __restrict__ ws, int T, int DV, int nchunks, int nitems) {
+    char* __restrict__ ws, int T, int DV, int nchunks, int nitems, const Tin* __restrict__ zq,
+    const float* __restrict__ alog, const float* __restrict__ gstat, int H) {
   using L = IntraSmem<Tin, DK, CM>;
   constexpr bool F32 = L::F32;
   static_assert(!FM || (!F32 && DK % 32 == 0 && CM % 32 == 0), "F order needs bf16, d_k and C multiples of 32");
@@ -278,6 +284,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
   const int nvi = CM * (DV / 8);
   typename RW::R2 xa[8], xk[8], xb[8], xq[8];
   typename RW::R8 xv[MAXVI], xw[MAXVI];
+  // GATED: query-gain logits z_q (zero when not given)
+  typename RW::R2 xz[GATED ? 8 : 1];
   // parts: 1 = alpha and k, 2 = b and q, 4 = v and w
   auto issue = [&](int it, int parts) {
     const int bh = it / nchunks, tb = (it % nchunks) * CM;
@@ -306,6 +314,12 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         for (int r = 0; r < 8; ++r) {
           xb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo + r * DK * ES, 0, 0);
           xq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo + r * DK * ES, 0, 0);
+        }
+        if constexpr (GATED) {
+          // no z_q: a buffer of zero records, every load reads zero
+          const __amdgpu_buffer_rsrc_t rz = zq ? rs(zq, sK, nbK) : rs(q, 0, 0u);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) xz[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, vo + r * DK * ES, 0, 0);
         }
       }
       if (parts & 4) {
@@ -338,6 +352,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           const size_t off = sK + (size_t)(t < T ? t : T - 1) * DK;
           xb[r] = RW::ld2(bgate + off);
           xq[r] = RW::ld2(q + off);
+          if constexpr (GATED) xz[r] = zq ? RW::ld2(zq + off) : RW::pad2(0.f);
         }
       }
       if (parts & 4) {
@@ -387,10 +402,24 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     constexpr int ES = (int)sizeof(Tin);
 
     // identity padding past the end of the sequence: alpha = 1, k = b = q = 0,
-    // v = w = 0 (bf16: the buffer loads already read zeros there)
+    // v = w = 0 (bf16: the buffer loads already read zeros there). GATED: the
+    // decay logit -inf gives alpha = 1.
     float vh[MAXVI][8];
+    float rate = 1.f, gsx = 1.f, gsy = 1.f;
+    const float* gzh = nullptr;
+    if constexpr (GATED) {
+      const int hh = bh % H;
+      rate = expf(alog[hh]);
+      if (gstat) {
+        gzh = gstat + (size_t)hh * DK;
+        gsx = gzh[j];
+        gsy = gzh[j + 1];
+      }
+    }
+    // the exact in-block path reads the gates itself (from their logits when GATED)
+    const GateRead<Tin, GATED> gread{zq, gzh, rate};
     {
-      const typename RW::R2 one = RW::pad2(1.f), zero = RW::pad2(0.f);
+      const typename RW::R2 one = RW::pad2(GATED ? -__builtin_inff() : 1.f), zero = RW::pad2(0.f);
       if (t0 + CM > T) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -409,6 +438,10 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         float fv[8], fw[8];
         RW::un8(xv[i], fv);
         RW::un8(xw[i], fw);
+        if constexpr (GATED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) fw[e] = gate_sigmoid(fw[e]);
+        }
         if constexpr (F32) {
           const bool okv = idx < nvi && t0 + idx / (DV / 8) < T;
 #pragma unroll
@@ -440,10 +473,23 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     }
 
     // ================= prep 1: half-block products -> block totals G
+    // GATED: the decays are formed from their logits once, here, in fp32
+    float2 af[GATED ? 8 : 1];
+    if constexpr (GATED) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float2 z = RW::un2(xa[r]);
+        af[r] = make_float2(gate_alpha(z.x, rate), gate_alpha(z.y, rate));
+      }
+    }
+    auto alpha_at = [&](int r) {
+      if constexpr (GATED) return af[r];
+      else return RW::un2(xa[r]);
+    };
     float2 ph = make_float2(1.f, 1.f);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const float2 a = RW::un2(xa[r]);
+      const float2 a = alpha_at(r);
       ph.x *= a.x;
       ph.y *= a.y;
     }
@@ -484,7 +530,13 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       float2 P = hq ? p0 : make_float2(1.f, 1.f);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float2 a = RW::un2(xa[r]), kk = RW::un2(xk[r]), bb = RW::un2(xb[r]), qq = RW::un2(xq[r]);
+        const float2 a = alpha_at(r), kk = RW::un2(xk[r]);
+        float2 bb = RW::un2(xb[r]), qq = RW::un2(xq[r]);
+        if constexpr (GATED) {
+          const float2 zz = RW::un2(xz[r]);
+          bb = make_float2(2.f * gate_sigmoid(bb.x), 2.f * gate_sigmoid(bb.y));
+          qq = make_float2(qq.x * gsx * 2.f * gate_sigmoid(zz.x), qq.y * gsy * 2.f * gate_sigmoid(zz.y));
+        }
         P.x *= a.x;
         P.y *= a.y;
         const float krx = bb.x * kk.x * P.x, kry = bb.y * kk.y * P.y;
@@ -502,7 +554,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
       float2 qs = hq ? make_float2(1.f, 1.f) : p1;
 #pragma unroll
       for (int r = 7; r >= 0; --r) {
-        const float2 kk = RW::un2(xk[r]), a = RW::un2(xa[r]);
+        const float2 kk = RW::un2(xk[r]), a = alpha_at(r);
         const float kcx = kk.x * qs.x, kcy = kk.y * qs.y;
         st2<MM>(smem + L::KC, L::P_CK, (r0 + r) * L::LDK + j, kcx, kcy);
         ktx[r] = kcx * E.x;
@@ -578,7 +630,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           const int t = 16 * I + c16, s0 = 16 * J + 4 * g;
           f32x4 lv = gL[i], mv = gM[i];
           if (I == J) {
-            if (FLAGS[I]) exact_diag<Tin, DK>(k, bgate, q, alpha, seqK, t0, T, t, s0, lv, mv);
+            if (FLAGS[I]) exact_diag<Tin, DK, GATED>(k, bgate, q, alpha, seqK, t0, T, t, s0, lv, mv, gread);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (s0 + e >= t) lv[e] = 0.f;
@@ -751,7 +803,7 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           // M layout), brought to the L layout through LDS
           float* Lb = LBD + I * BLKF;   // L_II [t][s], fp32
           f32x4 lx;
-          exact_diag<Tin, DK>(k, bgate, q, alpha, seqK, t0, T, t, s0, lx, mv);
+          exact_diag<Tin, DK, GATED>(k, bgate, q, alpha, seqK, t0, T, t, s0, lx, mv, gread);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (s0 + e >= t) lx[e] = 0.f;
@@ -1773,10 +1825,10 @@ size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype)
   return (size_t)B * H * nchunks * (size_t)rec_layout(dk, dv, chunk, es).bytes;
 }
 
-template <typename Tin, int DK, int CM, bool FM>
-static int launch_intra(const ChunkArgs& a, char* ws) {
+template <typename Tin, int DK, int CM, bool FM, bool GATED>
+static int launch_intra_g(const ChunkArgs& a, char* ws) {
   using L = IntraSmem<Tin, DK, CM>;
-  auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM, FM>;
+  auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM, FM, GATED>;
   if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   int nchunks = (a.T + CM - 1) / CM;
   int nitems = a.B * a.H * nchunks;
@@ -1785,11 +1837,18 @@ static int launch_intra(const ChunkArgs& a, char* ws) {
   const int grid = nitems < cus ? nitems : cus;
   const Tin *q = (const Tin*)a.q, *k = (const Tin*)a.k, *v = (const Tin*)a.v;
   const Tin *al = (const Tin*)a.alpha, *bg = (const Tin*)a.b, *wg = (const Tin*)a.w;
-  int T = a.T, DV = a.dv;
-  void* args[] = {&q, &k, &v, &al, &bg, &wg, &ws, &T, &DV, &nchunks, &nitems};
+  const Tin* zq = (const Tin*)a.zq;
+  const float *alog = a.a_log, *gst = a.gamma_stat;
+  int T = a.T, DV = a.dv, H = a.H;
+  void* args[] = {&q, &k, &v, &al, &bg, &wg, &ws, &T, &DV, &nchunks, &nitems, &zq, &alog, &gst, &H};
   hipError_t e = hipLaunchKernel((const void*)kern, dim3(grid), dim3(kIntraThreads), args, L::TOTAL,
                                  (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+template <typename Tin, int DK, int CM, bool FM>
+static int launch_intra(const ChunkArgs& a, char* ws) {
+  return a.gated ? launch_intra_g<Tin, DK, CM, FM, true>(a, ws) : launch_intra_g<Tin, DK, CM, FM, false>(a, ws);
 }
 
 template <typename Tin, int DK, int VT, int CM>

@@ -53,21 +53,53 @@ __device__ __forceinline__ Frag<MODE> frag_f32(const float* p, bool valid) {
   return f;
 }
 
+// Gate values as the exact path reads them: the stored gates, or (GATED, the
+// Muir gate prologue) the gates formed from their logits: alpha from z_f,
+// b = 2 sigmoid(z_b), and the query scaled by gamma = gstat * 2 sigmoid(z_q)
+// (gz = this head's gstat row or NULL, zq NULL for z_q = 0).
+template <typename Tin, bool GATED>
+struct GateRead {
+  const Tin* zq;
+  const float* gz;
+  float rate;
+  __device__ __forceinline__ float alpha(const Tin* p) const {
+    const float x = In<Tin>::load1(p);
+    if constexpr (GATED) return gate_alpha(x, rate);
+    else return x;
+  }
+  __device__ __forceinline__ float erase(const Tin* p) const {
+    const float x = In<Tin>::load1(p);
+    if constexpr (GATED) return 2.f * gate_sigmoid(x);
+    else return x;
+  }
+  __device__ __forceinline__ float query(const Tin* q, size_t off, int j) const {
+    const float x = In<Tin>::load1(q + off);
+    if constexpr (GATED) {
+      const float z = zq ? In<Tin>::load1(zq + off) : 0.f;
+      return x * (gz ? gz[j] : 1.f) * 2.f * gate_sigmoid(z);
+    } else {
+      return x;
+    }
+  }
+};
+
 // Exact in-block Gram entries for the tile (I, I) from alpha products (slow path).
-template <typename Tin, int DK>
+template <typename Tin, int DK, bool GATED = false>
 __device__ void exact_diag(const Tin* __restrict__ k, const Tin* __restrict__ bg,
                            const Tin* __restrict__ q, const Tin* __restrict__ al,
-                           size_t seqK, int t0, int T, int t, int s0, f32x4& lv, f32x4& mv) {
+                           size_t seqK, int t0, int T, int t, int s0, f32x4& lv, f32x4& mv,
+                           GateRead<Tin, GATED> gr = GateRead<Tin, GATED>{nullptr, nullptr, 1.f}) {
   float aL[4] = {0.f, 0.f, 0.f, 0.f}, aM[4] = {0.f, 0.f, 0.f, 0.f};
   const int tg = t0 + t;
   if (tg < T && t >= s0) {
     for (int j = 0; j < DK; ++j) {
-      const float kt = In<Tin>::load1(k + seqK + (size_t)tg * DK + j);
-      const float kh = kt * In<Tin>::load1(bg + seqK + (size_t)tg * DK + j);
-      const float qt = In<Tin>::load1(q + seqK + (size_t)tg * DK + j);
+      const size_t rt = seqK + (size_t)tg * DK + j;
+      const float kt = In<Tin>::load1(k + rt);
+      const float kh = kt * gr.erase(bg + rt);
+      const float qt = gr.query(q, rt, j);
       float p = 1.f;  // prod_{r=s+1..t} alpha_r
       for (int s = t; s >= s0; --s) {
-        if (s < t) p *= In<Tin>::load1(al + seqK + (size_t)(t0 + s + 1) * DK + j);
+        if (s < t) p *= gr.alpha(al + seqK + (size_t)(t0 + s + 1) * DK + j);
         const int e = s - s0;
         if (e < 4) {
           const float ks = In<Tin>::load1(k + seqK + (size_t)(t0 + s) * DK + j) * p;

@@ -10,20 +10,26 @@
 // The step is a streaming read-modify-write of S (HBM-bound): one workgroup
 // per state, 256 threads, each thread holding DK*DV/256 state elements as
 // float4 rows segments (d_v contiguous, so every wave reads whole rows).
+//
+// GATED (the Muir gate prologue, "Muir: ...", §2.1 and §4.1): alpha, bgate and
+// wgate hold the logits z_f, z_b, z_w; alpha = exp(-exp(a_log) softplus(z_f)),
+// b = 2 sigmoid(z_b), w = sigmoid(z_w) and the query is gamma * q with
+// gamma = gamma_stat * 2 sigmoid(z_q), all formed here in fp32.
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
 
 namespace gdr {
 
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(256) void gdn2_decode_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
-    float* __restrict__ S, Tin* __restrict__ o) {
+    float* __restrict__ S, Tin* __restrict__ o, const Tin* __restrict__ zq,
+    const float* __restrict__ alog, const float* __restrict__ gstat, int H) {
   constexpr int TPR = DV / 4;                 // threads per state row (float4 each)
   constexpr int RPP = 256 / TPR;              // rows per pass
   constexpr int NPASS = (DK + RPP - 1) / RPP;
-  __shared__ float s_qa[DK], s_kb[DK], s_al[DK], s_k[DK], s_vh[DV];
+  __shared__ float s_qa[DK], s_kb[DK], s_al[DK], s_k[DK], s_vh[DV], s_qh[DK];
   __shared__ float s_red[2][RPP][DV];
   __shared__ float s_qk;
 
@@ -41,27 +47,38 @@ __global__ __launch_bounds__(256) void gdn2_decode_kernel(
     const int j = rg + RPP * p;
     st[p] = (rg < RPP && j < DK) ? *(const f32x4*)(Sh + (size_t)j * DV + c4) : f4zero();
   }
+  float rate = 1.f;
+  if constexpr (GATED) rate = expf(alog[head % H]);
   for (int j = tid; j < DK; j += 256) {
-    const float a = In<Tin>::load1(alpha + offK + j);
+    float a = In<Tin>::load1(alpha + offK + j);
     const float kk = In<Tin>::load1(k + offK + j);
-    const float bb = In<Tin>::load1(bgate + offK + j);
-    const float qq = In<Tin>::load1(q + offK + j);
+    float bb = In<Tin>::load1(bgate + offK + j);
+    float qq = In<Tin>::load1(q + offK + j);
+    if constexpr (GATED) {
+      a = gate_alpha(a, rate);
+      bb = 2.f * gate_sigmoid(bb);
+      const float zz = zq ? In<Tin>::load1(zq + offK + j) : 0.f;
+      qq *= (gstat ? gstat[(head % H) * DK + j] : 1.f) * 2.f * gate_sigmoid(zz);
+    }
     s_al[j] = a;
     s_k[j] = kk;
     s_kb[j] = a * bb * kk;
     s_qa[j] = a * qq;
+    s_qh[j] = qq;
   }
-  for (int c = tid; c < DV; c += 256)
-    s_vh[c] = In<Tin>::load1(wgate + offV + c) * In<Tin>::load1(v + offV + c);
+  for (int c = tid; c < DV; c += 256) {
+    float ww = In<Tin>::load1(wgate + offV + c);
+    if constexpr (GATED) ww = gate_sigmoid(ww);
+    s_vh[c] = ww * In<Tin>::load1(v + offV + c);
+  }
+  __syncthreads();
   if (tid < 64) {  // q . k by one wave
     float acc = 0.f;
-    for (int j = tid; j < DK; j += 64)
-      acc += In<Tin>::load1(q + offK + j) * In<Tin>::load1(k + offK + j);
+    for (int j = tid; j < DK; j += 64) acc += s_qh[j] * s_k[j];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (tid == 0) s_qk = acc;
   }
-  __syncthreads();
 
   f32x4 r = f4zero(), pq = f4zero();
   if (rg < RPP) {
@@ -119,9 +136,13 @@ static int launch_decode(const DecodeArgs& a) {
   const Tin *al = (const Tin*)a.alpha, *bg = (const Tin*)a.b, *wg = (const Tin*)a.w;
   float* S = a.S;
   Tin* o = (Tin*)a.o;
-  void* args[] = {&q, &k, &v, &al, &bg, &wg, &S, &o};
-  hipError_t e = hipLaunchKernel((const void*)gdn2_decode_kernel<Tin, DK, DV>, dim3(a.N * a.H), dim3(256),
-                                 args, 0, (hipStream_t)a.stream);
+  const Tin* zq = (const Tin*)a.zq;
+  const float *alog = a.a_log, *gst = a.gamma_stat;
+  int H = a.H;
+  void* args[] = {&q, &k, &v, &al, &bg, &wg, &S, &o, &zq, &alog, &gst, &H};
+  const void* kern = a.gated ? (const void*)gdn2_decode_kernel<Tin, DK, DV, true>
+                             : (const void*)gdn2_decode_kernel<Tin, DK, DV, false>;
+  hipError_t e = hipLaunchKernel(kern, dim3(a.N * a.H), dim3(256), args, 0, (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 

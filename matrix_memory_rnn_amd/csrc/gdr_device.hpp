@@ -296,4 +296,18 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks, int group) {
   return (bid % kXcd) * per + bid / kXcd;
 }
 
+// ---- gate activations of "Muir: ..." (§2.1 "Gated DeltaNet-2", §4.1 eq.(9)
+// and the gate list after it), evaluated in fp32 from the logits:
+//   log alpha = -exp(a_log) * softplus(z_f),  b = 2 sigmoid(z_b),
+//   w = sigmoid(z_w),  gamma = gamma_stat * 2 sigmoid(z_q).
+// softplus(z) = max(z, 0) + log(1 + e^{-|z|}) has no overflow for large |z|
+// and gives 0 at z = -inf (alpha = 1, the identity padding of a ragged tail).
+// The hardware exp2/log2/reciprocal forms (__expf, __logf, v_rcp_f32, about
+// 1 ulp each) keep the prologue cheap; log(1 + x) for x below float epsilon
+// returns 0 instead of x, an absolute error under 6e-8 in softplus.
+__device__ __forceinline__ float gate_softplus(float z) { return fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))); }
+__device__ __forceinline__ float gate_sigmoid(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+// alpha from its logit; rate = exp(a_log) of the head
+__device__ __forceinline__ float gate_alpha(float z, float rate) { return __expf(-rate * gate_softplus(z)); }
+
 }  // namespace gdr

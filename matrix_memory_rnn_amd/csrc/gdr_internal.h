@@ -16,6 +16,12 @@ struct ChunkArgs {
   float* S_out;
   int B, H, T, dk, dv, chunk, dtype;
   void* stream;
+  // gate logits in place of the gates (alpha, b, w hold z_f, z_b, z_w): the
+  // Muir gate prologue; zq (may be NULL), a_log [H], gamma_stat [H, dk] (may be NULL)
+  bool gated = false;
+  const void* zq = nullptr;
+  const float* a_log = nullptr;
+  const float* gamma_stat = nullptr;
 };
 
 struct DecodeArgs {
@@ -24,6 +30,11 @@ struct DecodeArgs {
   void* o;
   int N, H, dk, dv, dtype;
   void* stream;
+  // Muir gate prologue, as in ChunkArgs
+  bool gated = false;
+  const void* zq = nullptr;
+  const float* a_log = nullptr;
+  const float* gamma_stat = nullptr;
 };
 
 struct MlstmArgs {

@@ -11,6 +11,8 @@ Sources (cited by page title and section/equation):
   write, GLA form, chunkwise form), §4.2 stage (i) and eq.(10) (the chunk
   matrix T = I + L_strict and the chunkwise readout and state update, used to
   measure how ill-conditioned the tests' chunk systems are).
+* the same page, §2.1 (gate parameterisation) and §4.1 eq.(8)-(9): the Muir
+  gate prologue (gates from logits, readout with the gain-modulated query).
 * "Exponential gates and matrix memory: xLSTM and RWKV-7" — §13.2 (spectrum of
   the diagonal-plus-rank-one transition, Prop. 13.1 and Exercise 13.4), §13.3
   (reduction to Gated DeltaNet), §13.4 and Exercise 13.6 (mLSTM cell, log-domain
@@ -34,6 +36,9 @@ from .gdn2 import (  # noqa: F401
     gdn2_effective_write, gdn2_decode, delta_rule_textbook, gated_deltanet,
     gla_closed_form, linear_attention_closed_form, bruteforce_exact,
     gdn2_chunk_system, gdn2_chunkwise, chunk_condition_numbers,
+)
+from .muir import (  # noqa: F401
+    muir_gates, muir_recurrent, muir_decode,
 )
 from .mlstm import (  # noqa: F401
     mlstm_stabilized, mlstm_naive, mlstm_with_stabilizer, stabilizer_closed_form,

@@ -32,6 +32,7 @@ __all__ = [
     "gdn2_inputs",
     "gdn2_inputs_correlated",
     "decode_inputs",
+    "muir_inputs",
     "mlstm_inputs",
     "CONFIGS",
 ]
@@ -137,6 +138,41 @@ def decode_inputs(N, H, dk, dv, *, step, alpha_mu=4.0, alpha_sigma=1.5, seed=0,
     d = gdn2_inputs(N, H, 1, dk, dv, alpha_mu=alpha_mu, alpha_sigma=alpha_sigma,
                     dtype=dtype, rng=g)
     return {k_: (v_[:, :, 0] if isinstance(v_, np.ndarray) else v_) for k_, v_ in d.items()}
+
+
+def muir_inputs(B, H, T, dk, dv, *, seed=0, dtype="bf16", zf_mu=-3.0, zf_sigma=1.0, alog_mu=-1.0,
+                alog_sigma=0.3, with_zq=True, with_gamma=True, s0_std=None, rng=None):
+    """Inputs of the Muir gate prologue: q, k (unit SiLU of N(0,1)), v ~ N(0,1);
+    logits z_f ~ N(zf_mu, zf_sigma) (bias included), z_b, z_w, z_q ~ N(0,1)
+    (``[B,H,T,d]``, rounded to ``dtype``); a_log ~ N(alog_mu, alog_sigma) per
+    head and gamma_stat = exp(N(0, 0.3)) per (head, channel), both float32.
+    With the defaults the decays alpha = exp(-exp(a_log) softplus(z_f)) are
+    about 0.98 (0.9 to 0.998), like sigmoid(N(4, 1.5)).
+
+    Draw order: q, k, v, z_f, z_b, z_w, z_q, a_log, gamma_stat, S0.
+    """
+    g = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
+    q = _unit_silu(g.standard_normal((B, H, T, dk)))
+    k = _unit_silu(g.standard_normal((B, H, T, dk)))
+    v = g.standard_normal((B, H, T, dv))
+    zf = zf_mu + zf_sigma * g.standard_normal((B, H, T, dk))
+    zb = g.standard_normal((B, H, T, dk))
+    zw = g.standard_normal((B, H, T, dv))
+    zq = g.standard_normal((B, H, T, dk))
+    alog = alog_mu + alog_sigma * g.standard_normal(H)
+    gs = np.exp(0.3 * g.standard_normal((H, dk)))
+    S0 = None
+    if s0_std is not None:
+        S0 = round_to(s0_std * g.standard_normal((B, H, dk, dv)), "f32")
+    out = {name: round_to(x, dtype) for name, x in
+           (("q", q), ("k", k), ("v", v), ("z_f", zf), ("z_b", zb), ("z_w", zw), ("z_q", zq))}
+    if not with_zq:
+        out["z_q"] = None
+    out["a_log"] = round_to(alog, "f32")
+    out["gamma_stat"] = round_to(gs, "f32") if with_gamma else None
+    out["S0"] = S0
+    out["dtype"] = dtype
+    return out
 
 
 def mlstm_inputs(B, H, T, dk, dv, *, seed=0, dtype="bf16", i_sigma=2.0, f_mu=3.0,
