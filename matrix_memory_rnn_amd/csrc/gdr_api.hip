@@ -424,7 +424,7 @@ extern "C" int gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v
   if (st != GDR_OK) return st;
   // heads are independent: they go through the scratch array in groups of
   // consecutive (b, h) pairs, as many per group as the array holds
-  const size_t per_head = gdr::chunk_ws_bytes(1, 1, T, dk, dv, chunk, dtype);
+  const size_t per_head = gdr::chunk_ws_bytes(1, 1, T, dk, dv, chunk, dtype, false);
   if (per_head > kScratchBytes) return GDR_ERR_TOO_LARGE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_LAUNCH;
@@ -442,6 +442,7 @@ extern "C" int gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v
                      (const char*)alpha + oK, (const char*)b + oK, (const char*)w + oV,
                      S0 ? S0 + oS : nullptr, (char*)o + oV, S_out ? S_out + oS : nullptr,
                      1, g, T, dk, dv, chunk, dtype, stream};
+    a.no_seg = true;   // records only: the scratch is sized per head
     st = gdr::chunk_fwd_ws_launch(a, ws, 3);
     if (st != GDR_OK) return st;
   }

@@ -1508,6 +1508,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void gdn2_chunk_scan_staged_kernel
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 constexpr int kScanFmWaves = 10;
 constexpr int kScanFmThreads = 64 * kScanFmWaves;
+constexpr int kSegTargetUnits = 256;  // scan workgroups the segmented scan aims for (one per CU)
 constexpr int kScanFmPrefetch = 3;   // chunks ahead that the record is pulled into L2
 constexpr int kScanFmSets = 3;       // register sets per wave: loads run NS - 1 chunks ahead
 
@@ -1530,10 +1531,15 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Sequence segments: with seg < the chunk count, the chunks of a head are
+// split into segments of seg chunks, one workgroup per (b, h, segment, value
+// tile), and segment g starts from the state Sseg[g][b*H + h] that the
+// segment pass left there (g = 0: S0); only the last segment writes S_out.
+// With seg >= the chunk count there is one segment, starting from S0.
 template <int DK, int CM, int PF, int NS>
 __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
     const char* __restrict__ ws, const float* __restrict__ S0, __bf16* __restrict__ o, float* S_out,
-    int T, int DV) {
+    int T, int DV, int seg, const float* __restrict__ Sseg) {
   constexpr int NI2 = CM / 32, NJ2 = DK / 32, KSD = DK / 16, KSC = CM / 16;
   constexpr int LDK = DK + 8, LDC = CM + 8;      // LDS row pitches (elements): 16-byte reads conflict free
   static_assert(DK % 32 == 0 && CM % 32 == 0 && NJ2 <= 4 && NI2 <= 2, "F-order scan shape");
@@ -1546,11 +1552,18 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
   const int h = lane >> 5, r = lane & 31;
   const int nvt = DV / 32;
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
-  const int bh = lin / nvt, vt = lin % nvt, vt0 = 32 * vt;
-  const int nchunks = (T + CM - 1) / CM;
+  const int ntot = (T + CM - 1) / CM;                  // chunks of the sequence
+  const int nseg = (ntot + seg - 1) / seg;
+  const int unit = lin / nvt, vt = lin % nvt, vt0 = 32 * vt;
+  const int bh = unit / nseg, sg = unit % nseg;
+  const int c0 = sg * seg;                             // first chunk of this segment
+  const int nchunks = ntot - c0 < seg ? ntot - c0 : seg;
   const size_t stOff = (size_t)bh * DK * DV;
+  // start state: S0 (or zero) for one segment, else this segment's slot
+  const float* S0w = nseg == 1 ? S0 : Sseg + ((size_t)sg * (gridDim.x / (nvt * nseg)) + bh) * DK * DV;
+  float* S_outw = sg == nseg - 1 ? S_out : nullptr;
   const RecLayout RL = rec_layout(DK, DV, CM, 2);
-  const char* wsh = ws + (size_t)bh * nchunks * RL.bytes;
+  const char* wsh = ws + ((size_t)bh * ntot + c0) * RL.bytes;
   // the records of this head through a buffer resource; the wave-uniform
   // part of each offset goes in the scalar offset, past the last chunk the
   // loads repeat it
@@ -1697,7 +1710,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
         for (int s = 0; s < NM; ++s) acc = mma32(vfrag(s), RM[u][s], acc);
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
         typedef __attribute__((ext_vector_type(2))) uint32_t u2;
-        const int t0 = ch * CM;
+        const int t0 = (c0 + ch) * CM;
         const __amdgpu_buffer_rsrc_t orsrc =
             __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
 #pragma unroll
@@ -1749,7 +1762,8 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        Sacc[4 * q + e] = (live && S0) ? S0[stOff + (size_t)(32 * J2 + 8 * q + 4 * h + e) * DV + vt0 + r] : 0.f;
+        Sacc[4 * q + e] = (live && S0w) ? S0w[(nseg == 1 ? stOff : 0) + (size_t)(32 * J2 + 8 * q + 4 * h + e) * DV + vt0 + r]
+                                        : 0.f;
     auto st_s0t = [&]() {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -1807,22 +1821,286 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
         for (int u = 0; u < PF; ++u) sink ^= PFV[u];
         if (sink == 0x7fc00001u && T < 0) o[0] = (__bf16)0.f;   // never true (T > 0): keeps the touches alive
       }
-      if (S_out) {
+      if (S_outw) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            S_out[stOff + (size_t)(32 * J2 + 8 * q + 4 * h + e) * DV + vt0 + r] = Sacc[4 * q + e];
+            S_outw[stOff + (size_t)(32 * J2 + 8 * q + 4 * h + e) * DV + vt0 + r] = Sacc[4 * q + e];
       }
     }
   }
 }
 
+// ------------------------------------------------------------------ sequence segments
+//
+// The chunk maps of "Muir: ...", §4.2 eq.(10) are affine in the state:
+// S_C = A_c S_0 + K~^T U with A_c = Diag(pi_C) - K~^T Y. So a run of chunks
+// (a segment g) maps its start state affinely, S_end = P_g S_start + Q_g, and
+// a head with few value tiles but many chunks can walk its segments side by
+// side:
+//   seg_state:   every (b, h, segment, 32-column tile of [Q | P]) walks the
+//                segment from [0 | I]: the Q tiles with the record's U, the P
+//                tiles with U = 0 (d_k identity columns carried through the
+//                homogeneous map), giving [Q_g | P_g] (fp32);
+//   seg_combine: per (b, h, value tile), S_start(g + 1) = P_g S_start(g) + Q_g
+//                in order over the segments, from S_start(0) = S0;
+//   the F-order scan then walks every segment from its start state and
+//   writes O (and S_T from the last segment).
+// The state tile walk of seg_state is the V~ / state-update half of the
+// F-order scan (the same MFMA layouts), without the readout.
+
+// Augmented state [Q_g | P_g] of (segment g, head bh): rows j, DV + DK columns.
+__host__ __device__ __forceinline__ size_t seg_aug_off(int g, int bh, int BH, int DK, int DV) {
+  return ((size_t)g * BH + bh) * DK * (DV + DK);
+}
+
+constexpr int kSegThreads = 64 * 6;   // seg_state: V~ waves (C/32) and state waves (d_k/32), at most 6
+
+template <int DK, int CM>
+__global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const char* __restrict__ ws,
+                                                                            float* __restrict__ Saug, int T,
+                                                                            int DV, int seg) {
+  constexpr int NI2 = CM / 32, NJ2 = DK / 32, KSD = DK / 16, KSC = CM / 16;
+  constexpr int LDK = DK + 8, LDC = CM + 8;
+  static_assert(DK % 32 == 0 && CM % 32 == 0 && NJ2 <= 4 && NI2 <= 2, "F-order segment shape");
+  __shared__ __attribute__((aligned(16))) __bf16 S0T[32 * LDK];   // bf16 copy of the state tile, [col][j]
+  __shared__ __attribute__((aligned(16))) __bf16 VTT[32 * LDC];   // V~^T [col][t]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r = lane & 31;
+  const int nvt = DV / 32, ntile = nvt + DK / 32;
+  const int ntot = (T + CM - 1) / CM, nseg = (ntot + seg - 1) / seg;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, ntile);
+  const int unit = lin / ntile, tile = lin % ntile;
+  const int bh = unit / nseg, sg = unit % nseg;
+  const int BH = gridDim.x / (ntile * nseg);
+  const bool ptile = tile >= nvt;                      // a column tile of P (U = 0, identity start)
+  const int c0 = sg * seg, nch = ntot - c0 < seg ? ntot - c0 : seg;
+  const RecLayout RL = rec_layout(DK, DV, CM, 2);
+  const char* wsh = ws + ((size_t)bh * ntot + c0) * RL.bytes;
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wsh), 0, nch * RL.bytes, 0x00020000);
+  auto ld16 = [&](int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, soff, 0));
+  };
+  // past the segment's last chunk the loads repeat it (never used)
+  auto cbase = [&](int ch) { return (ch < nch ? ch : nch - 1) * RL.bytes; };
+  const int l16 = lane * 16;
+  auto s0frag = [&](int s) { return *(const u32x4*)(S0T + r * LDK + 16 * s + 8 * h); };
+  auto vfrag = [&](int s) { return *(const u32x4*)(VTT + r * LDC + 16 * s + 8 * h); };
+  // each role walks the chunks with two register sets (the next chunk's
+  // operands load while this one's are used), unrolled by hand over the two
+  // sets with a single exit so the wait counts stay exact
+  auto walk = [&](auto&& step) {
+    int ch = 0;
+    for (; ch + 2 <= nch; ch += 2) {
+      step(ch, Ic<0>{});
+      step(ch + 1, Ic<1>{});
+    }
+    if (ch < nch) step(ch, Ic<0>{});
+  };
+
+  if (wid < NI2) {
+    // ================= V: V~ rows 32 wid .. = U - Y S (U = 0 for P tiles) -> V~^T in LDS
+    const int I2 = wid;
+    u32x4 RY[2][KSD], RU[2][2];
+    // P tiles read U at an offset past the buffer's end: the loads return zero
+    // (and every path issues the same loads)
+    const int ub = ptile ? 0x7ffffff0 : lane * 32;
+    const int uo = RL.ut + ((ptile ? 0 : tile) * NI2 + I2) * 2048;
+    auto load = [&](int ch, u32x4* Y, u32x4* U) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) Y[s] = ld16(l16, cb + RL.y + I2 * KSD * 1024 + 1024 * s);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) U[s] = ld16(ub, cb + uo + 16 * s);
+    };
+    __syncthreads();                                    // initial state copy written
+    __builtin_amdgcn_s_waitcnt(0);
+    load(0, RY[0], RU[0]);
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      load(ch + 1, RY[1 - u], RU[1 - u]);
+      f32x16 acc = f16zero();
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) acc = mma32(RY[u][s], s0frag(s), acc);
+      typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4& up = RU[u][q >> 1];
+        const f32x4 uu = Raw<__bf16>::un4(u2{up[2 * (q & 1)], up[2 * (q & 1) + 1]});
+        In<__bf16>::store4(VTT + r * LDC + 32 * I2 + 8 * q + 4 * h,
+                           f32x4{uu[0] - acc[4 * q], uu[1] - acc[4 * q + 1], uu[2] - acc[4 * q + 2],
+                                 uu[3] - acc[4 * q + 3]});
+      }
+      phase_barrier();                                  // A: V~ ready
+      phase_barrier();                                  // B: state copy ready
+    });
+  } else if (wid < NI2 + NJ2) {
+    // ================= S: state rows 32 J2 .. of this tile's 32 columns (entry
+    // 4q + e is row 32 J2 + 8q + 4h + e, column r), from [0 | I]
+    const int J2 = wid - NI2;
+    const int pcol = 32 * (tile - nvt) + r;            // P tile: the identity column of this lane
+    u32x4 RK[2][KSC];
+    float RP[2];
+    auto load = [&](int ch, u32x4* X, float& pv) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) X[s] = ld16(l16, cb + RL.kt + J2 * KSC * 1024 + 1024 * s);
+      pv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wrsrc, 4 * r, cb + RL.pic + 128 * J2, 0));
+    };
+    f32x16 Sacc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Sacc[4 * q + e] = (ptile && 32 * J2 + 8 * q + 4 * h + e == pcol) ? 1.f : 0.f;
+    auto st_s0t = [&]() {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        In<__bf16>::store4(S0T + r * LDK + 32 * J2 + 8 * q + 4 * h,
+                           f32x4{Sacc[4 * q], Sacc[4 * q + 1], Sacc[4 * q + 2], Sacc[4 * q + 3]});
+    };
+    st_s0t();
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    const int pbase = 16 * h;
+    load(0, RK[0], RP[0]);
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      load(ch + 1, RK[1 - u], RP[1 - u]);
+      const int pb = __float_as_int(RP[u]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Sacc[4 * q + e] *= __int_as_float(__builtin_amdgcn_ds_bpermute(pbase + 4 * (8 * q + e), pb));
+      phase_barrier();                                  // A
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) Sacc = mma32(RK[u][s], vfrag(s), Sacc);
+      st_s0t();
+      phase_barrier();                                  // B
+    });
+    float* out = Saug + seg_aug_off(sg, bh, BH, DK, DV);
+    const int col = ptile ? DV + pcol : 32 * tile + r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(size_t)(32 * J2 + 8 * q + 4 * h + e) * (DV + DK) + col] = Sacc[4 * q + e];
+  } else {
+    __syncthreads();
+    walk([&](int, auto) { phase_barrier(); phase_barrier(); });
+  }
+}
+
+// Segment start states: per (b, h, 32-column value tile), in segment order,
+// Sseg[g] = S_start(g) and S_start(g + 1) = P_g S_start(g) + Q_g (fp32).
+// Each thread holds a 4 x 4 block of the d_k x 32 tile; P_g and the tile go
+// through LDS.
+template <int DK>
+__global__ __launch_bounds__(256) void gdn2_chunk_seg_combine_kernel(const float* __restrict__ Saug,
+                                                                      const float* __restrict__ S0,
+                                                                      float* __restrict__ Sseg, int DV,
+                                                                      int nseg) {
+  constexpr int NRQ = DK / 4;                          // row quads; 8 column quads
+  static_assert(NRQ * 8 <= 256, "one 4 x 4 block per thread");
+  __shared__ __attribute__((aligned(16))) float Pl[DK][DK + 4];
+  __shared__ __attribute__((aligned(16))) float St[DK][36];
+  const int tid = threadIdx.x;
+  const int nvt = DV / 32;
+  const int bh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
+  const int BH = gridDim.x / nvt;
+  const bool act = tid < NRQ * 8;
+  const int rq = tid >> 3, cq = tid & 7;
+  const int r0 = 4 * rq, c0 = 4 * cq, col = 32 * vt + c0;
+  f32x4 sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    sv[i] = (act && S0) ? *(const f32x4*)(S0 + ((size_t)bh * DK + r0 + i) * DV + col) : f4zero();
+  for (int g = 0; g < nseg; ++g) {
+    float* dst = Sseg + ((size_t)g * BH + bh) * DK * DV;
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(f32x4*)(dst + (size_t)(r0 + i) * DV + col) = sv[i];
+    }
+    if (g == nseg - 1) break;
+    const float* aug = Saug + seg_aug_off(g, bh, BH, DK, DV);
+    __syncthreads();                                   // the previous step's reads of Pl / St are done
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(f32x4*)&St[r0 + i][c0] = sv[i];
+    }
+    for (int x = tid; x < DK * DK / 4; x += 256) {     // P_g: columns DV .. DV + DK of the augmented rows
+      const int rr = x / (DK / 4), cc = 4 * (x % (DK / 4));
+      *(f32x4*)&Pl[rr][cc] = *(const f32x4*)(aug + (size_t)rr * (DV + DK) + DV + cc);
+    }
+    __syncthreads();
+    if (act) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = *(const f32x4*)(aug + (size_t)(r0 + i) * (DV + DK) + col);   // Q_g
+      for (int j4 = 0; j4 < DK; j4 += 4) {
+        f32x4 sr[4], pr[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          sr[x] = *(const f32x4*)&St[j4 + x][c0];
+          pr[x] = *(const f32x4*)&Pl[r0 + x][j4];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] += pr[i][x] * sr[x][e];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = acc[i];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host launch
-size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+// Whether the F-order (fragment-major) record and scan serve these shapes:
+// bf16, d_k, d_v and C multiples of 32, one head's records under 2 GiB.
+static bool fm_path(int dk, int dv, int chunk, int dtype, long long T) {
+  if (dtype != GDR_BF16 || dk % 32 || dv % 32 || chunk % 32) return false;
+  return ((T + chunk - 1) / chunk) * (long long)rec_layout(dk, dv, chunk, 2).bytes < (1LL << 31);
+}
+
+// Segment length (chunks) of the sequence-segmented scan, or 0 for the plain
+// scan. Segments pay only when the (b, h, value tile) workgroups of the plain
+// scan leave most of the GPU's 256 compute units idle and the chunk chain is
+// long: then the chain is cut into nseg segments so that about 256 scan
+// workgroups run side by side, each segment at least 16 chunks long. The
+// plan depends on the shapes alone (the workspace size has to).
+static int seg_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  if (!fm_path(dk, dv, chunk, dtype, T)) return 0;
+  const long long units = (long long)B * H * (dv / 32);
+  const int ntot = (T + chunk - 1) / chunk;
+  if (units * 2 > kSegTargetUnits || ntot < 32) return 0;
+  int nseg = (int)(kSegTargetUnits / units);
+  if (nseg > ntot / 16) nseg = ntot / 16;
+  if (nseg < 2) return 0;
+  return (ntot + nseg - 1) / nseg;
+}
+
+static size_t seg_extra_bytes(int B, int H, int T, int dk, int dv, int chunk, int seg) {
+  const int ntot = (T + chunk - 1) / chunk, nseg = (ntot + seg - 1) / seg;
+  return (size_t)nseg * B * H * dk * ((size_t)(dv + dk) + dv) * 4;
+}
+
+static size_t records_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
   const int es = dtype == GDR_BF16 ? 2 : 4;
   const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
   return (size_t)B * H * nchunks * (size_t)rec_layout(dk, dv, chunk, es).bytes;
+}
+
+size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, bool allow_seg) {
+  size_t n = records_bytes(B, H, T, dk, dv, chunk, dtype);
+  const int seg = allow_seg ? seg_plan(B, H, T, dk, dv, chunk, dtype) : 0;
+  if (seg) n = (n + 255) / 256 * 256 + seg_extra_bytes(B, H, T, dk, dv, chunk, seg);
+  return n;
 }
 
 template <typename Tin, int DK, int CM, bool FM, bool GATED>
@@ -1876,12 +2154,36 @@ static int launch_scan(const ChunkArgs& a, const char* ws) {
 template <int DK, int CM>
 static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
   const void* kern = (const void*)gdn2_chunk_scan_fm_kernel<DK, CM, kScanFmPrefetch, kScanFmSets>;
-  const int nblocks = a.B * a.H * (a.dv / 32);
   const float* S0 = a.S0;
   __bf16* o = (__bf16*)a.o;
   float* So = a.S_out;
   int T = a.T, DV = a.dv;
-  void* args[] = {&ws, &S0, &o, &So, &T, &DV};
+  const int ntot = (T + CM - 1) / CM;
+  const int BH = a.B * a.H;
+  int seg = a.no_seg ? 0 : seg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype);
+  const float* Sseg = nullptr;
+  if (seg) {
+    // segment pass and start states, then every segment's scan from its start
+    const size_t rec = (records_bytes(a.B, a.H, T, DK, a.dv, CM, GDR_BF16) + 255) / 256 * 256;
+    const int nseg = (ntot + seg - 1) / seg;
+    float* Saug = (float*)(const_cast<char*>(ws) + rec);
+    float* Ss = Saug + (size_t)nseg * BH * DK * (a.dv + DK);
+    const int ntile = a.dv / 32 + DK / 32;
+    void* a1[] = {&ws, &Saug, &T, &DV, &seg};
+    hipError_t e = hipLaunchKernel((const void*)gdn2_chunk_seg_state_kernel<DK, CM>, dim3(nseg * BH * ntile),
+                                   dim3(kSegThreads), a1, 0, (hipStream_t)a.stream);
+    if (e != hipSuccess) return GDR_ERR_LAUNCH;
+    int nsg = nseg;
+    void* a2[] = {&Saug, &S0, &Ss, &DV, &nsg};
+    e = hipLaunchKernel((const void*)gdn2_chunk_seg_combine_kernel<DK>, dim3(BH * (a.dv / 32)), dim3(256), a2, 0,
+                        (hipStream_t)a.stream);
+    if (e != hipSuccess) return GDR_ERR_LAUNCH;
+    Sseg = Ss;
+  } else {
+    seg = ntot;
+  }
+  const int nblocks = BH * (a.dv / 32) * ((ntot + seg - 1) / seg);
+  void* args[] = {&ws, &S0, &o, &So, &T, &DV, &seg, &Sseg};
   hipError_t e = hipLaunchKernel(kern, dim3(nblocks), dim3(kScanFmThreads), args, 0, (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
@@ -1897,8 +2199,7 @@ static int launch_pair(const ChunkArgs& a, char* ws, int phases) {
   // scan phases (also as separate calls) take the same one. The F-order scan
   // addresses a head's records with 32-bit offsets.
   if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
-    const long long head_bytes = (long long)((a.T + CM - 1) / CM) * rec_layout(DK, a.dv, CM, 2).bytes;
-    if (a.dv % 32 == 0 && head_bytes < (1LL << 31)) {
+    if (fm_path(DK, a.dv, CM, a.dtype, a.T)) {
       if (phases & 1) {
         const int st = launch_intra<Tin, DK, CM, true>(a, ws);
         if (st != GDR_OK) return st;

@@ -22,6 +22,8 @@ struct ChunkArgs {
   const void* zq = nullptr;
   const float* a_log = nullptr;
   const float* gamma_stat = nullptr;
+  // plain chunk scan even where the sequence-segmented one would be used
+  bool no_seg = false;
 };
 
 struct DecodeArgs {
@@ -48,7 +50,9 @@ struct MlstmArgs {
 
 int chunk_fwd_launch(const ChunkArgs& a);
 // two-kernel form (intra-chunk kernel over all chunks, then the chunk scan)
-size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+// allow_seg: include the buffers of the sequence-segmented scan where the
+// shapes take it (false for callers that launch with no_seg)
+size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, bool allow_seg = true);
 // phases: bit 0 = intra-chunk kernel (writes the workspace), bit 1 = chunk scan
 int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases);
 int decode_launch(const DecodeArgs& a);
