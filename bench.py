@@ -58,7 +58,8 @@ def chunk_bytes(B, H, T, dk, dv, es, s0=False, s_out=True):
 # that file includes): a committed counter reading of that kernel stays valid
 # until one of them changes.
 KERNEL_SOURCES = {
-    "chunk": ("gdr_chunk2.hip", "gdr_chunk_common.hpp", "gdr_device.hpp", "gdr_internal.h", "gdr_host.hpp"),
+    "chunk": ("gdr_chunk2.hip", "gdr_chunk_common.hpp", "gdr_device.hpp", "gdr_internal.h", "gdr_host.hpp",
+              "gdr_record.hpp"),
     "chunk_fused": ("gdr_chunk.hip", "gdr_chunk_common.hpp", "gdr_device.hpp", "gdr_internal.h", "gdr_host.hpp"),
     "decode": ("gdr_decode.hip", "gdr_device.hpp", "gdr_internal.h"),
     "mlstm": ("gdr_mlstm2.hip", "gdr_device.hpp", "gdr_internal.h", "gdr_host.hpp"),

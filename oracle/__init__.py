@@ -11,6 +11,9 @@ Sources (cited by page title and section/equation):
   write, GLA form, chunkwise form), §4.2 stage (i) and eq.(10) (the chunk
   matrix T = I + L_strict and the chunkwise readout and state update, used to
   measure how ill-conditioned the tests' chunk systems are).
+* the same page, §4.2 "Custom Backward Pass": gradients of a scalar loss
+  through eq.(1) (float64 reverse-mode differentiation of the step, pinned by
+  finite differences and closed forms).
 * the same page, §2.1 (gate parameterisation) and §4.1 eq.(8)-(9): the Muir
   gate prologue (gates from logits, readout with the gain-modulated query).
 * "Exponential gates and matrix memory: xLSTM and RWKV-7" — §13.2 (spectrum of
@@ -37,6 +40,7 @@ from .gdn2 import (  # noqa: F401
     gla_closed_form, linear_attention_closed_form, bruteforce_exact,
     gdn2_chunk_system, gdn2_chunkwise, chunk_condition_numbers,
 )
+from .gdn2_grad import gdn2_grad  # noqa: F401
 from .muir import (  # noqa: F401
     muir_gates, muir_recurrent, muir_decode,
 )
