@@ -208,6 +208,26 @@ def bench_muir(steps, warmup):
     return dict(B=B, T=T, region_ms=region_ms, bytes=nbytes)
 
 
+def bench_bwd(steps, warmup, c, x):
+    """gdr_chunk_bwd on the 4K workload (bf16, S0 = 0, dS_T = 0): gradients
+    of every input from dO, once recomputing the forward records and once
+    from records the forward left in the workspace."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv, C = c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    dO = torch.randn((B, H, T, dv), generator=g, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(gdr.gdr_chunk_bwd_workspace_size(B, H, T, dk, dv, C, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    gdr.gdr_chunk_intra(*x, chunk=C, workspace=ws)
+    full, _ = time_launches(lambda: gdr.gdr_chunk_bwd(*x, None, dO, chunk=C, workspace=ws), steps, warmup)
+    gdr.gdr_chunk_intra(*x, chunk=C, workspace=ws)
+    ready, _ = time_launches(lambda: gdr.gdr_chunk_bwd(*x, None, dO, chunk=C, workspace=ws, records_ready=True),
+                             steps, warmup)
+    return dict(B=B, T=T, full_ms=full, ready_ms=ready, ws_bytes=ws.numel())
+
+
 def bench_decode(N, steps=1024):
     """N sequences x 16 heads, d = 128, fp32 states resident in HBM: `steps`
     sequential one-token updates, each with its own inputs (all `steps` input
@@ -391,6 +411,12 @@ def main():
         "kernels": kern,
         "token_heads_per_s": value * r["H"],
     }
+    if not args.no_side:
+        bw = bench_bwd(max(10, args.steps // 4), max(3, args.warmup // 10), c, x)
+        out["backward"] = {"workload": "4K workload, gradients of q, k, v, alpha, b, w and S0 from dO",
+                           "entry": "gdr_chunk_bwd", "ms_per_step": bw["full_ms"],
+                           "ms_per_step_records_ready": bw["ready_ms"],
+                           "tokens/s": bw["B"] * bw["T"] / (bw["full_ms"] * 1e-3), "workspace_bytes": bw["ws_bytes"]}
     del x
     if not args.no_side:
         f_region, f_launch = bench_fused(args.steps, args.warmup, c, chunk_inputs("chunk_4k")[2], None)

@@ -144,6 +144,43 @@ int gdr_chunk_scan(const void* workspace, size_t workspace_bytes,
                    void* stream);
 
 /*
+ * gdr_chunk_bwd_workspace_size, gdr_chunk_bwd — gradients of the chunkwise
+ * forward ("Muir: ...", §4.2 "Custom Backward Pass"): for a scalar loss J with
+ * dO = dJ/do and dS_T = dJ/dS_T, returns dJ/dq, dJ/dk, dJ/dv, dJ/dalpha,
+ * dJ/db, dJ/dw and dJ/dS0 of the recurrence of §2.1 eq.(1).
+ *
+ * The chunk readout and state update of eq.(10) are differentiated with
+ * matrix products, the triangular solve through the transposed solve
+ * d[V^ | K^_pi] = T^{-T} d[U | Y] and dL = -stril(d[V^ | K^_pi] [U | Y]^T),
+ * and the decay-scaled Gram products back to q, k, b and the cumulative
+ * log-decay, whose reverse cumulative sum gives d log alpha (dalpha =
+ * d log alpha / alpha, so alpha must be > 0 here).
+ *
+ *   q, k, v, alpha, b, w, S0   the forward's inputs (as gdr_chunk_fwd; S0 may
+ *                              be NULL for zeros)
+ *   dO        [B,H,T,dv]  input dtype, gradient of the outputs
+ *   dS_T      [B,H,dk,dv] float32 gradient of the final state, or NULL (zero)
+ *   dq, dk, dalpha, db  [B,H,T,dk] float32 outputs
+ *   dv, dw              [B,H,T,dv] float32 outputs
+ *   dS0       [B,H,dk,dv] float32 output, or NULL to skip
+ *   workspace at least gdr_chunk_bwd_workspace_size bytes; it begins with
+ *             the forward's records (the first gdr_chunk_workspace_size
+ *             bytes of the same shapes, records only). records_ready = 1
+ *             when the caller's workspace already holds them for these
+ *             inputs (written by gdr_chunk_intra or gdr_chunk_fwd_ws into
+ *             the same buffer), 0 to recompute them first.
+ * Outputs must not overlap inputs, each other or the workspace. Returns
+ * GDR_OK or a negative GDR_ERR_* code.
+ */
+int gdr_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype, size_t* bytes);
+int gdr_chunk_bwd(const void* q, const void* k, const void* v,
+                  const void* alpha, const void* b, const void* w,
+                  const float* S0, const void* dO, const float* dS_T,
+                  float* dq, float* dk_, float* dv_, float* dalpha, float* db, float* dw, float* dS0,
+                  int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                  void* workspace, size_t workspace_bytes, int records_ready, void* stream);
+
+/*
  * gdr_chunk_fwd_noalloc — gdr_chunk_fwd_ws without a caller workspace and
  * without any allocation, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

@@ -27,6 +27,7 @@ import ctypes
 import os
 
 __all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_fwd_noalloc", "gdr_muir_chunk_fwd_ws",
+           "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
            "gdr_muir_decode_step", "gdr_chunk_workspace_size", "gdr_chunk_intra",
            "gdr_chunk_scan", "gdr_mlstm_fwd_ws", "gdr_mlstm_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
@@ -77,6 +78,10 @@ def load_library():
     lib.gdr_muir_chunk_fwd_ws.restype = I
     lib.gdr_muir_decode_step.argtypes = [P] * 11 + [I] * 5 + [P]
     lib.gdr_muir_decode_step.restype = I
+    lib.gdr_chunk_bwd_workspace_size.argtypes = [I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_bwd_workspace_size.restype = I
+    lib.gdr_chunk_bwd.argtypes = [P] * 16 + [I] * 7 + [P, ctypes.c_size_t, I, P]
+    lib.gdr_chunk_bwd.restype = I
     lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
     lib.gdr_decode_step.restype = I
     lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
@@ -232,6 +237,51 @@ def gdr_chunk_fwd_noalloc(q, k, v, alpha, b, w, S0=None, *, chunk=64, o, S_out=N
                                               _dtype_code(q), _stream(stream))
     _check("gdr_chunk_fwd_noalloc", st)
     return o, S_out
+
+
+def gdr_chunk_bwd_workspace_size(B, H, T, dk, dv, chunk=64, dtype=None) -> int:
+    """Bytes of workspace :func:`gdr_chunk_bwd` needs (dtype: torch dtype, default bf16)."""
+    import torch
+    code = GDR_BF16 if dtype in (None, torch.bfloat16) else GDR_F32 if dtype == torch.float32 else -1
+    n = ctypes.c_size_t(0)
+    st = load_library().gdr_chunk_bwd_workspace_size(int(B), int(H), int(T), int(dk), int(dv), int(chunk),
+                                                     code, ctypes.byref(n))
+    _check("gdr_chunk_bwd_workspace_size", st)
+    return int(n.value)
+
+
+def gdr_chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, chunk=64, workspace=None, records_ready=False,
+                  want_dS0=True, stream=None):
+    """Gradients of the chunkwise forward ("Muir: ...", §4.2 "Custom Backward
+    Pass") for output gradient dO ``[B,H,T,dv]`` (input dtype) and optional
+    final-state gradient dS_T ``[B,H,dk,dv]`` float32. Returns a dict of
+    float32 tensors dq, dk, dv, dalpha, db, dw (shaped like the inputs) and
+    dS0 (``[B,H,dk,dv]``, if ``want_dS0``). ``workspace``: at least
+    :func:`gdr_chunk_bwd_workspace_size` bytes; ``records_ready`` when its
+    leading records were written by the forward for these inputs."""
+    import torch
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("alpha", alpha, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv), ("dO", dO, dv)):
+        _req(t, name, (B, H, T, d), dt, dev)
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _req(t, name, (B, H, dk, dv), torch.float32, dev)
+    need = gdr_chunk_bwd_workspace_size(B, H, T, dk, dv, chunk, dt)
+    workspace = _workspace(workspace, need, dev, stream)
+    with _alloc_on(stream):
+        g = {n: torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+             for n, d in (("dq", dk), ("dk", dk), ("dv", dv), ("dalpha", dk), ("db", dk), ("dw", dv))}
+        g["dS0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    st = load_library().gdr_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T),
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+        _ptr(g["dS0"]), B, H, T, dk, dv, int(chunk), _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), int(bool(records_ready)), _stream(stream))
+    _check("gdr_chunk_bwd", st)
+    return g
 
 
 def _workspace(workspace, need, device, stream=None):

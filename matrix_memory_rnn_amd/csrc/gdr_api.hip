@@ -384,6 +384,48 @@ int gdr_mlstm_fwd_ws(const void* q, const void* k, const void* v, const float* i
 
 }  // extern "C"
 
+// ------------------------------------------------------------------ backward
+extern "C" int gdr_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                                            size_t* bytes) {
+  if (!bytes) return GDR_ERR_NULL;
+  *bytes = 0;
+  int st = check_sizes(B, H, T, dk, dv, dtype, 128);
+  if (st != GDR_OK) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDR_ERR_UNSUPPORTED;
+  *bytes = gdr::chunk_bwd_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  return GDR_OK;
+}
+
+extern "C" int gdr_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* b,
+                             const void* w, const float* S0, const void* dO, const float* dS_T, float* dq,
+                             float* dk_, float* dv_, float* dalpha, float* db, float* dw, float* dS0, int B,
+                             int H, int T, int dk, int dv, int chunk, int dtype, void* workspace,
+                             size_t workspace_bytes, int records_ready, void* stream) {
+  int st = check_chunk_inputs(q, k, v, alpha, b, w, B, H, T, dk, dv, chunk, dtype);
+  if (st != GDR_OK) return st;
+  if (!dO || !dq || !dk_ || !dv_ || !dalpha || !db || !dw || !workspace) return GDR_ERR_NULL;
+  const void* al[] = {S0, dO, dS_T, dq, dk_, dv_, dalpha, db, dw, dS0, workspace};
+  for (const void* p : al)
+    if (!aligned16(p)) return GDR_ERR_ALIGN;
+  const size_t need = gdr::chunk_bwd_ws_bytes(B, H, T, dk, dv, chunk, dtype);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
+  const size_t es = esize(dtype), n = (size_t)B * H * T;
+  const size_t nK = n * dk * es, nV = n * dv * es, nS = (size_t)B * H * dk * dv * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, nK}, {k, nK}, {alpha, nK}, {b, nK}, {v, nV}, {w, nV}, {S0, nS}, {dO, nV}, {dS_T, nS}};
+  const R outs[] = {{dq, n * dk * 4}, {dk_, n * dk * 4}, {dalpha, n * dk * 4}, {db, n * dk * 4},
+                    {dv_, n * dv * 4}, {dw, n * dv * 4}, {dS0, nS}, {workspace, need}};
+  for (const R& x : outs) {
+    for (const R& y : ins)
+      if (overlap(x.p, x.n, y.p, y.n)) return GDR_ERR_ALIAS;
+    for (const R& y : outs)
+      if (x.p != y.p && overlap(x.p, x.n, y.p, y.n)) return GDR_ERR_ALIAS;
+  }
+  gdr::ChunkBwdArgs a{q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk_, dv_, dalpha, db, dw, dS0,
+                      B, H, T, dk, dv, chunk, dtype, stream};
+  return gdr::chunk_bwd_launch(a, workspace, records_ready != 0);
+}
+
 // ------------------------------------------------------------------ no-allocation entry point
 //
 // gdr_chunk_fwd_noalloc runs the two-kernel chunk forward through a scratch

@@ -1,0 +1,718 @@
+// Chunkwise backward of the channel-wise gated delta rule on gfx950.
+//
+// Method: "Muir: Linear Attention with Sensitivity-Allocated Gating and
+// Matched-Filter Readout", §4.2 "Custom Backward Pass": differentiate the
+// chunk readout and state update of eq.(10) with matrix products only, and
+// the triangular solve T [U | Y] = [V^ | K^_pi] through the transposed solve
+// d[V^ | K^_pi] = T^{-T} d[U | Y], dL = -stril(d[V^ | K^_pi] [U | Y]^T),
+// then the decay-scaled Gram products L and M back to q, k, k^ and the
+// cumulative log-decay, and d log alpha as a reverse cumulative sum.
+//
+// Per chunk, from the forward record (Y, U, M, Q_pi, K~, pi_C of the
+// two-kernel forward) and the chunk-start state S0:
+//   V~   = U - Y S0
+//   dV~  = M^T dO + K~ dS_C               (dS_C: gradient of the chunk-end state)
+//   dS0  = Diag(pi_C) dS_C + Q_pi^T dO - Y^T dV~
+//   dU = dV~,  dY = -dV~ S0^T,  dQ_pi = dO S0^T,  dK~ = V~ dS_C^T,
+//   dM = dO V~^T (t >= s),  dpi_C = rowsum(dS_C * S0).
+// Kernels (one launch each, in this order):
+//   bwd_states   per (b, h, 16-column value tile): walks the chunks forward
+//                and stores every chunk-start state (fp32);
+//   bwd_dstates  per (b, h, 16-column value tile): walks the chunks backward
+//                from dS_T and stores every chunk-end state gradient; the
+//                last one is dS0;
+//   bwd_chunk    per (b, h, chunk): the products above over the value tiles,
+//                contractions over d_v accumulated in registers;
+//   bwd_solve    per (b, h, chunk): L from the inputs (fp32, pairwise decays
+//                exp(Lambda_t - Lambda_s), every exponent <= 0), the
+//                transposed unit-triangular solve by back substitution,
+//                dv and dw, and dL;
+//   bwd_decay    per (b, h, chunk, 64 key channels): the key channels are
+//                independent in what is left: dk^, dq, dk from dL and dM
+//                (column and row sums with pairwise decays), the direct
+//                terms of Q_pi, K^_pi, K~ and pi_C, d Lambda, and
+//                d alpha = (reverse cumulative sum of d Lambda) / alpha.
+// Products run on the fp32 matrix cores (16x16x4 fp32 MFMA, operands staged
+// in LDS in fp32), so the backward keeps fp32 precision apart from the bf16
+// record of a bf16 forward.
+#include "gdr_device.hpp"
+#include "gdr_internal.h"
+#include "gdr_host.hpp"
+#include "gdr_record.hpp"
+
+namespace gdr {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel
+
+// One 16 x 16 output tile of A B^T: A [m][k] and B [n][k] fp32 in LDS, k
+// contiguous (pitches lda, ldb in floats, multiples of 4), k in [0, K).
+// Accumulator entry e of a lane is row m0 + 4 (lane / 16) + e, column
+// n0 + lane % 16.
+__device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int m0, const float* B, int ldb,
+                                        int n0, int K, int lane) {
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const Frag<kF32> a = ldfrag<kF32>((const char*)A, 0, lda, m0, k0, K, lane);
+    const Frag<kF32> b = ldfrag<kF32>((const char*)B, 0, ldb, n0, k0, K, lane);
+    mma<kF32>(acc, a, b);
+  }
+}
+
+__device__ __forceinline__ int acc_row(int lane, int e) { return 4 * (lane >> 4) + e; }
+
+// Element reads of one forward record (row-major or F order) as float.
+template <typename E, bool FM>
+struct Rec {
+  const char* p;
+  RecLayout RL;
+  int DK, C;
+  __device__ float at(int base, int elem) const { return (float)((const E*)(p + base))[elem]; }
+  __device__ float y(int t, int j) const { return at(RL.y, FM ? fm_off(t, j, DK) : t * DK + j); }
+  __device__ float qp(int t, int j) const { return at(RL.qp, FM ? fm_off(t, j, DK) : t * DK + j); }
+  // M is lower triangular (t >= s); its other entries are not kept in the record
+  __device__ float m(int t, int s) const { return s > t ? 0.f : at(RL.m, FM ? fm_off(t, s, C) : t * C + s); }
+  __device__ float kt(int j, int s) const { return at(RL.kt, FM ? fm_off(j, s, C) : j * C + s); }   // K~^T
+  __device__ float ut(int v, int t) const { return at(RL.ut, FM ? fu_off(v, t, C) : v * C + t); }  // U^T
+  __device__ float pic(int j) const { return ((const float*)(p + RL.pic))[j]; }
+};
+
+}  // namespace
+
+// Per-(b, h, chunk) buffers of the backward, after the forward records.
+struct BwdLayout {
+  size_t rec, H, dH, dZ, dQp, dKt, dM, dL, dpic, total;
+};
+__host__ __device__ constexpr size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+static BwdLayout bwd_layout(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  const size_t BH = (size_t)B * H, nch = ((size_t)T + chunk - 1) / chunk, n = BH * nch;
+  const int es = dtype == GDR_BF16 ? 2 : 4;
+  BwdLayout L;
+  L.rec = 0;
+  L.H = a256(n * rec_layout(dk, dv, chunk, es).bytes);
+  L.dH = L.H + a256(n * dk * dv * 4);
+  L.dZ = L.dH + a256(n * dk * dv * 4);
+  L.dQp = L.dZ + a256(n * chunk * (size_t)(dv + dk) * 4);
+  L.dKt = L.dQp + a256(n * chunk * dk * 4);
+  L.dM = L.dKt + a256(n * chunk * dk * 4);
+  L.dL = L.dM + a256(n * chunk * chunk * 4);
+  L.dpic = L.dL + a256(n * chunk * chunk * 4);
+  L.total = L.dpic + a256(n * dk * 4);
+  return L;
+}
+size_t chunk_bwd_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  return bwd_layout(B, H, T, dk, dv, chunk, dtype).total;
+}
+
+// ------------------------------------------------------------------ chunk-start states
+template <typename E, int DK, int CM, bool FM>
+__global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_states_kernel(const char* __restrict__ ws,
+                                                                       const float* __restrict__ S0,
+                                                                       float* __restrict__ Hs, int T, int DV) {
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* Yl = (float*)smem;          // Y     [t][j]
+  float* KTl = Yl + CM * LY;         // K~^T  [j][s]
+  float* STl = KTl + DK * LC;        // S^T   [v][j]
+  float* VTl = STl + kVT * LY;       // V~^T  [v][s]
+  float* Ul = VTl + kVT * LC;        // U     [t][v]
+  float* PIl = Ul + CM * kVT;        // pi_C  [j]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nvt = DV / kVT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kVT;
+  const int nch = (T + CM - 1) / CM;
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
+  const int vl = lane & 15;
+  f32x4 S[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int J = wid + 4 * i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * J + acc_row(lane, e);
+      S[i][e] = (J < NST && S0) ? S0[((size_t)bh * DK + row) * DV + v0 + vl] : 0.f;
+    }
+  }
+  for (int c = 0; c < nch; ++c) {
+    const Rec<E, FM> R{ws + ((size_t)bh * nch + c) * RL.bytes, RL, DK, CM};
+    float* Hc = Hs + ((size_t)bh * nch + c) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * J + acc_row(lane, e);
+          Hc[(size_t)row * DV + v0 + vl] = S[i][e];
+          STl[vl * LY + row] = S[i][e];
+        }
+      }
+    }
+    for (int x = tid; x < CM * DK; x += kBwdThreads) Yl[(x / DK) * LY + x % DK] = R.y(x / DK, x % DK);
+    for (int x = tid; x < DK * CM; x += kBwdThreads) KTl[(x / CM) * LC + x % CM] = R.kt(x / CM, x % CM);
+    for (int x = tid; x < CM * kVT; x += kBwdThreads) Ul[x] = R.ut(v0 + x % kVT, x / kVT);
+    for (int j = tid; j < DK; j += kBwdThreads) PIl[j] = R.pic(j);
+    __syncthreads();
+    // V~ = U - Y S
+    for (int it = wid; it < CM / 16; it += 4) {
+      f32x4 acc = f4zero();
+      tile_nt(acc, Yl, LY, 16 * it, STl, LY, 0, DK, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * it + acc_row(lane, e);
+        VTl[vl * LC + t] = Ul[t * kVT + vl] - acc[e];
+      }
+    }
+    __syncthreads();
+    // S <- Diag(pi_C) S + K~^T V~
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[i][e] *= PIl[16 * J + acc_row(lane, e)];
+        tile_nt(S[i], KTl, LC, 16 * J, VTl, LC, 0, CM, lane);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ chunk-end state gradients
+template <typename E, int DK, int CM, bool FM>
+__global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const char* __restrict__ ws,
+                                                                        const E* __restrict__ dO,
+                                                                        const float* __restrict__ dST,
+                                                                        float* __restrict__ dHs,
+                                                                        float* __restrict__ dS0, int T, int DV) {
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* MTl = (float*)smem;         // M^T    [s][t]
+  float* Kl = MTl + CM * LC;         // K~     [s][j]
+  float* QTl = Kl + CM * LY;         // Q_pi^T [j][t]
+  float* YTl = QTl + DK * LC;        // Y^T    [j][t]
+  float* DOTl = YTl + DK * LC;       // dO^T   [v][t]
+  float* DSTl = DOTl + kVT * LC;     // dS^T   [v][j]
+  float* DVTl = DSTl + kVT * LY;     // dV~^T  [v][s]
+  float* PIl = DVTl + kVT * LC;      // pi_C   [j]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nvt = DV / kVT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kVT;
+  const int nch = (T + CM - 1) / CM;
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
+  const int vl = lane & 15;
+  f32x4 D[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int J = wid + 4 * i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * J + acc_row(lane, e);
+      D[i][e] = (J < NST && dST) ? dST[((size_t)bh * DK + row) * DV + v0 + vl] : 0.f;
+    }
+  }
+  for (int c = nch - 1; c >= 0; --c) {
+    const Rec<E, FM> R{ws + ((size_t)bh * nch + c) * RL.bytes, RL, DK, CM};
+    float* dHc = dHs + ((size_t)bh * nch + c) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * J + acc_row(lane, e);
+          dHc[(size_t)row * DV + v0 + vl] = D[i][e];
+          DSTl[vl * LY + row] = D[i][e];
+        }
+      }
+    }
+    const int t0 = c * CM;
+    for (int x = tid; x < CM * CM; x += kBwdThreads) MTl[(x % CM) * LC + x / CM] = R.m(x / CM, x % CM);
+    for (int x = tid; x < DK * CM; x += kBwdThreads) Kl[(x % CM) * LY + x / CM] = R.kt(x / CM, x % CM);
+    for (int x = tid; x < CM * DK; x += kBwdThreads) {
+      const int t = x / DK, j = x % DK;
+      QTl[j * LC + t] = R.qp(t, j);
+      YTl[j * LC + t] = R.y(t, j);
+    }
+    for (int x = tid; x < CM * kVT; x += kBwdThreads) {
+      const int t = x / kVT, v = x % kVT;
+      DOTl[v * LC + t] = t0 + t < T ? (float)dO[((size_t)bh * T + t0 + t) * DV + v0 + v] : 0.f;
+    }
+    for (int j = tid; j < DK; j += kBwdThreads) PIl[j] = R.pic(j);
+    __syncthreads();
+    // dV~ = M^T dO + K~ dS
+    for (int it = wid; it < CM / 16; it += 4) {
+      f32x4 acc = f4zero();
+      tile_nt(acc, MTl, LC, 16 * it, DOTl, LC, 0, CM, lane);
+      tile_nt(acc, Kl, LY, 16 * it, DSTl, LY, 0, DK, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DVTl[vl * LC + 16 * it + acc_row(lane, e)] = acc[e];
+    }
+    __syncthreads();
+    // dS <- Diag(pi_C) dS + Q_pi^T dO - Y^T dV~
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[i][e] *= PIl[16 * J + acc_row(lane, e)];
+        tile_nt(D[i], QTl, LC, 16 * J, DOTl, LC, 0, CM, lane);
+        f32x4 yv = f4zero();
+        tile_nt(yv, YTl, LC, 16 * J, DVTl, LC, 0, CM, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[i][e] -= yv[e];
+      }
+    }
+    __syncthreads();
+  }
+  if (dS0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS0[((size_t)bh * DK + 16 * J + acc_row(lane, e)) * DV + v0 + vl] = D[i][e];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ per-chunk state-side gradients
+template <typename E, int DK, int CM, bool FM>
+__global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
+    const char* __restrict__ ws, const float* __restrict__ Hs, const float* __restrict__ dHs,
+    const E* __restrict__ dO, float* __restrict__ dZ, float* __restrict__ dQp, float* __restrict__ dKt,
+    float* __restrict__ dMb, float* __restrict__ dpic, int T, int DV) {
+  constexpr int LY = DK + 4, LC = CM + 4, L16 = kVT + 4;
+  constexpr int NYT = (CM / 16) * (DK / 16), NMT = (CM / 16) * (CM / 16);
+  constexpr int PY = (NYT + 3) / 4, PM = (NMT + 3) / 4;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* Yl = (float*)smem;          // Y     [t][j]
+  float* MTl = Yl + CM * LY;         // M^T   [s][t]
+  float* Kl = MTl + CM * LC;         // K~    [s][j]
+  float* S0l = Kl + CM * LY;         // S0    [j][v]
+  float* S0Tl = S0l + DK * L16;      // S0^T  [v][j]
+  float* dSl = S0Tl + kVT * LY;      // dS    [j][v]
+  float* dSTl = dSl + DK * L16;      // dS^T  [v][j]
+  float* dOl = dSTl + kVT * LY;      // dO    [t][v]
+  float* dOTl = dOl + CM * L16;      // dO^T  [v][t]
+  float* Vl = dOTl + kVT * LC;       // V~    [s][v]
+  float* dVl = Vl + CM * L16;        // dV~   [t][v]
+  float* Ul = dVl + CM * L16;        // U     [t][v]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nch = (T + CM - 1) / CM;
+  const int bh = blockIdx.x / nch, c = blockIdx.x % nch, t0 = c * CM;
+  const size_t item = (size_t)bh * nch + c;
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
+  const Rec<E, FM> R{ws + item * RL.bytes, RL, DK, CM};
+  const float* Hc = Hs + item * DK * DV;
+  const float* dHc = dHs + item * DK * DV;
+  float* dZc = dZ + item * CM * (DV + DK);
+  const int vl = lane & 15;
+  for (int x = tid; x < CM * DK; x += kBwdThreads) Yl[(x / DK) * LY + x % DK] = R.y(x / DK, x % DK);
+  for (int x = tid; x < CM * CM; x += kBwdThreads) MTl[(x % CM) * LC + x / CM] = R.m(x / CM, x % CM);
+  for (int x = tid; x < DK * CM; x += kBwdThreads) Kl[(x % CM) * LY + x / CM] = R.kt(x / CM, x % CM);
+  f32x4 aY[PY], aQ[PY], aK[PY], aM[PM];
+#pragma unroll
+  for (int i = 0; i < PY; ++i) aY[i] = aQ[i] = aK[i] = f4zero();
+#pragma unroll
+  for (int i = 0; i < PM; ++i) aM[i] = f4zero();
+  float pacc = 0.f;
+  for (int v0 = 0; v0 < DV; v0 += kVT) {
+    for (int x = tid; x < DK * kVT; x += kBwdThreads) {
+      const int j = x / kVT, v = x % kVT;
+      const float s0 = Hc[(size_t)j * DV + v0 + v], ds = dHc[(size_t)j * DV + v0 + v];
+      S0l[j * L16 + v] = s0;
+      S0Tl[v * LY + j] = s0;
+      dSl[j * L16 + v] = ds;
+      dSTl[v * LY + j] = ds;
+    }
+    for (int x = tid; x < CM * kVT; x += kBwdThreads) {
+      const int t = x / kVT, v = x % kVT;
+      const float g = t0 + t < T ? (float)dO[((size_t)bh * T + t0 + t) * DV + v0 + v] : 0.f;
+      dOl[t * L16 + v] = g;
+      dOTl[v * LC + t] = g;
+      Ul[t * kVT + v] = R.ut(v0 + v, t);
+    }
+    __syncthreads();
+    for (int it = wid; it < CM / 16; it += 4) {
+      f32x4 acc = f4zero();
+      tile_nt(acc, Yl, LY, 16 * it, S0Tl, LY, 0, DK, lane);             // Y S0
+      f32x4 dv = f4zero();
+      tile_nt(dv, MTl, LC, 16 * it, dOTl, LC, 0, CM, lane);             // M^T dO
+      tile_nt(dv, Kl, LY, 16 * it, dSTl, LY, 0, DK, lane);              // + K~ dS
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * it + acc_row(lane, e);
+        Vl[t * L16 + vl] = Ul[t * kVT + vl] - acc[e];
+        dVl[t * L16 + vl] = dv[e];
+        dZc[(size_t)t * (DV + DK) + v0 + vl] = dv[e];                    // dU
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PY; ++i) {
+      const int p = wid + 4 * i;
+      if (p < NYT) {
+        const int ti = p / (DK / 16), tj = p % (DK / 16);
+        tile_nt(aY[i], dVl, L16, 16 * ti, S0l, L16, 16 * tj, kVT, lane);   // dV~ S0^T
+        tile_nt(aQ[i], dOl, L16, 16 * ti, S0l, L16, 16 * tj, kVT, lane);   // dO S0^T
+        tile_nt(aK[i], Vl, L16, 16 * ti, dSl, L16, 16 * tj, kVT, lane);    // V~ dS^T
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      const int p = wid + 4 * i;
+      if (p < NMT) tile_nt(aM[i], dOl, L16, 16 * (p / (CM / 16)), Vl, L16, 16 * (p % (CM / 16)), kVT, lane);
+    }
+    if (tid < DK) {
+#pragma unroll
+      for (int v = 0; v < kVT; ++v) pacc += dSl[tid * L16 + v] * S0l[tid * L16 + v];
+    }
+    __syncthreads();
+  }
+  float* dQc = dQp + item * CM * DK;
+  float* dKc = dKt + item * CM * DK;
+  float* dMc = dMb + item * CM * CM;
+#pragma unroll
+  for (int i = 0; i < PY; ++i) {
+    const int p = wid + 4 * i;
+    if (p < NYT) {
+      const int ti = p / (DK / 16), tj = p % (DK / 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ti + acc_row(lane, e), j = 16 * tj + vl;
+        dZc[(size_t)t * (DV + DK) + DV + j] = -aY[i][e];                  // dY
+        dQc[t * DK + j] = aQ[i][e];
+        dKc[t * DK + j] = aK[i][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PM; ++i) {
+    const int p = wid + 4 * i;
+    if (p < NMT) {
+      const int ti = p / (CM / 16), si = p % (CM / 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ti + acc_row(lane, e), s = 16 * si + vl;
+        dMc[t * CM + s] = s <= t ? aM[i][e] : 0.f;
+      }
+    }
+  }
+  if (tid < DK) dpic[item * DK + tid] = pacc;
+}
+
+// ------------------------------------------------------------------ transposed solve, dv, dw, dL
+// Chunk rows past T are identity padding (alpha = 1, k = b = 0).
+template <typename E, int DK, int CM, bool FM>
+__global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
+    const E* __restrict__ k, const E* __restrict__ alpha, const E* __restrict__ bgate, const E* __restrict__ v,
+    const E* __restrict__ wgate, const char* __restrict__ ws, float* __restrict__ dZ, float* __restrict__ dL,
+    float* __restrict__ dv_out, float* __restrict__ dw_out, int T, int DV) {
+  constexpr int LP = DK + 1, LL = CM + 1;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* Ll = (float*)smem;               // L [t][s]
+  float* U0 = Ll + a256(CM * LL * 4) / 4; // union: phase 1 (Lam, Kl, KHl) / phase 2 (Xl, Zl)
+  float* Lam = U0;                        // Lambda [t][j] (pitch LP)
+  float* Kl = Lam + CM * LP;              // k      [t][j]
+  float* KHl = Kl + CM * LP;              // b * k  [t][j]
+  const int NX = DV + DK + 4;             // X and Z row pitch
+  float* Xl = U0;                         // d[V^ | K^_pi] [t][c]
+  float* Zl = Xl + CM * NX;               // [U | Y]       [s][c]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nch = (T + CM - 1) / CM;
+  const int bh = blockIdx.x / nch, c = blockIdx.x % nch, t0 = c * CM;
+  const size_t item = (size_t)bh * nch + c;
+  const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
+  for (int x = tid; x < CM * DK; x += kBwdThreads) {
+    const int t = x / DK, j = x % DK;
+    const bool ok = t0 + t < T;
+    const size_t off = sK + (size_t)(t0 + t) * DK + j;
+    const float a = ok ? (float)alpha[off] : 1.f, kk = ok ? (float)k[off] : 0.f, bb = ok ? (float)bgate[off] : 0.f;
+    Lam[t * LP + j] = logf(a);
+    Kl[t * LP + j] = kk;
+    KHl[t * LP + j] = bb * kk;
+  }
+  __syncthreads();
+  for (int j = tid; j < DK; j += kBwdThreads) {   // Lambda_t = sum_{r <= t} log alpha_r
+    float acc = 0.f;
+    for (int t = 0; t < CM; ++t) {
+      acc += Lam[t * LP + j];
+      Lam[t * LP + j] = acc;
+    }
+  }
+  __syncthreads();
+  // L[t][s] = sum_j k^_t[j] k_s[j] exp(Lambda_t[j] - Lambda_s[j]), t > s
+  for (int p = tid; p < CM * CM; p += kBwdThreads) {
+    const int t = p / CM, s = p % CM;
+    float acc = 0.f;
+    if (s < t) {
+      for (int j = 0; j < DK; ++j)
+        acc += KHl[t * LP + j] * Kl[s * LP + j] * __expf(Lam[t * LP + j] - Lam[s * LP + j]);
+    }
+    Ll[t * LL + s] = acc;
+  }
+  __syncthreads();
+  // T^T X = dZ column by column: x_t = dz_t - sum_{s > t} L[s][t] x_s (rows from the last)
+  float* dZc = dZ + item * CM * (DV + DK);
+  const int col = tid;
+  if (col < DV + DK) {
+    float x[CM];
+#pragma unroll
+    for (int t = 0; t < CM; ++t) x[t] = dZc[(size_t)t * (DV + DK) + col];
+#pragma unroll
+    for (int t = CM - 1; t >= 0; --t) {
+      float acc = x[t];
+#pragma unroll
+      for (int s = t + 1; s < CM; ++s) acc -= Ll[s * LL + t] * x[s];
+      x[t] = acc;
+    }
+    // the phase-1 area is dead once every thread has passed the L products
+    // above (the barrier before the solve); X goes there
+#pragma unroll
+    for (int t = 0; t < CM; ++t) {
+      Xl[t * NX + col] = x[t];
+      dZc[(size_t)t * (DV + DK) + col] = x[t];
+    }
+    if (col < DV) {   // dV^: dv = dV^ * w, dw = dV^ * v
+#pragma unroll
+      for (int t = 0; t < CM; ++t) {
+        if (t0 + t < T) {
+          const size_t off = sV + (size_t)(t0 + t) * DV + col;
+          dv_out[off] = x[t] * (float)wgate[off];
+          dw_out[off] = x[t] * (float)v[off];
+        }
+      }
+    }
+  }
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
+  const Rec<E, FM> R{ws + item * RL.bytes, RL, DK, CM};
+  for (int x = tid; x < CM * (DV + DK); x += kBwdThreads) {
+    const int s = x / (DV + DK), cc = x % (DV + DK);
+    Zl[s * NX + cc] = cc < DV ? R.ut(cc, s) : R.y(s, cc - DV);
+  }
+  __syncthreads();
+  // dL = -stril(X Z^T)
+  float* dLc = dL + item * CM * CM;
+  constexpr int NT = CM / 16;
+  for (int p = wid; p < NT * NT; p += 4) {
+    const int ti = p / NT, si = p % NT;
+    f32x4 acc = f4zero();
+    if (si <= ti) tile_nt(acc, Xl, NX, 16 * ti, Zl, NX, 16 * si, DV + DK, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * ti + acc_row(lane, e), s = 16 * si + (lane & 15);
+      dLc[t * CM + s] = s < t ? -acc[e] : 0.f;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decay and key/query gradients
+// One wave per (b, h, chunk, 64 key channels); lane = channel. Per channel,
+// with e_ts = exp(Lambda_t - Lambda_s) (t >= s):
+//   dk^_t = sum_{s<t} dL_ts e_ts k_s + pi_t dK^_pi_t
+//   dq_t  = sum_{s<=t} dM_ts e_ts k_s + pi_t dQ_pi_t
+//   dk_s  = sum_{t>s} dL_ts e_ts k^_t + sum_{t>=s} dM_ts e_ts q_t + pi_{C,s} dK~_s
+//   dLambda_t = k^_t dk^_t + q_t dq_t - k_t (dk_t without the K~ term)
+//               - k_t pi_{C,t} dK~_t, and at t = C-1 also + sum_s k_s pi_{C,s} dK~_s
+//               + pi_C dpi_C
+//   dalpha_r = (sum_{t >= r} dLambda_t) / alpha_r,  db = k dk^,  dk += b dk^.
+template <typename E, int DK, int CM>
+__global__ __launch_bounds__(64) void gdn2_bwd_decay_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ alpha, const E* __restrict__ bgate,
+    const float* __restrict__ dZ, const float* __restrict__ dQp, const float* __restrict__ dKt,
+    const float* __restrict__ dMb, const float* __restrict__ dLb, const float* __restrict__ dpic,
+    float* __restrict__ dq_out, float* __restrict__ dk_out, float* __restrict__ da_out,
+    float* __restrict__ db_out, int T, int DV) {
+  constexpr int NG = (DK + 63) / 64;
+  __shared__ float Lam[CM][64], Kc[CM][64], KHc[CM][64], Qc[CM][64], DKH[CM][64], DLam[CM][64];
+  const int lane = threadIdx.x;
+  const int nch = (T + CM - 1) / CM;
+  const int grp = blockIdx.x % NG, item_i = blockIdx.x / NG;
+  const int bh = item_i / nch, c = item_i % nch, t0 = c * CM;
+  const size_t item = (size_t)bh * nch + c;
+  const int j = 64 * grp + lane;
+  const bool act = j < DK;
+  const int jj = act ? j : 0;
+  const size_t sK = (size_t)bh * T * DK;
+  {
+    float acc = 0.f;
+    for (int t = 0; t < CM; ++t) {
+      const bool ok = t0 + t < T;
+      const size_t off = sK + (size_t)(t0 + t) * DK + jj;
+      const float a = ok ? (float)alpha[off] : 1.f, kk = ok ? (float)k[off] : 0.f;
+      const float bb = ok ? (float)bgate[off] : 0.f, qq = ok ? (float)q[off] : 0.f;
+      acc += logf(a);
+      Lam[t][lane] = acc;
+      Kc[t][lane] = kk;
+      KHc[t][lane] = bb * kk;
+      Qc[t][lane] = qq;
+    }
+  }
+  const float* dLc = dLb + item * CM * CM;
+  const float* dMc = dMb + item * CM * CM;
+  const float* dZc = dZ + item * CM * (DV + DK);
+  const float* dQc = dQp + item * CM * DK;
+  const float* dKc = dKt + item * CM * DK;
+  // rows: dk^_t, dq_t and the row side of dLambda
+  for (int t = 0; t < CM; ++t) {
+    const float lt = Lam[t][lane];
+    float dkh = 0.f, dq = 0.f;
+    for (int s = 0; s <= t; ++s) {
+      const float ek = __expf(lt - Lam[s][lane]) * Kc[s][lane];
+      dq += dMc[t * CM + s] * ek;
+      if (s < t) dkh += dLc[t * CM + s] * ek;
+    }
+    const float pt = __expf(lt);
+    dq += pt * dQc[t * DK + jj];
+    dkh += pt * dZc[(size_t)t * (DV + DK) + DV + jj];
+    DKH[t][lane] = dkh;
+    DLam[t][lane] = KHc[t][lane] * dkh + Qc[t][lane] * dq;
+    if (act && t0 + t < T) dq_out[sK + (size_t)(t0 + t) * DK + j] = dq;
+  }
+  // columns: dk_s and the column side of dLambda
+  const float lC = Lam[CM - 1][lane];
+  float gK = 0.f;
+  for (int s = 0; s < CM; ++s) {
+    const float ls = Lam[s][lane];
+    float dk = 0.f;
+    for (int t = s; t < CM; ++t) {
+      const float e = __expf(Lam[t][lane] - ls);
+      float g = dMc[t * CM + s] * Qc[t][lane];
+      if (t > s) g += dLc[t * CM + s] * KHc[t][lane];
+      dk += e * g;
+    }
+    const float ks = Kc[s][lane];
+    const float kt = __expf(lC - ls) * dKc[s * DK + jj];   // pi_{C,s} dK~_s
+    DLam[s][lane] -= ks * (dk + kt);
+    gK += ks * kt;
+    dk += kt;
+    const float dkh = DKH[s][lane];
+    const size_t off = sK + (size_t)(t0 + s) * DK + j;
+    if (act && t0 + s < T) {
+      const float bb = (float)bgate[off];
+      dk_out[off] = dk + bb * dkh;
+      db_out[off] = ks * dkh;
+    }
+  }
+  DLam[CM - 1][lane] += gK + __expf(lC) * dpic[item * DK + jj];
+  float acc = 0.f;
+  for (int t = CM - 1; t >= 0; --t) {
+    acc += DLam[t][lane];
+    if (act && t0 + t < T) {
+      const size_t off = sK + (size_t)(t0 + t) * DK + j;
+      da_out[off] = acc / (float)alpha[off];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host launch
+template <typename E, int DK, int CM, bool FM>
+static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
+  const BwdLayout BL = bwd_layout(a.B, a.H, a.T, DK, a.dv, CM, a.dtype);
+  const int BH = a.B * a.H, nch = (a.T + CM - 1) / CM;
+  int DV = a.dv, T = a.T;
+  float* Hs = (float*)(ws + BL.H);
+  float* dHs = (float*)(ws + BL.dH);
+  float* dZ = (float*)(ws + BL.dZ);
+  float* dQp = (float*)(ws + BL.dQp);
+  float* dKt = (float*)(ws + BL.dKt);
+  float* dM = (float*)(ws + BL.dM);
+  float* dL = (float*)(ws + BL.dL);
+  float* dpic = (float*)(ws + BL.dpic);
+  const hipStream_t st = (hipStream_t)a.stream;
+  const char* wsc = ws;
+  constexpr int LY = DK + 4, LC = CM + 4, L16 = kVT + 4;
+  {
+    const int lds = 4 * (CM * LY + DK * LC + kVT * LY + kVT * LC + CM * kVT + DK);
+    auto kern = gdn2_bwd_states_kernel<E, DK, CM, FM>;
+    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const float* S0 = a.S0;
+    void* args[] = {&wsc, &S0, &Hs, &T, &DV};
+    if (hipLaunchKernel((const void*)kern, dim3(BH * (DV / kVT)), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    const int lds = 4 * (CM * LC + CM * LY + 2 * DK * LC + kVT * LC + kVT * LY + kVT * LC + DK);
+    auto kern = gdn2_bwd_dstates_kernel<E, DK, CM, FM>;
+    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const E* dO = (const E*)a.dO;
+    const float* dST = a.dS_T;
+    float* dS0 = a.dS0;
+    void* args[] = {&wsc, &dO, &dST, &dHs, &dS0, &T, &DV};
+    if (hipLaunchKernel((const void*)kern, dim3(BH * (DV / kVT)), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    const int lds = 4 * (2 * CM * LY + CM * LC + 2 * DK * L16 + 2 * kVT * LY + 3 * CM * L16 + kVT * LC +
+                         CM * kVT);
+    auto kern = gdn2_bwd_chunk_kernel<E, DK, CM, FM>;
+    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const E* dO = (const E*)a.dO;
+    const float *Hc = Hs, *dHc = dHs;
+    void* args[] = {&wsc, &Hc, &dHc, &dO, &dZ, &dQp, &dKt, &dM, &dpic, &T, &DV};
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    const int p1 = 3 * CM * (DK + 1), p2 = 2 * CM * (DV + DK + 4);
+    const int lds = (int)a256(CM * (CM + 1) * 4) + 4 * (p1 > p2 ? p1 : p2);
+    auto kern = gdn2_bwd_solve_kernel<E, DK, CM, FM>;
+    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const E *k = (const E*)a.k, *al = (const E*)a.alpha, *bg = (const E*)a.b, *v = (const E*)a.v,
+            *wg = (const E*)a.w;
+    float *dv = a.dv_out, *dw = a.dw_out;
+    void* args[] = {&k, &al, &bg, &v, &wg, &wsc, &dZ, &dL, &dv, &dw, &T, &DV};
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    auto kern = gdn2_bwd_decay_kernel<E, DK, CM>;
+    const E *q = (const E*)a.q, *k = (const E*)a.k, *al = (const E*)a.alpha, *bg = (const E*)a.b;
+    const float *cdZ = dZ, *cdQ = dQp, *cdK = dKt, *cdM = dM, *cdL = dL, *cpi = dpic;
+    float *dq = a.dq_out, *dk = a.dk_out, *da = a.dalpha_out, *db = a.db_out;
+    void* args[] = {&q, &k, &al, &bg, &cdZ, &cdQ, &cdK, &cdM, &cdL, &cpi, &dq, &dk, &da, &db, &T, &DV};
+    const int ng = (DK + 63) / 64;
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch * ng), dim3(64), args, 0, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  return GDR_OK;
+}
+
+template <typename E, int CM>
+static int bwd_dk(const ChunkBwdArgs& a, char* ws) {
+  const bool fm = fm_path(a.dk, a.dv, CM, a.dtype, a.T);
+  switch (a.dk) {
+    case 16: return bwd_launch_t<E, 16, CM, false>(a, ws);
+    case 32: return fm ? bwd_launch_t<E, 32, CM, std::is_same<E, __bf16>::value>(a, ws)
+                       : bwd_launch_t<E, 32, CM, false>(a, ws);
+    case 64: return fm ? bwd_launch_t<E, 64, CM, std::is_same<E, __bf16>::value>(a, ws)
+                       : bwd_launch_t<E, 64, CM, false>(a, ws);
+    case 128: return fm ? bwd_launch_t<E, 128, CM, std::is_same<E, __bf16>::value>(a, ws)
+                        : bwd_launch_t<E, 128, CM, false>(a, ws);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+template <typename E>
+static int bwd_chunk(const ChunkBwdArgs& a, char* ws) {
+  switch (a.chunk) {
+    case 16: return bwd_dk<E, 16>(a, ws);
+    case 32: return bwd_dk<E, 32>(a, ws);
+    case 64: return bwd_dk<E, 64>(a, ws);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+int chunk_bwd_launch(const ChunkBwdArgs& a, void* ws, bool records_ready) {
+  if (!records_ready) {
+    // the forward records (the intra-chunk kernel of the two-kernel forward)
+    ChunkArgs f{a.q, a.k, a.v, a.alpha, a.b, a.w, nullptr, nullptr, nullptr, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
+                a.dtype, a.stream};
+    const int st = chunk_fwd_ws_launch(f, ws, 1);
+    if (st != GDR_OK) return st;
+  }
+  return a.dtype == GDR_BF16 ? bwd_chunk<__bf16>(a, (char*)ws) : bwd_chunk<float>(a, (char*)ws);
+}
+
+}  // namespace gdr

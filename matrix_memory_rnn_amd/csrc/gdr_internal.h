@@ -39,6 +39,16 @@ struct DecodeArgs {
   const float* gamma_stat = nullptr;
 };
 
+struct ChunkBwdArgs {
+  const void *q, *k, *v, *alpha, *b, *w;
+  const float* S0;
+  const void* dO;
+  const float* dS_T;
+  float *dq_out, *dk_out, *dv_out, *dalpha_out, *db_out, *dw_out, *dS0;
+  int B, H, T, dk, dv, chunk, dtype;
+  void* stream;
+};
+
 struct MlstmArgs {
   const void *q, *k, *v;
   const float *i_tilde, *f_tilde, *C0, *n0, *m0;
@@ -55,6 +65,10 @@ int chunk_fwd_launch(const ChunkArgs& a);
 size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype, bool allow_seg = true);
 // phases: bit 0 = intra-chunk kernel (writes the workspace), bit 1 = chunk scan
 int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases);
+// chunkwise backward: workspace = the forward records, then the backward's
+// own buffers; records_ready skips recomputing the records
+size_t chunk_bwd_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+int chunk_bwd_launch(const ChunkBwdArgs& a, void* ws, bool records_ready);
 int decode_launch(const DecodeArgs& a);
 int mlstm_launch(const MlstmArgs& a);
 // two-kernel form (intra-chunk kernel over all chunks, then the chunk scan)
