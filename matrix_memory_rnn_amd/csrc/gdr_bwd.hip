@@ -76,6 +76,43 @@ struct Rec {
   __device__ float kt(int j, int s) const { return at(RL.kt, FM ? fm_off(j, s, C) : j * C + s); }   // K~^T
   __device__ float ut(int v, int t) const { return at(RL.ut, FM ? fu_off(v, t, C) : v * C + t); }  // U^T
   __device__ float pic(int j) const { return ((const float*)(p + RL.pic))[j]; }
+  // n (4 or 8) consecutive elements from element `elem` (a multiple of n) of
+  // the matrix at byte offset `base`, as floats: one 8- or 16-byte load (two
+  // for fp32 rows of 8)
+  template <int N>
+  __device__ void run(int base, int elem, float* o) const {
+    const E* src = (const E*)(p + base) + elem;
+    if constexpr (std::is_same<E, __bf16>::value) {
+      if constexpr (N == 8) {
+        const u32x4 w = *(const u32x4*)src;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[2 * i] = Raw<__bf16>::lo(w[i]); o[2 * i + 1] = Raw<__bf16>::hi(w[i]); }
+      } else {
+        typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+        const u2 w = *(const u2*)src;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) { o[2 * i] = Raw<__bf16>::lo(w[i]); o[2 * i + 1] = Raw<__bf16>::hi(w[i]); }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        const f32x4 w = *(const f32x4*)(src + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[i + e] = w[e];
+      }
+    }
+  }
+  // rows of 8 along the contraction index
+  __device__ void y8(int t, int j0, float* o) const { run<8>(RL.y, FM ? fm_off(t, j0, DK) : t * DK + j0, o); }
+  __device__ void qp8(int t, int j0, float* o) const { run<8>(RL.qp, FM ? fm_off(t, j0, DK) : t * DK + j0, o); }
+  __device__ void kt8(int j, int s0, float* o) const { run<8>(RL.kt, FM ? fm_off(j, s0, C) : j * C + s0, o); }
+  __device__ void m8(int t, int s0, float* o) const {
+    run<8>(RL.m, FM ? fm_off(t, s0, C) : t * C + s0, o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = s0 + i > t ? 0.f : o[i];
+  }
+  // U^T[v][t0 .. t0+3]
+  __device__ void ut4(int v, int t0, float* o) const { run<4>(RL.ut, FM ? fu_off(v, t0, C) : v * C + t0, o); }
 };
 
 }  // namespace
@@ -148,9 +185,27 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_states_kernel(const char
         }
       }
     }
-    for (int x = tid; x < CM * DK; x += kBwdThreads) Yl[(x / DK) * LY + x % DK] = R.y(x / DK, x % DK);
-    for (int x = tid; x < DK * CM; x += kBwdThreads) KTl[(x / CM) * LC + x % CM] = R.kt(x / CM, x % CM);
-    for (int x = tid; x < CM * kVT; x += kBwdThreads) Ul[x] = R.ut(v0 + x % kVT, x / kVT);
+    for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {
+      const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
+      float o[8];
+      R.y8(t, j0, o);
+      *(f32x4*)&Yl[t * LY + j0] = f32x4{o[0], o[1], o[2], o[3]};
+      *(f32x4*)&Yl[t * LY + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
+    }
+    for (int x = tid; x < DK * CM / 8; x += kBwdThreads) {
+      const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
+      float o[8];
+      R.kt8(jr, s0, o);
+      *(f32x4*)&KTl[jr * LC + s0] = f32x4{o[0], o[1], o[2], o[3]};
+      *(f32x4*)&KTl[jr * LC + s0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
+    }
+    for (int x = tid; x < kVT * CM / 4; x += kBwdThreads) {
+      const int v = x / (CM / 4), tq = 4 * (x % (CM / 4));
+      float o[4];
+      R.ut4(v0 + v, tq, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ul[(tq + e) * kVT + v] = o[e];
+    }
     for (int j = tid; j < DK; j += kBwdThreads) PIl[j] = R.pic(j);
     __syncthreads();
     // V~ = U - Y S
@@ -226,12 +281,30 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       }
     }
     const int t0 = c * CM;
-    for (int x = tid; x < CM * CM; x += kBwdThreads) MTl[(x % CM) * LC + x / CM] = R.m(x / CM, x % CM);
-    for (int x = tid; x < DK * CM; x += kBwdThreads) Kl[(x % CM) * LY + x / CM] = R.kt(x / CM, x % CM);
-    for (int x = tid; x < CM * DK; x += kBwdThreads) {
-      const int t = x / DK, j = x % DK;
-      QTl[j * LC + t] = R.qp(t, j);
-      YTl[j * LC + t] = R.y(t, j);
+    for (int x = tid; x < CM * CM / 8; x += kBwdThreads) {
+      const int t = x / (CM / 8), s0 = 8 * (x % (CM / 8));
+      float o[8];
+      R.m8(t, s0, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = o[e];
+    }
+    for (int x = tid; x < DK * CM / 8; x += kBwdThreads) {
+      const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
+      float o[8];
+      R.kt8(jr, s0, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = o[e];
+    }
+    for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {
+      const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
+      float o[8], p8[8];
+      R.qp8(t, j0, o);
+      R.y8(t, j0, p8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        QTl[(j0 + e) * LC + t] = o[e];
+        YTl[(j0 + e) * LC + t] = p8[e];
+      }
     }
     for (int x = tid; x < CM * kVT; x += kBwdThreads) {
       const int t = x / kVT, v = x % kVT;
@@ -308,9 +381,27 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   const float* dHc = dHs + item * DK * DV;
   float* dZc = dZ + item * CM * (DV + DK);
   const int vl = lane & 15;
-  for (int x = tid; x < CM * DK; x += kBwdThreads) Yl[(x / DK) * LY + x % DK] = R.y(x / DK, x % DK);
-  for (int x = tid; x < CM * CM; x += kBwdThreads) MTl[(x % CM) * LC + x / CM] = R.m(x / CM, x % CM);
-  for (int x = tid; x < DK * CM; x += kBwdThreads) Kl[(x % CM) * LY + x / CM] = R.kt(x / CM, x % CM);
+  for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {
+    const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
+    float o[8];
+    R.y8(t, j0, o);
+    *(f32x4*)&Yl[t * LY + j0] = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4*)&Yl[t * LY + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
+  }
+  for (int x = tid; x < CM * CM / 8; x += kBwdThreads) {
+    const int t = x / (CM / 8), s0 = 8 * (x % (CM / 8));
+    float o[8];
+    R.m8(t, s0, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = o[e];
+  }
+  for (int x = tid; x < DK * CM / 8; x += kBwdThreads) {
+    const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
+    float o[8];
+    R.kt8(jr, s0, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = o[e];
+  }
   f32x4 aY[PY], aQ[PY], aK[PY], aM[PM];
 #pragma unroll
   for (int i = 0; i < PY; ++i) aY[i] = aQ[i] = aK[i] = f4zero();
@@ -331,7 +422,13 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
       const float g = t0 + t < T ? (float)dO[((size_t)bh * T + t0 + t) * DV + v0 + v] : 0.f;
       dOl[t * L16 + v] = g;
       dOTl[v * LC + t] = g;
-      Ul[t * kVT + v] = R.ut(v0 + v, t);
+    }
+    for (int x = tid; x < kVT * CM / 4; x += kBwdThreads) {
+      const int v = x / (CM / 4), tq = 4 * (x % (CM / 4));
+      float o[4];
+      R.ut4(v0 + v, tq, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ul[(tq + e) * kVT + v] = o[e];
     }
     __syncthreads();
     for (int it = wid; it < CM / 16; it += 4) {
@@ -487,9 +584,19 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
   }
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
   const Rec<E, FM> R{ws + item * RL.bytes, RL, DK, CM};
-  for (int x = tid; x < CM * (DV + DK); x += kBwdThreads) {
-    const int s = x / (DV + DK), cc = x % (DV + DK);
-    Zl[s * NX + cc] = cc < DV ? R.ut(cc, s) : R.y(s, cc - DV);
+  for (int x = tid; x < DV * CM / 4; x += kBwdThreads) {      // U^T rows
+    const int cc = x / (CM / 4), sq = 4 * (x % (CM / 4));
+    float o[4];
+    R.ut4(cc, sq, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Zl[(sq + e) * NX + cc] = o[e];
+  }
+  for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {      // Y rows
+    const int sr = x / (DK / 8), j0 = 8 * (x % (DK / 8));
+    float o[8];
+    R.y8(sr, j0, o);
+    *(f32x4*)&Zl[sr * NX + DV + j0] = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4*)&Zl[sr * NX + DV + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
   }
   __syncthreads();
   // dL = -stril(X Z^T)
@@ -508,8 +615,9 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
 }
 
 // ------------------------------------------------------------------ decay and key/query gradients
-// One wave per (b, h, chunk, 64 key channels); lane = channel. Per channel,
-// with e_ts = exp(Lambda_t - Lambda_s) (t >= s):
+// One workgroup per (b, h, chunk, 64 key channels): lane = channel, and the
+// four waves split the rows (row sums) and the columns (column sums). Per
+// channel, with e_ts = exp(Lambda_t - Lambda_s) (t >= s):
 //   dk^_t = sum_{s<t} dL_ts e_ts k_s + pi_t dK^_pi_t
 //   dq_t  = sum_{s<=t} dM_ts e_ts k_s + pi_t dQ_pi_t
 //   dk_s  = sum_{t>s} dL_ts e_ts k^_t + sum_{t>=s} dM_ts e_ts q_t + pi_{C,s} dK~_s
@@ -517,16 +625,20 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
 //               - k_t pi_{C,t} dK~_t, and at t = C-1 also + sum_s k_s pi_{C,s} dK~_s
 //               + pi_C dpi_C
 //   dalpha_r = (sum_{t >= r} dLambda_t) / alpha_r,  db = k dk^,  dk += b dk^.
+constexpr int kDecayWaves = 8;
+
 template <typename E, int DK, int CM>
-__global__ __launch_bounds__(64) void gdn2_bwd_decay_kernel(
+__global__ __launch_bounds__(64 * kDecayWaves) void gdn2_bwd_decay_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ alpha, const E* __restrict__ bgate,
     const float* __restrict__ dZ, const float* __restrict__ dQp, const float* __restrict__ dKt,
     const float* __restrict__ dMb, const float* __restrict__ dLb, const float* __restrict__ dpic,
     float* __restrict__ dq_out, float* __restrict__ dk_out, float* __restrict__ da_out,
     float* __restrict__ db_out, int T, int DV) {
-  constexpr int NG = (DK + 63) / 64;
-  __shared__ float Lam[CM][64], Kc[CM][64], KHc[CM][64], Qc[CM][64], DKH[CM][64], DLam[CM][64];
-  const int lane = threadIdx.x;
+  constexpr int NG = (DK + 63) / 64, NW = kDecayWaves, RPW = (CM + NW - 1) / NW;
+  __shared__ float Lam[CM][64], Kc[CM][64], KHc[CM][64], Qc[CM][64], DLam[CM][64];
+  __shared__ float dLs[CM][CM], dMs[CM][CM];
+  __shared__ float gKs[NW][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nch = (T + CM - 1) / CM;
   const int grp = blockIdx.x % NG, item_i = blockIdx.x / NG;
   const int bh = item_i / nch, c = item_i % nch, t0 = c * CM;
@@ -535,73 +647,99 @@ __global__ __launch_bounds__(64) void gdn2_bwd_decay_kernel(
   const bool act = j < DK;
   const int jj = act ? j : 0;
   const size_t sK = (size_t)bh * T * DK;
-  {
-    float acc = 0.f;
-    for (int t = 0; t < CM; ++t) {
-      const bool ok = t0 + t < T;
-      const size_t off = sK + (size_t)(t0 + t) * DK + jj;
-      const float a = ok ? (float)alpha[off] : 1.f, kk = ok ? (float)k[off] : 0.f;
-      const float bb = ok ? (float)bgate[off] : 0.f, qq = ok ? (float)q[off] : 0.f;
-      acc += logf(a);
-      Lam[t][lane] = acc;
-      Kc[t][lane] = kk;
-      KHc[t][lane] = bb * kk;
-      Qc[t][lane] = qq;
-    }
-  }
   const float* dLc = dLb + item * CM * CM;
   const float* dMc = dMb + item * CM * CM;
+  for (int x = threadIdx.x; x < CM * CM; x += 64 * NW) {
+    dLs[x / CM][x % CM] = dLc[x];
+    dMs[x / CM][x % CM] = dMc[x];
+  }
+  for (int t = wid; t < CM; t += NW) {
+    const bool ok = t0 + t < T;
+    const size_t off = sK + (size_t)(t0 + t) * DK + jj;
+    const float a = ok ? (float)alpha[off] : 1.f, kk = ok ? (float)k[off] : 0.f;
+    const float bb = ok ? (float)bgate[off] : 0.f, qq = ok ? (float)q[off] : 0.f;
+    Lam[t][lane] = logf(a);
+    Kc[t][lane] = kk;
+    KHc[t][lane] = bb * kk;
+    Qc[t][lane] = qq;
+  }
+  __syncthreads();
+  if (wid == 0) {   // Lambda_t = sum_{r <= t} log alpha_r
+    float acc = 0.f;
+    for (int t = 0; t < CM; ++t) {
+      acc += Lam[t][lane];
+      Lam[t][lane] = acc;
+    }
+  }
+  __syncthreads();
   const float* dZc = dZ + item * CM * (DV + DK);
   const float* dQc = dQp + item * CM * DK;
   const float* dKc = dKt + item * CM * DK;
-  // rows: dk^_t, dq_t and the row side of dLambda
-  for (int t = 0; t < CM; ++t) {
-    const float lt = Lam[t][lane];
-    float dkh = 0.f, dq = 0.f;
-    for (int s = 0; s <= t; ++s) {
-      const float ek = __expf(lt - Lam[s][lane]) * Kc[s][lane];
-      dq += dMc[t * CM + s] * ek;
-      if (s < t) dkh += dLc[t * CM + s] * ek;
+  // this wave's rows (and, below, columns) t = wid + NW i
+  float dkh_r[RPW], dlam_r[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int t = wid + NW * i;
+    dkh_r[i] = dlam_r[i] = 0.f;
+    if (t < CM) {
+      const float lt = Lam[t][lane];
+      float dkh = 0.f, dq = 0.f;
+#pragma unroll 8
+      for (int s = 0; s < CM; ++s) {
+        if (s <= t) {
+          const float ek = __expf(lt - Lam[s][lane]) * Kc[s][lane];
+          dq += dMs[t][s] * ek;
+          dkh += dLs[t][s] * ek;   // dL is zero on and above the diagonal
+        }
+      }
+      const float pt = __expf(lt);
+      dq += pt * dQc[t * DK + jj];
+      dkh += pt * dZc[(size_t)t * (DV + DK) + DV + jj];
+      dkh_r[i] = dkh;
+      dlam_r[i] = KHc[t][lane] * dkh + Qc[t][lane] * dq;
+      if (act && t0 + t < T) dq_out[sK + (size_t)(t0 + t) * DK + j] = dq;
     }
-    const float pt = __expf(lt);
-    dq += pt * dQc[t * DK + jj];
-    dkh += pt * dZc[(size_t)t * (DV + DK) + DV + jj];
-    DKH[t][lane] = dkh;
-    DLam[t][lane] = KHc[t][lane] * dkh + Qc[t][lane] * dq;
-    if (act && t0 + t < T) dq_out[sK + (size_t)(t0 + t) * DK + j] = dq;
   }
   // columns: dk_s and the column side of dLambda
   const float lC = Lam[CM - 1][lane];
   float gK = 0.f;
-  for (int s = 0; s < CM; ++s) {
-    const float ls = Lam[s][lane];
-    float dk = 0.f;
-    for (int t = s; t < CM; ++t) {
-      const float e = __expf(Lam[t][lane] - ls);
-      float g = dMc[t * CM + s] * Qc[t][lane];
-      if (t > s) g += dLc[t * CM + s] * KHc[t][lane];
-      dk += e * g;
-    }
-    const float ks = Kc[s][lane];
-    const float kt = __expf(lC - ls) * dKc[s * DK + jj];   // pi_{C,s} dK~_s
-    DLam[s][lane] -= ks * (dk + kt);
-    gK += ks * kt;
-    dk += kt;
-    const float dkh = DKH[s][lane];
-    const size_t off = sK + (size_t)(t0 + s) * DK + j;
-    if (act && t0 + s < T) {
-      const float bb = (float)bgate[off];
-      dk_out[off] = dk + bb * dkh;
-      db_out[off] = ks * dkh;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int s = wid + NW * i;
+    if (s < CM) {
+      const float ls = Lam[s][lane];
+      float dk = 0.f;
+#pragma unroll 8
+      for (int t = 0; t < CM; ++t) {
+        if (t >= s) dk += __expf(Lam[t][lane] - ls) * (dMs[t][s] * Qc[t][lane] + dLs[t][s] * KHc[t][lane]);
+      }
+      const float ks = Kc[s][lane];
+      const float kt = __expf(lC - ls) * dKc[s * DK + jj];   // pi_{C,s} dK~_s
+      DLam[s][lane] = dlam_r[i] - ks * (dk + kt);
+      gK += ks * kt;
+      dk += kt;
+      const size_t off = sK + (size_t)(t0 + s) * DK + j;
+      if (act && t0 + s < T) {
+        const float bb = (float)bgate[off];
+        dk_out[off] = dk + bb * dkh_r[i];
+        db_out[off] = ks * dkh_r[i];
+      }
     }
   }
-  DLam[CM - 1][lane] += gK + __expf(lC) * dpic[item * DK + jj];
-  float acc = 0.f;
-  for (int t = CM - 1; t >= 0; --t) {
-    acc += DLam[t][lane];
-    if (act && t0 + t < T) {
-      const size_t off = sK + (size_t)(t0 + t) * DK + j;
-      da_out[off] = acc / (float)alpha[off];
+  gKs[wid][lane] = gK;
+  __syncthreads();
+  if (wid == 0) {
+    float g = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) g += gKs[w][lane];
+    DLam[CM - 1][lane] += g + __expf(lC) * dpic[item * DK + jj];
+    float acc = 0.f;
+    for (int t = CM - 1; t >= 0; --t) {
+      acc += DLam[t][lane];
+      if (act && t0 + t < T) {
+        const size_t off = sK + (size_t)(t0 + t) * DK + j;
+        da_out[off] = acc / (float)alpha[off];
+      }
     }
   }
 }
@@ -673,7 +811,7 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
     float *dq = a.dq_out, *dk = a.dk_out, *da = a.dalpha_out, *db = a.db_out;
     void* args[] = {&q, &k, &al, &bg, &cdZ, &cdQ, &cdK, &cdM, &cdL, &cpi, &dq, &dk, &da, &db, &T, &DV};
     const int ng = (DK + 63) / 64;
-    if (hipLaunchKernel((const void*)kern, dim3(BH * nch * ng), dim3(64), args, 0, st) != hipSuccess)
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch * ng), dim3(64 * kDecayWaves), args, 0, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   return GDR_OK;
