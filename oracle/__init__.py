@@ -16,7 +16,10 @@ Sources (cited by page title and section/equation):
   finite differences and closed forms).
 * the same page, §2.1 (gate parameterisation) and §4.1 eq.(8)-(9): the Muir
   gate prologue (gates from logits, readout with the gain-modulated query).
-* "Exponential gates and matrix memory: xLSTM and RWKV-7" — §13.2 (spectrum of
+* "Exponential gates and matrix memory: xLSTM and RWKV-7" — §13.3 and the
+  solution to Exercise 13.5: RWKV-7's generalized delta rule (free removal
+  direction, decoupled write key), pinned by the page's eviction demo.
+* the same page — §13.2 (spectrum of
   the diagonal-plus-rank-one transition, Prop. 13.1 and Exercise 13.4), §13.3
   (reduction to Gated DeltaNet), §13.4 and Exercise 13.6 (mLSTM cell, log-domain
   stabilizer).
@@ -41,6 +44,7 @@ from .gdn2 import (  # noqa: F401
     gdn2_chunk_system, gdn2_chunkwise, chunk_condition_numbers,
 )
 from .gdn2_grad import gdn2_grad  # noqa: F401
+from .rwkv7 import rwkv7_recurrent, rwkv7_decode, rwkv7_materialized  # noqa: F401
 from .muir import (  # noqa: F401
     muir_gates, muir_recurrent, muir_decode,
 )

@@ -33,6 +33,7 @@ __all__ = [
     "gdn2_inputs_correlated",
     "decode_inputs",
     "muir_inputs",
+    "rwkv7_inputs",
     "mlstm_inputs",
     "CONFIGS",
 ]
@@ -170,6 +171,31 @@ def muir_inputs(B, H, T, dk, dv, *, seed=0, dtype="bf16", zf_mu=-3.0, zf_sigma=1
         out["z_q"] = None
     out["a_log"] = round_to(alog, "f32")
     out["gamma_stat"] = round_to(gs, "f32") if with_gamma else None
+    out["S0"] = S0
+    out["dtype"] = dtype
+    return out
+
+
+def rwkv7_inputs(B, H, T, dk, dv, *, seed=0, dtype="bf16", w_mu=4.0, w_sigma=1.5, s0_std=None):
+    """Inputs of RWKV-7's generalized delta rule: q and the write key kw as the
+    GDN-2 keys (unit SiLU of N(0,1)); the removal direction a a unit vector of
+    N(0,1); decay w = sigmoid(N(w_mu, w_sigma)) per channel (the GDN-2 decay
+    distribution); removal coefficient c = sigmoid(N(0,1)) in (0, 1) per token
+    (float32, [B,H,T]); value u ~ N(0,1). Draw order: q, kw, a, u, w-logit,
+    c-logit, S0."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = _unit_silu(g.standard_normal((B, H, T, dk)))
+    kw = _unit_silu(g.standard_normal((B, H, T, dk)))
+    a = g.standard_normal((B, H, T, dk))
+    a /= np.linalg.norm(a, axis=-1, keepdims=True)
+    u = g.standard_normal((B, H, T, dv))
+    w = _sigmoid(w_mu + w_sigma * g.standard_normal((B, H, T, dk)))
+    c = _sigmoid(g.standard_normal((B, H, T)))
+    S0 = None
+    if s0_std is not None:
+        S0 = round_to(s0_std * g.standard_normal((B, H, dk, dv)), "f32")
+    out = {name: round_to(x, dtype) for name, x in (("q", q), ("w", w), ("a", a), ("kw", kw), ("u", u))}
+    out["c"] = round_to(c, "f32")
     out["S0"] = S0
     out["dtype"] = dtype
     return out
