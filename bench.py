@@ -228,6 +228,27 @@ def bench_bwd(steps, warmup, c, x):
     return dict(B=B, T=T, full_ms=full, ready_ms=ready, ws_bytes=ws.numel())
 
 
+def bench_rwkv7(steps, warmup):
+    """RWKV-7's generalized delta rule on the 4K workload's shape (B=4, H=16,
+    T=4096, d=128, bf16, chunk 32) through gdr_rwkv7_fwd."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    from synth import CONFIGS, rwkv7_inputs
+    c = CONFIGS["chunk_4k"]
+    B, H, T, dk, dv = c["B"], c["H"], c["T"], c["dk"], c["dv"]
+    d = rwkv7_inputs(B, H, T, dk, dv, seed=0, dtype="bf16")
+    x = {n: to_dev(d[n], torch.bfloat16) for n in ("q", "w", "a", "kw", "u")}
+    cc = to_dev(d["c"], torch.float32)
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gdr.gdr_rwkv7_workspace_size(B, H, T, dk, dv, 32), dtype=torch.uint8, device="cuda")
+    fn = lambda: gdr.gdr_rwkv7_fwd(x["q"], x["w"], x["a"], cc, x["kw"], x["u"], chunk=32, o=o, S_out=S,
+                                   workspace=ws)
+    region_ms, _ = time_launches(fn, steps, warmup)
+    nbytes = B * H * T * (4 * dk + 2 * dv) * 2 + B * H * T * 4 + B * H * dk * dv * 4
+    return dict(B=B, T=T, region_ms=region_ms, bytes=nbytes)
+
+
 def bench_decode(N, steps=1024):
     """N sequences x 16 heads, d = 128, fp32 states resident in HBM: `steps`
     sequential one-token updates, each with its own inputs (all `steps` input
@@ -431,6 +452,12 @@ def main():
                                 "entry": "gdr_muir_chunk_fwd_ws", "ms_per_step": mu["region_ms"],
                                 "tokens/s": mu["B"] * mu["T"] / (mu["region_ms"] * 1e-3),
                                 "algorithmic_bytes": mu["bytes"], "GB/s": mg, "frac_hbm": mg / PEAK_HBM_GBS}
+        r7 = bench_rwkv7(max(10, args.steps // 4), max(3, args.warmup // 10))
+        g7 = r7["bytes"] / (r7["region_ms"] * 1e-3) / 1e9
+        out["rwkv7"] = {"workload": "4K workload shape, RWKV-7 generalized delta rule, bf16, chunk 32",
+                        "entry": "gdr_rwkv7_fwd", "ms_per_step": r7["region_ms"],
+                        "tokens/s": r7["B"] * r7["T"] / (r7["region_ms"] * 1e-3), "GB/s": g7,
+                        "frac_hbm": g7 / PEAK_HBM_GBS}
         c3, _, x3, S03 = chunk_inputs("chunk_32k")
         r3 = bench_chunk(max(10, args.steps // 4), max(5, args.warmup // 4), c3, x3, S03)
         g3 = r3["bytes"] / (r3["region_ms"] * 1e-3) / 1e9

@@ -272,6 +272,40 @@ int gdr_muir_decode_step(const void* q, const void* k, const void* v,
                          int N, int H, int dk, int dv, int dtype, void* stream);
 
 /*
+ * gdr_rwkv7_workspace_size, gdr_rwkv7_fwd, gdr_rwkv7_decode_step — RWKV-7's
+ * generalized delta rule ("Exponential gates and matrix memory: xLSTM and
+ * RWKV-7", §13.3 and the solution to Exercise 13.5) in this library's
+ * orientation (state S[dk, dv], row vectors):
+ *     S_t = (Diag(w_t) - c_t a_t^T a_t) S_{t-1} + kw_t^T u_t,   o_t = q_t S_t,
+ * a per-channel decay w, a unit removal direction a with coefficient c, and a
+ * write key kw decoupled from a (the page's b, renamed: it is not GDN-2's
+ * erase gate). The removal reads the previous, undecayed state.
+ *
+ * gdr_rwkv7_fwd runs two kernels through a caller workspace (float32
+ * records): every chunk independently (decay-scaled Gram matrices, the unit
+ * lower-triangular solve for the removal amounts, and the state-independent
+ * parts of the readout and state update), then one pass over the chunks of
+ * each head. Every decay factor is exp of a non-positive difference of
+ * cumulative log-decays.
+ *
+ *   q, w, a, kw     [B,H,T,dk]  input dtype (w in (0, 1], a unit)
+ *   u               [B,H,T,dv]  input dtype
+ *   c               [B,H,T]     float32 removal coefficients
+ *   S0, S_out, o    as for gdr_chunk_fwd
+ *   chunk           16 or 32 (GDR_ERR_UNSUPPORTED otherwise)
+ * gdr_rwkv7_decode_step: one token for N sequences, inputs [N,H,d], c [N,H],
+ * S [N,H,dk,dv] updated in place (read once, written once), o [N,H,dv].
+ */
+int gdr_rwkv7_workspace_size(int B, int H, int T, int dk, int dv, int chunk, size_t* bytes);
+int gdr_rwkv7_fwd(const void* q, const void* w, const void* a, const float* c,
+                  const void* kw, const void* u, const float* S0, void* o, float* S_out,
+                  int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+int gdr_rwkv7_decode_step(const void* q, const void* w, const void* a, const float* c,
+                          const void* kw, const void* u, float* S, void* o,
+                          int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
  * gdr_mlstm_fwd — chunkwise forward of the xLSTM mLSTM cell with its
  * log-domain stabiliser ("Exponential gates and matrix memory: xLSTM and
  * RWKV-7", §13.4 and Exercise 13.6), in the [dk, dv] orientation:

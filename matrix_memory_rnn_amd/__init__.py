@@ -27,7 +27,8 @@ import ctypes
 import os
 
 __all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_fwd_noalloc", "gdr_muir_chunk_fwd_ws",
-           "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size",
+           "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_size", "gdr_rwkv7_fwd", "gdr_rwkv7_workspace_size",
+           "gdr_rwkv7_decode_step",
            "gdr_muir_decode_step", "gdr_chunk_workspace_size", "gdr_chunk_intra",
            "gdr_chunk_scan", "gdr_mlstm_fwd_ws", "gdr_mlstm_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
            "GdrError", "load_library"]
@@ -82,6 +83,12 @@ def load_library():
     lib.gdr_chunk_bwd_workspace_size.restype = I
     lib.gdr_chunk_bwd.argtypes = [P] * 16 + [I] * 7 + [P, ctypes.c_size_t, I, P]
     lib.gdr_chunk_bwd.restype = I
+    lib.gdr_rwkv7_workspace_size.argtypes = [I] * 6 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_rwkv7_workspace_size.restype = I
+    lib.gdr_rwkv7_fwd.argtypes = [P] * 9 + [I] * 7 + [P, ctypes.c_size_t, P]
+    lib.gdr_rwkv7_fwd.restype = I
+    lib.gdr_rwkv7_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
+    lib.gdr_rwkv7_decode_step.restype = I
     lib.gdr_decode_step.argtypes = [P] * 8 + [I] * 5 + [P]
     lib.gdr_decode_step.restype = I
     lib.gdr_mlstm_fwd.argtypes = [P] * 12 + [I] * 7 + [P]
@@ -282,6 +289,63 @@ def gdr_chunk_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, *, chunk=64, workspac
         workspace.numel() * workspace.element_size(), int(bool(records_ready)), _stream(stream))
     _check("gdr_chunk_bwd", st)
     return g
+
+
+def gdr_rwkv7_workspace_size(B, H, T, dk, dv, chunk=32) -> int:
+    """Bytes of workspace :func:`gdr_rwkv7_fwd` needs (float32 records)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().gdr_rwkv7_workspace_size(int(B), int(H), int(T), int(dk), int(dv), int(chunk),
+                                                 ctypes.byref(n))
+    _check("gdr_rwkv7_workspace_size", st)
+    return int(n.value)
+
+
+def gdr_rwkv7_fwd(q, w, a, c, kw, u, S0=None, *, chunk=32, o=None, S_out=None, workspace=None,
+                  return_state=True, stream=None):
+    """RWKV-7 generalized delta rule over whole sequences ("Exponential gates and
+    matrix memory: xLSTM and RWKV-7", §13.3): q, w, a, kw ``[B,H,T,dk]`` and u
+    ``[B,H,T,dv]`` (bf16 or fp32), c ``[B,H,T]`` float32, S0 ``[B,H,dk,dv]``
+    float32 or None. Returns ``(o, S_T)``."""
+    import torch
+    B, H, T, dk = q.shape
+    dv = u.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, d in (("q", q, dk), ("w", w, dk), ("a", a, dk), ("kw", kw, dk), ("u", u, dv)):
+        _req(t, name, (B, H, T, d), dt, dev)
+    _req(c, "c", (B, H, T), torch.float32, dev)
+    if S0 is not None:
+        _req(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+        if S_out is None and return_state:
+            S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    workspace = _workspace(workspace, gdr_rwkv7_workspace_size(B, H, T, dk, dv, chunk), dev, stream)
+    st = load_library().gdr_rwkv7_fwd(_ptr(q), _ptr(w), _ptr(a), _ptr(c), _ptr(kw), _ptr(u), _ptr(S0), _ptr(o),
+                                      _ptr(S_out), B, H, T, dk, dv, int(chunk), _dtype_code(q), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gdr_rwkv7_fwd", st)
+    return o, S_out
+
+
+def gdr_rwkv7_decode_step(q, w, a, c, kw, u, S, *, o=None, stream=None):
+    """One RWKV-7 token for N sequences: q, w, a, kw ``[N,H,dk]``, u ``[N,H,dv]``,
+    c ``[N,H]`` float32, S ``[N,H,dk,dv]`` float32 updated in place. Returns o."""
+    import torch
+    N, H, dk = q.shape
+    dv = u.shape[-1]
+    dt, dev = q.dtype, q.device
+    for name, t, d in (("q", q, dk), ("w", w, dk), ("a", a, dk), ("kw", kw, dk), ("u", u, dv)):
+        _req(t, name, (N, H, d), dt, dev)
+    _req(c, "c", (N, H), torch.float32, dev)
+    _req(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        with _alloc_on(stream):
+            o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    st = load_library().gdr_rwkv7_decode_step(_ptr(q), _ptr(w), _ptr(a), _ptr(c), _ptr(kw), _ptr(u), _ptr(S),
+                                              _ptr(o), N, H, dk, dv, _dtype_code(q), _stream(stream))
+    _check("gdr_rwkv7_decode_step", st)
+    return o
 
 
 def _workspace(workspace, need, device, stream=None):

@@ -426,6 +426,75 @@ extern "C" int gdr_chunk_bwd(const void* q, const void* k, const void* v, const 
   return gdr::chunk_bwd_launch(a, workspace, records_ready != 0);
 }
 
+// ------------------------------------------------------------------ RWKV-7
+namespace {
+
+int check_rwkv7(const void* q, const void* w, const void* a, const float* c, const void* kw, const void* u,
+                const float* S0, const void* o, const float* S_out, int B, int H, int T, int dk, int dv,
+                int dtype) {
+  if (!q || !w || !a || !c || !kw || !u || !o) return GDR_ERR_NULL;
+  int st = check_sizes(B, H, T, dk, dv, dtype, 128);
+  if (st != GDR_OK) return st;
+  const void* ptrs[] = {q, w, a, c, kw, u, S0, o, S_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GDR_ERR_ALIGN;
+  const size_t es = esize(dtype), n = (size_t)B * H * T;
+  const size_t nK = n * dk * es, nV = n * dv * es, nS = (size_t)B * H * dk * dv * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, nK}, {w, nK}, {a, nK}, {c, n * 4}, {kw, nK}, {u, nV}};
+  for (const R& x : ins) {
+    if (overlap(o, nV, x.p, x.n) || overlap(S_out, nS, x.p, x.n)) return GDR_ERR_ALIAS;
+  }
+  if (overlap(o, nV, S0, nS) || overlap(o, nV, S_out, nS)) return GDR_ERR_ALIAS;
+  if (S_out && S0 && S_out != S0 && overlap(S_out, nS, S0, nS)) return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" int gdr_rwkv7_workspace_size(int B, int H, int T, int dk, int dv, int chunk, size_t* bytes) {
+  if (!bytes) return GDR_ERR_NULL;
+  *bytes = 0;
+  int st = check_sizes(B, H, T, dk, dv, GDR_F32, 128);
+  if (st != GDR_OK) return st;
+  if (chunk != 16 && chunk != 32) return GDR_ERR_UNSUPPORTED;
+  *bytes = gdr::rwkv7_ws_bytes(B, H, T, dk, dv, chunk);
+  return GDR_OK;
+}
+
+extern "C" int gdr_rwkv7_fwd(const void* q, const void* w, const void* a, const float* c, const void* kw,
+                             const void* u, const float* S0, void* o, float* S_out, int B, int H, int T, int dk,
+                             int dv, int chunk, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int st = check_rwkv7(q, w, a, c, kw, u, S0, o, S_out, B, H, T, dk, dv, dtype);
+  if (st != GDR_OK) return st;
+  if (chunk != 16 && chunk != 32) return GDR_ERR_UNSUPPORTED;
+  if (!workspace) return GDR_ERR_NULL;
+  if (!aligned16(workspace)) return GDR_ERR_ALIGN;
+  const size_t need = gdr::rwkv7_ws_bytes(B, H, T, dk, dv, chunk);
+  if (workspace_bytes < need) return GDR_ERR_WORKSPACE;
+  const size_t es = esize(dtype), n = (size_t)B * H * T, nS = (size_t)B * H * dk * dv * 4;
+  const void* bufs[] = {q, w, a, kw};
+  for (const void* p : bufs)
+    if (overlap(workspace, need, p, n * dk * es)) return GDR_ERR_ALIAS;
+  if (overlap(workspace, need, u, n * dv * es) || overlap(workspace, need, o, n * dv * es) ||
+      overlap(workspace, need, c, n * 4) || overlap(workspace, need, S0, nS) ||
+      overlap(workspace, need, S_out, nS))
+    return GDR_ERR_ALIAS;
+  gdr::Rwkv7Args r{q, w, a, c, kw, u, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
+  return gdr::rwkv7_fwd_launch(r, workspace);
+}
+
+extern "C" int gdr_rwkv7_decode_step(const void* q, const void* w, const void* a, const float* c, const void* kw,
+                                     const void* u, float* S, void* o, int N, int H, int dk, int dv, int dtype,
+                                     void* stream) {
+  if (!S) return GDR_ERR_NULL;
+  int st = check_rwkv7(q, w, a, c, kw, u, nullptr, o, S, N, H, 1, dk, dv, dtype);
+  if (st != GDR_OK) return st;
+  gdr::Rwkv7Args r{q, w, a, c, kw, u, nullptr, o, S, N, H, 1, dk, dv, 16, dtype, stream};
+  return gdr::rwkv7_decode_launch(r);
+}
+
 // ------------------------------------------------------------------ no-allocation entry point
 //
 // gdr_chunk_fwd_noalloc runs the two-kernel chunk forward through a scratch

@@ -47,19 +47,6 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel
 
-// One 16 x 16 output tile of A B^T: A [m][k] and B [n][k] fp32 in LDS, k
-// contiguous (pitches lda, ldb in floats, multiples of 4), k in [0, K).
-// Accumulator entry e of a lane is row m0 + 4 (lane / 16) + e, column
-// n0 + lane % 16.
-__device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int m0, const float* B, int ldb,
-                                        int n0, int K, int lane) {
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const Frag<kF32> a = ldfrag<kF32>((const char*)A, 0, lda, m0, k0, K, lane);
-    const Frag<kF32> b = ldfrag<kF32>((const char*)B, 0, ldb, n0, k0, K, lane);
-    mma<kF32>(acc, a, b);
-  }
-}
-
 __device__ __forceinline__ int acc_row(int lane, int e) { return 4 * (lane >> 4) + e; }
 
 // Element reads of one forward record (row-major or F order) as float.

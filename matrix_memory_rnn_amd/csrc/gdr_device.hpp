@@ -285,6 +285,19 @@ __device__ __forceinline__ void scale_frag(Frag<MODE>& f, const float* s) {
   }
 }
 
+// One 16 x 16 output tile of A B^T on the fp32 matrix cores: A [m][k] and
+// B [n][k] fp32 in LDS, k contiguous (pitches lda, ldb in floats, multiples
+// of 4), k in [0, K). Accumulator entry e of a lane is row m0 + 4 (lane / 16)
+// + e, column n0 + lane % 16.
+__device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int m0, const float* B, int ldb,
+                                        int n0, int K, int lane) {
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const Frag<kF32> a = ldfrag<kF32>((const char*)A, 0, lda, m0, k0, K, lane);
+    const Frag<kF32> b = ldfrag<kF32>((const char*)B, 0, ldb, n0, k0, K, lane);
+    mma<kF32>(acc, a, b);
+  }
+}
+
 // Workgroup index -> linear work index that places consecutive work items of
 // one group (e.g. the value tiles of one head) on the same XCD. Workgroups are
 // dispatched round-robin over the 8 XCDs of an MI355X; each XCD has its own L2.

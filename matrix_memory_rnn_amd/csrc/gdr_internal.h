@@ -49,6 +49,20 @@ struct ChunkBwdArgs {
   void* stream;
 };
 
+// RWKV-7 generalized delta rule: decay w, removal direction a, removal
+// coefficient c (fp32 [B,H,T] or [N,H]), write key kw, value u; for the decode
+// step S_out is the resident state and B the sequence count.
+struct Rwkv7Args {
+  const void *q, *w, *a;
+  const float* c;
+  const void *kw, *u;
+  const float* S0;
+  void* o;
+  float* S_out;
+  int B, H, T, dk, dv, chunk, dtype;
+  void* stream;
+};
+
 struct MlstmArgs {
   const void *q, *k, *v;
   const float *i_tilde, *f_tilde, *C0, *n0, *m0;
@@ -70,6 +84,9 @@ int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases);
 size_t chunk_bwd_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 int chunk_bwd_launch(const ChunkBwdArgs& a, void* ws, bool records_ready);
 int decode_launch(const DecodeArgs& a);
+size_t rwkv7_ws_bytes(int B, int H, int T, int dk, int dv, int chunk);
+int rwkv7_fwd_launch(const Rwkv7Args& a, void* ws);
+int rwkv7_decode_launch(const Rwkv7Args& a);
 int mlstm_launch(const MlstmArgs& a);
 // two-kernel form (intra-chunk kernel over all chunks, then the chunk scan)
 size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);

@@ -1,0 +1,503 @@
+// RWKV-7's generalized delta rule on gfx950: chunkwise forward (two kernels
+// through a workspace) and the one-token decode step.
+//
+// "Exponential gates and matrix memory: xLSTM and RWKV-7", §13.3 and the
+// solution to Exercise 13.5, in this library's orientation (state
+// S[d_k, d_v], row vectors, o = q S):
+//     S_t = (Diag(w_t) - c_t a_t^T a_t) S_{t-1} + kw_t^T u_t,   o_t = q_t S_t.
+// The removal reads the previous, undecayed state: e_t = c_t a_t S_{t-1}.
+//
+// Chunkwise form (chunk of C tokens from S0; Lambda_t = sum_{r<=t} log w_r,
+// pi_t = e^{Lambda_t}, every decay below a product of w over an interval,
+// evaluated as exp of a non-positive difference of Lambda):
+//   y_t = c_t a_t
+//   L_a[t,s] = <y_t, e^{Lambda_{t-1} - Lambda_s} a_s>,  L_z likewise with kw_s (s < t)
+//   M_a[t,s] = <q_t, e^{Lambda_t - Lambda_s} a_s>,      M_z likewise with kw_s (s <= t)
+//   (I + L_a) [E0 | G] = [L_z U | Y_pi'],  (Y_pi')_t = y_t e^{Lambda_{t-1}}
+//   the removal amounts E = E0 + G S0, and
+//   O   = Q_pi S0 - M_a E + M_z U,
+//   S_C = Diag(pi_C) S0 - A~^T E + Z~^T U   (A~_s, Z~_s = e^{Lambda_C - Lambda_s} a_s, kw_s).
+// The intra kernel does every chunk independently and writes G, E0, M_a,
+// Q_pi, A~^T, pi_C, O_z = M_z U and W_z = Z~^T U (fp32); the scan walks the
+// chunks of each head: E = E0 + G S0, O = Q_pi S0 - M_a E + O_z,
+// S = Diag(pi_C) S0 - A~^T E + W_z, on the fp32 matrix cores.
+#include "gdr_device.hpp"
+#include "gdr_internal.h"
+#include "gdr_host.hpp"
+
+namespace gdr {
+
+namespace {
+
+constexpr int kR7Threads = 256;
+constexpr int kR7VT = 16;    // value tile of the scan
+
+// Record of one (b, h, chunk), fp32 element offsets.
+struct R7Layout {
+  int g, e0, ma, qp, at, pic, oz, wz, floats;
+};
+__host__ __device__ inline R7Layout r7_layout(int dk, int dv, int C) {
+  R7Layout r;
+  r.g = 0;                    // G     [t][j]  C x dk
+  r.e0 = r.g + C * dk;        // E0    [t][v]  C x dv
+  r.ma = r.e0 + C * dv;       // M_a   [t][s]  C x C (lower, diagonal included)
+  r.qp = r.ma + C * C;        // Q_pi  [t][j]  C x dk
+  r.at = r.qp + C * dk;       // A~^T  [j][s]  dk x C
+  r.pic = r.at + dk * C;      // pi_C  [j]     dk
+  r.oz = r.pic + dk;          // O_z   [t][v]  C x dv
+  r.wz = r.oz + C * dv;       // W_z   [j][v]  dk x dv
+  r.floats = (r.wz + dk * dv + 3) / 4 * 4;
+  return r;
+}
+
+}  // namespace
+
+size_t rwkv7_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
+  const size_t nch = ((size_t)T + chunk - 1) / chunk;
+  return (size_t)B * H * nch * r7_layout(dk, dv, chunk).floats * 4;
+}
+
+// ------------------------------------------------------------------ intra-chunk kernel
+template <typename E, int DK, int CM>
+__global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
+    const E* __restrict__ q, const E* __restrict__ w, const E* __restrict__ a, const float* __restrict__ c,
+    const E* __restrict__ kw, const E* __restrict__ u, float* __restrict__ ws, int T, int DV) {
+  constexpr int LP = DK + 1, LQ = CM + 1;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* Lam = (float*)smem;            // Lambda [t][j]
+  float* Al = Lam + CM * LP;            // a      [t][j]
+  float* Zl = Al + CM * LP;             // kw     [t][j]
+  float* Ql = Zl + CM * LP;             // q      [t][j]
+  float* Yl = Ql + CM * LP;             // c a    [t][j]
+  float* La = Yl + CM * LP;             // L_a    [t][s]
+  float* Lz = La + CM * LQ;
+  float* Ma = Lz + CM * LQ;
+  float* Mz = Ma + CM * LQ;
+  float* UT = Mz + CM * LQ;             // u^T    [v][s]
+  float* Xl = UT + DV * LQ;             // [L_z U | Y_pi'] -> [E0 | G], [t][c]
+  const int NX = DV + DK + 1;
+  const int tid = threadIdx.x;
+  const int nch = (T + CM - 1) / CM;
+  const int bh = blockIdx.x / nch, ch = blockIdx.x % nch, t0 = ch * CM;
+  const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
+  const R7Layout RL = r7_layout(DK, DV, CM);
+  float* rec = ws + ((size_t)bh * nch + ch) * RL.floats;
+  // rows past T: w = 1, a = kw = q = 0, c = 0, u = 0 (identity steps)
+  for (int x = tid; x < CM * DK; x += kR7Threads) {
+    const int t = x / DK, j = x % DK;
+    const bool ok = t0 + t < T;
+    const size_t off = sK + (size_t)(t0 + t) * DK + j;
+    const float aa = ok ? (float)a[off] : 0.f;
+    Lam[t * LP + j] = ok ? logf((float)w[off]) : 0.f;
+    Al[t * LP + j] = aa;
+    Zl[t * LP + j] = ok ? (float)kw[off] : 0.f;
+    Ql[t * LP + j] = ok ? (float)q[off] : 0.f;
+    Yl[t * LP + j] = ok ? c[(size_t)bh * T + t0 + t] * aa : 0.f;
+  }
+  for (int x = tid; x < CM * DV; x += kR7Threads) {
+    const int t = x / DV, v = x % DV;
+    UT[v * LQ + t] = t0 + t < T ? (float)u[sV + (size_t)(t0 + t) * DV + v] : 0.f;
+  }
+  __syncthreads();
+  for (int j = tid; j < DK; j += kR7Threads) {
+    float acc = 0.f;
+    for (int t = 0; t < CM; ++t) {
+      acc += Lam[t * LP + j];
+      Lam[t * LP + j] = acc;
+    }
+  }
+  __syncthreads();
+  // the four decay-scaled Gram matrices, one (t, s) pair per thread
+  for (int p = tid; p < CM * CM; p += kR7Threads) {
+    const int t = p / CM, s = p % CM;
+    float la = 0.f, lz = 0.f, ma = 0.f, mz = 0.f;
+    if (s <= t) {
+      for (int j = 0; j < DK; ++j) {
+        const float ls = Lam[s * LP + j];
+        const float e2 = __expf(Lam[t * LP + j] - ls);
+        const float as = Al[s * LP + j], zs = Zl[s * LP + j];
+        const float qt = Ql[t * LP + j];
+        ma += qt * e2 * as;
+        mz += qt * e2 * zs;
+        if (s < t) {
+          const float e1 = __expf(Lam[(t - 1) * LP + j] - ls);
+          const float yt = Yl[t * LP + j];
+          la += yt * e1 * as;
+          lz += yt * e1 * zs;
+        }
+      }
+    }
+    La[t * LQ + s] = la;
+    Lz[t * LQ + s] = lz;
+    Ma[t * LQ + s] = ma;
+    Mz[t * LQ + s] = mz;
+  }
+  __syncthreads();
+  // right-hand side [L_z U | Y_pi']
+  for (int x = tid; x < CM * DV; x += kR7Threads) {
+    const int t = x / DV, v = x % DV;
+    float acc = 0.f;
+    for (int s = 0; s < t; ++s) acc += Lz[t * LQ + s] * UT[v * LQ + s];
+    Xl[t * NX + v] = acc;
+  }
+  for (int x = tid; x < CM * DK; x += kR7Threads) {
+    const int t = x / DK, j = x % DK;
+    Xl[t * NX + DV + j] = Yl[t * LP + j] * (t > 0 ? __expf(Lam[(t - 1) * LP + j]) : 1.f);
+  }
+  __syncthreads();
+  // (I + L_a) X = RHS by forward substitution, one column per thread
+  for (int col = tid; col < DV + DK; col += kR7Threads) {
+    float x[CM];
+#pragma unroll
+    for (int t = 0; t < CM; ++t) x[t] = Xl[t * NX + col];
+#pragma unroll
+    for (int t = 1; t < CM; ++t) {
+      float acc = x[t];
+#pragma unroll
+      for (int s = 0; s < t; ++s) acc -= La[t * LQ + s] * x[s];
+      x[t] = acc;
+    }
+#pragma unroll
+    for (int t = 0; t < CM; ++t) {
+      if (col < DV) rec[RL.e0 + t * DV + col] = x[t];
+      else rec[RL.g + t * DK + col - DV] = x[t];
+    }
+  }
+  // O_z = M_z U, W_z = Z~^T U, M_a, Q_pi, A~^T, pi_C
+  for (int x = tid; x < CM * DV; x += kR7Threads) {
+    const int t = x / DV, v = x % DV;
+    float acc = 0.f;
+    for (int s = 0; s <= t; ++s) acc += Mz[t * LQ + s] * UT[v * LQ + s];
+    rec[RL.oz + t * DV + v] = acc;
+  }
+  for (int x = tid; x < DK * DV; x += kR7Threads) {
+    const int j = x / DV, v = x % DV;
+    const float lc = Lam[(CM - 1) * LP + j];
+    float acc = 0.f;
+    for (int s = 0; s < CM; ++s) acc += __expf(lc - Lam[s * LP + j]) * Zl[s * LP + j] * UT[v * LQ + s];
+    rec[RL.wz + j * DV + v] = acc;
+  }
+  for (int x = tid; x < CM * CM; x += kR7Threads) rec[RL.ma + x] = Ma[(x / CM) * LQ + x % CM];
+  for (int x = tid; x < CM * DK; x += kR7Threads) {
+    const int t = x / DK, j = x % DK;
+    rec[RL.qp + t * DK + j] = __expf(Lam[t * LP + j]) * Ql[t * LP + j];
+  }
+  for (int x = tid; x < DK * CM; x += kR7Threads) {
+    const int j = x / CM, s = x % CM;
+    rec[RL.at + j * CM + s] = __expf(Lam[(CM - 1) * LP + j] - Lam[s * LP + j]) * Al[s * LP + j];
+  }
+  for (int j = tid; j < DK; j += kR7Threads) rec[RL.pic + j] = __expf(Lam[(CM - 1) * LP + j]);
+}
+
+// ------------------------------------------------------------------ chunk scan
+template <typename E, int DK, int CM>
+__global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __restrict__ ws,
+                                                                 const float* __restrict__ S0, E* __restrict__ o,
+                                                                 float* __restrict__ S_out, int T, int DV) {
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NT = CM / 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* Gl = (float*)smem;             // G     [t][j]
+  float* Qpl = Gl + CM * LY;            // Q_pi  [t][j]
+  float* Mal = Qpl + CM * LY;           // M_a   [t][s]
+  float* ATl = Mal + CM * LC;           // A~^T  [j][s]
+  float* STl = ATl + DK * LC;           // S^T   [v][j]
+  float* ETl = STl + kR7VT * LY;        // E^T   [v][s]
+  float* E0l = ETl + kR7VT * LC;        // E0    [t][v]
+  float* OZl = E0l + CM * kR7VT;        // O_z   [t][v]
+  float* WZl = OZl + CM * kR7VT;        // W_z   [j][v]
+  float* PIl = WZl + DK * kR7VT;        // pi_C  [j]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, vl = lane & 15;
+  const int nvt = DV / kR7VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kR7VT;
+  const int nch = (T + CM - 1) / CM;
+  const R7Layout RL = r7_layout(DK, DV, CM);
+  f32x4 S[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int J = wid + 4 * i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * J + 4 * (lane >> 4) + e;
+      S[i][e] = (J < NST && S0) ? S0[((size_t)bh * DK + row) * DV + v0 + vl] : 0.f;
+    }
+  }
+  for (int c = 0; c < nch; ++c) {
+    const float* rec = ws + ((size_t)bh * nch + c) * RL.floats;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) STl[vl * LY + 16 * J + 4 * (lane >> 4) + e] = S[i][e];
+      }
+    }
+    for (int x = tid; x < CM * DK / 4; x += kR7Threads) {
+      const int t = x / (DK / 4), j0 = 4 * (x % (DK / 4));
+      *(f32x4*)&Gl[t * LY + j0] = *(const f32x4*)&rec[RL.g + t * DK + j0];
+      *(f32x4*)&Qpl[t * LY + j0] = *(const f32x4*)&rec[RL.qp + t * DK + j0];
+    }
+    for (int x = tid; x < CM * CM / 4; x += kR7Threads) {
+      const int t = x / (CM / 4), s0 = 4 * (x % (CM / 4));
+      *(f32x4*)&Mal[t * LC + s0] = *(const f32x4*)&rec[RL.ma + t * CM + s0];
+    }
+    for (int x = tid; x < DK * CM / 4; x += kR7Threads) {
+      const int j = x / (CM / 4), s0 = 4 * (x % (CM / 4));
+      *(f32x4*)&ATl[j * LC + s0] = *(const f32x4*)&rec[RL.at + j * CM + s0];
+    }
+    for (int x = tid; x < CM * kR7VT / 4; x += kR7Threads) {
+      const int t = x / (kR7VT / 4), q0 = 4 * (x % (kR7VT / 4));
+      *(f32x4*)&E0l[t * kR7VT + q0] = *(const f32x4*)&rec[RL.e0 + t * DV + v0 + q0];
+      *(f32x4*)&OZl[t * kR7VT + q0] = *(const f32x4*)&rec[RL.oz + t * DV + v0 + q0];
+    }
+    for (int x = tid; x < DK * kR7VT / 4; x += kR7Threads) {
+      const int j = x / (kR7VT / 4), q0 = 4 * (x % (kR7VT / 4));
+      *(f32x4*)&WZl[j * kR7VT + q0] = *(const f32x4*)&rec[RL.wz + j * DV + v0 + q0];
+    }
+    for (int j = tid; j < DK; j += kR7Threads) PIl[j] = rec[RL.pic + j];
+    __syncthreads();
+    // E = E0 + G S0 (to LDS, transposed); the readout's Q_pi S0 kept in registers
+    f32x4 oacc[(NT + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (NT + 3) / 4; ++i) {
+      const int it = wid + 4 * i;
+      oacc[i] = f4zero();
+      if (it < NT) {
+        f32x4 acc = f4zero();
+        tile_nt(acc, Gl, LY, 16 * it, STl, LY, 0, DK, lane);
+        tile_nt(oacc[i], Qpl, LY, 16 * it, STl, LY, 0, DK, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * it + 4 * (lane >> 4) + e;
+          ETl[vl * LC + t] = E0l[t * kR7VT + vl] + acc[e];
+        }
+      }
+    }
+    __syncthreads();
+    // O = Q_pi S0 - M_a E + O_z
+#pragma unroll
+    for (int i = 0; i < (NT + 3) / 4; ++i) {
+      const int it = wid + 4 * i;
+      if (it < NT) {
+        f32x4 me = f4zero();
+        tile_nt(me, Mal, LC, 16 * it, ETl, LC, 0, CM, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * it + 4 * (lane >> 4) + e;
+          if (c * CM + t < T)
+            In<E>::store1(o + ((size_t)bh * T + c * CM + t) * DV + v0 + vl,
+                          oacc[i][e] - me[e] + OZl[t * kR7VT + vl]);
+        }
+      }
+    }
+    // S <- Diag(pi_C) S - A~^T E + W_z
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+        f32x4 ae = f4zero();
+        tile_nt(ae, ATl, LC, 16 * J, ETl, LC, 0, CM, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * J + 4 * (lane >> 4) + e;
+          S[i][e] = PIl[row] * S[i][e] - ae[e] + WZl[row * kR7VT + vl];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (S_out) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int J = wid + 4 * i;
+      if (J < NST) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          S_out[((size_t)bh * DK + 16 * J + 4 * (lane >> 4) + e) * DV + v0 + vl] = S[i][e];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode step
+// Per (n, h): r = a S and p = (q * w) S from one read of S, e = c r,
+// S <- Diag(w) S - a^T e + kw^T u,  o = p - (q . a) e + (q . kw) u.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void rwkv7_decode_kernel(const E* __restrict__ q, const E* __restrict__ w,
+                                                           const E* __restrict__ a, const float* __restrict__ c,
+                                                           const E* __restrict__ kw, const E* __restrict__ u,
+                                                           float* __restrict__ S, E* __restrict__ o) {
+  constexpr int TPR = DV / 4, RPP = 256 / TPR, NPASS = (DK + RPP - 1) / RPP;
+  __shared__ float s_a[DK], s_qw[DK], s_w[DK], s_kw[DK], s_q[DK], s_u[DV];
+  __shared__ float s_red[2][RPP][DV];
+  __shared__ float s_dot[2];
+  const int tid = threadIdx.x;
+  const size_t head = blockIdx.x;
+  const size_t offK = head * DK, offV = head * DV;
+  float* Sh = S + head * DK * DV;
+  const int c4 = (tid % TPR) * 4, rg = tid / TPR;
+  f32x4 st[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int j = rg + RPP * p;
+    st[p] = (rg < RPP && j < DK) ? *(const f32x4*)(Sh + (size_t)j * DV + c4) : f4zero();
+  }
+  for (int j = tid; j < DK; j += 256) {
+    const float ww = (float)w[offK + j], qq = (float)q[offK + j];
+    s_a[j] = (float)a[offK + j];
+    s_w[j] = ww;
+    s_kw[j] = (float)kw[offK + j];
+    s_q[j] = qq;
+    s_qw[j] = qq * ww;
+  }
+  for (int v = tid; v < DV; v += 256) s_u[v] = (float)u[offV + v];
+  __syncthreads();
+  if (tid < 64) {   // q . a and q . kw by one wave
+    float da = 0.f, dz = 0.f;
+    for (int j = tid; j < DK; j += 64) {
+      da += s_q[j] * s_a[j];
+      dz += s_q[j] * s_kw[j];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      da += __shfl_xor(da, off, 64);
+      dz += __shfl_xor(dz, off, 64);
+    }
+    if (tid == 0) {
+      s_dot[0] = da;
+      s_dot[1] = dz;
+    }
+  }
+  f32x4 r = f4zero(), pq = f4zero();
+  if (rg < RPP) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int j = rg + RPP * p;
+      if (j < DK) {
+        const float aj = s_a[j], qw = s_qw[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r[e] += aj * st[p][e];
+          pq[e] += qw * st[p][e];
+        }
+      }
+    }
+    *(f32x4*)&s_red[0][rg][c4] = r;
+    *(f32x4*)&s_red[1][rg][c4] = pq;
+  }
+  __syncthreads();
+  const float cc = c[head];
+  f32x4 ev = f4zero(), pr = f4zero();
+  for (int x = 0; x < RPP; ++x) {
+    const f32x4 a4 = *(const f32x4*)&s_red[0][x][c4];
+    const f32x4 b4 = *(const f32x4*)&s_red[1][x][c4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { ev[e] += a4[e]; pr[e] += b4[e]; }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ev[e] *= cc;
+  if (rg < RPP) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int j = rg + RPP * p;
+      if (j < DK) {
+        const float ww = s_w[j], aj = s_a[j], zj = s_kw[j];
+        f32x4 nv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nv[e] = ww * st[p][e] - aj * ev[e] + zj * s_u[c4 + e];
+        *(f32x4*)(Sh + (size_t)j * DV + c4) = nv;
+      }
+    }
+  }
+  if (rg == 0) {
+    const float da = s_dot[0], dz = s_dot[1];
+    f32x4 ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ov[e] = pr[e] - da * ev[e] + dz * s_u[c4 + e];
+    In<E>::store4(o + offV + c4, ov);
+  }
+}
+
+// ------------------------------------------------------------------ host launch
+template <typename E, int DK, int CM>
+static int r7_launch(const Rwkv7Args& a, void* ws) {
+  const int BH = a.B * a.H, nch = (a.T + CM - 1) / CM;
+  int T = a.T, DV = a.dv;
+  const hipStream_t st = (hipStream_t)a.stream;
+  float* wsf = (float*)ws;
+  {
+    const int lds = 4 * (5 * CM * (DK + 1) + 4 * CM * (CM + 1) + DV * (CM + 1) + CM * (DV + DK + 1));
+    auto kern = rwkv7_intra_kernel<E, DK, CM>;
+    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const E *q = (const E*)a.q, *w = (const E*)a.w, *aa = (const E*)a.a, *kw = (const E*)a.kw, *u = (const E*)a.u;
+    const float* c = a.c;
+    void* args[] = {&q, &w, &aa, &c, &kw, &u, &wsf, &T, &DV};
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kR7Threads), args, lds, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    constexpr int LY = DK + 4, LC = CM + 4;
+    const int lds = 4 * (2 * CM * LY + CM * LC + DK * LC + kR7VT * LY + kR7VT * LC + 2 * CM * kR7VT + DK * kR7VT + DK);
+    auto kern = rwkv7_scan_kernel<E, DK, CM>;
+    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const float* wsc = wsf;
+    const float* S0 = a.S0;
+    E* o = (E*)a.o;
+    float* So = a.S_out;
+    void* args[] = {&wsc, &S0, &o, &So, &T, &DV};
+    if (hipLaunchKernel((const void*)kern, dim3(BH * (DV / kR7VT)), dim3(kR7Threads), args, lds, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  return GDR_OK;
+}
+
+template <typename E, int CM>
+static int r7_dk(const Rwkv7Args& a, void* ws) {
+  switch (a.dk) {
+    case 16: return r7_launch<E, 16, CM>(a, ws);
+    case 32: return r7_launch<E, 32, CM>(a, ws);
+    case 64: return r7_launch<E, 64, CM>(a, ws);
+    case 128: return r7_launch<E, 128, CM>(a, ws);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+int rwkv7_fwd_launch(const Rwkv7Args& a, void* ws) {
+  if (a.dtype == GDR_BF16) return a.chunk == 16 ? r7_dk<__bf16, 16>(a, ws) : r7_dk<__bf16, 32>(a, ws);
+  return a.chunk == 16 ? r7_dk<float, 16>(a, ws) : r7_dk<float, 32>(a, ws);
+}
+
+template <typename E, int DK>
+static int r7_decode_dv(const Rwkv7Args& a) {
+  const E *q = (const E*)a.q, *w = (const E*)a.w, *aa = (const E*)a.a, *kw = (const E*)a.kw, *u = (const E*)a.u;
+  const float* c = a.c;
+  float* S = a.S_out;
+  E* o = (E*)a.o;
+  void* args[] = {&q, &w, &aa, &c, &kw, &u, &S, &o};
+  const void* kern = nullptr;
+  switch (a.dv) {
+    case 16: kern = (const void*)rwkv7_decode_kernel<E, DK, 16>; break;
+    case 32: kern = (const void*)rwkv7_decode_kernel<E, DK, 32>; break;
+    case 64: kern = (const void*)rwkv7_decode_kernel<E, DK, 64>; break;
+    case 128: kern = (const void*)rwkv7_decode_kernel<E, DK, 128>; break;
+    default: return GDR_ERR_UNSUPPORTED;
+  }
+  return hipLaunchKernel(kern, dim3(a.B * a.H), dim3(256), args, 0, (hipStream_t)a.stream) == hipSuccess
+             ? GDR_OK
+             : GDR_ERR_LAUNCH;
+}
+
+template <typename E>
+static int r7_decode_dk(const Rwkv7Args& a) {
+  switch (a.dk) {
+    case 16: return r7_decode_dv<E, 16>(a);
+    case 32: return r7_decode_dv<E, 32>(a);
+    case 64: return r7_decode_dv<E, 64>(a);
+    case 128: return r7_decode_dv<E, 128>(a);
+  }
+  return GDR_ERR_UNSUPPORTED;
+}
+
+int rwkv7_decode_launch(const Rwkv7Args& a) {
+  return a.dtype == GDR_BF16 ? r7_decode_dk<__bf16>(a) : r7_decode_dk<float>(a);
+}
+
+}  // namespace gdr
