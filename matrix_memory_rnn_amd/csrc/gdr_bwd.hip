@@ -748,7 +748,14 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
   const hipStream_t st = (hipStream_t)a.stream;
   const char* wsc = ws;
   constexpr int LY = DK + 4, LC = CM + 4, L16 = kVT + 4;
-  {
+  if constexpr (FM && std::is_same<E, __bf16>::value) {
+    // F-order records: the forward's F-order scan walks the states (bf16
+    // copies of the state in its products, as in the forward itself)
+    ChunkArgs f{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, a.S0, nullptr, nullptr, a.B, a.H, a.T, DK,
+                a.dv, CM, a.dtype, a.stream};
+    const int st0 = chunk_states_fm_launch(f, ws, Hs);
+    if (st0 != GDR_OK) return st0;
+  } else {
     const int lds = 4 * (CM * LY + DK * LC + kVT * LY + kVT * LC + CM * kVT + DK);
     auto kern = gdn2_bwd_states_kernel<E, DK, CM, FM>;
     if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;

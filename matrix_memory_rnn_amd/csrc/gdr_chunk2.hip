@@ -1504,10 +1504,12 @@ __device__ __forceinline__ void phase_barrier() {
 // tile), and segment g starts from the state Sseg[g][b*H + h] that the
 // segment pass left there (g = 0: S0); only the last segment writes S_out.
 // With seg >= the chunk count there is one segment, starting from S0.
+// Hst (may be NULL): every chunk-start state, fp32 [b*H + h][chunk][d_k][d_v]
+// (the backward's saved states); o may be NULL then (no outputs stored).
 template <int DK, int CM, int PF, int NS>
 __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
     const char* __restrict__ ws, const float* __restrict__ S0, __bf16* __restrict__ o, float* S_out,
-    int T, int DV, int seg, const float* __restrict__ Sseg) {
+    int T, int DV, int seg, const float* __restrict__ Sseg, float* __restrict__ Hst) {
   constexpr int NI2 = CM / 32, NJ2 = DK / 32, KSD = DK / 16, KSC = CM / 16;
   constexpr int LDK = DK + 8, LDC = CM + 8;      // LDS row pitches (elements): 16-byte reads conflict free
   static_assert(DK % 32 == 0 && CM % 32 == 0 && NJ2 <= 4 && NI2 <= 2, "F-order scan shape");
@@ -1679,13 +1681,15 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
         typedef __attribute__((ext_vector_type(2))) uint32_t u2;
         const int t0 = (c0 + ch) * CM;
-        const __amdgpu_buffer_rsrc_t orsrc =
-            __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
+        if (o != nullptr) {
+          const __amdgpu_buffer_rsrc_t orsrc =
+              __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x4 x = bf16x4{(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2],
-                                  (__bf16)acc[4 * q + 3]};
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, x), orsrc, oct + 16 * q, 0, 0);
+          for (int q = 0; q < 4; ++q) {
+            const bf16x4 x = bf16x4{(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2],
+                                    (__bf16)acc[4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, x), orsrc, oct + 16 * q, 0, 0);
+          }
         }
         phase_barrier();                                // B
       });
@@ -1763,6 +1767,13 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
         if (toucher) {
           sink ^= PFV[u % PF];
           PFV[u % PF] = touch(ch + PF);
+        }
+        if (Hst != nullptr) {                           // the chunk-start state, fp32
+          float* hc = Hst + (((size_t)bh * ntot + c0 + ch) * DK + 32 * J2 + 4 * h) * DV + vt0 + r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hc[(size_t)(8 * q + e) * DV] = Sacc[4 * q + e];
         }
         // entry 4q + e is row 32 J2 + 8q + 4h + e, whose pi_C lane 8q + 4h + e
         // holds: one lane permute per entry (the constant part of the lane
@@ -2145,9 +2156,41 @@ static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
     seg = ntot;
   }
   const int nblocks = BH * (a.dv / 32) * ((ntot + seg - 1) / seg);
-  void* args[] = {&ws, &S0, &o, &So, &T, &DV, &seg, &Sseg};
+  float* Hst = nullptr;
+  void* args[] = {&ws, &S0, &o, &So, &T, &DV, &seg, &Sseg, &Hst};
   hipError_t e = hipLaunchKernel(kern, dim3(nblocks), dim3(kScanFmThreads), args, 0, (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+// Chunk-start states of the F-order records in `ws` (written by the intra
+// kernel for these shapes) for the backward: the F-order scan without outputs,
+// one segment per head.
+template <int DK, int CM>
+static int launch_states_fm(const ChunkArgs& a, const char* ws, float* Hst) {
+  const void* kern = (const void*)gdn2_chunk_scan_fm_kernel<DK, CM, kScanFmPrefetch, kScanFmSets>;
+  const float* S0 = a.S0;
+  __bf16* o = nullptr;
+  float* So = nullptr;
+  const float* Sseg = nullptr;
+  int T = a.T, DV = a.dv;
+  int seg = (T + CM - 1) / CM;
+  const int nblocks = a.B * a.H * (a.dv / 32);
+  void* args[] = {&ws, &S0, &o, &So, &T, &DV, &seg, &Sseg, &Hst};
+  hipError_t e = hipLaunchKernel(kern, dim3(nblocks), dim3(kScanFmThreads), args, 0, (hipStream_t)a.stream);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+int chunk_states_fm_launch(const ChunkArgs& a, const void* ws, float* Hst) {
+  if (!fm_path(a.dk, a.dv, a.chunk, a.dtype, a.T)) return GDR_ERR_UNSUPPORTED;
+  switch (a.dk * 1000 + a.chunk) {
+    case 32032: return launch_states_fm<32, 32>(a, (const char*)ws, Hst);
+    case 32064: return launch_states_fm<32, 64>(a, (const char*)ws, Hst);
+    case 64032: return launch_states_fm<64, 32>(a, (const char*)ws, Hst);
+    case 64064: return launch_states_fm<64, 64>(a, (const char*)ws, Hst);
+    case 128032: return launch_states_fm<128, 32>(a, (const char*)ws, Hst);
+    case 128064: return launch_states_fm<128, 64>(a, (const char*)ws, Hst);
+  }
+  return GDR_ERR_UNSUPPORTED;
 }
 
 template <typename Tin, int DK, int CM>

@@ -82,6 +82,9 @@ int chunk_fwd_ws_launch(const ChunkArgs& a, void* ws, int phases);
 // chunkwise backward: workspace = the forward records, then the backward's
 // own buffers; records_ready skips recomputing the records
 size_t chunk_bwd_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+// Every chunk-start state (fp32, [b*H + h][chunk][dk][dv]) from F-order
+// records; GDR_ERR_UNSUPPORTED for shapes without them.
+int chunk_states_fm_launch(const ChunkArgs& a, const void* ws, float* Hst);
 int chunk_bwd_launch(const ChunkBwdArgs& a, void* ws, bool records_ready);
 int decode_launch(const DecodeArgs& a);
 size_t rwkv7_ws_bytes(int B, int H, int T, int dk, int dv, int chunk);
