@@ -172,28 +172,28 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_states_kernel(const char
         }
       }
     }
-    for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {
       const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
       float o[8];
       R.y8(t, j0, o);
       *(f32x4*)&Yl[t * LY + j0] = f32x4{o[0], o[1], o[2], o[3]};
       *(f32x4*)&Yl[t * LY + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
     }
-    for (int x = tid; x < DK * CM / 8; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, DK * CM / 8, kBwdThreads) {
       const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
       float o[8];
       R.kt8(jr, s0, o);
       *(f32x4*)&KTl[jr * LC + s0] = f32x4{o[0], o[1], o[2], o[3]};
       *(f32x4*)&KTl[jr * LC + s0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
     }
-    for (int x = tid; x < kVT * CM / 4; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, kVT * CM / 4, kBwdThreads) {
       const int v = x / (CM / 4), tq = 4 * (x % (CM / 4));
       float o[4];
       R.ut4(v0 + v, tq, o);
 #pragma unroll
       for (int e = 0; e < 4; ++e) Ul[(tq + e) * kVT + v] = o[e];
     }
-    for (int j = tid; j < DK; j += kBwdThreads) PIl[j] = R.pic(j);
+    GDR_STAGE_FOR(j, DK, kBwdThreads) PIl[j] = R.pic(j);
     __syncthreads();
     // V~ = U - Y S
     for (int it = wid; it < CM / 16; it += 4) {
@@ -268,21 +268,21 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       }
     }
     const int t0 = c * CM;
-    for (int x = tid; x < CM * CM / 8; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, CM * CM / 8, kBwdThreads) {
       const int t = x / (CM / 8), s0 = 8 * (x % (CM / 8));
       float o[8];
       R.m8(t, s0, o);
 #pragma unroll
       for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = o[e];
     }
-    for (int x = tid; x < DK * CM / 8; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, DK * CM / 8, kBwdThreads) {
       const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
       float o[8];
       R.kt8(jr, s0, o);
 #pragma unroll
       for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = o[e];
     }
-    for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {
       const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
       float o[8], p8[8];
       R.qp8(t, j0, o);
@@ -293,11 +293,12 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
         YTl[(j0 + e) * LC + t] = p8[e];
       }
     }
-    for (int x = tid; x < CM * kVT; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, CM * kVT, kBwdThreads) {
       const int t = x / kVT, v = x % kVT;
-      DOTl[v * LC + t] = t0 + t < T ? (float)dO[((size_t)bh * T + t0 + t) * DV + v0 + v] : 0.f;
+      const float g = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
+      DOTl[v * LC + t] = t0 + t < T ? g : 0.f;
     }
-    for (int j = tid; j < DK; j += kBwdThreads) PIl[j] = R.pic(j);
+    GDR_STAGE_FOR(j, DK, kBwdThreads) PIl[j] = R.pic(j);
     __syncthreads();
     // dV~ = M^T dO + K~ dS
     for (int it = wid; it < CM / 16; it += 4) {
@@ -368,21 +369,21 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   const float* dHc = dHs + item * DK * DV;
   float* dZc = dZ + item * CM * (DV + DK);
   const int vl = lane & 15;
-  for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {
+  GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {
     const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
     float o[8];
     R.y8(t, j0, o);
     *(f32x4*)&Yl[t * LY + j0] = f32x4{o[0], o[1], o[2], o[3]};
     *(f32x4*)&Yl[t * LY + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
   }
-  for (int x = tid; x < CM * CM / 8; x += kBwdThreads) {
+  GDR_STAGE_FOR(x, CM * CM / 8, kBwdThreads) {
     const int t = x / (CM / 8), s0 = 8 * (x % (CM / 8));
     float o[8];
     R.m8(t, s0, o);
 #pragma unroll
     for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = o[e];
   }
-  for (int x = tid; x < DK * CM / 8; x += kBwdThreads) {
+  GDR_STAGE_FOR(x, DK * CM / 8, kBwdThreads) {
     const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
     float o[8];
     R.kt8(jr, s0, o);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   for (int i = 0; i < PM; ++i) aM[i] = f4zero();
   float pacc = 0.f;
   for (int v0 = 0; v0 < DV; v0 += kVT) {
-    for (int x = tid; x < DK * kVT; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, DK * kVT, kBwdThreads) {
       const int j = x / kVT, v = x % kVT;
       const float s0 = Hc[(size_t)j * DV + v0 + v], ds = dHc[(size_t)j * DV + v0 + v];
       S0l[j * L16 + v] = s0;
@@ -404,13 +405,14 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
       dSl[j * L16 + v] = ds;
       dSTl[v * LY + j] = ds;
     }
-    for (int x = tid; x < CM * kVT; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, CM * kVT, kBwdThreads) {
       const int t = x / kVT, v = x % kVT;
-      const float g = t0 + t < T ? (float)dO[((size_t)bh * T + t0 + t) * DV + v0 + v] : 0.f;
+      const float g0 = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
+      const float g = t0 + t < T ? g0 : 0.f;
       dOl[t * L16 + v] = g;
       dOTl[v * LC + t] = g;
     }
-    for (int x = tid; x < kVT * CM / 4; x += kBwdThreads) {
+    GDR_STAGE_FOR(x, kVT * CM / 4, kBwdThreads) {
       const int v = x / (CM / 4), tq = 4 * (x % (CM / 4));
       float o[4];
       R.ut4(v0 + v, tq, o);
@@ -508,11 +510,12 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch, t0 = c * CM;
   const size_t item = (size_t)bh * nch + c;
   const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
-  for (int x = tid; x < CM * DK; x += kBwdThreads) {
+  GDR_STAGE_FOR(x, CM * DK, kBwdThreads) {
     const int t = x / DK, j = x % DK;
     const bool ok = t0 + t < T;
-    const size_t off = sK + (size_t)(t0 + t) * DK + j;
-    const float a = ok ? (float)alpha[off] : 1.f, kk = ok ? (float)k[off] : 0.f, bb = ok ? (float)bgate[off] : 0.f;
+    const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j;
+    const float a0 = (float)alpha[off], k0 = (float)k[off], b0 = (float)bgate[off];
+    const float a = ok ? a0 : 1.f, kk = ok ? k0 : 0.f, bb = ok ? b0 : 0.f;
     Lam[t * LP + j] = logf(a);
     Kl[t * LP + j] = kk;
     KHl[t * LP + j] = bb * kk;
@@ -559,26 +562,33 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
       dZc[(size_t)t * (DV + DK) + col] = x[t];
     }
     if (col < DV) {   // dV^: dv = dV^ * w, dw = dV^ * v
+      float wv[CM], vv[CM];
+#pragma unroll
+      for (int t = 0; t < CM; ++t) {
+        const size_t off = sV + (size_t)row_in(t0 + t, T) * DV + col;
+        wv[t] = (float)wgate[off];
+        vv[t] = (float)v[off];
+      }
 #pragma unroll
       for (int t = 0; t < CM; ++t) {
         if (t0 + t < T) {
           const size_t off = sV + (size_t)(t0 + t) * DV + col;
-          dv_out[off] = x[t] * (float)wgate[off];
-          dw_out[off] = x[t] * (float)v[off];
+          dv_out[off] = x[t] * wv[t];
+          dw_out[off] = x[t] * vv[t];
         }
       }
     }
   }
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
   const Rec<E, FM> R{ws + item * RL.bytes, RL, DK, CM};
-  for (int x = tid; x < DV * CM / 4; x += kBwdThreads) {      // U^T rows
+  GDR_STAGE_FOR(x, DV * CM / 4, kBwdThreads) {      // U^T rows
     const int cc = x / (CM / 4), sq = 4 * (x % (CM / 4));
     float o[4];
     R.ut4(cc, sq, o);
 #pragma unroll
     for (int e = 0; e < 4; ++e) Zl[(sq + e) * NX + cc] = o[e];
   }
-  for (int x = tid; x < CM * DK / 8; x += kBwdThreads) {      // Y rows
+  GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {      // Y rows
     const int sr = x / (DK / 8), j0 = 8 * (x % (DK / 8));
     float o[8];
     R.y8(sr, j0, o);
@@ -602,9 +612,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
 }
 
 // ------------------------------------------------------------------ decay and key/query gradients
-// One workgroup per (b, h, chunk, 64 key channels): lane = channel, and the
-// four waves split the rows (row sums) and the columns (column sums). Per
-// channel, with e_ts = exp(Lambda_t - Lambda_s) (t >= s):
+// Per channel j, with e_ts = exp(Lambda_t - Lambda_s) (t >= s):
 //   dk^_t = sum_{s<t} dL_ts e_ts k_s + pi_t dK^_pi_t
 //   dq_t  = sum_{s<=t} dM_ts e_ts k_s + pi_t dQ_pi_t
 //   dk_s  = sum_{t>s} dL_ts e_ts k^_t + sum_{t>=s} dM_ts e_ts q_t + pi_{C,s} dK~_s
@@ -612,121 +620,260 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
 //               - k_t pi_{C,t} dK~_t, and at t = C-1 also + sum_s k_s pi_{C,s} dK~_s
 //               + pi_C dpi_C
 //   dalpha_r = (sum_{t >= r} dLambda_t) / alpha_r,  db = k dk^,  dk += b dk^.
-constexpr int kDecayWaves = 8;
+// One workgroup per (b, h, chunk, 32 key channels), four waves; wave w owns
+// the 16-row block w, as rows t (dk^, dq) and as columns s (dk). The sums are
+// split at block boundaries the way the forward splits its Gram matrices:
+// for t in block I and s in an earlier block, e_ts = e^{Lambda_t - Lambda_p}
+// e^{Lambda_p - Lambda_s} with p the last row before block I, both factors
+// <= 1, so the off-diagonal part of a row block is one fp32 MFMA product of
+// dL (or dM) with the rows k_s e^{Lambda_p - Lambda_s} (formed lane by lane as
+// the B operand), scaled by e^{Lambda_t - Lambda_p}; the columns likewise with
+// p the block's last row. Inside a block the pairwise factors are exact.
+constexpr int kDecayThreads = 256;
+
+template <int DK, int CM>
+struct DecayShape {
+  static constexpr int NCH = DK < 32 ? DK : 32;   // key channels per workgroup
+  static constexpr int NG = DK / NCH, NJT = NCH / 16, NB = CM / 16;
+  static constexpr int LP = NCH + 1, LD = CM + 1; // LDS pitches (floats)
+  // the cumulative sums over t run as kDecayThreads / NCH segments of RPS rows
+  static constexpr int NSEG = kDecayThreads / NCH, RPS = CM / NSEG;
+  static constexpr int LDS = 4 * (4 * CM * LP + 2 * CM * LD + 4 * NCH + kDecayThreads);
+};
 
 template <typename E, int DK, int CM>
-__global__ __launch_bounds__(64 * kDecayWaves) void gdn2_bwd_decay_kernel(
+__global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ alpha, const E* __restrict__ bgate,
     const float* __restrict__ dZ, const float* __restrict__ dQp, const float* __restrict__ dKt,
     const float* __restrict__ dMb, const float* __restrict__ dLb, const float* __restrict__ dpic,
     float* __restrict__ dq_out, float* __restrict__ dk_out, float* __restrict__ da_out,
     float* __restrict__ db_out, int T, int DV) {
-  constexpr int NG = (DK + 63) / 64, NW = kDecayWaves, RPW = (CM + NW - 1) / NW;
-  __shared__ float Lam[CM][64], Kc[CM][64], KHc[CM][64], Qc[CM][64], DLam[CM][64];
-  __shared__ float dLs[CM][CM], dMs[CM][CM];
-  __shared__ float gKs[NW][64];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  using Sh = DecayShape<DK, CM>;
+  constexpr int NCH = Sh::NCH, NG = Sh::NG, NJT = Sh::NJT, NB = Sh::NB, LP = Sh::LP, LD = Sh::LD;
+  extern __shared__ __attribute__((aligned(16))) float dsm[];
+  float* Lam = dsm;                 // Lambda [t][j]
+  float* Kc = Lam + CM * LP;        // k      [t][j]
+  float* KHc = Kc + CM * LP;        // b * k  [t][j]
+  float* Qc = KHc + CM * LP;        // q      [t][j]
+  float* dLs = Qc + CM * LP;        // dL     [t][s]
+  float* dMs = dLs + CM * LD;       // dM     [t][s]
+  float* gKs = dMs + CM * LD;       // [wave][j] partial sums of k_s pi_{C,s} dK~_s
+  float* Part = gKs + 4 * NCH;      // [segment][j] partial sums of the cumulative sums
+  float* DLam = dLs;                // d Lambda [t][j], once the products are done
+  static_assert(Sh::RPS >= 1 && Sh::NSEG * Sh::RPS == CM, "decay kernel: row segments");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int m16 = lane & 15, k4 = lane >> 4;       // MFMA lane roles
   const int nch = (T + CM - 1) / CM;
-  const int grp = blockIdx.x % NG, item_i = blockIdx.x / NG;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, NG);
+  const int grp = lin % NG, item_i = lin / NG;
   const int bh = item_i / nch, c = item_i % nch, t0 = c * CM;
-  const size_t item = (size_t)bh * nch + c;
-  const int j = 64 * grp + lane;
-  const bool act = j < DK;
-  const int jj = act ? j : 0;
+  const size_t item = (size_t)item_i;
+  const int j0 = NCH * grp;
   const size_t sK = (size_t)bh * T * DK;
-  const float* dLc = dLb + item * CM * CM;
-  const float* dMc = dMb + item * CM * CM;
-  for (int x = threadIdx.x; x < CM * CM; x += 64 * NW) {
-    dLs[x / CM][x % CM] = dLc[x];
-    dMs[x / CM][x % CM] = dMc[x];
-  }
-  for (int t = wid; t < CM; t += NW) {
-    const bool ok = t0 + t < T;
-    const size_t off = sK + (size_t)(t0 + t) * DK + jj;
-    const float a = ok ? (float)alpha[off] : 1.f, kk = ok ? (float)k[off] : 0.f;
-    const float bb = ok ? (float)bgate[off] : 0.f, qq = ok ? (float)q[off] : 0.f;
-    Lam[t][lane] = logf(a);
-    Kc[t][lane] = kk;
-    KHc[t][lane] = bb * kk;
-    Qc[t][lane] = qq;
-  }
-  __syncthreads();
-  if (wid == 0) {   // Lambda_t = sum_{r <= t} log alpha_r
-    float acc = 0.f;
-    for (int t = 0; t < CM; ++t) {
-      acc += Lam[t][lane];
-      Lam[t][lane] = acc;
-    }
-  }
-  __syncthreads();
   const float* dZc = dZ + item * CM * (DV + DK);
   const float* dQc = dQp + item * CM * DK;
   const float* dKc = dKt + item * CM * DK;
-  // this wave's rows (and, below, columns) t = wid + NW i
-  float dkh_r[RPW], dlam_r[RPW];
+  const int B0 = 16 * wid;                          // this wave's block
+  const int cj = tid % NCH, sg = tid / NCH, r0 = sg * Sh::RPS;
+  // everything a lane reads from memory after the products starts loading
+  // now, so that no load latency sits between the phases: the direct terms of
+  // its output entries (rows B0 + 4 k4 + e, channels 16 n + m16), their erase
+  // gates, the decays of its row segment, dpi_C
+  float pdz[NJT][4], pdq[NJT][4], pdk[NJT][4], pbg[NJT][4], pal[Sh::RPS], pdp = 0.f;
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int t = wid + NW * i;
-    dkh_r[i] = dlam_r[i] = 0.f;
-    if (t < CM) {
-      const float lt = Lam[t][lane];
-      float dkh = 0.f, dq = 0.f;
-#pragma unroll 8
-      for (int s = 0; s < CM; ++s) {
-        if (s <= t) {
-          const float ek = __expf(lt - Lam[s][lane]) * Kc[s][lane];
-          dq += dMs[t][s] * ek;
-          dkh += dLs[t][s] * ek;   // dL is zero on and above the diagonal
+  for (int n = 0; n < NJT; ++n)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = (wid < NB ? B0 : 0) + 4 * k4 + e, j = j0 + 16 * n + m16;
+      pdz[n][e] = dZc[(size_t)t * (DV + DK) + DV + j];
+      pdq[n][e] = dQc[t * DK + j];
+      pdk[n][e] = dKc[t * DK + j];
+      const float bg = (float)bgate[sK + (size_t)row_in(t0 + t, T) * DK + j];
+      pbg[n][e] = t0 + t < T ? bg : 0.f;
+    }
+#pragma unroll
+  for (int i = 0; i < Sh::RPS; ++i)
+    pal[i] = (float)alpha[sK + (size_t)row_in(t0 + r0 + i, T) * DK + j0 + cj];
+  if (tid < NCH) pdp = dpic[item * DK + j0 + tid];
+  GDR_STAGE_FOR(x, CM * NCH, kDecayThreads) {
+    const int t = x / NCH, jl = x % NCH;
+    const bool ok = t0 + t < T;
+    const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j0 + jl;
+    const float a0 = (float)alpha[off], k0 = (float)k[off], b0 = (float)bgate[off], q0 = (float)q[off];
+    const float a = ok ? a0 : 1.f, kk = ok ? k0 : 0.f;
+    const float bb = ok ? b0 : 0.f, qq = ok ? q0 : 0.f;
+    Lam[t * LP + jl] = logf(a);
+    Kc[t * LP + jl] = kk;
+    KHc[t * LP + jl] = bb * kk;
+    Qc[t * LP + jl] = qq;
+  }
+  const float* dLc = dLb + item * CM * CM;
+  const float* dMc = dMb + item * CM * CM;
+  GDR_STAGE_FOR(x, CM * CM / 4, kDecayThreads) {
+    const int t = x / (CM / 4), s4 = 4 * (x % (CM / 4));
+    const f32x4 l4 = *(const f32x4*)(dLc + t * CM + s4), m4 = *(const f32x4*)(dMc + t * CM + s4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dLs[t * LD + s4 + e] = l4[e];
+      dMs[t * LD + s4 + e] = m4[e];
+    }
+  }
+  __syncthreads();
+  // Lambda_t = sum_{r <= t} log alpha_r: row segments of RPS rows per thread,
+  // their totals, then each segment from the sum of the ones before it
+  {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < Sh::RPS; ++i) tot += Lam[(r0 + i) * LP + cj];
+    Part[sg * NCH + cj] = tot;
+  }
+  __syncthreads();
+  {
+    float acc = 0.f;
+    for (int g = 0; g < sg; ++g) acc += Part[g * NCH + cj];
+#pragma unroll
+    for (int i = 0; i < Sh::RPS; ++i) {
+      acc += Lam[(r0 + i) * LP + cj];
+      Lam[(r0 + i) * LP + cj] = acc;
+    }
+  }
+  __syncthreads();
+  float gK[NJT], dlam[NJT][4];
+#pragma unroll
+  for (int n = 0; n < NJT; ++n) gK[n] = 0.f;
+  if (wid < NB) {
+    // ---- rows t of block wid: dk^ and dq
+    float dkh[NJT][4];
+#pragma unroll
+    for (int n = 0; n < NJT; ++n) {
+      const int jl = 16 * n + m16;
+      f32x4 a1 = f4zero(), a2 = f4zero();
+      const float lp = wid > 0 ? Lam[(B0 - 1) * LP + jl] : 0.f;
+      for (int s0 = 0; s0 < B0; s0 += 4) {
+        const int s = s0 + k4;
+        const float bv = __expf(lp - Lam[s * LP + jl]) * Kc[s * LP + jl];
+        a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(dLs[(B0 + m16) * LD + s], bv, a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(dMs[(B0 + m16) * LD + s], bv, a2, 0, 0, 0);
+      }
+      float lt[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lt[e] = Lam[(B0 + 4 * k4 + e) * LP + jl];
+        const float sc = wid > 0 ? __expf(lt[e] - lp) : 0.f;
+        a1[e] *= sc;
+        a2[e] *= sc;
+      }
+#pragma unroll 4
+      for (int s = B0; s < B0 + 16; ++s) {          // the diagonal block, exact
+        const float ls = Lam[s * LP + jl], ks = Kc[s * LP + jl];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = B0 + 4 * k4 + e;
+          if (s <= t) {
+            const float wv = __expf(lt[e] - ls) * ks;
+            a2[e] += dMs[t * LD + s] * wv;
+            if (s < t) a1[e] += dLs[t * LD + s] * wv;
+          }
         }
       }
-      const float pt = __expf(lt);
-      dq += pt * dQc[t * DK + jj];
-      dkh += pt * dZc[(size_t)t * (DV + DK) + DV + jj];
-      dkh_r[i] = dkh;
-      dlam_r[i] = KHc[t][lane] * dkh + Qc[t][lane] * dq;
-      if (act && t0 + t < T) dq_out[sK + (size_t)(t0 + t) * DK + j] = dq;
-    }
-  }
-  // columns: dk_s and the column side of dLambda
-  const float lC = Lam[CM - 1][lane];
-  float gK = 0.f;
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int s = wid + NW * i;
-    if (s < CM) {
-      const float ls = Lam[s][lane];
-      float dk = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < CM; ++t) {
-        if (t >= s) dk += __expf(Lam[t][lane] - ls) * (dMs[t][s] * Qc[t][lane] + dLs[t][s] * KHc[t][lane]);
+      for (int e = 0; e < 4; ++e) {
+        const int t = B0 + 4 * k4 + e;
+        const float pt = __expf(lt[e]);
+        a1[e] += pt * pdz[n][e];
+        a2[e] += pt * pdq[n][e];
+        dkh[n][e] = a1[e];
+        dlam[n][e] = KHc[t * LP + jl] * a1[e] + Qc[t * LP + jl] * a2[e];
+        if (t0 + t < T) dq_out[sK + (size_t)(t0 + t) * DK + j0 + jl] = a2[e];
       }
-      const float ks = Kc[s][lane];
-      const float kt = __expf(lC - ls) * dKc[s * DK + jj];   // pi_{C,s} dK~_s
-      DLam[s][lane] = dlam_r[i] - ks * (dk + kt);
-      gK += ks * kt;
-      dk += kt;
-      const size_t off = sK + (size_t)(t0 + s) * DK + j;
-      if (act && t0 + s < T) {
-        const float bb = (float)bgate[off];
-        dk_out[off] = dk + bb * dkh_r[i];
-        db_out[off] = ks * dkh_r[i];
+    }
+    // ---- columns s of block wid: dk, and the column side of d Lambda
+#pragma unroll
+    for (int n = 0; n < NJT; ++n) {
+      const int jl = 16 * n + m16;
+      const float lq = Lam[(B0 + 15) * LP + jl];
+      f32x4 acc = f4zero();
+      for (int tb = B0 + 16; tb < CM; tb += 4) {
+        const int t = tb + k4;
+        const float sc = __expf(Lam[t * LP + jl] - lq);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dLs[t * LD + B0 + m16], sc * KHc[t * LP + jl], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dMs[t * LD + B0 + m16], sc * Qc[t * LP + jl], acc, 0, 0, 0);
+      }
+      float ls[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ls[e] = Lam[(B0 + 4 * k4 + e) * LP + jl];
+        acc[e] *= __expf(lq - ls[e]);
+      }
+#pragma unroll 4
+      for (int t = B0; t < B0 + 16; ++t) {          // the diagonal block, exact
+        const float lt = Lam[t * LP + jl], kh = KHc[t * LP + jl], qq = Qc[t * LP + jl];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = B0 + 4 * k4 + e;
+          if (t >= s) {
+            const float wv = __expf(lt - ls[e]);
+            acc[e] += wv * (dMs[t * LD + s] * qq + (t > s ? dLs[t * LD + s] * kh : 0.f));
+          }
+        }
+      }
+      const float lCj = Lam[(CM - 1) * LP + jl];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = B0 + 4 * k4 + e;
+        const float ks = Kc[s * LP + jl];
+        const float kt = __expf(lCj - ls[e]) * pdk[n][e];   // pi_{C,s} dK~_s
+        dlam[n][e] -= ks * (acc[e] + kt);
+        gK[n] += ks * kt;
+        if (t0 + s < T) {
+          const size_t off = sK + (size_t)(t0 + s) * DK + j0 + jl;
+          dk_out[off] = acc[e] + kt + pbg[n][e] * dkh[n][e];
+          db_out[off] = ks * dkh[n][e];
+        }
       }
     }
   }
-  gKs[wid][lane] = gK;
+  // per-channel sums of k_s pi_{C,s} dK~_s: over the four lane groups of the
+  // wave, then (below) over the waves
+#pragma unroll
+  for (int n = 0; n < NJT; ++n) {
+    float g = gK[n];
+    g += __shfl_xor(g, 16, 64);
+    g += __shfl_xor(g, 32, 64);
+    if (k4 == 0) gKs[wid * NCH + 16 * n + m16] = wid < NB ? g : 0.f;
+  }
+  __syncthreads();                                  // dL, dM no longer read: d Lambda goes there
+  if (wid < NB) {
+#pragma unroll
+    for (int n = 0; n < NJT; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DLam[(B0 + 4 * k4 + e) * LP + 16 * n + m16] = dlam[n][e];
+  }
   __syncthreads();
-  if (wid == 0) {
+  if (tid < NCH) {
     float g = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) g += gKs[w][lane];
-    DLam[CM - 1][lane] += g + __expf(lC) * dpic[item * DK + jj];
+    for (int w = 0; w < 4; ++w) g += gKs[w * NCH + tid];
+    const float lC = Lam[(CM - 1) * LP + tid];
+    DLam[(CM - 1) * LP + tid] += g + __expf(lC) * pdp;
+  }
+  __syncthreads();
+  // dalpha_r = (sum_{t >= r} d Lambda_t) / alpha_r, by row segments as above
+  {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < Sh::RPS; ++i) tot += DLam[(r0 + i) * LP + cj];
+    Part[sg * NCH + cj] = tot;
+  }
+  __syncthreads();
+  {
     float acc = 0.f;
-    for (int t = CM - 1; t >= 0; --t) {
-      acc += DLam[t][lane];
-      if (act && t0 + t < T) {
-        const size_t off = sK + (size_t)(t0 + t) * DK + j;
-        da_out[off] = acc / (float)alpha[off];
-      }
+    for (int g = sg + 1; g < Sh::NSEG; ++g) acc += Part[g * NCH + cj];
+#pragma unroll
+    for (int i = Sh::RPS - 1; i >= 0; --i) {
+      const int t = r0 + i;
+      acc += DLam[t * LP + cj];
+      if (t0 + t < T) da_out[sK + (size_t)(t0 + t) * DK + j0 + cj] = acc / pal[i];
     }
   }
 }
@@ -804,8 +951,10 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
     const float *cdZ = dZ, *cdQ = dQp, *cdK = dKt, *cdM = dM, *cdL = dL, *cpi = dpic;
     float *dq = a.dq_out, *dk = a.dk_out, *da = a.dalpha_out, *db = a.db_out;
     void* args[] = {&q, &k, &al, &bg, &cdZ, &cdQ, &cdK, &cdM, &cdL, &cpi, &dq, &dk, &da, &db, &T, &DV};
-    const int ng = (DK + 63) / 64;
-    if (hipLaunchKernel((const void*)kern, dim3(BH * nch * ng), dim3(64 * kDecayWaves), args, 0, st) != hipSuccess)
+    using DS = DecayShape<DK, CM>;
+    if (!allow_lds((const void*)kern, DS::LDS)) return GDR_ERR_LAUNCH;
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch * DS::NG), dim3(kDecayThreads), args, DS::LDS, st) !=
+        hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   return GDR_OK;

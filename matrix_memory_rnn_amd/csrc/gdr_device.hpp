@@ -301,6 +301,20 @@ __device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int
 // Workgroup index -> linear work index that places consecutive work items of
 // one group (e.g. the value tiles of one head) on the same XCD. Workgroups are
 // dispatched round-robin over the 8 XCDs of an MI355X; each XCD has its own L2.
+// A staging loop x = tid, tid + NT, .. < N over compile-time N and NT, fully
+// unrolled, so that the loads of all its iterations are issued before the
+// first of them is used: a plain strided loop (whose trip count the compiler
+// cannot see) waits for each iteration's loads before issuing the next. Loads
+// inside must be unconditional to be issued together: clamp the row with
+// row_in and select the value afterwards.
+#define GDR_STAGE_FOR(x, N, NT)                                                       \
+  _Pragma("unroll") for (int x##_it = 0; x##_it < ((N) + (NT) - 1) / (NT); ++x##_it) \
+    if (const int x = tid + x##_it * (NT); (N) % (NT) == 0 || x < (N))
+
+// Row t of a sequence of T rows, or its last row when t is past the end (the
+// caller replaces what it read there).
+__device__ __forceinline__ int row_in(int t, int T) { return t < T ? t : T - 1; }
+
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks, int group) {
   constexpr int kXcd = 8;
   if (nblocks % kXcd != 0) return bid;

@@ -83,20 +83,24 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
   const R7Layout RL = r7_layout(DK, DV, CM);
   float* rec = ws + ((size_t)bh * nch + ch) * RL.floats;
   // rows past T: w = 1, a = kw = q = 0, c = 0, u = 0 (identity steps)
-  for (int x = tid; x < CM * DK; x += kR7Threads) {
+  GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
     const int t = x / DK, j = x % DK;
     const bool ok = t0 + t < T;
-    const size_t off = sK + (size_t)(t0 + t) * DK + j;
-    const float aa = ok ? (float)a[off] : 0.f;
-    Lam[t * LP + j] = ok ? logf((float)w[off]) : 0.f;
+    const int tr = row_in(t0 + t, T);
+    const size_t off = sK + (size_t)tr * DK + j;
+    const float a0 = (float)a[off], w0 = (float)w[off], z0 = (float)kw[off], q0 = (float)q[off];
+    const float c0 = c[(size_t)bh * T + tr];
+    const float aa = ok ? a0 : 0.f;
+    Lam[t * LP + j] = ok ? logf(w0) : 0.f;
     Al[t * LP + j] = aa;
-    Zl[t * LP + j] = ok ? (float)kw[off] : 0.f;
-    Ql[t * LP + j] = ok ? (float)q[off] : 0.f;
-    Yl[t * LP + j] = ok ? c[(size_t)bh * T + t0 + t] * aa : 0.f;
+    Zl[t * LP + j] = ok ? z0 : 0.f;
+    Ql[t * LP + j] = ok ? q0 : 0.f;
+    Yl[t * LP + j] = ok ? c0 * aa : 0.f;
   }
-  for (int x = tid; x < CM * DV; x += kR7Threads) {
+  GDR_STAGE_FOR(x, CM * DV, kR7Threads) {
     const int t = x / DV, v = x % DV;
-    UT[v * LQ + t] = t0 + t < T ? (float)u[sV + (size_t)(t0 + t) * DV + v] : 0.f;
+    const float u0 = (float)u[sV + (size_t)row_in(t0 + t, T) * DV + v];
+    UT[v * LQ + t] = t0 + t < T ? u0 : 0.f;
   }
   __syncthreads();
   for (int j = tid; j < DK; j += kR7Threads) {
@@ -230,29 +234,29 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
         for (int e = 0; e < 4; ++e) STl[vl * LY + 16 * J + 4 * (lane >> 4) + e] = S[i][e];
       }
     }
-    for (int x = tid; x < CM * DK / 4; x += kR7Threads) {
+    GDR_STAGE_FOR(x, CM * DK / 4, kR7Threads) {
       const int t = x / (DK / 4), j0 = 4 * (x % (DK / 4));
       *(f32x4*)&Gl[t * LY + j0] = *(const f32x4*)&rec[RL.g + t * DK + j0];
       *(f32x4*)&Qpl[t * LY + j0] = *(const f32x4*)&rec[RL.qp + t * DK + j0];
     }
-    for (int x = tid; x < CM * CM / 4; x += kR7Threads) {
+    GDR_STAGE_FOR(x, CM * CM / 4, kR7Threads) {
       const int t = x / (CM / 4), s0 = 4 * (x % (CM / 4));
       *(f32x4*)&Mal[t * LC + s0] = *(const f32x4*)&rec[RL.ma + t * CM + s0];
     }
-    for (int x = tid; x < DK * CM / 4; x += kR7Threads) {
+    GDR_STAGE_FOR(x, DK * CM / 4, kR7Threads) {
       const int j = x / (CM / 4), s0 = 4 * (x % (CM / 4));
       *(f32x4*)&ATl[j * LC + s0] = *(const f32x4*)&rec[RL.at + j * CM + s0];
     }
-    for (int x = tid; x < CM * kR7VT / 4; x += kR7Threads) {
+    GDR_STAGE_FOR(x, CM * kR7VT / 4, kR7Threads) {
       const int t = x / (kR7VT / 4), q0 = 4 * (x % (kR7VT / 4));
       *(f32x4*)&E0l[t * kR7VT + q0] = *(const f32x4*)&rec[RL.e0 + t * DV + v0 + q0];
       *(f32x4*)&OZl[t * kR7VT + q0] = *(const f32x4*)&rec[RL.oz + t * DV + v0 + q0];
     }
-    for (int x = tid; x < DK * kR7VT / 4; x += kR7Threads) {
+    GDR_STAGE_FOR(x, DK * kR7VT / 4, kR7Threads) {
       const int j = x / (kR7VT / 4), q0 = 4 * (x % (kR7VT / 4));
       *(f32x4*)&WZl[j * kR7VT + q0] = *(const f32x4*)&rec[RL.wz + j * DV + v0 + q0];
     }
-    for (int j = tid; j < DK; j += kR7Threads) PIl[j] = rec[RL.pic + j];
+    GDR_STAGE_FOR(j, DK, kR7Threads) PIl[j] = rec[RL.pic + j];
     __syncthreads();
     // E = E0 + G S0 (to LDS, transposed); the readout's Q_pi S0 kept in registers
     f32x4 oacc[(NT + 3) / 4];
