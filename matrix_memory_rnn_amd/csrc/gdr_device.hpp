@@ -298,9 +298,6 @@ __device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int
   }
 }
 
-// Workgroup index -> linear work index that places consecutive work items of
-// one group (e.g. the value tiles of one head) on the same XCD. Workgroups are
-// dispatched round-robin over the 8 XCDs of an MI355X; each XCD has its own L2.
 // A staging loop x = tid, tid + NT, .. < N over compile-time N and NT, fully
 // unrolled, so that the loads of all its iterations are issued before the
 // first of them is used: a plain strided loop (whose trip count the compiler
@@ -315,6 +312,9 @@ __device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int
 // caller replaces what it read there).
 __device__ __forceinline__ int row_in(int t, int T) { return t < T ? t : T - 1; }
 
+// Workgroup index -> linear work index that places consecutive work items of
+// one group (e.g. the value tiles of one head) on the same XCD. Workgroups are
+// dispatched round-robin over the 8 XCDs of an MI355X; each XCD has its own L2.
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks, int group) {
   constexpr int kXcd = 8;
   if (nblocks % kXcd != 0) return bid;

@@ -58,95 +58,181 @@ size_t rwkv7_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
 }
 
 // ------------------------------------------------------------------ intra-chunk kernel
+// One workgroup (four waves) per (b, h, chunk), fp32 throughout. The four
+// decay-scaled Gram matrices are fp32 MFMA products over the key channels,
+// split at the 16-row blocks of the chunk as the GDN-2 forward splits its
+// Gram: for row block I with pivot p = 16 I - 1 (Lambda_{-1} = 0),
+//   M[t][s] = sum_j (q_t e^{Lambda_t - Lambda_p})_j (a_s e^{Lambda_p - Lambda_s})_j,
+//   L[t][s] = sum_j (c_t a_t e^{Lambda_{t-1} - Lambda_p})_j (a_s e^{Lambda_p - Lambda_s})_j,
+// and likewise with kw_s. The left factors are <= 1; the right ones are <= 1
+// for s <= p and at most 1 / (the block's decay) inside the block, so a block
+// in which some channel decays below 2^-60 takes exact pairwise factors for
+// its diagonal tile instead. The products with U (L_z U, M_z U, Z~^T U) are
+// MFMA tiles too; the unit lower-triangular solve runs one column per thread.
 template <typename E, int DK, int CM>
 __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ w, const E* __restrict__ a, const float* __restrict__ c,
     const E* __restrict__ kw, const E* __restrict__ u, float* __restrict__ ws, int T, int DV) {
-  constexpr int LP = DK + 1, LQ = CM + 1;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* Lam = (float*)smem;            // Lambda [t][j]
-  float* Al = Lam + CM * LP;            // a      [t][j]
-  float* Zl = Al + CM * LP;             // kw     [t][j]
-  float* Ql = Zl + CM * LP;             // q      [t][j]
-  float* Yl = Ql + CM * LP;             // c a    [t][j]
-  float* La = Yl + CM * LP;             // L_a    [t][s]
-  float* Lz = La + CM * LQ;
-  float* Ma = Lz + CM * LQ;
-  float* Mz = Ma + CM * LQ;
-  float* UT = Mz + CM * LQ;             // u^T    [v][s]
-  float* Xl = UT + DV * LQ;             // [L_z U | Y_pi'] -> [E0 | G], [t][c]
-  const int NX = DV + DK + 1;
-  const int tid = threadIdx.x;
+  constexpr int P = DK + 4, PC = CM + 4, NB = CM / 16;
+  extern __shared__ __attribute__((aligned(16))) float r7s[];
+  float* Lam = r7s;                     // Lambda [t][j]
+  float* Al = Lam + CM * P;             // a      [t][j]
+  float* Zl = Al + CM * P;              // kw     [t][j]
+  float* Ql = Zl + CM * P;              // q      [t][j]
+  float* cv = Ql + CM * P;              // c      [t]
+  float* La = cv + CM;                  // L_a    [t][s]
+  float* Lz = La + CM * PC;             // L_z
+  float* Ma = Lz + CM * PC;             // M_a
+  float* Mz = Ma + CM * PC;             // M_z
+  float* TMP = Mz + CM * PC;
+  // phase G
+  float* Aq = TMP;                      // q_t e^{Lambda_t - Lambda_p}         [16][j]
+  float* Ay = Aq + 16 * P;              // c_t a_t e^{Lambda_{t-1} - Lambda_p} [16][j]
+  float* Ba = Ay + 16 * P;              // a_s e^{Lambda_p - Lambda_s}          [s][j]
+  float* Bz = Ba + CM * P;              // kw_s e^{Lambda_p - Lambda_s}         [s][j]
+  // phase R
+  const int NX = DV + DK + 4;
+  float* UT = TMP;                      // u^T  [v][s]
+  float* Xl = UT + DV * PC;             // [L_z U | Y_pi'] -> [E0 | G]  [t][col]
+  float* ZT = Xl + CM * NX;             // Z~^T [j][s] = e^{Lambda_C - Lambda_s} kw_s
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nch = (T + CM - 1) / CM;
   const int bh = blockIdx.x / nch, ch = blockIdx.x % nch, t0 = ch * CM;
   const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
   const R7Layout RL = r7_layout(DK, DV, CM);
   float* rec = ws + ((size_t)bh * nch + ch) * RL.floats;
+  __shared__ int gflag[4];
   // rows past T: w = 1, a = kw = q = 0, c = 0, u = 0 (identity steps)
   GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
     const int t = x / DK, j = x % DK;
     const bool ok = t0 + t < T;
-    const int tr = row_in(t0 + t, T);
-    const size_t off = sK + (size_t)tr * DK + j;
+    const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j;
     const float a0 = (float)a[off], w0 = (float)w[off], z0 = (float)kw[off], q0 = (float)q[off];
-    const float c0 = c[(size_t)bh * T + tr];
-    const float aa = ok ? a0 : 0.f;
-    Lam[t * LP + j] = ok ? logf(w0) : 0.f;
-    Al[t * LP + j] = aa;
-    Zl[t * LP + j] = ok ? z0 : 0.f;
-    Ql[t * LP + j] = ok ? q0 : 0.f;
-    Yl[t * LP + j] = ok ? c0 * aa : 0.f;
+    Lam[t * P + j] = ok ? logf(w0) : 0.f;
+    Al[t * P + j] = ok ? a0 : 0.f;
+    Zl[t * P + j] = ok ? z0 : 0.f;
+    Ql[t * P + j] = ok ? q0 : 0.f;
   }
+  GDR_STAGE_FOR(t, CM, kR7Threads) {
+    const float c0 = c[(size_t)bh * T + row_in(t0 + t, T)];
+    cv[t] = t0 + t < T ? c0 : 0.f;
+  }
+  if (tid < 4) gflag[tid] = 0;
+  // the Gram tiles above the diagonal blocks are never formed: zero
+  GDR_STAGE_FOR(x, 4 * CM * PC, kR7Threads) La[x] = 0.f;
+  __syncthreads();
+  GDR_STAGE_FOR(j, DK, kR7Threads) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < CM; ++t) {
+      acc += Lam[t * P + j];
+      Lam[t * P + j] = acc;
+    }
+    // blocks in which channel j decays below 2^-60 (log 2^-60 = -41.59)
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      const float lp = I > 0 ? Lam[(16 * I - 1) * P + j] : 0.f;
+      if (Lam[(16 * I + 15) * P + j] - lp < -41.5f) gflag[I] = 1;
+    }
+  }
+  __syncthreads();
+  // ---- phase G: the Gram matrices, one row block at a time
+  for (int I = 0; I < NB; ++I) {
+    const int p = 16 * I - 1, ns = 16 * (I + 1);
+    GDR_STAGE_FOR(x, 16 * DK, kR7Threads) {
+      const int tl = x / DK, j = x % DK, t = 16 * I + tl;
+      const float lp = I > 0 ? Lam[p * P + j] : 0.f;
+      const float lt1 = t > 0 ? Lam[(t - 1) * P + j] : 0.f;
+      Aq[tl * P + j] = Ql[t * P + j] * __expf(Lam[t * P + j] - lp);
+      Ay[tl * P + j] = cv[t] * Al[t * P + j] * __expf(lt1 - lp);
+    }
+    GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
+      const int s2 = x / DK, j = x % DK;
+      if (s2 < ns) {
+        const float lp = I > 0 ? Lam[p * P + j] : 0.f;
+        const float e = __expf(lp - Lam[s2 * P + j]);
+        Ba[s2 * P + j] = Al[s2 * P + j] * e;
+        Bz[s2 * P + j] = Zl[s2 * P + j] * e;
+      }
+    }
+    __syncthreads();
+    const bool exact = gflag[I] != 0;
+    // tiles (which, J): which = 0 M_a, 1 M_z, 2 L_a, 3 L_z; J = 0 .. I
+    for (int tile = wid; tile < 4 * (I + 1); tile += 4) {
+      const int which = tile % 4, J = tile / 4;
+      const float* A = which < 2 ? Aq : Ay;
+      const float* Bm = (which & 1) ? Bz : Ba;
+      f32x4 acc = f4zero();
+      tile_nt(acc, A, P, 0, Bm, P, 16 * J, DK, lane);
+      float* G = which == 0 ? Ma : which == 1 ? Mz : which == 2 ? La : Lz;
+      const bool strict = which >= 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * (lane >> 4) + e, s2 = 16 * J + (lane & 15);
+        float val = acc[e];
+        if (exact && J == I) {
+          // the pairwise decays of the diagonal tile, exact
+          val = 0.f;
+          if (strict ? s2 < t : s2 <= t) {
+            const float* Xs = (which & 1) ? Zl : Al;
+            for (int j = 0; j < DK; ++j) {
+              const float ls = Lam[s2 * P + j];
+              const float lt = strict ? (t > 0 ? Lam[(t - 1) * P + j] : 0.f) : Lam[t * P + j];
+              const float lhs = strict ? cv[t] * Al[t * P + j] : Ql[t * P + j];
+              val += lhs * __expf(lt - ls) * Xs[s2 * P + j];
+            }
+          }
+        }
+        G[t * PC + s2] = (strict ? s2 < t : s2 <= t) ? val : 0.f;
+      }
+    }
+    __syncthreads();
+  }
+  // ---- phase R
   GDR_STAGE_FOR(x, CM * DV, kR7Threads) {
     const int t = x / DV, v = x % DV;
     const float u0 = (float)u[sV + (size_t)row_in(t0 + t, T) * DV + v];
-    UT[v * LQ + t] = t0 + t < T ? u0 : 0.f;
+    UT[v * PC + t] = t0 + t < T ? u0 : 0.f;
   }
-  __syncthreads();
-  for (int j = tid; j < DK; j += kR7Threads) {
-    float acc = 0.f;
-    for (int t = 0; t < CM; ++t) {
-      acc += Lam[t * LP + j];
-      Lam[t * LP + j] = acc;
-    }
+  GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
+    const int t = x / DK, j = x % DK;
+    const float lt1 = t > 0 ? Lam[(t - 1) * P + j] : 0.f;
+    Xl[t * NX + DV + j] = cv[t] * Al[t * P + j] * __expf(lt1);                 // Y_pi'
+    ZT[j * PC + t] = __expf(Lam[(CM - 1) * P + j] - Lam[t * P + j]) * Zl[t * P + j];
+    rec[RL.qp + t * DK + j] = __expf(Lam[t * P + j]) * Ql[t * P + j];
   }
+  GDR_STAGE_FOR(x, DK * CM, kR7Threads) {              // A~^T, rows j: consecutive threads store consecutive s
+    const int j = x / CM, s2 = x % CM;
+    rec[RL.at + j * CM + s2] = __expf(Lam[(CM - 1) * P + j] - Lam[s2 * P + j]) * Al[s2 * P + j];
+  }
+  GDR_STAGE_FOR(j, DK, kR7Threads) rec[RL.pic + j] = __expf(Lam[(CM - 1) * P + j]);
+  GDR_STAGE_FOR(x, CM * CM, kR7Threads) rec[RL.ma + x] = Ma[(x / CM) * PC + x % CM];
   __syncthreads();
-  // the four decay-scaled Gram matrices, one (t, s) pair per thread
-  for (int p = tid; p < CM * CM; p += kR7Threads) {
-    const int t = p / CM, s = p % CM;
-    float la = 0.f, lz = 0.f, ma = 0.f, mz = 0.f;
-    if (s <= t) {
-      for (int j = 0; j < DK; ++j) {
-        const float ls = Lam[s * LP + j];
-        const float e2 = __expf(Lam[t * LP + j] - ls);
-        const float as = Al[s * LP + j], zs = Zl[s * LP + j];
-        const float qt = Ql[t * LP + j];
-        ma += qt * e2 * as;
-        mz += qt * e2 * zs;
-        if (s < t) {
-          const float e1 = __expf(Lam[(t - 1) * LP + j] - ls);
-          const float yt = Yl[t * LP + j];
-          la += yt * e1 * as;
-          lz += yt * e1 * zs;
+  // L_z U into the right-hand side; O_z = M_z U and W_z = Z~^T U to the record
+  {
+    constexpr int NT = CM / 16;
+    const int NV = DV / 16;
+    for (int tile = wid; tile < 2 * NT * NV + (DK / 16) * NV; tile += 4) {
+      f32x4 acc = f4zero();
+      if (tile < 2 * NT * NV) {
+        const int which = tile / (NT * NV), r = tile % (NT * NV), it = r / NV, vt = r % NV;
+        tile_nt(acc, which == 0 ? Lz : Mz, PC, 16 * it, UT, PC, 16 * vt, CM, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * it + 4 * (lane >> 4) + e, v = 16 * vt + (lane & 15);
+          if (which == 0) Xl[t * NX + v] = acc[e];
+          else rec[RL.oz + t * DV + v] = acc[e];
+        }
+      } else {
+        const int r = tile - 2 * NT * NV, jt = r / NV, vt = r % NV;
+        tile_nt(acc, ZT, PC, 16 * jt, UT, PC, 16 * vt, CM, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * (lane >> 4) + e, v = 16 * vt + (lane & 15);
+          rec[RL.wz + j * DV + v] = acc[e];
         }
       }
     }
-    La[t * LQ + s] = la;
-    Lz[t * LQ + s] = lz;
-    Ma[t * LQ + s] = ma;
-    Mz[t * LQ + s] = mz;
-  }
-  __syncthreads();
-  // right-hand side [L_z U | Y_pi']
-  for (int x = tid; x < CM * DV; x += kR7Threads) {
-    const int t = x / DV, v = x % DV;
-    float acc = 0.f;
-    for (int s = 0; s < t; ++s) acc += Lz[t * LQ + s] * UT[v * LQ + s];
-    Xl[t * NX + v] = acc;
-  }
-  for (int x = tid; x < CM * DK; x += kR7Threads) {
-    const int t = x / DK, j = x % DK;
-    Xl[t * NX + DV + j] = Yl[t * LP + j] * (t > 0 ? __expf(Lam[(t - 1) * LP + j]) : 1.f);
   }
   __syncthreads();
   // (I + L_a) X = RHS by forward substitution, one column per thread
@@ -158,7 +244,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
     for (int t = 1; t < CM; ++t) {
       float acc = x[t];
 #pragma unroll
-      for (int s = 0; s < t; ++s) acc -= La[t * LQ + s] * x[s];
+      for (int s2 = 0; s2 < t; ++s2) acc -= La[t * PC + s2] * x[s2];
       x[t] = acc;
     }
 #pragma unroll
@@ -167,30 +253,6 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
       else rec[RL.g + t * DK + col - DV] = x[t];
     }
   }
-  // O_z = M_z U, W_z = Z~^T U, M_a, Q_pi, A~^T, pi_C
-  for (int x = tid; x < CM * DV; x += kR7Threads) {
-    const int t = x / DV, v = x % DV;
-    float acc = 0.f;
-    for (int s = 0; s <= t; ++s) acc += Mz[t * LQ + s] * UT[v * LQ + s];
-    rec[RL.oz + t * DV + v] = acc;
-  }
-  for (int x = tid; x < DK * DV; x += kR7Threads) {
-    const int j = x / DV, v = x % DV;
-    const float lc = Lam[(CM - 1) * LP + j];
-    float acc = 0.f;
-    for (int s = 0; s < CM; ++s) acc += __expf(lc - Lam[s * LP + j]) * Zl[s * LP + j] * UT[v * LQ + s];
-    rec[RL.wz + j * DV + v] = acc;
-  }
-  for (int x = tid; x < CM * CM; x += kR7Threads) rec[RL.ma + x] = Ma[(x / CM) * LQ + x % CM];
-  for (int x = tid; x < CM * DK; x += kR7Threads) {
-    const int t = x / DK, j = x % DK;
-    rec[RL.qp + t * DK + j] = __expf(Lam[t * LP + j]) * Ql[t * LP + j];
-  }
-  for (int x = tid; x < DK * CM; x += kR7Threads) {
-    const int j = x / CM, s = x % CM;
-    rec[RL.at + j * CM + s] = __expf(Lam[(CM - 1) * LP + j] - Lam[s * LP + j]) * Al[s * LP + j];
-  }
-  for (int j = tid; j < DK; j += kR7Threads) rec[RL.pic + j] = __expf(Lam[(CM - 1) * LP + j]);
 }
 
 // ------------------------------------------------------------------ chunk scan
@@ -428,7 +490,9 @@ static int r7_launch(const Rwkv7Args& a, void* ws) {
   const hipStream_t st = (hipStream_t)a.stream;
   float* wsf = (float*)ws;
   {
-    const int lds = 4 * (5 * CM * (DK + 1) + 4 * CM * (CM + 1) + DV * (CM + 1) + CM * (DV + DK + 1));
+    const int P = DK + 4, PC = CM + 4, NX = DV + DK + 4;
+    const int tg = (2 * 16 + 2 * CM) * P, tr = DV * PC + CM * NX + DK * PC;
+    const int lds = 4 * (4 * CM * P + CM + 4 * CM * PC + (tg > tr ? tg : tr));
     auto kern = rwkv7_intra_kernel<E, DK, CM>;
     if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
     const E *q = (const E*)a.q, *w = (const E*)a.w, *aa = (const E*)a.a, *kw = (const E*)a.kw, *u = (const E*)a.u;

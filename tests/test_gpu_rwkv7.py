@@ -112,3 +112,22 @@ def test_rwkv7_eviction_demo_on_gpu():
         res.append(np.linalg.norm(kA @ host(S)[0, 0]))
     say(f"[rwkv7] eviction demo: aimed {res[0]:.6f} locked {res[1]:.6f}")
     assert abs(res[0] - 0.028576) < 1e-6 and abs(res[1] - 0.674096) < 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rwkv7_strong_decay_block_takes_exact_factors(dtype):
+    """Channels whose decay falls below 2^-60 within one 16-token block: the
+    kernel's Gram matrices use exact pairwise decays for that block instead of
+    the block-pivot factors (which would exceed fp32 range there)."""
+    import torch
+    d = rwkv7_inputs(1, 2, 80, 64, 32, seed=11, dtype=dtype, s0_std=0.1)
+    w = d["w"].copy()
+    w[:, :, 16:32, :8] = 0.01            # 0.01^16 = 1e-32 in one block of chunk 0
+    w[:, 1, 40:56, 20:30] = 0.02         # and inside chunk 1 for head 1
+    from synth import round_to
+    d["w"] = round_to(w, dtype)
+    for chunk in (16, 32):
+        o, S = _run(d, chunk)
+        torch.cuda.synchronize()
+        o_ref, S_ref = _ref(d)
+        check_outputs(host(o), o_ref, host(S), S_ref, dtype, f"[rwkv7] {dtype} strong decay C={chunk}")
