@@ -396,29 +396,48 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
 #pragma unroll
   for (int i = 0; i < PM; ++i) aM[i] = f4zero();
   float pacc = 0.f;
-  for (int v0 = 0; v0 < DV; v0 += kVT) {
-    GDR_STAGE_FOR(x, DK * kVT, kBwdThreads) {
-      const int j = x / kVT, v = x % kVT;
-      const float s0 = Hc[(size_t)j * DV + v0 + v], ds = dHc[(size_t)j * DV + v0 + v];
-      S0l[j * L16 + v] = s0;
-      S0Tl[v * LY + j] = s0;
-      dSl[j * L16 + v] = ds;
-      dSTl[v * LY + j] = ds;
-    }
-    GDR_STAGE_FOR(x, CM * kVT, kBwdThreads) {
-      const int t = x / kVT, v = x % kVT;
-      const float g0 = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
-      const float g = t0 + t < T ? g0 : 0.f;
-      dOl[t * L16 + v] = g;
-      dOTl[v * LC + t] = g;
-    }
-    GDR_STAGE_FOR(x, kVT * CM / 4, kBwdThreads) {
-      const int v = x / (CM / 4), tq = 4 * (x % (CM / 4));
-      float o[4];
-      R.ut4(v0 + v, tq, o);
+  // the state, state-gradient, dO and U slices of value tile v0 + kVT load
+  // into registers while tile v0 is worked on
+  constexpr int NH = DK * kVT / kBwdThreads, NG = CM * kVT / kBwdThreads, NU = kVT * CM / 4;
+  static_assert(DK * kVT % kBwdThreads == 0 && CM * kVT % kBwdThreads == 0 && NU <= kBwdThreads, "bwd chunk tiles");
+  float rh[NH], rd[NH], rg[NG], ru[4];
+  auto fetch = [&](int v0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Ul[(tq + e) * kVT + v] = o[e];
+    for (int i = 0; i < NH; ++i) {
+      const int x = tid + i * kBwdThreads, j = x / kVT, v = x % kVT;
+      rh[i] = Hc[(size_t)j * DV + v0 + v];
+      rd[i] = dHc[(size_t)j * DV + v0 + v];
     }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int x = tid + i * kBwdThreads, t = x / kVT, v = x % kVT;
+      const float g0 = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
+      rg[i] = t0 + t < T ? g0 : 0.f;
+    }
+    if (tid < NU) R.ut4(v0 + tid / (CM / 4), 4 * (tid % (CM / 4)), ru);
+  };
+  fetch(0);
+  for (int v0 = 0; v0 < DV; v0 += kVT) {
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int x = tid + i * kBwdThreads, j = x / kVT, v = x % kVT;
+      S0l[j * L16 + v] = rh[i];
+      S0Tl[v * LY + j] = rh[i];
+      dSl[j * L16 + v] = rd[i];
+      dSTl[v * LY + j] = rd[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int x = tid + i * kBwdThreads, t = x / kVT, v = x % kVT;
+      dOl[t * L16 + v] = rg[i];
+      dOTl[v * LC + t] = rg[i];
+    }
+    if (tid < NU) {
+      const int v = tid / (CM / 4), tq = 4 * (tid % (CM / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ul[(tq + e) * kVT + v] = ru[e];
+    }
+    if (v0 + kVT < DV) fetch(v0 + kVT);
     __syncthreads();
     for (int it = wid; it < CM / 16; it += 4) {
       f32x4 acc = f4zero();
@@ -510,6 +529,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch, t0 = c * CM;
   const size_t item = (size_t)bh * nch + c;
   const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
+  __shared__ int sflag[4];
+  if (tid < 4) sflag[tid] = 0;
   GDR_STAGE_FOR(x, CM * DK, kBwdThreads) {
     const int t = x / DK, j = x % DK;
     const bool ok = t0 + t < T;
@@ -521,23 +542,58 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
     KHl[t * LP + j] = bb * kk;
   }
   __syncthreads();
-  for (int j = tid; j < DK; j += kBwdThreads) {   // Lambda_t = sum_{r <= t} log alpha_r
+  GDR_STAGE_FOR(j, DK, kBwdThreads) {   // Lambda_t = sum_{r <= t} log alpha_r
     float acc = 0.f;
+#pragma unroll
     for (int t = 0; t < CM; ++t) {
       acc += Lam[t * LP + j];
       Lam[t * LP + j] = acc;
     }
+    // blocks in which channel j decays below 2^-60 (log 2^-60 = -41.59)
+#pragma unroll
+    for (int I = 0; I < CM / 16; ++I) {
+      const float lp = I > 0 ? Lam[(16 * I - 1) * LP + j] : 0.f;
+      if (Lam[(16 * I + 15) * LP + j] - lp < -41.5f) sflag[I] = 1;
+    }
   }
   __syncthreads();
-  // L[t][s] = sum_j k^_t[j] k_s[j] exp(Lambda_t[j] - Lambda_s[j]), t > s
-  for (int p = tid; p < CM * CM; p += kBwdThreads) {
-    const int t = p / CM, s = p % CM;
-    float acc = 0.f;
-    if (s < t) {
-      for (int j = 0; j < DK; ++j)
-        acc += KHl[t * LP + j] * Kl[s * LP + j] * __expf(Lam[t * LP + j] - Lam[s * LP + j]);
+  // L[t][s] = sum_j k^_t[j] k_s[j] exp(Lambda_t[j] - Lambda_s[j]), t > s, as
+  // fp32 MFMA tiles over j, split at the 16-row blocks as the forward splits
+  // its Gram: for row block I with pivot p = 16 I - 1 (Lambda_{-1} = 0) the
+  // operands k^_t e^{Lambda_t - Lambda_p} (<= 1) and k_s e^{Lambda_p - Lambda_s}
+  // (<= 1 below the block, at most 1 / (the block's decay) inside it), formed
+  // lane by lane; a diagonal tile whose block decays below 2^-60 in some
+  // channel takes the exact pairwise factors instead.
+  {
+    constexpr int NB = CM / 16;
+    const int m16 = lane & 15, k4 = lane >> 4;
+    for (int tile = wid; tile < NB * (NB + 1) / 2; tile += 4) {
+      int I = 0;
+      while ((I + 1) * (I + 2) / 2 <= tile) ++I;
+      const int J = tile - I * (I + 1) / 2, p = 16 * I - 1;
+      const int ta = 16 * I + m16, sb = 16 * J + m16;
+      f32x4 acc = f4zero();
+      for (int j0 = 0; j0 < DK; j0 += 4) {
+        const int j = j0 + k4;
+        const float lp = I > 0 ? Lam[p * LP + j] : 0.f;
+        const float av = KHl[ta * LP + j] * __expf(Lam[ta * LP + j] - lp);
+        const float bv = Kl[sb * LP + j] * __expf(lp - Lam[sb * LP + j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+      }
+      const bool exact = J == I && sflag[I] != 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * k4 + e, s2 = 16 * J + m16;
+        float val = acc[e];
+        if (exact) {
+          val = 0.f;
+          if (s2 < t)
+            for (int j = 0; j < DK; ++j)
+              val += KHl[t * LP + j] * Kl[s2 * LP + j] * __expf(Lam[t * LP + j] - Lam[s2 * LP + j]);
+        }
+        Ll[t * LL + s2] = s2 < t ? val : 0.f;
+      }
     }
-    Ll[t * LL + s] = acc;
   }
   __syncthreads();
   // T^T X = dZ column by column: x_t = dz_t - sum_{s > t} L[s][t] x_s (rows from the last)

@@ -72,6 +72,21 @@ def test_bwd_ill_conditioned_f32():
     _check(d, 32, "f32 correlated keys")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_strong_decay_blocks(dtype):
+    """Channels whose decay falls below 2^-60 inside one 16-token block (the
+    forward's and the backward's Gram factors take exact pairwise decays
+    there), and strong decays straddling two blocks (large but finite factor
+    ratios)."""
+    from synth import round_to
+    d = gdn2_inputs(1, 2, 150, 64, 64, alpha_mu=4.0, alpha_sigma=1.5, seed=12, dtype=dtype, s0_std=0.1)
+    a = d["alpha"].copy()
+    a[:, :, 16:32, :8] = 0.01
+    a[:, 1, 72:88, 20:30] = 0.02
+    d["alpha"] = round_to(a, dtype)
+    _check(d, 32, f"{dtype} strong decay blocks")
+
+
 def test_bwd_records_ready_equals_recompute():
     """A workspace whose records the two-kernel forward wrote (records_ready)
     gives the same gradients bit for bit as recomputing them."""
