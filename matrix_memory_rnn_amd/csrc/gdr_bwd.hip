@@ -45,6 +45,7 @@ namespace gdr {
 namespace {
 
 constexpr int kBwdThreads = 256;
+constexpr float kBwdExactLog = -13.86f;   // log 2^-20: in-block decays below it take exact factors
 constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel
 
 __device__ __forceinline__ int acc_row(int lane, int e) { return 4 * (lane >> 4) + e; }
@@ -549,11 +550,11 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
       acc += Lam[t * LP + j];
       Lam[t * LP + j] = acc;
     }
-    // blocks in which channel j decays below 2^-60 (log 2^-60 = -41.59)
+    // blocks in which channel j decays below 2^-20 (log 2^-20 = -13.86)
 #pragma unroll
     for (int I = 0; I < CM / 16; ++I) {
       const float lp = I > 0 ? Lam[(16 * I - 1) * LP + j] : 0.f;
-      if (Lam[(16 * I + 15) * LP + j] - lp < -41.5f) sflag[I] = 1;
+      if (Lam[(16 * I + 15) * LP + j] - lp < kBwdExactLog) sflag[I] = 1;
     }
   }
   __syncthreads();
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
   // its Gram: for row block I with pivot p = 16 I - 1 (Lambda_{-1} = 0) the
   // operands k^_t e^{Lambda_t - Lambda_p} (<= 1) and k_s e^{Lambda_p - Lambda_s}
   // (<= 1 below the block, at most 1 / (the block's decay) inside it), formed
-  // lane by lane; a diagonal tile whose block decays below 2^-60 in some
+  // lane by lane; a diagonal tile whose block decays below 2^-20 in some
   // channel takes the exact pairwise factors instead.
   {
     constexpr int NB = CM / 16;
@@ -751,6 +752,8 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
   for (int i = 0; i < Sh::RPS; ++i)
     pal[i] = (float)alpha[sK + (size_t)row_in(t0 + r0 + i, T) * DK + j0 + cj];
   if (tid < NCH) pdp = dpic[item * DK + j0 + tid];
+  __shared__ int dflag[4];
+  if (tid < 4) dflag[tid] = 0;
   GDR_STAGE_FOR(x, CM * NCH, kDecayThreads) {
     const int t = x / NCH, jl = x % NCH;
     const bool ok = t0 + t < T;
@@ -794,6 +797,18 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
     }
   }
   __syncthreads();
+  // blocks in which some channel decays below 2^-20 (log 2^-20 = -13.86):
+  // their diagonal tiles take exact pairwise factors (a tighter bound than the
+  // forward's 2^-60 keeps the in-block factor ratios, and with them the fp32
+  // rounding of the gradients, small)
+  if (tid < NCH) {
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      const float lp = I > 0 ? Lam[(16 * I - 1) * LP + tid] : 0.f;
+      if (Lam[(16 * I + 15) * LP + tid] - lp < kBwdExactLog) dflag[I] = 1;
+    }
+  }
+  __syncthreads();
   float gK[NJT], dlam[NJT][4];
 #pragma unroll
   for (int n = 0; n < NJT; ++n) gK[n] = 0.f;
@@ -805,7 +820,10 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
       const int jl = 16 * n + m16;
       f32x4 a1 = f4zero(), a2 = f4zero();
       const float lp = wid > 0 ? Lam[(B0 - 1) * LP + jl] : 0.f;
-      for (int s0 = 0; s0 < B0; s0 += 4) {
+      // the diagonal block joins the product (factors e^{Lambda_p - Lambda_s}
+      // up to 1 / the block's decay) unless the block is flagged
+      const bool exact = dflag[wid] != 0;
+      for (int s0 = 0; s0 < (exact ? B0 : B0 + 16); s0 += 4) {
         const int s = s0 + k4;
         const float bv = __expf(lp - Lam[s * LP + jl]) * Kc[s * LP + jl];
         a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(dLs[(B0 + m16) * LD + s], bv, a1, 0, 0, 0);
@@ -815,12 +833,12 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         lt[e] = Lam[(B0 + 4 * k4 + e) * LP + jl];
-        const float sc = wid > 0 ? __expf(lt[e] - lp) : 0.f;
+        const float sc = __expf(lt[e] - lp);
         a1[e] *= sc;
         a2[e] *= sc;
       }
 #pragma unroll 4
-      for (int s = B0; s < B0 + 16; ++s) {          // the diagonal block, exact
+      for (int s = B0; s < (exact ? B0 + 16 : B0); ++s) {   // a flagged diagonal block, exact
         const float ls = Lam[s * LP + jl], ks = Kc[s * LP + jl];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -848,8 +866,9 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
     for (int n = 0; n < NJT; ++n) {
       const int jl = 16 * n + m16;
       const float lq = Lam[(B0 + 15) * LP + jl];
+      const bool exact = dflag[wid] != 0;
       f32x4 acc = f4zero();
-      for (int tb = B0 + 16; tb < CM; tb += 4) {
+      for (int tb = exact ? B0 + 16 : B0; tb < CM; tb += 4) {
         const int t = tb + k4;
         const float sc = __expf(Lam[t * LP + jl] - lq);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dLs[t * LD + B0 + m16], sc * KHc[t * LP + jl], acc, 0, 0, 0);
@@ -862,7 +881,7 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
         acc[e] *= __expf(lq - ls[e]);
       }
 #pragma unroll 4
-      for (int t = B0; t < B0 + 16; ++t) {          // the diagonal block, exact
+      for (int t = B0; t < (exact ? B0 + 16 : B0); ++t) {   // a flagged diagonal block, exact
         const float lt = Lam[t * LP + jl], kh = KHc[t * LP + jl], qq = Qc[t * LP + jl];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -76,13 +76,15 @@ def test_bwd_ill_conditioned_f32():
 def test_bwd_strong_decay_blocks(dtype):
     """Channels whose decay falls below 2^-60 inside one 16-token block (the
     forward's and the backward's Gram factors take exact pairwise decays
-    there), and strong decays straddling two blocks (large but finite factor
-    ratios)."""
+    there), below 2^-20 across two blocks (the backward's exact factors), and
+    to e^-12.8 inside one block (the backward's block factors, with in-block
+    ratios up to e^12.8)."""
     from synth import round_to
     d = gdn2_inputs(1, 2, 150, 64, 64, alpha_mu=4.0, alpha_sigma=1.5, seed=12, dtype=dtype, s0_std=0.1)
     a = d["alpha"].copy()
     a[:, :, 16:32, :8] = 0.01
     a[:, 1, 72:88, 20:30] = 0.02
+    a[:, 0, 96:112, 30:40] = 0.45
     d["alpha"] = round_to(a, dtype)
     _check(d, 32, f"{dtype} strong decay blocks")
 
