@@ -222,36 +222,41 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_states_kernel(const char
 }
 
 // ------------------------------------------------------------------ chunk-end state gradients
-template <typename E, int DK, int CM, bool FM>
+// Per (b, h, VT-column value tile) (VT = 32, or 16 for d_v = 16), walking the
+// chunks from the last: every chunk-end state gradient is stored, the last
+// one (the chunk-start gradient of chunk 0) is dS0.
+template <typename E, int DK, int CM, bool FM, int VT>
 __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const char* __restrict__ ws,
                                                                         const E* __restrict__ dO,
                                                                         const float* __restrict__ dST,
                                                                         float* __restrict__ dHs,
                                                                         float* __restrict__ dS0, int T, int DV) {
-  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4;
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NHV = VT / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* MTl = (float*)smem;         // M^T    [s][t]
   float* Kl = MTl + CM * LC;         // K~     [s][j]
   float* QTl = Kl + CM * LY;         // Q_pi^T [j][t]
   float* YTl = QTl + DK * LC;        // Y^T    [j][t]
   float* DOTl = YTl + DK * LC;       // dO^T   [v][t]
-  float* DSTl = DOTl + kVT * LC;     // dS^T   [v][j]
-  float* DVTl = DSTl + kVT * LY;     // dV~^T  [v][s]
-  float* PIl = DVTl + kVT * LC;      // pi_C   [j]
+  float* DSTl = DOTl + VT * LC;      // dS^T   [v][j]
+  float* DVTl = DSTl + VT * LY;      // dV~^T  [v][s]
+  float* PIl = DVTl + VT * LC;       // pi_C   [j]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nvt = DV / kVT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kVT;
+  const int nvt = DV / VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * VT;
   const int nch = (T + CM - 1) / CM;
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
   const int vl = lane & 15;
-  f32x4 D[PER];
+  f32x4 D[PER][NHV];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int J = wid + 4 * i;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * J + acc_row(lane, e);
-      D[i][e] = (J < NST && dST) ? dST[((size_t)bh * DK + row) * DV + v0 + vl] : 0.f;
-    }
+    for (int hv = 0; hv < NHV; ++hv)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * J + acc_row(lane, e);
+        D[i][hv][e] = (J < NST && dST) ? dST[((size_t)bh * DK + row) * DV + v0 + 16 * hv + vl] : 0.f;
+      }
   }
   for (int c = nch - 1; c >= 0; --c) {
     const Rec<E, FM> R{ws + ((size_t)bh * nch + c) * RL.bytes, RL, DK, CM};
@@ -261,11 +266,13 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       const int J = wid + 4 * i;
       if (J < NST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * J + acc_row(lane, e);
-          dHc[(size_t)row * DV + v0 + vl] = D[i][e];
-          DSTl[vl * LY + row] = D[i][e];
-        }
+        for (int hv = 0; hv < NHV; ++hv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * J + acc_row(lane, e);
+            dHc[(size_t)row * DV + v0 + 16 * hv + vl] = D[i][hv][e];
+            DSTl[(16 * hv + vl) * LY + row] = D[i][hv][e];
+          }
       }
     }
     const int t0 = c * CM;
@@ -294,20 +301,21 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
         YTl[(j0 + e) * LC + t] = p8[e];
       }
     }
-    GDR_STAGE_FOR(x, CM * kVT, kBwdThreads) {
-      const int t = x / kVT, v = x % kVT;
+    GDR_STAGE_FOR(x, CM * VT, kBwdThreads) {
+      const int t = x / VT, v = x % VT;
       const float g = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
       DOTl[v * LC + t] = t0 + t < T ? g : 0.f;
     }
     GDR_STAGE_FOR(j, DK, kBwdThreads) PIl[j] = R.pic(j);
     __syncthreads();
     // dV~ = M^T dO + K~ dS
-    for (int it = wid; it < CM / 16; it += 4) {
+    for (int p = wid; p < (CM / 16) * NHV; p += 4) {
+      const int it = p / NHV, hv = p % NHV;
       f32x4 acc = f4zero();
-      tile_nt(acc, MTl, LC, 16 * it, DOTl, LC, 0, CM, lane);
-      tile_nt(acc, Kl, LY, 16 * it, DSTl, LY, 0, DK, lane);
+      tile_nt(acc, MTl, LC, 16 * it, DOTl, LC, 16 * hv, CM, lane);
+      tile_nt(acc, Kl, LY, 16 * it, DSTl, LY, 16 * hv, DK, lane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) DVTl[vl * LC + 16 * it + acc_row(lane, e)] = acc[e];
+      for (int e = 0; e < 4; ++e) DVTl[(16 * hv + vl) * LC + 16 * it + acc_row(lane, e)] = acc[e];
     }
     __syncthreads();
     // dS <- Diag(pi_C) dS + Q_pi^T dO - Y^T dV~
@@ -316,12 +324,15 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       const int J = wid + 4 * i;
       if (J < NST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) D[i][e] *= PIl[16 * J + acc_row(lane, e)];
-        tile_nt(D[i], QTl, LC, 16 * J, DOTl, LC, 0, CM, lane);
-        f32x4 yv = f4zero();
-        tile_nt(yv, YTl, LC, 16 * J, DVTl, LC, 0, CM, lane);
+        for (int hv = 0; hv < NHV; ++hv) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) D[i][e] -= yv[e];
+          for (int e = 0; e < 4; ++e) D[i][hv][e] *= PIl[16 * J + acc_row(lane, e)];
+          tile_nt(D[i][hv], QTl, LC, 16 * J, DOTl, LC, 16 * hv, CM, lane);
+          f32x4 yv = f4zero();
+          tile_nt(yv, YTl, LC, 16 * J, DVTl, LC, 16 * hv, CM, lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) D[i][hv][e] -= yv[e];
+        }
       }
     }
     __syncthreads();
@@ -332,7 +343,10 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       const int J = wid + 4 * i;
       if (J < NST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dS0[((size_t)bh * DK + 16 * J + acc_row(lane, e)) * DV + v0 + vl] = D[i][e];
+        for (int hv = 0; hv < NHV; ++hv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dS0[((size_t)bh * DK + 16 * J + acc_row(lane, e)) * DV + v0 + 16 * hv + vl] = D[i][hv][e];
       }
     }
   }
@@ -987,14 +1001,19 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
       return GDR_ERR_LAUNCH;
   }
   {
-    const int lds = 4 * (CM * LC + CM * LY + 2 * DK * LC + kVT * LC + kVT * LY + kVT * LC + DK);
-    auto kern = gdn2_bwd_dstates_kernel<E, DK, CM, FM>;
-    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    // 32-column value tiles (one round of workgroups over the CUs where 16
+    // would take two), 16 for d_v = 16
+    const bool wide = DV % 32 == 0;
+    const int vt = wide ? 32 : 16;
+    const int lds = 4 * (CM * LC + CM * LY + 2 * DK * LC + vt * LC + vt * LY + vt * LC + DK);
+    const void* kern = wide ? (const void*)gdn2_bwd_dstates_kernel<E, DK, CM, FM, 32>
+                            : (const void*)gdn2_bwd_dstates_kernel<E, DK, CM, FM, 16>;
+    if (!allow_lds(kern, lds)) return GDR_ERR_LAUNCH;
     const E* dO = (const E*)a.dO;
     const float* dST = a.dS_T;
     float* dS0 = a.dS0;
     void* args[] = {&wsc, &dO, &dST, &dHs, &dS0, &T, &DV};
-    if (hipLaunchKernel((const void*)kern, dim3(BH * (DV / kVT)), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+    if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kBwdThreads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   {
