@@ -1504,9 +1504,12 @@ __device__ __forceinline__ void phase_barrier() {
 // tile), and segment g starts from the state Sseg[g][b*H + h] that the
 // segment pass left there (g = 0: S0); only the last segment writes S_out.
 // With seg >= the chunk count there is one segment, starting from S0.
-// Hst (may be NULL): every chunk-start state, fp32 [b*H + h][chunk][d_k][d_v]
-// (the backward's saved states); o may be NULL then (no outputs stored).
-template <int DK, int CM, int PF, int NS>
+// OUT_H: every chunk-start state goes to Hst, fp32 [b*H + h][chunk][d_k][d_v]
+// (the backward's saved states); without OUT_O no outputs are stored. Both
+// are compile-time choices: a run-time branch around the stores would leave
+// the compiler unable to count the loads in flight, and it would then wait
+// for all of them.
+template <int DK, int CM, int PF, int NS, bool OUT_O = true, bool OUT_H = false>
 __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
     const char* __restrict__ ws, const float* __restrict__ S0, __bf16* __restrict__ o, float* S_out,
     int T, int DV, int seg, const float* __restrict__ Sseg, float* __restrict__ Hst) {
@@ -1681,7 +1684,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
         typedef __attribute__((ext_vector_type(2))) uint32_t u2;
         const int t0 = (c0 + ch) * CM;
-        if (o != nullptr) {
+        if constexpr (OUT_O) {
           const __amdgpu_buffer_rsrc_t orsrc =
               __builtin_amdgcn_make_buffer_rsrc(o + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
 #pragma unroll
@@ -1768,7 +1771,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
           sink ^= PFV[u % PF];
           PFV[u % PF] = touch(ch + PF);
         }
-        if (Hst != nullptr) {                           // the chunk-start state, fp32
+        if constexpr (OUT_H) {                          // the chunk-start state, fp32
           float* hc = Hst + (((size_t)bh * ntot + c0 + ch) * DK + 32 * J2 + 4 * h) * DV + vt0 + r;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -2167,7 +2170,7 @@ static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
 // one segment per head.
 template <int DK, int CM>
 static int launch_states_fm(const ChunkArgs& a, const char* ws, float* Hst) {
-  const void* kern = (const void*)gdn2_chunk_scan_fm_kernel<DK, CM, kScanFmPrefetch, kScanFmSets>;
+  const void* kern = (const void*)gdn2_chunk_scan_fm_kernel<DK, CM, kScanFmPrefetch, kScanFmSets, false, true>;
   const float* S0 = a.S0;
   __bf16* o = nullptr;
   float* So = nullptr;
