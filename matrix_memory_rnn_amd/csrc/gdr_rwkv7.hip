@@ -30,7 +30,6 @@ namespace gdr {
 namespace {
 
 constexpr int kR7Threads = 256;
-constexpr int kR7VT = 16;    // value tile of the scan
 
 // Record of one (b, h, chunk), fp32 element offsets.
 struct R7Layout {
@@ -256,101 +255,173 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
 }
 
 // ------------------------------------------------------------------ chunk scan
-template <typename E, int DK, int CM>
+// Per (b, h, VT value columns) (VT = 32, or 16 for d_v = 16), walking the
+// chunks: E = E0 + G S0, O = Q_pi S0 - M_a E + O_z, S = Diag(pi_C) S0 - A~^T E
+// + W_z on the fp32 matrix cores. The next chunk's record slices load into
+// registers while the current chunk is worked on.
+template <typename E, int DK, int CM, int VT>
 __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __restrict__ ws,
                                                                  const float* __restrict__ S0, E* __restrict__ o,
                                                                  float* __restrict__ S_out, int T, int DV) {
-  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NT = CM / 16;
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NT = CM / 16, NHV = VT / 16;
+  constexpr int NTH = kR7Threads;
+  // f32x4 pieces of each slice and the loads per thread
+  constexpr int QA = CM * DK / 4, QM = CM * CM / 4, QT = DK * CM / 4, QE = CM * VT / 4, QW = DK * VT / 4;
+  constexpr int NA = (QA + NTH - 1) / NTH, NM = (QM + NTH - 1) / NTH, NAT = (QT + NTH - 1) / NTH,
+                NE = (QE + NTH - 1) / NTH, NW = (QW + NTH - 1) / NTH;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* Gl = (float*)smem;             // G     [t][j]
   float* Qpl = Gl + CM * LY;            // Q_pi  [t][j]
   float* Mal = Qpl + CM * LY;           // M_a   [t][s]
   float* ATl = Mal + CM * LC;           // A~^T  [j][s]
   float* STl = ATl + DK * LC;           // S^T   [v][j]
-  float* ETl = STl + kR7VT * LY;        // E^T   [v][s]
-  float* E0l = ETl + kR7VT * LC;        // E0    [t][v]
-  float* OZl = E0l + CM * kR7VT;        // O_z   [t][v]
-  float* WZl = OZl + CM * kR7VT;        // W_z   [j][v]
-  float* PIl = WZl + DK * kR7VT;        // pi_C  [j]
+  float* ETl = STl + VT * LY;           // E^T   [v][s]
+  float* E0l = ETl + VT * LC;           // E0    [t][v]
+  float* OZl = E0l + CM * VT;           // O_z   [t][v]
+  float* WZl = OZl + CM * VT;           // W_z   [j][v]
+  float* PIl = WZl + DK * VT;           // pi_C  [j]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, vl = lane & 15;
-  const int nvt = DV / kR7VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kR7VT;
+  const int nvt = DV / VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * VT;
   const int nch = (T + CM - 1) / CM;
   const R7Layout RL = r7_layout(DK, DV, CM);
-  f32x4 S[PER];
+  f32x4 S[PER][NHV];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int J = wid + 4 * i;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * J + 4 * (lane >> 4) + e;
-      S[i][e] = (J < NST && S0) ? S0[((size_t)bh * DK + row) * DV + v0 + vl] : 0.f;
-    }
+    for (int hv = 0; hv < NHV; ++hv)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * J + 4 * (lane >> 4) + e;
+        S[i][hv][e] = (J < NST && S0) ? S0[((size_t)bh * DK + row) * DV + v0 + 16 * hv + vl] : 0.f;
+      }
   }
-  for (int c = 0; c < nch; ++c) {
+  f32x4 pg[NA], pq[NA], pm[NM], pa[NAT], pe[NE], po[NE], pw[NW];
+  float pp = 0.f;
+  auto fetch = [&](int c) {
     const float* rec = ws + ((size_t)bh * nch + c) * RL.floats;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int x = tid + NTH * i;
+      if (QA % NTH == 0 || x < QA) {
+        const int t = x / (DK / 4), j0 = 4 * (x % (DK / 4));
+        pg[i] = *(const f32x4*)&rec[RL.g + t * DK + j0];
+        pq[i] = *(const f32x4*)&rec[RL.qp + t * DK + j0];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int x = tid + NTH * i;
+      if (QM % NTH == 0 || x < QM) pm[i] = *(const f32x4*)&rec[RL.ma + 4 * x];
+    }
+#pragma unroll
+    for (int i = 0; i < NAT; ++i) {
+      const int x = tid + NTH * i;
+      if (QT % NTH == 0 || x < QT) pa[i] = *(const f32x4*)&rec[RL.at + 4 * x];
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int x = tid + NTH * i;
+      if (QE % NTH == 0 || x < QE) {
+        const int t = x / (VT / 4), q0 = 4 * (x % (VT / 4));
+        pe[i] = *(const f32x4*)&rec[RL.e0 + t * DV + v0 + q0];
+        po[i] = *(const f32x4*)&rec[RL.oz + t * DV + v0 + q0];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int x = tid + NTH * i;
+      if (QW % NTH == 0 || x < QW) {
+        const int jr = x / (VT / 4), q0 = 4 * (x % (VT / 4));
+        pw[i] = *(const f32x4*)&rec[RL.wz + jr * DV + v0 + q0];
+      }
+    }
+    if (tid < DK) pp = rec[RL.pic + tid];
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int x = tid + NTH * i;
+      if (QA % NTH == 0 || x < QA) {
+        const int t = x / (DK / 4), j0 = 4 * (x % (DK / 4));
+        *(f32x4*)&Gl[t * LY + j0] = pg[i];
+        *(f32x4*)&Qpl[t * LY + j0] = pq[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int x = tid + NTH * i;
+      if (QM % NTH == 0 || x < QM) *(f32x4*)&Mal[(x / (CM / 4)) * LC + 4 * (x % (CM / 4))] = pm[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NAT; ++i) {
+      const int x = tid + NTH * i;
+      if (QT % NTH == 0 || x < QT) *(f32x4*)&ATl[(x / (CM / 4)) * LC + 4 * (x % (CM / 4))] = pa[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int x = tid + NTH * i;
+      if (QE % NTH == 0 || x < QE) {
+        *(f32x4*)&E0l[4 * x] = pe[i];
+        *(f32x4*)&OZl[4 * x] = po[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int x = tid + NTH * i;
+      if (QW % NTH == 0 || x < QW) *(f32x4*)&WZl[4 * x] = pw[i];
+    }
+    if (tid < DK) PIl[tid] = pp;
+  };
+  fetch(0);
+  for (int c = 0; c < nch; ++c) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int J = wid + 4 * i;
       if (J < NST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) STl[vl * LY + 16 * J + 4 * (lane >> 4) + e] = S[i][e];
+        for (int hv = 0; hv < NHV; ++hv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) STl[(16 * hv + vl) * LY + 16 * J + 4 * (lane >> 4) + e] = S[i][hv][e];
       }
     }
-    GDR_STAGE_FOR(x, CM * DK / 4, kR7Threads) {
-      const int t = x / (DK / 4), j0 = 4 * (x % (DK / 4));
-      *(f32x4*)&Gl[t * LY + j0] = *(const f32x4*)&rec[RL.g + t * DK + j0];
-      *(f32x4*)&Qpl[t * LY + j0] = *(const f32x4*)&rec[RL.qp + t * DK + j0];
-    }
-    GDR_STAGE_FOR(x, CM * CM / 4, kR7Threads) {
-      const int t = x / (CM / 4), s0 = 4 * (x % (CM / 4));
-      *(f32x4*)&Mal[t * LC + s0] = *(const f32x4*)&rec[RL.ma + t * CM + s0];
-    }
-    GDR_STAGE_FOR(x, DK * CM / 4, kR7Threads) {
-      const int j = x / (CM / 4), s0 = 4 * (x % (CM / 4));
-      *(f32x4*)&ATl[j * LC + s0] = *(const f32x4*)&rec[RL.at + j * CM + s0];
-    }
-    GDR_STAGE_FOR(x, CM * kR7VT / 4, kR7Threads) {
-      const int t = x / (kR7VT / 4), q0 = 4 * (x % (kR7VT / 4));
-      *(f32x4*)&E0l[t * kR7VT + q0] = *(const f32x4*)&rec[RL.e0 + t * DV + v0 + q0];
-      *(f32x4*)&OZl[t * kR7VT + q0] = *(const f32x4*)&rec[RL.oz + t * DV + v0 + q0];
-    }
-    GDR_STAGE_FOR(x, DK * kR7VT / 4, kR7Threads) {
-      const int j = x / (kR7VT / 4), q0 = 4 * (x % (kR7VT / 4));
-      *(f32x4*)&WZl[j * kR7VT + q0] = *(const f32x4*)&rec[RL.wz + j * DV + v0 + q0];
-    }
-    GDR_STAGE_FOR(j, DK, kR7Threads) PIl[j] = rec[RL.pic + j];
+    stage();
+    if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
     // E = E0 + G S0 (to LDS, transposed); the readout's Q_pi S0 kept in registers
-    f32x4 oacc[(NT + 3) / 4];
+    constexpr int NP = NT * NHV, PP = (NP + 3) / 4;
+    f32x4 oacc[PP];
 #pragma unroll
-    for (int i = 0; i < (NT + 3) / 4; ++i) {
-      const int it = wid + 4 * i;
+    for (int i = 0; i < PP; ++i) {
+      const int p = wid + 4 * i;
       oacc[i] = f4zero();
-      if (it < NT) {
+      if (p < NP) {
+        const int it = p / NHV, hv = p % NHV;
         f32x4 acc = f4zero();
-        tile_nt(acc, Gl, LY, 16 * it, STl, LY, 0, DK, lane);
-        tile_nt(oacc[i], Qpl, LY, 16 * it, STl, LY, 0, DK, lane);
+        tile_nt(acc, Gl, LY, 16 * it, STl, LY, 16 * hv, DK, lane);
+        tile_nt(oacc[i], Qpl, LY, 16 * it, STl, LY, 16 * hv, DK, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * it + 4 * (lane >> 4) + e;
-          ETl[vl * LC + t] = E0l[t * kR7VT + vl] + acc[e];
+          ETl[(16 * hv + vl) * LC + t] = E0l[t * VT + 16 * hv + vl] + acc[e];
         }
       }
     }
     __syncthreads();
     // O = Q_pi S0 - M_a E + O_z
 #pragma unroll
-    for (int i = 0; i < (NT + 3) / 4; ++i) {
-      const int it = wid + 4 * i;
-      if (it < NT) {
+    for (int i = 0; i < PP; ++i) {
+      const int p = wid + 4 * i;
+      if (p < NP) {
+        const int it = p / NHV, hv = p % NHV;
         f32x4 me = f4zero();
-        tile_nt(me, Mal, LC, 16 * it, ETl, LC, 0, CM, lane);
+        tile_nt(me, Mal, LC, 16 * it, ETl, LC, 16 * hv, CM, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * it + 4 * (lane >> 4) + e;
           if (c * CM + t < T)
-            In<E>::store1(o + ((size_t)bh * T + c * CM + t) * DV + v0 + vl,
-                          oacc[i][e] - me[e] + OZl[t * kR7VT + vl]);
+            In<E>::store1(o + ((size_t)bh * T + c * CM + t) * DV + v0 + 16 * hv + vl,
+                          oacc[i][e] - me[e] + OZl[t * VT + 16 * hv + vl]);
         }
       }
     }
@@ -359,12 +430,15 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
     for (int i = 0; i < PER; ++i) {
       const int J = wid + 4 * i;
       if (J < NST) {
-        f32x4 ae = f4zero();
-        tile_nt(ae, ATl, LC, 16 * J, ETl, LC, 0, CM, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * J + 4 * (lane >> 4) + e;
-          S[i][e] = PIl[row] * S[i][e] - ae[e] + WZl[row * kR7VT + vl];
+        for (int hv = 0; hv < NHV; ++hv) {
+          f32x4 ae = f4zero();
+          tile_nt(ae, ATl, LC, 16 * J, ETl, LC, 16 * hv, CM, lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * J + 4 * (lane >> 4) + e;
+            S[i][hv][e] = PIl[row] * S[i][hv][e] - ae[e] + WZl[row * VT + 16 * hv + vl];
+          }
         }
       }
     }
@@ -376,8 +450,10 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
       const int J = wid + 4 * i;
       if (J < NST) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          S_out[((size_t)bh * DK + 16 * J + 4 * (lane >> 4) + e) * DV + v0 + vl] = S[i][e];
+        for (int hv = 0; hv < NHV; ++hv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S_out[((size_t)bh * DK + 16 * J + 4 * (lane >> 4) + e) * DV + v0 + 16 * hv + vl] = S[i][hv][e];
       }
     }
   }
@@ -502,16 +578,19 @@ static int r7_launch(const Rwkv7Args& a, void* ws) {
       return GDR_ERR_LAUNCH;
   }
   {
+    // 32-column value tiles where d_v allows, else 16
     constexpr int LY = DK + 4, LC = CM + 4;
-    const int lds = 4 * (2 * CM * LY + CM * LC + DK * LC + kR7VT * LY + kR7VT * LC + 2 * CM * kR7VT + DK * kR7VT + DK);
-    auto kern = rwkv7_scan_kernel<E, DK, CM>;
-    if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
+    const int vt = a.dv % 32 == 0 ? 32 : 16;
+    const int lds = 4 * (2 * CM * LY + CM * LC + DK * LC + vt * LY + vt * LC + 2 * CM * vt + DK * vt + DK);
+    const void* kern = vt == 32 ? (const void*)rwkv7_scan_kernel<E, DK, CM, 32>
+                                : (const void*)rwkv7_scan_kernel<E, DK, CM, 16>;
+    if (!allow_lds(kern, lds)) return GDR_ERR_LAUNCH;
     const float* wsc = wsf;
     const float* S0 = a.S0;
     E* o = (E*)a.o;
     float* So = a.S_out;
     void* args[] = {&wsc, &S0, &o, &So, &T, &DV};
-    if (hipLaunchKernel((const void*)kern, dim3(BH * (DV / kR7VT)), dim3(kR7Threads), args, lds, st) != hipSuccess)
+    if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kR7Threads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   return GDR_OK;
