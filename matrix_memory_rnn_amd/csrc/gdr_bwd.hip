@@ -258,8 +258,88 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
         D[i][hv][e] = (J < NST && dST) ? dST[((size_t)bh * DK + row) * DV + v0 + 16 * hv + vl] : 0.f;
       }
   }
-  for (int c = nch - 1; c >= 0; --c) {
+  // The next (earlier) chunk's record slices and dO tile load into registers
+  // while this chunk is worked on; in LDS every transposed slice is written
+  // with consecutive lanes on consecutive addresses (conflict free), which
+  // also makes consecutive lanes read consecutive 16-byte pieces of the
+  // F-order record.
+  constexpr int QM = CM * CM / 8, QK = DK * CM / 8, QQ = CM * DK / 8, QO = CM * VT;
+  constexpr int NTH = kBwdThreads;
+  constexpr int NM = (QM + NTH - 1) / NTH, NK = (QK + NTH - 1) / NTH, NQ = (QQ + NTH - 1) / NTH,
+                NO = (QO + NTH - 1) / NTH;
+  float rm[NM][8], rk[NK][8], rq[NQ][8], ry[NQ][8], rg[NO], rp = 0.f;
+  auto fetch = [&](int c) {
     const Rec<E, FM> R{ws + ((size_t)bh * nch + c) * RL.bytes, RL, DK, CM};
+    const int t0 = c * CM;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int x = tid + NTH * i;
+      if (QM % NTH == 0 || x < QM) R.m8(x % CM, 8 * (x / CM), rm[i]);          // M rows t, columns s0..
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int x = tid + NTH * i;
+      if (QK % NTH == 0 || x < QK) R.kt8(x % DK, 8 * (x / DK), rk[i]);         // K~^T rows j, columns s0..
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int x = tid + NTH * i;
+      if (QQ % NTH == 0 || x < QQ) {
+        R.qp8(x % CM, 8 * (x / CM), rq[i]);                                     // rows t, columns j0..
+        R.y8(x % CM, 8 * (x / CM), ry[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const int x = tid + NTH * i;
+      if (QO % NTH == 0 || x < QO) {
+        const int t = x / VT, v = x % VT;
+        const float g = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
+        rg[i] = t0 + t < T ? g : 0.f;
+      }
+    }
+    if (tid < DK) rp = R.pic(tid);
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int x = tid + NTH * i;
+      if (QM % NTH == 0 || x < QM) {
+        const int t = x % CM, s0 = 8 * (x / CM);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = rm[i][e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int x = tid + NTH * i;
+      if (QK % NTH == 0 || x < QK) {
+        const int jr = x % DK, s0 = 8 * (x / DK);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = rk[i][e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int x = tid + NTH * i;
+      if (QQ % NTH == 0 || x < QQ) {
+        const int t = x % CM, j0 = 8 * (x / CM);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          QTl[(j0 + e) * LC + t] = rq[i][e];
+          YTl[(j0 + e) * LC + t] = ry[i][e];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const int x = tid + NTH * i;
+      if (QO % NTH == 0 || x < QO) DOTl[(x % VT) * LC + x / VT] = rg[i];
+    }
+    if (tid < DK) PIl[tid] = rp;
+  };
+  fetch(nch - 1);
+  for (int c = nch - 1; c >= 0; --c) {
     float* dHc = dHs + ((size_t)bh * nch + c) * DK * DV;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -275,38 +355,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
           }
       }
     }
-    const int t0 = c * CM;
-    GDR_STAGE_FOR(x, CM * CM / 8, kBwdThreads) {
-      const int t = x / (CM / 8), s0 = 8 * (x % (CM / 8));
-      float o[8];
-      R.m8(t, s0, o);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = o[e];
-    }
-    GDR_STAGE_FOR(x, DK * CM / 8, kBwdThreads) {
-      const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
-      float o[8];
-      R.kt8(jr, s0, o);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = o[e];
-    }
-    GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {
-      const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
-      float o[8], p8[8];
-      R.qp8(t, j0, o);
-      R.y8(t, j0, p8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        QTl[(j0 + e) * LC + t] = o[e];
-        YTl[(j0 + e) * LC + t] = p8[e];
-      }
-    }
-    GDR_STAGE_FOR(x, CM * VT, kBwdThreads) {
-      const int t = x / VT, v = x % VT;
-      const float g = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
-      DOTl[v * LC + t] = t0 + t < T ? g : 0.f;
-    }
-    GDR_STAGE_FOR(j, DK, kBwdThreads) PIl[j] = R.pic(j);
+    stage();
+    if (c > 0) fetch(c - 1);
     __syncthreads();
     // dV~ = M^T dO + K~ dS
     for (int p = wid; p < (CM / 16) * NHV; p += 4) {
