@@ -1821,7 +1821,7 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
 // (a segment g) maps its start state affinely, S_end = P_g S_start + Q_g, and
 // a head with few value tiles but many chunks can walk its segments side by
 // side:
-//   seg_state:   every (b, h, segment, 32-column tile of [Q | P]) walks the
+//   seg_state:   every (b, h, segment but the last, 32-column tile of [Q | P]) walks the
 //                segment from [0 | I]: the Q tiles with the record's U, the P
 //                tiles with U = 0 (d_k identity columns carried through the
 //                homogeneous map), giving [Q_g | P_g] (fp32);
@@ -1853,11 +1853,12 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const int nvt = DV / 32, ntile = nvt + DK / 32;
-  const int ntot = (T + CM - 1) / CM, nseg = (ntot + seg - 1) / seg;
+  // the maps of segments 0 .. nseg - 2 (the last segment's map is never used)
+  const int ntot = (T + CM - 1) / CM, nseg = (ntot + seg - 1) / seg, nmap = nseg - 1;
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x, ntile);
   const int unit = lin / ntile, tile = lin % ntile;
-  const int bh = unit / nseg, sg = unit % nseg;
-  const int BH = gridDim.x / (ntile * nseg);
+  const int bh = unit / nmap, sg = unit % nmap;
+  const int BH = gridDim.x / (ntile * nmap);
   const bool ptile = tile >= nvt;                      // a column tile of P (U = 0, identity start)
   const int c0 = sg * seg, nch = ntot - c0 < seg ? ntot - c0 : seg;
   const RecLayout RL = rec_layout(DK, DV, CM, 2);
@@ -2146,7 +2147,7 @@ static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
     float* Ss = Saug + (size_t)nseg * BH * DK * (a.dv + DK);
     const int ntile = a.dv / 32 + DK / 32;
     void* a1[] = {&ws, &Saug, &T, &DV, &seg};
-    hipError_t e = hipLaunchKernel((const void*)gdn2_chunk_seg_state_kernel<DK, CM>, dim3(nseg * BH * ntile),
+    hipError_t e = hipLaunchKernel((const void*)gdn2_chunk_seg_state_kernel<DK, CM>, dim3((nseg - 1) * BH * ntile),
                                    dim3(kSegThreads), a1, 0, (hipStream_t)a.stream);
     if (e != hipSuccess) return GDR_ERR_LAUNCH;
     int nsg = nseg;
