@@ -16,25 +16,29 @@
 //   dU = dV~,  dY = -dV~ S0^T,  dQ_pi = dO S0^T,  dK~ = V~ dS_C^T,
 //   dM = dO V~^T (t >= s),  dpi_C = rowsum(dS_C * S0).
 // Kernels (one launch each, in this order):
-//   bwd_states   per (b, h, 16-column value tile): walks the chunks forward
-//                and stores every chunk-start state (fp32);
-//   bwd_dstates  per (b, h, 16-column value tile): walks the chunks backward
-//                from dS_T and stores every chunk-end state gradient; the
-//                last one is dS0;
-//   bwd_chunk    per (b, h, chunk): the products above over the value tiles,
-//                contractions over d_v accumulated in registers;
-//   bwd_solve    per (b, h, chunk): L from the inputs (fp32, pairwise decays
-//                exp(Lambda_t - Lambda_s), every exponent <= 0), the
-//                transposed unit-triangular solve by back substitution,
-//                dv and dw, and dL;
-//   bwd_decay    per (b, h, chunk, 64 key channels): the key channels are
-//                independent in what is left: dk^, dq, dk from dL and dM
-//                (column and row sums with pairwise decays), the direct
-//                terms of Q_pi, K^_pi, K~ and pi_C, d Lambda, and
-//                d alpha = (reverse cumulative sum of d Lambda) / alpha.
-// Products run on the fp32 matrix cores (16x16x4 fp32 MFMA, operands staged
-// in LDS in fp32), so the backward keeps fp32 precision apart from the bf16
-// record of a bf16 forward.
+//   chunk states  every chunk-start state (fp32): for F-order records the
+//                 forward's F-order scan instantiated without outputs and with
+//                 a state store, otherwise bwd_states per (b, h, 16-column
+//                 value tile);
+//   bwd_dstates   per (b, h, 32-column value tile; 16 for d_v = 16): walks the
+//                 chunks backward from dS_T and stores every chunk-end state
+//                 gradient; the last one is dS0;
+//   bwd_chunk     per (b, h, chunk): the products above over the value tiles,
+//                 contractions over d_v accumulated in registers;
+//   bwd_solve     per (b, h, chunk): L from the inputs (fp32 MFMA over the key
+//                 channels, split at 16-row blocks with pivots), the
+//                 transposed unit-triangular solve by back substitution, dv
+//                 and dw, and dL;
+//   bwd_decay     per (b, h, chunk, 32 key channels): the key channels are
+//                 independent in what is left: dk^, dq, dk from dL and dM
+//                 (fp32 MFMA products with the decays split at the 16-row
+//                 blocks), the direct terms of Q_pi, K^_pi, K~ and pi_C,
+//                 d Lambda, and d alpha = (reverse cumulative sum of d Lambda)
+//                 / alpha.
+// Products run on the fp32 matrix cores (16x16x4 fp32 MFMA), so the backward
+// keeps fp32 precision apart from the bf16 record of a bf16 forward. A block
+// whose decay falls below 2^-20 in some channel takes exact pairwise decay
+// factors for its diagonal tile.
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
 #include "gdr_host.hpp"
