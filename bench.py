@@ -225,7 +225,10 @@ def bench_bwd(steps, warmup, c, x):
     gdr.gdr_chunk_intra(*x, chunk=C, workspace=ws)
     ready, _ = time_launches(lambda: gdr.gdr_chunk_bwd(*x, None, dO, chunk=C, workspace=ws, records_ready=True),
                              steps, warmup)
-    return dict(B=B, T=T, full_ms=full, ready_ms=ready, ws_bytes=ws.numel())
+    # algorithmic bytes: q, k, alpha, b, v, w, dO read (bf16), the six input
+    # gradients written (fp32), dS0 written
+    nbytes = B * H * T * ((4 * dk + 3 * dv) * 2 + (4 * dk + 2 * dv) * 4) + B * H * dk * dv * 4
+    return dict(B=B, T=T, full_ms=full, ready_ms=ready, ws_bytes=ws.numel(), bytes=nbytes)
 
 
 def bench_rwkv7(steps, warmup):
@@ -437,7 +440,9 @@ def main():
         out["backward"] = {"workload": "4K workload, gradients of q, k, v, alpha, b, w and S0 from dO",
                            "entry": "gdr_chunk_bwd", "ms_per_step": bw["full_ms"],
                            "ms_per_step_records_ready": bw["ready_ms"],
-                           "tokens/s": bw["B"] * bw["T"] / (bw["full_ms"] * 1e-3), "workspace_bytes": bw["ws_bytes"]}
+                           "tokens/s": bw["B"] * bw["T"] / (bw["full_ms"] * 1e-3), "workspace_bytes": bw["ws_bytes"],
+                           "algorithmic_bytes": bw["bytes"], "GB/s": bw["bytes"] / (bw["full_ms"] * 1e-3) / 1e9,
+                           "frac_hbm": bw["bytes"] / (bw["full_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del x
     if not args.no_side:
         f_region, f_launch = bench_fused(args.steps, args.warmup, c, chunk_inputs("chunk_4k")[2], None)
