@@ -50,7 +50,7 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 constexpr float kBwdExactLog = -13.86f;   // log 2^-20: in-block decays below it take exact factors
-constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel
+constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel (tile_nt16 there)
 
 __device__ __forceinline__ int acc_row(int lane, int e) { return 4 * (lane >> 4) + e; }
 
@@ -528,15 +528,15 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
       const int p = wid + 4 * i;
       if (p < NYT) {
         const int ti = p / (DK / 16), tj = p % (DK / 16);
-        tile_nt(aY[i], dVl, L16, 16 * ti, S0l, L16, 16 * tj, kVT, lane);   // dV~ S0^T
-        tile_nt(aQ[i], dOl, L16, 16 * ti, S0l, L16, 16 * tj, kVT, lane);   // dO S0^T
-        tile_nt(aK[i], Vl, L16, 16 * ti, dSl, L16, 16 * tj, kVT, lane);    // V~ dS^T
+        tile_nt16(aY[i], dVl, L16, 16 * ti, S0l, L16, 16 * tj, lane);   // dV~ S0^T
+        tile_nt16(aQ[i], dOl, L16, 16 * ti, S0l, L16, 16 * tj, lane);   // dO S0^T
+        tile_nt16(aK[i], Vl, L16, 16 * ti, dSl, L16, 16 * tj, lane);    // V~ dS^T
       }
     }
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
       const int p = wid + 4 * i;
-      if (p < NMT) tile_nt(aM[i], dOl, L16, 16 * (p / (CM / 16)), Vl, L16, 16 * (p % (CM / 16)), kVT, lane);
+      if (p < NMT) tile_nt16(aM[i], dOl, L16, 16 * (p / (CM / 16)), Vl, L16, 16 * (p % (CM / 16)), lane);
     }
     if (tid < DK) {
 #pragma unroll

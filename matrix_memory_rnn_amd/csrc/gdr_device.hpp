@@ -298,6 +298,18 @@ __device__ __forceinline__ void tile_nt(f32x4& acc, const float* A, int lda, int
   }
 }
 
+// The same tile for K = 16: lane group g supplies k = 4g .. 4g+3 of its row,
+// instruction e takes k = 4g + e from group g, so four instructions cover the
+// 16 k once (tile_nt would run eight, half of them on zeros).
+__device__ __forceinline__ void tile_nt16(f32x4& acc, const float* A, int lda, int m0, const float* B, int ldb,
+                                          int n0, int lane) {
+  const int k = 4 * (lane >> 4);
+  const f32x4 a = *(const f32x4*)(A + (m0 + (lane & 15)) * lda + k);
+  const f32x4 b = *(const f32x4*)(B + (n0 + (lane & 15)) * ldb + k);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], b[e], acc);
+}
+
 // A staging loop x = tid, tid + NT, .. < N over compile-time N and NT, fully
 // unrolled, so that the loads of all its iterations are issued before the
 // first of them is used: a plain strided loop (whose trip count the compiler
