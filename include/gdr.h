@@ -27,8 +27,17 @@
  * LDS); gdr_chunk_fwd_ws has no such limit.
  * Alignment: every pointer must be 16-byte aligned.
  *
- * Preconditions not checked on the hot path: alpha in (0, 1]; inputs finite;
- * output buffers do not overlap input buffers except where stated.
+ * Preconditions not checked on the hot path: alpha (and RWKV-7's w) in
+ * (0, 1]; inputs finite; output buffers do not overlap input buffers except
+ * where stated. The overlap rule is checked on the host in every build. The
+ * value rules are checked only by the debug library, libgdr_debug.so (the
+ * same sources built with GDR_DEBUG defined; the Python binding loads it when
+ * the environment variable GDR_DEBUG is set to 1): before enqueuing any compute
+ * kernel each entry point reads its inputs once on the GPU, waits for the
+ * result and returns GDR_ERR_PRECONDITION, with nothing enqueued, when an
+ * element breaks its rule; gdr_debug_violation then names the arguments.
+ * Those checks synchronise the stream, so the debug library's entry points
+ * cannot be captured into a HIP graph.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -50,6 +59,7 @@ extern "C" {
 #define GDR_ERR_ALIAS       -7  /* an output buffer overlaps an input buffer */
 #define GDR_ERR_WORKSPACE   -8  /* workspace smaller than gdr_chunk_workspace_size reports */
 #define GDR_ERR_TOO_LARGE   -9  /* one head needs more than gdr_chunk_fwd_noalloc's static scratch */
+#define GDR_ERR_PRECONDITION -10 /* debug library only: a non-finite input, or a decay outside (0, 1] */
 
 /* Input/output element types. States (S, C, n, m) are always float32. */
 #define GDR_F32  0
@@ -370,6 +380,21 @@ const char* gdr_status_string(int status);
 
 /* Library version: major*10000 + minor*100 + patch. */
 int gdr_version(void);
+
+/*
+ * gdr_debug_build — 1 for the debug library (GDR_DEBUG defined: every entry
+ * point checks its inputs' values, see the top of this header), 0 otherwise.
+ *
+ * gdr_debug_violation — after an entry point of the debug library returned
+ * GDR_ERR_PRECONDITION on the calling thread: the names of the arguments that
+ * broke their rule (as in this header, comma-separated; the decays alpha and
+ * w must lie in (0, 1], the mLSTM stabiliser m0 may also be -inf, every other
+ * input must be finite). "" after a call that passed, and always "" in the
+ * release library. The text is thread-local and valid until the thread's
+ * next call into the library.
+ */
+int gdr_debug_build(void);
+const char* gdr_debug_violation(void);
 
 #ifdef __cplusplus
 }

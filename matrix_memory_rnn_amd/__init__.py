@@ -4,7 +4,11 @@ A thin ctypes layer over ``libgdr.so`` (see ``include/gdr.h``): it checks
 tensor shapes and dtypes, allocates outputs with torch, and passes raw device
 pointers and the current HIP stream to the C entry points. Every step of the
 computation runs in the library's HIP kernels; there is no fallback. If the
-library has not been built the first call raises.
+library has not been built the first call raises. With the environment
+variable ``GDR_DEBUG=1`` the binding loads ``libgdr_debug.so`` instead: the
+same kernels, with every entry point first checking on the GPU that its inputs
+are finite and its decays lie in (0, 1] (a :class:`GdrError` with status
+``GDR_ERR_PRECONDITION`` names the offending arguments).
 
 Entry points (same names as the C ABI):
 
@@ -31,10 +35,15 @@ __all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_ws", "gdr_chunk_fwd_noalloc", "gdr_mu
            "gdr_rwkv7_decode_step",
            "gdr_muir_decode_step", "gdr_chunk_workspace_size", "gdr_chunk_intra",
            "gdr_chunk_scan", "gdr_mlstm_fwd_ws", "gdr_mlstm_workspace_size", "gdr_decode_step", "gdr_mlstm_fwd", "gdr_version", "lib_path",
-           "GdrError", "load_library"]
+           "GdrError", "load_library", "declare"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_PKG, "libgdr.so")
+# GDR_DEBUG=1 selects the debug library: the same kernels, with every entry
+# point checking its inputs' values (finite; decays in (0, 1]) on the GPU
+# before it enqueues them, and returning GDR_ERR_PRECONDITION otherwise
+DEBUG = os.environ.get("GDR_DEBUG", "0") not in ("", "0")
+lib_path = os.path.join(_PKG, "libgdr_debug.so" if DEBUG else "libgdr.so")
+GDR_ERR_PRECONDITION = -10
 
 GDR_F32, GDR_BF16 = 0, 1
 _lib = None
@@ -61,7 +70,13 @@ def load_library():
     # same runtime instance instead of initialising a second one (which then
     # may see no device)
     import torch  # noqa: F401
-    lib = ctypes.CDLL(lib_path)
+    _lib = declare(ctypes.CDLL(lib_path))
+    return _lib
+
+
+def declare(lib):
+    """Set the argument and result types of every entry point on a loaded
+    libgdr (any of its builds); returns ``lib``."""
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.gdr_chunk_fwd.argtypes = [P] * 9 + [I] * 7 + [P]
     lib.gdr_chunk_fwd.restype = I
@@ -101,7 +116,10 @@ def load_library():
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
     lib.gdr_version.restype = I
-    _lib = lib
+    lib.gdr_debug_build.argtypes = []
+    lib.gdr_debug_build.restype = I
+    lib.gdr_debug_violation.argtypes = []
+    lib.gdr_debug_violation.restype = ctypes.c_char_p
     return lib
 
 
@@ -112,7 +130,10 @@ def gdr_version() -> int:
 def _check(fn, status):
     if status != 0:
         lib = load_library()
-        raise GdrError(fn, status, lib.gdr_status_string(status).decode())
+        text = lib.gdr_status_string(status).decode()
+        if status == GDR_ERR_PRECONDITION:
+            text += f" [{lib.gdr_debug_violation().decode()}]"
+        raise GdrError(fn, status, text)
 
 
 def _dtype_code(t):

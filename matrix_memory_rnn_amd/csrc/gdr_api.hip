@@ -1,6 +1,8 @@
 // C-ABI entry points of libgdr: host-side argument validation, then dispatch
 // to the gfx950 kernel launchers. Validation touches no GPU state, so every
-// error code is returned before anything is enqueued.
+// error code is returned before anything is enqueued. Built with GDR_DEBUG
+// defined, each entry point also checks its inputs' values on the GPU (see
+// gdr_debug.hpp) after the host checks and before its first compute kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,6 +10,21 @@
 
 #include "gdr_internal.h"
 #include "gdr_host.hpp"
+
+#ifdef GDR_DEBUG
+#include "gdr_debug.hpp"
+// Runs a value check and returns its status from the entry point on failure.
+#define GDR_DEBUG_CHECK(call)            \
+  do {                                   \
+    const int gdr_dbg_st_ = (call);      \
+    if (gdr_dbg_st_ != GDR_OK) return gdr_dbg_st_; \
+  } while (0)
+#else
+// Release build: the value checks are not compiled.
+#define GDR_DEBUG_CHECK(call) \
+  do {                        \
+  } while (0)
+#endif
 
 namespace {
 
@@ -116,6 +133,68 @@ int check_decode(const void* q, const void* k, const void* v, const void* alpha,
   return GDR_OK;
 }
 
+#ifdef GDR_DEBUG
+// Value checks of the debug build, one per family of entry points. Sequence
+// tensors have B*H*T rows, states B*H; `sname` names the state argument.
+using gdr::dbg::Arg;
+constexpr int kFin = gdr::dbg::kFinite, kUnit = gdr::dbg::kUnitDecay;
+
+int precheck_gdn(void* stream, const void* q, const void* k, const void* v, const void* alpha,
+                 const void* b, const void* w, const float* S, const char* sname, long long B, long long H,
+                 long long T, int dk, int dv, int dtype) {
+  const size_t nK = (size_t)(B * H * T) * dk, nV = (size_t)(B * H * T) * dv, nS = (size_t)(B * H) * dk * dv;
+  const Arg a[] = {{"q", q, nK, dtype, kFin},         {"k", k, nK, dtype, kFin}, {"v", v, nV, dtype, kFin},
+                   {"alpha", alpha, nK, dtype, kUnit}, {"b", b, nK, dtype, kFin}, {"w", w, nV, dtype, kFin},
+                   {sname, S, nS, GDR_F32, kFin}};
+  return gdr::dbg::check(stream, a, 7);
+}
+
+int precheck_muir(void* stream, const void* q, const void* k, const void* v, const void* zf, const void* zb,
+                  const void* zw, const void* zq, const float* a_log, const float* gamma, const float* S,
+                  const char* sname, long long B, long long H, long long T, int dk, int dv, int dtype) {
+  const size_t nK = (size_t)(B * H * T) * dk, nV = (size_t)(B * H * T) * dv, nS = (size_t)(B * H) * dk * dv;
+  const Arg a[] = {{"q", q, nK, dtype, kFin},      {"k", k, nK, dtype, kFin},
+                   {"v", v, nV, dtype, kFin},      {"z_f", zf, nK, dtype, kFin},
+                   {"z_b", zb, nK, dtype, kFin},   {"z_w", zw, nV, dtype, kFin},
+                   {"z_q", zq, nK, dtype, kFin},   {"a_log", a_log, (size_t)H, GDR_F32, kFin},
+                   {"gamma_stat", gamma, (size_t)H * dk, GDR_F32, kFin}, {sname, S, nS, GDR_F32, kFin}};
+  return gdr::dbg::check(stream, a, 10);
+}
+
+int precheck_mlstm(void* stream, const void* q, const void* k, const void* v, const float* it, const float* ft,
+                   const float* C0, const float* n0, const float* m0, int B, int H, int T, int dk, int dv,
+                   int dtype) {
+  const size_t n = (size_t)B * H * T, nh = (size_t)B * H;
+  const Arg a[] = {{"q", q, n * dk, dtype, kFin},   {"k", k, n * dk, dtype, kFin},
+                   {"v", v, n * dv, dtype, kFin},   {"i_tilde", it, n, GDR_F32, kFin},
+                   {"f_tilde", ft, n, GDR_F32, kFin}, {"C0", C0, nh * dk * dv, GDR_F32, kFin},
+                   {"n0", n0, nh * dk, GDR_F32, kFin}, {"m0", m0, nh, GDR_F32, gdr::dbg::kFiniteOrNegInf}};
+  return gdr::dbg::check(stream, a, 8);
+}
+
+int precheck_rwkv7(void* stream, const void* q, const void* w, const void* a_, const float* c, const void* kw,
+                   const void* u, const float* S, const char* sname, int B, int H, int T, int dk, int dv,
+                   int dtype) {
+  const size_t n = (size_t)B * H * T, nS = (size_t)B * H * dk * dv;
+  const Arg a[] = {{"q", q, n * dk, dtype, kFin},  {"w", w, n * dk, dtype, kUnit}, {"a", a_, n * dk, dtype, kFin},
+                   {"c", c, n, GDR_F32, kFin},     {"kw", kw, n * dk, dtype, kFin}, {"u", u, n * dv, dtype, kFin},
+                   {sname, S, nS, GDR_F32, kFin}};
+  return gdr::dbg::check(stream, a, 7);
+}
+
+int precheck_bwd_extra(void* stream, const void* dO, const float* dS_T, int B, int H, int T, int dk, int dv,
+                       int dtype) {
+  const Arg a[] = {{"dO", dO, (size_t)B * H * T * dv, dtype, kFin},
+                   {"dS_T", dS_T, (size_t)B * H * dk * dv, GDR_F32, kFin}};
+  return gdr::dbg::check(stream, a, 2);
+}
+
+int precheck_state(void* stream, const float* S, const char* sname, int B, int H, int dk, int dv) {
+  const Arg a[] = {{sname, S, (size_t)B * H * dk * dv, GDR_F32, kFin}};
+  return gdr::dbg::check(stream, a, 1);
+}
+#endif  // GDR_DEBUG
+
 }  // namespace
 
 extern "C" {
@@ -135,6 +214,8 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_WORKSPACE: return "the workspace is smaller than gdr_chunk_workspace_size reports";
     case GDR_ERR_TOO_LARGE:
       return "one head needs more scratch than the library's static array holds (GDR_NOALLOC_SCRATCH_BYTES)";
+    case GDR_ERR_PRECONDITION:
+      return "an input is not finite, or a decay lies outside (0, 1] (debug library; gdr_debug_violation names it)";
   }
   return "unknown status";
 }
@@ -145,6 +226,7 @@ int gdr_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha
   int st = check_chunk(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype);
   if (st != GDR_OK) return st;
   if (dtype == GDR_F32 && dk >= 64 && chunk > 32) return GDR_ERR_UNSUPPORTED;
+  GDR_DEBUG_CHECK(precheck_gdn(stream, q, k, v, alpha, b, w, S0, "S0", B, H, T, dk, dv, dtype));
   gdr::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::chunk_fwd_launch(a);
 }
@@ -168,6 +250,7 @@ int gdr_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* al
   st = check_workspace(q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, workspace,
                        workspace_bytes);
   if (st != GDR_OK) return st;
+  GDR_DEBUG_CHECK(precheck_gdn(stream, q, k, v, alpha, b, w, S0, "S0", B, H, T, dk, dv, dtype));
   gdr::ChunkArgs a{q, k, v, alpha, b, w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::chunk_fwd_ws_launch(a, workspace, 3);
 }
@@ -180,6 +263,7 @@ int gdr_chunk_intra(const void* q, const void* k, const void* v, const void* alp
   st = check_workspace(q, k, v, alpha, b, w, nullptr, nullptr, nullptr, B, H, T, dk, dv, chunk, dtype,
                        workspace, workspace_bytes);
   if (st != GDR_OK) return st;
+  GDR_DEBUG_CHECK(precheck_gdn(stream, q, k, v, alpha, b, w, nullptr, "S0", B, H, T, dk, dv, dtype));
   gdr::ChunkArgs a{q, k, v, alpha, b, w, nullptr, nullptr, nullptr, B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::chunk_fwd_ws_launch(a, workspace, 1);
 }
@@ -201,6 +285,7 @@ int gdr_chunk_scan(const void* workspace, size_t workspace_bytes, const float* S
       overlap(S0, nS, workspace, need) || overlap(o, nV, S0, nS) || overlap(o, nV, S_out, nS))
     return GDR_ERR_ALIAS;
   if (S_out && S0 && S_out != S0 && overlap(S_out, nS, S0, nS)) return GDR_ERR_ALIAS;
+  GDR_DEBUG_CHECK(precheck_state(stream, S0, "S0", B, H, dk, dv));
   gdr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S0, o, S_out, B, H, T, dk, dv,
                    chunk, dtype, stream};
   return gdr::chunk_fwd_ws_launch(a, const_cast<void*>(workspace), 2);
@@ -211,6 +296,7 @@ int gdr_decode_step(const void* q, const void* k, const void* v, const void* alp
                     void* stream) {
   int st = check_decode(q, k, v, alpha, b, w, S, o, N, H, dk, dv, dtype);
   if (st != GDR_OK) return st;
+  GDR_DEBUG_CHECK(precheck_gdn(stream, q, k, v, alpha, b, w, S, "S", N, H, 1, dk, dv, dtype));
   gdr::DecodeArgs a{q, k, v, alpha, b, w, S, o, N, H, dk, dv, dtype, stream};
   return gdr::decode_launch(a);
 }
@@ -254,6 +340,8 @@ int gdr_muir_chunk_fwd_ws(const void* q, const void* k, const void* v, const voi
   if (st != GDR_OK) return st;
   if (overlap(workspace, gdr::chunk_ws_bytes(B, H, T, dk, dv, chunk, dtype), z_q, (size_t)B * H * T * dk * es))
     return GDR_ERR_ALIAS;
+  GDR_DEBUG_CHECK(precheck_muir(stream, q, k, v, z_f, z_b, z_w, z_q, a_log, gamma_stat, S0, "S0", B, H, T, dk,
+                                dv, dtype));
   gdr::ChunkArgs a{q, k, v, z_f, z_b, z_w, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
   a.gated = true;
   a.zq = z_q;
@@ -271,6 +359,8 @@ int gdr_muir_decode_step(const void* q, const void* k, const void* v, const void
   st = check_muir_extra(z_q, a_log, gamma_stat, o, (size_t)N * H * dv * es, S,
                         (size_t)N * H * dk * dv * 4, (size_t)N * H * dk * es, H, dk);
   if (st != GDR_OK) return st;
+  GDR_DEBUG_CHECK(precheck_muir(stream, q, k, v, z_f, z_b, z_w, z_q, a_log, gamma_stat, S, "S", N, H, 1, dk, dv,
+                                dtype));
   gdr::DecodeArgs a{q, k, v, z_f, z_b, z_w, S, o, N, H, dk, dv, dtype, stream};
   a.gated = true;
   a.zq = z_q;
@@ -340,6 +430,7 @@ int gdr_mlstm_fwd(const void* q, const void* k, const void* v, const float* i_ti
   int st = check_mlstm(q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out, B, H, T, dk, dv,
                        chunk, dtype);
   if (st != GDR_OK) return st;
+  GDR_DEBUG_CHECK(precheck_mlstm(stream, q, k, v, i_tilde, f_tilde, C0, n0, m0, B, H, T, dk, dv, dtype));
   gdr::MlstmArgs a{q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out,
                    B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::mlstm_launch(a);
@@ -377,6 +468,7 @@ int gdr_mlstm_fwd_ws(const void* q, const void* k, const void* v, const float* i
                     {m0, nM}, {h, nV}, {C_out, nC}, {n_out, nN}, {m_out, nM}};
   for (const R& x : bufs)
     if (overlap(workspace, need, x.p, x.n)) return GDR_ERR_ALIAS;
+  GDR_DEBUG_CHECK(precheck_mlstm(stream, q, k, v, i_tilde, f_tilde, C0, n0, m0, B, H, T, dk, dv, dtype));
   gdr::MlstmArgs a{q, k, v, i_tilde, f_tilde, C0, n0, m0, h, C_out, n_out, m_out,
                    B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::mlstm_ws_launch(a, workspace);
@@ -421,6 +513,8 @@ extern "C" int gdr_chunk_bwd(const void* q, const void* k, const void* v, const 
     for (const R& y : outs)
       if (x.p != y.p && overlap(x.p, x.n, y.p, y.n)) return GDR_ERR_ALIAS;
   }
+  GDR_DEBUG_CHECK(precheck_gdn(stream, q, k, v, alpha, b, w, S0, "S0", B, H, T, dk, dv, dtype));
+  GDR_DEBUG_CHECK(precheck_bwd_extra(stream, dO, dS_T, B, H, T, dk, dv, dtype));
   gdr::ChunkBwdArgs a{q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk_, dv_, dalpha, db, dw, dS0,
                       B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::chunk_bwd_launch(a, workspace, records_ready != 0);
@@ -481,6 +575,7 @@ extern "C" int gdr_rwkv7_fwd(const void* q, const void* w, const void* a, const 
       overlap(workspace, need, c, n * 4) || overlap(workspace, need, S0, nS) ||
       overlap(workspace, need, S_out, nS))
     return GDR_ERR_ALIAS;
+  GDR_DEBUG_CHECK(precheck_rwkv7(stream, q, w, a, c, kw, u, S0, "S0", B, H, T, dk, dv, dtype));
   gdr::Rwkv7Args r{q, w, a, c, kw, u, S0, o, S_out, B, H, T, dk, dv, chunk, dtype, stream};
   return gdr::rwkv7_fwd_launch(r, workspace);
 }
@@ -491,6 +586,7 @@ extern "C" int gdr_rwkv7_decode_step(const void* q, const void* w, const void* a
   if (!S) return GDR_ERR_NULL;
   int st = check_rwkv7(q, w, a, c, kw, u, nullptr, o, S, N, H, 1, dk, dv, dtype);
   if (st != GDR_OK) return st;
+  GDR_DEBUG_CHECK(precheck_rwkv7(stream, q, w, a, c, kw, u, S, "S", N, H, 1, dk, dv, dtype));
   gdr::Rwkv7Args r{q, w, a, c, kw, u, nullptr, o, S, N, H, 1, dk, dv, 16, dtype, stream};
   return gdr::rwkv7_decode_launch(r);
 }
@@ -537,6 +633,7 @@ extern "C" int gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v
   // consecutive (b, h) pairs, as many per group as the array holds
   const size_t per_head = gdr::chunk_ws_bytes(1, 1, T, dk, dv, chunk, dtype, false);
   if (per_head > kScratchBytes) return GDR_ERR_TOO_LARGE;
+  GDR_DEBUG_CHECK(precheck_gdn(stream, q, k, v, alpha, b, w, S0, "S0", B, H, T, dk, dv, dtype));
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_LAUNCH;
   if (gdr::stream_device(stream) != dev) return GDR_ERR_LAUNCH;

@@ -1,16 +1,27 @@
 """C-ABI checks that need no GPU: the library loads, exports every function that
 include/gdr.h declares, and rejects bad arguments with the documented codes
-before enqueuing anything (all pointers here are fake and never dereferenced)."""
+before enqueuing anything (all pointers here are fake and never dereferenced).
+
+The same module also runs against libgdr_hostsan.so, whose entry points' host
+code carries AddressSanitizer and UndefinedBehaviorSanitizer checks: the last
+test starts a second pytest process on this file with that library selected
+(GDR_ABI_LIB) and the sanitizer runtime preloaded, so every validation path
+below also runs under the sanitizers."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdr.h")
-LIB = os.path.join(ROOT, "matrix_memory_rnn_amd", "libgdr.so")
+PKG = os.path.join(ROOT, "matrix_memory_rnn_amd")
+LIB = os.environ.get("GDR_ABI_LIB") or os.path.join(PKG, "libgdr.so")
+LIB_DEBUG = os.path.join(PKG, "libgdr_debug.so")
+LIB_HOSTSAN = os.path.join(PKG, "libgdr_hostsan.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libgdr.so not built")
 
@@ -28,6 +39,8 @@ def _codes():
 @pytest.fixture(scope="module")
 def lib():
     import matrix_memory_rnn_amd as m
+    if os.environ.get("GDR_ABI_LIB"):
+        return m.declare(ctypes.CDLL(LIB))   # no torch under the sanitizer runtime
     return m.load_library()
 
 
@@ -39,8 +52,11 @@ def test_header_declares_the_three_entry_points():
         assert n in names
 
 
-def test_library_exports_every_declared_symbol():
-    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+@pytest.mark.parametrize("path", [LIB, LIB_DEBUG, LIB_HOSTSAN])
+def test_library_exports_every_declared_symbol(path):
+    if not os.path.exists(path):
+        pytest.skip(f"{os.path.basename(path)} not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT\s+(gdr_\w+)", out))
     missing = [n for n in _declared() if n not in exported]
     assert not missing, f"declared but not exported: {missing}"
@@ -50,6 +66,22 @@ def test_symbols_resolve_through_dlopen(lib):
     for n in _declared():
         assert hasattr(lib, n)
     assert lib.gdr_version() == 200
+    assert lib.gdr_debug_violation().decode() == ""
+
+
+def test_debug_library_says_so():
+    """libgdr_debug.so reports itself as the checking build; libgdr.so does not."""
+    if not os.path.exists(LIB_DEBUG) or os.environ.get("GDR_ABI_LIB"):
+        pytest.skip("libgdr_debug.so not built")
+    import matrix_memory_rnn_amd as m
+    dbg = m.declare(ctypes.CDLL(LIB_DEBUG))
+    rel = m.declare(ctypes.CDLL(os.path.join(PKG, "libgdr.so")))
+    assert dbg.gdr_debug_build() == 1 and rel.gdr_debug_build() == 0
+    assert _codes()["GDR_ERR_PRECONDITION"] == -10
+    assert "gdr_debug_violation" in dbg.gdr_status_string(-10).decode()
+    # host validation runs first in the debug build too: nothing reaches the GPU
+    p = P[:7]
+    assert dbg.gdr_chunk_fwd(None, *p[1:6], None, p[6], None, 1, 2, 64, 16, 16, 16, 1, None) == -1
 
 
 def test_status_strings(lib):
@@ -239,3 +271,136 @@ def test_noalloc_rejects_a_head_larger_than_its_scratch(lib):
     st = lib.gdr_chunk_fwd_noalloc(None, p[1], p[2], p[3], p[4], p[5], None, p[6], None,
                                    1, 2, 64, 16, 16, 16, 1, None)
     assert st == c["GDR_ERR_NULL"]
+
+
+def test_muir_validation(lib):
+    c = _codes()
+    need = _ws_size(lib)[1]
+
+    def f(zq=None, a_log=P[11], gamma=None, ws=P[10], nbytes=None, o=P[6], ptrs=None):
+        p = list(P[:6]) if ptrs is None else ptrs
+        return lib.gdr_muir_chunk_fwd_ws(*p, zq, a_log, gamma, None, o, None, 1, 2, 64, 16, 16, 16, 1,
+                                         ws, need if nbytes is None else nbytes, None)
+
+    def g(zq=None, a_log=P[11], gamma=None, S=P[7], o=P[6], N=4, dk=16):
+        return lib.gdr_muir_decode_step(*P[:6], zq, a_log, gamma, S, o, N, 2, dk, 16, 1, None)
+
+    assert f(a_log=None) == c["GDR_ERR_NULL"]
+    assert f(ptrs=[None] + P[1:6]) == c["GDR_ERR_NULL"]
+    assert f(zq=P[12] + 8) == c["GDR_ERR_ALIGN"]
+    assert f(a_log=P[11] + 2) == c["GDR_ERR_ALIGN"]          # float32 arrays: 4-byte alignment
+    assert f(gamma=P[12] + 1) == c["GDR_ERR_ALIGN"]
+    assert f(o=P[11]) == c["GDR_ERR_ALIAS"]                  # o over a_log
+    assert f(nbytes=need - 1) == c["GDR_ERR_WORKSPACE"]
+    assert f(ws=P[12], zq=P[12] + 256) == c["GDR_ERR_ALIAS"]  # z_q inside the workspace
+    assert g(a_log=None) == c["GDR_ERR_NULL"]
+    assert g(S=None) == c["GDR_ERR_NULL"]
+    assert g(N=0) == c["GDR_ERR_SHAPE"]
+    assert g(dk=24) == c["GDR_ERR_UNSUPPORTED"]
+    assert g(gamma=P[12] + 2) == c["GDR_ERR_ALIGN"]
+    assert g(o=P[11]) == c["GDR_ERR_ALIAS"]
+
+
+def test_bwd_validation(lib):
+    c = _codes()
+
+    def need(T=64, chunk=16, dtype=1):
+        n = ctypes.c_size_t(7)
+        st = lib.gdr_chunk_bwd_workspace_size(1, 2, T, 16, 16, chunk, dtype, ctypes.byref(n))
+        return st, n.value
+
+    def f(ptrs=None, dO=P[7], dS_T=None, outs=None, ws=P[14], nbytes=None, chunk=16, T=64):
+        p = list(P[:6]) if ptrs is None else ptrs
+        o = [P[8], P[9], P[10], P[11], P[12], P[13], None] if outs is None else outs
+        n = need(64, 16)[1] if nbytes is None else nbytes
+        return lib.gdr_chunk_bwd(*p, None, dO, dS_T, *o, 1, 2, T, 16, 16, chunk, 1, ws, n, 0, None)
+
+    st, n = need()
+    assert st == c["GDR_OK"] and n > 0
+    assert need(T=0) == (c["GDR_ERR_SHAPE"], 0)
+    assert need(chunk=128)[0] == c["GDR_ERR_UNSUPPORTED"]
+    assert lib.gdr_chunk_bwd_workspace_size(1, 2, 64, 16, 16, 16, 1, None) == c["GDR_ERR_NULL"]
+    assert f(dO=None) == c["GDR_ERR_NULL"]
+    assert f(ws=None) == c["GDR_ERR_NULL"]
+    assert f(outs=[None, P[9], P[10], P[11], P[12], P[13], None]) == c["GDR_ERR_NULL"]
+    assert f(T=0) == c["GDR_ERR_SHAPE"]
+    assert f(chunk=8) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(dS_T=P[15] + 8) == c["GDR_ERR_ALIGN"]
+    assert f(nbytes=n - 1) == c["GDR_ERR_WORKSPACE"]
+    assert f(outs=[P[0], P[9], P[10], P[11], P[12], P[13], None]) == c["GDR_ERR_ALIAS"]          # dq over q
+    assert f(outs=[P[8], P[8] + 64, P[10], P[11], P[12], P[13], None]) == c["GDR_ERR_ALIAS"]     # dk over dq
+    assert f(ws=P[7] + 256) == c["GDR_ERR_ALIAS"]                                               # ws inside dO
+
+
+def test_rwkv7_validation(lib):
+    c = _codes()
+
+    def need(T=64, chunk=16):
+        n = ctypes.c_size_t(7)
+        st = lib.gdr_rwkv7_workspace_size(1, 2, T, 16, 16, chunk, ctypes.byref(n))
+        return st, n.value
+
+    def f(cc=P[3], ws=P[10], nbytes=None, chunk=16, o=P[6], S0=None, S_out=None, dk=16, T=64, q=P[0]):
+        n = need()[1] if nbytes is None else nbytes
+        return lib.gdr_rwkv7_fwd(q, P[1], P[2], cc, P[4], P[5], S0, o, S_out, 1, 2, T, dk, 16, chunk, 1,
+                                 ws, n, None)
+
+    def g(S=P[7], o=P[6], N=4, q=P[0]):
+        return lib.gdr_rwkv7_decode_step(q, P[1], P[2], P[3], P[4], P[5], S, o, N, 2, 16, 16, 1, None)
+
+    st, n = need()
+    assert st == c["GDR_OK"] and n > 0
+    assert need(chunk=64)[0] == c["GDR_ERR_UNSUPPORTED"]
+    assert need(T=0) == (c["GDR_ERR_SHAPE"], 0)
+    assert lib.gdr_rwkv7_workspace_size(1, 2, 64, 16, 16, 16, None) == c["GDR_ERR_NULL"]
+    assert f(cc=None) == c["GDR_ERR_NULL"]
+    assert f(ws=None) == c["GDR_ERR_NULL"]
+    assert f(T=0) == c["GDR_ERR_SHAPE"]
+    assert f(chunk=64) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(dk=48) == c["GDR_ERR_UNSUPPORTED"]
+    assert f(cc=P[3] + 4) == c["GDR_ERR_ALIGN"]
+    assert f(nbytes=n - 1) == c["GDR_ERR_WORKSPACE"]
+    assert f(o=P[5] + 32) == c["GDR_ERR_ALIAS"]              # o over u
+    assert f(ws=P[3]) == c["GDR_ERR_ALIAS"]                  # workspace over c
+    assert f(S0=P[8], S_out=P[8] + 64) == c["GDR_ERR_ALIAS"]
+    assert g(S=None) == c["GDR_ERR_NULL"]
+    assert g(N=0) == c["GDR_ERR_SHAPE"]
+    assert g(S=P[0]) == c["GDR_ERR_ALIAS"]                   # state over q
+    assert g(q=P[0] + 4) == c["GDR_ERR_ALIGN"]
+
+
+def _asan_runtime():
+    for clang in ("/opt/rocm/lib/llvm/bin/clang", "clang"):
+        try:
+            out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                                 text=True, timeout=30).stdout.strip()
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if out and os.path.isabs(out) and os.path.exists(out):
+            return out
+    hits = glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    return hits[0] if hits else None
+
+
+def test_validation_paths_under_host_sanitizers():
+    """Every validation test of this module, run again in a fresh process on
+    libgdr_hostsan.so with the ASan runtime preloaded: an out-of-bounds access,
+    use after free or undefined behaviour (signed overflow, misaligned access,
+    bad shift) in the host-side argument checks aborts that process."""
+    if os.environ.get("GDR_ABI_LIB"):
+        pytest.skip("already the sanitized run")
+    rt = _asan_runtime()
+    if not os.path.exists(LIB_HOSTSAN) or rt is None:
+        pytest.skip("libgdr_hostsan.so or the ASan runtime is missing")
+    env = dict(os.environ, GDR_ABI_LIB=LIB_HOSTSAN, LD_PRELOAD=rt,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_abi.py"),
+                        "-k", "not host_sanitizers and not fails_loudly"],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    tail = (r.stdout[-3000:] + "\n" + r.stderr[-3000:])
+    assert r.returncode == 0, tail
+    assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, tail
+    m = re.search(r"(\d+) passed", r.stdout)
+    assert m and int(m.group(1)) >= 10, tail
