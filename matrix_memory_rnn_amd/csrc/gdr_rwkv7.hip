@@ -29,7 +29,9 @@ namespace gdr {
 
 namespace {
 
-constexpr int kR7Threads = 256;
+constexpr int kR7Threads = 256;        // scan
+constexpr int kR7IntraThreads = 512;   // intra: eight waves, two per SIMD
+constexpr int kR7IntraWaves = kR7IntraThreads / 64;
 
 // Record of one (b, h, chunk), fp32 element offsets.
 struct R7Layout {
@@ -69,7 +71,7 @@ size_t rwkv7_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
 // its diagonal tile instead. The products with U (L_z U, M_z U, Z~^T U) are
 // MFMA tiles too; the unit lower-triangular solve runs one column per thread.
 template <typename E, int DK, int CM>
-__global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
+__global__ __launch_bounds__(kR7IntraThreads) void rwkv7_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ w, const E* __restrict__ a, const float* __restrict__ c,
     const E* __restrict__ kw, const E* __restrict__ u, float* __restrict__ ws, int T, int DV) {
   constexpr int P = DK + 4, PC = CM + 4, NB = CM / 16;
@@ -101,26 +103,54 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
   const R7Layout RL = r7_layout(DK, DV, CM);
   float* rec = ws + ((size_t)bh * nch + ch) * RL.floats;
   __shared__ int gflag[4];
-  // rows past T: w = 1, a = kw = q = 0, c = 0, u = 0 (identity steps)
-  GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
-    const int t = x / DK, j = x % DK;
-    const bool ok = t0 + t < T;
-    const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j;
-    const float a0 = (float)a[off], w0 = (float)w[off], z0 = (float)kw[off], q0 = (float)q[off];
-    Lam[t * P + j] = ok ? logf(w0) : 0.f;
-    Al[t * P + j] = ok ? a0 : 0.f;
-    Zl[t * P + j] = ok ? z0 : 0.f;
-    Ql[t * P + j] = ok ? q0 : 0.f;
+  static_assert(CM * DK / 8 <= kR7IntraThreads && CM * 128 / 8 <= kR7IntraThreads,
+                "one 8-element piece of each input per thread (d_v <= 128)");
+  // Every input of the chunk is loaded up front, 16 bytes per lane and at
+  // most one piece per thread and input (u too, though it is staged only
+  // after the Gram phase), so all their latencies overlap. The loads are
+  // unconditional (rows clamped into the sequence); rows past T become
+  // identity steps below: w = 1, a = kw = q = 0, c = 0, u = 0.
+  using RW = Raw<E>;
+  const int kt = tid / (DK / 8), kj = 8 * (tid % (DK / 8));          // [t][j] piece of this thread
+  const size_t koff = sK + (size_t)row_in(t0 + (kt < CM ? kt : 0), T) * DK + kj;
+  const typename RW::R8 rq = RW::ld8(q + koff), rw = RW::ld8(w + koff), ra = RW::ld8(a + koff),
+                        rz = RW::ld8(kw + koff);
+  // u pieces: consecutive threads take consecutive rows t (so the transposed
+  // LDS writes below hit distinct banks), then the next 8 value columns
+  const int ut = tid % CM, uv = 8 * (tid / CM);
+  const bool u_on = uv < DV;
+  const typename RW::R8 ru = RW::ld8(u + sV + (size_t)row_in(t0 + ut, T) * DV + (u_on ? uv : 0));
+  const float c0 = c[(size_t)bh * T + row_in(t0 + (tid < CM ? tid : 0), T)];
+  if (kt < CM) {
+    const bool ok = t0 + kt < T;
+    float fq[8], fw[8], fa[8], fz[8];
+    RW::un8(rq, fq);
+    RW::un8(rw, fw);
+    RW::un8(ra, fa);
+    RW::un8(rz, fz);
+#pragma unroll
+    for (int h4 = 0; h4 < 2; ++h4) {
+      f32x4 vl, va, vz, vq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vl[e] = ok ? logf(fw[4 * h4 + e]) : 0.f;
+        va[e] = ok ? fa[4 * h4 + e] : 0.f;
+        vz[e] = ok ? fz[4 * h4 + e] : 0.f;
+        vq[e] = ok ? fq[4 * h4 + e] : 0.f;
+      }
+      const int o4 = kt * P + kj + 4 * h4;
+      *(f32x4*)&Lam[o4] = vl;
+      *(f32x4*)&Al[o4] = va;
+      *(f32x4*)&Zl[o4] = vz;
+      *(f32x4*)&Ql[o4] = vq;
+    }
   }
-  GDR_STAGE_FOR(t, CM, kR7Threads) {
-    const float c0 = c[(size_t)bh * T + row_in(t0 + t, T)];
-    cv[t] = t0 + t < T ? c0 : 0.f;
-  }
+  if (tid < CM) cv[tid] = t0 + tid < T ? c0 : 0.f;
   if (tid < 4) gflag[tid] = 0;
   // the Gram tiles above the diagonal blocks are never formed: zero
-  GDR_STAGE_FOR(x, 4 * CM * PC, kR7Threads) La[x] = 0.f;
+  GDR_STAGE_FOR(x, 4 * CM * PC, kR7IntraThreads) La[x] = 0.f;
   __syncthreads();
-  GDR_STAGE_FOR(j, DK, kR7Threads) {
+  GDR_STAGE_FOR(j, DK, kR7IntraThreads) {
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < CM; ++t) {
@@ -138,14 +168,14 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
   // ---- phase G: the Gram matrices, one row block at a time
   for (int I = 0; I < NB; ++I) {
     const int p = 16 * I - 1, ns = 16 * (I + 1);
-    GDR_STAGE_FOR(x, 16 * DK, kR7Threads) {
+    GDR_STAGE_FOR(x, 16 * DK, kR7IntraThreads) {
       const int tl = x / DK, j = x % DK, t = 16 * I + tl;
       const float lp = I > 0 ? Lam[p * P + j] : 0.f;
       const float lt1 = t > 0 ? Lam[(t - 1) * P + j] : 0.f;
       Aq[tl * P + j] = Ql[t * P + j] * __expf(Lam[t * P + j] - lp);
       Ay[tl * P + j] = cv[t] * Al[t * P + j] * __expf(lt1 - lp);
     }
-    GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
+    GDR_STAGE_FOR(x, CM * DK, kR7IntraThreads) {
       const int s2 = x / DK, j = x % DK;
       if (s2 < ns) {
         const float lp = I > 0 ? Lam[p * P + j] : 0.f;
@@ -157,7 +187,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
     __syncthreads();
     const bool exact = gflag[I] != 0;
     // tiles (which, J): which = 0 M_a, 1 M_z, 2 L_a, 3 L_z; J = 0 .. I
-    for (int tile = wid; tile < 4 * (I + 1); tile += 4) {
+    for (int tile = wid; tile < 4 * (I + 1); tile += kR7IntraWaves) {
       const int which = tile % 4, J = tile / 4;
       const float* A = which < 2 ? Aq : Ay;
       const float* Bm = (which & 1) ? Bz : Ba;
@@ -188,30 +218,32 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
     __syncthreads();
   }
   // ---- phase R
-  GDR_STAGE_FOR(x, CM * DV, kR7Threads) {
-    const int t = x / DV, v = x % DV;
-    const float u0 = (float)u[sV + (size_t)row_in(t0 + t, T) * DV + v];
-    UT[v * PC + t] = t0 + t < T ? u0 : 0.f;
+  if (u_on) {
+    float fu[8];
+    RW::un8(ru, fu);
+    const bool ok = t0 + ut < T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) UT[(uv + e) * PC + ut] = ok ? fu[e] : 0.f;
   }
-  GDR_STAGE_FOR(x, CM * DK, kR7Threads) {
+  GDR_STAGE_FOR(x, CM * DK, kR7IntraThreads) {
     const int t = x / DK, j = x % DK;
     const float lt1 = t > 0 ? Lam[(t - 1) * P + j] : 0.f;
     Xl[t * NX + DV + j] = cv[t] * Al[t * P + j] * __expf(lt1);                 // Y_pi'
     ZT[j * PC + t] = __expf(Lam[(CM - 1) * P + j] - Lam[t * P + j]) * Zl[t * P + j];
     rec[RL.qp + t * DK + j] = __expf(Lam[t * P + j]) * Ql[t * P + j];
   }
-  GDR_STAGE_FOR(x, DK * CM, kR7Threads) {              // A~^T, rows j: consecutive threads store consecutive s
+  GDR_STAGE_FOR(x, DK * CM, kR7IntraThreads) {              // A~^T, rows j: consecutive threads store consecutive s
     const int j = x / CM, s2 = x % CM;
     rec[RL.at + j * CM + s2] = __expf(Lam[(CM - 1) * P + j] - Lam[s2 * P + j]) * Al[s2 * P + j];
   }
-  GDR_STAGE_FOR(j, DK, kR7Threads) rec[RL.pic + j] = __expf(Lam[(CM - 1) * P + j]);
-  GDR_STAGE_FOR(x, CM * CM, kR7Threads) rec[RL.ma + x] = Ma[(x / CM) * PC + x % CM];
+  GDR_STAGE_FOR(j, DK, kR7IntraThreads) rec[RL.pic + j] = __expf(Lam[(CM - 1) * P + j]);
+  GDR_STAGE_FOR(x, CM * CM, kR7IntraThreads) rec[RL.ma + x] = Ma[(x / CM) * PC + x % CM];
   __syncthreads();
   // L_z U into the right-hand side; O_z = M_z U and W_z = Z~^T U to the record
   {
     constexpr int NT = CM / 16;
     const int NV = DV / 16;
-    for (int tile = wid; tile < 2 * NT * NV + (DK / 16) * NV; tile += 4) {
+    for (int tile = wid; tile < 2 * NT * NV + (DK / 16) * NV; tile += kR7IntraWaves) {
       f32x4 acc = f4zero();
       if (tile < 2 * NT * NV) {
         const int which = tile / (NT * NV), r = tile % (NT * NV), it = r / NV, vt = r % NV;
@@ -235,16 +267,29 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_intra_kernel(
   }
   __syncthreads();
   // (I + L_a) X = RHS by forward substitution, one column per thread
-  for (int col = tid; col < DV + DK; col += kR7Threads) {
+  // Row t of L_a is read as 16-byte pieces when step t comes up; the
+  // scheduling barrier keeps the compiler from hoisting every row's loads to
+  // the top (which needs several hundred registers and spills at two waves
+  // per SIMD). Two partial sums halve the dependent chain of a step.
+  for (int col = tid; col < DV + DK; col += kR7IntraThreads) {
     float x[CM];
 #pragma unroll
     for (int t = 0; t < CM; ++t) x[t] = Xl[t * NX + col];
 #pragma unroll
     for (int t = 1; t < CM; ++t) {
-      float acc = x[t];
+      float acc0 = x[t], acc1 = 0.f;
 #pragma unroll
-      for (int s2 = 0; s2 < t; ++s2) acc -= La[t * PC + s2] * x[s2];
-      x[t] = acc;
+      for (int s4 = 0; s4 < t; s4 += 4) {
+        const f32x4 l4 = *(const f32x4*)&La[t * PC + s4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s4 + e < t) {
+            if (e & 1) acc1 -= l4[e] * x[s4 + e];
+            else acc0 -= l4[e] * x[s4 + e];
+          }
+      }
+      x[t] = acc0 + acc1;
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int t = 0; t < CM; ++t) {
@@ -574,7 +619,7 @@ static int r7_launch(const Rwkv7Args& a, void* ws) {
     const E *q = (const E*)a.q, *w = (const E*)a.w, *aa = (const E*)a.a, *kw = (const E*)a.kw, *u = (const E*)a.u;
     const float* c = a.c;
     void* args[] = {&q, &w, &aa, &c, &kw, &u, &wsf, &T, &DV};
-    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kR7Threads), args, lds, st) != hipSuccess)
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kR7IntraThreads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   {
