@@ -18,9 +18,12 @@
 //   O   = Q_pi S0 - M_a E + M_z U,
 //   S_C = Diag(pi_C) S0 - A~^T E + Z~^T U   (A~_s, Z~_s = e^{Lambda_C - Lambda_s} a_s, kw_s).
 // The intra kernel does every chunk independently and writes G, E0, M_a,
-// Q_pi, A~^T, pi_C, O_z = M_z U and W_z = Z~^T U (fp32); the scan walks the
-// chunks of each head: E = E0 + G S0, O = Q_pi S0 - M_a E + O_z,
-// S = Diag(pi_C) S0 - A~^T E + W_z, on the fp32 matrix cores.
+// Q_pi, A~^T, pi_C, O_z = M_z U and Z~^T (fp32); the scan walks the chunks of
+// each head: E = E0 + G S0, O = Q_pi S0 - M_a E + O_z,
+// S = Diag(pi_C) S0 - A~^T E + Z~^T U (U read from the input), on the fp32
+// matrix cores. Keeping Z~^T (d_k x C) in the record instead of the product
+// Z~^T U (d_k x d_v) makes the record a third smaller and moves that product
+// from the intra kernel to the scan, where it costs no extra load time.
 #include "gdr_device.hpp"
 #include "gdr_internal.h"
 #include "gdr_host.hpp"
@@ -35,7 +38,7 @@ constexpr int kR7IntraWaves = kR7IntraThreads / 64;
 
 // Record of one (b, h, chunk), fp32 element offsets.
 struct R7Layout {
-  int g, e0, ma, qp, at, pic, oz, wz, floats;
+  int g, e0, ma, qp, at, pic, oz, zt, floats;
 };
 __host__ __device__ inline R7Layout r7_layout(int dk, int dv, int C) {
   R7Layout r;
@@ -46,8 +49,8 @@ __host__ __device__ inline R7Layout r7_layout(int dk, int dv, int C) {
   r.at = r.qp + C * dk;       // A~^T  [j][s]  dk x C
   r.pic = r.at + dk * C;      // pi_C  [j]     dk
   r.oz = r.pic + dk;          // O_z   [t][v]  C x dv
-  r.wz = r.oz + C * dv;       // W_z   [j][v]  dk x dv
-  r.floats = (r.wz + dk * dv + 3) / 4 * 4;
+  r.zt = r.oz + C * dv;       // Z~^T  [j][s]  dk x C
+  r.floats = (r.zt + dk * C + 3) / 4 * 4;
   return r;
 }
 
@@ -68,8 +71,8 @@ size_t rwkv7_ws_bytes(int B, int H, int T, int dk, int dv, int chunk) {
 // and likewise with kw_s. The left factors are <= 1; the right ones are <= 1
 // for s <= p and at most 1 / (the block's decay) inside the block, so a block
 // in which some channel decays below 2^-60 takes exact pairwise factors for
-// its diagonal tile instead. The products with U (L_z U, M_z U, Z~^T U) are
-// MFMA tiles too; the unit lower-triangular solve runs one column per thread.
+// its diagonal tile instead. The products with U (L_z U, M_z U) are MFMA
+// tiles too; the unit lower-triangular solve runs one column per thread.
 template <typename E, int DK, int CM>
 __global__ __launch_bounds__(kR7IntraThreads) void rwkv7_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ w, const E* __restrict__ a, const float* __restrict__ c,
@@ -95,7 +98,6 @@ __global__ __launch_bounds__(kR7IntraThreads) void rwkv7_intra_kernel(
   const int NX = DV + DK + 4;
   float* UT = TMP;                      // u^T  [v][s]
   float* Xl = UT + DV * PC;             // [L_z U | Y_pi'] -> [E0 | G]  [t][col]
-  float* ZT = Xl + CM * NX;             // Z~^T [j][s] = e^{Lambda_C - Lambda_s} kw_s
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nch = (T + CM - 1) / CM;
   const int bh = blockIdx.x / nch, ch = blockIdx.x % nch, t0 = ch * CM;
@@ -229,39 +231,30 @@ __global__ __launch_bounds__(kR7IntraThreads) void rwkv7_intra_kernel(
     const int t = x / DK, j = x % DK;
     const float lt1 = t > 0 ? Lam[(t - 1) * P + j] : 0.f;
     Xl[t * NX + DV + j] = cv[t] * Al[t * P + j] * __expf(lt1);                 // Y_pi'
-    ZT[j * PC + t] = __expf(Lam[(CM - 1) * P + j] - Lam[t * P + j]) * Zl[t * P + j];
     rec[RL.qp + t * DK + j] = __expf(Lam[t * P + j]) * Ql[t * P + j];
   }
-  GDR_STAGE_FOR(x, DK * CM, kR7IntraThreads) {              // A~^T, rows j: consecutive threads store consecutive s
+  GDR_STAGE_FOR(x, DK * CM, kR7IntraThreads) {   // A~^T, Z~^T, rows j: consecutive threads store consecutive s
     const int j = x / CM, s2 = x % CM;
-    rec[RL.at + j * CM + s2] = __expf(Lam[(CM - 1) * P + j] - Lam[s2 * P + j]) * Al[s2 * P + j];
+    const float e = __expf(Lam[(CM - 1) * P + j] - Lam[s2 * P + j]);
+    rec[RL.at + j * CM + s2] = e * Al[s2 * P + j];
+    rec[RL.zt + j * CM + s2] = e * Zl[s2 * P + j];
   }
   GDR_STAGE_FOR(j, DK, kR7IntraThreads) rec[RL.pic + j] = __expf(Lam[(CM - 1) * P + j]);
   GDR_STAGE_FOR(x, CM * CM, kR7IntraThreads) rec[RL.ma + x] = Ma[(x / CM) * PC + x % CM];
   __syncthreads();
-  // L_z U into the right-hand side; O_z = M_z U and W_z = Z~^T U to the record
+  // L_z U into the right-hand side; O_z = M_z U to the record
   {
     constexpr int NT = CM / 16;
     const int NV = DV / 16;
-    for (int tile = wid; tile < 2 * NT * NV + (DK / 16) * NV; tile += kR7IntraWaves) {
+    for (int tile = wid; tile < 2 * NT * NV; tile += kR7IntraWaves) {
       f32x4 acc = f4zero();
-      if (tile < 2 * NT * NV) {
-        const int which = tile / (NT * NV), r = tile % (NT * NV), it = r / NV, vt = r % NV;
-        tile_nt(acc, which == 0 ? Lz : Mz, PC, 16 * it, UT, PC, 16 * vt, CM, lane);
+      const int which = tile / (NT * NV), r = tile % (NT * NV), it = r / NV, vt = r % NV;
+      tile_nt(acc, which == 0 ? Lz : Mz, PC, 16 * it, UT, PC, 16 * vt, CM, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * it + 4 * (lane >> 4) + e, v = 16 * vt + (lane & 15);
-          if (which == 0) Xl[t * NX + v] = acc[e];
-          else rec[RL.oz + t * DV + v] = acc[e];
-        }
-      } else {
-        const int r = tile - 2 * NT * NV, jt = r / NV, vt = r % NV;
-        tile_nt(acc, ZT, PC, 16 * jt, UT, PC, 16 * vt, CM, lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * jt + 4 * (lane >> 4) + e, v = 16 * vt + (lane & 15);
-          rec[RL.wz + j * DV + v] = acc[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * it + 4 * (lane >> 4) + e, v = 16 * vt + (lane & 15);
+        if (which == 0) Xl[t * NX + v] = acc[e];
+        else rec[RL.oz + t * DV + v] = acc[e];
       }
     }
   }
@@ -301,19 +294,22 @@ __global__ __launch_bounds__(kR7IntraThreads) void rwkv7_intra_kernel(
 
 // ------------------------------------------------------------------ chunk scan
 // Per (b, h, VT value columns) (VT = 32, or 16 for d_v = 16), walking the
-// chunks: E = E0 + G S0, O = Q_pi S0 - M_a E + O_z, S = Diag(pi_C) S0 - A~^T E
-// + W_z on the fp32 matrix cores. The next chunk's record slices load into
-// registers while the current chunk is worked on.
+// chunks: E = E0 + G S0, O = Q_pi S0 - M_a E + O_z,
+// S = Diag(pi_C) S0 - A~^T E + Z~^T U on the fp32 matrix cores, with the
+// chunk's U slice read from the input u. The next chunk's record slices and
+// U load into registers while the current chunk is worked on.
 template <typename E, int DK, int CM, int VT>
 __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __restrict__ ws,
+                                                                 const E* __restrict__ u,
                                                                  const float* __restrict__ S0, E* __restrict__ o,
                                                                  float* __restrict__ S_out, int T, int DV) {
   constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NT = CM / 16, NHV = VT / 16;
   constexpr int NTH = kR7Threads;
-  // f32x4 pieces of each slice and the loads per thread
-  constexpr int QA = CM * DK / 4, QM = CM * CM / 4, QT = DK * CM / 4, QE = CM * VT / 4, QW = DK * VT / 4;
+  // f32x4 pieces of each slice (4-element pieces of U) and the loads per thread
+  constexpr int QA = CM * DK / 4, QM = CM * CM / 4, QT = DK * CM / 4, QE = CM * VT / 4, QU = CM * VT / 4;
   constexpr int NA = (QA + NTH - 1) / NTH, NM = (QM + NTH - 1) / NTH, NAT = (QT + NTH - 1) / NTH,
-                NE = (QE + NTH - 1) / NTH, NW = (QW + NTH - 1) / NTH;
+                NE = (QE + NTH - 1) / NTH, NU = (QU + NTH - 1) / NTH;
+  using RW = Raw<E>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* Gl = (float*)smem;             // G     [t][j]
   float* Qpl = Gl + CM * LY;            // Q_pi  [t][j]
@@ -323,8 +319,9 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
   float* ETl = STl + VT * LY;           // E^T   [v][s]
   float* E0l = ETl + VT * LC;           // E0    [t][v]
   float* OZl = E0l + CM * VT;           // O_z   [t][v]
-  float* WZl = OZl + CM * VT;           // W_z   [j][v]
-  float* PIl = WZl + DK * VT;           // pi_C  [j]
+  float* ZTl = OZl + CM * VT;           // Z~^T  [j][s]
+  float* UTl = ZTl + DK * LC;           // U^T   [v][s]
+  float* PIl = UTl + VT * LC;           // pi_C  [j]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, vl = lane & 15;
   const int nvt = DV / VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * VT;
   const int nch = (T + CM - 1) / CM;
@@ -341,7 +338,8 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
         S[i][hv][e] = (J < NST && S0) ? S0[((size_t)bh * DK + row) * DV + v0 + 16 * hv + vl] : 0.f;
       }
   }
-  f32x4 pg[NA], pq[NA], pm[NM], pa[NAT], pe[NE], po[NE], pw[NW];
+  f32x4 pg[NA], pq[NA], pm[NM], pa[NAT], pz[NAT], pe[NE], po[NE];
+  typename RW::R4 pu[NU];
   float pp = 0.f;
   auto fetch = [&](int c) {
     const float* rec = ws + ((size_t)bh * nch + c) * RL.floats;
@@ -362,7 +360,10 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
 #pragma unroll
     for (int i = 0; i < NAT; ++i) {
       const int x = tid + NTH * i;
-      if (QT % NTH == 0 || x < QT) pa[i] = *(const f32x4*)&rec[RL.at + 4 * x];
+      if (QT % NTH == 0 || x < QT) {
+        pa[i] = *(const f32x4*)&rec[RL.at + 4 * x];
+        pz[i] = *(const f32x4*)&rec[RL.zt + 4 * x];
+      }
     }
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
@@ -373,17 +374,20 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
         po[i] = *(const f32x4*)&rec[RL.oz + t * DV + v0 + q0];
       }
     }
+    // U: consecutive threads take consecutive rows t (the transposed LDS
+    // writes in stage then hit distinct banks); rows past T are clamped
+    // here and zeroed in stage
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
+    for (int i = 0; i < NU; ++i) {
       const int x = tid + NTH * i;
-      if (QW % NTH == 0 || x < QW) {
-        const int jr = x / (VT / 4), q0 = 4 * (x % (VT / 4));
-        pw[i] = *(const f32x4*)&rec[RL.wz + jr * DV + v0 + q0];
+      if (QU % NTH == 0 || x < QU) {
+        const int t = x % CM, q0 = 4 * (x / CM);
+        pu[i] = RW::ld4(u + ((size_t)bh * T + row_in(c * CM + t, T)) * DV + v0 + q0);
       }
     }
     if (tid < DK) pp = rec[RL.pic + tid];
   };
-  auto stage = [&]() {
+  auto stage = [&](int c) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int x = tid + NTH * i;
@@ -401,7 +405,10 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
 #pragma unroll
     for (int i = 0; i < NAT; ++i) {
       const int x = tid + NTH * i;
-      if (QT % NTH == 0 || x < QT) *(f32x4*)&ATl[(x / (CM / 4)) * LC + 4 * (x % (CM / 4))] = pa[i];
+      if (QT % NTH == 0 || x < QT) {
+        *(f32x4*)&ATl[(x / (CM / 4)) * LC + 4 * (x % (CM / 4))] = pa[i];
+        *(f32x4*)&ZTl[(x / (CM / 4)) * LC + 4 * (x % (CM / 4))] = pz[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
@@ -412,9 +419,15 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
       }
     }
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
+    for (int i = 0; i < NU; ++i) {
       const int x = tid + NTH * i;
-      if (QW % NTH == 0 || x < QW) *(f32x4*)&WZl[4 * x] = pw[i];
+      if (QU % NTH == 0 || x < QU) {
+        const int t = x % CM, q0 = 4 * (x / CM);
+        const bool ok = c * CM + t < T;
+        const f32x4 uu = RW::un4(pu[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) UTl[(q0 + e) * LC + t] = ok ? uu[e] : 0.f;
+      }
     }
     if (tid < DK) PIl[tid] = pp;
   };
@@ -430,7 +443,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
           for (int e = 0; e < 4; ++e) STl[(16 * hv + vl) * LY + 16 * J + 4 * (lane >> 4) + e] = S[i][hv][e];
       }
     }
-    stage();
+    stage(c);
     if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
     // E = E0 + G S0 (to LDS, transposed); the readout's Q_pi S0 kept in registers
@@ -470,19 +483,20 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
         }
       }
     }
-    // S <- Diag(pi_C) S - A~^T E + W_z
+    // S <- Diag(pi_C) S - A~^T E + Z~^T U
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int J = wid + 4 * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv) {
-          f32x4 ae = f4zero();
+          f32x4 ae = f4zero(), zu = f4zero();
           tile_nt(ae, ATl, LC, 16 * J, ETl, LC, 16 * hv, CM, lane);
+          tile_nt(zu, ZTl, LC, 16 * J, UTl, LC, 16 * hv, CM, lane);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * J + 4 * (lane >> 4) + e;
-            S[i][hv][e] = PIl[row] * S[i][hv][e] - ae[e] + WZl[row * VT + 16 * hv + vl];
+            S[i][hv][e] = PIl[row] * S[i][hv][e] - ae[e] + zu[e];
           }
         }
       }
@@ -612,7 +626,7 @@ static int r7_launch(const Rwkv7Args& a, void* ws) {
   float* wsf = (float*)ws;
   {
     const int P = DK + 4, PC = CM + 4, NX = DV + DK + 4;
-    const int tg = (2 * 16 + 2 * CM) * P, tr = DV * PC + CM * NX + DK * PC;
+    const int tg = (2 * 16 + 2 * CM) * P, tr = DV * PC + CM * NX;
     const int lds = 4 * (4 * CM * P + CM + 4 * CM * PC + (tg > tr ? tg : tr));
     auto kern = rwkv7_intra_kernel<E, DK, CM>;
     if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
@@ -626,15 +640,16 @@ static int r7_launch(const Rwkv7Args& a, void* ws) {
     // 32-column value tiles where d_v allows, else 16
     constexpr int LY = DK + 4, LC = CM + 4;
     const int vt = a.dv % 32 == 0 ? 32 : 16;
-    const int lds = 4 * (2 * CM * LY + CM * LC + DK * LC + vt * LY + vt * LC + 2 * CM * vt + DK * vt + DK);
+    const int lds = 4 * (2 * CM * LY + CM * LC + DK * LC + vt * LY + vt * LC + 2 * CM * vt + DK * LC + vt * LC + DK);
     const void* kern = vt == 32 ? (const void*)rwkv7_scan_kernel<E, DK, CM, 32>
                                 : (const void*)rwkv7_scan_kernel<E, DK, CM, 16>;
     if (!allow_lds(kern, lds)) return GDR_ERR_LAUNCH;
     const float* wsc = wsf;
+    const E* u = (const E*)a.u;
     const float* S0 = a.S0;
     E* o = (E*)a.o;
     float* So = a.S_out;
-    void* args[] = {&wsc, &S0, &o, &So, &T, &DV};
+    void* args[] = {&wsc, &u, &S0, &o, &So, &T, &DV};
     if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kR7Threads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
