@@ -32,7 +32,8 @@ namespace gdr {
 
 namespace {
 
-constexpr int kR7Threads = 256;        // scan
+constexpr int kR7ScanThreads = 512;    // scan: eight waves, two per SIMD
+constexpr int kR7ScanWaves = kR7ScanThreads / 64;
 constexpr int kR7IntraThreads = 512;   // intra: eight waves, two per SIMD
 constexpr int kR7IntraWaves = kR7IntraThreads / 64;
 
@@ -299,12 +300,13 @@ __global__ __launch_bounds__(kR7IntraThreads) void rwkv7_intra_kernel(
 // chunk's U slice read from the input u. The next chunk's record slices and
 // U load into registers while the current chunk is worked on.
 template <typename E, int DK, int CM, int VT>
-__global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __restrict__ ws,
+__global__ __launch_bounds__(kR7ScanThreads) void rwkv7_scan_kernel(const float* __restrict__ ws,
                                                                  const E* __restrict__ u,
                                                                  const float* __restrict__ S0, E* __restrict__ o,
                                                                  float* __restrict__ S_out, int T, int DV) {
-  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NT = CM / 16, NHV = VT / 16;
-  constexpr int NTH = kR7Threads;
+  constexpr int NW8 = kR7ScanWaves;
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + NW8 - 1) / NW8, NT = CM / 16, NHV = VT / 16;
+  constexpr int NTH = kR7ScanThreads;
   // f32x4 pieces of each slice (4-element pieces of U) and the loads per thread
   constexpr int QA = CM * DK / 4, QM = CM * CM / 4, QT = DK * CM / 4, QE = CM * VT / 4, QU = CM * VT / 4;
   constexpr int NA = (QA + NTH - 1) / NTH, NM = (QM + NTH - 1) / NTH, NAT = (QT + NTH - 1) / NTH,
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
   f32x4 S[PER][NHV];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int J = wid + 4 * i;
+    const int J = wid + NW8 * i;
 #pragma unroll
     for (int hv = 0; hv < NHV; ++hv)
 #pragma unroll
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
   for (int c = 0; c < nch; ++c) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int J = wid + 4 * i;
+      const int J = wid + NW8 * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv)
@@ -446,32 +448,37 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
     stage(c);
     if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
-    // E = E0 + G S0 (to LDS, transposed); the readout's Q_pi S0 kept in registers
-    constexpr int NP = NT * NHV, PP = (NP + 3) / 4;
-    f32x4 oacc[PP];
+    // Jobs 0 .. NP-1: E = E0 + G S0 for output tile p (to LDS, transposed);
+    // jobs NP .. 2NP-1: the readout's Q_pi S0 for tile p, kept in the
+    // registers of the wave that then finishes that tile of O
+    constexpr int NP = NT * NHV, NJOB = 2 * NP, PJ = (NJOB + NW8 - 1) / NW8;
+    f32x4 oacc[PJ];
 #pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int p = wid + 4 * i;
+    for (int i = 0; i < PJ; ++i) {
+      const int job = wid + NW8 * i;
       oacc[i] = f4zero();
-      if (p < NP) {
-        const int it = p / NHV, hv = p % NHV;
-        f32x4 acc = f4zero();
-        tile_nt(acc, Gl, LY, 16 * it, STl, LY, 16 * hv, DK, lane);
-        tile_nt(oacc[i], Qpl, LY, 16 * it, STl, LY, 16 * hv, DK, lane);
+      if (job < NJOB) {
+        const int p = job % NP, it = p / NHV, hv = p % NHV;
+        if (job < NP) {
+          f32x4 acc = f4zero();
+          tile_nt(acc, Gl, LY, 16 * it, STl, LY, 16 * hv, DK, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * it + 4 * (lane >> 4) + e;
-          ETl[(16 * hv + vl) * LC + t] = E0l[t * VT + 16 * hv + vl] + acc[e];
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * it + 4 * (lane >> 4) + e;
+            ETl[(16 * hv + vl) * LC + t] = E0l[t * VT + 16 * hv + vl] + acc[e];
+          }
+        } else {
+          tile_nt(oacc[i], Qpl, LY, 16 * it, STl, LY, 16 * hv, DK, lane);
         }
       }
     }
     __syncthreads();
     // O = Q_pi S0 - M_a E + O_z
 #pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int p = wid + 4 * i;
-      if (p < NP) {
-        const int it = p / NHV, hv = p % NHV;
+    for (int i = 0; i < PJ; ++i) {
+      const int job = wid + NW8 * i;
+      if (job >= NP && job < NJOB) {
+        const int p = job - NP, it = p / NHV, hv = p % NHV;
         f32x4 me = f4zero();
         tile_nt(me, Mal, LC, 16 * it, ETl, LC, 16 * hv, CM, lane);
 #pragma unroll
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
     // S <- Diag(pi_C) S - A~^T E + Z~^T U
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int J = wid + 4 * i;
+      const int J = wid + NW8 * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv) {
@@ -506,7 +513,7 @@ __global__ __launch_bounds__(kR7Threads) void rwkv7_scan_kernel(const float* __r
   if (S_out) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int J = wid + 4 * i;
+      const int J = wid + NW8 * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv)
@@ -650,7 +657,7 @@ static int r7_launch(const Rwkv7Args& a, void* ws) {
     E* o = (E*)a.o;
     float* So = a.S_out;
     void* args[] = {&wsc, &u, &S0, &o, &So, &T, &DV};
-    if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kR7Threads), args, lds, st) != hipSuccess)
+    if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kR7ScanThreads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   return GDR_OK;
