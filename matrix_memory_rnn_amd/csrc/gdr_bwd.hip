@@ -583,10 +583,10 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
     const E* __restrict__ k, const E* __restrict__ alpha, const E* __restrict__ bgate, const E* __restrict__ v,
     const E* __restrict__ wgate, const char* __restrict__ ws, float* __restrict__ dZ, float* __restrict__ dL,
     float* __restrict__ dv_out, float* __restrict__ dw_out, int T, int DV) {
-  constexpr int LP = DK + 1, LL = CM + 1;
+  constexpr int LP = DK + 1, LTP = CM + 4;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* Ll = (float*)smem;               // L [t][s]
-  float* U0 = Ll + a256(CM * LL * 4) / 4; // union: phase 1 (Lam, Kl, KHl) / phase 2 (Xl, Zl)
+  float* LT = (float*)smem;               // L^T [s][t] (row t of L^T is column t of L)
+  float* U0 = LT + a256(CM * LTP * 4) / 4; // union: phase 1 (Lam, Kl, KHl) / phase 2 (Xl, Zl)
   float* Lam = U0;                        // Lambda [t][j] (pitch LP)
   float* Kl = Lam + CM * LP;              // k      [t][j]
   float* KHl = Kl + CM * LP;              // b * k  [t][j]
@@ -600,15 +600,39 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
   const size_t sK = (size_t)bh * T * DK, sV = (size_t)bh * T * DV;
   __shared__ int sflag[4];
   if (tid < 4) sflag[tid] = 0;
-  GDR_STAGE_FOR(x, CM * DK, kBwdThreads) {
-    const int t = x / DK, j = x % DK;
-    const bool ok = t0 + t < T;
-    const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j;
-    const float a0 = (float)alpha[off], k0 = (float)k[off], b0 = (float)bgate[off];
-    const float a = ok ? a0 : 1.f, kk = ok ? k0 : 0.f, bb = ok ? b0 : 0.f;
-    Lam[t * LP + j] = logf(a);
-    Kl[t * LP + j] = kk;
-    KHl[t * LP + j] = bb * kk;
+  // alpha, k, b in 16-byte pieces (8 channels of one row), all issued before
+  // the first is used; rows past T become alpha = 1, k = b = 0
+  using RW = Raw<E>;
+  constexpr int NPC = CM * DK / 8, NPI = (NPC + kBwdThreads - 1) / kBwdThreads;
+  {
+    typename RW::R8 ra[NPI], rk[NPI], rb[NPI];
+#pragma unroll
+    for (int i = 0; i < NPI; ++i) {
+      const int x = tid + kBwdThreads * i, t = x < NPC ? x / (DK / 8) : 0, j0 = 8 * (x % (DK / 8));
+      const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j0;
+      ra[i] = RW::ld8(alpha + off);
+      rk[i] = RW::ld8(k + off);
+      rb[i] = RW::ld8(bgate + off);
+    }
+#pragma unroll
+    for (int i = 0; i < NPI; ++i) {
+      const int x = tid + kBwdThreads * i;
+      if (NPC % kBwdThreads == 0 || x < NPC) {
+        const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
+        const bool ok = t0 + t < T;
+        float fa[8], fk[8], fb[8];
+        RW::un8(ra[i], fa);
+        RW::un8(rk[i], fk);
+        RW::un8(rb[i], fb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kk = ok ? fk[e] : 0.f;
+          Lam[t * LP + j0 + e] = ok ? logf(fa[e]) : 0.f;
+          Kl[t * LP + j0 + e] = kk;
+          KHl[t * LP + j0 + e] = ok ? fb[e] * kk : 0.f;
+        }
+      }
+    }
   }
   __syncthreads();
   GDR_STAGE_FOR(j, DK, kBwdThreads) {   // Lambda_t = sum_{r <= t} log alpha_r
@@ -642,6 +666,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
       const int J = tile - I * (I + 1) / 2, p = 16 * I - 1;
       const int ta = 16 * I + m16, sb = 16 * J + m16;
       f32x4 acc = f4zero();
+#pragma unroll 8
       for (int j0 = 0; j0 < DK; j0 += 4) {
         const int j = j0 + k4;
         const float lp = I > 0 ? Lam[p * LP + j] : 0.f;
@@ -660,12 +685,28 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
             for (int j = 0; j < DK; ++j)
               val += KHl[t * LP + j] * Kl[s2 * LP + j] * __expf(Lam[t * LP + j] - Lam[s2 * LP + j]);
         }
-        Ll[t * LL + s2] = s2 < t ? val : 0.f;
+        LT[s2 * LTP + t] = s2 < t ? val : 0.f;
       }
     }
   }
   __syncthreads();
-  // T^T X = dZ column by column: x_t = dz_t - sum_{s > t} L[s][t] x_s (rows from the last)
+  // w and v of the chunk in 16-byte pieces (8 value columns of one row) for
+  // dv and dw below, issued now so they arrive during the solve
+  constexpr int NWP = CM * 128 / 8 / kBwdThreads;   // pieces per thread at d_v = 128
+  const int nwp = CM * DV / 8;
+  typename RW::R8 rwp[NWP], rvp[NWP];
+#pragma unroll
+  for (int i = 0; i < NWP; ++i) {
+    const int x = tid + kBwdThreads * i, t = x < nwp ? x / (DV / 8) : 0, v0 = x < nwp ? 8 * (x % (DV / 8)) : 0;
+    const size_t off = sV + (size_t)row_in(t0 + t, T) * DV + v0;
+    rwp[i] = RW::ld8(wgate + off);
+    rvp[i] = RW::ld8(v + off);
+  }
+  // T^T X = dZ column by column: x_t = dz_t - sum_{s > t} L[s][t] x_s (rows
+  // from the last). Row t of L^T is read as 16-byte pieces when step t comes
+  // up; the scheduling barrier keeps the compiler from hoisting every row's
+  // loads to the top (hundreds of registers). Two partial sums halve the
+  // dependent chain of a step.
   float* dZc = dZ + item * CM * (DV + DK);
   const int col = tid;
   if (col < DV + DK) {
@@ -674,10 +715,19 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
     for (int t = 0; t < CM; ++t) x[t] = dZc[(size_t)t * (DV + DK) + col];
 #pragma unroll
     for (int t = CM - 1; t >= 0; --t) {
-      float acc = x[t];
+      float acc0 = x[t], acc1 = 0.f;
 #pragma unroll
-      for (int s = t + 1; s < CM; ++s) acc -= Ll[s * LL + t] * x[s];
-      x[t] = acc;
+      for (int s4 = (t + 1) & ~3; s4 < CM; s4 += 4) {
+        const f32x4 l4 = *(const f32x4*)&LT[t * LTP + s4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s4 + e > t) {
+            if (e & 1) acc1 -= l4[e] * x[s4 + e];
+            else acc0 -= l4[e] * x[s4 + e];
+          }
+      }
+      x[t] = acc0 + acc1;
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the phase-1 area is dead once every thread has passed the L products
     // above (the barrier before the solve); X goes there
@@ -685,23 +735,6 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
     for (int t = 0; t < CM; ++t) {
       Xl[t * NX + col] = x[t];
       dZc[(size_t)t * (DV + DK) + col] = x[t];
-    }
-    if (col < DV) {   // dV^: dv = dV^ * w, dw = dV^ * v
-      float wv[CM], vv[CM];
-#pragma unroll
-      for (int t = 0; t < CM; ++t) {
-        const size_t off = sV + (size_t)row_in(t0 + t, T) * DV + col;
-        wv[t] = (float)wgate[off];
-        vv[t] = (float)v[off];
-      }
-#pragma unroll
-      for (int t = 0; t < CM; ++t) {
-        if (t0 + t < T) {
-          const size_t off = sV + (size_t)(t0 + t) * DV + col;
-          dv_out[off] = x[t] * wv[t];
-          dw_out[off] = x[t] * vv[t];
-        }
-      }
     }
   }
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
@@ -721,6 +754,26 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
     *(f32x4*)&Zl[sr * NX + DV + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
   }
   __syncthreads();
+  // dV^ = the first d_v columns of X: dv = dV^ * w, dw = dV^ * v, 8 value
+  // columns of one row per piece
+#pragma unroll
+  for (int i = 0; i < NWP; ++i) {
+    const int x = tid + kBwdThreads * i;
+    if (x < nwp) {
+      const int t = x / (DV / 8), v0 = 8 * (x % (DV / 8));
+      if (t0 + t < T) {
+        float fw[8], fv[8];
+        RW::un8(rwp[i], fw);
+        RW::un8(rvp[i], fv);
+        const f32x4 x0 = *(const f32x4*)&Xl[t * NX + v0], x1 = *(const f32x4*)&Xl[t * NX + v0 + 4];
+        const size_t off = sV + (size_t)(t0 + t) * DV + v0;
+        *(f32x4*)&dv_out[off] = f32x4{x0[0] * fw[0], x0[1] * fw[1], x0[2] * fw[2], x0[3] * fw[3]};
+        *(f32x4*)&dv_out[off + 4] = f32x4{x1[0] * fw[4], x1[1] * fw[5], x1[2] * fw[6], x1[3] * fw[7]};
+        *(f32x4*)&dw_out[off] = f32x4{x0[0] * fv[0], x0[1] * fv[1], x0[2] * fv[2], x0[3] * fv[3]};
+        *(f32x4*)&dw_out[off + 4] = f32x4{x1[0] * fv[4], x1[1] * fv[5], x1[2] * fv[6], x1[3] * fv[7]};
+      }
+    }
+  }
   // dL = -stril(X Z^T)
   float* dLc = dL + item * CM * CM;
   constexpr int NT = CM / 16;
@@ -1083,7 +1136,7 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
   }
   {
     const int p1 = 3 * CM * (DK + 1), p2 = 2 * CM * (DV + DK + 4);
-    const int lds = (int)a256(CM * (CM + 1) * 4) + 4 * (p1 > p2 ? p1 : p2);
+    const int lds = (int)a256(CM * (CM + 4) * 4) + 4 * (p1 > p2 ? p1 : p2);
     auto kern = gdn2_bwd_solve_kernel<E, DK, CM, FM>;
     if (!allow_lds((const void*)kern, lds)) return GDR_ERR_LAUNCH;
     const E *k = (const E*)a.k, *al = (const E*)a.alpha, *bg = (const E*)a.b, *v = (const E*)a.v,
