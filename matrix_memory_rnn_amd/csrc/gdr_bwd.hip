@@ -853,10 +853,64 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
   const float* dKc = dKt + item * CM * DK;
   const int B0 = 16 * wid;                          // this wave's block
   const int cj = tid % NCH, sg = tid / NCH, r0 = sg * Sh::RPS;
-  // everything a lane reads from memory after the products starts loading
-  // now, so that no load latency sits between the phases: the direct terms of
-  // its output entries (rows B0 + 4 k4 + e, channels 16 n + m16), their erase
-  // gates, the decays of its row segment, dpi_C
+  __shared__ int dflag[4];
+  if (tid < 4) dflag[tid] = 0;
+  // alpha, k, b, q of the chunk's rows and channels in 16-byte pieces (8
+  // channels of one row; rows past T become alpha = 1, k = b = q = 0), and
+  // the chunk's dL and dM rows, all issued before the first is used
+  using RW = Raw<E>;
+  constexpr int NPC = CM * NCH / 8;
+  static_assert(NPC <= kDecayThreads, "decay kernel: one input piece per thread");
+  {
+    const int pt = tid < NPC ? tid / (NCH / 8) : 0, pj = 8 * (tid % (NCH / 8));
+    const size_t off = sK + (size_t)row_in(t0 + pt, T) * DK + j0 + pj;
+    const typename RW::R8 ra = RW::ld8(alpha + off), rk = RW::ld8(k + off), rb = RW::ld8(bgate + off),
+                          rq = RW::ld8(q + off);
+    const float* dLc = dLb + item * CM * CM;
+    const float* dMc = dMb + item * CM * CM;
+    constexpr int QL = CM * CM / 4, NL = (QL + kDecayThreads - 1) / kDecayThreads;
+    f32x4 l4[NL], m4[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int x = tid + kDecayThreads * i, xc = x < QL ? x : 0;
+      const int t = xc / (CM / 4), s4 = 4 * (xc % (CM / 4));
+      l4[i] = *(const f32x4*)(dLc + t * CM + s4);
+      m4[i] = *(const f32x4*)(dMc + t * CM + s4);
+    }
+    if (tid < NPC) {
+      const bool ok = t0 + pt < T;
+      float fa[8], fk[8], fb[8], fq[8];
+      RW::un8(ra, fa);
+      RW::un8(rk, fk);
+      RW::un8(rb, fb);
+      RW::un8(rq, fq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kk = ok ? fk[e] : 0.f;
+        Lam[pt * LP + pj + e] = ok ? logf(fa[e]) : 0.f;
+        Kc[pt * LP + pj + e] = kk;
+        KHc[pt * LP + pj + e] = ok ? fb[e] * kk : 0.f;
+        Qc[pt * LP + pj + e] = ok ? fq[e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int x = tid + kDecayThreads * i, t = x / (CM / 4), s4 = 4 * (x % (CM / 4));
+      if (QL % kDecayThreads == 0 || x < QL) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dLs[t * LD + s4 + e] = l4[i][e];
+          dMs[t * LD + s4 + e] = m4[i][e];
+        }
+      }
+    }
+  }
+  // Everything a lane reads from memory after the products is issued now,
+  // after the loads above (so the wait before the first barrier does not
+  // include it) and long before it is used: the direct terms of its output
+  // entries (rows B0 + 4 k4 + e, channels 16 n + m16), their erase gates, the
+  // decays of its row segment, dpi_C.
+  __builtin_amdgcn_sched_barrier(0);
   float pdz[NJT][4], pdq[NJT][4], pdk[NJT][4], pbg[NJT][4], pal[Sh::RPS], pdp = 0.f;
 #pragma unroll
   for (int n = 0; n < NJT; ++n)
@@ -873,31 +927,6 @@ __global__ __launch_bounds__(kDecayThreads, 2) void gdn2_bwd_decay_kernel(
   for (int i = 0; i < Sh::RPS; ++i)
     pal[i] = (float)alpha[sK + (size_t)row_in(t0 + r0 + i, T) * DK + j0 + cj];
   if (tid < NCH) pdp = dpic[item * DK + j0 + tid];
-  __shared__ int dflag[4];
-  if (tid < 4) dflag[tid] = 0;
-  GDR_STAGE_FOR(x, CM * NCH, kDecayThreads) {
-    const int t = x / NCH, jl = x % NCH;
-    const bool ok = t0 + t < T;
-    const size_t off = sK + (size_t)row_in(t0 + t, T) * DK + j0 + jl;
-    const float a0 = (float)alpha[off], k0 = (float)k[off], b0 = (float)bgate[off], q0 = (float)q[off];
-    const float a = ok ? a0 : 1.f, kk = ok ? k0 : 0.f;
-    const float bb = ok ? b0 : 0.f, qq = ok ? q0 : 0.f;
-    Lam[t * LP + jl] = logf(a);
-    Kc[t * LP + jl] = kk;
-    KHc[t * LP + jl] = bb * kk;
-    Qc[t * LP + jl] = qq;
-  }
-  const float* dLc = dLb + item * CM * CM;
-  const float* dMc = dMb + item * CM * CM;
-  GDR_STAGE_FOR(x, CM * CM / 4, kDecayThreads) {
-    const int t = x / (CM / 4), s4 = 4 * (x % (CM / 4));
-    const f32x4 l4 = *(const f32x4*)(dLc + t * CM + s4), m4 = *(const f32x4*)(dMc + t * CM + s4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dLs[t * LD + s4 + e] = l4[e];
-      dMs[t * LD + s4 + e] = m4[e];
-    }
-  }
   __syncthreads();
   // Lambda_t = sum_{r <= t} log alpha_r: row segments of RPS rows per thread,
   // their totals, then each segment from the sum of the ones before it
