@@ -49,6 +49,8 @@ namespace gdr {
 namespace {
 
 constexpr int kBwdThreads = 256;
+constexpr int kBwdChunkThreads = 512;   // bwd_chunk: eight waves, two per SIMD
+constexpr int kBwdChunkWaves = kBwdChunkThreads / 64;
 constexpr float kBwdExactLog = -13.86f;   // log 2^-20: in-block decays below it take exact factors
 constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel (tile_nt16 there)
 
@@ -408,13 +410,14 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
 
 // ------------------------------------------------------------------ per-chunk state-side gradients
 template <typename E, int DK, int CM, bool FM>
-__global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
+__global__ __launch_bounds__(kBwdChunkThreads) void gdn2_bwd_chunk_kernel(
     const char* __restrict__ ws, const float* __restrict__ Hs, const float* __restrict__ dHs,
     const E* __restrict__ dO, float* __restrict__ dZ, float* __restrict__ dQp, float* __restrict__ dKt,
     float* __restrict__ dMb, float* __restrict__ dpic, int T, int DV) {
   constexpr int LY = DK + 4, LC = CM + 4, L16 = kVT + 4;
   constexpr int NYT = (CM / 16) * (DK / 16), NMT = (CM / 16) * (CM / 16);
-  constexpr int PY = (NYT + 3) / 4, PM = (NMT + 3) / 4;
+  constexpr int NTH = kBwdChunkThreads, NWV = kBwdChunkWaves;
+  constexpr int PY = (NYT + NWV - 1) / NWV, PM = (NMT + NWV - 1) / NWV;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* Yl = (float*)smem;          // Y     [t][j]
   float* MTl = Yl + CM * LY;         // M^T   [s][t]
@@ -438,21 +441,21 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   const float* dHc = dHs + item * DK * DV;
   float* dZc = dZ + item * CM * (DV + DK);
   const int vl = lane & 15;
-  GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {
+  GDR_STAGE_FOR(x, CM * DK / 8, NTH) {
     const int t = x / (DK / 8), j0 = 8 * (x % (DK / 8));
     float o[8];
     R.y8(t, j0, o);
     *(f32x4*)&Yl[t * LY + j0] = f32x4{o[0], o[1], o[2], o[3]};
     *(f32x4*)&Yl[t * LY + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
   }
-  GDR_STAGE_FOR(x, CM * CM / 8, kBwdThreads) {
+  GDR_STAGE_FOR(x, CM * CM / 8, NTH) {
     const int t = x / (CM / 8), s0 = 8 * (x % (CM / 8));
     float o[8];
     R.m8(t, s0, o);
 #pragma unroll
     for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = o[e];
   }
-  GDR_STAGE_FOR(x, DK * CM / 8, kBwdThreads) {
+  GDR_STAGE_FOR(x, DK * CM / 8, NTH) {
     const int jr = x / (CM / 8), s0 = 8 * (x % (CM / 8));
     float o[8];
     R.kt8(jr, s0, o);
@@ -467,19 +470,22 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   float pacc = 0.f;
   // the state, state-gradient, dO and U slices of value tile v0 + kVT load
   // into registers while tile v0 is worked on
-  constexpr int NH = DK * kVT / kBwdThreads, NG = CM * kVT / kBwdThreads, NU = kVT * CM / 4;
-  static_assert(DK * kVT % kBwdThreads == 0 && CM * kVT % kBwdThreads == 0 && NU <= kBwdThreads, "bwd chunk tiles");
+  constexpr int QH = DK * kVT, QG = CM * kVT, NU = kVT * CM / 4;
+  constexpr int NH = (QH + NTH - 1) / NTH, NG = (QG + NTH - 1) / NTH;
+  static_assert(NU <= NTH, "bwd chunk tiles");
   float rh[NH], rd[NH], rg[NG], ru[4];
+  // loads are unconditional (indices clamped into range); the stores below
+  // skip the clamped ones
   auto fetch = [&](int v0) {
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int x = tid + i * kBwdThreads, j = x / kVT, v = x % kVT;
+      const int x = tid + i * NTH, xc = x < QH ? x : 0, j = xc / kVT, v = xc % kVT;
       rh[i] = Hc[(size_t)j * DV + v0 + v];
       rd[i] = dHc[(size_t)j * DV + v0 + v];
     }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int x = tid + i * kBwdThreads, t = x / kVT, v = x % kVT;
+      const int x = tid + i * NTH, xc = x < QG ? x : 0, t = xc / kVT, v = xc % kVT;
       const float g0 = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
       rg[i] = t0 + t < T ? g0 : 0.f;
     }
@@ -489,17 +495,21 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   for (int v0 = 0; v0 < DV; v0 += kVT) {
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int x = tid + i * kBwdThreads, j = x / kVT, v = x % kVT;
-      S0l[j * L16 + v] = rh[i];
-      S0Tl[v * LY + j] = rh[i];
-      dSl[j * L16 + v] = rd[i];
-      dSTl[v * LY + j] = rd[i];
+      const int x = tid + i * NTH, j = x / kVT, v = x % kVT;
+      if (QH % NTH == 0 || x < QH) {
+        S0l[j * L16 + v] = rh[i];
+        S0Tl[v * LY + j] = rh[i];
+        dSl[j * L16 + v] = rd[i];
+        dSTl[v * LY + j] = rd[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int x = tid + i * kBwdThreads, t = x / kVT, v = x % kVT;
-      dOl[t * L16 + v] = rg[i];
-      dOTl[v * LC + t] = rg[i];
+      const int x = tid + i * NTH, t = x / kVT, v = x % kVT;
+      if (QG % NTH == 0 || x < QG) {
+        dOl[t * L16 + v] = rg[i];
+        dOTl[v * LC + t] = rg[i];
+      }
     }
     if (tid < NU) {
       const int v = tid / (CM / 4), tq = 4 * (tid % (CM / 4));
@@ -508,7 +518,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
     }
     if (v0 + kVT < DV) fetch(v0 + kVT);
     __syncthreads();
-    for (int it = wid; it < CM / 16; it += 4) {
+    for (int it = wid; it < CM / 16; it += NWV) {
       f32x4 acc = f4zero();
       tile_nt(acc, Yl, LY, 16 * it, S0Tl, LY, 0, DK, lane);             // Y S0
       f32x4 dv = f4zero();
@@ -525,7 +535,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PY; ++i) {
-      const int p = wid + 4 * i;
+      const int p = wid + NWV * i;
       if (p < NYT) {
         const int ti = p / (DK / 16), tj = p % (DK / 16);
         tile_nt16(aY[i], dVl, L16, 16 * ti, S0l, L16, 16 * tj, lane);   // dV~ S0^T
@@ -535,7 +545,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
     }
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
-      const int p = wid + 4 * i;
+      const int p = wid + NWV * i;
       if (p < NMT) tile_nt16(aM[i], dOl, L16, 16 * (p / (CM / 16)), Vl, L16, 16 * (p % (CM / 16)), lane);
     }
     if (tid < DK) {
@@ -549,7 +559,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   float* dMc = dMb + item * CM * CM;
 #pragma unroll
   for (int i = 0; i < PY; ++i) {
-    const int p = wid + 4 * i;
+    const int p = wid + NWV * i;
     if (p < NYT) {
       const int ti = p / (DK / 16), tj = p % (DK / 16);
 #pragma unroll
@@ -563,7 +573,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_chunk_kernel(
   }
 #pragma unroll
   for (int i = 0; i < PM; ++i) {
-    const int p = wid + 4 * i;
+    const int p = wid + NWV * i;
     if (p < NMT) {
       const int ti = p / (CM / 16), si = p % (CM / 16);
 #pragma unroll
@@ -1160,7 +1170,7 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
     const E* dO = (const E*)a.dO;
     const float *Hc = Hs, *dHc = dHs;
     void* args[] = {&wsc, &Hc, &dHc, &dO, &dZ, &dQp, &dKt, &dM, &dpic, &T, &DV};
-    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+    if (hipLaunchKernel((const void*)kern, dim3(BH * nch), dim3(kBwdChunkThreads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   {
