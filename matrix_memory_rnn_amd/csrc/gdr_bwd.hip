@@ -49,7 +49,7 @@ namespace gdr {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kBwdChunkThreads = 512;   // bwd_chunk: eight waves, two per SIMD
+constexpr int kBwdChunkThreads = 512;   // bwd_chunk, bwd_dstates: eight waves, two per SIMD
 constexpr int kBwdChunkWaves = kBwdChunkThreads / 64;
 constexpr float kBwdExactLog = -13.86f;   // log 2^-20: in-block decays below it take exact factors
 constexpr int kVT = 16;           // value tile of the state passes and of the chunk kernel (tile_nt16 there)
@@ -107,6 +107,15 @@ struct Rec {
   }
   // U^T[v][t0 .. t0+3]
   __device__ void ut4(int v, int t0, float* o) const { run<4>(RL.ut, FM ? fu_off(v, t0, C) : v * C + t0, o); }
+  // the same rows of 8 as undecoded words, so a load can be issued well
+  // before its values are needed (decode with Raw<E>::un8; M's entries above
+  // the diagonal are not kept and must be masked by the caller)
+  using R8 = typename Raw<E>::R8;
+  __device__ R8 ld8(int base, int elem) const { return Raw<E>::ld8((const E*)(p + base) + elem); }
+  __device__ R8 y8r(int t, int j0) const { return ld8(RL.y, FM ? fm_off(t, j0, DK) : t * DK + j0); }
+  __device__ R8 qp8r(int t, int j0) const { return ld8(RL.qp, FM ? fm_off(t, j0, DK) : t * DK + j0); }
+  __device__ R8 kt8r(int j, int s0) const { return ld8(RL.kt, FM ? fm_off(j, s0, C) : j * C + s0); }
+  __device__ R8 m8r(int t, int s0) const { return ld8(RL.m, FM ? fm_off(t, s0, C) : t * C + s0); }
 };
 
 }  // namespace
@@ -232,12 +241,13 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_states_kernel(const char
 // chunks from the last: every chunk-end state gradient is stored, the last
 // one (the chunk-start gradient of chunk 0) is dS0.
 template <typename E, int DK, int CM, bool FM, int VT>
-__global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const char* __restrict__ ws,
-                                                                        const E* __restrict__ dO,
-                                                                        const float* __restrict__ dST,
-                                                                        float* __restrict__ dHs,
-                                                                        float* __restrict__ dS0, int T, int DV) {
-  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + 3) / 4, NHV = VT / 16;
+__global__ __launch_bounds__(kBwdChunkThreads) void gdn2_bwd_dstates_kernel(const char* __restrict__ ws,
+                                                                             const E* __restrict__ dO,
+                                                                             const float* __restrict__ dST,
+                                                                             float* __restrict__ dHs,
+                                                                             float* __restrict__ dS0, int T, int DV) {
+  constexpr int NTH = kBwdChunkThreads, NWV = kBwdChunkWaves;
+  constexpr int LY = DK + 4, LC = CM + 4, NST = DK / 16, PER = (NST + NWV - 1) / NWV, NHV = VT / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* MTl = (float*)smem;         // M^T    [s][t]
   float* Kl = MTl + CM * LC;         // K~     [s][j]
@@ -252,10 +262,11 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
   const int nch = (T + CM - 1) / CM;
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
   const int vl = lane & 15;
+  using RW = Raw<E>;
   f32x4 D[PER][NHV];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int J = wid + 4 * i;
+    const int J = wid + NWV * i;
 #pragma unroll
     for (int hv = 0; hv < NHV; ++hv)
 #pragma unroll
@@ -265,55 +276,54 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       }
   }
   // The next (earlier) chunk's record slices and dO tile load into registers
-  // while this chunk is worked on; in LDS every transposed slice is written
-  // with consecutive lanes on consecutive addresses (conflict free), which
-  // also makes consecutive lanes read consecutive 16-byte pieces of the
-  // F-order record.
-  constexpr int QM = CM * CM / 8, QK = DK * CM / 8, QQ = CM * DK / 8, QO = CM * VT;
-  constexpr int NTH = kBwdThreads;
+  // as undecoded 16-byte pieces while this chunk is worked on (decoded when
+  // they are staged, so no wait sits at the load); in LDS every transposed
+  // slice is written with consecutive lanes on consecutive addresses
+  // (conflict free), which also makes consecutive lanes read consecutive
+  // 16-byte pieces of the F-order record. Loads are unconditional (indices
+  // clamped into range); the stores skip the clamped ones.
+  constexpr int QM = CM * CM / 8, QK = DK * CM / 8, QQ = CM * DK / 8, QO = CM * VT / 8;
   constexpr int NM = (QM + NTH - 1) / NTH, NK = (QK + NTH - 1) / NTH, NQ = (QQ + NTH - 1) / NTH,
                 NO = (QO + NTH - 1) / NTH;
-  float rm[NM][8], rk[NK][8], rq[NQ][8], ry[NQ][8], rg[NO], rp = 0.f;
+  typename RW::R8 rm[NM], rk[NK], rq[NQ], ry[NQ], rg[NO];
+  float rp = 0.f;
   auto fetch = [&](int c) {
     const Rec<E, FM> R{ws + ((size_t)bh * nch + c) * RL.bytes, RL, DK, CM};
     const int t0 = c * CM;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      const int x = tid + NTH * i;
-      if (QM % NTH == 0 || x < QM) R.m8(x % CM, 8 * (x / CM), rm[i]);          // M rows t, columns s0..
+      const int x = tid + NTH * i, xc = x < QM ? x : 0;
+      rm[i] = R.m8r(xc % CM, 8 * (xc / CM));                                   // M rows t, columns s0..
     }
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int x = tid + NTH * i;
-      if (QK % NTH == 0 || x < QK) R.kt8(x % DK, 8 * (x / DK), rk[i]);         // K~^T rows j, columns s0..
+      const int x = tid + NTH * i, xc = x < QK ? x : 0;
+      rk[i] = R.kt8r(xc % DK, 8 * (xc / DK));                                  // K~^T rows j, columns s0..
     }
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      const int x = tid + NTH * i;
-      if (QQ % NTH == 0 || x < QQ) {
-        R.qp8(x % CM, 8 * (x / CM), rq[i]);                                     // rows t, columns j0..
-        R.y8(x % CM, 8 * (x / CM), ry[i]);
-      }
+      const int x = tid + NTH * i, xc = x < QQ ? x : 0;
+      rq[i] = R.qp8r(xc % CM, 8 * (xc / CM));                                  // rows t, columns j0..
+      ry[i] = R.y8r(xc % CM, 8 * (xc / CM));
     }
 #pragma unroll
-    for (int i = 0; i < NO; ++i) {
-      const int x = tid + NTH * i;
-      if (QO % NTH == 0 || x < QO) {
-        const int t = x / VT, v = x % VT;
-        const float g = (float)dO[((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v];
-        rg[i] = t0 + t < T ? g : 0.f;
-      }
+    for (int i = 0; i < NO; ++i) {                                             // dO rows t, columns v..v+7
+      const int x = tid + NTH * i, xc = x < QO ? x : 0, t = xc % CM, v = 8 * (xc / CM);
+      rg[i] = RW::ld8(dO + ((size_t)bh * T + row_in(t0 + t, T)) * DV + v0 + v);
     }
     if (tid < DK) rp = R.pic(tid);
   };
-  auto stage = [&]() {
+  auto stage = [&](int c) {
+    const int t0 = c * CM;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int x = tid + NTH * i;
       if (QM % NTH == 0 || x < QM) {
         const int t = x % CM, s0 = 8 * (x / CM);
+        float o[8];
+        RW::un8(rm[i], o);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = rm[i][e];
+        for (int e = 0; e < 8; ++e) MTl[(s0 + e) * LC + t] = s0 + e > t ? 0.f : o[e];
       }
     }
 #pragma unroll
@@ -321,8 +331,10 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       const int x = tid + NTH * i;
       if (QK % NTH == 0 || x < QK) {
         const int jr = x % DK, s0 = 8 * (x / DK);
+        float o[8];
+        RW::un8(rk[i], o);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = rk[i][e];
+        for (int e = 0; e < 8; ++e) Kl[(s0 + e) * LY + jr] = o[e];
       }
     }
 #pragma unroll
@@ -330,17 +342,27 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
       const int x = tid + NTH * i;
       if (QQ % NTH == 0 || x < QQ) {
         const int t = x % CM, j0 = 8 * (x / CM);
+        float oq[8], oy[8];
+        RW::un8(rq[i], oq);
+        RW::un8(ry[i], oy);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          QTl[(j0 + e) * LC + t] = rq[i][e];
-          YTl[(j0 + e) * LC + t] = ry[i][e];
+          QTl[(j0 + e) * LC + t] = oq[e];
+          YTl[(j0 + e) * LC + t] = oy[e];
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
       const int x = tid + NTH * i;
-      if (QO % NTH == 0 || x < QO) DOTl[(x % VT) * LC + x / VT] = rg[i];
+      if (QO % NTH == 0 || x < QO) {
+        const int t = x % CM, v = 8 * (x / CM);
+        const bool ok = t0 + t < T;
+        float o[8];
+        RW::un8(rg[i], o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) DOTl[(v + e) * LC + t] = ok ? o[e] : 0.f;
+      }
     }
     if (tid < DK) PIl[tid] = rp;
   };
@@ -349,7 +371,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
     float* dHc = dHs + ((size_t)bh * nch + c) * DK * DV;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int J = wid + 4 * i;
+      const int J = wid + NWV * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv)
@@ -361,11 +383,11 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
           }
       }
     }
-    stage();
+    stage(c);
     if (c > 0) fetch(c - 1);
     __syncthreads();
     // dV~ = M^T dO + K~ dS
-    for (int p = wid; p < (CM / 16) * NHV; p += 4) {
+    for (int p = wid; p < (CM / 16) * NHV; p += NWV) {
       const int it = p / NHV, hv = p % NHV;
       f32x4 acc = f4zero();
       tile_nt(acc, MTl, LC, 16 * it, DOTl, LC, 16 * hv, CM, lane);
@@ -377,7 +399,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
     // dS <- Diag(pi_C) dS + Q_pi^T dO - Y^T dV~
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int J = wid + 4 * i;
+      const int J = wid + NWV * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv) {
@@ -396,7 +418,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_dstates_kernel(const cha
   if (dS0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int J = wid + 4 * i;
+      const int J = wid + NWV * i;
       if (J < NST) {
 #pragma unroll
         for (int hv = 0; hv < NHV; ++hv)
@@ -1159,7 +1181,7 @@ static int bwd_launch_t(const ChunkBwdArgs& a, char* ws) {
     const float* dST = a.dS_T;
     float* dS0 = a.dS0;
     void* args[] = {&wsc, &dO, &dST, &dHs, &dS0, &T, &DV};
-    if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kBwdThreads), args, lds, st) != hipSuccess)
+    if (hipLaunchKernel(kern, dim3(BH * (DV / vt)), dim3(kBwdChunkThreads), args, lds, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
   }
   {
