@@ -116,6 +116,9 @@ struct Rec {
   __device__ R8 qp8r(int t, int j0) const { return ld8(RL.qp, FM ? fm_off(t, j0, DK) : t * DK + j0); }
   __device__ R8 kt8r(int j, int s0) const { return ld8(RL.kt, FM ? fm_off(j, s0, C) : j * C + s0); }
   __device__ R8 m8r(int t, int s0) const { return ld8(RL.m, FM ? fm_off(t, s0, C) : t * C + s0); }
+  __device__ typename Raw<E>::R4 ut4r(int v, int t0) const {
+    return Raw<E>::ld4((const E*)(p + RL.ut) + (FM ? fu_off(v, t0, C) : v * C + t0));
+  }
 };
 
 }  // namespace
@@ -666,6 +669,25 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
       }
     }
   }
+  // [U | Y] of the chunk's record for dL, loaded now as undecoded pieces and
+  // staged into LDS once the L products are done (U^T rows of 4 tokens, Y
+  // rows of 8 channels; the U^T loop is sized for d_v = 128)
+  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
+  const Rec<E, FM> R{ws + item * RL.bytes, RL, DK, CM};
+  constexpr int NUP = 128 * CM / 4 / kBwdThreads, QY = CM * DK / 8, NYP = (QY + kBwdThreads - 1) / kBwdThreads;
+  const int nup = DV * CM / 4;
+  typename RW::R4 rup[NUP];
+  typename RW::R8 ryp[NYP];
+#pragma unroll
+  for (int i = 0; i < NUP; ++i) {
+    const int x = tid + kBwdThreads * i, xc = x < nup ? x : 0;
+    rup[i] = R.ut4r(xc / (CM / 4), 4 * (xc % (CM / 4)));
+  }
+#pragma unroll
+  for (int i = 0; i < NYP; ++i) {
+    const int x = tid + kBwdThreads * i, xc = x < QY ? x : 0;
+    ryp[i] = R.y8r(xc / (DK / 8), 8 * (xc % (DK / 8)));
+  }
   __syncthreads();
   GDR_STAGE_FOR(j, DK, kBwdThreads) {   // Lambda_t = sum_{r <= t} log alpha_r
     float acc = 0.f;
@@ -722,6 +744,28 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
     }
   }
   __syncthreads();
+  // the phase-1 area is dead: [U | Y] goes to Zl
+#pragma unroll
+  for (int i = 0; i < NUP; ++i) {
+    const int x = tid + kBwdThreads * i;
+    if (x < nup) {
+      const int cc = x / (CM / 4), sq = 4 * (x % (CM / 4));
+      const f32x4 o = RW::un4(rup[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Zl[(sq + e) * NX + cc] = o[e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NYP; ++i) {
+    const int x = tid + kBwdThreads * i;
+    if (QY % kBwdThreads == 0 || x < QY) {
+      const int sr = x / (DK / 8), j0 = 8 * (x % (DK / 8));
+      float o[8];
+      RW::un8(ryp[i], o);
+      *(f32x4*)&Zl[sr * NX + DV + j0] = f32x4{o[0], o[1], o[2], o[3]};
+      *(f32x4*)&Zl[sr * NX + DV + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
+    }
+  }
   // w and v of the chunk in 16-byte pieces (8 value columns of one row) for
   // dv and dw below, issued now so they arrive during the solve
   constexpr int NWP = CM * 128 / 8 / kBwdThreads;   // pieces per thread at d_v = 128
@@ -768,22 +812,6 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_solve_kernel(
       Xl[t * NX + col] = x[t];
       dZc[(size_t)t * (DV + DK) + col] = x[t];
     }
-  }
-  const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
-  const Rec<E, FM> R{ws + item * RL.bytes, RL, DK, CM};
-  GDR_STAGE_FOR(x, DV * CM / 4, kBwdThreads) {      // U^T rows
-    const int cc = x / (CM / 4), sq = 4 * (x % (CM / 4));
-    float o[4];
-    R.ut4(cc, sq, o);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Zl[(sq + e) * NX + cc] = o[e];
-  }
-  GDR_STAGE_FOR(x, CM * DK / 8, kBwdThreads) {      // Y rows
-    const int sr = x / (DK / 8), j0 = 8 * (x % (DK / 8));
-    float o[8];
-    R.y8(sr, j0, o);
-    *(f32x4*)&Zl[sr * NX + DV + j0] = f32x4{o[0], o[1], o[2], o[3]};
-    *(f32x4*)&Zl[sr * NX + DV + j0 + 4] = f32x4{o[4], o[5], o[6], o[7]};
   }
   __syncthreads();
   // dV^ = the first d_v columns of X: dv = dV^ * w, dw = dV^ * v, 8 value
