@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn2_bwd_states_kernel(const char
   float* Ul = VTl + kVT * LC;        // U     [t][v]
   float* PIl = Ul + CM * kVT;        // pi_C  [j]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nvt = DV / kVT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kVT;
+  const int nvt = DV / kVT, lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, v0 = (lin % nvt) * kVT;
   const int nch = (T + CM - 1) / CM;
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
   const int vl = lane & 15;
@@ -261,7 +262,10 @@ __global__ __launch_bounds__(kBwdChunkThreads) void gdn2_bwd_dstates_kernel(cons
   float* DVTl = DSTl + VT * LY;      // dV~^T  [v][s]
   float* PIl = DVTl + VT * LC;       // pi_C   [j]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nvt = DV / VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * VT;
+  // the value tiles of one head on one XCD (their record slices then hit
+  // that XCD's L2 after the first read)
+  const int nvt = DV / VT, lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, v0 = (lin % nvt) * VT;
   const int nch = (T + CM - 1) / CM;
   const RecLayout RL = rec_layout(DK, DV, CM, sizeof(E));
   const int vl = lane & 15;

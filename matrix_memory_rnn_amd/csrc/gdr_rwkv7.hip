@@ -325,7 +325,10 @@ __global__ __launch_bounds__(kR7ScanThreads) void rwkv7_scan_kernel(const float*
   float* UTl = ZTl + DK * LC;           // U^T   [v][s]
   float* PIl = UTl + VT * LC;           // pi_C  [j]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, vl = lane & 15;
-  const int nvt = DV / VT, bh = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * VT;
+  // the value tiles of one head on one XCD, so its record slices are read
+  // from HBM once and then hit that XCD's L2
+  const int nvt = DV / VT, lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int bh = lin / nvt, v0 = (lin % nvt) * VT;
   const int nch = (T + CM - 1) / CM;
   const R7Layout RL = r7_layout(DK, DV, CM);
   f32x4 S[PER][NHV];
