@@ -972,11 +972,473 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
   }
 }
 
+// ============================================================================ segmented wide scan
+// The register scan with 64 value columns per workgroup (a quarter of the
+// record bytes per column: q and K~^T are shared by every column of a
+// workgroup) and the chunks of a head cut into segments, so that few heads
+// still give a workgroup per CU.
+//
+// The chunk map of the mLSTM is scalar-decay affine: over a segment g whose
+// log-forget gates sum to F_g, a start (C, n, m) goes to
+//   m' = max(m + F_g, mQ),   [C | n]' = e^{m + F_g - m'} [C | n] + e^{mQ - m'} [Q | nQ],
+// where (Q, nQ, mQ) is the segment's own end state from a zero start
+// (m = -inf): the page's stabiliser recurrence m_t = max(log f_t + m_{t-1}, i~_t)
+// unrolls to the same maximum either way. Three launches:
+//   MAP  pass: every segment but the last, from a zero start, state only;
+//   combine:   the start (C, n, m) of every segment, in order (segment 0:
+//              the caller's C0, n0, m0 copied, so the scan never reads C0 and
+//              C_out may alias it);
+//   scan:      every segment from its start, h stored, the last segment
+//              writing (C, n, m)_T.
+// The normaliser n is fp32 throughout (no extra MFMA tile): the update waves
+// add e^{A_C - mu_C} sum_s K~^T[j][s] on the VALU and the readout waves form
+// q_t . n0 from their q fragments. The V tile of a chunk is loaded once per
+// workgroup (each update wave a quarter) and passed to all update waves
+// through LDS.
+constexpr int kMSegTargetUnits = 256;   // workgroups the segmented scan aims for (one per CU)
+constexpr int kMWideVT = 64;
+
+template <int DK, int CM>
+struct MWideSmem {
+  static constexpr int NVL = kMWideVT / 16, KSC = CM / 32;
+  static constexpr int LDK = DK + 8;
+  static constexpr int PL = 16 * NVL * LDK;              // bf16 elements of one plane of the state copy
+  static constexpr int S0T = 0;                          // [buffer][plane] state copy [v][j]
+  static constexpr int NL = S0T + 4 * PL * 2;            // [buffer] n fp32 [j]
+  static constexpr int VS = NL + 2 * DK * 4;             // [buffer] V tile operand slices, 1 KiB each
+  static constexpr int VSTAGE = NVL * KSC * 1024;
+  static constexpr int TOTAL = VS + 2 * VSTAGE;
+  static_assert(TOTAL <= 160 * 1024, "wide mLSTM scan LDS exceeds 160 KiB");
+};
+
+template <int DK, int CM, bool MAP>
+__global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
+    const char* __restrict__ ws, const float* __restrict__ Cst, const float* __restrict__ nst,
+    const float* __restrict__ mst, __bf16* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV,
+    int seg, float* __restrict__ Qmap, float* __restrict__ nQ, float* __restrict__ mF) {
+  using L = MWideSmem<DK, CM>;
+  constexpr int NS = kMScanRgSets;
+  constexpr int NW = kMScanThreads / 64;
+  constexpr int NB = CM / 16, NU = NW - NB;             // readout waves, update waves
+  constexpr int NVL = L::NVL;
+  constexpr int KS = DK / 32, KSC = L::KSC;
+  constexpr int NJB = DK / 16, JPW = (NJB + NU - 1) / NU;
+  constexpr int LDK = L::LDK, PL = L::PL;
+  constexpr int NVT = NVL * KSC, VPW = NVT / NB;        // V slices per chunk, per readout wave
+  // every update wave holds JPW whole j-blocks: no branch in its chunk loop
+  // (a branch there leaves the compiler waiting for every load in flight at
+  // the loop's back edge)
+  static_assert(DK % 64 == 0 && CM == 64 && NB < NW && NS == 3 && NVT % NB == 0 && NJB % NU == 0,
+                "wide mLSTM scan shape");
+  typedef __attribute__((ext_vector_type(2))) uint32_t u2;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __bf16* S0T = (__bf16*)(smem + L::S0T);
+  float* NLs = (float*)(smem + L::NL);
+  char* VS = smem + L::VS;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nvt = DV / kMWideVT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int ntot = (T + CM - 1) / CM;
+  const int nseg = (ntot + seg - 1) / seg;
+  const int nsl = MAP ? nseg - 1 : nseg;                // segments this launch walks
+  const int unit = lin / nvt, vt0 = (lin % nvt) * kMWideVT;
+  const int bh = unit / nsl, sg = unit % nsl;
+  const int BH = gridDim.x / (nvt * nsl);
+  const int c0 = sg * seg;
+  const int nchunks = ntot - c0 < seg ? ntot - c0 : seg;
+  const MRec RL = mrec_layout(DK, DV, CM, 2, true);
+  const char* wsh = ws + ((size_t)bh * ntot + c0) * RL.bytes;
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wsh), 0, nchunks * RL.bytes, 0x00020000);
+  auto cbase = [&](int ch) { return (ch < nchunks ? ch : nchunks - 1) * RL.bytes; };
+  auto ld16 = [&](int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, soff, 0));
+  };
+  auto ld4 = [&](int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, voff, soff, 0));
+  };
+  const int l16 = 16 * lane;
+  const size_t slot = (size_t)sg * BH + bh;             // this segment's start / map slot
+  float mprev = MAP ? -INFINITY : mst[slot];
+
+  auto walk = [&](auto&& step) {
+    int ch = 0;
+    for (; ch + 3 <= nchunks; ch += 3) {
+      step(ch, RgI<0>{});
+      step(ch + 1, RgI<1>{});
+      step(ch + 2, RgI<2>{});
+    }
+    if (ch < nchunks) step(ch, RgI<0>{});
+    if (ch + 1 < nchunks) step(ch + 1, RgI<1>{});
+  };
+
+  // V tile of a chunk: slices p = VPW I .. VPW I + VPW - 1 (vl = p / KSC,
+  // s = p % KSC) are loaded by readout wave I and staged in LDS a chunk
+  // ahead, already scaled by the chunk's e^{A_C - mu_C} (once per workgroup,
+  // not once per update wave), and read by every update wave
+  auto stage_v = [&](const u32x4* X, int I, int buf, float dI) {
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, X[i]);
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * dI);
+      *(bf16x8*)(VS + buf * L::VSTAGE + (VPW * I + i) * 1024 + l16) = y;
+    }
+  };
+  // e^{A_C - mu_C} of a chunk whose A_C is aC, entered with stabiliser m
+  auto write_scale = [](float m, float aC) { return __expf(aC - fmaxf(m, aC)); };
+
+  if (wid < NB) {
+    // ================= readout: t-block I, 64 value columns (MAP: V tile only)
+    const int I = wid;
+    struct Set {
+      u32x4 q[MAP ? 1 : KS];
+      u2 hv[NVL];
+      u32x4 v[VPW];
+      float sA, sN, sF, aC, fC;
+    };
+    Set R[NS];
+    const int lh = (c16 * DV + 4 * g) * 2;
+    auto load = [&](int ch, Set& X) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int i = 0; i < VPW; ++i) {
+        const int p = VPW * I + i;
+        X.v[i] = ld16(l16, cb + RL.vt + ((vt0 / 16 + p / KSC) * KSC + p % KSC) * 1024);
+      }
+      X.aC = ld4(0, cb + RL.a + 4 * (CM - 1));
+      X.fC = ld4(0, cb + RL.f + 4 * (CM - 1));
+      if constexpr (!MAP) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) X.q[s] = ld16(l16, cb + RL.qf + (I * KS + s) * 1024);
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl)
+          X.hv[vl] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                wr, 8 * lane, cb + RL.hi + (I * (DV / 16) + vt0 / 16 + vl) * 512, 0));
+        X.sA = ld4(4 * c16, cb + RL.a + 64 * I);
+        X.sN = ld4(4 * c16, cb + RL.ni + 64 * I);
+        X.sF = ld4(4 * c16, cb + RL.f + 64 * I);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      load(u, R[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_v(R[0].v, I, 0, write_scale(mprev, R[0].aC));
+    __syncthreads();                                    // first state copy and V tile written
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      if constexpr (!MAP) {
+        const __bf16* SB = S0T + 2 * (ch & 1) * PL;
+        const float* Nb = NLs + (ch & 1) * DK;
+        f32x4 acc[NVL];
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl) acc[vl] = f4zero();
+        float qn = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 B = __builtin_bit_cast(bf16x8, R[u].q[s]);
+          // hi planes of the four tiles, then the lo planes: no MFMA waits on
+          // the one just issued
+          bf16x8 Fh[NVL], Fl[NVL];
+#pragma unroll
+          for (int vl = 0; vl < NVL; ++vl) {
+            const int o = (16 * vl + c16) * LDK + 32 * s + 8 * g;
+            Fh[vl] = *(const bf16x8*)(SB + o);
+            Fl[vl] = *(const bf16x8*)(SB + PL + o);
+          }
+#pragma unroll
+          for (int vl = 0; vl < NVL; ++vl) acc[vl] = mfma_bf16(Fh[vl], B, acc[vl]);
+#pragma unroll
+          for (int vl = 0; vl < NVL; ++vl) acc[vl] = mfma_bf16(Fl[vl], B, acc[vl]);
+          // q_t . n0 over this lane's 8 k of the slice
+          const f32x4 na = *(const f32x4*)(Nb + 32 * s + 8 * g);
+          const f32x4 nb = *(const f32x4*)(Nb + 32 * s + 8 * g + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qn += (float)B[e] * na[e] + (float)B[4 + e] * nb[e];
+        }
+        qn += __shfl_xor(qn, 16, 64);
+        qn += __shfl_xor(qn, 32, 64);
+        // acc[vl][e] = (q_t C0)[v = vt0 + 16vl + 4g + e], t = 16I + c16; qn = q_t . n0
+        const float At = R[u].sA;
+        const float mu = fmaxf(mprev, At);
+        const float si = __expf(At - mu);
+        const float se = mprev == -INFINITY ? 0.f : __expf(mprev - mu);
+        const float nbar = se * qn + si * R[u].sN;
+        const float inv = 1.f / fmaxf(fabsf(nbar), __expf(-(R[u].sF + mu)));
+        const int t0 = (c0 + ch) * CM;
+        const __amdgpu_buffer_rsrc_t hr =
+            __builtin_amdgcn_make_buffer_rsrc(h + ((size_t)bh * T + t0) * DV, 0, (T - t0) * DV * 2, 0x00020000);
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl) {
+          const f32x4 hv = Raw<__bf16>::un4(R[u].hv[vl]);
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (__bf16)((se * acc[vl][e] + si * hv[e]) * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, o), hr, lh + (16 * I * DV + vt0 + 16 * vl) * 2,
+                                                0, 0);
+        }
+      }
+      mprev = R[u].fC + fmaxf(mprev, R[u].aC);
+      // the next chunk's V tile (loaded two chunks ago), then this set refilled
+      stage_v(R[(u + 1) % NS].v, I, (ch + 1) & 1, write_scale(mprev, R[(u + 1) % NS].aC));
+      load(ch + NS, R[u]);
+      rg_phase_barrier();
+    });
+  } else {
+    // ================= state update: j-blocks uid, uid + NU, .. of the 64 columns
+    const int uid = wid - NB;
+    struct Set {
+      u32x4 k[JPW][KSC];
+      float aC, fC;
+    };
+    Set U[NS];
+    auto load = [&](int ch, Set& X) {
+      const int cb = cbase(ch);
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = uid + NU * jj;
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) X.k[jj][s] = ld16(l16, cb + RL.kt + (jt * KSC + s) * 1024);
+      }
+      X.aC = ld4(0, cb + RL.a + 4 * (CM - 1));
+      X.fC = ld4(0, cb + RL.f + 4 * (CM - 1));
+    };
+    // state: Sacc[jj][vl][e] = C[j = 16 jt + 4g + e][v = vt0 + 16 vl + c16];
+    // nr[jj][e] = n[j = 16 jt + 4g + e] (the same in all 16 columns)
+    f32x4 Sacc[JPW][NVL], nr[JPW];
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj) {
+      const int jt = uid + NU * jj;
+      nr[jj] = !MAP ? *(const f32x4*)(nst + slot * DK + 16 * jt + 4 * g) : f4zero();
+#pragma unroll
+      for (int vl = 0; vl < NVL; ++vl) {
+        Sacc[jj][vl] = f4zero();
+        if (!MAP) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Sacc[jj][vl][e] = Cst[slot * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16];
+        }
+      }
+    }
+    auto put_state = [&](int buf) {
+      if constexpr (!MAP) {
+        __bf16* SN = S0T + 2 * buf * PL;
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          const int jt = uid + NU * jj;
+#pragma unroll
+          for (int vl = 0; vl < NVL; ++vl)
+            st4<kSP>((char*)SN, PL * 2, (16 * vl + c16) * LDK + 16 * jt + 4 * g, Sacc[jj][vl]);
+          if (c16 == 0) *(f32x4*)(NLs + buf * DK + 16 * jt + 4 * g) = nr[jj];
+        }
+      }
+    };
+    put_state(0);
+    __syncthreads();                                    // first state copy and V tile written
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+      load(u, U[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // L2 warm-up: the workgroups of a segment touch the record's 128-byte
+    // lines that this launch reads (MAP: V^T and K~^T only), one dword per
+    // lane of every update wave, kPF chunks ahead, so that their loads hit L2
+    // (each line is read by every workgroup of the segment). The values are
+    // folded into `sink` three chunks later, which keeps the loads alive
+    // without waiting for them early.
+    constexpr int kPF = 5;
+    constexpr bool kTouch = !MAP;   // the map pass reads less and ran slower with them
+    const int tb = MAP ? RL.vt : 0;
+    const int nlines = ((MAP ? RL.qf - RL.vt : RL.bytes) + 127) / 128;
+    const int pl = ((lin % nvt) * NU + uid) * 64 + lane;
+    const int v_pf = tb + (pl < nlines ? pl : nlines - 1) * 128;
+    auto touch = [&](int ch) { return __builtin_amdgcn_raw_buffer_load_b32(wr, v_pf, cbase(ch), 0); };
+    uint32_t sink = 0, PFV[3] = {0u, 0u, 0u};
+    if constexpr (kTouch) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) PFV[u] = touch(kPF - 3 + u);
+    }
+    float Fsum = 0.f;
+    constexpr int NLU = JPW * KSC + 2;
+    walk([&](int ch, auto Uc) {
+      constexpr int u = decltype(Uc)::value;
+      // the touch first: issued after this set's loads, the compiler would
+      // wait for every load in flight at the loop's back edge
+      if constexpr (kTouch) {
+        sink ^= PFV[u];
+        PFV[u] = touch(ch + kPF);
+      }
+      load(ch + NS - 1, U[(u + NS - 1) % NS]);
+      // [C | n] <- e^{m0 - mu_C} [C | n] + e^{A_C - mu_C} K~^T [V | 1]
+      const float AC = U[u].aC;
+      const float muC = fmaxf(mprev, AC);
+      const float dI = __expf(AC - muC);
+      const float dC = mprev == -INFINITY ? 0.f : __expf(mprev - muC);
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] *= dC;
+      // V arrives scaled by dI; n takes the row sums of K~^T on the matrix
+      // cores against an operand holding bf16(dI) in every entry (as the
+      // scaled V it is rounded to bf16)
+      const char* Vb = VS + (ch & 1) * L::VSTAGE;
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nr[jj][e] *= dC;
+      bf16x8 ones;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ones[e] = (__bf16)dI;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl) {
+          const bf16x8 Bv = *(const bf16x8*)(Vb + (vl * KSC + s) * 1024 + l16);
+#pragma unroll
+          for (int jj = 0; jj < JPW; ++jj)
+            Sacc[jj][vl] = mfma_bf16(__builtin_bit_cast(bf16x8, U[u].k[jj][s]), Bv, Sacc[jj][vl]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) nr[jj] = mfma_bf16(__builtin_bit_cast(bf16x8, U[u].k[jj][s]), ones, nr[jj]);
+      }
+#pragma unroll
+      for (int i = 0; i < NLU; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      }
+      put_state((ch + 1) & 1);
+      mprev = U[u].fC + fmaxf(mprev, AC);
+      Fsum += U[u].fC;
+      rg_phase_barrier();
+    });
+    if constexpr (kTouch) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) sink ^= PFV[u];
+    }
+    if (sink == 0x7fc00001u && T < 0) mF[0] = 0.f;   // never true (T > 0): keeps the touches alive
+    if constexpr (MAP) {
+      // this segment's end state from a zero start, its stabiliser and F_g
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = uid + NU * jj;
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Qmap[slot * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
+        if (c16 == 0 && vt0 == 0) *(f32x4*)(nQ + slot * DK + 16 * jt + 4 * g) = nr[jj];
+      }
+      if (uid == 0 && lane == 0 && vt0 == 0) {
+        mF[2 * slot] = mprev;
+        mF[2 * slot + 1] = Fsum;
+      }
+    } else if (C_out && sg == nseg - 1) {
+#pragma unroll
+      for (int jj = 0; jj < JPW; ++jj) {
+        const int jt = uid + NU * jj;
+#pragma unroll
+        for (int vl = 0; vl < NVL; ++vl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            C_out[(size_t)bh * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
+        if (c16 == 0 && vt0 == 0) *(f32x4*)(n_out + (size_t)bh * DK + 16 * jt + 4 * g) = nr[jj];
+      }
+      if (uid == 0 && lane == 0 && vt0 == 0) m_out[bh] = mprev;
+    }
+  }
+}
+
+// Segment start states in order: slot 0 = (C0, n0, m0) (zero and -inf without
+// C0), slot g + 1 = the map of segment g applied to slot g. One thread per
+// element of a head's [C | n] (DK * DV + DK), grid (heads, element blocks).
+__global__ __launch_bounds__(256) void mlstm_seg_combine_kernel(
+    const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
+    const float* __restrict__ Qmap, const float* __restrict__ nQ, const float* __restrict__ mF, float* Cst,
+    float* nst, float* mst, int BH, int DK, int DV, int nseg) {
+  const int bh = blockIdx.y;
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  const int nC = DK * DV;
+  if (x >= nC + DK) return;
+  const bool isC = x < nC;
+  float ms = C0 != nullptr ? m0[bh] : -INFINITY;
+  float xs = C0 == nullptr ? 0.f : isC ? C0[(size_t)bh * nC + x] : n0[(size_t)bh * DK + (x - nC)];
+  auto put = [&](int sg, float val, float m) {
+    const size_t slot = (size_t)sg * BH + bh;
+    if (isC) Cst[slot * nC + x] = val;
+    else nst[slot * DK + (x - nC)] = val;
+    if (x == 0) mst[slot] = m;
+  };
+  put(0, xs, ms);
+  for (int sg = 0; sg + 1 < nseg; ++sg) {
+    const size_t slot = (size_t)sg * BH + bh;
+    const float mQ = mF[2 * slot], F = mF[2 * slot + 1];
+    const float me = fmaxf(ms + F, mQ);
+    const float q = isC ? Qmap[slot * nC + x] : nQ[slot * DK + (x - nC)];
+    xs = expf(ms + F - me) * xs + expf(mQ - me) * q;
+    ms = me;
+    put(sg + 1, xs, ms);
+  }
+}
+
 // ------------------------------------------------------------------ host launch
-size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+// The segmented wide scan's plan from the shapes alone: chunks per segment,
+// or 0 where the plain register scan is used (enough workgroups without
+// segments, short sequences, or shapes the wide scan does not take).
+static int mseg_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  if (!mlstm_fm(dtype, dk, dv, chunk, T) || chunk != 64 || dk % 64 != 0 || dv % kMWideVT != 0) return 0;
+  const long long units = (long long)B * H * (dv / kMWideVT);
+  const int ntot = (T + chunk - 1) / chunk;
+  if (units * 2 > kMSegTargetUnits || ntot < 32) return 0;
+  int nseg = (int)(kMSegTargetUnits / units);
+  if (nseg > ntot / 16) nseg = ntot / 16;
+  if (nseg < 2) return 0;
+  return (ntot + nseg - 1) / nseg;
+}
+
+static size_t mrecords_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
   const int es = dtype == GDR_BF16 ? 2 : 4;
   const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
   return (size_t)B * H * nchunks * (size_t)mrec_layout(dk, dv, chunk, es, mlstm_fm(dtype, dk, dv, chunk, T)).bytes;
+}
+
+// Buffers of the segmented scan after the records (fp32): maps [nseg-1][BH]
+// of [dk][dv], [dk] and (mQ, F); starts [nseg][BH] of [dk][dv], [dk] and m.
+struct MSegBufs {
+  float *Q, *nQ, *mF, *Cst, *nst, *mst;
+  size_t bytes;
+};
+static MSegBufs mseg_bufs(char* base, int BH, int dk, int dv, int nseg) {
+  MSegBufs b;
+  const size_t nm = (size_t)(nseg - 1) * BH, ns = (size_t)nseg * BH;
+  float* p = (float*)base;
+  b.Q = p;   p += nm * dk * dv;
+  b.nQ = p;  p += nm * dk;
+  b.mF = p;  p += 2 * nm;
+  b.Cst = p; p += ns * dk * dv;
+  b.nst = p; p += ns * dk;
+  b.mst = p; p += ns;
+  b.bytes = (size_t)((char*)p - base);
+  return b;
+}
+
+size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  size_t n = mrecords_bytes(B, H, T, dk, dv, chunk, dtype);
+  const int seg = mseg_plan(B, H, T, dk, dv, chunk, dtype);
+  if (seg) {
+    const int ntot = (T + chunk - 1) / chunk, nseg = (ntot + seg - 1) / seg;
+    n = (n + 255) / 256 * 256 + mseg_bufs(nullptr, B * H, dk, dv, nseg).bytes;
+  }
+  return n;
 }
 
 template <typename Tin, int DK, int CM, bool FM>
@@ -1031,6 +1493,48 @@ static int launch_mscan_rg(const MlstmArgs& a, const char* ws) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
+// Segmented wide scan: segment maps, start states, then every segment's scan.
+template <int DK, int CM>
+static int launch_mscan_wide(const MlstmArgs& a, char* ws, int seg) {
+  using L = MWideSmem<DK, CM>;
+  auto kmap = mlstm_scan_wide_kernel<DK, CM, true>;
+  auto kscan = mlstm_scan_wide_kernel<DK, CM, false>;
+  if (!allow_lds((const void*)kmap, L::TOTAL) || !allow_lds((const void*)kscan, L::TOTAL)) return GDR_ERR_LAUNCH;
+  const int BH = a.B * a.H, nvt = a.dv / kMWideVT;
+  const int ntot = (a.T + CM - 1) / CM, nseg = (ntot + seg - 1) / seg;
+  const size_t rec = (mrecords_bytes(a.B, a.H, a.T, DK, a.dv, CM, GDR_BF16) + 255) / 256 * 256;
+  const MSegBufs sb = mseg_bufs(ws + rec, BH, DK, a.dv, nseg);
+  hipStream_t st = (hipStream_t)a.stream;
+  const char* wsc = ws;
+  const float* nulf = nullptr;
+  __bf16* h = (__bf16*)a.h;
+  float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
+  float *Q = sb.Q, *nQ = sb.nQ, *mF = sb.mF, *Cst = sb.Cst, *nst = sb.nst, *mst = sb.mst;
+  int T = a.T, DV = a.dv, DKi = DK, BHi = BH, nsegi = nseg;
+  {
+    void* args[] = {&wsc, &nulf, &nulf, &nulf, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF};
+    if (hipLaunchKernel((const void*)kmap, dim3(BH * (nseg - 1) * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
+        hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
+    const float *cQ = Q, *cnQ = nQ, *cmF = mF;
+    void* args[] = {&C0, &n0, &m0, &cQ, &cnQ, &cmF, &Cst, &nst, &mst, &BHi, &DKi, &DV, &nsegi};
+    const dim3 grid((DK * a.dv + DK + 255) / 256, BH);
+    if (hipLaunchKernel((const void*)mlstm_seg_combine_kernel, grid, dim3(256), args, 0, st) != hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  {
+    const float *cC = Cst, *cn = nst, *cm = mst;
+    void* args[] = {&wsc, &cC, &cn, &cm, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF};
+    if (hipLaunchKernel((const void*)kscan, dim3(BH * nseg * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
+        hipSuccess)
+      return GDR_ERR_LAUNCH;
+  }
+  return GDR_OK;
+}
+
 template <typename Tin, int DK, int CM>
 static int mlstm_pair(const MlstmArgs& a, char* ws) {
   // value tiles of 32 columns when that still gives a workgroup per CU, else 16
@@ -1039,6 +1543,10 @@ static int mlstm_pair(const MlstmArgs& a, char* ws) {
     if (mlstm_fm(a.dtype, DK, a.dv, CM, a.T)) {
       const int st = launch_mintra<Tin, DK, CM, true>(a, ws);
       if (st != GDR_OK) return st;
+      if constexpr (CM == 64 && DK % 64 == 0) {
+        const int seg = mseg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype);
+        if (seg) return launch_mscan_wide<DK, CM>(a, ws, seg);
+      }
       if (!wide) return launch_mscan_rg<DK, 16, CM>(a, ws);
       return launch_mscan_rg<DK, 32, CM>(a, ws);
     }
