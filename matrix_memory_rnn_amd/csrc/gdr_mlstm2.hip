@@ -985,11 +985,13 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
 // (m = -inf): the page's stabiliser recurrence m_t = max(log f_t + m_{t-1}, i~_t)
 // unrolls to the same maximum either way. Three launches:
 //   MAP  pass: every segment but the last, from a zero start, state only;
-//   combine:   the start (C, n, m) of every segment, in order (segment 0:
-//              the caller's C0, n0, m0 copied, so the scan never reads C0 and
-//              C_out may alias it);
 //   scan:      every segment from its start, h stored, the last segment
-//              writing (C, n, m)_T.
+//              writing (C, n, m)_T. A segment's workgroup forms its start in
+//              its prologue: (C0, n0, m0) with the maps of the segments
+//              before it applied in order. Where C_out, n_out or m_out
+//              overlaps its input, a copy of (C0, n0, m0) is made first (the
+//              last segment's final store could otherwise land before another
+//              segment has read the start).
 // The normaliser n is fp32 throughout (no extra MFMA tile): the update waves
 // add e^{A_C - mu_C} sum_s K~^T[j][s] on the VALU and the readout waves form
 // q_t . n0 from their q fragments. The V tile of a chunk is loaded once per
@@ -1062,8 +1064,17 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, voff, soff, 0));
   };
   const int l16 = 16 * lane;
-  const size_t slot = (size_t)sg * BH + bh;             // this segment's start / map slot
-  float mprev = MAP ? -INFINITY : mst[slot];
+  const size_t slot = (size_t)sg * BH + bh;             // this segment's map slot (MAP)
+  // the stabiliser this segment starts from: m0 (or -inf), then each earlier
+  // segment's map; Cst, nst, mst hold (C0, n0, m0) or are NULL (zero start)
+  float mprev = -INFINITY;
+  if constexpr (!MAP) {
+    if (Cst != nullptr) mprev = mst[bh];
+    for (int gq = 0; gq < sg; ++gq) {
+      const size_t sl = (size_t)gq * BH + bh;
+      mprev = fmaxf(mprev + mF[2 * sl + 1], mF[2 * sl]);
+    }
+  }
 
   auto walk = [&](auto&& step) {
     int ch = 0;
@@ -1215,16 +1226,42 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     f32x4 Sacc[JPW][NVL], nr[JPW];
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
-      const int jt = uid + NU * jj;
-      nr[jj] = !MAP ? *(const f32x4*)(nst + slot * DK + 16 * jt + 4 * g) : f4zero();
+      nr[jj] = f4zero();
 #pragma unroll
-      for (int vl = 0; vl < NVL; ++vl) {
-        Sacc[jj][vl] = f4zero();
-        if (!MAP) {
+      for (int vl = 0; vl < NVL; ++vl) Sacc[jj][vl] = f4zero();
+    }
+    // element (jj, vl, e) of a [dk][dv] array / element (jj, e) of a [dk] one
+    auto cidx = [&](int jj, int vl, int e) { return (size_t)(16 * (uid + NU * jj) + 4 * g + e) * DV + vt0 + 16 * vl + c16; };
+    auto nidx = [&](int jj) { return 16 * (uid + NU * jj) + 4 * g; };
+    if constexpr (!MAP) {
+      if (Cst != nullptr) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            Sacc[jj][vl][e] = Cst[slot * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16];
+        for (int jj = 0; jj < JPW; ++jj) {
+          nr[jj] = *(const f32x4*)(nst + (size_t)bh * DK + nidx(jj));
+#pragma unroll
+          for (int vl = 0; vl < NVL; ++vl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] = Cst[(size_t)bh * DK * DV + cidx(jj, vl, e)];
         }
+      }
+      // the maps of the segments before this one, in order
+      float ms = Cst != nullptr ? mst[bh] : -INFINITY;
+      for (int gq = 0; gq < sg; ++gq) {
+        const size_t sl = (size_t)gq * BH + bh;
+        const float mQ = mF[2 * sl], me = fmaxf(ms + mF[2 * sl + 1], mQ);
+        const float a = __expf(ms + mF[2 * sl + 1] - me), b = __expf(mQ - me);
+        const float* Qs = Qmap + sl * DK * DV;
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+          const f32x4 nq = *(const f32x4*)(nQ + sl * DK + nidx(jj));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nr[jj][e] = a * nr[jj][e] + b * nq[e];
+#pragma unroll
+          for (int vl = 0; vl < NVL; ++vl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] = a * Sacc[jj][vl][e] + b * Qs[cidx(jj, vl, e)];
+        }
+        ms = me;
       }
     }
     auto put_state = [&](int buf) {
@@ -1361,6 +1398,8 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
 // Segment start states in order: slot 0 = (C0, n0, m0) (zero and -inf without
 // C0), slot g + 1 = the map of segment g applied to slot g. One thread per
 // element of a head's [C | n] (DK * DV + DK), grid (heads, element blocks).
+// The wide scan forms its starts itself; this kernel runs with nseg = 1, as
+// the copy of (C0, n0, m0) that an in-place call (C_out = C0) scans from.
 __global__ __launch_bounds__(256) void mlstm_seg_combine_kernel(
     const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
     const float* __restrict__ Qmap, const float* __restrict__ nQ, const float* __restrict__ mF, float* Cst,
@@ -1412,14 +1451,15 @@ static size_t mrecords_bytes(int B, int H, int T, int dk, int dv, int chunk, int
 }
 
 // Buffers of the segmented scan after the records (fp32): maps [nseg-1][BH]
-// of [dk][dv], [dk] and (mQ, F); starts [nseg][BH] of [dk][dv], [dk] and m.
+// of [dk][dv], [dk] and (mQ, F); a copy of (C0, n0, m0) for calls whose C_out
+// is C0: [BH] of [dk][dv], [dk] and m.
 struct MSegBufs {
   float *Q, *nQ, *mF, *Cst, *nst, *mst;
   size_t bytes;
 };
 static MSegBufs mseg_bufs(char* base, int BH, int dk, int dv, int nseg) {
   MSegBufs b;
-  const size_t nm = (size_t)(nseg - 1) * BH, ns = (size_t)nseg * BH;
+  const size_t nm = (size_t)(nseg - 1) * BH, ns = (size_t)BH;
   float* p = (float*)base;
   b.Q = p;   p += nm * dk * dv;
   b.nQ = p;  p += nm * dk;
@@ -1510,23 +1550,29 @@ static int launch_mscan_wide(const MlstmArgs& a, char* ws, int seg) {
   __bf16* h = (__bf16*)a.h;
   float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
   float *Q = sb.Q, *nQ = sb.nQ, *mF = sb.mF, *Cst = sb.Cst, *nst = sb.nst, *mst = sb.mst;
-  int T = a.T, DV = a.dv, DKi = DK, BHi = BH, nsegi = nseg;
+  int T = a.T, DV = a.dv, DKi = DK, BHi = BH;
   {
     void* args[] = {&wsc, &nulf, &nulf, &nulf, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF};
     if (hipLaunchKernel((const void*)kmap, dim3(BH * (nseg - 1) * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
         hipSuccess)
       return GDR_ERR_LAUNCH;
   }
-  {
+  // the scan reads (C0, n0, m0) in every segment's prologue; with C_out = C0
+  // it reads a copy instead (nseg = 1: the combine kernel copies slot 0 only)
+  const float *cC = a.C0, *cn = a.n0, *cm = a.m0;
+  if (a.C0 != nullptr && a.C_out == a.C0) {
     const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
     const float *cQ = Q, *cnQ = nQ, *cmF = mF;
-    void* args[] = {&C0, &n0, &m0, &cQ, &cnQ, &cmF, &Cst, &nst, &mst, &BHi, &DKi, &DV, &nsegi};
+    int one = 1;
+    void* args[] = {&C0, &n0, &m0, &cQ, &cnQ, &cmF, &Cst, &nst, &mst, &BHi, &DKi, &DV, &one};
     const dim3 grid((DK * a.dv + DK + 255) / 256, BH);
     if (hipLaunchKernel((const void*)mlstm_seg_combine_kernel, grid, dim3(256), args, 0, st) != hipSuccess)
       return GDR_ERR_LAUNCH;
+    cC = Cst;
+    cn = nst;
+    cm = mst;
   }
   {
-    const float *cC = Cst, *cn = nst, *cm = mst;
     void* args[] = {&wsc, &cC, &cn, &cm, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF};
     if (hipLaunchKernel((const void*)kscan, dim3(BH * nseg * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
         hipSuccess)
