@@ -121,7 +121,10 @@ struct MIntraSmem {
   static_assert(TOTAL <= 160 * 1024, "mLSTM intra kernel LDS exceeds 160 KiB");
 };
 
-template <typename Tin, int DK, int CM, bool FM>
+// QC: the fragment-form record also gets the tile-order copy of q (the
+// register scan reads it; the wide scan reads q from the input instead and
+// leaves that part of the record unwritten).
+template <typename Tin, int DK, int CM, bool FM, bool QC = true>
 __global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ i_tilde, const float* __restrict__ f_tilde, char* __restrict__ ws,
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(kMThreads, 2) void mlstm_intra_kernel(
       *(P16*)dst = *(const P16*)src;
       if constexpr (F32) *(P16*)(dst + 16) = *(const P16*)(src + 16);
     }
-    if constexpr (FM) {
+    if constexpr (FM && QC) {
       // q (rows past T are zero in LDS) in the operand tiles of the readout
       constexpr int KSQ = DK / 32;
       for (int p = tid; p < CM * DK / 8; p += kMThreads) {
@@ -1017,7 +1020,8 @@ template <int DK, int CM, bool MAP>
 __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     const char* __restrict__ ws, const float* __restrict__ Cst, const float* __restrict__ nst,
     const float* __restrict__ mst, __bf16* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV,
-    int seg, float* __restrict__ Qmap, float* __restrict__ nQ, float* __restrict__ mF) {
+    int seg, float* __restrict__ Qmap, float* __restrict__ nQ, float* __restrict__ mF,
+    const __bf16* __restrict__ qin) {
   using L = MWideSmem<DK, CM>;
   constexpr int NS = kMScanRgSets;
   constexpr int NW = kMScanThreads / 64;
@@ -1115,6 +1119,13 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     };
     Set R[NS];
     const int lh = (c16 * DV + 4 * g) * 2;
+    // q of this head from the segment's first row to row T, straight from the
+    // input (rows past T read as zero): lane l of t-block I reads row
+    // 16 I + l % 16, columns 32 s + 8 (l / 16) .. +7, the B operand of the
+    // readout's 16x16x32 MFMA
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(qin) + ((size_t)bh * T + (size_t)c0 * CM) * DK, 0, (T - c0 * CM) * DK * 2, 0x00020000);
+    const int lq = ((16 * I + c16) * DK + 8 * g) * 2;
     auto load = [&](int ch, Set& X) {
       const int cb = cbase(ch);
 #pragma unroll
@@ -1125,8 +1136,10 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
       X.aC = ld4(0, cb + RL.a + 4 * (CM - 1));
       X.fC = ld4(0, cb + RL.f + 4 * (CM - 1));
       if constexpr (!MAP) {
+        const int qb = (ch < nchunks ? ch : nchunks - 1) * CM * DK * 2;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) X.q[s] = ld16(l16, cb + RL.qf + (I * KS + s) * 1024);
+        for (int s = 0; s < KS; ++s)
+          X.q[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, lq, qb + 64 * s, 0));
 #pragma unroll
         for (int vl = 0; vl < NVL; ++vl)
           X.hv[vl] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(
@@ -1286,7 +1299,7 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     // L2 warm-up: the workgroups of a segment touch the record's 128-byte
-    // lines that this launch reads (MAP: V^T and K~^T only), one dword per
+    // lines that this launch reads (H, V^T, K~^T; MAP: V^T and K~^T), one dword per
     // lane of every update wave, kPF chunks ahead, so that their loads hit L2
     // (each line is read by every workgroup of the segment). The values are
     // folded into `sink` three chunks later, which keeps the loads alive
@@ -1294,7 +1307,7 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     constexpr int kPF = 5;
     constexpr bool kTouch = !MAP;   // the map pass reads less and ran slower with them
     const int tb = MAP ? RL.vt : 0;
-    const int nlines = ((MAP ? RL.qf - RL.vt : RL.bytes) + 127) / 128;
+    const int nlines = ((MAP ? RL.qf - RL.vt : RL.qf) + 127) / 128;
     const int pl = ((lin % nvt) * NU + uid) * 64 + lane;
     const int v_pf = tb + (pl < nlines ? pl : nlines - 1) * 128;
     auto touch = [&](int ch) { return __builtin_amdgcn_raw_buffer_load_b32(wr, v_pf, cbase(ch), 0); };
@@ -1481,10 +1494,10 @@ size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype)
   return n;
 }
 
-template <typename Tin, int DK, int CM, bool FM>
+template <typename Tin, int DK, int CM, bool FM, bool QC = true>
 static int launch_mintra(const MlstmArgs& a, char* ws) {
   using L = MIntraSmem<Tin, DK, CM>;
-  auto kern = mlstm_intra_kernel<Tin, DK, CM, FM>;
+  auto kern = mlstm_intra_kernel<Tin, DK, CM, FM, QC>;
   if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   int nchunks = (a.T + CM - 1) / CM;
   int nitems = a.B * a.H * nchunks;
@@ -1551,8 +1564,9 @@ static int launch_mscan_wide(const MlstmArgs& a, char* ws, int seg) {
   float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
   float *Q = sb.Q, *nQ = sb.nQ, *mF = sb.mF, *Cst = sb.Cst, *nst = sb.nst, *mst = sb.mst;
   int T = a.T, DV = a.dv, DKi = DK, BHi = BH;
+  const __bf16* qin = (const __bf16*)a.q;
   {
-    void* args[] = {&wsc, &nulf, &nulf, &nulf, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF};
+    void* args[] = {&wsc, &nulf, &nulf, &nulf, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF, &qin};
     if (hipLaunchKernel((const void*)kmap, dim3(BH * (nseg - 1) * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
         hipSuccess)
       return GDR_ERR_LAUNCH;
@@ -1573,7 +1587,7 @@ static int launch_mscan_wide(const MlstmArgs& a, char* ws, int seg) {
     cm = mst;
   }
   {
-    void* args[] = {&wsc, &cC, &cn, &cm, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF};
+    void* args[] = {&wsc, &cC, &cn, &cm, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF, &qin};
     if (hipLaunchKernel((const void*)kscan, dim3(BH * nseg * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
         hipSuccess)
       return GDR_ERR_LAUNCH;
@@ -1587,12 +1601,16 @@ static int mlstm_pair(const MlstmArgs& a, char* ws) {
   const bool wide = a.dv >= 32 && (long long)a.B * a.H * (a.dv / 32) >= stream_cus(a.stream);
   if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
     if (mlstm_fm(a.dtype, DK, a.dv, CM, a.T)) {
-      const int st = launch_mintra<Tin, DK, CM, true>(a, ws);
-      if (st != GDR_OK) return st;
       if constexpr (CM == 64 && DK % 64 == 0) {
         const int seg = mseg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype);
-        if (seg) return launch_mscan_wide<DK, CM>(a, ws, seg);
+        if (seg) {
+          const int st = launch_mintra<Tin, DK, CM, true, false>(a, ws);
+          if (st != GDR_OK) return st;
+          return launch_mscan_wide<DK, CM>(a, ws, seg);
+        }
       }
+      const int st = launch_mintra<Tin, DK, CM, true>(a, ws);
+      if (st != GDR_OK) return st;
       if (!wide) return launch_mscan_rg<DK, 16, CM>(a, ws);
       return launch_mscan_rg<DK, 32, CM>(a, ws);
     }
