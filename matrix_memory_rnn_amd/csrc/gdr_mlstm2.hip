@@ -986,20 +986,22 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_rg_kernel(
 //   m' = max(m + F_g, mQ),   [C | n]' = e^{m + F_g - m'} [C | n] + e^{mQ - m'} [Q | nQ],
 // where (Q, nQ, mQ) is the segment's own end state from a zero start
 // (m = -inf): the page's stabiliser recurrence m_t = max(log f_t + m_{t-1}, i~_t)
-// unrolls to the same maximum either way. Three launches:
-//   MAP  pass: every segment but the last, from a zero start, state only;
-//   scan:      every segment from its start, h stored, the last segment
-//              writing (C, n, m)_T. A segment's workgroup forms its start in
-//              its prologue: (C0, n0, m0) with the maps of the segments
-//              before it applied in order. Where C_out, n_out or m_out
-//              overlaps its input, a copy of (C0, n0, m0) is made first (the
-//              last segment's final store could otherwise land before another
-//              segment has read the start).
+// unrolls to the same maximum either way. The chunks of a head are cut into a
+// short first segment and P segments of L chunks, and two launches of P
+// workgroups per (head, 64-column tile) run them:
+//   phase 0: segment 0 scanned from (C0, n0, m0) (h stored, its end state kept
+//            for the others) beside the maps of segments 1 .. P-1 (state
+//            only, from a zero start); segment 0 needs no map, and its length
+//            is chosen so it takes about as long as a map pass over L chunks;
+//   phase 1: segments 1 .. P scanned, each from segment 0's end state with the
+//            maps of the segments between applied in its prologue; the last
+//            one writes (C, n, m)_T.
+// C0 is read only in phase 0 and C_out written only in phase 1, so C_out may
+// be C0.
 // The normaliser n is fp32 throughout (no extra MFMA tile): the update waves
-// add e^{A_C - mu_C} sum_s K~^T[j][s] on the VALU and the readout waves form
-// q_t . n0 from their q fragments. The V tile of a chunk is loaded once per
-// workgroup (each update wave a quarter) and passed to all update waves
-// through LDS.
+// accumulate K~^T against a bf16(e^{A_C - mu_C}) operand and the readout waves
+// form q_t . n0 from their q fragments. The V tile of a chunk is loaded once
+// per workgroup and passed to all update waves through LDS.
 constexpr int kMSegTargetUnits = 256;   // workgroups the segmented scan aims for (one per CU)
 constexpr int kMWideVT = 64;
 
@@ -1016,11 +1018,18 @@ struct MWideSmem {
   static_assert(TOTAL <= 160 * 1024, "wide mLSTM scan LDS exceeds 160 KiB");
 };
 
+// One (head, segment, 64-column tile): chunks c0 .. c0 + nchunks - 1 of head
+// bh. Start (Cs, ns, ms) indexed by head (NULL: zero state, m = -inf), then
+// the first nmaps maps (slots m * BH + bh of Qmap, nQ, mF) applied in order.
+// MAP: state only, the end state, its stabiliser and the summed log-forget
+// to (Qo, nQo, mFo); otherwise h stored and the end state to (Cend, nend,
+// mend) (indexed by head) unless Cend is NULL.
 template <int DK, int CM, bool MAP>
-__global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
-    const char* __restrict__ ws, const float* __restrict__ Cst, const float* __restrict__ nst,
-    const float* __restrict__ mst, __bf16* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV,
-    int seg, float* __restrict__ Qmap, float* __restrict__ nQ, float* __restrict__ mF,
+__device__ __forceinline__ void mlstm_wide_body(
+    char* smem, const char* __restrict__ ws, int bh, int BH, int ntot, int c0, int nchunks, int vt0,
+    const float* __restrict__ Cs, const float* __restrict__ ns, const float* __restrict__ ms, int nmaps,
+    const float* __restrict__ Qmap, const float* __restrict__ nQ, const float* __restrict__ mF,
+    __bf16* __restrict__ h, float* Cend, float* nend, float* mend, float* Qo, float* nQo, float* mFo, int T, int DV,
     const __bf16* __restrict__ qin) {
   using L = MWideSmem<DK, CM>;
   constexpr int NS = kMScanRgSets;
@@ -1038,7 +1047,6 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
                 "wide mLSTM scan shape");
   typedef __attribute__((ext_vector_type(2))) uint32_t u2;
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   __bf16* S0T = (__bf16*)(smem + L::S0T);
   float* NLs = (float*)(smem + L::NL);
   char* VS = smem + L::VS;
@@ -1046,16 +1054,6 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int nvt = DV / kMWideVT;
-  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
-  const int ntot = (T + CM - 1) / CM;
-  const int nseg = (ntot + seg - 1) / seg;
-  const int nsl = MAP ? nseg - 1 : nseg;                // segments this launch walks
-  const int unit = lin / nvt, vt0 = (lin % nvt) * kMWideVT;
-  const int bh = unit / nsl, sg = unit % nsl;
-  const int BH = gridDim.x / (nvt * nsl);
-  const int c0 = sg * seg;
-  const int nchunks = ntot - c0 < seg ? ntot - c0 : seg;
   const MRec RL = mrec_layout(DK, DV, CM, 2, true);
   const char* wsh = ws + ((size_t)bh * ntot + c0) * RL.bytes;
   const __amdgpu_buffer_rsrc_t wr =
@@ -1068,13 +1066,11 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, voff, soff, 0));
   };
   const int l16 = 16 * lane;
-  const size_t slot = (size_t)sg * BH + bh;             // this segment's map slot (MAP)
-  // the stabiliser this segment starts from: m0 (or -inf), then each earlier
-  // segment's map; Cst, nst, mst hold (C0, n0, m0) or are NULL (zero start)
+  // the stabiliser this segment starts from: ms (or -inf), then each map
   float mprev = -INFINITY;
   if constexpr (!MAP) {
-    if (Cst != nullptr) mprev = mst[bh];
-    for (int gq = 0; gq < sg; ++gq) {
+    if (Cs != nullptr) mprev = ms[bh];
+    for (int gq = 0; gq < nmaps; ++gq) {
       const size_t sl = (size_t)gq * BH + bh;
       mprev = fmaxf(mprev + mF[2 * sl + 1], mF[2 * sl]);
     }
@@ -1247,22 +1243,22 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     auto cidx = [&](int jj, int vl, int e) { return (size_t)(16 * (uid + NU * jj) + 4 * g + e) * DV + vt0 + 16 * vl + c16; };
     auto nidx = [&](int jj) { return 16 * (uid + NU * jj) + 4 * g; };
     if constexpr (!MAP) {
-      if (Cst != nullptr) {
+      if (Cs != nullptr) {
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
-          nr[jj] = *(const f32x4*)(nst + (size_t)bh * DK + nidx(jj));
+          nr[jj] = *(const f32x4*)(ns + (size_t)bh * DK + nidx(jj));
 #pragma unroll
           for (int vl = 0; vl < NVL; ++vl)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] = Cst[(size_t)bh * DK * DV + cidx(jj, vl, e)];
+            for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] = Cs[(size_t)bh * DK * DV + cidx(jj, vl, e)];
         }
       }
       // the maps of the segments before this one, in order
-      float ms = Cst != nullptr ? mst[bh] : -INFINITY;
-      for (int gq = 0; gq < sg; ++gq) {
+      float mcur = Cs != nullptr ? ms[bh] : -INFINITY;
+      for (int gq = 0; gq < nmaps; ++gq) {
         const size_t sl = (size_t)gq * BH + bh;
-        const float mQ = mF[2 * sl], me = fmaxf(ms + mF[2 * sl + 1], mQ);
-        const float a = __expf(ms + mF[2 * sl + 1] - me), b = __expf(mQ - me);
+        const float mQ = mF[2 * sl], me = fmaxf(mcur + mF[2 * sl + 1], mQ);
+        const float a = __expf(mcur + mF[2 * sl + 1] - me), b = __expf(mQ - me);
         const float* Qs = Qmap + sl * DK * DV;
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
@@ -1274,7 +1270,7 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) Sacc[jj][vl][e] = a * Sacc[jj][vl][e] + b * Qs[cidx(jj, vl, e)];
         }
-        ms = me;
+        mcur = me;
       }
     }
     auto put_state = [&](int buf) {
@@ -1308,7 +1304,7 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
     constexpr bool kTouch = !MAP;   // the map pass reads less and ran slower with them
     const int tb = MAP ? RL.vt : 0;
     const int nlines = ((MAP ? RL.qf - RL.vt : RL.qf) + 127) / 128;
-    const int pl = ((lin % nvt) * NU + uid) * 64 + lane;
+    const int pl = ((vt0 / kMWideVT) * NU + uid) * 64 + lane;
     const int v_pf = tb + (pl < nlines ? pl : nlines - 1) * 128;
     auto touch = [&](int ch) { return __builtin_amdgcn_raw_buffer_load_b32(wr, v_pf, cbase(ch), 0); };
     uint32_t sink = 0, PFV[3] = {0u, 0u, 0u};
@@ -1375,7 +1371,7 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
 #pragma unroll
       for (int u = 0; u < 3; ++u) sink ^= PFV[u];
     }
-    if (sink == 0x7fc00001u && T < 0) mF[0] = 0.f;   // never true (T > 0): keeps the touches alive
+    if (sink == 0x7fc00001u && T < 0) h[0] = (__bf16)0.f;   // never true (T > 0): keeps the touches alive
     if constexpr (MAP) {
       // this segment's end state from a zero start, its stabiliser and F_g
 #pragma unroll
@@ -1385,14 +1381,14 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
         for (int vl = 0; vl < NVL; ++vl)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            Qmap[slot * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
-        if (c16 == 0 && vt0 == 0) *(f32x4*)(nQ + slot * DK + 16 * jt + 4 * g) = nr[jj];
+            Qo[(size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
+        if (c16 == 0 && vt0 == 0) *(f32x4*)(nQo + 16 * jt + 4 * g) = nr[jj];
       }
       if (uid == 0 && lane == 0 && vt0 == 0) {
-        mF[2 * slot] = mprev;
-        mF[2 * slot + 1] = Fsum;
+        mFo[0] = mprev;
+        mFo[1] = Fsum;
       }
-    } else if (C_out && sg == nseg - 1) {
+    } else if (Cend != nullptr) {
 #pragma unroll
       for (int jj = 0; jj < JPW; ++jj) {
         const int jt = uid + NU * jj;
@@ -1400,61 +1396,79 @@ __global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
         for (int vl = 0; vl < NVL; ++vl)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            C_out[(size_t)bh * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
-        if (c16 == 0 && vt0 == 0) *(f32x4*)(n_out + (size_t)bh * DK + 16 * jt + 4 * g) = nr[jj];
+            Cend[(size_t)bh * DK * DV + (size_t)(16 * jt + 4 * g + e) * DV + vt0 + 16 * vl + c16] = Sacc[jj][vl][e];
+        if (c16 == 0 && vt0 == 0) *(f32x4*)(nend + (size_t)bh * DK + 16 * jt + 4 * g) = nr[jj];
       }
-      if (uid == 0 && lane == 0 && vt0 == 0) m_out[bh] = mprev;
+      if (uid == 0 && lane == 0 && vt0 == 0) mend[bh] = mprev;
     }
   }
 }
 
-// Segment start states in order: slot 0 = (C0, n0, m0) (zero and -inf without
-// C0), slot g + 1 = the map of segment g applied to slot g. One thread per
-// element of a head's [C | n] (DK * DV + DK), grid (heads, element blocks).
-// The wide scan forms its starts itself; this kernel runs with nseg = 1, as
-// the copy of (C0, n0, m0) that an in-place call (C_out = C0) scans from.
-__global__ __launch_bounds__(256) void mlstm_seg_combine_kernel(
-    const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
-    const float* __restrict__ Qmap, const float* __restrict__ nQ, const float* __restrict__ mF, float* Cst,
-    float* nst, float* mst, int BH, int DK, int DV, int nseg) {
-  const int bh = blockIdx.y;
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  const int nC = DK * DV;
-  if (x >= nC + DK) return;
-  const bool isC = x < nC;
-  float ms = C0 != nullptr ? m0[bh] : -INFINITY;
-  float xs = C0 == nullptr ? 0.f : isC ? C0[(size_t)bh * nC + x] : n0[(size_t)bh * DK + (x - nC)];
-  auto put = [&](int sg, float val, float m) {
-    const size_t slot = (size_t)sg * BH + bh;
-    if (isC) Cst[slot * nC + x] = val;
-    else nst[slot * DK + (x - nC)] = val;
-    if (x == 0) mst[slot] = m;
-  };
-  put(0, xs, ms);
-  for (int sg = 0; sg + 1 < nseg; ++sg) {
-    const size_t slot = (size_t)sg * BH + bh;
-    const float mQ = mF[2 * slot], F = mF[2 * slot + 1];
-    const float me = fmaxf(ms + F, mQ);
-    const float q = isC ? Qmap[slot * nC + x] : nQ[slot * DK + (x - nC)];
-    xs = expf(ms + F - me) * xs + expf(mQ - me) * q;
-    ms = me;
-    put(sg + 1, xs, ms);
+// The two launches of the segmented wide scan (PHASE 0 and 1, see above):
+// grid B*H * P * (d_v / 64) workgroups; segment 0 has L0 chunks, segments
+// 1 .. P have L (the last one possibly fewer). E0 holds segment 0's end state:
+// [B*H][dk][dv], then [B*H][dk], then [B*H].
+template <int DK, int CM, int PHASE>
+__global__ __launch_bounds__(kMScanThreads, 1) void mlstm_scan_wide_kernel(
+    const char* __restrict__ ws, const float* __restrict__ C0, const float* __restrict__ n0,
+    const float* __restrict__ m0, __bf16* __restrict__ h, float* C_out, float* n_out, float* m_out, int T, int DV,
+    int L0, int L, float* __restrict__ Qmap, float* __restrict__ nQ, float* __restrict__ mF, float* __restrict__ E0,
+    const __bf16* __restrict__ qin) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nvt = DV / kMWideVT;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, nvt);
+  const int ntot = (T + CM - 1) / CM;
+  const int P = (ntot - L0 + L - 1) / L;               // segments after the first
+  const int unit = lin / nvt, vt0 = (lin % nvt) * kMWideVT;
+  const int bh = unit / P, sl = unit % P;
+  const int BH = gridDim.x / (nvt * P);
+  float* E0C = E0;
+  float* E0n = E0 + (size_t)BH * DK * DV;
+  float* E0m = E0n + (size_t)BH * DK;
+  if constexpr (PHASE == 0) {
+    if (sl == 0) {
+      mlstm_wide_body<DK, CM, false>(smem, ws, bh, BH, ntot, 0, L0, vt0, C0, n0, m0, 0, Qmap, nQ, mF, h, E0C, E0n,
+                                     E0m, nullptr, nullptr, nullptr, T, DV, qin);
+    } else {
+      const int c0 = L0 + (sl - 1) * L;
+      const size_t slot = (size_t)(sl - 1) * BH + bh;
+      mlstm_wide_body<DK, CM, true>(smem, ws, bh, BH, ntot, c0, ntot - c0 < L ? ntot - c0 : L, vt0, nullptr,
+                                    nullptr, nullptr, 0, Qmap, nQ, mF, h, nullptr, nullptr, nullptr,
+                                    Qmap + slot * DK * DV, nQ + slot * DK, mF + 2 * slot, T, DV, qin);
+    }
+  } else {
+    // segment sl + 1 from segment 0's end state and the maps of segments 1 .. sl
+    const int c0 = L0 + sl * L;
+    const bool last = sl == P - 1;
+    mlstm_wide_body<DK, CM, false>(smem, ws, bh, BH, ntot, c0, ntot - c0 < L ? ntot - c0 : L, vt0, E0C, E0n, E0m,
+                                   sl, Qmap, nQ, mF, h, last ? C_out : nullptr, last ? n_out : nullptr,
+                                   last ? m_out : nullptr, nullptr, nullptr, nullptr, T, DV, qin);
   }
 }
 
 // ------------------------------------------------------------------ host launch
-// The segmented wide scan's plan from the shapes alone: chunks per segment,
-// or 0 where the plain register scan is used (enough workgroups without
-// segments, short sequences, or shapes the wide scan does not take).
-static int mseg_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
-  if (!mlstm_fm(dtype, dk, dv, chunk, T) || chunk != 64 || dk % 64 != 0 || dv % kMWideVT != 0) return 0;
+// The segmented wide scan's plan from the shapes alone: P segments of L
+// chunks after a first segment of L0, or false where the register scan is
+// used (enough workgroups without segments, short sequences, or shapes the
+// wide scan does not take). P workgroups per (head, tile) in each launch; the
+// first segment, scanned beside the maps, is about a third of the others
+// (a map pass over a chunk costs about a third of a scan step).
+static bool mseg_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, int* L0, int* L) {
+  if (!mlstm_fm(dtype, dk, dv, chunk, T) || chunk != 64 || dk % 64 != 0 || dv % kMWideVT != 0) return false;
   const long long units = (long long)B * H * (dv / kMWideVT);
   const int ntot = (T + chunk - 1) / chunk;
-  if (units * 2 > kMSegTargetUnits || ntot < 32) return 0;
-  int nseg = (int)(kMSegTargetUnits / units);
-  if (nseg > ntot / 16) nseg = ntot / 16;
-  if (nseg < 2) return 0;
-  return (ntot + nseg - 1) / nseg;
+  if (units * 2 > kMSegTargetUnits || ntot < 32) return false;
+  int P = (int)(kMSegTargetUnits / units);
+  if (P > ntot / 12) P = ntot / 12;                  // segments of about 12 chunks or more
+  int l = (3 * ntot + 3 * P) / (3 * P + 1);          // ceil(3 ntot / (3P + 1))
+  int l0 = ntot - P * l;
+  if (l0 < 1) {
+    l = (ntot - 1) / P;
+    l0 = ntot - P * l;
+  }
+  *L0 = l0;
+  *L = l;
+  return true;
 }
 
 static size_t mrecords_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
@@ -1463,33 +1477,31 @@ static size_t mrecords_bytes(int B, int H, int T, int dk, int dv, int chunk, int
   return (size_t)B * H * nchunks * (size_t)mrec_layout(dk, dv, chunk, es, mlstm_fm(dtype, dk, dv, chunk, T)).bytes;
 }
 
-// Buffers of the segmented scan after the records (fp32): maps [nseg-1][BH]
-// of [dk][dv], [dk] and (mQ, F); a copy of (C0, n0, m0) for calls whose C_out
-// is C0: [BH] of [dk][dv], [dk] and m.
+// Buffers of the segmented scan after the records (fp32): maps [P-1][BH] of
+// [dk][dv], [dk] and (mQ, F); segment 0's end state: [BH][dk][dv], [BH][dk],
+// [BH].
 struct MSegBufs {
-  float *Q, *nQ, *mF, *Cst, *nst, *mst;
+  float *Q, *nQ, *mF, *E0;
   size_t bytes;
 };
-static MSegBufs mseg_bufs(char* base, int BH, int dk, int dv, int nseg) {
+static MSegBufs mseg_bufs(char* base, int BH, int dk, int dv, int P) {
   MSegBufs b;
-  const size_t nm = (size_t)(nseg - 1) * BH, ns = (size_t)BH;
+  const size_t nm = (size_t)(P - 1) * BH;
   float* p = (float*)base;
   b.Q = p;   p += nm * dk * dv;
   b.nQ = p;  p += nm * dk;
   b.mF = p;  p += 2 * nm;
-  b.Cst = p; p += ns * dk * dv;
-  b.nst = p; p += ns * dk;
-  b.mst = p; p += ns;
+  b.E0 = p;  p += (size_t)BH * (dk * dv + dk + 1);
   b.bytes = (size_t)((char*)p - base);
   return b;
 }
 
 size_t mlstm_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
   size_t n = mrecords_bytes(B, H, T, dk, dv, chunk, dtype);
-  const int seg = mseg_plan(B, H, T, dk, dv, chunk, dtype);
-  if (seg) {
-    const int ntot = (T + chunk - 1) / chunk, nseg = (ntot + seg - 1) / seg;
-    n = (n + 255) / 256 * 256 + mseg_bufs(nullptr, B * H, dk, dv, nseg).bytes;
+  int L0, L;
+  if (mseg_plan(B, H, T, dk, dv, chunk, dtype, &L0, &L)) {
+    const int ntot = (T + chunk - 1) / chunk, P = (ntot - L0 + L - 1) / L;
+    n = (n + 255) / 256 * 256 + mseg_bufs(nullptr, B * H, dk, dv, P).bytes;
   }
   return n;
 }
@@ -1546,52 +1558,31 @@ static int launch_mscan_rg(const MlstmArgs& a, const char* ws) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
-// Segmented wide scan: segment maps, start states, then every segment's scan.
+// Segmented wide scan: phase 0 (segment 0 and the maps), then phase 1.
 template <int DK, int CM>
-static int launch_mscan_wide(const MlstmArgs& a, char* ws, int seg) {
-  using L = MWideSmem<DK, CM>;
-  auto kmap = mlstm_scan_wide_kernel<DK, CM, true>;
-  auto kscan = mlstm_scan_wide_kernel<DK, CM, false>;
-  if (!allow_lds((const void*)kmap, L::TOTAL) || !allow_lds((const void*)kscan, L::TOTAL)) return GDR_ERR_LAUNCH;
+static int launch_mscan_wide(const MlstmArgs& a, char* ws, int L0, int L) {
+  using L_ = MWideSmem<DK, CM>;
+  auto k0 = mlstm_scan_wide_kernel<DK, CM, 0>;
+  auto k1 = mlstm_scan_wide_kernel<DK, CM, 1>;
+  if (!allow_lds((const void*)k0, L_::TOTAL) || !allow_lds((const void*)k1, L_::TOTAL)) return GDR_ERR_LAUNCH;
   const int BH = a.B * a.H, nvt = a.dv / kMWideVT;
-  const int ntot = (a.T + CM - 1) / CM, nseg = (ntot + seg - 1) / seg;
+  const int ntot = (a.T + CM - 1) / CM, P = (ntot - L0 + L - 1) / L;
   const size_t rec = (mrecords_bytes(a.B, a.H, a.T, DK, a.dv, CM, GDR_BF16) + 255) / 256 * 256;
-  const MSegBufs sb = mseg_bufs(ws + rec, BH, DK, a.dv, nseg);
+  const MSegBufs sb = mseg_bufs(ws + rec, BH, DK, a.dv, P);
   hipStream_t st = (hipStream_t)a.stream;
   const char* wsc = ws;
-  const float* nulf = nullptr;
+  const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
   __bf16* h = (__bf16*)a.h;
   float *Co = a.C_out, *no = a.n_out, *mo = a.m_out;
-  float *Q = sb.Q, *nQ = sb.nQ, *mF = sb.mF, *Cst = sb.Cst, *nst = sb.nst, *mst = sb.mst;
-  int T = a.T, DV = a.dv, DKi = DK, BHi = BH;
+  float *Q = sb.Q, *nQ = sb.nQ, *mF = sb.mF, *E0 = sb.E0;
+  int T = a.T, DV = a.dv;
   const __bf16* qin = (const __bf16*)a.q;
-  {
-    void* args[] = {&wsc, &nulf, &nulf, &nulf, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF, &qin};
-    if (hipLaunchKernel((const void*)kmap, dim3(BH * (nseg - 1) * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-  }
-  // the scan reads (C0, n0, m0) in every segment's prologue; with C_out = C0
-  // it reads a copy instead (nseg = 1: the combine kernel copies slot 0 only)
-  const float *cC = a.C0, *cn = a.n0, *cm = a.m0;
-  if (a.C0 != nullptr && a.C_out == a.C0) {
-    const float *C0 = a.C0, *n0 = a.n0, *m0 = a.m0;
-    const float *cQ = Q, *cnQ = nQ, *cmF = mF;
-    int one = 1;
-    void* args[] = {&C0, &n0, &m0, &cQ, &cnQ, &cmF, &Cst, &nst, &mst, &BHi, &DKi, &DV, &one};
-    const dim3 grid((DK * a.dv + DK + 255) / 256, BH);
-    if (hipLaunchKernel((const void*)mlstm_seg_combine_kernel, grid, dim3(256), args, 0, st) != hipSuccess)
-      return GDR_ERR_LAUNCH;
-    cC = Cst;
-    cn = nst;
-    cm = mst;
-  }
-  {
-    void* args[] = {&wsc, &cC, &cn, &cm, &h, &Co, &no, &mo, &T, &DV, &seg, &Q, &nQ, &mF, &qin};
-    if (hipLaunchKernel((const void*)kscan, dim3(BH * nseg * nvt), dim3(kMScanThreads), args, L::TOTAL, st) !=
-        hipSuccess)
-      return GDR_ERR_LAUNCH;
-  }
+  void* args[] = {&wsc, &C0, &n0, &m0, &h, &Co, &no, &mo, &T, &DV, &L0, &L, &Q, &nQ, &mF, &E0, &qin};
+  const dim3 grid(BH * P * nvt);
+  if (hipLaunchKernel((const void*)k0, grid, dim3(kMScanThreads), args, L_::TOTAL, st) != hipSuccess)
+    return GDR_ERR_LAUNCH;
+  if (hipLaunchKernel((const void*)k1, grid, dim3(kMScanThreads), args, L_::TOTAL, st) != hipSuccess)
+    return GDR_ERR_LAUNCH;
   return GDR_OK;
 }
 
@@ -1602,11 +1593,11 @@ static int mlstm_pair(const MlstmArgs& a, char* ws) {
   if constexpr (std::is_same<Tin, __bf16>::value && DK % 32 == 0 && CM % 32 == 0) {
     if (mlstm_fm(a.dtype, DK, a.dv, CM, a.T)) {
       if constexpr (CM == 64 && DK % 64 == 0) {
-        const int seg = mseg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype);
-        if (seg) {
+        int L0, L;
+        if (mseg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype, &L0, &L)) {
           const int st = launch_mintra<Tin, DK, CM, true, false>(a, ws);
           if (st != GDR_OK) return st;
-          return launch_mscan_wide<DK, CM>(a, ws, seg);
+          return launch_mscan_wide<DK, CM>(a, ws, L0, L);
         }
       }
       const int st = launch_mintra<Tin, DK, CM, true>(a, ws);

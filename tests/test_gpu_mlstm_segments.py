@@ -1,15 +1,17 @@
 """The segmented wide mLSTM scan (HIP, gfx950) against the float64 oracle.
 
 With few (b, h, 64-column tile) workgroups and at least 32 chunks of 64, the
-two-kernel mLSTM forward cuts each head's chunks into segments. The chunk map
-of the mLSTM is affine with a scalar decay ("Exponential gates and matrix
-memory: xLSTM and RWKV-7", §13.4: the state is decayed by the forget gate and
-written by k^T v, with the max-log stabiliser), so every segment's end state
-from a zero start is found side by side, the segment start states follow in
-order, and the segments are then scanned side by side from them. The plan
-depends on the shapes only; the shapes below take it (bf16, C = 64, d_v a
-multiple of 64, B*H*d_v/64 at most 128). The fused entry point never
-segments, so it serves as the plain scan to compare with."""
+two-kernel mLSTM forward cuts each head's chunks into a short first segment
+and P segments of L chunks. The chunk map of the mLSTM is affine with a
+scalar decay ("Exponential gates and matrix memory: xLSTM and RWKV-7", §13.4:
+the state is decayed by the forget gate and written by k^T v, with the
+max-log stabiliser), so the first segment is scanned beside the end states of
+segments 1 .. P-1 from a zero start, and segments 1 .. P are then scanned side
+by side, each from the first segment's end state with the maps between
+applied. The plan depends on the shapes only; the shapes below take it (bf16,
+C = 64, d_k and d_v multiples of 64, B*H*d_v/64 at most 128, at least 32
+chunks). The fused entry point never segments, so it serves as the plain scan
+to compare with."""
 import numpy as np
 import pytest
 
@@ -37,10 +39,10 @@ def _args(d, state=None):
     return (t("q"), t("k"), t("v"), g("i_tilde"), g("f_tilde"), *st)
 
 
-@pytest.mark.parametrize("B,H,T,dk,dv,init", [(1, 2, 64 * 40 + 13, 64, 64, False),     # 2 segments of 21
-                                              (1, 1, 64 * 70, 128, 128, True),        # 4 segments of 18
-                                              (2, 2, 64 * 64 + 5, 256, 256, True),    # 16 units: 4 segments
-                                              (1, 1, 64 * 130 + 37, 64, 64, False)])  # 8 segments of 17
+@pytest.mark.parametrize("B,H,T,dk,dv,init", [(1, 2, 64 * 40 + 13, 64, 64, False),     # L0 2, 3 x 13, ragged
+                                              (1, 1, 64 * 70, 128, 128, True),        # L0 5, 5 x 13
+                                              (2, 2, 64 * 64 + 5, 256, 256, True),    # L0 5, 5 x 12, ragged
+                                              (1, 1, 64 * 130 + 37, 64, 64, False)])  # L0 1, 10 x 13, ragged
 def test_segmented_mlstm_parity(B, H, T, dk, dv, init):
     import torch
     import matrix_memory_rnn_amd as gdr
@@ -67,9 +69,9 @@ def test_segmented_mlstm_parity(B, H, T, dk, dv, init):
 
 
 def test_segmented_mlstm_state_in_place():
-    """C_out may be C0 on the segmented path too: the segment starts are copied
-    from C0 before any segment is scanned, so the in-place call equals the one
-    with separate outputs bit for bit."""
+    """C_out may be C0 on the segmented path too: C0 is read only by the first
+    launch and C_out written only by the second, so the in-place call equals
+    the one with separate outputs bit for bit."""
     import torch
     import matrix_memory_rnn_amd as gdr
     B, H, T, dk, dv = 1, 2, 64 * 48, 64, 128
