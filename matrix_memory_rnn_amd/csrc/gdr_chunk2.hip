@@ -2014,7 +2014,9 @@ __global__ __launch_bounds__(256) void gdn2_chunk_seg_combine_kernel(const float
 #pragma unroll
       for (int i = 0; i < 4; ++i) *(f32x4*)&St[r0 + i][c0] = sv[i];
     }
-    for (int x = tid; x < DK * DK / 4; x += 256) {     // P_g: columns DV .. DV + DK of the augmented rows
+    // P_g: columns DV .. DV + DK of the augmented rows; unrolled, so all of
+    // its loads are in flight together
+    GDR_STAGE_FOR(x, DK * DK / 4, 256) {
       const int rr = x / (DK / 4), cc = 4 * (x % (DK / 4));
       *(f32x4*)&Pl[rr][cc] = *(const f32x4*)(aug + (size_t)rr * (DV + DK) + DV + cc);
     }
