@@ -1490,7 +1490,7 @@ static MSegBufs mseg_bufs(char* base, int BH, int dk, int dv, int P) {
   float* p = (float*)base;
   b.Q = p;   p += nm * dk * dv;
   b.nQ = p;  p += nm * dk;
-  b.mF = p;  p += 2 * nm;
+  b.mF = p;  p += (2 * nm + 3) / 4 * 4;                 // padded: E0's n part takes 16-byte accesses
   b.E0 = p;  p += (size_t)BH * (dk * dv + dk + 1);
   b.bytes = (size_t)((char*)p - base);
   return b;

@@ -108,3 +108,34 @@ def test_mlstm_fwd_ws_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(h_g, h_e)
+
+
+def test_mlstm_fwd_ws_segmented_graph_replays():
+    """The segmented wide mLSTM scan (two launches, segment maps and the first
+    segment's end state in the workspace) under capture, with an initial state
+    and the final (C, n, m): every replay equals the eager call."""
+    import torch
+    import matrix_memory_rnn_amd as gdr
+    B, H, T, dk, dv, C = 1, 2, 64 * 40 + 13, 64, 128, 64
+    d = mlstm_inputs(B, H, T, dk, dv, seed=7, dtype="bf16")
+    q, k, v = (dev(d[n], "bf16") for n in ("q", "k", "v"))
+    it, ft = dev(d["i_tilde"]), dev(d["f_tilde"])
+    rng = np.random.default_rng(7)
+    C0 = dev(rng.standard_normal((B, H, dk, dv)))
+    n0 = dev(np.abs(rng.standard_normal((B, H, dk))))
+    m0 = dev(rng.uniform(-1, 2, (B, H)))
+    ws = torch.empty(gdr.gdr_mlstm_workspace_size(B, H, T, dk, dv, C, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    h_e, C_e, n_e, m_e = gdr.gdr_mlstm_fwd_ws(q, k, v, it, ft, C0, n0, m0, chunk=C, workspace=ws)
+    h_g, C_g, n_g, m_g = torch.empty_like(h_e), torch.empty_like(C_e), torch.empty_like(n_e), torch.empty_like(m_e)
+    g = _capture(lambda: gdr.gdr_mlstm_fwd_ws(q, k, v, it, ft, C0, n0, m0, chunk=C, h=h_g, C_out=C_g, n_out=n_g,
+                                               m_out=m_g, workspace=ws))
+    for r in range(3):
+        for x in (h_g, C_g, n_g, m_g):
+            x.fill_(float("nan"))
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"[graph] segmented mLSTM replay {r}")
+        assert torch.equal(h_g, h_e) and torch.equal(C_g, C_e) and torch.equal(n_g, n_e) and torch.equal(m_g, m_e)
