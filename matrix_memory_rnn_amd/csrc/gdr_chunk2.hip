@@ -1979,69 +1979,62 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
 
 // Segment start states: per (b, h, 32-column value tile), in segment order,
 // Sseg[g] = S_start(g) and S_start(g + 1) = P_g S_start(g) + Q_g (fp32).
-// Each thread holds a 4 x 4 block of the d_k x 32 tile; P_g and the tile go
-// through LDS.
+// The products run on the fp32 matrix cores (16x16x4, fp32 products and
+// accumulation): P_g in LDS as [j][k], the state tile transposed as [v][k];
+// each of the four waves holds whole 16 x 16 output tiles in accumulator
+// layout (entry e of a lane: row 16 jt + 4 (lane / 16) + e, column
+// 16 vl + lane % 16).
 template <int DK>
 __global__ __launch_bounds__(256) void gdn2_chunk_seg_combine_kernel(const float* __restrict__ Saug,
                                                                       const float* __restrict__ S0,
                                                                       float* __restrict__ Sseg, int DV,
                                                                       int nseg) {
-  constexpr int NRQ = DK / 4;                          // row quads; 8 column quads
-  static_assert(NRQ * 8 <= 256, "one 4 x 4 block per thread");
-  __shared__ __attribute__((aligned(16))) float Pl[DK][DK + 4];
-  __shared__ __attribute__((aligned(16))) float St[DK][36];
-  const int tid = threadIdx.x;
+  constexpr int LP = DK + 4;                           // LDS row pitch (floats)
+  constexpr int NT = DK / 8, TPW = NT / 4;             // 16 x 16 tiles of the DK x 32 tile, per wave
+  static_assert(NT % 4 == 0, "whole tiles per wave");
+  __shared__ __attribute__((aligned(16))) float Pl[DK][LP];
+  __shared__ __attribute__((aligned(16))) float St[32][LP];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g4 = lane >> 4, c16 = lane & 15;
   const int nvt = DV / 32;
   const int bh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
   const int BH = gridDim.x / nvt;
-  const bool act = tid < NRQ * 8;
-  const int rq = tid >> 3, cq = tid & 7;
-  const int r0 = 4 * rq, c0 = 4 * cq, col = 32 * vt + c0;
-  f32x4 sv[4];
+  // element e of this lane's entry of tile i: row, column of the DK x DV state
+  auto row = [&](int i, int e) { return 16 * ((wid + 4 * i) >> 1) + 4 * g4 + e; };
+  auto col = [&](int i) { return 32 * vt + 16 * ((wid + 4 * i) & 1) + c16; };
+  f32x4 sv[TPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    sv[i] = (act && S0) ? *(const f32x4*)(S0 + ((size_t)bh * DK + r0 + i) * DV + col) : f4zero();
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[i][e] = S0 ? S0[((size_t)bh * DK + row(i, e)) * DV + col(i)] : 0.f;
   for (int g = 0; g < nseg; ++g) {
     float* dst = Sseg + ((size_t)g * BH + bh) * DK * DV;
-    if (act) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(f32x4*)(dst + (size_t)(r0 + i) * DV + col) = sv[i];
-    }
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(size_t)row(i, e) * DV + col(i)] = sv[i][e];
     if (g == nseg - 1) break;
     const float* aug = Saug + seg_aug_off(g, bh, BH, DK, DV);
     __syncthreads();                                   // the previous step's reads of Pl / St are done
-    if (act) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(f32x4*)&St[r0 + i][c0] = sv[i];
-    }
+    for (int i = 0; i < TPW; ++i) *(f32x4*)&St[col(i) - 32 * vt][row(i, 0)] = sv[i];
     // P_g: columns DV .. DV + DK of the augmented rows; unrolled, so all of
     // its loads are in flight together
     GDR_STAGE_FOR(x, DK * DK / 4, 256) {
       const int rr = x / (DK / 4), cc = 4 * (x % (DK / 4));
       *(f32x4*)&Pl[rr][cc] = *(const f32x4*)(aug + (size_t)rr * (DV + DK) + DV + cc);
     }
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)                       // Q_g
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] = aug[(size_t)row(i, e) * (DV + DK) + col(i)];
     __syncthreads();
-    if (act) {
-      f32x4 acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = *(const f32x4*)(aug + (size_t)(r0 + i) * (DV + DK) + col);   // Q_g
-      for (int j4 = 0; j4 < DK; j4 += 4) {
-        f32x4 sr[4], pr[4];
+    for (int i = 0; i < TPW; ++i)
+      tile_nt(acc[i], &Pl[0][0], LP, 16 * ((wid + 4 * i) >> 1), &St[0][0], LP, 16 * ((wid + 4 * i) & 1), DK, lane);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          sr[x] = *(const f32x4*)&St[j4 + x][c0];
-          pr[x] = *(const f32x4*)&Pl[r0 + x][j4];
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] += pr[i][x] * sr[x][e];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = acc[i];
-    }
+    for (int i = 0; i < TPW; ++i) sv[i] = acc[i];
   }
 }
 
