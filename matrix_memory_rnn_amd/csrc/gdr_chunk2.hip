@@ -1780,7 +1780,8 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hc[(size_t)(8 * q + e) * DV] = Sacc[4 * q + e];
+            for (int e = 0; e < 4; ++e)   // non-temporal (4K backward 2.49 -> 2.46 ms)
+              __builtin_nontemporal_store(Sacc[4 * q + e], &hc[(size_t)(8 * q + e) * DV]);
         }
         // entry 4q + e is row 32 J2 + 8q + 4h + e, whose pi_C lane 8q + 4h + e
         // holds: one lane permute per entry (the constant part of the lane
