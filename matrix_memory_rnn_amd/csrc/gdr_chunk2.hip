@@ -63,6 +63,11 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u2_t;
 // record back runs 124 -> 121 us with the intra kernel unchanged (nt on the
 // 16-byte stores as well slowed the intra kernel by a fifth).
 constexpr int kRecNt = 2;   // cache-policy operand of the buffer stores: nt
+// The intra kernel's input loads are non-temporal too (each input row is read
+// once): with the record stores above, intra 129 -> 116 us and the scan after
+// it 120 -> 129 us, 0.2497 -> 0.2451 ms per 4K step (interleaved runs; with
+// plain record stores the scan lost more than the intra kernel gained).
+constexpr int kInNt = 2;
 template <typename E> struct RecSt;
 template <> struct RecSt<float> {
   __amdgpu_buffer_rsrc_t r;
@@ -276,22 +281,22 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         const __amdgpu_buffer_rsrc_t ra = rs(alpha, sK, nbK), rk = rs(k, sK, nbK);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          xa[r] = __builtin_amdgcn_raw_buffer_load_b32(ra, vo + r * DK * ES, 0, 0);
-          xk[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo + r * DK * ES, 0, 0);
+          xa[r] = __builtin_amdgcn_raw_buffer_load_b32(ra, vo + r * DK * ES, 0, kInNt);
+          xk[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo + r * DK * ES, 0, kInNt);
         }
       }
       if (parts & 2) {
         const __amdgpu_buffer_rsrc_t rb = rs(bgate, sK, nbK), rq = rs(q, sK, nbK);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          xb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo + r * DK * ES, 0, 0);
-          xq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo + r * DK * ES, 0, 0);
+          xb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo + r * DK * ES, 0, kInNt);
+          xq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo + r * DK * ES, 0, kInNt);
         }
         if constexpr (GATED) {
           // no z_q: a buffer of zero records, every load reads zero
           const __amdgpu_buffer_rsrc_t rz = zq ? rs(zq, sK, nbK) : rs(q, 0, 0u);
 #pragma unroll
-          for (int r = 0; r < 8; ++r) xz[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, vo + r * DK * ES, 0, 0);
+          for (int r = 0; r < 8; ++r) xz[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, vo + r * DK * ES, 0, kInNt);
         }
       }
       if (parts & 4) {
@@ -302,8 +307,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
           // items past the tile read past the buffer's end (zero)
           const int vv = idx < nvi ? ((tb + vrow) * DV + vcol) * ES : 0x7ffffff0;
-          xv[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rv, vv, 0, 0));
-          xw[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rw, vv, 0, 0));
+          xv[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rv, vv, 0, kInNt));
+          xw[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rw, vv, 0, kInNt));
         }
       }
     } else {
