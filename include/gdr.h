@@ -362,9 +362,17 @@ int gdr_mlstm_fwd(const void* q, const void* k, const void* v,
  * 3*C float32, rounded up to 16 bytes; with bfloat16 inputs, d_k and C
  * multiples of 32 and a head's records under 2 GiB, the record also holds
  * a copy of the chunk's q (C*dk elements) and its matrices are stored in
- * MFMA tile order. gdr_mlstm_workspace_size reports the size for the given
- * shapes. Workspace rules as for gdr_chunk_fwd_ws. With float32 inputs d_v
- * must be at most 128 here.
+ * MFMA tile order. With few heads and long sequences (bfloat16, C = 64, d_k
+ * and d_v multiples of 64, B*H*d_v/64 at most 128, at least 32 chunks) pass 2
+ * runs segmented: the chunk map is scalar-decay affine, so a short first
+ * segment is scanned beside the end states of the middle segments from a
+ * zero start, and the remaining segments then run side by side from the
+ * first one's end state with those maps applied; the q copy is then not
+ * written (the scan reads q from the input) and the workspace also holds the
+ * maps and the first segment's end state (float32). C_out may be C0 on every
+ * path. gdr_mlstm_workspace_size reports the size for the given shapes (the
+ * plan depends on the shapes only). Workspace rules as for gdr_chunk_fwd_ws.
+ * With float32 inputs d_v must be at most 128 here.
  */
 int gdr_mlstm_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
                              int dtype, size_t* bytes);
