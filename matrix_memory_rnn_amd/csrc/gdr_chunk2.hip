@@ -200,7 +200,11 @@ struct IntraSmem {
 // 2 gate_sigmoid, gate_sigmoid); q is read as the gain-modulated query
 // gamma * q with gamma = gstat[h] * 2 sigmoid(z_q) (zq NULL: z_q = 0; gstat
 // NULL: ones), and alog[h] is the head's log-rate.
-template <typename Tin, int DK, int CM, bool FM, bool GATED>
+// INNT: the bf16 input loads take the non-temporal cache policy (kInNt). The
+// launcher turns it off where the sequence-segmented scan follows: there the
+// segment pass reading the records lost more (32K workload, 0.625-0.638 ms
+// per step with plain loads against 0.633-0.645).
+template <typename Tin, int DK, int CM, bool FM, bool GATED, bool INNT = true>
 __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ alpha, const Tin* __restrict__ bgate, const Tin* __restrict__ wgate,
@@ -281,22 +285,22 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
         const __amdgpu_buffer_rsrc_t ra = rs(alpha, sK, nbK), rk = rs(k, sK, nbK);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          xa[r] = __builtin_amdgcn_raw_buffer_load_b32(ra, vo + r * DK * ES, 0, kInNt);
-          xk[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo + r * DK * ES, 0, kInNt);
+          xa[r] = __builtin_amdgcn_raw_buffer_load_b32(ra, vo + r * DK * ES, 0, INNT ? kInNt : 0);
+          xk[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo + r * DK * ES, 0, INNT ? kInNt : 0);
         }
       }
       if (parts & 2) {
         const __amdgpu_buffer_rsrc_t rb = rs(bgate, sK, nbK), rq = rs(q, sK, nbK);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          xb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo + r * DK * ES, 0, kInNt);
-          xq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo + r * DK * ES, 0, kInNt);
+          xb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, vo + r * DK * ES, 0, INNT ? kInNt : 0);
+          xq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo + r * DK * ES, 0, INNT ? kInNt : 0);
         }
         if constexpr (GATED) {
           // no z_q: a buffer of zero records, every load reads zero
           const __amdgpu_buffer_rsrc_t rz = zq ? rs(zq, sK, nbK) : rs(q, 0, 0u);
 #pragma unroll
-          for (int r = 0; r < 8; ++r) xz[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, vo + r * DK * ES, 0, kInNt);
+          for (int r = 0; r < 8; ++r) xz[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, vo + r * DK * ES, 0, INNT ? kInNt : 0);
         }
       }
       if (parts & 4) {
@@ -307,8 +311,8 @@ __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
           const int vrow = idx / (DV / 8), vcol = (idx % (DV / 8)) * 8;
           // items past the tile read past the buffer's end (zero)
           const int vv = idx < nvi ? ((tb + vrow) * DV + vcol) * ES : 0x7ffffff0;
-          xv[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rv, vv, 0, kInNt));
-          xw[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rw, vv, 0, kInNt));
+          xv[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rv, vv, 0, INNT ? kInNt : 0));
+          xw[i] = __builtin_bit_cast(typename RW::R8, __builtin_amdgcn_raw_buffer_load_b128(rw, vv, 0, INNT ? kInNt : 0));
         }
       }
     } else {
@@ -2088,8 +2092,14 @@ size_t chunk_ws_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype,
 template <typename Tin, int DK, int CM, bool FM, bool GATED>
 static int launch_intra_g(const ChunkArgs& a, char* ws) {
   using L = IntraSmem<Tin, DK, CM>;
-  auto kern = gdn2_chunk_intra_kernel<Tin, DK, CM, FM, GATED>;
-  if (!allow_lds((const void*)kern, L::TOTAL)) return GDR_ERR_LAUNCH;
+  const void* kern = (const void*)gdn2_chunk_intra_kernel<Tin, DK, CM, FM, GATED, true>;
+  if constexpr (FM) {
+    // plain input loads where the segmented scan follows (the plan depends on
+    // the shapes alone, so the intra and scan calls agree)
+    if (!a.no_seg && seg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype) != 0)
+      kern = (const void*)gdn2_chunk_intra_kernel<Tin, DK, CM, FM, GATED, false>;
+  }
+  if (!allow_lds(kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   int nchunks = (a.T + CM - 1) / CM;
   int nitems = a.B * a.H * nchunks;
   // one resident workgroup per CU, each walking items with a stride of the grid
@@ -2101,8 +2111,7 @@ static int launch_intra_g(const ChunkArgs& a, char* ws) {
   const float *alog = a.a_log, *gst = a.gamma_stat;
   int T = a.T, DV = a.dv, H = a.H;
   void* args[] = {&q, &k, &v, &al, &bg, &wg, &ws, &T, &DV, &nchunks, &nitems, &zq, &alog, &gst, &H};
-  hipError_t e = hipLaunchKernel((const void*)kern, dim3(grid), dim3(kIntraThreads), args, L::TOTAL,
-                                 (hipStream_t)a.stream);
+  hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kIntraThreads), args, L::TOTAL, (hipStream_t)a.stream);
   return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
 }
 
