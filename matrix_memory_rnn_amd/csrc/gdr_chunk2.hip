@@ -1835,10 +1835,12 @@ __global__ __launch_bounds__(kScanFmThreads, 1) void gdn2_chunk_scan_fm_kernel(
 // (a segment g) maps its start state affinely, S_end = P_g S_start + Q_g, and
 // a head with few value tiles but many chunks can walk its segments side by
 // side:
-//   seg_state:   every (b, h, segment but the last, 32-column tile of [Q | P]) walks the
-//                segment from [0 | I]: the Q tiles with the record's U, the P
-//                tiles with U = 0 (d_k identity columns carried through the
-//                homogeneous map), giving [Q_g | P_g] (fp32);
+//   seg_state:   every (b, h, segment but the last, one or two 32-column tiles of
+//                [Q | P]) walks the segment from [0 | I]: the Q tiles with the
+//                record's U, the P tiles with U = 0 (d_k identity columns
+//                carried through the homogeneous map), giving [Q_g | P_g]
+//                (fp32); two tiles per workgroup read the chunk's Y and K~^T
+//                once for both;
 //   seg_combine: per (b, h, value tile), S_start(g + 1) = P_g S_start(g) + Q_g
 //                in order over the segments, from S_start(0) = S0;
 //   the F-order scan then walks every segment from its start state and
@@ -1853,27 +1855,31 @@ __host__ __device__ __forceinline__ size_t seg_aug_off(int g, int bh, int BH, in
 
 constexpr int kSegThreads = 64 * 6;   // seg_state: V~ waves (C/32) and state waves (d_k/32), at most 6
 
-template <int DK, int CM>
+template <int DK, int CM, int NTW>
 __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const char* __restrict__ ws,
                                                                             float* __restrict__ Saug, int T,
                                                                             int DV, int seg) {
   constexpr int NI2 = CM / 32, NJ2 = DK / 32, KSD = DK / 16, KSC = CM / 16;
   constexpr int LDK = DK + 8, LDC = CM + 8;
   static_assert(DK % 32 == 0 && CM % 32 == 0 && NJ2 <= 4 && NI2 <= 2, "F-order segment shape");
-  __shared__ __attribute__((aligned(16))) __bf16 S0T[32 * LDK];   // bf16 copy of the state tile, [col][j]
-  __shared__ __attribute__((aligned(16))) __bf16 VTT[32 * LDC];   // V~^T [col][t]
+  static_assert(NTW == 1 || NTW == 2, "one or two 32-column tiles per workgroup");
+  // bf16 copy of the state tiles, [col][j], and V~^T [col][t]; NTW tiles side by side
+  __shared__ __attribute__((aligned(16))) __bf16 S0T[NTW * 32 * LDK];
+  __shared__ __attribute__((aligned(16))) __bf16 VTT[NTW * 32 * LDC];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
-  const int nvt = DV / 32, ntile = nvt + DK / 32;
+  const int nvt = DV / 32, ntile = nvt + DK / 32, ngrp = ntile / NTW;
   // the maps of segments 0 .. nseg - 2 (the last segment's map is never used)
   const int ntot = (T + CM - 1) / CM, nseg = (ntot + seg - 1) / seg, nmap = nseg - 1;
-  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, ntile);
-  const int unit = lin / ntile, tile = lin % ntile;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x, ngrp);
+  const int unit = lin / ngrp, tile0 = NTW * (lin % ngrp);
   const int bh = unit / nmap, sg = unit % nmap;
-  const int BH = gridDim.x / (ntile * nmap);
-  const bool ptile = tile >= nvt;                      // a column tile of P (U = 0, identity start)
+  const int BH = gridDim.x / (ngrp * nmap);
+  // column tiles of P (U = 0, identity start); with NTW = 2 the host keeps
+  // nvt even, so both tiles of a workgroup are of one kind
+  const bool ptile = tile0 >= nvt;
   const int c0 = sg * seg, nch = ntot - c0 < seg ? ntot - c0 : seg;
   const RecLayout RL = rec_layout(DK, DV, CM, 2);
   const char* wsh = ws + ((size_t)bh * ntot + c0) * RL.bytes;
@@ -1885,8 +1891,8 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
   // past the segment's last chunk the loads repeat it (never used)
   auto cbase = [&](int ch) { return (ch < nch ? ch : nch - 1) * RL.bytes; };
   const int l16 = lane * 16;
-  auto s0frag = [&](int s) { return *(const u32x4*)(S0T + r * LDK + 16 * s + 8 * h); };
-  auto vfrag = [&](int s) { return *(const u32x4*)(VTT + r * LDC + 16 * s + 8 * h); };
+  auto s0frag = [&](int t, int s) { return *(const u32x4*)(S0T + (32 * t + r) * LDK + 16 * s + 8 * h); };
+  auto vfrag = [&](int t, int s) { return *(const u32x4*)(VTT + (32 * t + r) * LDC + 16 * s + 8 * h); };
   // each role walks the chunks with two register sets (the next chunk's
   // operands load while this one's are used), unrolled by hand over the two
   // sets with a single exit so the wait counts stay exact
@@ -1902,17 +1908,18 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
   if (wid < NI2) {
     // ================= V: V~ rows 32 wid .. = U - Y S (U = 0 for P tiles) -> V~^T in LDS
     const int I2 = wid;
-    u32x4 RY[2][KSD], RU[2][2];
+    u32x4 RY[2][KSD], RU[2][NTW][2];
     // P tiles read U at an offset past the buffer's end: the loads return zero
     // (and every path issues the same loads)
     const int ub = ptile ? 0x7ffffff0 : lane * 32;
-    const int uo = RL.ut + ((ptile ? 0 : tile) * NI2 + I2) * 2048;
-    auto load = [&](int ch, u32x4* Y, u32x4* U) {
+    auto load = [&](int ch, u32x4* Y, u32x4 (*U)[2]) {
       const int cb = cbase(ch);
 #pragma unroll
       for (int s = 0; s < KSD; ++s) Y[s] = ld16(l16, cb + RL.y + I2 * KSD * 1024 + 1024 * s);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) U[s] = ld16(ub, cb + uo + 16 * s);
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) U[t][s] = ld16(ub, cb + RL.ut + ((ptile ? 0 : tile0 + t) * NI2 + I2) * 2048 + 16 * s);
     };
     __syncthreads();                                    // initial state copy written
     __builtin_amdgcn_s_waitcnt(0);
@@ -1920,26 +1927,32 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
     walk([&](int ch, auto Uc) {
       constexpr int u = decltype(Uc)::value;
       load(ch + 1, RY[1 - u], RU[1 - u]);
-      f32x16 acc = f16zero();
+      f32x16 acc[NTW];
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) acc = mma32(RY[u][s], s0frag(s), acc);
+      for (int t = 0; t < NTW; ++t) acc[t] = f16zero();
+#pragma unroll
+      for (int s = 0; s < KSD; ++s)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[t] = mma32(RY[u][s], s0frag(t, s), acc[t]);
       typedef __attribute__((ext_vector_type(2))) uint32_t u2;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4& up = RU[u][q >> 1];
-        const f32x4 uu = Raw<__bf16>::un4(u2{up[2 * (q & 1)], up[2 * (q & 1) + 1]});
-        In<__bf16>::store4(VTT + r * LDC + 32 * I2 + 8 * q + 4 * h,
-                           f32x4{uu[0] - acc[4 * q], uu[1] - acc[4 * q + 1], uu[2] - acc[4 * q + 2],
-                                 uu[3] - acc[4 * q + 3]});
-      }
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4& up = RU[u][t][q >> 1];
+          const f32x4 uu = Raw<__bf16>::un4(u2{up[2 * (q & 1)], up[2 * (q & 1) + 1]});
+          In<__bf16>::store4(VTT + (32 * t + r) * LDC + 32 * I2 + 8 * q + 4 * h,
+                             f32x4{uu[0] - acc[t][4 * q], uu[1] - acc[t][4 * q + 1], uu[2] - acc[t][4 * q + 2],
+                                   uu[3] - acc[t][4 * q + 3]});
+        }
       phase_barrier();                                  // A: V~ ready
       phase_barrier();                                  // B: state copy ready
     });
   } else if (wid < NI2 + NJ2) {
-    // ================= S: state rows 32 J2 .. of this tile's 32 columns (entry
-    // 4q + e is row 32 J2 + 8q + 4h + e, column r), from [0 | I]
+    // ================= S: state rows 32 J2 .. of this workgroup's NTW x 32
+    // columns (entry 4q + e of tile t is row 32 J2 + 8q + 4h + e, column
+    // 32 (tile0 + t) + r), from [0 | I]
     const int J2 = wid - NI2;
-    const int pcol = 32 * (tile - nvt) + r;            // P tile: the identity column of this lane
     u32x4 RK[2][KSC];
     float RP[2];
     auto load = [&](int ch, u32x4* X, float& pv) {
@@ -1948,16 +1961,23 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
       for (int s = 0; s < KSC; ++s) X[s] = ld16(l16, cb + RL.kt + J2 * KSC * 1024 + 1024 * s);
       pv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wrsrc, 4 * r, cb + RL.pic + 128 * J2, 0));
     };
-    f32x16 Sacc;
+    f32x16 Sacc[NTW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Sacc[4 * q + e] = (ptile && 32 * J2 + 8 * q + 4 * h + e == pcol) ? 1.f : 0.f;
-    auto st_s0t = [&]() {
+    for (int t = 0; t < NTW; ++t) {
+      const int pcol = 32 * (tile0 + t - nvt) + r;     // P tile: the identity column of this lane
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        In<__bf16>::store4(S0T + r * LDK + 32 * J2 + 8 * q + 4 * h,
-                           f32x4{Sacc[4 * q], Sacc[4 * q + 1], Sacc[4 * q + 2], Sacc[4 * q + 3]});
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Sacc[t][4 * q + e] = (ptile && 32 * J2 + 8 * q + 4 * h + e == pcol) ? 1.f : 0.f;
+    }
+    auto st_s0t = [&]() {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          In<__bf16>::store4(S0T + (32 * t + r) * LDK + 32 * J2 + 8 * q + 4 * h,
+                             f32x4{Sacc[t][4 * q], Sacc[t][4 * q + 1], Sacc[t][4 * q + 2], Sacc[t][4 * q + 3]});
     };
     st_s0t();
     __syncthreads();
@@ -1971,20 +1991,29 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Sacc[4 * q + e] *= __int_as_float(__builtin_amdgcn_ds_bpermute(pbase + 4 * (8 * q + e), pb));
+        for (int e = 0; e < 4; ++e) {
+          const float f = __int_as_float(__builtin_amdgcn_ds_bpermute(pbase + 4 * (8 * q + e), pb));
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) Sacc[t][4 * q + e] *= f;
+        }
       phase_barrier();                                  // A
 #pragma unroll
-      for (int s = 0; s < KSC; ++s) Sacc = mma32(RK[u][s], vfrag(s), Sacc);
+      for (int s = 0; s < KSC; ++s)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) Sacc[t] = mma32(RK[u][s], vfrag(t, s), Sacc[t]);
       st_s0t();
       phase_barrier();                                  // B
     });
     float* out = Saug + seg_aug_off(sg, bh, BH, DK, DV);
-    const int col = ptile ? DV + pcol : 32 * tile + r;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int t = 0; t < NTW; ++t) {
+      const int col = ptile ? DV + 32 * (tile0 + t - nvt) + r : 32 * (tile0 + t) + r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[(size_t)(32 * J2 + 8 * q + 4 * h + e) * (DV + DK) + col] = Sacc[4 * q + e];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          out[(size_t)(32 * J2 + 8 * q + 4 * h + e) * (DV + DK) + col] = Sacc[t][4 * q + e];
+    }
   } else {
     __syncthreads();
     walk([&](int, auto) { phase_barrier(); phase_barrier(); });
@@ -2163,8 +2192,15 @@ static int launch_scan_fm(const ChunkArgs& a, const char* ws) {
     float* Ss = Saug + (size_t)nseg * BH * DK * (a.dv + DK);
     const int ntile = a.dv / 32 + DK / 32;
     void* a1[] = {&ws, &Saug, &T, &DV, &seg};
-    hipError_t e = hipLaunchKernel((const void*)gdn2_chunk_seg_state_kernel<DK, CM>, dim3((nseg - 1) * BH * ntile),
-                                   dim3(kSegThreads), a1, 0, (hipStream_t)a.stream);
+    // two 32-column tiles per workgroup where both the value and the P
+    // columns split into pairs (the shared operands are read once for both)
+    const bool pair = (a.dv / 32) % 2 == 0 && (DK / 32) % 2 == 0;
+    hipError_t e = pair ? hipLaunchKernel((const void*)gdn2_chunk_seg_state_kernel<DK, CM, 2>,
+                                          dim3((nseg - 1) * BH * (ntile / 2)), dim3(kSegThreads), a1, 0,
+                                          (hipStream_t)a.stream)
+                        : hipLaunchKernel((const void*)gdn2_chunk_seg_state_kernel<DK, CM, 1>,
+                                          dim3((nseg - 1) * BH * ntile), dim3(kSegThreads), a1, 0,
+                                          (hipStream_t)a.stream);
     if (e != hipSuccess) return GDR_ERR_LAUNCH;
     int nsg = nseg;
     void* a2[] = {&Saug, &S0, &Ss, &DV, &nsg};
