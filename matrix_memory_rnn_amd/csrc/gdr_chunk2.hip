@@ -1893,22 +1893,24 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
   const int l16 = lane * 16;
   auto s0frag = [&](int t, int s) { return *(const u32x4*)(S0T + (32 * t + r) * LDK + 16 * s + 8 * h); };
   auto vfrag = [&](int t, int s) { return *(const u32x4*)(VTT + (32 * t + r) * LDC + 16 * s + 8 * h); };
-  // each role walks the chunks with two register sets (the next chunk's
-  // operands load while this one's are used), unrolled by hand over the two
-  // sets with a single exit so the wait counts stay exact
+  // each role walks the chunks with three register sets (the operands of the
+  // next two chunks load while this one's are used), unrolled by hand over
+  // the sets with a single exit so the wait counts stay exact
   auto walk = [&](auto&& step) {
     int ch = 0;
-    for (; ch + 2 <= nch; ch += 2) {
+    for (; ch + 3 <= nch; ch += 3) {
       step(ch, Ic<0>{});
       step(ch + 1, Ic<1>{});
+      step(ch + 2, Ic<2>{});
     }
     if (ch < nch) step(ch, Ic<0>{});
+    if (ch + 1 < nch) step(ch + 1, Ic<1>{});
   };
 
   if (wid < NI2) {
     // ================= V: V~ rows 32 wid .. = U - Y S (U = 0 for P tiles) -> V~^T in LDS
     const int I2 = wid;
-    u32x4 RY[2][KSD], RU[2][NTW][2];
+    u32x4 RY[3][KSD], RU[3][NTW][2];
     // P tiles read U at an offset past the buffer's end: the loads return zero
     // (and every path issues the same loads)
     const int ub = ptile ? 0x7ffffff0 : lane * 32;
@@ -1924,9 +1926,10 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
     __syncthreads();                                    // initial state copy written
     __builtin_amdgcn_s_waitcnt(0);
     load(0, RY[0], RU[0]);
+    load(1, RY[1], RU[1]);
     walk([&](int ch, auto Uc) {
       constexpr int u = decltype(Uc)::value;
-      load(ch + 1, RY[1 - u], RU[1 - u]);
+      load(ch + 2, RY[(u + 2) % 3], RU[(u + 2) % 3]);
       f32x16 acc[NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) acc[t] = f16zero();
@@ -1953,8 +1956,8 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
     // columns (entry 4q + e of tile t is row 32 J2 + 8q + 4h + e, column
     // 32 (tile0 + t) + r), from [0 | I]
     const int J2 = wid - NI2;
-    u32x4 RK[2][KSC];
-    float RP[2];
+    u32x4 RK[3][KSC];
+    float RP[3];
     auto load = [&](int ch, u32x4* X, float& pv) {
       const int cb = cbase(ch);
 #pragma unroll
@@ -1984,9 +1987,10 @@ __global__ __launch_bounds__(kSegThreads) void gdn2_chunk_seg_state_kernel(const
     __builtin_amdgcn_s_waitcnt(0);
     const int pbase = 16 * h;
     load(0, RK[0], RP[0]);
+    load(1, RK[1], RP[1]);
     walk([&](int ch, auto Uc) {
       constexpr int u = decltype(Uc)::value;
-      load(ch + 1, RK[1 - u], RP[1 - u]);
+      load(ch + 2, RK[(u + 2) % 3], RP[(u + 2) % 3]);
       const int pb = __float_as_int(RP[u]);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
