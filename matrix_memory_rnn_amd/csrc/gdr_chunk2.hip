@@ -201,9 +201,8 @@ struct IntraSmem {
 // gamma * q with gamma = gstat[h] * 2 sigmoid(z_q) (zq NULL: z_q = 0; gstat
 // NULL: ones), and alog[h] is the head's log-rate.
 // INNT: the bf16 input loads take the non-temporal cache policy (kInNt). The
-// launcher turns it off where the sequence-segmented scan follows (there the
-// segment pass reading the records lost more: 32K workload, 0.625-0.638 ms
-// per step with plain loads against 0.633-0.645) and for the gate prologue.
+// launcher turns it off for the gate prologue (4K shape: 0.2808 ms per step
+// with plain loads against 0.2840).
 template <typename Tin, int DK, int CM, bool FM, bool GATED, bool INNT = true>
 __global__ __launch_bounds__(kIntraThreads, 2) void gdn2_chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
@@ -2128,12 +2127,6 @@ static int launch_intra_g(const ChunkArgs& a, char* ws) {
   // non-temporal input loads only for the plain gates: with the gate
   // prologue (4K shape) plain loads measured 0.2808 ms against 0.2840
   const void* kern = (const void*)gdn2_chunk_intra_kernel<Tin, DK, CM, FM, GATED, !GATED>;
-  if constexpr (FM) {
-    // plain input loads where the segmented scan follows (the plan depends on
-    // the shapes alone, so the intra and scan calls agree)
-    if (!a.no_seg && seg_plan(a.B, a.H, a.T, DK, a.dv, CM, a.dtype) != 0)
-      kern = (const void*)gdn2_chunk_intra_kernel<Tin, DK, CM, FM, GATED, false>;
-  }
   if (!allow_lds(kern, L::TOTAL)) return GDR_ERR_LAUNCH;
   int nchunks = (a.T + CM - 1) / CM;
   int nitems = a.B * a.H * nchunks;
