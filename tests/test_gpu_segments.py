@@ -19,6 +19,8 @@ pytestmark = pytest.mark.gpu
 SEQ = ("q", "k", "v", "alpha", "b", "w")
 
 
+# The segment maps take two 32-column tiles per workgroup where d_v/32 and
+# d_k/32 are both even (the first and third shapes), one tile otherwise.
 @pytest.mark.parametrize("B,H,T,dk,dv,chunk", [(1, 2, 64 * 40 + 13, 128, 128, 64),   # 2 segments of 21
                                                (1, 2, 32 * 70, 64, 32, 32),          # 4 segments of 18
                                                (2, 3, 64 * 64 + 5, 128, 64, 64),     # 6 units: 4 segments
